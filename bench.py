@@ -1,0 +1,192 @@
+"""KDA prefill + decode benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one synthetic batch:
+  * kda_prefill on the K3-shaped single-layer workload
+    (B=1, H=96, T=65536, d_k=d_v=128, bf16 q/k/v, fp32 z/beta, fp32 state out), then
+  * kda_decode on the batched decode workload
+    (256 sequences x 96 heads, 128x128 fp32 state updated in place).
+Inputs are seeded and already resident in HBM when timing starts.  W warmup
+steps run untimed, then exactly K steps are timed between two device
+synchronisations; HIP events on the launch stream time each entry point.
+After the timed region, 1000 extra decode steps measure the decode state
+bandwidth, and the fp64 oracle runs on a bounded sample on the host cores
+(the CPU baseline).  Rank 0 prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s & MFMA % (H=96,d=128); decode state GB/s vs HBM peak"
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, AMD published
+BF16_DENSE_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, AMD published
+# Algorithmic work per (token, head) pair at d = 128, chunk 64:
+#   bytes: q, k, v bf16 (3 x 256) + z fp32 (512) + beta (4) + o bf16 (256) = 1540
+#   useful flops: 6 d^2 (W S, Q S, K^T V') + 5 C d (lower-triangular C x C products) + C^2/3 (solve)
+PREFILL_BYTES_PER_PAIR = 1540
+PREFILL_FLOPS_PER_PAIR = 6 * 128 * 128 + 5 * 64 * 128 + (64 * 64) // 3
+# decode: state read + write (2 x 128 x 128 x 4) + q, k, v, o bf16 + z fp32 + beta = 132612
+DECODE_BYTES_PER_PAIR = 2 * 128 * 128 * 4 + 4 * 128 * 2 + 128 * 4 + 4
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--decode-steps", type=int, default=1000)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target wall time of the oracle sample")
+    return p.parse_args()
+
+
+def cpu_baseline(pre: dict, target_s: float) -> dict:
+    """The fp64 oracle, as it stands, on a bounded sample of the prefill
+    workload: the first `tok` tokens of `nh` heads, sized to run about
+    target_s seconds on every host core."""
+    import numpy as np
+    import oracle
+    from gated_delta_rule_21_amd import workloads as W
+
+    cores = os.cpu_count() or 1
+    H = pre["q"].shape[1]
+    nh = min(H, max(1, cores))
+
+    def run(tok):
+        sl = lambda t: t[:tok, :nh]
+        args = [W.as_numpy(sl(pre[n])) for n in ("q", "k", "v", "z")]
+        A = W.as_numpy(pre["A"][:nh])
+        beta = W.as_numpy(sl(pre["beta"]))
+        cu = np.array([0, tok], np.int32)
+        t0 = time.perf_counter()
+        oracle.prefill(args[0], args[1], args[2], args[3], A, beta, None, cu, nthreads=nh)
+        return time.perf_counter() - t0
+
+    tok = 256
+    dt = run(tok)
+    T = pre["q"].shape[0]
+    while dt < target_s / 4 and tok < T:
+        tok = min(T, int(tok * min(8.0, max(2.0, target_s / max(dt, 1e-3)))))
+        dt = run(tok)
+    pairs = tok * nh
+    return {"value": pairs / H / dt, "unit": "tokens/s", "cores": nh, "kind": "oracle",
+            "sample": "fp64 token-loop oracle (C, OpenMP) on the first %d tokens of %d of %d "
+                      "heads of the prefill workload; tokens/s counts full %d-head tokens "
+                      "(pairs / %d); %.2f s wall; host %s, %d logical cores"
+                      % (tok, nh, H, H, H, dt, platform.processor() or platform.machine(), cores)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
+              "(the multi-GPU sharding is described in DESIGN.md)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_21_amd as kda
+    from gated_delta_rule_21_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pre = W.make("k3_prefill", device=dev)
+    dec = W.make("k3_decode", device=dev)
+    T, H, D = pre["q"].shape
+    Nd = dec["q"].shape[0]
+    o = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+    ws = kda.prefill_workspace(1, T, H, D, kda.KDA_BF16, dev)
+    S = dec["S"].clone()
+    od = torch.empty((Nd, H, D), dtype=torch.bfloat16, device=dev)
+
+    def prefill():
+        kda.prefill(pre["q"], pre["k"], pre["v"], pre["z"], pre["A"], pre["beta"],
+                    pre["cu_seqlens"], h0=None, o=o, hT=hT, workspace=ws)
+
+    def decode():
+        kda.decode(dec["q"], dec["k"], dec["v"], dec["z"], dec["A"], dec["beta"], S, o=od)
+
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        prefill()
+        e[1].record()
+        decode()
+        e[2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    dec_ms_step = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    step_ms = wall * 1e3 / args.steps
+
+    # decode state bandwidth over repeated in-place steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.decode_steps):
+        decode()
+    e1.record()
+    torch.cuda.synchronize()
+    dec_ms = e0.elapsed_time(e1) / args.decode_steps
+
+    pairs = T * H
+    pre_bytes = PREFILL_BYTES_PER_PAIR * pairs
+    pre_gbps = pre_bytes / (pre_ms * 1e-3) / 1e9
+    pre_tflops = PREFILL_FLOPS_PER_PAIR * pairs / (pre_ms * 1e-3) / 1e12
+    dec_bytes = DECODE_BYTES_PER_PAIR * Nd * H
+    dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
+
+    line = {
+        "metric": METRIC,
+        "value": round((T + Nd) / (step_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k unit-norm bf16, v bf16, z and beta fp32)",
+        "config": {"workload": "k3_prefill B=1 H=96 T=65536 d=128 bf16 + k3_decode 256x96 "
+                               "fp32 128x128 state",
+                   "global_batch": 1, "seq_len": T, "heads": H, "head_dim": D,
+                   "decode_batch": Nd, "chunk": 64, "parallelism": "single GPU"},
+        "prefill": {"ms": round(pre_ms, 4), "tokens_per_s": round(T / (pre_ms * 1e-3), 1),
+                    "algorithmic_GBps": round(pre_gbps, 1),
+                    "hbm_frac": round(pre_gbps / HBM_PEAK_GBPS, 4),
+                    "useful_TFLOPs": round(pre_tflops, 2),
+                    "mfma_useful_frac": round(pre_tflops / BF16_DENSE_PEAK_TFLOPS, 4)},
+        "decode": {"ms_per_step": round(dec_ms, 4), "steps": args.decode_steps,
+                   "state_GBps": round(dec_gbps, 1), "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                   "ms_in_step": round(dec_ms_step, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(pre_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(pre_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "kda_prefill (chunk table + intra + inter kernels), "
+                               "1540 algorithmic B per (token, head) x 6291456 pairs per launch"},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

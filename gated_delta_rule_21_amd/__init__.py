@@ -1,0 +1,171 @@
+"""Kimi Delta Attention (KDA) on MI355X: Python binding of libkda.so.
+
+The binding only marshals arguments: torch tensors become device pointers,
+the current torch stream becomes the hipStream_t, and every step of the
+computation runs in the library's HIP kernels.  There is no CPU fallback: if
+the library is missing or the tensors are not on a GPU, the call raises.
+
+Entry points (same names as the C ABI in include/kda.h):
+  kda_prefill(...)                  raw C call, pointers as ints
+  kda_decode(...)                   raw C call
+  kda_prefill_workspace_size(...)
+  kda_status_string(status)
+Convenience wrappers over torch tensors:
+  prefill(q, k, v, z, A, beta, cu_seqlens, h0=None, ...) -> (o, hT)
+  decode(q, k, v, z, A, beta, S) -> o          (S updated in place)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_build", "libkda.so")
+
+KDA_BF16 = 0
+KDA_F32 = 1
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s failed: %s (%d)" % (fn, kda_status_string(status), status))
+        self.status = status
+
+
+def lib():
+    """The loaded libkda.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libkda.so not found at %s; build it with "
+                           "`python -m gated_delta_rule_21_amd.build`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, ci, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.kda_prefill.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, vp, vp, vp,
+                              sz, vp]
+    L.kda_prefill.restype = ci
+    L.kda_prefill_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
+    L.kda_prefill_workspace_size.restype = sz
+    L.kda_decode.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, vp, vp]
+    L.kda_decode.restype = ci
+    L.kda_status_string.argtypes = [ci]
+    L.kda_status_string.restype = ctypes.c_char_p
+    L.kda_build_info.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+# ---------------------------------------------------------------------------
+# Raw C entry points
+# ---------------------------------------------------------------------------
+def kda_prefill(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv, o, hT,
+                workspace, workspace_bytes, stream) -> int:
+    return lib().kda_prefill(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv, o,
+                             hT, workspace, workspace_bytes, stream)
+
+
+def kda_decode(io_dtype, q, k, v, z, A, beta, S_inout, N, H, dk, dv, o, stream) -> int:
+    return lib().kda_decode(io_dtype, q, k, v, z, A, beta, S_inout, N, H, dk, dv, o, stream)
+
+
+def kda_prefill_workspace_size(N, T, H, dk, dv, io_dtype) -> int:
+    return int(lib().kda_prefill_workspace_size(N, T, H, dk, dv, io_dtype))
+
+
+def kda_status_string(status: int) -> str:
+    return lib().kda_status_string(int(status)).decode()
+
+
+def kda_build_info() -> str:
+    return lib().kda_build_info().decode()
+
+
+# ---------------------------------------------------------------------------
+# torch wrappers (allocation and pointer marshalling only)
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _io_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError("q, k, v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _check_gpu(**tensors):
+    torch = _torch()
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError("%s must be a GPU tensor (the library has no CPU path)" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def prefill_workspace(N, T, H, d, io_dtype, device):
+    """Allocate the prefill workspace (a byte tensor of the size the library asks)."""
+    torch = _torch()
+    n = kda_prefill_workspace_size(N, T, H, d, d, io_dtype)
+    if n == 0:
+        raise ValueError("unsupported prefill sizes N=%d T=%d H=%d d=%d" % (N, T, H, d))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def prefill(q, k, v, z, A, beta, cu_seqlens, h0=None, o=None, hT=None, workspace=None,
+            final_state: bool = True):
+    """KDA prefill over packed sequences.  Returns (o, hT); hT is None when
+    final_state is False and no hT buffer is given."""
+    torch = _torch()
+    _check_gpu(q=q, k=k, v=v, z=z, A=A, beta=beta, cu_seqlens=cu_seqlens, h0=h0, o=o, hT=hT,
+               workspace=workspace)
+    io = _io_code(q)
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    if hT is None and final_state:
+        hT = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = prefill_workspace(N, T, H, dk, io, q.device)
+    st = kda_prefill(io, _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A), _ptr(beta), _ptr(h0),
+                     _ptr(cu_seqlens), N, T, H, dk, dv, _ptr(o), _ptr(hT), _ptr(workspace),
+                     workspace.numel(), _stream(q.device))
+    if st != 0:
+        raise KdaError("kda_prefill", st)
+    return o, hT
+
+
+def decode(q, k, v, z, A, beta, S, o=None):
+    """One decode step; S ([N, H, dv, dk] fp32) is updated in place.  Returns o."""
+    torch = _torch()
+    _check_gpu(q=q, k=k, v=v, z=z, A=A, beta=beta, S=S, o=o)
+    io = _io_code(q)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    st = kda_decode(io, _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A), _ptr(beta), _ptr(S), N, H,
+                    dk, dv, _ptr(o), _stream(q.device))
+    if st != 0:
+        raise KdaError("kda_decode", st)
+    return o

@@ -1,0 +1,155 @@
+// kda_api.hip -- the extern "C" entry points declared in include/kda.h:
+// argument checks, the prefill workspace plan, and kernel launches on the
+// caller's stream.  Nothing here allocates device memory or synchronises,
+// except the opt-in cu_seqlens check (KDA_DEBUG_CHECK_CU=1).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+bool supported_dim(int dk, int dv) { return dk == dv && (dk == 32 || dk == 64 || dk == 128); }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t io_size(kda_dtype t) { return t == KDA_F32 ? 4 : 2; }
+
+// [a, a + na) and [b, b + nb) overlap (byte ranges); empty ranges never do.
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+bool debug_check_cu() {
+    const char *e = std::getenv("KDA_DEBUG_CHECK_CU");
+    return e && e[0] == '1';
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_string(int status) {
+    switch (status) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case KDA_ERR_NULL_POINTER: return "required pointer is NULL";
+        case KDA_ERR_UNSUPPORTED_DIM: return "unsupported head dim (need dk == dv in {32, 64, 128})";
+        case KDA_ERR_UNSUPPORTED_DTYPE: return "unsupported io dtype";
+        case KDA_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+        case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case KDA_ERR_HIP: return "HIP kernel launch failed";
+        case KDA_ERR_ALIAS: return "output overlaps an input";
+    }
+    return "unknown kda status";
+}
+
+const char *kda_build_info(void) {
+    return "kda gfx950: chunk 64, bf16 MFMA 16x16x32 with split-precision operands, "
+           "fp32 MFMA 16x16x4, d in {32,64,128}";
+}
+
+size_t kda_prefill_workspace_size(int N, int T, int H, int dk, int dv, kda_dtype io_dtype) {
+    if (io_dtype != KDA_BF16 && io_dtype != KDA_F32) return 0;
+    if (!supported_dim(dk, dv) || N < 0 || T < 0 || H <= 0) return 0;
+    kda::PrefillPlan p;
+    if (!kda::plan_prefill(N, T, H, dk, dv, io_dtype == KDA_F32, &p)) return 0;
+    return p.total;
+}
+
+int kda_prefill(kda_dtype io_dtype, const void *q, const void *k, const void *v, const float *z,
+                const float *A, const float *beta, const float *h0, const int32_t *cu_seqlens,
+                int N, int T, int H, int dk, int dv, void *o, float *hT, void *workspace,
+                size_t workspace_bytes, void *stream) {
+    if (io_dtype != KDA_BF16 && io_dtype != KDA_F32) return KDA_ERR_UNSUPPORTED_DTYPE;
+    if (N < 0 || T < 0 || H <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (!supported_dim(dk, dv)) return KDA_ERR_UNSUPPORTED_DIM;
+    if (!A || !cu_seqlens || !workspace) return KDA_ERR_NULL_POINTER;
+    if (T > 0 && (!q || !k || !v || !z || !beta || !o)) return KDA_ERR_NULL_POINTER;
+    const void *ptrs[] = {q, k, v, z, A, beta, h0, cu_seqlens, o, hT};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_MISALIGNED;
+
+    kda::PrefillPlan plan;
+    if (!kda::plan_prefill(N, T, H, dk, dv, io_dtype == KDA_F32, &plan))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < plan.total) return KDA_ERR_WORKSPACE_TOO_SMALL;
+
+    const size_t tok = (size_t)T * H;
+    const size_t o_bytes = tok * dv * io_size(io_dtype);
+    const size_t st_bytes = (size_t)N * H * dv * dk * 4;
+    const struct { const void *p; size_t n; } ins[] = {
+        {q, tok * dk * io_size(io_dtype)}, {k, tok * dk * io_size(io_dtype)},
+        {v, tok * dv * io_size(io_dtype)}, {z, tok * dk * 4}, {A, (size_t)H * 4},
+        {beta, tok * 4}, {cu_seqlens, (size_t)(N + 1) * 4}, {h0, st_bytes},
+        {workspace, plan.total}};
+    for (const auto &in : ins) {
+        if (overlaps(o, o_bytes, in.p, in.n)) return KDA_ERR_ALIAS;
+        if (in.p != h0 && overlaps(hT, st_bytes, in.p, in.n)) return KDA_ERR_ALIAS;
+    }
+    if (hT && h0 && hT != h0 && overlaps(hT, st_bytes, h0, st_bytes)) return KDA_ERR_ALIAS;
+    if (overlaps(o, o_bytes, hT, st_bytes)) return KDA_ERR_ALIAS;
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (debug_check_cu()) {
+        std::vector<int32_t> cu(N + 1);
+        if (hipMemcpyAsync(cu.data(), cu_seqlens, sizeof(int32_t) * (N + 1), hipMemcpyDeviceToHost,
+                           st) != hipSuccess ||
+            hipStreamSynchronize(st) != hipSuccess)
+            return KDA_ERR_HIP;
+        if (cu[0] != 0 || cu[N] != T) return KDA_ERR_INVALID_ARGUMENT;
+        for (int n = 0; n < N; ++n)
+            if (cu[n + 1] < cu[n]) return KDA_ERR_INVALID_ARGUMENT;
+    }
+
+    kda::PrefillArgs a;
+    a.f32io = io_dtype == KDA_F32;
+    a.q = q; a.k = k; a.v = v; a.z = z; a.A = A; a.beta = beta; a.h0 = h0;
+    a.cu = cu_seqlens;
+    a.N = N; a.T = T; a.H = H; a.dk = dk; a.dv = dv;
+    a.o = o; a.hT = hT;
+    a.ws = static_cast<unsigned char *>(workspace);
+    a.plan = plan;
+    a.stream = st;
+    return kda::launch_prefill(a) == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_decode(kda_dtype io_dtype, const void *q, const void *k, const void *v, const float *z,
+               const float *A, const float *beta, float *S_inout, int N, int H, int dk, int dv,
+               void *o, void *stream) {
+    if (io_dtype != KDA_BF16 && io_dtype != KDA_F32) return KDA_ERR_UNSUPPORTED_DTYPE;
+    if (N < 0 || H <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (!supported_dim(dk, dv)) return KDA_ERR_UNSUPPORTED_DIM;
+    if (!A) return KDA_ERR_NULL_POINTER;
+    if (N > 0 && (!q || !k || !v || !z || !beta || !S_inout || !o)) return KDA_ERR_NULL_POINTER;
+    const void *ptrs[] = {q, k, v, z, A, beta, S_inout, o};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    const size_t nh = (size_t)N * H;
+    const size_t st_bytes = nh * dv * dk * 4, o_bytes = nh * dv * io_size(io_dtype);
+    const struct { const void *p; size_t n; } ins[] = {
+        {q, nh * dk * io_size(io_dtype)}, {k, nh * dk * io_size(io_dtype)},
+        {v, nh * dv * io_size(io_dtype)}, {z, nh * dk * 4}, {A, (size_t)H * 4}, {beta, nh * 4}};
+    for (const auto &in : ins)
+        if (overlaps(o, o_bytes, in.p, in.n) || overlaps(S_inout, st_bytes, in.p, in.n))
+            return KDA_ERR_ALIAS;
+    if (overlaps(o, o_bytes, S_inout, st_bytes)) return KDA_ERR_ALIAS;
+
+    kda::DecodeArgs a;
+    a.f32io = io_dtype == KDA_F32;
+    a.q = q; a.k = k; a.v = v; a.z = z; a.A = A; a.beta = beta;
+    a.S = S_inout; a.o = o;
+    a.N = N; a.H = H; a.dk = dk; a.dv = dv;
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+    return kda::launch_decode(a) == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

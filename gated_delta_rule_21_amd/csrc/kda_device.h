@@ -1,0 +1,130 @@
+// kda_device.h -- device-side helpers shared by the gfx950 KDA kernels:
+// bf16 conversion and splitting, the bounded gate, and 16x16 MFMA tiles.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Chunk length of the chunkwise prefill and the MFMA tile edge.
+constexpr int kChunk = 64;
+constexpr int kTile = 16;
+
+// log2(e) and g_min * log2(e): the kernels keep log-decays in base 2 so that
+// every exponential is a single v_exp_f32.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kGminLog2e = -5.0f * 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+    // round to nearest even; NaN keeps a quiet mantissa bit
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): 16 mantissa bits in total.
+__device__ __forceinline__ void split_bf16(float x, uint32_t &hi, uint32_t &lo) {
+    hi = f32_to_bf16_bits(x);
+    lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+}
+__device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return lo16 | (hi16 << 16); }
+
+// Load element i of an io-dtype array as fp32.
+template <bool F32IO>
+__device__ __forceinline__ float load_io(const void *p, size_t i) {
+    if constexpr (F32IO) {
+        return reinterpret_cast<const float *>(p)[i];
+    } else {
+        return bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(p)[i]);
+    }
+}
+template <bool F32IO>
+__device__ __forceinline__ void store_io(void *p, size_t i, float x) {
+    if constexpr (F32IO) {
+        reinterpret_cast<float *>(p)[i] = x;
+    } else {
+        reinterpret_cast<uint16_t *>(p)[i] = (uint16_t)f32_to_bf16_bits(x);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Bounded gate in base 2: g * log2(e) with g = -5 sigmoid(exp(A_h) z)
+// (devpress K3 walk-through §3.2, Eq 5; "Kimi K3：架构…" §3.2).
+// `ea` is exp(A_h).  sigmoid saturates to exactly 0 or 1 at the ends, so the
+// result spans [-5 log2 e, 0].
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float gate_log2(float ea, float z) {
+    float x = ea * z;
+    float s = __frcp_rn(1.0f + exp2f(-x * kLog2e));
+    return kGminLog2e * s;
+}
+
+// ---------------------------------------------------------------------------
+// 16x16 MFMA tiles.  Fragment convention used by every kernel here:
+//   A operand (16 x K16):  lane (m, g) = (l % 16, l / 16) holds A[m][4g + j], j = 0..3
+//   B operand (K16 x 16):  lane (n, g) holds B[4g + j][n]
+//   accumulator (16x16):   lane (n, g) holds D[4g + j][n]
+// so an accumulator is directly a B operand of the next product.  Two K16
+// tiles are fused into one 16x16x32 bf16 MFMA by concatenating the lanes'
+// quads (A and B use the same slot for the same k, which is all the
+// instruction needs).  fp32 operands use four 16x16x4 MFMAs per K16 tile.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mma_bf16_k32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_f32_k16(f32x4 a, f32x4 b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+    return c;
+}
+
+// Two fp32 quads (K16 tiles t0, t1) -> one bf16 K32 fragment, rounded (hi)
+// or split into hi and lo parts.
+__device__ __forceinline__ u32x4 quads_to_bf16(f32x4 x0, f32x4 x1) {
+    u32x4 r;
+    r[0] = pack2(f32_to_bf16_bits(x0[0]), f32_to_bf16_bits(x0[1]));
+    r[1] = pack2(f32_to_bf16_bits(x0[2]), f32_to_bf16_bits(x0[3]));
+    r[2] = pack2(f32_to_bf16_bits(x1[0]), f32_to_bf16_bits(x1[1]));
+    r[3] = pack2(f32_to_bf16_bits(x1[2]), f32_to_bf16_bits(x1[3]));
+    return r;
+}
+__device__ __forceinline__ void quads_to_bf16_split(f32x4 x0, f32x4 x1, u32x4 &hi, u32x4 &lo) {
+    uint32_t h[8], l[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        split_bf16(x0[j], h[j], l[j]);
+        split_bf16(x1[j], h[4 + j], l[4 + j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        hi[j] = pack2(h[2 * j], h[2 * j + 1]);
+        lo[j] = pack2(l[2 * j], l[2 * j + 1]);
+    }
+}
+
+// acc + (ah + al)(bh + bl) without the lo*lo term: a product of two
+// split operands, good to about 2^-16 relative per term.
+__device__ __forceinline__ f32x4 mma3_bf16(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f32x4 c) {
+    c = mma_bf16_k32(ah, bh, c);
+    c = mma_bf16_k32(ah, bl, c);
+    return mma_bf16_k32(al, bh, c);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace kda

@@ -1,0 +1,51 @@
+// kda_internal.h -- launch descriptors shared by the host entry points and
+// the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeArgs {
+    bool f32io;
+    const void *q, *k, *v;
+    const float *z, *A, *beta;
+    float *S;
+    void *o;
+    int N, H, dk, dv;
+    hipStream_t stream;
+};
+
+// Workspace plan of the chunkwise prefill.  Offsets are bytes from the
+// workspace base; every region is 256-byte aligned.
+struct PrefillPlan {
+    int max_chunks;          // ceil(T / 64) + N: an upper bound on the chunk count
+    size_t slab_bytes;       // per (chunk, head) intermediate slab
+    size_t off_meta;         // int32 [N + 1] per-sequence first chunk, then [1] total
+    size_t off_table;        // int32x4 [max_chunks]: sequence, first token, length, -
+    size_t off_slabs;        // slabs, head-major: [H][max_chunks]
+    size_t total;
+};
+
+struct PrefillArgs {
+    bool f32io;
+    const void *q, *k, *v;
+    const float *z, *A, *beta, *h0;
+    const int32_t *cu;
+    int N, T, H, dk, dv;
+    void *o;
+    float *hT;
+    unsigned char *ws;
+    PrefillPlan plan;
+    hipStream_t stream;
+};
+
+bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, PrefillPlan *plan);
+size_t slab_bytes(int dk, int dv, bool f32io);
+
+int launch_decode(const DecodeArgs &a);
+int launch_prefill(const PrefillArgs &a);
+
+}  // namespace kda

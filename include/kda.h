@@ -1,0 +1,129 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library.
+ *
+ * Operation (per head, state S in R^{dk x dv}):
+ *   g_t     = g_min * sigmoid(exp(A_h) * z_t),  g_min = -5,  alpha_t = exp(g_t)
+ *   S_t     = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *   o_t     = S_t^T q_t
+ * -- devpress K3 technical-report walk-through §3.1 (Eq 1) and §3.2 (Eq 5);
+ *    "Kimi K3：架构、训练与推理系统研究" §3.1-3.2; "Hybrid KDA–MLA：Kimi K3
+ *    注意力机制解析" (core update and decay design).  No query scale is
+ *    applied; q and k are expected to be L2-normalised by the caller (the
+ *    feature path of P5 §3.2 ends in an L2Norm), which is not checked.
+ *
+ * Two entry points, matching the two execution paths the pages describe
+ * ("Kimi K3：架构…" §14: chunked kernel for prompts, fused recurrent kernel
+ * for cached single-token decode; §11.1-11.2: prefill saves the final
+ * states, decode updates them in place):
+ *   kda_prefill  packed variable-length sequences, chunkwise-parallel inside
+ *                64-token chunks, state carried serially between chunks;
+ *   kda_decode   one new token per sequence, state updated in place.
+ *
+ * Layouts (all row-major, all device memory unless noted):
+ *   q, k, z      [T][H][dk]          v, o  [T][H][dv]
+ *   beta         [T][H]  fp32, used as given (already passed through sigmoid)
+ *   A            [H]     fp32 per-head log-scale
+ *   z            fp32 decay logits (raw, before the gate)
+ *   states       [N][H][dv][dk] fp32: element (n, h, j, i) is S_{i,j}
+ *                (row j = value channel, contiguous over key channels; the
+ *                [B,H,V,K] state shape of P5 §13.1)
+ *   cu_seqlens   [N+1] int32, cu[0] = 0, non-decreasing, cu[N] = T
+ * The io dtype applies to q, k, v and o; z, A, beta and all states are fp32.
+ *
+ * Supported: dk == dv in {32, 64, 128}; io dtype KDA_BF16 or KDA_F32.
+ * All pointers must be 16-byte aligned.  Every call is asynchronous on
+ * `stream` (a hipStream_t; NULL is the default stream), never synchronises
+ * the host and never throws.  The library keeps no pointer after a call
+ * returns and allocates no device memory in these calls.
+ *
+ * Return value: KDA_OK (0) or a negative kda_status.  On an error the call
+ * launches nothing and leaves every output untouched, except KDA_ERR_HIP,
+ * which reports a failed launch (outputs then undefined).
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_dtype {
+    KDA_BF16 = 0, /* bfloat16 q, k, v, o; bf16 MFMA with split-precision operands */
+    KDA_F32 = 1   /* fp32 q, k, v, o; fp32 MFMA throughout */
+} kda_dtype;
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = -1,     /* negative size, bad cu_seqlens size, ... */
+    KDA_ERR_NULL_POINTER = -2,         /* a required pointer is NULL */
+    KDA_ERR_UNSUPPORTED_DIM = -3,      /* dk != dv or d not in {32, 64, 128} */
+    KDA_ERR_UNSUPPORTED_DTYPE = -4,    /* io dtype not KDA_BF16 / KDA_F32 */
+    KDA_ERR_MISALIGNED = -5,           /* a pointer is not 16-byte aligned */
+    KDA_ERR_WORKSPACE_TOO_SMALL = -6,  /* workspace_bytes < kda_prefill_workspace_size */
+    KDA_ERR_HIP = -7,                  /* a kernel launch failed */
+    KDA_ERR_ALIAS = -8                 /* an output overlaps an input it may not alias */
+} kda_status;
+
+/*
+ * Workspace bytes kda_prefill needs for these sizes.  Depends only on the
+ * arguments (an upper bound over every cu_seqlens with N sequences and T
+ * tokens).  Returns 0 for sizes kda_prefill would reject.
+ */
+size_t kda_prefill_workspace_size(int N, int T, int H, int dk, int dv, kda_dtype io_dtype);
+
+/*
+ * Chunkwise prefill over N packed sequences (T tokens in total).
+ *
+ *   q, k, v      inputs, io dtype (layouts above)
+ *   z, A, beta   fp32 gate inputs
+ *   h0           [N][H][dv][dk] initial states, or NULL for zeros
+ *   cu_seqlens   [N+1] int32 device array; sequence n is tokens
+ *                [cu[n], cu[n+1]); its chunks of 64 start at cu[n], the last
+ *                one may be partial; a zero-length sequence gives hT = h0
+ *   o            [T][H][dv] output, io dtype
+ *   hT           [N][H][dv][dk] final states, or NULL to skip; may be the
+ *                same pointer as h0 (each block reads its slice of h0 before
+ *                writing that slice of hT), but must not overlap it otherwise
+ *   workspace    device scratch of at least kda_prefill_workspace_size(...)
+ *                bytes, 256-byte aligned, owned by the caller; contents on
+ *                entry are ignored, on return undefined
+ *
+ * cu_seqlens content is not read on the host.  With KDA_DEBUG_CHECK_CU=1 in
+ * the environment the call copies it to the host, synchronises `stream`
+ * and returns KDA_ERR_INVALID_ARGUMENT if it is not a valid prefix sum.
+ */
+int kda_prefill(kda_dtype io_dtype, const void *q, const void *k, const void *v,
+                const float *z, const float *A, const float *beta, const float *h0,
+                const int32_t *cu_seqlens, int N, int T, int H, int dk, int dv, void *o,
+                float *hT, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step for N sequences, one token each.
+ *
+ *   q, k         [N][H][dk] io dtype;  v [N][H][dv] io dtype
+ *   z            [N][H][dk] fp32;  A [H] fp32;  beta [N][H] fp32
+ *   S_inout      [N][H][dv][dk] fp32 state, read once and overwritten once
+ *   o            [N][H][dv] output, io dtype
+ *
+ * Each (sequence, head) state is read from HBM exactly once and written
+ * back exactly once ("Kimi K3：架构…" §11.4 and §13.2: a decode step costs
+ * one full read and write of the state).
+ */
+int kda_decode(kda_dtype io_dtype, const void *q, const void *k, const void *v,
+               const float *z, const float *A, const float *beta, float *S_inout, int N,
+               int H, int dk, int dv, void *o, void *stream);
+
+/* Static, human-readable text for a kda_status value. */
+const char *kda_status_string(int status);
+
+/* Static build description (target, chunk size, library version). */
+const char *kda_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

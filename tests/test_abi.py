@@ -1,0 +1,96 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/kda.h declares, sizes the workspace, and rejects bad arguments with
+the documented status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_21_amd as kda
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "kda.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(["kda_build_info", "kda_decode", "kda_prefill",
+                                           "kda_prefill_workspace_size", "kda_status_string"])
+
+
+def test_library_exports_every_declared_symbol():
+    L = kda.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = os.popen("nm -D --defined-only %s" % kda.LIB_PATH).read()
+    for name in declared_functions():
+        assert re.search(r"\bT %s\b" % name, out), name
+
+
+def test_status_strings():
+    assert kda.kda_status_string(0) == "ok"
+    for s in range(-8, 0):
+        assert kda.kda_status_string(s) != "unknown kda status"
+    assert kda.kda_status_string(-99) == "unknown kda status"
+
+
+def test_workspace_size():
+    # slabs: H * (ceil(T/64) + N) chunks, one slab each
+    n1 = kda.kda_prefill_workspace_size(1, 65536, 96, 128, 128, kda.KDA_BF16)
+    n2 = kda.kda_prefill_workspace_size(1, 65536 + 64, 96, 128, 128, kda.KDA_BF16)
+    per = (n2 - n1) // 96
+    assert per > 0 and per % 256 == 0
+    assert n1 >= 96 * 1025 * per
+    assert kda.kda_prefill_workspace_size(1, 100, 2, 32, 64, kda.KDA_BF16) == 0   # dk != dv
+    assert kda.kda_prefill_workspace_size(1, 100, 2, 96, 96, kda.KDA_BF16) == 0   # d unsupported
+    assert kda.kda_prefill_workspace_size(1, 100, 2, 32, 32, 7) == 0              # dtype
+    assert kda.kda_prefill_workspace_size(0, 0, 2, 32, 32, kda.KDA_F32) > 0
+
+
+FAKE = 1 << 20   # an aligned address that is never dereferenced: every call below fails its checks first
+
+
+def _prefill(**over):
+    a = dict(io_dtype=kda.KDA_BF16, q=FAKE, k=FAKE + 4096, v=FAKE + 8192, z=FAKE + 16384,
+             A=FAKE + 32768, beta=FAKE + 40960, h0=None, cu=FAKE + 49152, N=1, T=16, H=2,
+             dk=32, dv=32, o=FAKE + 65536, hT=None, ws=1 << 24, ws_bytes=0, stream=None)
+    a.update(over)
+    if a["ws_bytes"] == 0 and "ws_bytes" not in over:
+        a["ws_bytes"] = kda.kda_prefill_workspace_size(a["N"], a["T"], a["H"], a["dk"], a["dv"], 0) - 1
+    return kda.kda_prefill(a["io_dtype"], a["q"], a["k"], a["v"], a["z"], a["A"], a["beta"], a["h0"],
+                           a["cu"], a["N"], a["T"], a["H"], a["dk"], a["dv"], a["o"], a["hT"], a["ws"],
+                           a["ws_bytes"], a["stream"])
+
+
+def test_prefill_rejects_bad_arguments():
+    assert _prefill(io_dtype=5) == -4
+    assert _prefill(N=-1) == -1
+    assert _prefill(H=0) == -1
+    assert _prefill(dk=64) == -3
+    assert _prefill(dk=48, dv=48) == -3
+    assert _prefill(q=None) == -2
+    assert _prefill(cu=None) == -2
+    assert _prefill(ws=None) == -2
+    assert _prefill(q=FAKE + 2) == -5
+    assert _prefill(ws=(1 << 24) + 16) == -5
+    assert _prefill() == -6                       # workspace one byte short
+    big = 1 << 40
+    assert _prefill(ws_bytes=big, o=FAKE) == -8   # o on top of q
+
+
+def test_decode_rejects_bad_arguments():
+    d = lambda **o: kda.kda_decode(o.get("io", 0), o.get("q", FAKE), FAKE + 4096, FAKE + 8192,
+                                   FAKE + 16384, FAKE + 32768, FAKE + 40960, o.get("S", FAKE + 65536),
+                                   o.get("N", 2), 2, o.get("d", 32), o.get("d", 32),
+                                   o.get("o", 1 << 22), None)
+    assert d(io=3) == -4
+    assert d(N=-2) == -1
+    assert d(d=16) == -3
+    assert d(q=None) == -2
+    assert d(S=FAKE + 8) == -5
+    assert d(o=FAKE + 4096) == -8                 # o on top of k
