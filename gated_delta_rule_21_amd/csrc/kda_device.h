@@ -23,16 +23,20 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kGminLog2e = -5.0f * 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
-// bf16 <-> fp32
+// bf16 <-> fp32.  fp32 -> bf16 uses the hardware packed convert
+// (v_cvt_pk_bf16_f32, round to nearest even).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
-    // round to nearest even; NaN keeps a quiet mantissa bit
-    uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) { return f32x2_to_bf16x2(x, 0.f) & 0xffffu; }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ float bf16_lo_half(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_half(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): 16 mantissa bits in total.
 __device__ __forceinline__ void split_bf16(float x, uint32_t &hi, uint32_t &lo) {
@@ -55,7 +59,7 @@ __device__ __forceinline__ void store_io(void *p, size_t i, float x) {
     if constexpr (F32IO) {
         reinterpret_cast<float *>(p)[i] = x;
     } else {
-        reinterpret_cast<uint16_t *>(p)[i] = (uint16_t)f32_to_bf16_bits(x);
+        reinterpret_cast<__bf16 *>(p)[i] = (__bf16)x;
     }
 }
 
@@ -96,25 +100,19 @@ __device__ __forceinline__ f32x4 mma_f32_k16(f32x4 a, f32x4 b, f32x4 c) {
 // Two fp32 quads (K16 tiles t0, t1) -> one bf16 K32 fragment, rounded (hi)
 // or split into hi and lo parts.
 __device__ __forceinline__ u32x4 quads_to_bf16(f32x4 x0, f32x4 x1) {
-    u32x4 r;
-    r[0] = pack2(f32_to_bf16_bits(x0[0]), f32_to_bf16_bits(x0[1]));
-    r[1] = pack2(f32_to_bf16_bits(x0[2]), f32_to_bf16_bits(x0[3]));
-    r[2] = pack2(f32_to_bf16_bits(x1[0]), f32_to_bf16_bits(x1[1]));
-    r[3] = pack2(f32_to_bf16_bits(x1[2]), f32_to_bf16_bits(x1[3]));
-    return r;
+    return u32x4{f32x2_to_bf16x2(x0[0], x0[1]), f32x2_to_bf16x2(x0[2], x0[3]),
+                 f32x2_to_bf16x2(x1[0], x1[1]), f32x2_to_bf16x2(x1[2], x1[3])};
+}
+// The fp32 values of a packed bf16 fragment (slot order).
+__device__ __forceinline__ void bf16_to_quads(u32x4 w, f32x4 &x0, f32x4 &x1) {
+    x0 = f32x4{bf16_lo_half(w[0]), bf16_hi_half(w[0]), bf16_lo_half(w[1]), bf16_hi_half(w[1])};
+    x1 = f32x4{bf16_lo_half(w[2]), bf16_hi_half(w[2]), bf16_lo_half(w[3]), bf16_hi_half(w[3])};
 }
 __device__ __forceinline__ void quads_to_bf16_split(f32x4 x0, f32x4 x1, u32x4 &hi, u32x4 &lo) {
-    uint32_t h[8], l[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        split_bf16(x0[j], h[j], l[j]);
-        split_bf16(x1[j], h[4 + j], l[4 + j]);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        hi[j] = pack2(h[2 * j], h[2 * j + 1]);
-        lo[j] = pack2(l[2 * j], l[2 * j + 1]);
-    }
+    hi = quads_to_bf16(x0, x1);
+    f32x4 h0, h1;
+    bf16_to_quads(hi, h0, h1);
+    lo = quads_to_bf16(x0 - h0, x1 - h1);
 }
 
 // acc + (ah + al)(bh + bl) without the lo*lo term: a product of two

@@ -31,6 +31,9 @@
 #include "kda_device.h"
 #include "kda_internal.h"
 
+#include <algorithm>
+#include <type_traits>
+
 namespace kda {
 
 // ---------------------------------------------------------------------------
@@ -139,22 +142,35 @@ __global__ void __launch_bounds__(256) chunk_table_kernel(const int32_t *__restr
 }
 
 // ---------------------------------------------------------------------------
-// Intra-chunk kernel.
+// Intra-chunk kernel.  Persistent: each workgroup walks (chunk, head) items
+// with a stride of the grid size and prefetches the next item's raw inputs
+// into registers while it computes the current one.
+//
+// In phase 1 wave w owns the 16-row block I = w; lane (ln, lg) = (l % 16,
+// l / 16) holds row 16w + ln and key channels 16kt + 4lg + {0..3}.  That is
+// the MFMA A-operand layout, and a scan over the 16 lanes of a row group
+// gives the block-local cumulative log-decay of every channel.
 // ---------------------------------------------------------------------------
 template <int D>
 struct IntraLds {
-    static constexpr int P = D + 4;  // row pitch (floats) of the [64][D] arrays
-    float kr[64][P];   // k_r * exp2(Gl_r): row operand of A_kk; Gamma*K after a block prefix
-    float qr[64][P];   // q_r * exp2(Gl_r): row operand of A_qk; reused for V
-    float ke[64][P];   // k_i * exp2(bt_J - Gl_i): decay from i to the end of its block
-    float a[64][68];   // A_kk (beta and the strict lower mask applied)
-    float tm[64][68];  // T = (I + A_kk)^{-1}
+    static constexpr int P = D + 4;          // fp32 row pitch (floats)
+    static constexpr int RB = 4 * P;         // row pitch (bytes) of the row-operand arrays
+    static constexpr int TP = 64 + 4;        // row pitch (elements) of the transposed bf16 arrays
+    // Row operands k_r exp2(Gl_r) and q_r exp2(Gl_r).  bf16 path: per row,
+    // [pair p][hi, lo][lane group][8 bf16], so one 16-byte read is one MFMA
+    // fragment slot; fp32 path: [64][P] floats.  After the Gram phase the
+    // bf16 path reuses both arrays for (Gamma*K)^T split into hi and lo.
+    unsigned char krs[64 * RB];
+    unsigned char qrs[64 * RB];
+    float ke[64][P];      // k_i exp2(bt_J - Gl_i); fp32 path: V after the Gram phase
+    float a[64][68];      // A_kk, then T = (I + A_kk)^{-1} in place
+    uint16_t vt[D][TP];   // bf16 path: V^T (bf16 bits)
     float beta[64];
-    float bt[4][D];    // block log2-decay totals
-    float pfx[4][D];   // exp2(sum_{m<I} bt_m)       decay from the chunk start to block I
-    float sfx[4][D];   // exp2(sum_{m>J} bt_m)       decay from block J+1 to the chunk end
-    float dg[4][D];    // exp2(-bt_J)                undo one block: diagonal column factor
-    float off[6][D];   // exp2(sum_{J<m<I} bt_m)     blocks strictly between J and I
+    float bt[4][D];       // block log2-decay totals
+    float pfx[4][D];      // exp2(sum_{m<I} bt_m)       chunk start -> start of block I
+    float sfx[4][D];      // exp2(sum_{m>J} bt_m)       end of block J -> chunk end
+    float dg[4][D];       // exp2(-bt_J)                undo one block: diagonal column factor
+    float off[6][D];      // exp2(sum_{J<m<I} bt_m)     blocks strictly between J and I
 };
 
 __device__ __forceinline__ int off_index(int J, int I) {
@@ -170,6 +186,63 @@ template <int P>
 __device__ __forceinline__ f32x4 lds_col4(const float (*a)[P], int row0, int col) {
     return f32x4{a[row0][col], a[row0 + 1][col], a[row0 + 2][col], a[row0 + 3][col]};
 }
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ u32x4 cat2(u32x2 a, u32x2 b) { return u32x4{a[0], a[1], b[0], b[1]}; }
+template <int TP>
+__device__ __forceinline__ u32x2 lds_bf16x4(const uint16_t (*a)[TP], int row, int col) {
+    return *reinterpret_cast<const u32x2 *>(&a[row][col]);
+}
+
+// Raw inputs of one (chunk, head) item for one lane: KT quads of z, k, q, v.
+template <int D, bool F32IO>
+struct IntraRegs {
+    static constexpr int KT = D / 16;
+    using Q = typename std::conditional<F32IO, f32x4, u32x2>::type;
+    f32x4 z[KT];
+    Q k[KT], q[KT], v[KT];
+    float beta;
+};
+
+template <int D, bool F32IO>
+__device__ __forceinline__ void intra_load(IntraRegs<D, F32IO> &R, const void *q, const void *k,
+                                           const void *v, const float *z, const float *beta,
+                                           int4 ent, int h, int H, int lane, int wave) {
+    constexpr int KT = D / 16;
+    constexpr int ES = F32IO ? 4 : 2;
+    using Q = typename IntraRegs<D, F32IO>::Q;
+    const int ln = lane & 15, lg = lane >> 4;
+    const int row = 16 * wave + ln;
+    const bool ok = row < ent.z;
+    const size_t base = ((size_t)(ent.y + (ok ? row : 0)) * H + h) * D + 4 * lg;
+    const unsigned char *kb = reinterpret_cast<const unsigned char *>(k);
+    const unsigned char *qb = reinterpret_cast<const unsigned char *>(q);
+    const unsigned char *vb = reinterpret_cast<const unsigned char *>(v);
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        const size_t idx = base + 16 * kt;
+        if (ok) {
+            R.z[kt] = ld4(z + idx);
+            R.k[kt] = *reinterpret_cast<const Q *>(kb + idx * ES);
+            R.q[kt] = *reinterpret_cast<const Q *>(qb + idx * ES);
+            R.v[kt] = *reinterpret_cast<const Q *>(vb + idx * ES);
+        } else {
+            R.z[kt] = zero4();
+            R.k[kt] = Q{};
+            R.q[kt] = Q{};
+            R.v[kt] = Q{};
+        }
+    }
+    R.beta = (ok && lg == 0) ? beta[(size_t)(ent.y + row) * H + h] : 0.f;
+}
+
+template <bool F32IO, typename Q>
+__device__ __forceinline__ f32x4 quad_f32(Q x) {
+    if constexpr (F32IO) {
+        return x;
+    } else {
+        return f32x4{bf16_lo_half(x[0]), bf16_hi_half(x[0]), bf16_lo_half(x[1]), bf16_hi_half(x[1])};
+    }
+}
 
 template <int D, bool F32IO>
 __global__ void __launch_bounds__(256) intra_kernel(
@@ -178,274 +251,354 @@ __global__ void __launch_bounds__(256) intra_kernel(
     const int32_t *__restrict__ meta, const int4 *__restrict__ table, int N, int H,
     int max_chunks, unsigned char *__restrict__ slabs, size_t slab_stride) {
     using SL = Slab<D, F32IO>;
+    using LDS = IntraLds<D>;
     constexpr int KT = D / 16;
+    constexpr int P = LDS::P, RB = LDS::RB, TP = LDS::TP;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
-    IntraLds<D> &s = *reinterpret_cast<IntraLds<D> *>(lds_raw);
+    LDS &s = *reinterpret_cast<LDS *>(lds_raw);
+    float (*krf)[P] = reinterpret_cast<float (*)[P]>(s.krs);   // fp32 path views
+    float (*qrf)[P] = reinterpret_cast<float (*)[P]>(s.qrs);
+    uint16_t (*gkh)[TP] = reinterpret_cast<uint16_t (*)[TP]>(s.krs);               // bf16 path:
+    uint16_t (*gkl)[TP] = reinterpret_cast<uint16_t (*)[TP]>(s.krs + D * TP * 2);  // (Gamma*K)^T
 
-    const int chunk = blockIdx.x;
-    const int h = blockIdx.y;
-    if (chunk >= meta[N]) return;
-    const int4 ent = table[chunk];
-    const int t0 = ent.y, L = ent.z;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int ln = lane & 15, lg = lane >> 4;
-    unsigned char *slab = slabs + ((size_t)h * max_chunks + chunk) * slab_stride;
+    const int total = meta[N] * H;
+    const int stride = gridDim.x;
 
-    // ---- phase 1: gate, block-local cumulative log2-decay, scaled operands
-    for (int i = tid; i < 64 * 68; i += 256) {
-        (&s.a[0][0])[i] = 0.f;
-        (&s.tm[0][0])[i] = 0.f;
-    }
-    if (tid < 64) s.beta[tid] = tid < L ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
-    const float ea = __expf(A[h]);
-    for (int task = tid; task < 4 * D; task += 256) {
-        const int c = task % D, I = task / D;
-        float gl[16], kk[16];
-        float run = 0.f;
+    int it = blockIdx.x;
+    if (it >= total) return;
+    IntraRegs<D, F32IO> R;
+    int4 ent = table[it / H];
+    intra_load<D, F32IO>(R, q, k, v, z, beta, ent, it % H, H, lane, wave);
+    int4 ent_next = (it + stride < total) ? table[(it + stride) / H] : make_int4(0, 0, 0, 0);
+
+    for (; it < total; it += stride) {
+        const int chunk = it / H, h = it % H;
+        const int L = ent.z;
+        unsigned char *slab = slabs + ((size_t)h * max_chunks + chunk) * slab_stride;
+        const float ea = __expf(A[h]);
+        const int row = 16 * wave + ln;
+        const bool ok = row < L;
+
+        // ---- phase 1: gate, block-local cumulative log2-decay, row operands
+        for (int i = tid; i < 64 * 68; i += 256) (&s.a[0][0])[i] = 0.f;
+        if (lg == 0) s.beta[row] = R.beta;
+        f32x4 krv[KT], qrv[KT], vreg[KT];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = 16 * I + r;
-            const bool ok = row < L;
-            const size_t idx = ((size_t)(t0 + row) * H + h) * D + c;
-            const float zz = ok ? z[idx] : 0.f;
-            kk[r] = ok ? load_io<F32IO>(k, idx) : 0.f;
-            const float qq = ok ? load_io<F32IO>(q, idx) : 0.f;
-            run += ok ? gate_log2(ea, zz) : 0.f;
-            gl[r] = run;
-            const float rf = exp2f(run);
-            s.kr[row][c] = kk[r] * rf;
-            s.qr[row][c] = qq * rf;
+        for (int kt = 0; kt < KT; ++kt) {
+            const int c0 = 16 * kt + 4 * lg;
+            const f32x4 kk = quad_f32<F32IO>(R.k[kt]);
+            const f32x4 qq = quad_f32<F32IO>(R.q[kt]);
+            vreg[kt] = quad_f32<F32IO>(R.v[kt]);
+            f32x4 gl;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) gl[j] = ok ? gate_log2(ea, R.z[kt][j]) : 0.f;
+#pragma unroll
+            for (int d = 1; d < 16; d <<= 1) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float y = __shfl_up(gl[j], d, 16);
+                    if (ln >= d) gl[j] += y;
+                }
+            }
+            f32x4 bt, rf, kev;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bt[j] = __shfl(gl[j], 15, 16);
+                rf[j] = exp2f(gl[j]);
+                kev[j] = kk[j] * exp2f(bt[j] - gl[j]);
+            }
+            krv[kt] = kk * rf;
+            qrv[kt] = qq * rf;
+            *reinterpret_cast<f32x4 *>(&s.ke[row][c0]) = kev;
+            if (ln == 15) *reinterpret_cast<f32x4 *>(&s.bt[wave][c0]) = bt;
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s.ke[16 * I + r][c] = kk[r] * exp2f(run - gl[r]);
-        s.bt[I][c] = run;
-    }
-    __syncthreads();
-    for (int c = tid; c < D; c += 256) {
-        const float b0 = s.bt[0][c], b1 = s.bt[1][c], b2 = s.bt[2][c], b3 = s.bt[3][c];
-        s.pfx[0][c] = 1.f;
-        s.pfx[1][c] = exp2f(b0);
-        s.pfx[2][c] = exp2f(b0 + b1);
-        s.pfx[3][c] = exp2f(b0 + b1 + b2);
-        s.sfx[0][c] = exp2f(b1 + b2 + b3);
-        s.sfx[1][c] = exp2f(b2 + b3);
-        s.sfx[2][c] = exp2f(b3);
-        s.sfx[3][c] = 1.f;
-        s.dg[0][c] = exp2f(-b0);
-        s.dg[1][c] = exp2f(-b1);
-        s.dg[2][c] = exp2f(-b2);
-        s.dg[3][c] = exp2f(-b3);
-        s.off[0][c] = 1.f;            // (0,1)
-        s.off[1][c] = exp2f(b1);      // (0,2)
-        s.off[2][c] = exp2f(b1 + b2); // (0,3)
-        s.off[3][c] = 1.f;            // (1,2)
-        s.off[4][c] = exp2f(b2);      // (1,3)
-        s.off[5][c] = 1.f;            // (2,3)
-        reinterpret_cast<float *>(slab + SL::gamma)[c] = exp2f(b0 + b1 + b2 + b3);
-    }
-    __syncthreads();
-
-    // ---- phase 2: decayed Gram tiles A_kk (I, J) and A_qk^T, J <= I
-    // A_kk[r][i] = beta_r sum_c k_rc k_ic e^{G_rc - G_ic} is formed as
-    // (kr row of block I) x (ke row of block J) * factor, where the factor is
-    // exp2(-bt_J) on the diagonal block (the <= e^80 case) and the decay of the
-    // blocks strictly between J and I otherwise (<= 1).
-    for (int tile = wave; tile < 10; tile += 4) {
-        const int I = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
-        const int J = tile - (I * (I + 1)) / 2;
-        const float *fac = (I == J) ? s.dg[J] : s.off[off_index(J, I)];
-        f32x4 akk = zero4(), aqt = zero4();
         if constexpr (F32IO) {
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
-                const int c0 = 16 * kt + 4 * lg;
-                const f32x4 kr = lds_quad(s.kr, 16 * I + ln, c0);
-                const f32x4 qr = lds_quad(s.qr, 16 * I + ln, c0);
-                const f32x4 kc = lds_quad(s.ke, 16 * J + ln, c0) * *reinterpret_cast<const f32x4 *>(fac + c0);
-                akk = mma_f32_k16(kr, kc, akk);
-                aqt = mma_f32_k16(kc, qr, aqt);
+                *reinterpret_cast<f32x4 *>(&krf[row][16 * kt + 4 * lg]) = krv[kt];
+                *reinterpret_cast<f32x4 *>(&qrf[row][16 * kt + 4 * lg]) = qrv[kt];
             }
         } else {
 #pragma unroll
             for (int p = 0; p < KT / 2; ++p) {
-                const int c0 = 32 * p + 4 * lg, c1 = c0 + 16;
-                const f32x4 kr0 = lds_quad(s.kr, 16 * I + ln, c0), kr1 = lds_quad(s.kr, 16 * I + ln, c1);
-                const f32x4 qr0 = lds_quad(s.qr, 16 * I + ln, c0), qr1 = lds_quad(s.qr, 16 * I + ln, c1);
-                const f32x4 kc0 = lds_quad(s.ke, 16 * J + ln, c0) * *reinterpret_cast<const f32x4 *>(fac + c0);
-                const f32x4 kc1 = lds_quad(s.ke, 16 * J + ln, c1) * *reinterpret_cast<const f32x4 *>(fac + c1);
-                u32x4 krh, krl, kch, kcl, qrh, qrl;
-                quads_to_bf16_split(kr0, kr1, krh, krl);
-                quads_to_bf16_split(kc0, kc1, kch, kcl);
-                quads_to_bf16_split(qr0, qr1, qrh, qrl);
-                akk = mma3_bf16(krh, krl, kch, kcl, akk);
-                aqt = mma3_bf16(kch, kcl, qrh, qrl, aqt);
+                u32x4 hi, lo;
+                quads_to_bf16_split(krv[2 * p], krv[2 * p + 1], hi, lo);
+                *reinterpret_cast<u32x4 *>(s.krs + row * RB + (2 * p) * 64 + lg * 16) = hi;
+                *reinterpret_cast<u32x4 *>(s.krs + row * RB + (2 * p + 1) * 64 + lg * 16) = lo;
+                quads_to_bf16_split(qrv[2 * p], qrv[2 * p + 1], hi, lo);
+                *reinterpret_cast<u32x4 *>(s.qrs + row * RB + (2 * p) * 64 + lg * 16) = hi;
+                *reinterpret_cast<u32x4 *>(s.qrs + row * RB + (2 * p + 1) * 64 + lg * 16) = lo;
+            }
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                const u32x2 vv = R.v[kt];
+                const int c0 = 16 * kt + 4 * lg;
+                s.vt[c0 + 0][row] = (uint16_t)(vv[0] & 0xffffu);
+                s.vt[c0 + 1][row] = (uint16_t)(vv[0] >> 16);
+                s.vt[c0 + 2][row] = (uint16_t)(vv[1] & 0xffffu);
+                s.vt[c0 + 3][row] = (uint16_t)(vv[1] >> 16);
             }
         }
-        // A_kk: lane (n = i, g) holds rows r = 4g + j of the tile
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int rl = 4 * lg + j;
-            float x = akk[j] * s.beta[16 * I + rl];
-            if (I == J && ln >= rl) x = 0.f;
-            s.a[16 * I + rl][16 * J + ln] = x;
-        }
-        // A_qk^T: lane (n = r, g) holds i = 4g + j, i.e. the A_qk operand
-        // fragment of row tile I; keep i <= r on the diagonal tile.
-        f32x4 aq;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) aq[j] = (I == J && 4 * lg + j > ln) ? 0.f : aqt[j];
-        if constexpr (F32IO) {
-            *reinterpret_cast<f32x4 *>(slab + SL::aqk + ((size_t)(I * 4 + J) * 64 + lane) * 16) = aq;
-        } else {
-            uint32_t hb[4], lb[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) split_bf16(aq[j], hb[j], lb[j]);
-            const int qf = J >> 1, half = J & 1;
-            u32x2 hv = {pack2(hb[0], hb[1]), pack2(hb[2], hb[3])};
-            u32x2 lv = {pack2(lb[0], lb[1]), pack2(lb[2], lb[3])};
-            unsigned char *base = slab + SL::aqk + ((size_t)((I * 2 + qf) * 2) * 64 + lane) * 16 + half * 8;
-            *reinterpret_cast<u32x2 *>(base) = hv;
-            *reinterpret_cast<u32x2 *>(base + 64 * 16) = lv;
-            if (I == J && (I & 1) == 0) {  // the tile right of an even diagonal shares its fragment
-                *reinterpret_cast<u32x2 *>(base + 8) = u32x2{0u, 0u};
-                *reinterpret_cast<u32x2 *>(base + 64 * 16 + 8) = u32x2{0u, 0u};
+        // The raw inputs are consumed: fetch the next item (bf16 path; the
+        // fp32 path keeps V in registers until phase 3 and fetches there).
+        const int it_next = it + stride;
+        if constexpr (!F32IO) {
+            if (it_next < total) {
+                intra_load<D, F32IO>(R, q, k, v, z, beta, ent_next, it_next % H, H, lane, wave);
+                ent = ent_next;
+                if (it_next + stride < total) ent_next = table[(it_next + stride) / H];
             }
-        }
-    }
-
-    // Gamma*Q fragments (row tile I, key fragment f) and the transposed,
-    // end-of-chunk-decayed keys ((gamma_C/Gamma)*K)^T (key tile t, row fragment f).
-    for (int fr = wave; fr < 4 * SL::NKF; fr += 4) {
-        const int I = fr / SL::NKF, f = fr % SL::NKF;
-        unsigned char *dst = slab + SL::qg + ((size_t)fr * SL::SPL * 64 + lane) * 16;
-        if constexpr (F32IO) {
-            const int c0 = 16 * f + 4 * lg;
-            *reinterpret_cast<f32x4 *>(dst) =
-                lds_quad(s.qr, 16 * I + ln, c0) * *reinterpret_cast<const f32x4 *>(&s.pfx[I][c0]);
-        } else {
-            const int c0 = 32 * f + 4 * lg, c1 = c0 + 16;
-            store_split(dst,
-                        lds_quad(s.qr, 16 * I + ln, c0) * *reinterpret_cast<const f32x4 *>(&s.pfx[I][c0]),
-                        lds_quad(s.qr, 16 * I + ln, c1) * *reinterpret_cast<const f32x4 *>(&s.pfx[I][c1]));
-        }
-    }
-    for (int fr = wave; fr < KT * SL::NCF; fr += 4) {
-        const int t = fr / SL::NCF, f = fr % SL::NCF;
-        const int c = 16 * t + ln;
-        unsigned char *dst = slab + SL::kdT + ((size_t)fr * SL::SPL * 64 + lane) * 16;
-        if constexpr (F32IO) {
-            const int J = f;
-            *reinterpret_cast<f32x4 *>(dst) = lds_col4(s.ke, 16 * J + 4 * lg, c) * s.sfx[J][c];
-        } else {
-            const int J0 = 2 * f, J1 = 2 * f + 1;
-            store_split(dst, lds_col4(s.ke, 16 * J0 + 4 * lg, c) * s.sfx[J0][c],
-                        lds_col4(s.ke, 16 * J1 + 4 * lg, c) * s.sfx[J1][c]);
-        }
-    }
-    __syncthreads();
-
-    // ---- phase 3: V into LDS (over q's rows) and the diagonal 16x16 inverses
-    for (int i = tid; i < 64 * D; i += 256) {
-        const int row = i / D, c = i % D;
-        s.qr[row][c] = row < L ? load_io<F32IO>(v, ((size_t)(t0 + row) * H + h) * D + c) : 0.f;
-    }
-    if (lane < 16) {
-        // forward substitution for column `lane` of (I + A_ww)^{-1}
-        const int b = 16 * wave;
-        float col[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float x = (r == lane) ? 1.f : 0.f;
-#pragma unroll
-            for (int i = 0; i < r; ++i) x -= s.a[b + r][b + i] * col[i];
-            col[r] = x;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s.tm[b + r][b + lane] = col[r];
-    }
-    __syncthreads();
-
-    // ---- phase 4: off-diagonal blocks, T_IJ = -T_II sum_{J<=m<I} A_Im T_mJ (fp32 MFMA)
-    for (int I = 1; I < 4; ++I) {
-        if (wave < I) {
-            const int J = wave;
-            f32x4 x = zero4();
-            for (int m = J; m < I; ++m)
-                x = mma_f32_k16(lds_quad(s.a, 16 * I + ln, 16 * m + 4 * lg),
-                                lds_col4(s.tm, 16 * m + 4 * lg, 16 * J + ln), x);
-            f32x4 y = mma_f32_k16(lds_quad(s.tm, 16 * I + ln, 16 * I + 4 * lg), x, zero4());
-#pragma unroll
-            for (int j = 0; j < 4; ++j) s.tm[16 * I + 4 * lg + j][16 * J + ln] = -y[j];
         }
         __syncthreads();
-    }
 
-    // ---- phase 5: -W fragments (from W^T tiles) and U tiles.  M = T Diag(beta).
-    // W^T tile (t, I) = sum_J (Gamma*K)^T_{tJ} M^T_{JI}: the accumulator lane
-    // (n = r, g) holds W[16I + r][16t + 4g + j], which is the A-operand
-    // fragment of -W in the state-propagation product.
-    for (int I = 0; I < 4; ++I) {
-        const int nJ = I + 1;
-        // M row quads of row tile I (B operand of W^T, A operand of U)
-        for (int tp = wave; tp < SL::NKF; tp += 4) {
+        for (int c = tid; c < D; c += 256) {
+            const float b0 = s.bt[0][c], b1 = s.bt[1][c], b2 = s.bt[2][c], b3 = s.bt[3][c];
+            s.pfx[0][c] = 1.f;
+            s.pfx[1][c] = exp2f(b0);
+            s.pfx[2][c] = exp2f(b0 + b1);
+            s.pfx[3][c] = exp2f(b0 + b1 + b2);
+            s.sfx[0][c] = exp2f(b1 + b2 + b3);
+            s.sfx[1][c] = exp2f(b2 + b3);
+            s.sfx[2][c] = exp2f(b3);
+            s.sfx[3][c] = 1.f;
+            s.dg[0][c] = exp2f(-b0);
+            s.dg[1][c] = exp2f(-b1);
+            s.dg[2][c] = exp2f(-b2);
+            s.dg[3][c] = exp2f(-b3);
+            s.off[0][c] = 1.f;             // (0,1)
+            s.off[1][c] = exp2f(b1);       // (0,2)
+            s.off[2][c] = exp2f(b1 + b2);  // (0,3)
+            s.off[3][c] = 1.f;             // (1,2)
+            s.off[4][c] = exp2f(b2);       // (1,3)
+            s.off[5][c] = 1.f;             // (2,3)
+            reinterpret_cast<float *>(slab + SL::gamma)[c] = exp2f(b0 + b1 + b2 + b3);
+        }
+        __syncthreads();
+
+        // ---- phase 2: decayed Gram tiles A_kk (I, J) and A_qk^T, J <= I.
+        // A_kk[r][i] = beta_r sum_c k_rc k_ic e^{G_rc - G_ic} is (row operand of
+        // block I) x (ke of block J) x factor: exp2(-bt_J) on the diagonal block
+        // (the <= e^80 case), the decay of the blocks strictly between J and I
+        // otherwise (<= 1).
+        for (int tile = wave; tile < 10; tile += 4) {
+            const int I = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
+            const int J = tile - (I * (I + 1)) / 2;
+            const float *fac = (I == J) ? s.dg[J] : s.off[off_index(J, I)];
+            f32x4 akk = zero4(), aqt = zero4();
             if constexpr (F32IO) {
-                const int t = tp;
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) {
+                    const int c0 = 16 * kt + 4 * lg;
+                    const f32x4 kc = lds_quad(s.ke, 16 * J + ln, c0) * ld4(fac + c0);
+                    akk = mma_f32_k16(lds_quad(krf, 16 * I + ln, c0), kc, akk);
+                    aqt = mma_f32_k16(kc, lds_quad(qrf, 16 * I + ln, c0), aqt);
+                }
+            } else {
+                const unsigned char *kr_row = s.krs + (16 * I + ln) * RB + lg * 16;
+                const unsigned char *qr_row = s.qrs + (16 * I + ln) * RB + lg * 16;
+#pragma unroll
+                for (int p = 0; p < KT / 2; ++p) {
+                    const int c0 = 32 * p + 4 * lg, c1 = c0 + 16;
+                    const u32x4 krh = *reinterpret_cast<const u32x4 *>(kr_row + (2 * p) * 64);
+                    const u32x4 krl = *reinterpret_cast<const u32x4 *>(kr_row + (2 * p + 1) * 64);
+                    const u32x4 qrh = *reinterpret_cast<const u32x4 *>(qr_row + (2 * p) * 64);
+                    const u32x4 qrl = *reinterpret_cast<const u32x4 *>(qr_row + (2 * p + 1) * 64);
+                    u32x4 kch, kcl;
+                    quads_to_bf16_split(lds_quad(s.ke, 16 * J + ln, c0) * ld4(fac + c0),
+                                        lds_quad(s.ke, 16 * J + ln, c1) * ld4(fac + c1), kch, kcl);
+                    akk = mma3_bf16(krh, krl, kch, kcl, akk);
+                    aqt = mma3_bf16(kch, kcl, qrh, qrl, aqt);
+                }
+            }
+            // A_kk: lane (n = i, g) holds rows r = 4g + j of the tile
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int rl = 4 * lg + j;
+                float x = akk[j] * s.beta[16 * I + rl];
+                if (I == J && ln >= rl) x = 0.f;
+                s.a[16 * I + rl][16 * J + ln] = x;
+            }
+            // A_qk^T: lane (n = r, g) holds i = 4g + j, i.e. the A_qk operand
+            // fragment of row tile I; keep i <= r on the diagonal tile.
+            f32x4 aq;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) aq[j] = (I == J && 4 * lg + j > ln) ? 0.f : aqt[j];
+            if constexpr (F32IO) {
+                *reinterpret_cast<f32x4 *>(slab + SL::aqk + ((size_t)(I * 4 + J) * 64 + lane) * 16) = aq;
+            } else {
+                const u32x2 hv = {f32x2_to_bf16x2(aq[0], aq[1]), f32x2_to_bf16x2(aq[2], aq[3])};
+                f32x4 hq;
+                hq = f32x4{bf16_lo_half(hv[0]), bf16_hi_half(hv[0]), bf16_lo_half(hv[1]), bf16_hi_half(hv[1])};
+                const f32x4 r4 = aq - hq;
+                const u32x2 lv = {f32x2_to_bf16x2(r4[0], r4[1]), f32x2_to_bf16x2(r4[2], r4[3])};
+                const int qf = J >> 1, half = J & 1;
+                unsigned char *base = slab + SL::aqk + ((size_t)((I * 2 + qf) * 2) * 64 + lane) * 16 + half * 8;
+                *reinterpret_cast<u32x2 *>(base) = hv;
+                *reinterpret_cast<u32x2 *>(base + 64 * 16) = lv;
+                if (I == J && (I & 1) == 0) {  // the tile right of an even diagonal shares its fragment
+                    *reinterpret_cast<u32x2 *>(base + 8) = u32x2{0u, 0u};
+                    *reinterpret_cast<u32x2 *>(base + 64 * 16 + 8) = u32x2{0u, 0u};
+                }
+            }
+        }
+
+        // Gamma*Q fragments (row tile I, key fragment f) and the transposed,
+        // end-of-chunk-decayed keys ((gamma_C/Gamma)*K)^T (key tile t, row fragment f).
+        for (int fr = wave; fr < 4 * SL::NKF; fr += 4) {
+            const int I = fr / SL::NKF, f = fr % SL::NKF;
+            unsigned char *dst = slab + SL::qg + ((size_t)fr * SL::SPL * 64 + lane) * 16;
+            if constexpr (F32IO) {
+                const int c0 = 16 * f + 4 * lg;
+                *reinterpret_cast<f32x4 *>(dst) = lds_quad(qrf, 16 * I + ln, c0) * ld4(&s.pfx[I][c0]);
+            } else {
+                const unsigned char *qr_row = s.qrs + (16 * I + ln) * RB + lg * 16;
+                f32x4 h0, h1, l0, l1;
+                bf16_to_quads(*reinterpret_cast<const u32x4 *>(qr_row + (2 * f) * 64), h0, h1);
+                bf16_to_quads(*reinterpret_cast<const u32x4 *>(qr_row + (2 * f + 1) * 64), l0, l1);
+                const int c0 = 32 * f + 4 * lg, c1 = c0 + 16;
+                store_split(dst, (h0 + l0) * ld4(&s.pfx[I][c0]), (h1 + l1) * ld4(&s.pfx[I][c1]));
+            }
+        }
+        for (int fr = wave; fr < KT * SL::NCF; fr += 4) {
+            const int t = fr / SL::NCF, f = fr % SL::NCF;
+            const int c = 16 * t + ln;
+            unsigned char *dst = slab + SL::kdT + ((size_t)fr * SL::SPL * 64 + lane) * 16;
+            if constexpr (F32IO) {
+                const int J = f;
+                *reinterpret_cast<f32x4 *>(dst) = lds_col4(s.ke, 16 * J + 4 * lg, c) * s.sfx[J][c];
+            } else {
+                const int J0 = 2 * f, J1 = 2 * f + 1;
+                store_split(dst, lds_col4(s.ke, 16 * J0 + 4 * lg, c) * s.sfx[J0][c],
+                            lds_col4(s.ke, 16 * J1 + 4 * lg, c) * s.sfx[J1][c]);
+            }
+        }
+        __syncthreads();
+
+        // ---- phase 3: (Gamma*K)^T (bf16) or V (fp32 path) into the freed
+        // arrays, and the diagonal 16x16 inverses, in place.
+        if constexpr (F32IO) {
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+                *reinterpret_cast<f32x4 *>(&s.ke[row][16 * kt + 4 * lg]) = vreg[kt];
+            if (it_next < total) {
+                intra_load<D, F32IO>(R, q, k, v, z, beta, ent_next, it_next % H, H, lane, wave);
+                ent = ent_next;
+                if (it_next + stride < total) ent_next = table[(it_next + stride) / H];
+            }
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                const int c0 = 16 * kt + 4 * lg;
+                const f32x4 gk = krv[kt] * ld4(&s.pfx[wave][c0]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    uint32_t hb, lb;
+                    split_bf16(gk[j], hb, lb);
+                    gkh[c0 + j][row] = (uint16_t)hb;
+                    gkl[c0 + j][row] = (uint16_t)lb;
+                }
+            }
+        }
+        if (lane < 16) {
+            // forward substitution for column `lane` of (I + A_ww)^{-1}
+            const int b = 16 * wave;
+            float col[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float x = (r == lane) ? 1.f : 0.f;
+#pragma unroll
+                for (int i = 0; i < r; ++i) x -= s.a[b + r][b + i] * col[i];
+                col[r] = x;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s.a[b + r][b + lane] = col[r];
+        }
+        __syncthreads();
+
+        // ---- phase 4: off-diagonal blocks, T_IJ = -T_II sum_{J<=m<I} A_Im T_mJ
+        // (fp32 MFMA), written over A_IJ once every wave has read row block I.
+        for (int I = 1; I < 4; ++I) {
+            f32x4 y = zero4();
+            if (wave < I) {
+                const int J = wave;
+                f32x4 x = zero4();
+                for (int m = J; m < I; ++m)
+                    x = mma_f32_k16(lds_quad(s.a, 16 * I + ln, 16 * m + 4 * lg),
+                                    lds_col4(s.a, 16 * m + 4 * lg, 16 * J + ln), x);
+                y = mma_f32_k16(lds_quad(s.a, 16 * I + ln, 16 * I + 4 * lg), x, zero4());
+            }
+            __syncthreads();
+            if (wave < I) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s.a[16 * I + 4 * lg + j][16 * wave + ln] = -y[j];
+            }
+            __syncthreads();
+        }
+
+        // ---- phase 5: -W fragments (from W^T tiles) and U tiles; M = T Diag(beta).
+        // W^T tile (t, I) = sum_J (Gamma*K)^T_{tJ} M^T_{JI}: the accumulator
+        // lane (n = r, g) holds W[16I + r][16t + 4g + j], the A-operand
+        // fragment of -W in the state-propagation product.
+        for (int I = 0; I < 4; ++I) {
+            const int nJ = I + 1;
+            for (int tp = wave; tp < SL::NKF; tp += 4) {
+                if constexpr (F32IO) {
+                    const int t = tp;
+                    f32x4 acc = zero4();
+                    for (int J = 0; J < nJ; ++J) {
+                        const int cJ = 16 * J + 4 * lg;
+                        const f32x4 mq = lds_quad(s.a, 16 * I + ln, cJ) * ld4(&s.beta[cJ]);
+                        const f32x4 gk = lds_col4(krf, 16 * J + 4 * lg, 16 * t + ln) * s.pfx[J][16 * t + ln];
+                        acc = mma_f32_k16(gk, mq, acc);
+                    }
+                    *reinterpret_cast<f32x4 *>(slab + SL::negW + ((size_t)(I * SL::NKF + tp) * 64 + lane) * 16) = -acc;
+                } else {
+                    const int ca = 32 * tp + ln, cb = ca + 16;
+                    f32x4 acc0 = zero4(), acc1 = zero4();
+                    for (int pj = 0; pj < (nJ + 1) / 2; ++pj) {
+                        const int cJ0 = 32 * pj + 4 * lg, cJ1 = cJ0 + 16;
+                        u32x4 mh, ml;
+                        quads_to_bf16_split(lds_quad(s.a, 16 * I + ln, cJ0) * ld4(&s.beta[cJ0]),
+                                            lds_quad(s.a, 16 * I + ln, cJ1) * ld4(&s.beta[cJ1]), mh, ml);
+                        const u32x4 gah = cat2(lds_bf16x4(gkh, ca, cJ0), lds_bf16x4(gkh, ca, cJ1));
+                        const u32x4 gal = cat2(lds_bf16x4(gkl, ca, cJ0), lds_bf16x4(gkl, ca, cJ1));
+                        const u32x4 gbh = cat2(lds_bf16x4(gkh, cb, cJ0), lds_bf16x4(gkh, cb, cJ1));
+                        const u32x4 gbl = cat2(lds_bf16x4(gkl, cb, cJ0), lds_bf16x4(gkl, cb, cJ1));
+                        acc0 = mma3_bf16(gah, gal, mh, ml, acc0);
+                        acc1 = mma3_bf16(gbh, gbl, mh, ml, acc1);
+                    }
+                    store_split(slab + SL::negW + ((size_t)(I * SL::NKF + tp) * 2 * 64 + lane) * 16, -acc0, -acc1);
+                }
+            }
+            // U tile (I, w) = sum_J M_{IJ} V_{Jw}, in the accumulator layout the
+            // state-propagation kernel starts V' from.
+            for (int w = wave; w < KT; w += 4) {
                 f32x4 acc = zero4();
-                for (int J = 0; J < nJ; ++J) {
-                    const int cJ = 16 * J + 4 * lg;
-                    const f32x4 mq = lds_quad(s.tm, 16 * I + ln, cJ) * *reinterpret_cast<const f32x4 *>(&s.beta[cJ]);
-                    const f32x4 gk = lds_col4(s.kr, 16 * J + 4 * lg, 16 * t + ln) * s.pfx[J][16 * t + ln];
-                    acc = mma_f32_k16(gk, mq, acc);
+                if constexpr (F32IO) {
+                    for (int J = 0; J < nJ; ++J) {
+                        const int cJ = 16 * J + 4 * lg;
+                        const f32x4 mq = lds_quad(s.a, 16 * I + ln, cJ) * ld4(&s.beta[cJ]);
+                        acc = mma_f32_k16(mq, lds_col4(s.ke, 16 * J + 4 * lg, 16 * w + ln), acc);
+                    }
+                } else {
+                    for (int pj = 0; pj < (nJ + 1) / 2; ++pj) {
+                        const int cJ0 = 32 * pj + 4 * lg, cJ1 = cJ0 + 16;
+                        u32x4 mh, ml;
+                        quads_to_bf16_split(lds_quad(s.a, 16 * I + ln, cJ0) * ld4(&s.beta[cJ0]),
+                                            lds_quad(s.a, 16 * I + ln, cJ1) * ld4(&s.beta[cJ1]), mh, ml);
+                        const u32x4 vb = cat2(lds_bf16x4(s.vt, 16 * w + ln, cJ0),
+                                              lds_bf16x4(s.vt, 16 * w + ln, cJ1));
+                        acc = mma_bf16_k32(mh, vb, acc);
+                        acc = mma_bf16_k32(ml, vb, acc);
+                    }
                 }
-                *reinterpret_cast<f32x4 *>(slab + SL::negW + ((size_t)(I * SL::NKF + tp) * 64 + lane) * 16) = -acc;
-            } else {
-                const int t0_ = 2 * tp, t1_ = 2 * tp + 1;
-                f32x4 acc0 = zero4(), acc1 = zero4();
-                for (int pj = 0; pj < (nJ + 1) / 2; ++pj) {
-                    const int J0 = 2 * pj, J1 = 2 * pj + 1;
-                    const int cJ0 = 16 * J0 + 4 * lg, cJ1 = 16 * J1 + 4 * lg;
-                    const f32x4 m0 = lds_quad(s.tm, 16 * I + ln, cJ0) * *reinterpret_cast<const f32x4 *>(&s.beta[cJ0]);
-                    const f32x4 m1 = lds_quad(s.tm, 16 * I + ln, cJ1) * *reinterpret_cast<const f32x4 *>(&s.beta[cJ1]);
-                    u32x4 mh, ml, gah, gal, gbh, gbl;
-                    quads_to_bf16_split(m0, m1, mh, ml);
-                    const int ca = 16 * t0_ + ln, cb = 16 * t1_ + ln;
-                    quads_to_bf16_split(lds_col4(s.kr, 16 * J0 + 4 * lg, ca) * s.pfx[J0][ca],
-                                        lds_col4(s.kr, 16 * J1 + 4 * lg, ca) * s.pfx[J1][ca], gah, gal);
-                    quads_to_bf16_split(lds_col4(s.kr, 16 * J0 + 4 * lg, cb) * s.pfx[J0][cb],
-                                        lds_col4(s.kr, 16 * J1 + 4 * lg, cb) * s.pfx[J1][cb], gbh, gbl);
-                    acc0 = mma3_bf16(gah, gal, mh, ml, acc0);
-                    acc1 = mma3_bf16(gbh, gbl, mh, ml, acc1);
-                }
-                store_split(slab + SL::negW + ((size_t)(I * SL::NKF + tp) * 2 * 64 + lane) * 16, -acc0, -acc1);
+                *reinterpret_cast<f32x4 *>(slab + SL::u + ((size_t)(I * KT + w) * 64 + lane) * 16) = acc;
             }
         }
-        // U tile (I, w) = sum_J M_{IJ} V_{Jw}; accumulator layout is what the
-        // state-propagation kernel starts V' from.
-        for (int w = wave; w < KT; w += 4) {
-            f32x4 acc = zero4();
-            if constexpr (F32IO) {
-                for (int J = 0; J < nJ; ++J) {
-                    const int cJ = 16 * J + 4 * lg;
-                    const f32x4 mq = lds_quad(s.tm, 16 * I + ln, cJ) * *reinterpret_cast<const f32x4 *>(&s.beta[cJ]);
-                    acc = mma_f32_k16(mq, lds_col4(s.qr, 16 * J + 4 * lg, 16 * w + ln), acc);
-                }
-            } else {
-                for (int pj = 0; pj < (nJ + 1) / 2; ++pj) {
-                    const int J0 = 2 * pj, J1 = 2 * pj + 1;
-                    const int cJ0 = 16 * J0 + 4 * lg, cJ1 = 16 * J1 + 4 * lg;
-                    const f32x4 m0 = lds_quad(s.tm, 16 * I + ln, cJ0) * *reinterpret_cast<const f32x4 *>(&s.beta[cJ0]);
-                    const f32x4 m1 = lds_quad(s.tm, 16 * I + ln, cJ1) * *reinterpret_cast<const f32x4 *>(&s.beta[cJ1]);
-                    u32x4 mh, ml;
-                    quads_to_bf16_split(m0, m1, mh, ml);
-                    const u32x4 vb = quads_to_bf16(lds_col4(s.qr, 16 * J0 + 4 * lg, 16 * w + ln),
-                                                   lds_col4(s.qr, 16 * J1 + 4 * lg, 16 * w + ln));
-                    acc = mma_bf16_k32(mh, vb, acc);
-                    acc = mma_bf16_k32(ml, vb, acc);
-                }
-            }
-            *reinterpret_cast<f32x4 *>(slab + SL::u + ((size_t)(I * KT + w) * 64 + lane) * 16) = acc;
-        }
+        __syncthreads();
     }
 }
 
@@ -459,15 +612,35 @@ __global__ void __launch_bounds__(256) intra_kernel(
 //   S  = Diag(gamma_C) S + ((gamma_C/Gamma)*K)^T V'
 // Every bf16 operand (stored fragments and the S, V' accumulators) enters
 // the MFMAs split into hi + lo parts; each product is hi*hi + hi*lo + lo*hi.
+// The operands every wave shares (-W, Gamma*Q, K~^T, A_qk, gamma) sit in LDS;
+// the next chunk's copy is loaded into registers while this chunk computes.
 // ---------------------------------------------------------------------------
+template <int D, bool F32IO>
+struct InterShape {
+    using SL = Slab<D, F32IO>;
+    static constexpr int KT = D / 16;
+    static constexpr int WPG = KT < 4 ? KT : 4;          // waves per workgroup
+    static constexpr int NT = 64 * WPG;
+    static constexpr int SH = (int)(SL::u / 16);          // shared 16-byte vectors before U
+    static constexpr int NPF = SH / NT;
+    static constexpr int NG = D / 4;                      // gamma as 16-byte vectors
+    static constexpr size_t lds_bytes = (size_t)(SH + NG) * 16;
+    static_assert(NPF * NT == SH, "shared slab region must split evenly over the threads");
+    static_assert(NG <= NT, "gamma vectors");
+};
+
 template <int D, bool F32IO>
 __global__ void __launch_bounds__(256) inter_kernel(
     const float *__restrict__ h0, const int32_t *__restrict__ meta, const int4 *__restrict__ table,
     int N, int H, int max_chunks, const unsigned char *__restrict__ slabs, size_t slab_stride,
     void *__restrict__ o, float *__restrict__ hT, int groups) {
     using SL = Slab<D, F32IO>;
+    using SHP = InterShape<D, F32IO>;
     constexpr int KT = D / 16;
-    constexpr int WPG = KT < 4 ? KT : 4;  // waves per workgroup
+    constexpr int WPG = SHP::WPG, NT = SHP::NT, SH = SHP::SH, NPF = SHP::NPF, NG = SHP::NG;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    u32x4 *sh = reinterpret_cast<u32x4 *>(lds_raw);
+
     // blockIdx -> (pair, column group) with every group of a pair on the same XCD
     const int b = blockIdx.x;
     const int xcd = b & 7, rest = b >> 3;
@@ -475,7 +648,8 @@ __global__ void __launch_bounds__(256) inter_kernel(
     const int pair = (rest / groups) * 8 + xcd;
     if (pair >= N * H) return;
     const int n = pair / H, h = pair % H;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
     const int ln = lane & 15, lg = lane >> 4;
     const int vt = cg * WPG + wave;
     const int col = 16 * vt + ln;
@@ -487,55 +661,78 @@ __global__ void __launch_bounds__(256) inter_kernel(
         S[t] = h0 ? *reinterpret_cast<const f32x4 *>(h0 + srow + 16 * t + 4 * lg) : zero4();
 
     const int c_begin = meta[n], c_end = meta[n + 1];
+    u32x4 pf[NPF], pg = u32x4{0u, 0u, 0u, 0u};
+    f32x4 u[4], un[4];
+    auto slab_of = [&](int c) {
+        return slabs + ((size_t)h * max_chunks + c) * slab_stride;
+    };
+    auto issue = [&](int c) {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(slab_of(c));
+#pragma unroll
+        for (int i = 0; i < NPF; ++i) pf[i] = src[tid + i * NT];
+        if (tid < NG) pg = src[SL::gamma / 16 + tid];
+        const f32x4 *us = reinterpret_cast<const f32x4 *>(slab_of(c) + SL::u);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) un[I] = us[(I * KT + vt) * 64 + lane];
+    };
+    auto commit = [&]() {
+#pragma unroll
+        for (int i = 0; i < NPF; ++i) sh[tid + i * NT] = pf[i];
+        if (tid < NG) sh[SH + tid] = pg;
+#pragma unroll
+        for (int I = 0; I < 4; ++I) u[I] = un[I];
+    };
+    // fragment idx of the region at byte offset `off`, this lane's 16 bytes
+    auto frag = [&](size_t off, int idx) -> const u32x4 & { return sh[off / 16 + idx * 64 + lane]; };
+    auto fragf = [&](size_t off, int idx) -> f32x4 { return __builtin_bit_cast(f32x4, frag(off, idx)); };
+
+    if (c_begin < c_end) {
+        issue(c_begin);
+        commit();
+    }
+    __syncthreads();
     for (int c = c_begin; c < c_end; ++c) {
         const int4 ent = table[c];
         const int t0 = ent.y, L = ent.z;
-        const unsigned char *slab = slabs + ((size_t)h * max_chunks + c) * slab_stride;
-        auto frag = [&](size_t off, int idx) -> const void * {
-            return slab + off + ((size_t)idx * 64 + lane) * 16;
-        };
+        if (c + 1 < c_end) issue(c + 1);
+
         f32x4 vp[4], acc_o[4];
+        const f32x4 *gam = reinterpret_cast<const f32x4 *>(&sh[SH]);
         if constexpr (F32IO) {
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
-                vp[I] = *reinterpret_cast<const f32x4 *>(frag(SL::u, I * KT + vt));
+                vp[I] = u[I];
                 acc_o[I] = zero4();
 #pragma unroll
                 for (int t = 0; t < KT; ++t) {
-                    vp[I] = mma_f32_k16(*reinterpret_cast<const f32x4 *>(frag(SL::negW, I * KT + t)), S[t], vp[I]);
-                    acc_o[I] = mma_f32_k16(*reinterpret_cast<const f32x4 *>(frag(SL::qg, I * KT + t)), S[t], acc_o[I]);
+                    vp[I] = mma_f32_k16(fragf(SL::negW, I * KT + t), S[t], vp[I]);
+                    acc_o[I] = mma_f32_k16(fragf(SL::qg, I * KT + t), S[t], acc_o[I]);
                 }
             }
 #pragma unroll
             for (int I = 0; I < 4; ++I)
 #pragma unroll
                 for (int J = 0; J <= I; ++J)
-                    acc_o[I] = mma_f32_k16(*reinterpret_cast<const f32x4 *>(frag(SL::aqk, I * 4 + J)), vp[J], acc_o[I]);
-            const f32x4 *gam = reinterpret_cast<const f32x4 *>(slab + SL::gamma);
+                    acc_o[I] = mma_f32_k16(fragf(SL::aqk, I * 4 + J), vp[J], acc_o[I]);
 #pragma unroll
             for (int t = 0; t < KT; ++t) {
                 S[t] = S[t] * gam[4 * t + lg];
 #pragma unroll
-                for (int J = 0; J < 4; ++J)
-                    S[t] = mma_f32_k16(*reinterpret_cast<const f32x4 *>(frag(SL::kdT, t * 4 + J)), vp[J], S[t]);
+                for (int J = 0; J < 4; ++J) S[t] = mma_f32_k16(fragf(SL::kdT, t * 4 + J), vp[J], S[t]);
             }
         } else {
-            u32x4 sh[KT / 2], sl[KT / 2];
+            u32x4 shi[KT / 2], slo[KT / 2];
 #pragma unroll
-            for (int p = 0; p < KT / 2; ++p) quads_to_bf16_split(S[2 * p], S[2 * p + 1], sh[p], sl[p]);
+            for (int p = 0; p < KT / 2; ++p) quads_to_bf16_split(S[2 * p], S[2 * p + 1], shi[p], slo[p]);
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
-                vp[I] = *reinterpret_cast<const f32x4 *>(frag(SL::u, I * KT + vt));
+                vp[I] = u[I];
                 acc_o[I] = zero4();
 #pragma unroll
                 for (int p = 0; p < KT / 2; ++p) {
                     const int fi = (I * (KT / 2) + p) * 2;
-                    const u32x4 wh = *reinterpret_cast<const u32x4 *>(frag(SL::negW, fi));
-                    const u32x4 wl = *reinterpret_cast<const u32x4 *>(frag(SL::negW, fi + 1));
-                    const u32x4 gh = *reinterpret_cast<const u32x4 *>(frag(SL::qg, fi));
-                    const u32x4 gl = *reinterpret_cast<const u32x4 *>(frag(SL::qg, fi + 1));
-                    vp[I] = mma3_bf16(wh, wl, sh[p], sl[p], vp[I]);
-                    acc_o[I] = mma3_bf16(gh, gl, sh[p], sl[p], acc_o[I]);
+                    vp[I] = mma3_bf16(frag(SL::negW, fi), frag(SL::negW, fi + 1), shi[p], slo[p], vp[I]);
+                    acc_o[I] = mma3_bf16(frag(SL::qg, fi), frag(SL::qg, fi + 1), shi[p], slo[p], acc_o[I]);
                 }
             }
             u32x4 vh[2], vl[2];
@@ -544,21 +741,16 @@ __global__ void __launch_bounds__(256) inter_kernel(
 #pragma unroll
             for (int I = 0; I < 4; ++I)
 #pragma unroll
-                for (int qf = 0; qf <= I / 2; ++qf) {
-                    const u32x4 ah = *reinterpret_cast<const u32x4 *>(frag(SL::aqk, (I * 2 + qf) * 2));
-                    const u32x4 al = *reinterpret_cast<const u32x4 *>(frag(SL::aqk, (I * 2 + qf) * 2 + 1));
-                    acc_o[I] = mma3_bf16(ah, al, vh[qf], vl[qf], acc_o[I]);
-                }
-            const f32x4 *gam = reinterpret_cast<const f32x4 *>(slab + SL::gamma);
+                for (int qf = 0; qf <= I / 2; ++qf)
+                    acc_o[I] = mma3_bf16(frag(SL::aqk, (I * 2 + qf) * 2), frag(SL::aqk, (I * 2 + qf) * 2 + 1),
+                                         vh[qf], vl[qf], acc_o[I]);
 #pragma unroll
             for (int t = 0; t < KT; ++t) {
                 S[t] = S[t] * gam[4 * t + lg];
 #pragma unroll
-                for (int qf = 0; qf < 2; ++qf) {
-                    const u32x4 ah = *reinterpret_cast<const u32x4 *>(frag(SL::kdT, (t * 2 + qf) * 2));
-                    const u32x4 al = *reinterpret_cast<const u32x4 *>(frag(SL::kdT, (t * 2 + qf) * 2 + 1));
-                    S[t] = mma3_bf16(ah, al, vh[qf], vl[qf], S[t]);
-                }
+                for (int qf = 0; qf < 2; ++qf)
+                    S[t] = mma3_bf16(frag(SL::kdT, (t * 2 + qf) * 2), frag(SL::kdT, (t * 2 + qf) * 2 + 1),
+                                     vh[qf], vl[qf], S[t]);
             }
         }
 #pragma unroll
@@ -568,6 +760,9 @@ __global__ void __launch_bounds__(256) inter_kernel(
                 const int r = 16 * I + 4 * lg + j;
                 if (r < L) store_io<F32IO>(o, ((size_t)(t0 + r) * H + h) * D + col, acc_o[I][j]);
             }
+        __syncthreads();
+        if (c + 1 < c_end) commit();
+        __syncthreads();
     }
     if (hT) {
 #pragma unroll
@@ -576,6 +771,25 @@ __global__ void __launch_bounds__(256) inter_kernel(
 }
 
 // ---------------------------------------------------------------------------
+static int device_cus() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cus = n;
+        else
+            cus = 256;
+    }
+    return cus;
+}
+
+template <typename K>
+static bool set_lds(K kernel, size_t bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) == hipSuccess;
+}
+
 template <int D, bool F32IO>
 static int launch_prefill_t(const PrefillArgs &a) {
     const PrefillPlan &p = a.plan;
@@ -587,30 +801,26 @@ static int launch_prefill_t(const PrefillArgs &a) {
                        p.max_chunks, meta, table);
     if (hipGetLastError() != hipSuccess) return -1;
 
-    if (p.max_chunks > 0) {
+    const long long items = (long long)p.max_chunks * a.H;
+    if (items > 0) {
         const size_t lds = sizeof(IntraLds<D>);
-        static bool attr_set = false;
-        if (!attr_set) {
-            if (hipFuncSetAttribute(reinterpret_cast<const void *>(&intra_kernel<D, F32IO>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-                return -1;
-            attr_set = true;
-        }
-        hipLaunchKernelGGL((intra_kernel<D, F32IO>), dim3(p.max_chunks, a.H), dim3(256), lds, a.stream,
-                           a.q, a.k, a.v, a.z, a.A, a.beta, meta, table, a.N, a.H, p.max_chunks, slabs,
+        if (!set_lds(&intra_kernel<D, F32IO>, lds)) return -1;
+        const int grid = (int)std::min<long long>(items, (long long)device_cus());
+        hipLaunchKernelGGL((intra_kernel<D, F32IO>), dim3(grid), dim3(256), lds, a.stream, a.q, a.k,
+                           a.v, a.z, a.A, a.beta, meta, table, a.N, a.H, p.max_chunks, slabs,
                            p.slab_bytes);
         if (hipGetLastError() != hipSuccess) return -1;
     }
 
-    constexpr int KT = D / 16;
-    constexpr int WPG = KT < 4 ? KT : 4;
-    const int groups = KT / WPG;
+    using SHP = InterShape<D, F32IO>;
+    const int groups = SHP::KT / SHP::WPG;
     const int pairs = a.N * a.H;
     if (pairs > 0) {
+        if (!set_lds(&inter_kernel<D, F32IO>, SHP::lds_bytes)) return -1;
         const int pair_blocks = (pairs + 7) / 8 * 8;
-        hipLaunchKernelGGL((inter_kernel<D, F32IO>), dim3(pair_blocks * groups), dim3(64 * WPG), 0,
-                           a.stream, a.h0, meta, table, a.N, a.H, p.max_chunks, slabs, p.slab_bytes,
-                           a.o, a.hT, groups);
+        hipLaunchKernelGGL((inter_kernel<D, F32IO>), dim3(pair_blocks * groups), dim3(SHP::NT),
+                           SHP::lds_bytes, a.stream, a.h0, meta, table, a.N, a.H, p.max_chunks, slabs,
+                           p.slab_bytes, a.o, a.hT, groups);
         if (hipGetLastError() != hipSuccess) return -1;
     }
     return 0;
