@@ -53,38 +53,35 @@ def parse():
 
 def cpu_baseline(pre: dict, target_s: float) -> dict:
     """The fp64 oracle, as it stands, on a bounded sample of the prefill
-    workload: the first `tok` tokens of `nh` heads, sized to run about
-    target_s seconds on every host core."""
+    workload: the first `tok` tokens of every head, with `tok` grown until
+    one run takes about target_s / 2 seconds or covers the whole sequence."""
     import numpy as np
     import oracle
     from gated_delta_rule_21_amd import workloads as W
 
     cores = os.cpu_count() or 1
-    H = pre["q"].shape[1]
-    nh = min(H, max(1, cores))
+    T, H = pre["q"].shape[0], pre["q"].shape[1]
+    threads = min(cores, H)
 
     def run(tok):
-        sl = lambda t: t[:tok, :nh]
+        sl = lambda t: t[:tok]
         args = [W.as_numpy(sl(pre[n])) for n in ("q", "k", "v", "z")]
-        A = W.as_numpy(pre["A"][:nh])
         beta = W.as_numpy(sl(pre["beta"]))
+        A = W.as_numpy(pre["A"])
         cu = np.array([0, tok], np.int32)
         t0 = time.perf_counter()
-        oracle.prefill(args[0], args[1], args[2], args[3], A, beta, None, cu, nthreads=nh)
+        oracle.prefill(args[0], args[1], args[2], args[3], A, beta, None, cu, nthreads=threads)
         return time.perf_counter() - t0
 
-    tok = 256
+    tok = 64
     dt = run(tok)
-    T = pre["q"].shape[0]
-    while dt < target_s / 4 and tok < T:
-        tok = min(T, int(tok * min(8.0, max(2.0, target_s / max(dt, 1e-3)))))
+    while dt < target_s / 2 and tok < T:
+        tok = min(T, int(tok * min(8.0, max(1.5, target_s / 2 / max(dt, 1e-3)))))
         dt = run(tok)
-    pairs = tok * nh
-    return {"value": pairs / H / dt, "unit": "tokens/s", "cores": nh, "kind": "oracle",
-            "sample": "fp64 token-loop oracle (C, OpenMP) on the first %d tokens of %d of %d "
-                      "heads of the prefill workload; tokens/s counts full %d-head tokens "
-                      "(pairs / %d); %.2f s wall; host %s, %d logical cores"
-                      % (tok, nh, H, H, H, dt, platform.processor() or platform.machine(), cores)}
+    return {"value": tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "fp64 token-loop oracle (C, OpenMP over heads) on the first %d of %d tokens "
+                      "of all %d heads of the prefill workload, %.2f s wall; host %s, %d logical "
+                      "cores" % (tok, T, H, dt, platform.processor() or platform.machine(), cores)}
 
 
 def main():
