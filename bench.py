@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the oracle sample")
+    p.add_argument("--copy-probe-gib", type=float, default=0.0,
+                   help="after timing, run one plain device copy of this many GiB (a known "
+                        "byte count that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
 
 
@@ -142,6 +145,15 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     dec_ms = e0.elapsed_time(e1) / args.decode_steps
+
+    if args.copy_probe_gib > 0:
+        n = int(args.copy_probe_gib * (1 << 30)) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     pairs = T * H
     pre_bytes = PREFILL_BYTES_PER_PAIR * pairs

@@ -53,8 +53,13 @@ struct Slab {
     static constexpr size_t kdT = qg + 4 * NKF * SPL * FRAG;    // ((gamma_C/Gamma)*K)^T [t][NCF][SPL]
     static constexpr size_t aqk = kdT + KT * NCF * SPL * FRAG;  // A_qk    [I][NCF][SPL]
     static constexpr size_t u = aqk + 4 * NCF * SPL * FRAG;     // U (fp32 accumulator layout) [I][KT]
-    static constexpr size_t gamma = u + 4 * KT * FRAG;          // gamma_C [D] fp32
-    static constexpr size_t bytes = ((gamma + D * 4 + 255) / 256) * 256;
+    static constexpr size_t gamma = u + 4 * KT * FRAG;          // gamma_C [D] fp32, in one fragment
+    static constexpr size_t bytes = gamma + FRAG;
+    // The inter-chunk kernel stages two regions through LDS: A = [-W | Gamma*Q]
+    // and B = [K~^T | A_qk | gamma], each a whole number of fragments.
+    static constexpr int FA = (int)(qg - negW + (kdT - qg)) / (int)FRAG;
+    static constexpr int FB = (int)((u - kdT) / FRAG) + 1;   // + the gamma fragment
+    static_assert(D * 4 <= (int)FRAG, "gamma fits one fragment");
 };
 
 // Store an accumulator-pair as a split bf16 fragment (hi at `dst`, lo one
@@ -159,7 +164,8 @@ struct IntraLds {
     // Row operands k_r exp2(Gl_r) and q_r exp2(Gl_r).  bf16 path: per row,
     // [pair p][hi, lo][lane group][8 bf16], so one 16-byte read is one MFMA
     // fragment slot; fp32 path: [64][P] floats.  After the Gram phase the
-    // bf16 path reuses both arrays for (Gamma*K)^T split into hi and lo.
+    // bf16 path reuses both arrays for (Gamma*K)^T split into hi and lo, and
+    // ke's array for M = T Diag(beta) split in the same fragment-row layout.
     unsigned char krs[64 * RB];
     unsigned char qrs[64 * RB];
     float ke[64][P];      // k_i exp2(bt_J - Gl_i); fp32 path: V after the Gram phase
@@ -193,13 +199,30 @@ __device__ __forceinline__ u32x2 lds_bf16x4(const uint16_t (*a)[TP], int row, in
     return *reinterpret_cast<const u32x2 *>(&a[row][col]);
 }
 
-// Raw inputs of one (chunk, head) item for one lane: KT quads of z, k, q, v.
+// Inclusive prefix sum over the 16 lanes of each DPP row (row_shr by 1, 2,
+// 4, 8; lanes shifted in from outside the row read 0).
+__device__ __forceinline__ float row16_inclusive_scan(float x) {
+#define KDA_SHR(n)                                                                          \
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + (n), 0xf, \
+                                                    0xf, true))
+    KDA_SHR(1);
+    KDA_SHR(2);
+    KDA_SHR(4);
+    KDA_SHR(8);
+#undef KDA_SHR
+    return x;
+}
+
+constexpr int kIntraWaves = 8;
+
+// Raw inputs of one (chunk, head) item for one lane of an 8-wave group:
+// wave w loads row block (w & 3), key-channel half (w >> 2).
 template <int D, bool F32IO>
 struct IntraRegs {
-    static constexpr int KT = D / 16;
+    static constexpr int KH = D / 32;  // K16 tiles per channel half
     using Q = typename std::conditional<F32IO, f32x4, u32x2>::type;
-    f32x4 z[KT];
-    Q k[KT], q[KT], v[KT];
+    f32x4 z[KH];
+    Q k[KH], q[KH], v[KH];
     float beta;
 };
 
@@ -207,32 +230,32 @@ template <int D, bool F32IO>
 __device__ __forceinline__ void intra_load(IntraRegs<D, F32IO> &R, const void *q, const void *k,
                                            const void *v, const float *z, const float *beta,
                                            int4 ent, int h, int H, int lane, int wave) {
-    constexpr int KT = D / 16;
+    constexpr int KH = D / 32;
     constexpr int ES = F32IO ? 4 : 2;
     using Q = typename IntraRegs<D, F32IO>::Q;
     const int ln = lane & 15, lg = lane >> 4;
-    const int row = 16 * wave + ln;
+    const int row = 16 * (wave & 3) + ln;
     const bool ok = row < ent.z;
-    const size_t base = ((size_t)(ent.y + (ok ? row : 0)) * H + h) * D + 4 * lg;
+    const size_t base = ((size_t)(ent.y + (ok ? row : 0)) * H + h) * D + (D / 2) * (wave >> 2) + 4 * lg;
     const unsigned char *kb = reinterpret_cast<const unsigned char *>(k);
     const unsigned char *qb = reinterpret_cast<const unsigned char *>(q);
     const unsigned char *vb = reinterpret_cast<const unsigned char *>(v);
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-        const size_t idx = base + 16 * kt;
+    for (int kk = 0; kk < KH; ++kk) {
+        const size_t idx = base + 16 * kk;
         if (ok) {
-            R.z[kt] = ld4(z + idx);
-            R.k[kt] = *reinterpret_cast<const Q *>(kb + idx * ES);
-            R.q[kt] = *reinterpret_cast<const Q *>(qb + idx * ES);
-            R.v[kt] = *reinterpret_cast<const Q *>(vb + idx * ES);
+            R.z[kk] = ld4(z + idx);
+            R.k[kk] = *reinterpret_cast<const Q *>(kb + idx * ES);
+            R.q[kk] = *reinterpret_cast<const Q *>(qb + idx * ES);
+            R.v[kk] = *reinterpret_cast<const Q *>(vb + idx * ES);
         } else {
-            R.z[kt] = zero4();
-            R.k[kt] = Q{};
-            R.q[kt] = Q{};
-            R.v[kt] = Q{};
+            R.z[kk] = zero4();
+            R.k[kk] = Q{};
+            R.q[kk] = Q{};
+            R.v[kk] = Q{};
         }
     }
-    R.beta = (ok && lg == 0) ? beta[(size_t)(ent.y + row) * H + h] : 0.f;
+    R.beta = (ok && lg == 0 && wave < 4) ? beta[(size_t)(ent.y + row) * H + h] : 0.f;
 }
 
 template <bool F32IO, typename Q>
@@ -244,15 +267,29 @@ __device__ __forceinline__ f32x4 quad_f32(Q x) {
     }
 }
 
+// Split bf16 row operand in the fragment-row layout: row r, K16 tile kt,
+// lane group g -> 8 bytes of hi at [kt/2][0][g][kt%2], 8 bytes of lo at [kt/2][1][g][kt%2].
+template <int RB>
+__device__ __forceinline__ void store_row_split(unsigned char *arr, int row, int kt, int g, f32x4 x) {
+    const u32x2 hv = {f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3])};
+    const f32x4 hq = f32x4{bf16_lo_half(hv[0]), bf16_hi_half(hv[0]), bf16_lo_half(hv[1]), bf16_hi_half(hv[1])};
+    const f32x4 r4 = x - hq;
+    const u32x2 lv = {f32x2_to_bf16x2(r4[0], r4[1]), f32x2_to_bf16x2(r4[2], r4[3])};
+    unsigned char *b = arr + row * RB + (kt >> 1) * 128 + g * 16 + (kt & 1) * 8;
+    *reinterpret_cast<u32x2 *>(b) = hv;
+    *reinterpret_cast<u32x2 *>(b + 64) = lv;
+}
+
 template <int D, bool F32IO>
-__global__ void __launch_bounds__(256) intra_kernel(
+__global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
     const float *__restrict__ z, const float *__restrict__ A, const float *__restrict__ beta,
     const int32_t *__restrict__ meta, const int4 *__restrict__ table, int N, int H,
     int max_chunks, unsigned char *__restrict__ slabs, size_t slab_stride) {
     using SL = Slab<D, F32IO>;
     using LDS = IntraLds<D>;
-    constexpr int KT = D / 16;
+    constexpr int KT = D / 16, KH = D / 32;
+    constexpr int NW = kIntraWaves, NTH = 64 * NW;
     constexpr int P = LDS::P, RB = LDS::RB, TP = LDS::TP;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     LDS &s = *reinterpret_cast<LDS *>(lds_raw);
@@ -260,10 +297,12 @@ __global__ void __launch_bounds__(256) intra_kernel(
     float (*qrf)[P] = reinterpret_cast<float (*)[P]>(s.qrs);
     uint16_t (*gkh)[TP] = reinterpret_cast<uint16_t (*)[TP]>(s.krs);               // bf16 path:
     uint16_t (*gkl)[TP] = reinterpret_cast<uint16_t (*)[TP]>(s.krs + D * TP * 2);  // (Gamma*K)^T
+    unsigned char *msp = reinterpret_cast<unsigned char *>(&s.ke[0][0]);          // bf16 path: M split
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int ln = lane & 15, lg = lane >> 4;
+    const int blk = wave & 3, half = wave >> 2;   // phase-1 ownership: row block, channel half
     const int total = meta[N] * H;
     const int stride = gridDim.x;
 
@@ -279,63 +318,39 @@ __global__ void __launch_bounds__(256) intra_kernel(
         const int L = ent.z;
         unsigned char *slab = slabs + ((size_t)h * max_chunks + chunk) * slab_stride;
         const float ea = __expf(A[h]);
-        const int row = 16 * wave + ln;
+        const int row = 16 * blk + ln;
         const bool ok = row < L;
 
         // ---- phase 1: gate, block-local cumulative log2-decay, row operands
-        for (int i = tid; i < 64 * 68; i += 256) (&s.a[0][0])[i] = 0.f;
-        if (lg == 0) s.beta[row] = R.beta;
-        f32x4 krv[KT], qrv[KT], vreg[KT];
+        for (int i = tid; i < 64 * 68; i += NTH) (&s.a[0][0])[i] = 0.f;
+        if (lg == 0 && wave < 4) s.beta[row] = R.beta;
+        f32x4 krv[KH], qrv[KH], vreg[KH];
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
+        for (int kk = 0; kk < KH; ++kk) {
+            const int kt = half * KH + kk;
             const int c0 = 16 * kt + 4 * lg;
-            const f32x4 kk = quad_f32<F32IO>(R.k[kt]);
-            const f32x4 qq = quad_f32<F32IO>(R.q[kt]);
-            vreg[kt] = quad_f32<F32IO>(R.v[kt]);
-            f32x4 gl;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) gl[j] = ok ? gate_log2(ea, R.z[kt][j]) : 0.f;
-#pragma unroll
-            for (int d = 1; d < 16; d <<= 1) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float y = __shfl_up(gl[j], d, 16);
-                    if (ln >= d) gl[j] += y;
-                }
-            }
-            f32x4 bt, rf, kev;
+            const f32x4 kq = quad_f32<F32IO>(R.k[kk]);
+            const f32x4 qq = quad_f32<F32IO>(R.q[kk]);
+            vreg[kk] = quad_f32<F32IO>(R.v[kk]);
+            f32x4 gl, bt, rf, kev;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
+                gl[j] = row16_inclusive_scan(ok ? gate_log2(ea, R.z[kk][j]) : 0.f);
                 bt[j] = __shfl(gl[j], 15, 16);
                 rf[j] = exp2f(gl[j]);
-                kev[j] = kk[j] * exp2f(bt[j] - gl[j]);
+                kev[j] = kq[j] * exp2f(bt[j] - gl[j]);
             }
-            krv[kt] = kk * rf;
-            qrv[kt] = qq * rf;
+            krv[kk] = kq * rf;
+            qrv[kk] = qq * rf;
             *reinterpret_cast<f32x4 *>(&s.ke[row][c0]) = kev;
-            if (ln == 15) *reinterpret_cast<f32x4 *>(&s.bt[wave][c0]) = bt;
-        }
-        if constexpr (F32IO) {
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt) {
-                *reinterpret_cast<f32x4 *>(&krf[row][16 * kt + 4 * lg]) = krv[kt];
-                *reinterpret_cast<f32x4 *>(&qrf[row][16 * kt + 4 * lg]) = qrv[kt];
-            }
-        } else {
-#pragma unroll
-            for (int p = 0; p < KT / 2; ++p) {
-                u32x4 hi, lo;
-                quads_to_bf16_split(krv[2 * p], krv[2 * p + 1], hi, lo);
-                *reinterpret_cast<u32x4 *>(s.krs + row * RB + (2 * p) * 64 + lg * 16) = hi;
-                *reinterpret_cast<u32x4 *>(s.krs + row * RB + (2 * p + 1) * 64 + lg * 16) = lo;
-                quads_to_bf16_split(qrv[2 * p], qrv[2 * p + 1], hi, lo);
-                *reinterpret_cast<u32x4 *>(s.qrs + row * RB + (2 * p) * 64 + lg * 16) = hi;
-                *reinterpret_cast<u32x4 *>(s.qrs + row * RB + (2 * p + 1) * 64 + lg * 16) = lo;
-            }
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt) {
-                const u32x2 vv = R.v[kt];
-                const int c0 = 16 * kt + 4 * lg;
+            if (ln == 15) *reinterpret_cast<f32x4 *>(&s.bt[blk][c0]) = bt;
+            if constexpr (F32IO) {
+                *reinterpret_cast<f32x4 *>(&krf[row][c0]) = krv[kk];
+                *reinterpret_cast<f32x4 *>(&qrf[row][c0]) = qrv[kk];
+            } else {
+                store_row_split<RB>(s.krs, row, kt, lg, krv[kk]);
+                store_row_split<RB>(s.qrs, row, kt, lg, qrv[kk]);
+                const u32x2 vv = R.v[kk];
                 s.vt[c0 + 0][row] = (uint16_t)(vv[0] & 0xffffu);
                 s.vt[c0 + 1][row] = (uint16_t)(vv[0] >> 16);
                 s.vt[c0 + 2][row] = (uint16_t)(vv[1] & 0xffffu);
@@ -354,7 +369,7 @@ __global__ void __launch_bounds__(256) intra_kernel(
         }
         __syncthreads();
 
-        for (int c = tid; c < D; c += 256) {
+        for (int c = tid; c < D; c += NTH) {
             const float b0 = s.bt[0][c], b1 = s.bt[1][c], b2 = s.bt[2][c], b3 = s.bt[3][c];
             s.pfx[0][c] = 1.f;
             s.pfx[1][c] = exp2f(b0);
@@ -383,7 +398,7 @@ __global__ void __launch_bounds__(256) intra_kernel(
         // block I) x (ke of block J) x factor: exp2(-bt_J) on the diagonal block
         // (the <= e^80 case), the decay of the blocks strictly between J and I
         // otherwise (<= 1).
-        for (int tile = wave; tile < 10; tile += 4) {
+        for (int tile = wave; tile < 10; tile += NW) {
             const int I = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
             const int J = tile - (I * (I + 1)) / 2;
             const float *fac = (I == J) ? s.dg[J] : s.off[off_index(J, I)];
@@ -402,10 +417,10 @@ __global__ void __launch_bounds__(256) intra_kernel(
 #pragma unroll
                 for (int p = 0; p < KT / 2; ++p) {
                     const int c0 = 32 * p + 4 * lg, c1 = c0 + 16;
-                    const u32x4 krh = *reinterpret_cast<const u32x4 *>(kr_row + (2 * p) * 64);
-                    const u32x4 krl = *reinterpret_cast<const u32x4 *>(kr_row + (2 * p + 1) * 64);
-                    const u32x4 qrh = *reinterpret_cast<const u32x4 *>(qr_row + (2 * p) * 64);
-                    const u32x4 qrl = *reinterpret_cast<const u32x4 *>(qr_row + (2 * p + 1) * 64);
+                    const u32x4 krh = *reinterpret_cast<const u32x4 *>(kr_row + p * 128);
+                    const u32x4 krl = *reinterpret_cast<const u32x4 *>(kr_row + p * 128 + 64);
+                    const u32x4 qrh = *reinterpret_cast<const u32x4 *>(qr_row + p * 128);
+                    const u32x4 qrl = *reinterpret_cast<const u32x4 *>(qr_row + p * 128 + 64);
                     u32x4 kch, kcl;
                     quads_to_bf16_split(lds_quad(s.ke, 16 * J + ln, c0) * ld4(fac + c0),
                                         lds_quad(s.ke, 16 * J + ln, c1) * ld4(fac + c1), kch, kcl);
@@ -430,12 +445,11 @@ __global__ void __launch_bounds__(256) intra_kernel(
                 *reinterpret_cast<f32x4 *>(slab + SL::aqk + ((size_t)(I * 4 + J) * 64 + lane) * 16) = aq;
             } else {
                 const u32x2 hv = {f32x2_to_bf16x2(aq[0], aq[1]), f32x2_to_bf16x2(aq[2], aq[3])};
-                f32x4 hq;
-                hq = f32x4{bf16_lo_half(hv[0]), bf16_hi_half(hv[0]), bf16_lo_half(hv[1]), bf16_hi_half(hv[1])};
+                const f32x4 hq = f32x4{bf16_lo_half(hv[0]), bf16_hi_half(hv[0]), bf16_lo_half(hv[1]), bf16_hi_half(hv[1])};
                 const f32x4 r4 = aq - hq;
                 const u32x2 lv = {f32x2_to_bf16x2(r4[0], r4[1]), f32x2_to_bf16x2(r4[2], r4[3])};
-                const int qf = J >> 1, half = J & 1;
-                unsigned char *base = slab + SL::aqk + ((size_t)((I * 2 + qf) * 2) * 64 + lane) * 16 + half * 8;
+                const int qf = J >> 1, hh = J & 1;
+                unsigned char *base = slab + SL::aqk + ((size_t)((I * 2 + qf) * 2) * 64 + lane) * 16 + hh * 8;
                 *reinterpret_cast<u32x2 *>(base) = hv;
                 *reinterpret_cast<u32x2 *>(base + 64 * 16) = lv;
                 if (I == J && (I & 1) == 0) {  // the tile right of an even diagonal shares its fragment
@@ -447,7 +461,7 @@ __global__ void __launch_bounds__(256) intra_kernel(
 
         // Gamma*Q fragments (row tile I, key fragment f) and the transposed,
         // end-of-chunk-decayed keys ((gamma_C/Gamma)*K)^T (key tile t, row fragment f).
-        for (int fr = wave; fr < 4 * SL::NKF; fr += 4) {
+        for (int fr = wave; fr < 4 * SL::NKF; fr += NW) {
             const int I = fr / SL::NKF, f = fr % SL::NKF;
             unsigned char *dst = slab + SL::qg + ((size_t)fr * SL::SPL * 64 + lane) * 16;
             if constexpr (F32IO) {
@@ -456,13 +470,13 @@ __global__ void __launch_bounds__(256) intra_kernel(
             } else {
                 const unsigned char *qr_row = s.qrs + (16 * I + ln) * RB + lg * 16;
                 f32x4 h0, h1, l0, l1;
-                bf16_to_quads(*reinterpret_cast<const u32x4 *>(qr_row + (2 * f) * 64), h0, h1);
-                bf16_to_quads(*reinterpret_cast<const u32x4 *>(qr_row + (2 * f + 1) * 64), l0, l1);
+                bf16_to_quads(*reinterpret_cast<const u32x4 *>(qr_row + f * 128), h0, h1);
+                bf16_to_quads(*reinterpret_cast<const u32x4 *>(qr_row + f * 128 + 64), l0, l1);
                 const int c0 = 32 * f + 4 * lg, c1 = c0 + 16;
                 store_split(dst, (h0 + l0) * ld4(&s.pfx[I][c0]), (h1 + l1) * ld4(&s.pfx[I][c1]));
             }
         }
-        for (int fr = wave; fr < KT * SL::NCF; fr += 4) {
+        for (int fr = wave; fr < KT * SL::NCF; fr += NW) {
             const int t = fr / SL::NCF, f = fr % SL::NCF;
             const int c = 16 * t + ln;
             unsigned char *dst = slab + SL::kdT + ((size_t)fr * SL::SPL * 64 + lane) * 16;
@@ -481,8 +495,8 @@ __global__ void __launch_bounds__(256) intra_kernel(
         // arrays, and the diagonal 16x16 inverses, in place.
         if constexpr (F32IO) {
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-                *reinterpret_cast<f32x4 *>(&s.ke[row][16 * kt + 4 * lg]) = vreg[kt];
+            for (int kk = 0; kk < KH; ++kk)
+                *reinterpret_cast<f32x4 *>(&s.ke[row][16 * (half * KH + kk) + 4 * lg]) = vreg[kk];
             if (it_next < total) {
                 intra_load<D, F32IO>(R, q, k, v, z, beta, ent_next, it_next % H, H, lane, wave);
                 ent = ent_next;
@@ -490,9 +504,9 @@ __global__ void __launch_bounds__(256) intra_kernel(
             }
         } else {
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt) {
-                const int c0 = 16 * kt + 4 * lg;
-                const f32x4 gk = krv[kt] * ld4(&s.pfx[wave][c0]);
+            for (int kk = 0; kk < KH; ++kk) {
+                const int c0 = 16 * (half * KH + kk) + 4 * lg;
+                const f32x4 gk = krv[kk] * ld4(&s.pfx[blk][c0]);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     uint32_t hb, lb;
@@ -502,7 +516,7 @@ __global__ void __launch_bounds__(256) intra_kernel(
                 }
             }
         }
-        if (lane < 16) {
+        if (wave < 4 && lane < 16) {
             // forward substitution for column `lane` of (I + A_ww)^{-1}
             const int b = 16 * wave;
             float col[16];
@@ -538,65 +552,77 @@ __global__ void __launch_bounds__(256) intra_kernel(
             __syncthreads();
         }
 
+        // ---- phase 4b (bf16 path): M = T Diag(beta), split once, in the
+        // fragment-row layout [row][J pair][hi, lo][lane group][8 bf16].
+        if constexpr (!F32IO) {
+            const int pj = half;
+            const int c0 = 32 * pj + 4 * lg, c1 = c0 + 16;
+            u32x4 mh, ml;
+            quads_to_bf16_split(lds_quad(s.a, row, c0) * ld4(&s.beta[c0]),
+                                lds_quad(s.a, row, c1) * ld4(&s.beta[c1]), mh, ml);
+            unsigned char *b = msp + ((row * 2 + pj) * 2) * 64 + lg * 16;
+            *reinterpret_cast<u32x4 *>(b) = mh;
+            *reinterpret_cast<u32x4 *>(b + 64) = ml;
+            __syncthreads();
+        }
+
         // ---- phase 5: -W fragments (from W^T tiles) and U tiles; M = T Diag(beta).
         // W^T tile (t, I) = sum_J (Gamma*K)^T_{tJ} M^T_{JI}: the accumulator
         // lane (n = r, g) holds W[16I + r][16t + 4g + j], the A-operand
         // fragment of -W in the state-propagation product.
-        for (int I = 0; I < 4; ++I) {
+        for (int unit = wave; unit < 4 * SL::NKF; unit += NW) {
+            const int I = unit / SL::NKF, tp = unit % SL::NKF;
             const int nJ = I + 1;
-            for (int tp = wave; tp < SL::NKF; tp += 4) {
-                if constexpr (F32IO) {
-                    const int t = tp;
-                    f32x4 acc = zero4();
-                    for (int J = 0; J < nJ; ++J) {
-                        const int cJ = 16 * J + 4 * lg;
-                        const f32x4 mq = lds_quad(s.a, 16 * I + ln, cJ) * ld4(&s.beta[cJ]);
-                        const f32x4 gk = lds_col4(krf, 16 * J + 4 * lg, 16 * t + ln) * s.pfx[J][16 * t + ln];
-                        acc = mma_f32_k16(gk, mq, acc);
-                    }
-                    *reinterpret_cast<f32x4 *>(slab + SL::negW + ((size_t)(I * SL::NKF + tp) * 64 + lane) * 16) = -acc;
-                } else {
-                    const int ca = 32 * tp + ln, cb = ca + 16;
-                    f32x4 acc0 = zero4(), acc1 = zero4();
-                    for (int pj = 0; pj < (nJ + 1) / 2; ++pj) {
-                        const int cJ0 = 32 * pj + 4 * lg, cJ1 = cJ0 + 16;
-                        u32x4 mh, ml;
-                        quads_to_bf16_split(lds_quad(s.a, 16 * I + ln, cJ0) * ld4(&s.beta[cJ0]),
-                                            lds_quad(s.a, 16 * I + ln, cJ1) * ld4(&s.beta[cJ1]), mh, ml);
-                        const u32x4 gah = cat2(lds_bf16x4(gkh, ca, cJ0), lds_bf16x4(gkh, ca, cJ1));
-                        const u32x4 gal = cat2(lds_bf16x4(gkl, ca, cJ0), lds_bf16x4(gkl, ca, cJ1));
-                        const u32x4 gbh = cat2(lds_bf16x4(gkh, cb, cJ0), lds_bf16x4(gkh, cb, cJ1));
-                        const u32x4 gbl = cat2(lds_bf16x4(gkl, cb, cJ0), lds_bf16x4(gkl, cb, cJ1));
-                        acc0 = mma3_bf16(gah, gal, mh, ml, acc0);
-                        acc1 = mma3_bf16(gbh, gbl, mh, ml, acc1);
-                    }
-                    store_split(slab + SL::negW + ((size_t)(I * SL::NKF + tp) * 2 * 64 + lane) * 16, -acc0, -acc1);
-                }
-            }
-            // U tile (I, w) = sum_J M_{IJ} V_{Jw}, in the accumulator layout the
-            // state-propagation kernel starts V' from.
-            for (int w = wave; w < KT; w += 4) {
+            if constexpr (F32IO) {
+                const int t = tp;
                 f32x4 acc = zero4();
-                if constexpr (F32IO) {
-                    for (int J = 0; J < nJ; ++J) {
-                        const int cJ = 16 * J + 4 * lg;
-                        const f32x4 mq = lds_quad(s.a, 16 * I + ln, cJ) * ld4(&s.beta[cJ]);
-                        acc = mma_f32_k16(mq, lds_col4(s.ke, 16 * J + 4 * lg, 16 * w + ln), acc);
-                    }
-                } else {
-                    for (int pj = 0; pj < (nJ + 1) / 2; ++pj) {
-                        const int cJ0 = 32 * pj + 4 * lg, cJ1 = cJ0 + 16;
-                        u32x4 mh, ml;
-                        quads_to_bf16_split(lds_quad(s.a, 16 * I + ln, cJ0) * ld4(&s.beta[cJ0]),
-                                            lds_quad(s.a, 16 * I + ln, cJ1) * ld4(&s.beta[cJ1]), mh, ml);
-                        const u32x4 vb = cat2(lds_bf16x4(s.vt, 16 * w + ln, cJ0),
-                                              lds_bf16x4(s.vt, 16 * w + ln, cJ1));
-                        acc = mma_bf16_k32(mh, vb, acc);
-                        acc = mma_bf16_k32(ml, vb, acc);
-                    }
+                for (int J = 0; J < nJ; ++J) {
+                    const int cJ = 16 * J + 4 * lg;
+                    const f32x4 mq = lds_quad(s.a, 16 * I + ln, cJ) * ld4(&s.beta[cJ]);
+                    const f32x4 gk = lds_col4(krf, 16 * J + 4 * lg, 16 * t + ln) * s.pfx[J][16 * t + ln];
+                    acc = mma_f32_k16(gk, mq, acc);
                 }
-                *reinterpret_cast<f32x4 *>(slab + SL::u + ((size_t)(I * KT + w) * 64 + lane) * 16) = acc;
+                *reinterpret_cast<f32x4 *>(slab + SL::negW + ((size_t)(I * SL::NKF + tp) * 64 + lane) * 16) = -acc;
+            } else {
+                const int ca = 32 * tp + ln, cb = ca + 16;
+                f32x4 acc0 = zero4(), acc1 = zero4();
+                for (int pj = 0; pj < (nJ + 1) / 2; ++pj) {
+                    const int cJ0 = 32 * pj + 4 * lg, cJ1 = cJ0 + 16;
+                    const unsigned char *mb = msp + (((16 * I + ln) * 2 + pj) * 2) * 64 + lg * 16;
+                    const u32x4 mh = *reinterpret_cast<const u32x4 *>(mb);
+                    const u32x4 ml = *reinterpret_cast<const u32x4 *>(mb + 64);
+                    const u32x4 gah = cat2(lds_bf16x4(gkh, ca, cJ0), lds_bf16x4(gkh, ca, cJ1));
+                    const u32x4 gal = cat2(lds_bf16x4(gkl, ca, cJ0), lds_bf16x4(gkl, ca, cJ1));
+                    const u32x4 gbh = cat2(lds_bf16x4(gkh, cb, cJ0), lds_bf16x4(gkh, cb, cJ1));
+                    const u32x4 gbl = cat2(lds_bf16x4(gkl, cb, cJ0), lds_bf16x4(gkl, cb, cJ1));
+                    acc0 = mma3_bf16(gah, gal, mh, ml, acc0);
+                    acc1 = mma3_bf16(gbh, gbl, mh, ml, acc1);
+                }
+                store_split(slab + SL::negW + ((size_t)(I * SL::NKF + tp) * 2 * 64 + lane) * 16, -acc0, -acc1);
             }
+        }
+        // U tile (I, w) = sum_J M_{IJ} V_{Jw}, in the accumulator layout the
+        // state-propagation kernel starts V' from.
+        for (int unit = wave; unit < 4 * KT; unit += NW) {
+            const int I = unit / KT, w = unit % KT;
+            const int nJ = I + 1;
+            f32x4 acc = zero4();
+            if constexpr (F32IO) {
+                for (int J = 0; J < nJ; ++J) {
+                    const int cJ = 16 * J + 4 * lg;
+                    const f32x4 mq = lds_quad(s.a, 16 * I + ln, cJ) * ld4(&s.beta[cJ]);
+                    acc = mma_f32_k16(mq, lds_col4(s.ke, 16 * J + 4 * lg, 16 * w + ln), acc);
+                }
+            } else {
+                for (int pj = 0; pj < (nJ + 1) / 2; ++pj) {
+                    const int cJ0 = 32 * pj + 4 * lg, cJ1 = cJ0 + 16;
+                    const unsigned char *mb = msp + (((16 * I + ln) * 2 + pj) * 2) * 64 + lg * 16;
+                    const u32x4 vb = cat2(lds_bf16x4(s.vt, 16 * w + ln, cJ0), lds_bf16x4(s.vt, 16 * w + ln, cJ1));
+                    acc = mma_bf16_k32(*reinterpret_cast<const u32x4 *>(mb), vb, acc);
+                    acc = mma_bf16_k32(*reinterpret_cast<const u32x4 *>(mb + 64), vb, acc);
+                }
+            }
+            *reinterpret_cast<f32x4 *>(slab + SL::u + ((size_t)(I * KT + w) * 64 + lane) * 16) = acc;
         }
         __syncthreads();
     }
@@ -607,13 +633,14 @@ __global__ void __launch_bounds__(256) intra_kernel(
 // [16 vt, 16 vt + 16) of one (sequence, head); its state slice S[:, cols]
 // lives in DK/16 accumulator tiles (lane (n, g) holds S[16t + 4g + j][16vt + n]).
 // Per chunk, in the order of the chunk form:
-//   V' = U - W S                 (U is the initial accumulator, -W the A operand)
-//   O  = (Gamma*Q) S + A_qk V'
-//   S  = Diag(gamma_C) S + ((gamma_C/Gamma)*K)^T V'
+//   phase A:  V' = U - W S,   O = (Gamma*Q) S                    (-W, Gamma*Q from LDS A)
+//   phase B:  O += A_qk V',   S = Diag(gamma_C) S + K~^T V'       (A_qk, K~^T, gamma from LDS B)
 // Every bf16 operand (stored fragments and the S, V' accumulators) enters
 // the MFMAs split into hi + lo parts; each product is hi*hi + hi*lo + lo*hi.
-// The operands every wave shares (-W, Gamma*Q, K~^T, A_qk, gamma) sit in LDS;
-// the next chunk's copy is loaded into registers while this chunk computes.
+// The shared operands reach LDS by direct global->LDS copies
+// (global_load_lds_dwordx4, one 1 KiB fragment per wave instruction): region B
+// of this chunk streams in during phase A, region A of the next chunk during
+// phase B.
 // ---------------------------------------------------------------------------
 template <int D, bool F32IO>
 struct InterShape {
@@ -621,13 +648,19 @@ struct InterShape {
     static constexpr int KT = D / 16;
     static constexpr int WPG = KT < 4 ? KT : 4;          // waves per workgroup
     static constexpr int NT = 64 * WPG;
-    static constexpr int SH = (int)(SL::u / 16);          // shared 16-byte vectors before U
-    static constexpr int NPF = SH / NT;
-    static constexpr int NG = D / 4;                      // gamma as 16-byte vectors
-    static constexpr size_t lds_bytes = (size_t)(SH + NG) * 16;
-    static_assert(NPF * NT == SH, "shared slab region must split evenly over the threads");
-    static_assert(NG <= NT, "gamma vectors");
+    static constexpr size_t lds_bytes = (size_t)(SL::FA + SL::FB) * SL::FRAG;
 };
+
+// Copy `nfrag` consecutive 1 KiB fragments from global `src` to LDS `dst`,
+// spread over the workgroup's waves.  Asynchronous: wait on vmcnt before use.
+__device__ __forceinline__ void copy_frags_to_lds(const unsigned char *src, unsigned char *dst, int nfrag,
+                                                  int wave, int nwaves, int lane) {
+    for (int f = wave; f < nfrag; f += nwaves)
+        __builtin_amdgcn_global_load_lds(src + (size_t)f * 1024 + lane * 16,
+                                         (__attribute__((address_space(3))) void *)(dst + f * 1024), 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
 template <int D, bool F32IO>
 __global__ void __launch_bounds__(256) inter_kernel(
@@ -637,9 +670,10 @@ __global__ void __launch_bounds__(256) inter_kernel(
     using SL = Slab<D, F32IO>;
     using SHP = InterShape<D, F32IO>;
     constexpr int KT = D / 16;
-    constexpr int WPG = SHP::WPG, NT = SHP::NT, SH = SHP::SH, NPF = SHP::NPF, NG = SHP::NG;
+    constexpr int WPG = SHP::WPG;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
-    u32x4 *sh = reinterpret_cast<u32x4 *>(lds_raw);
+    unsigned char *bufA = lds_raw;                       // [-W | Gamma*Q]
+    unsigned char *bufB = lds_raw + SL::FA * SL::FRAG;   // [K~^T | A_qk | gamma]
 
     // blockIdx -> (pair, column group) with every group of a pair on the same XCD
     const int b = blockIdx.x;
@@ -661,43 +695,49 @@ __global__ void __launch_bounds__(256) inter_kernel(
         S[t] = h0 ? *reinterpret_cast<const f32x4 *>(h0 + srow + 16 * t + 4 * lg) : zero4();
 
     const int c_begin = meta[n], c_end = meta[n + 1];
-    u32x4 pf[NPF], pg = u32x4{0u, 0u, 0u, 0u};
-    f32x4 u[4], un[4];
-    auto slab_of = [&](int c) {
-        return slabs + ((size_t)h * max_chunks + c) * slab_stride;
-    };
-    auto issue = [&](int c) {
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(slab_of(c));
-#pragma unroll
-        for (int i = 0; i < NPF; ++i) pf[i] = src[tid + i * NT];
-        if (tid < NG) pg = src[SL::gamma / 16 + tid];
+    auto slab_of = [&](int c) { return slabs + ((size_t)h * max_chunks + c) * slab_stride; };
+    auto load_u = [&](int c, f32x4 *dst) {
         const f32x4 *us = reinterpret_cast<const f32x4 *>(slab_of(c) + SL::u);
 #pragma unroll
-        for (int I = 0; I < 4; ++I) un[I] = us[(I * KT + vt) * 64 + lane];
+        for (int I = 0; I < 4; ++I) dst[I] = us[(I * KT + vt) * 64 + lane];
     };
-    auto commit = [&]() {
-#pragma unroll
-        for (int i = 0; i < NPF; ++i) sh[tid + i * NT] = pf[i];
-        if (tid < NG) sh[SH + tid] = pg;
-#pragma unroll
-        for (int I = 0; I < 4; ++I) u[I] = un[I];
+    // this lane's 16 bytes of fragment idx in an LDS region
+    auto fa = [&](size_t off, int idx) -> u32x4 {
+        return *reinterpret_cast<const u32x4 *>(bufA + off + ((size_t)idx * 64 + lane) * 16);
     };
-    // fragment idx of the region at byte offset `off`, this lane's 16 bytes
-    auto frag = [&](size_t off, int idx) -> const u32x4 & { return sh[off / 16 + idx * 64 + lane]; };
-    auto fragf = [&](size_t off, int idx) -> f32x4 { return __builtin_bit_cast(f32x4, frag(off, idx)); };
+    auto fb = [&](size_t off, int idx) -> u32x4 {
+        return *reinterpret_cast<const u32x4 *>(bufB + (off - SL::kdT) + ((size_t)idx * 64 + lane) * 16);
+    };
+    const f32x4 *gam = reinterpret_cast<const f32x4 *>(bufB + (SL::FB - 1) * SL::FRAG);
 
+    f32x4 u[4], un[4];
+    f32x4 acc_o[4];
+    int o_t0 = 0, o_L = 0;     // pending output of the previous chunk
     if (c_begin < c_end) {
-        issue(c_begin);
-        commit();
+        copy_frags_to_lds(slab_of(c_begin), bufA, SL::FA, wave, WPG, lane);
+        load_u(c_begin, u);
     }
+    wait_all_memory();
     __syncthreads();
     for (int c = c_begin; c < c_end; ++c) {
+        const unsigned char *sc = slab_of(c);
+        copy_frags_to_lds(sc + SL::kdT, bufB, SL::FB - 1, wave, WPG, lane);            // K~^T, A_qk
+        copy_frags_to_lds(sc + SL::gamma, bufB + (SL::FB - 1) * SL::FRAG, 1, wave, WPG, lane);  // gamma
+        if (c + 1 < c_end) load_u(c + 1, un);
+        // the previous chunk's output rows
+        if (o_L > 0) {
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * I + 4 * lg + j;
+                    if (r < o_L) store_io<F32IO>(o, ((size_t)(o_t0 + r) * H + h) * D + col, acc_o[I][j]);
+                }
+        }
         const int4 ent = table[c];
-        const int t0 = ent.y, L = ent.z;
-        if (c + 1 < c_end) issue(c + 1);
 
-        f32x4 vp[4], acc_o[4];
-        const f32x4 *gam = reinterpret_cast<const f32x4 *>(&sh[SH]);
+        // ---- phase A
+        f32x4 vp[4];
         if constexpr (F32IO) {
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
@@ -705,20 +745,9 @@ __global__ void __launch_bounds__(256) inter_kernel(
                 acc_o[I] = zero4();
 #pragma unroll
                 for (int t = 0; t < KT; ++t) {
-                    vp[I] = mma_f32_k16(fragf(SL::negW, I * KT + t), S[t], vp[I]);
-                    acc_o[I] = mma_f32_k16(fragf(SL::qg, I * KT + t), S[t], acc_o[I]);
+                    vp[I] = mma_f32_k16(__builtin_bit_cast(f32x4, fa(SL::negW, I * KT + t)), S[t], vp[I]);
+                    acc_o[I] = mma_f32_k16(__builtin_bit_cast(f32x4, fa(SL::qg, I * KT + t)), S[t], acc_o[I]);
                 }
-            }
-#pragma unroll
-            for (int I = 0; I < 4; ++I)
-#pragma unroll
-                for (int J = 0; J <= I; ++J)
-                    acc_o[I] = mma_f32_k16(fragf(SL::aqk, I * 4 + J), vp[J], acc_o[I]);
-#pragma unroll
-            for (int t = 0; t < KT; ++t) {
-                S[t] = S[t] * gam[4 * t + lg];
-#pragma unroll
-                for (int J = 0; J < 4; ++J) S[t] = mma_f32_k16(fragf(SL::kdT, t * 4 + J), vp[J], S[t]);
             }
         } else {
             u32x4 shi[KT / 2], slo[KT / 2];
@@ -731,10 +760,30 @@ __global__ void __launch_bounds__(256) inter_kernel(
 #pragma unroll
                 for (int p = 0; p < KT / 2; ++p) {
                     const int fi = (I * (KT / 2) + p) * 2;
-                    vp[I] = mma3_bf16(frag(SL::negW, fi), frag(SL::negW, fi + 1), shi[p], slo[p], vp[I]);
-                    acc_o[I] = mma3_bf16(frag(SL::qg, fi), frag(SL::qg, fi + 1), shi[p], slo[p], acc_o[I]);
+                    vp[I] = mma3_bf16(fa(SL::negW, fi), fa(SL::negW, fi + 1), shi[p], slo[p], vp[I]);
+                    acc_o[I] = mma3_bf16(fa(SL::qg, fi), fa(SL::qg, fi + 1), shi[p], slo[p], acc_o[I]);
                 }
             }
+        }
+        wait_all_memory();
+        __syncthreads();
+        if (c + 1 < c_end) copy_frags_to_lds(slab_of(c + 1), bufA, SL::FA, wave, WPG, lane);
+
+        // ---- phase B
+        if constexpr (F32IO) {
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int J = 0; J <= I; ++J)
+                    acc_o[I] = mma_f32_k16(__builtin_bit_cast(f32x4, fb(SL::aqk, I * 4 + J)), vp[J], acc_o[I]);
+#pragma unroll
+            for (int t = 0; t < KT; ++t) {
+                S[t] = S[t] * gam[4 * t + lg];
+#pragma unroll
+                for (int J = 0; J < 4; ++J)
+                    S[t] = mma_f32_k16(__builtin_bit_cast(f32x4, fb(SL::kdT, t * 4 + J)), vp[J], S[t]);
+            }
+        } else {
             u32x4 vh[2], vl[2];
             quads_to_bf16_split(vp[0], vp[1], vh[0], vl[0]);
             quads_to_bf16_split(vp[2], vp[3], vh[1], vl[1]);
@@ -742,27 +791,32 @@ __global__ void __launch_bounds__(256) inter_kernel(
             for (int I = 0; I < 4; ++I)
 #pragma unroll
                 for (int qf = 0; qf <= I / 2; ++qf)
-                    acc_o[I] = mma3_bf16(frag(SL::aqk, (I * 2 + qf) * 2), frag(SL::aqk, (I * 2 + qf) * 2 + 1),
+                    acc_o[I] = mma3_bf16(fb(SL::aqk, (I * 2 + qf) * 2), fb(SL::aqk, (I * 2 + qf) * 2 + 1),
                                          vh[qf], vl[qf], acc_o[I]);
 #pragma unroll
             for (int t = 0; t < KT; ++t) {
                 S[t] = S[t] * gam[4 * t + lg];
 #pragma unroll
                 for (int qf = 0; qf < 2; ++qf)
-                    S[t] = mma3_bf16(frag(SL::kdT, (t * 2 + qf) * 2), frag(SL::kdT, (t * 2 + qf) * 2 + 1),
+                    S[t] = mma3_bf16(fb(SL::kdT, (t * 2 + qf) * 2), fb(SL::kdT, (t * 2 + qf) * 2 + 1),
                                      vh[qf], vl[qf], S[t]);
             }
         }
+        o_t0 = ent.y;
+        o_L = ent.z;
+        wait_all_memory();
+        __syncthreads();
+#pragma unroll
+        for (int I = 0; I < 4; ++I) u[I] = un[I];
+    }
+    if (o_L > 0) {
 #pragma unroll
         for (int I = 0; I < 4; ++I)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * I + 4 * lg + j;
-                if (r < L) store_io<F32IO>(o, ((size_t)(t0 + r) * H + h) * D + col, acc_o[I][j]);
+                if (r < o_L) store_io<F32IO>(o, ((size_t)(o_t0 + r) * H + h) * D + col, acc_o[I][j]);
             }
-        __syncthreads();
-        if (c + 1 < c_end) commit();
-        __syncthreads();
     }
     if (hT) {
 #pragma unroll
@@ -806,7 +860,7 @@ static int launch_prefill_t(const PrefillArgs &a) {
         const size_t lds = sizeof(IntraLds<D>);
         if (!set_lds(&intra_kernel<D, F32IO>, lds)) return -1;
         const int grid = (int)std::min<long long>(items, (long long)device_cus());
-        hipLaunchKernelGGL((intra_kernel<D, F32IO>), dim3(grid), dim3(256), lds, a.stream, a.q, a.k,
+        hipLaunchKernelGGL((intra_kernel<D, F32IO>), dim3(grid), dim3(64 * kIntraWaves), lds, a.stream, a.q, a.k,
                            a.v, a.z, a.A, a.beta, meta, table, a.N, a.H, p.max_chunks, slabs,
                            p.slab_bytes);
         if (hipGetLastError() != hipSuccess) return -1;
