@@ -4,7 +4,9 @@
 
 Every HIP source is compiled for gfx950 only.  Packed fp32 instructions are
 disabled (-packed-fp32-ops): the kernels are written as scalar / vector fp32
-code and must not be turned into v_pk_* fp32 forms.
+code and must not be turned into v_pk_* fp32 forms.  MFMA accumulators are
+kept in ordinary VGPRs (-amdgpu-mfma-vgpr-form): the kernels post-process
+every accumulator with VALU code, and AGPR copies would cost a move each.
 """
 from __future__ import annotations
 
@@ -22,6 +24,7 @@ SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prefill.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 
 

@@ -71,9 +71,14 @@ __device__ __forceinline__ void store_io(void *p, size_t i, float x) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float gate_log2(float ea, float z) {
     float x = ea * z;
-    float s = __frcp_rn(1.0f + exp2f(-x * kLog2e));
+    float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
     return kGminLog2e * s;
 }
+
+// 2^x on the transcendental unit (v_exp_f32).  Results below 2^-126 may
+// flush to zero; every use here is a decay factor whose true value is then
+// negligible.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
 // 16x16 MFMA tiles.  Fragment convention used by every kernel here:
@@ -114,6 +119,64 @@ __device__ __forceinline__ void quads_to_bf16_split(f32x4 x0, f32x4 x1, u32x4 &h
     bf16_to_quads(hi, h0, h1);
     lo = quads_to_bf16(x0 - h0, x1 - h1);
 }
+
+// ---------------------------------------------------------------------------
+// fp16 operands of the serial state chain (v_cvt_pk_f16_f32, round to
+// nearest even; v_mfma_f32_16x16x32_f16).
+// ---------------------------------------------------------------------------
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t f32x2_to_f16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+__device__ __forceinline__ u32x4 quads_to_f16(f32x4 x0, f32x4 x1) {
+    return u32x4{f32x2_to_f16x2(x0[0], x0[1]), f32x2_to_f16x2(x0[2], x0[3]),
+                 f32x2_to_f16x2(x1[0], x1[1]), f32x2_to_f16x2(x1[2], x1[3])};
+}
+__device__ __forceinline__ u32x2 quad_to_f16(f32x4 x) {
+    return u32x2{f32x2_to_f16x2(x[0], x[1]), f32x2_to_f16x2(x[2], x[3])};
+}
+__device__ __forceinline__ f32x4 mma_f16_k32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Power-of-two scaling for fp16 operands: scale_for(m) = 2^-e with e chosen
+// so that m * 2^-e lies in [2^11, 2^12) (m > 0), i.e. well inside the fp16
+// range whatever the magnitude of the data.  Multiplying by a power of two
+// is exact, so scaling and unscaling change no bits of the mantissas.
+__device__ __forceinline__ int scale_exp(float m) {
+    const int be = (int)((__float_as_uint(m) >> 23) & 0xffu);   // biased exponent of m
+    int e = be - 127 - 11;
+    e = be == 0 ? 0 : e;
+    return min(max(e, -100), 100);
+}
+__device__ __forceinline__ float exp2i(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
+
+// DPP lane movement inside 16-lane rows: row_shr:n (0x110 + n) shifts in
+// from lower lanes with zero fill; row_newbcast:n (0x150 + n) broadcasts lane
+// n of every row to that row.
+#define KDA_DPP(x, ctrl) \
+    __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), (ctrl), 0xf, 0xf, true))
+
+// Maximum over the 64 lanes of a wavefront of values x >= 0: a DPP max-scan
+// inside each 16-lane row, then the four row maxima through readlane.  The
+// result is wave-uniform.
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+    x = fmaxf(x, KDA_DPP(x, 0x111));
+    x = fmaxf(x, KDA_DPP(x, 0x112));
+    x = fmaxf(x, KDA_DPP(x, 0x114));
+    x = fmaxf(x, KDA_DPP(x, 0x118));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// Lane 15 of each 16-lane row, broadcast to the row.
+__device__ __forceinline__ float row16_last(float x) { return KDA_DPP(x, 0x15f); }
 
 // acc + (ah + al)(bh + bl) without the lo*lo term: a product of two
 // split operands, good to about 2^-16 relative per term.

@@ -38,15 +38,20 @@ namespace kda {
 
 // ---------------------------------------------------------------------------
 // Slab layout (bytes from the slab start).  A "fragment" is 64 lanes x 16 B
-// in the lane order of the MFMA operand it feeds (kda_device.h): a bf16
-// fragment spans two K16 tiles (one 16x16x32 MFMA), an fp32 fragment one.
+// in the lane order of the MFMA operand it feeds (kda_device.h).  fp32 path:
+// fp32 fragments, one K16 tile each.  bf16 path: the operands of the serial
+// state chain are stored in fp16, one fragment spanning two K16 tiles (one
+// 16x16x32 MFMA); they are bounded by construction (|Gamma*Q|, |K~| <= 1,
+// W and A_qk are products of contractions), and the state-carrying side of
+// every chain product is scaled by a power of two per chunk before it is
+// rounded to fp16.  U stays fp32.
 // ---------------------------------------------------------------------------
 template <int D, bool F32>
 struct Slab {
     static constexpr int KT = D / 16;                 // 16-wide key / value tiles
     static constexpr int NKF = F32 ? D / 16 : D / 32; // fragments over d per 16-row tile
     static constexpr int NCF = F32 ? 4 : 2;           // fragments over the 64 chunk rows
-    static constexpr int SPL = F32 ? 1 : 2;           // bf16 operands are stored as hi, lo pairs
+    static constexpr int SPL = 1;                     // one fragment per operand tile (fp32 or fp16)
     static constexpr size_t FRAG = 1024;
     static constexpr size_t negW = 0;                           // -W      [I][NKF][SPL]
     static constexpr size_t qg = negW + 4 * NKF * SPL * FRAG;   // Gamma*Q [I][NKF][SPL]
@@ -62,13 +67,9 @@ struct Slab {
     static_assert(D * 4 <= (int)FRAG, "gamma fits one fragment");
 };
 
-// Store an accumulator-pair as a split bf16 fragment (hi at `dst`, lo one
-// fragment later) or an fp32 quad as an fp32 fragment.
-__device__ __forceinline__ void store_split(unsigned char *dst, f32x4 x0, f32x4 x1) {
-    u32x4 hi, lo;
-    quads_to_bf16_split(x0, x1, hi, lo);
-    *reinterpret_cast<u32x4 *>(dst) = hi;
-    *reinterpret_cast<u32x4 *>(dst + 1024) = lo;
+// Store two fp32 quads (K16 tiles t, t + 1) as one fp16 fragment.
+__device__ __forceinline__ void store_f16(unsigned char *dst, f32x4 x0, f32x4 x1) {
+    *reinterpret_cast<u32x4 *>(dst) = quads_to_f16(x0, x1);
 }
 
 size_t slab_bytes(int dk, int dv, bool f32io) {
@@ -214,6 +215,9 @@ __device__ __forceinline__ float row16_inclusive_scan(float x) {
 }
 
 constexpr int kIntraWaves = 8;
+// Row pitch (bytes) of the split M array: 2 pairs x (hi, lo) x 64 B plus 16 B
+// so that the 16 rows a wave reads at once fall on different LDS banks.
+constexpr int kMsRow = 2 * 128 + 16;
 
 // Raw inputs of one (chunk, head) item for one lane of an 8-wave group:
 // wave w loads row block (w & 3), key-channel half (w >> 2).
@@ -311,13 +315,19 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
     IntraRegs<D, F32IO> R;
     int4 ent = table[it / H];
     intra_load<D, F32IO>(R, q, k, v, z, beta, ent, it % H, H, lane, wave);
+    // Chunk-table entries and A_h are read through the scalar cache, whose
+    // loads every barrier waits for: fetch them one item ahead of their use.
     int4 ent_next = (it + stride < total) ? table[(it + stride) / H] : make_int4(0, 0, 0, 0);
+    float a_cur = A[it % H];
 
     for (; it < total; it += stride) {
         const int chunk = it / H, h = it % H;
         const int L = ent.z;
         unsigned char *slab = slabs + ((size_t)h * max_chunks + chunk) * slab_stride;
-        const float ea = __expf(A[h]);
+        const float ea = __expf(a_cur);
+        const int it_next = it + stride;
+        const int4 ent_after = (it_next + stride < total) ? table[(it_next + stride) / H] : make_int4(0, 0, 0, 0);
+        const float a_next = it_next < total ? A[it_next % H] : 0.f;
         const int row = 16 * blk + ln;
         const bool ok = row < L;
 
@@ -336,9 +346,9 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 gl[j] = row16_inclusive_scan(ok ? gate_log2(ea, R.z[kk][j]) : 0.f);
-                bt[j] = __shfl(gl[j], 15, 16);
-                rf[j] = exp2f(gl[j]);
-                kev[j] = kq[j] * exp2f(bt[j] - gl[j]);
+                bt[j] = row16_last(gl[j]);
+                rf[j] = fast_exp2(gl[j]);
+                kev[j] = kq[j] * fast_exp2(bt[j] - gl[j]);
             }
             krv[kk] = kq * rf;
             qrv[kk] = qq * rf;
@@ -359,13 +369,8 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
         }
         // The raw inputs are consumed: fetch the next item (bf16 path; the
         // fp32 path keeps V in registers until phase 3 and fetches there).
-        const int it_next = it + stride;
         if constexpr (!F32IO) {
-            if (it_next < total) {
-                intra_load<D, F32IO>(R, q, k, v, z, beta, ent_next, it_next % H, H, lane, wave);
-                ent = ent_next;
-                if (it_next + stride < total) ent_next = table[(it_next + stride) / H];
-            }
+            if (it_next < total) intra_load<D, F32IO>(R, q, k, v, z, beta, ent_next, it_next % H, H, lane, wave);
         }
         __syncthreads();
 
@@ -444,18 +449,11 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
             if constexpr (F32IO) {
                 *reinterpret_cast<f32x4 *>(slab + SL::aqk + ((size_t)(I * 4 + J) * 64 + lane) * 16) = aq;
             } else {
-                const u32x2 hv = {f32x2_to_bf16x2(aq[0], aq[1]), f32x2_to_bf16x2(aq[2], aq[3])};
-                const f32x4 hq = f32x4{bf16_lo_half(hv[0]), bf16_hi_half(hv[0]), bf16_lo_half(hv[1]), bf16_hi_half(hv[1])};
-                const f32x4 r4 = aq - hq;
-                const u32x2 lv = {f32x2_to_bf16x2(r4[0], r4[1]), f32x2_to_bf16x2(r4[2], r4[3])};
                 const int qf = J >> 1, hh = J & 1;
-                unsigned char *base = slab + SL::aqk + ((size_t)((I * 2 + qf) * 2) * 64 + lane) * 16 + hh * 8;
-                *reinterpret_cast<u32x2 *>(base) = hv;
-                *reinterpret_cast<u32x2 *>(base + 64 * 16) = lv;
-                if (I == J && (I & 1) == 0) {  // the tile right of an even diagonal shares its fragment
+                unsigned char *base = slab + SL::aqk + ((size_t)(I * 2 + qf) * 64 + lane) * 16 + hh * 8;
+                *reinterpret_cast<u32x2 *>(base) = quad_to_f16(aq);
+                if (I == J && (I & 1) == 0)  // the tile right of an even diagonal shares its fragment
                     *reinterpret_cast<u32x2 *>(base + 8) = u32x2{0u, 0u};
-                    *reinterpret_cast<u32x2 *>(base + 64 * 16 + 8) = u32x2{0u, 0u};
-                }
             }
         }
 
@@ -473,7 +471,7 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
                 bf16_to_quads(*reinterpret_cast<const u32x4 *>(qr_row + f * 128), h0, h1);
                 bf16_to_quads(*reinterpret_cast<const u32x4 *>(qr_row + f * 128 + 64), l0, l1);
                 const int c0 = 32 * f + 4 * lg, c1 = c0 + 16;
-                store_split(dst, (h0 + l0) * ld4(&s.pfx[I][c0]), (h1 + l1) * ld4(&s.pfx[I][c1]));
+                store_f16(dst, (h0 + l0) * ld4(&s.pfx[I][c0]), (h1 + l1) * ld4(&s.pfx[I][c1]));
             }
         }
         for (int fr = wave; fr < KT * SL::NCF; fr += NW) {
@@ -485,8 +483,8 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
                 *reinterpret_cast<f32x4 *>(dst) = lds_col4(s.ke, 16 * J + 4 * lg, c) * s.sfx[J][c];
             } else {
                 const int J0 = 2 * f, J1 = 2 * f + 1;
-                store_split(dst, lds_col4(s.ke, 16 * J0 + 4 * lg, c) * s.sfx[J0][c],
-                            lds_col4(s.ke, 16 * J1 + 4 * lg, c) * s.sfx[J1][c]);
+                store_f16(dst, lds_col4(s.ke, 16 * J0 + 4 * lg, c) * s.sfx[J0][c],
+                          lds_col4(s.ke, 16 * J1 + 4 * lg, c) * s.sfx[J1][c]);
             }
         }
         __syncthreads();
@@ -497,11 +495,7 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
 #pragma unroll
             for (int kk = 0; kk < KH; ++kk)
                 *reinterpret_cast<f32x4 *>(&s.ke[row][16 * (half * KH + kk) + 4 * lg]) = vreg[kk];
-            if (it_next < total) {
-                intra_load<D, F32IO>(R, q, k, v, z, beta, ent_next, it_next % H, H, lane, wave);
-                ent = ent_next;
-                if (it_next + stride < total) ent_next = table[(it_next + stride) / H];
-            }
+            if (it_next < total) intra_load<D, F32IO>(R, q, k, v, z, beta, ent_next, it_next % H, H, lane, wave);
         } else {
 #pragma unroll
             for (int kk = 0; kk < KH; ++kk) {
@@ -553,14 +547,15 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
         }
 
         // ---- phase 4b (bf16 path): M = T Diag(beta), split once, in the
-        // fragment-row layout [row][J pair][hi, lo][lane group][8 bf16].
+        // fragment-row layout [row][J pair][hi, lo][lane group][8 bf16] with
+        // rows kMsRow bytes apart.
         if constexpr (!F32IO) {
             const int pj = half;
             const int c0 = 32 * pj + 4 * lg, c1 = c0 + 16;
             u32x4 mh, ml;
             quads_to_bf16_split(lds_quad(s.a, row, c0) * ld4(&s.beta[c0]),
                                 lds_quad(s.a, row, c1) * ld4(&s.beta[c1]), mh, ml);
-            unsigned char *b = msp + ((row * 2 + pj) * 2) * 64 + lg * 16;
+            unsigned char *b = msp + row * kMsRow + pj * 128 + lg * 16;
             *reinterpret_cast<u32x4 *>(b) = mh;
             *reinterpret_cast<u32x4 *>(b + 64) = ml;
             __syncthreads();
@@ -588,7 +583,7 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
                 f32x4 acc0 = zero4(), acc1 = zero4();
                 for (int pj = 0; pj < (nJ + 1) / 2; ++pj) {
                     const int cJ0 = 32 * pj + 4 * lg, cJ1 = cJ0 + 16;
-                    const unsigned char *mb = msp + (((16 * I + ln) * 2 + pj) * 2) * 64 + lg * 16;
+                    const unsigned char *mb = msp + (16 * I + ln) * kMsRow + pj * 128 + lg * 16;
                     const u32x4 mh = *reinterpret_cast<const u32x4 *>(mb);
                     const u32x4 ml = *reinterpret_cast<const u32x4 *>(mb + 64);
                     const u32x4 gah = cat2(lds_bf16x4(gkh, ca, cJ0), lds_bf16x4(gkh, ca, cJ1));
@@ -598,7 +593,7 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
                     acc0 = mma3_bf16(gah, gal, mh, ml, acc0);
                     acc1 = mma3_bf16(gbh, gbl, mh, ml, acc1);
                 }
-                store_split(slab + SL::negW + ((size_t)(I * SL::NKF + tp) * 2 * 64 + lane) * 16, -acc0, -acc1);
+                store_f16(slab + SL::negW + ((size_t)(I * SL::NKF + tp) * 64 + lane) * 16, -acc0, -acc1);
             }
         }
         // U tile (I, w) = sum_J M_{IJ} V_{Jw}, in the accumulator layout the
@@ -616,7 +611,7 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
             } else {
                 for (int pj = 0; pj < (nJ + 1) / 2; ++pj) {
                     const int cJ0 = 32 * pj + 4 * lg, cJ1 = cJ0 + 16;
-                    const unsigned char *mb = msp + (((16 * I + ln) * 2 + pj) * 2) * 64 + lg * 16;
+                    const unsigned char *mb = msp + (16 * I + ln) * kMsRow + pj * 128 + lg * 16;
                     const u32x4 vb = cat2(lds_bf16x4(s.vt, 16 * w + ln, cJ0), lds_bf16x4(s.vt, 16 * w + ln, cJ1));
                     acc = mma_bf16_k32(*reinterpret_cast<const u32x4 *>(mb), vb, acc);
                     acc = mma_bf16_k32(*reinterpret_cast<const u32x4 *>(mb + 64), vb, acc);
@@ -624,6 +619,9 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
             }
             *reinterpret_cast<f32x4 *>(slab + SL::u + ((size_t)(I * KT + w) * 64 + lane) * 16) = acc;
         }
+        ent = ent_next;
+        ent_next = ent_after;
+        a_cur = a_next;
         __syncthreads();
     }
 }
@@ -631,16 +629,21 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
 // ---------------------------------------------------------------------------
 // Inter-chunk kernel.  Wave w of a workgroup owns value columns
 // [16 vt, 16 vt + 16) of one (sequence, head); its state slice S[:, cols]
-// lives in DK/16 accumulator tiles (lane (n, g) holds S[16t + 4g + j][16vt + n]).
+// lives in DK/16 fp32 accumulator tiles (lane (n, g) holds S[16t + 4g + j][16vt + n]).
 // Per chunk, in the order of the chunk form:
-//   phase A:  V' = U - W S,   O = (Gamma*Q) S                    (-W, Gamma*Q from LDS A)
-//   phase B:  O += A_qk V',   S = Diag(gamma_C) S + K~^T V'       (A_qk, K~^T, gamma from LDS B)
-// Every bf16 operand (stored fragments and the S, V' accumulators) enters
-// the MFMAs split into hi + lo parts; each product is hi*hi + hi*lo + lo*hi.
-// The shared operands reach LDS by direct global->LDS copies
-// (global_load_lds_dwordx4, one 1 KiB fragment per wave instruction): region B
-// of this chunk streams in during phase A, region A of the next chunk during
-// phase B.
+//   V' = U - W S,   O = (Gamma*Q) S + A_qk V',   S = Diag(gamma_C) S + K~^T V'
+// Value columns are independent, so each wave may scale its own S and V'
+// slices: bf16 path, S and V' are multiplied by a power of two chosen from
+// the wave's largest magnitude, rounded to fp16 for the MFMAs (fp16 stored
+// operands, fp32 accumulation), and the products are scaled back exactly.
+// The fp32 path uses fp32 MFMA and no scaling.
+//
+// Staging: the operands every wave shares (-W, Gamma*Q, K~^T, A_qk, gamma)
+// reach LDS by direct global->LDS copies (global_load_lds_dwordx4, one 1 KiB
+// fragment per wave instruction).  bf16 path: two whole-chunk buffers, the
+// next chunk streams in while this one computes.  fp32 path (larger
+// fragments): region B of this chunk streams during phase A, region A of the
+// next chunk during phase B.
 // ---------------------------------------------------------------------------
 template <int D, bool F32IO>
 struct InterShape {
@@ -648,7 +651,8 @@ struct InterShape {
     static constexpr int KT = D / 16;
     static constexpr int WPG = KT < 4 ? KT : 4;          // waves per workgroup
     static constexpr int NT = 64 * WPG;
-    static constexpr size_t lds_bytes = (size_t)(SL::FA + SL::FB) * SL::FRAG;
+    static constexpr int NBUF = F32IO ? 1 : 2;
+    static constexpr size_t lds_bytes = (size_t)NBUF * (SL::FA + SL::FB) * SL::FRAG;
 };
 
 // Copy `nfrag` consecutive 1 KiB fragments from global `src` to LDS `dst`,
@@ -662,8 +666,31 @@ __device__ __forceinline__ void copy_frags_to_lds(const unsigned char *src, unsi
 
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Store a finished 64 x 16 output tile (accumulator layout) for rows < L.
+template <bool F32IO>
+__device__ __forceinline__ void store_o_tile(void *o, const f32x4 (&acc)[4], int t0, int L, int H, int h,
+                                             int D, int col, int lg) {
+    const size_t rstride = (size_t)H * D;
+    const size_t base = ((size_t)t0 * H + h) * D + col;
+    if (L >= 64) {
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                store_io<F32IO>(o, base + (size_t)(16 * I + 4 * lg + j) * rstride, acc[I][j]);
+    } else {
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * I + 4 * lg + j;
+                if (r < L) store_io<F32IO>(o, base + (size_t)r * rstride, acc[I][j]);
+            }
+    }
+}
+
 template <int D, bool F32IO>
-__global__ void __launch_bounds__(256) inter_kernel(
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) inter_kernel(
     const float *__restrict__ h0, const int32_t *__restrict__ meta, const int4 *__restrict__ table,
     int N, int H, int max_chunks, const unsigned char *__restrict__ slabs, size_t slab_stride,
     void *__restrict__ o, float *__restrict__ hT, int groups) {
@@ -671,9 +698,8 @@ __global__ void __launch_bounds__(256) inter_kernel(
     using SHP = InterShape<D, F32IO>;
     constexpr int KT = D / 16;
     constexpr int WPG = SHP::WPG;
+    constexpr size_t BUF = (size_t)(SL::FA + SL::FB) * SL::FRAG;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
-    unsigned char *bufA = lds_raw;                       // [-W | Gamma*Q]
-    unsigned char *bufB = lds_raw + SL::FA * SL::FRAG;   // [K~^T | A_qk | gamma]
 
     // blockIdx -> (pair, column group) with every group of a pair on the same XCD
     const int b = blockIdx.x;
@@ -701,123 +727,152 @@ __global__ void __launch_bounds__(256) inter_kernel(
 #pragma unroll
         for (int I = 0; I < 4; ++I) dst[I] = us[(I * KT + vt) * 64 + lane];
     };
-    // this lane's 16 bytes of fragment idx in an LDS region
-    auto fa = [&](size_t off, int idx) -> u32x4 {
-        return *reinterpret_cast<const u32x4 *>(bufA + off + ((size_t)idx * 64 + lane) * 16);
+    // region A = [-W | Gamma*Q], region B = [K~^T | A_qk | gamma] of a buffer
+    auto copy_A = [&](int c, unsigned char *buf) { copy_frags_to_lds(slab_of(c), buf, SL::FA, wave, WPG, lane); };
+    auto copy_B = [&](int c, unsigned char *buf) {
+        unsigned char *bb = buf + SL::FA * SL::FRAG;
+        copy_frags_to_lds(slab_of(c) + SL::kdT, bb, SL::FB - 1, wave, WPG, lane);
+        copy_frags_to_lds(slab_of(c) + SL::gamma, bb + (SL::FB - 1) * SL::FRAG, 1, wave, WPG, lane);
     };
-    auto fb = [&](size_t off, int idx) -> u32x4 {
-        return *reinterpret_cast<const u32x4 *>(bufB + (off - SL::kdT) + ((size_t)idx * 64 + lane) * 16);
+    // this lane's 16 bytes of fragment idx of the region at slab offset `off`
+    auto frag = [&](const unsigned char *buf, size_t off, int idx) -> u32x4 {
+        const size_t pos = off < SL::kdT ? off : SL::FA * SL::FRAG + (off - SL::kdT);
+        return *reinterpret_cast<const u32x4 *>(buf + pos + ((size_t)idx * 64 + lane) * 16);
     };
-    const f32x4 *gam = reinterpret_cast<const f32x4 *>(bufB + (SL::FB - 1) * SL::FRAG);
+    auto gamma_of = [&](const unsigned char *buf) {
+        return reinterpret_cast<const f32x4 *>(buf + (SL::FA + SL::FB - 1) * SL::FRAG);
+    };
 
     f32x4 u[4], un[4];
     f32x4 acc_o[4];
     int o_t0 = 0, o_L = 0;     // pending output of the previous chunk
-    if (c_begin < c_end) {
-        copy_frags_to_lds(slab_of(c_begin), bufA, SL::FA, wave, WPG, lane);
-        load_u(c_begin, u);
-    }
-    wait_all_memory();
-    __syncthreads();
-    for (int c = c_begin; c < c_end; ++c) {
-        const unsigned char *sc = slab_of(c);
-        copy_frags_to_lds(sc + SL::kdT, bufB, SL::FB - 1, wave, WPG, lane);            // K~^T, A_qk
-        copy_frags_to_lds(sc + SL::gamma, bufB + (SL::FB - 1) * SL::FRAG, 1, wave, WPG, lane);  // gamma
-        if (c + 1 < c_end) load_u(c + 1, un);
-        // the previous chunk's output rows
-        if (o_L > 0) {
+
+    if constexpr (!F32IO) {
+        // ------------------------------------------------------------- bf16 path
+        if (c_begin < c_end) {
+            copy_A(c_begin, lds_raw);
+            copy_B(c_begin, lds_raw);
+            load_u(c_begin, u);
+        }
+        wait_all_memory();
+        __syncthreads();
+        for (int c = c_begin; c < c_end; ++c) {
+            const unsigned char *buf = lds_raw + ((c - c_begin) & 1) * BUF;
+            unsigned char *nbuf = lds_raw + (((c - c_begin) & 1) ^ 1) * BUF;
+            if (c + 1 < c_end) {
+                copy_A(c + 1, nbuf);
+                copy_B(c + 1, nbuf);
+                load_u(c + 1, un);
+            }
+            if (o_L > 0) store_o_tile<F32IO>(o, acc_o, o_t0, o_L, H, h, D, col, lg);
+            const int4 ent = table[c];
+
+            // S -> fp16 with a per-wave power-of-two scale
+            float m = 0.f;
+#pragma unroll
+            for (int t = 0; t < KT; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(S[t][j]));
+            const int eS = scale_exp(wave_max_nonneg(m));
+            const float dS = exp2i(-eS), uS = exp2i(eS);
+            u32x4 sf[KT / 2];
+#pragma unroll
+            for (int p = 0; p < KT / 2; ++p) sf[p] = quads_to_f16(S[2 * p] * dS, S[2 * p + 1] * dS);
+
+            f32x4 vp[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                f32x4 ws = zero4(), qs = zero4();
+#pragma unroll
+                for (int p = 0; p < KT / 2; ++p) {
+                    ws = mma_f16_k32(frag(buf, SL::negW, I * (KT / 2) + p), sf[p], ws);
+                    qs = mma_f16_k32(frag(buf, SL::qg, I * (KT / 2) + p), sf[p], qs);
+                }
+                vp[I] = u[I] + ws * uS;
+                acc_o[I] = qs * uS;
+            }
+
+            // V' -> fp16 with its own per-wave scale
+            m = 0.f;
 #pragma unroll
             for (int I = 0; I < 4; ++I)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * I + 4 * lg + j;
-                    if (r < o_L) store_io<F32IO>(o, ((size_t)(o_t0 + r) * H + h) * D + col, acc_o[I][j]);
-                }
-        }
-        const int4 ent = table[c];
+                for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(vp[I][j]));
+            const int eV = scale_exp(wave_max_nonneg(m));
+            const float dV = exp2i(-eV), uV = exp2i(eV);
+            const u32x4 vf0 = quads_to_f16(vp[0] * dV, vp[1] * dV);
+            const u32x4 vf1 = quads_to_f16(vp[2] * dV, vp[3] * dV);
 
-        // ---- phase A
-        f32x4 vp[4];
-        if constexpr (F32IO) {
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                f32x4 a = mma_f16_k32(frag(buf, SL::aqk, I * 2), vf0, zero4());
+                if (I >= 2) a = mma_f16_k32(frag(buf, SL::aqk, I * 2 + 1), vf1, a);
+                acc_o[I] += a * uV;
+            }
+            const f32x4 *gam = gamma_of(buf);
+#pragma unroll
+            for (int t = 0; t < KT; ++t) {
+                f32x4 a = mma_f16_k32(frag(buf, SL::kdT, t * 2), vf0, zero4());
+                a = mma_f16_k32(frag(buf, SL::kdT, t * 2 + 1), vf1, a);
+                S[t] = S[t] * gam[4 * t + lg] + a * uV;
+            }
+            o_t0 = ent.y;
+            o_L = ent.z;
+            wait_all_memory();
+            __syncthreads();
+#pragma unroll
+            for (int I = 0; I < 4; ++I) u[I] = un[I];
+        }
+    } else {
+        // ------------------------------------------------------------- fp32 path
+        unsigned char *buf = lds_raw;
+        if (c_begin < c_end) {
+            copy_A(c_begin, buf);
+            load_u(c_begin, u);
+        }
+        wait_all_memory();
+        __syncthreads();
+        for (int c = c_begin; c < c_end; ++c) {
+            copy_B(c, buf);
+            if (c + 1 < c_end) load_u(c + 1, un);
+            if (o_L > 0) store_o_tile<F32IO>(o, acc_o, o_t0, o_L, H, h, D, col, lg);
+            const int4 ent = table[c];
+            f32x4 vp[4];
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 vp[I] = u[I];
                 acc_o[I] = zero4();
 #pragma unroll
                 for (int t = 0; t < KT; ++t) {
-                    vp[I] = mma_f32_k16(__builtin_bit_cast(f32x4, fa(SL::negW, I * KT + t)), S[t], vp[I]);
-                    acc_o[I] = mma_f32_k16(__builtin_bit_cast(f32x4, fa(SL::qg, I * KT + t)), S[t], acc_o[I]);
+                    vp[I] = mma_f32_k16(__builtin_bit_cast(f32x4, frag(buf, SL::negW, I * KT + t)), S[t], vp[I]);
+                    acc_o[I] = mma_f32_k16(__builtin_bit_cast(f32x4, frag(buf, SL::qg, I * KT + t)), S[t], acc_o[I]);
                 }
             }
-        } else {
-            u32x4 shi[KT / 2], slo[KT / 2];
-#pragma unroll
-            for (int p = 0; p < KT / 2; ++p) quads_to_bf16_split(S[2 * p], S[2 * p + 1], shi[p], slo[p]);
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                vp[I] = u[I];
-                acc_o[I] = zero4();
-#pragma unroll
-                for (int p = 0; p < KT / 2; ++p) {
-                    const int fi = (I * (KT / 2) + p) * 2;
-                    vp[I] = mma3_bf16(fa(SL::negW, fi), fa(SL::negW, fi + 1), shi[p], slo[p], vp[I]);
-                    acc_o[I] = mma3_bf16(fa(SL::qg, fi), fa(SL::qg, fi + 1), shi[p], slo[p], acc_o[I]);
-                }
-            }
-        }
-        wait_all_memory();
-        __syncthreads();
-        if (c + 1 < c_end) copy_frags_to_lds(slab_of(c + 1), bufA, SL::FA, wave, WPG, lane);
-
-        // ---- phase B
-        if constexpr (F32IO) {
+            wait_all_memory();
+            __syncthreads();
+            if (c + 1 < c_end) copy_A(c + 1, buf);
 #pragma unroll
             for (int I = 0; I < 4; ++I)
 #pragma unroll
                 for (int J = 0; J <= I; ++J)
-                    acc_o[I] = mma_f32_k16(__builtin_bit_cast(f32x4, fb(SL::aqk, I * 4 + J)), vp[J], acc_o[I]);
+                    acc_o[I] = mma_f32_k16(__builtin_bit_cast(f32x4, frag(buf, SL::aqk, I * 4 + J)), vp[J], acc_o[I]);
+            const f32x4 *gam = gamma_of(buf);
 #pragma unroll
             for (int t = 0; t < KT; ++t) {
                 S[t] = S[t] * gam[4 * t + lg];
 #pragma unroll
                 for (int J = 0; J < 4; ++J)
-                    S[t] = mma_f32_k16(__builtin_bit_cast(f32x4, fb(SL::kdT, t * 4 + J)), vp[J], S[t]);
+                    S[t] = mma_f32_k16(__builtin_bit_cast(f32x4, frag(buf, SL::kdT, t * 4 + J)), vp[J], S[t]);
             }
-        } else {
-            u32x4 vh[2], vl[2];
-            quads_to_bf16_split(vp[0], vp[1], vh[0], vl[0]);
-            quads_to_bf16_split(vp[2], vp[3], vh[1], vl[1]);
+            o_t0 = ent.y;
+            o_L = ent.z;
+            wait_all_memory();
+            __syncthreads();
 #pragma unroll
-            for (int I = 0; I < 4; ++I)
-#pragma unroll
-                for (int qf = 0; qf <= I / 2; ++qf)
-                    acc_o[I] = mma3_bf16(fb(SL::aqk, (I * 2 + qf) * 2), fb(SL::aqk, (I * 2 + qf) * 2 + 1),
-                                         vh[qf], vl[qf], acc_o[I]);
-#pragma unroll
-            for (int t = 0; t < KT; ++t) {
-                S[t] = S[t] * gam[4 * t + lg];
-#pragma unroll
-                for (int qf = 0; qf < 2; ++qf)
-                    S[t] = mma3_bf16(fb(SL::kdT, (t * 2 + qf) * 2), fb(SL::kdT, (t * 2 + qf) * 2 + 1),
-                                     vh[qf], vl[qf], S[t]);
-            }
+            for (int I = 0; I < 4; ++I) u[I] = un[I];
         }
-        o_t0 = ent.y;
-        o_L = ent.z;
-        wait_all_memory();
-        __syncthreads();
-#pragma unroll
-        for (int I = 0; I < 4; ++I) u[I] = un[I];
     }
-    if (o_L > 0) {
-#pragma unroll
-        for (int I = 0; I < 4; ++I)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * I + 4 * lg + j;
-                if (r < o_L) store_io<F32IO>(o, ((size_t)(o_t0 + r) * H + h) * D + col, acc_o[I][j]);
-            }
-    }
+    if (o_L > 0) store_o_tile<F32IO>(o, acc_o, o_t0, o_L, H, h, D, col, lg);
     if (hT) {
 #pragma unroll
         for (int t = 0; t < KT; ++t) *reinterpret_cast<f32x4 *>(hT + srow + 16 * t + 4 * lg) = S[t];
