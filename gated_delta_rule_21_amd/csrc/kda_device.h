@@ -188,4 +188,24 @@ __device__ __forceinline__ f32x4 mma3_bf16(u32x4 ah, u32x4 al, u32x4 bh, u32x4 b
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Transpose of a 16x16 accumulator tile, rounded to bf16: the tile enters a
+// 16x16x16 bf16 MFMA as its own A operand (lane (n, g) holds X[4g + j][n],
+// which is the A layout of X^T) against the identity, so the result lane
+// (n, g) holds X[n][4g + j] -- four consecutive columns of row n.  Exact for
+// finite values (each product is a bf16 value times 1 or 0); a non-finite
+// entry turns its whole row non-finite (inf * 0).
+__device__ __forceinline__ u32x2 transpose_tile_bf16(f32x4 x, int lane) {
+    const int n = lane & 15, g = lane >> 4;
+    const u32x2 a = u32x2{f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3])};
+    // identity B operand: lane (n, g) holds I[4g + j][n]
+    const uint32_t one = 0x3f80u;  // bf16 1.0
+    uint32_t e[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) e[j] = (4 * g + j == n) ? one : 0u;
+    const u32x2 b = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+    const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                             __builtin_bit_cast(s16x4, b), zero4(), 0, 0, 0);
+    return u32x2{f32x2_to_bf16x2(d[0], d[1]), f32x2_to_bf16x2(d[2], d[3])};
+}
+
 }  // namespace kda

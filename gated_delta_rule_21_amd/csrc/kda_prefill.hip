@@ -652,7 +652,10 @@ struct InterShape {
     static constexpr int WPG = KT < 4 ? KT : 4;          // waves per workgroup
     static constexpr int NT = 64 * WPG;
     static constexpr int NBUF = F32IO ? 1 : 2;
-    static constexpr size_t lds_bytes = (size_t)NBUF * (SL::FA + SL::FB) * SL::FRAG;
+    // bf16 path: two output staging tiles of 64 rows x (16 * WPG) bf16 columns
+    static constexpr int OPITCH = 16 * WPG + 8;                  // bf16 elements per staged row
+    static constexpr size_t obuf_bytes = F32IO ? 0 : (size_t)64 * OPITCH * 2;
+    static constexpr size_t lds_bytes = (size_t)NBUF * (SL::FA + SL::FB) * SL::FRAG + 2 * obuf_bytes;
 };
 
 // Copy `nfrag` consecutive 1 KiB fragments from global `src` to LDS `dst`,
@@ -749,6 +752,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 
     if constexpr (!F32IO) {
         // ------------------------------------------------------------- bf16 path
+        // Output rows go out as whole 16 * WPG-column segments: each wave
+        // transposes its 64 x 16 tile in registers, stages it in LDS, and after
+        // the next barrier every lane stores 16-byte pieces of full rows.
+        constexpr int OP = SHP::OPITCH;
+        uint16_t *obuf = reinterpret_cast<uint16_t *>(lds_raw + SHP::NBUF * BUF);
+        auto flush_o = [&](int par, int t0, int L) {
+            const uint16_t *ob = obuf + par * 64 * OP;
+            constexpr int SEG = 16 * WPG / 8;                   // 16-byte pieces per row
+            for (int i = tid; i < 64 * SEG; i += SHP::NT) {
+                const int r = i / SEG, sgm = i % SEG;
+                if (r < L)
+                    *reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(o) +
+                                               ((size_t)(t0 + r) * H + h) * D + 16 * WPG * cg + 8 * sgm) =
+                        *reinterpret_cast<const u32x4 *>(ob + r * OP + 8 * sgm);
+            }
+        };
         if (c_begin < c_end) {
             copy_A(c_begin, lds_raw);
             copy_B(c_begin, lds_raw);
@@ -757,14 +776,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
         wait_all_memory();
         __syncthreads();
         for (int c = c_begin; c < c_end; ++c) {
-            const unsigned char *buf = lds_raw + ((c - c_begin) & 1) * BUF;
-            unsigned char *nbuf = lds_raw + (((c - c_begin) & 1) ^ 1) * BUF;
+            const int par = (c - c_begin) & 1;
+            const unsigned char *buf = lds_raw + par * BUF;
+            unsigned char *nbuf = lds_raw + (par ^ 1) * BUF;
             if (c + 1 < c_end) {
                 copy_A(c + 1, nbuf);
                 copy_B(c + 1, nbuf);
                 load_u(c + 1, un);
             }
-            if (o_L > 0) store_o_tile<F32IO>(o, acc_o, o_t0, o_L, H, h, D, col, lg);
+            if (o_L > 0) flush_o(par ^ 1, o_t0, o_L);   // the previous chunk's rows
             const int4 ent = table[c];
 
             // S -> fp16 with a per-wave power-of-two scale
@@ -803,11 +823,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             const u32x4 vf0 = quads_to_f16(vp[0] * dV, vp[1] * dV);
             const u32x4 vf1 = quads_to_f16(vp[2] * dV, vp[3] * dV);
 
+            uint16_t *ob = obuf + par * 64 * OP;
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 f32x4 a = mma_f16_k32(frag(buf, SL::aqk, I * 2), vf0, zero4());
                 if (I >= 2) a = mma_f16_k32(frag(buf, SL::aqk, I * 2 + 1), vf1, a);
                 acc_o[I] += a * uV;
+                *reinterpret_cast<u32x2 *>(ob + (16 * I + ln) * OP + 16 * wave + 4 * lg) =
+                    transpose_tile_bf16(acc_o[I], lane);
             }
             const f32x4 *gam = gamma_of(buf);
 #pragma unroll
@@ -823,6 +846,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
             for (int I = 0; I < 4; ++I) u[I] = un[I];
         }
+        if (o_L > 0) flush_o((c_end - c_begin - 1) & 1, o_t0, o_L);
+        o_L = 0;
     } else {
         // ------------------------------------------------------------- fp32 path
         unsigned char *buf = lds_raw;
