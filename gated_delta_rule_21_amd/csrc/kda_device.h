@@ -126,6 +126,7 @@ __device__ __forceinline__ void quads_to_bf16_split(f32x4 x0, f32x4 x1, u32x4 &h
 // ---------------------------------------------------------------------------
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t f32x2_to_f16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
@@ -136,6 +137,10 @@ __device__ __forceinline__ u32x4 quads_to_f16(f32x4 x0, f32x4 x1) {
 }
 __device__ __forceinline__ u32x2 quad_to_f16(f32x4 x) {
     return u32x2{f32x2_to_f16x2(x[0], x[1]), f32x2_to_f16x2(x[2], x[3])};
+}
+// fp32 values of four packed fp16 (exact).
+__device__ __forceinline__ f32x4 f16x4_to_quad(u32x2 w) {
+    return __builtin_convertvector(__builtin_bit_cast(f16x4, w), f32x4);
 }
 __device__ __forceinline__ f32x4 mma_f16_k32(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),

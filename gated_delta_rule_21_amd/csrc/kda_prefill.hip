@@ -44,7 +44,9 @@ namespace kda {
 // 16x16x32 MFMA); they are bounded by construction (|Gamma*Q|, |K~| <= 1,
 // W and A_qk are products of contractions), and the state-carrying side of
 // every chain product is scaled by a power of two per chunk before it is
-// rounded to fp16.  U stays fp32.
+// rounded to fp16.  U is stored per 16x16 tile in fp16 times 2^-e, with the
+// tile's exponent e (from its largest magnitude) kept after gamma_C.  Of
+// A_qk's 8 fp16 fragments only the 6 that are not all zero are stored.
 // ---------------------------------------------------------------------------
 template <int D, bool F32>
 struct Slab {
@@ -52,20 +54,28 @@ struct Slab {
     static constexpr int NKF = F32 ? D / 16 : D / 32; // fragments over d per 16-row tile
     static constexpr int NCF = F32 ? 4 : 2;           // fragments over the 64 chunk rows
     static constexpr int SPL = 1;                     // one fragment per operand tile (fp32 or fp16)
+    static constexpr int NAQ = F32 ? 4 * NCF : 6;     // A_qk fragments stored
     static constexpr size_t FRAG = 1024;
+    static constexpr size_t UT = F32 ? FRAG : FRAG / 2;         // bytes per U tile
     static constexpr size_t negW = 0;                           // -W      [I][NKF][SPL]
     static constexpr size_t qg = negW + 4 * NKF * SPL * FRAG;   // Gamma*Q [I][NKF][SPL]
     static constexpr size_t kdT = qg + 4 * NKF * SPL * FRAG;    // ((gamma_C/Gamma)*K)^T [t][NCF][SPL]
-    static constexpr size_t aqk = kdT + KT * NCF * SPL * FRAG;  // A_qk    [I][NCF][SPL]
-    static constexpr size_t u = aqk + 4 * NCF * SPL * FRAG;     // U (fp32 accumulator layout) [I][KT]
-    static constexpr size_t gamma = u + 4 * KT * FRAG;          // gamma_C [D] fp32, in one fragment
-    static constexpr size_t bytes = gamma + FRAG;
-    // The inter-chunk kernel stages two regions through LDS: A = [-W | Gamma*Q]
-    // and B = [K~^T | A_qk | gamma], each a whole number of fragments.
-    static constexpr int FA = (int)(qg - negW + (kdT - qg)) / (int)FRAG;
-    static constexpr int FB = (int)((u - kdT) / FRAG) + 1;   // + the gamma fragment
-    static_assert(D * 4 <= (int)FRAG, "gamma fits one fragment");
+    static constexpr size_t aqk = kdT + KT * NCF * SPL * FRAG;  // A_qk    [NAQ]
+    static constexpr size_t gamma = aqk + NAQ * FRAG;           // gamma_C [D] fp32, then
+    static constexpr size_t uexp = gamma + D * 4;               //   U tile exponents [I][KT] int32 (bf16)
+    static constexpr size_t u = gamma + FRAG;                   // U (accumulator layout) [I][KT]
+    static constexpr size_t bytes = u + 4 * KT * UT;
+    // The inter-chunk kernel stages two regions through LDS, A = [-W | Gamma*Q]
+    // and B = [K~^T | A_qk | gamma], each a whole number of fragments; an LDS
+    // buffer holds them at their slab offsets.  U goes to registers.
+    static constexpr int FA = (int)((kdT - negW) / FRAG);
+    static constexpr int FB = (int)((u - kdT) / FRAG);
+    static_assert(D * 4 + 4 * KT * 4 <= (int)FRAG, "gamma and the U exponents fit one fragment");
 };
+
+// A_qk fragment index (bf16 path) of row tile I, column pair qf: tiles 0 and
+// 1 need one fragment, tiles 2 and 3 two.
+__device__ __forceinline__ int aqk_frag(int I, int qf) { return I < 2 ? I : 2 * I - 2 + qf; }
 
 // Store two fp32 quads (K16 tiles t, t + 1) as one fp16 fragment.
 __device__ __forceinline__ void store_f16(unsigned char *dst, f32x4 x0, f32x4 x1) {
@@ -220,14 +230,18 @@ constexpr int kIntraWaves = 8;
 constexpr int kMsRow = 2 * 128 + 16;
 
 // Raw inputs of one (chunk, head) item for one lane of an 8-wave group:
-// wave w loads row block (w & 3), key-channel half (w >> 2).
+// wave w loads row block (w & 3), key-channel half (w >> 2).  Lanes whose
+// row lies past the chunk's end load the chunk's first row instead; the
+// consumer masks them.  Every load is unconditional and issued in the order
+// of use, so a wait for one prefetched register never has to cover the
+// stores issued after the prefetch.
 template <int D, bool F32IO>
 struct IntraRegs {
     static constexpr int KH = D / 32;  // K16 tiles per channel half
     using Q = typename std::conditional<F32IO, f32x4, u32x2>::type;
+    float beta;
     f32x4 z[KH];
     Q k[KH], q[KH], v[KH];
-    float beta;
 };
 
 template <int D, bool F32IO>
@@ -239,27 +253,32 @@ __device__ __forceinline__ void intra_load(IntraRegs<D, F32IO> &R, const void *q
     using Q = typename IntraRegs<D, F32IO>::Q;
     const int ln = lane & 15, lg = lane >> 4;
     const int row = 16 * (wave & 3) + ln;
-    const bool ok = row < ent.z;
-    const size_t base = ((size_t)(ent.y + (ok ? row : 0)) * H + h) * D + (D / 2) * (wave >> 2) + 4 * lg;
+    const size_t trow = (size_t)(ent.y + (row < ent.z ? row : 0)) * H + h;
+    const size_t base = trow * D + (D / 2) * (wave >> 2) + 4 * lg;
     const unsigned char *kb = reinterpret_cast<const unsigned char *>(k);
     const unsigned char *qb = reinterpret_cast<const unsigned char *>(q);
     const unsigned char *vb = reinterpret_cast<const unsigned char *>(v);
+    R.beta = beta[trow];
 #pragma unroll
     for (int kk = 0; kk < KH; ++kk) {
         const size_t idx = base + 16 * kk;
-        if (ok) {
-            R.z[kk] = ld4(z + idx);
-            R.k[kk] = *reinterpret_cast<const Q *>(kb + idx * ES);
-            R.q[kk] = *reinterpret_cast<const Q *>(qb + idx * ES);
-            R.v[kk] = *reinterpret_cast<const Q *>(vb + idx * ES);
-        } else {
-            R.z[kk] = zero4();
-            R.k[kk] = Q{};
-            R.q[kk] = Q{};
-            R.v[kk] = Q{};
-        }
+        R.z[kk] = ld4(z + idx);
+        R.k[kk] = *reinterpret_cast<const Q *>(kb + idx * ES);
+        R.q[kk] = *reinterpret_cast<const Q *>(qb + idx * ES);
+        R.v[kk] = *reinterpret_cast<const Q *>(vb + idx * ES);
     }
-    R.beta = (ok && lg == 0 && wave < 4) ? beta[(size_t)(ent.y + row) * H + h] : 0.f;
+}
+
+// Units [0, n) spread over NW waves with a trip count fixed at compile time
+// (only the last pass is conditional, and only when NW does not divide n),
+// so the number of stores a wave has in flight is known to the compiler.
+template <int n, int NW, typename F>
+__device__ __forceinline__ void for_wave_units(int wave, F &&f) {
+#pragma unroll
+    for (int r = 0; r < (n + NW - 1) / NW; ++r) {
+        const int unit = wave + r * NW;
+        if (n % NW == 0 || unit < n) f(unit);
+    }
 }
 
 template <bool F32IO, typename Q>
@@ -304,7 +323,7 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
     unsigned char *msp = reinterpret_cast<unsigned char *>(&s.ke[0][0]);          // bf16 path: M split
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index in an SGPR
     const int ln = lane & 15, lg = lane >> 4;
     const int blk = wave & 3, half = wave >> 2;   // phase-1 ownership: row block, channel half
     const int total = meta[N] * H;
@@ -315,6 +334,10 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
     IntraRegs<D, F32IO> R;
     int4 ent = table[it / H];
     intra_load<D, F32IO>(R, q, k, v, z, beta, ent, it % H, H, lane, wave);
+    // Nothing else is in flight here: settle these loads so that the waits at
+    // the loop head are set by the loop body alone, where the previous item's
+    // stores stay in flight behind the prefetched loads.
+    __builtin_amdgcn_s_waitcnt(0);
     // Chunk-table entries and A_h are read through the scalar cache, whose
     // loads every barrier waits for: fetch them one item ahead of their use.
     int4 ent_next = (it + stride < total) ? table[(it + stride) / H] : make_int4(0, 0, 0, 0);
@@ -333,15 +356,15 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
 
         // ---- phase 1: gate, block-local cumulative log2-decay, row operands
         for (int i = tid; i < 64 * 68; i += NTH) (&s.a[0][0])[i] = 0.f;
-        if (lg == 0 && wave < 4) s.beta[row] = R.beta;
+        if (lg == 0 && wave < 4) s.beta[row] = ok ? R.beta : 0.f;
         f32x4 krv[KH], qrv[KH], vreg[KH];
 #pragma unroll
         for (int kk = 0; kk < KH; ++kk) {
             const int kt = half * KH + kk;
             const int c0 = 16 * kt + 4 * lg;
-            const f32x4 kq = quad_f32<F32IO>(R.k[kk]);
-            const f32x4 qq = quad_f32<F32IO>(R.q[kk]);
-            vreg[kk] = quad_f32<F32IO>(R.v[kk]);
+            const f32x4 kq = ok ? quad_f32<F32IO>(R.k[kk]) : zero4();
+            const f32x4 qq = ok ? quad_f32<F32IO>(R.q[kk]) : zero4();
+            vreg[kk] = ok ? quad_f32<F32IO>(R.v[kk]) : zero4();
             f32x4 gl, bt, rf, kev;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -360,7 +383,7 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
             } else {
                 store_row_split<RB>(s.krs, row, kt, lg, krv[kk]);
                 store_row_split<RB>(s.qrs, row, kt, lg, qrv[kk]);
-                const u32x2 vv = R.v[kk];
+                const u32x2 vv = ok ? R.v[kk] : u32x2{0u, 0u};
                 s.vt[c0 + 0][row] = (uint16_t)(vv[0] & 0xffffu);
                 s.vt[c0 + 1][row] = (uint16_t)(vv[0] >> 16);
                 s.vt[c0 + 2][row] = (uint16_t)(vv[1] & 0xffffu);
@@ -403,7 +426,7 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
         // block I) x (ke of block J) x factor: exp2(-bt_J) on the diagonal block
         // (the <= e^80 case), the decay of the blocks strictly between J and I
         // otherwise (<= 1).
-        for (int tile = wave; tile < 10; tile += NW) {
+        for_wave_units<10, NW>(wave, [&](int tile) {
             const int I = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
             const int J = tile - (I * (I + 1)) / 2;
             const float *fac = (I == J) ? s.dg[J] : s.off[off_index(J, I)];
@@ -450,16 +473,16 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
                 *reinterpret_cast<f32x4 *>(slab + SL::aqk + ((size_t)(I * 4 + J) * 64 + lane) * 16) = aq;
             } else {
                 const int qf = J >> 1, hh = J & 1;
-                unsigned char *base = slab + SL::aqk + ((size_t)(I * 2 + qf) * 64 + lane) * 16 + hh * 8;
+                unsigned char *base = slab + SL::aqk + ((size_t)aqk_frag(I, qf) * 64 + lane) * 16 + hh * 8;
                 *reinterpret_cast<u32x2 *>(base) = quad_to_f16(aq);
                 if (I == J && (I & 1) == 0)  // the tile right of an even diagonal shares its fragment
                     *reinterpret_cast<u32x2 *>(base + 8) = u32x2{0u, 0u};
             }
-        }
+        });
 
         // Gamma*Q fragments (row tile I, key fragment f) and the transposed,
         // end-of-chunk-decayed keys ((gamma_C/Gamma)*K)^T (key tile t, row fragment f).
-        for (int fr = wave; fr < 4 * SL::NKF; fr += NW) {
+        for_wave_units<4 * SL::NKF, NW>(wave, [&](int fr) {
             const int I = fr / SL::NKF, f = fr % SL::NKF;
             unsigned char *dst = slab + SL::qg + ((size_t)fr * SL::SPL * 64 + lane) * 16;
             if constexpr (F32IO) {
@@ -473,8 +496,8 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
                 const int c0 = 32 * f + 4 * lg, c1 = c0 + 16;
                 store_f16(dst, (h0 + l0) * ld4(&s.pfx[I][c0]), (h1 + l1) * ld4(&s.pfx[I][c1]));
             }
-        }
-        for (int fr = wave; fr < KT * SL::NCF; fr += NW) {
+        });
+        for_wave_units<KT * SL::NCF, NW>(wave, [&](int fr) {
             const int t = fr / SL::NCF, f = fr % SL::NCF;
             const int c = 16 * t + ln;
             unsigned char *dst = slab + SL::kdT + ((size_t)fr * SL::SPL * 64 + lane) * 16;
@@ -486,7 +509,7 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
                 store_f16(dst, lds_col4(s.ke, 16 * J0 + 4 * lg, c) * s.sfx[J0][c],
                           lds_col4(s.ke, 16 * J1 + 4 * lg, c) * s.sfx[J1][c]);
             }
-        }
+        });
         __syncthreads();
 
         // ---- phase 3: (Gamma*K)^T (bf16) or V (fp32 path) into the freed
@@ -565,7 +588,7 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
         // W^T tile (t, I) = sum_J (Gamma*K)^T_{tJ} M^T_{JI}: the accumulator
         // lane (n = r, g) holds W[16I + r][16t + 4g + j], the A-operand
         // fragment of -W in the state-propagation product.
-        for (int unit = wave; unit < 4 * SL::NKF; unit += NW) {
+        for_wave_units<4 * SL::NKF, NW>(wave, [&](int unit) {
             const int I = unit / SL::NKF, tp = unit % SL::NKF;
             const int nJ = I + 1;
             if constexpr (F32IO) {
@@ -595,10 +618,10 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
                 }
                 store_f16(slab + SL::negW + ((size_t)(I * SL::NKF + tp) * 64 + lane) * 16, -acc0, -acc1);
             }
-        }
+        });
         // U tile (I, w) = sum_J M_{IJ} V_{Jw}, in the accumulator layout the
         // state-propagation kernel starts V' from.
-        for (int unit = wave; unit < 4 * KT; unit += NW) {
+        for_wave_units<4 * KT, NW>(wave, [&](int unit) {
             const int I = unit / KT, w = unit % KT;
             const int nJ = I + 1;
             f32x4 acc = zero4();
@@ -617,8 +640,18 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
                     acc = mma_bf16_k32(*reinterpret_cast<const u32x4 *>(mb + 64), vb, acc);
                 }
             }
-            *reinterpret_cast<f32x4 *>(slab + SL::u + ((size_t)(I * KT + w) * 64 + lane) * 16) = acc;
-        }
+            if constexpr (F32IO) {
+                *reinterpret_cast<f32x4 *>(slab + SL::u + ((size_t)(I * KT + w) * 64 + lane) * 16) = acc;
+            } else {
+                float m = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(acc[j]));
+                const int e = scale_exp(wave_max_nonneg(m));
+                *reinterpret_cast<u32x2 *>(slab + SL::u + ((size_t)(I * KT + w) * 64 + lane) * 8) =
+                    quad_to_f16(acc * exp2i(-e));
+                if (lane == 0) reinterpret_cast<int *>(slab + SL::uexp)[I * KT + w] = e;
+            }
+        });
         ent = ent_next;
         ent_next = ent_after;
         a_cur = a_next;
@@ -712,7 +745,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     if (pair >= N * H) return;
     const int n = pair / H, h = pair % H;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index in an SGPR
     const int ln = lane & 15, lg = lane >> 4;
     const int vt = cg * WPG + wave;
     const int col = 16 * vt + ln;
@@ -725,28 +758,25 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 
     const int c_begin = meta[n], c_end = meta[n + 1];
     auto slab_of = [&](int c) { return slabs + ((size_t)h * max_chunks + c) * slab_stride; };
-    auto load_u = [&](int c, f32x4 *dst) {
-        const f32x4 *us = reinterpret_cast<const f32x4 *>(slab_of(c) + SL::u);
+    // U: fp32 tiles (fp32 path) or fp16 tiles with a per-tile exponent (bf16 path)
+    using UReg = typename std::conditional<F32IO, f32x4, u32x2>::type;
+    auto load_u = [&](int c, UReg *dst) {
+        const UReg *us = reinterpret_cast<const UReg *>(slab_of(c) + SL::u);
 #pragma unroll
         for (int I = 0; I < 4; ++I) dst[I] = us[(I * KT + vt) * 64 + lane];
     };
     // region A = [-W | Gamma*Q], region B = [K~^T | A_qk | gamma] of a buffer
     auto copy_A = [&](int c, unsigned char *buf) { copy_frags_to_lds(slab_of(c), buf, SL::FA, wave, WPG, lane); };
     auto copy_B = [&](int c, unsigned char *buf) {
-        unsigned char *bb = buf + SL::FA * SL::FRAG;
-        copy_frags_to_lds(slab_of(c) + SL::kdT, bb, SL::FB - 1, wave, WPG, lane);
-        copy_frags_to_lds(slab_of(c) + SL::gamma, bb + (SL::FB - 1) * SL::FRAG, 1, wave, WPG, lane);
+        copy_frags_to_lds(slab_of(c) + SL::kdT, buf + SL::kdT, SL::FB, wave, WPG, lane);
     };
     // this lane's 16 bytes of fragment idx of the region at slab offset `off`
     auto frag = [&](const unsigned char *buf, size_t off, int idx) -> u32x4 {
-        const size_t pos = off < SL::kdT ? off : SL::FA * SL::FRAG + (off - SL::kdT);
-        return *reinterpret_cast<const u32x4 *>(buf + pos + ((size_t)idx * 64 + lane) * 16);
+        return *reinterpret_cast<const u32x4 *>(buf + off + ((size_t)idx * 64 + lane) * 16);
     };
-    auto gamma_of = [&](const unsigned char *buf) {
-        return reinterpret_cast<const f32x4 *>(buf + (SL::FA + SL::FB - 1) * SL::FRAG);
-    };
+    auto gamma_of = [&](const unsigned char *buf) { return reinterpret_cast<const f32x4 *>(buf + SL::gamma); };
 
-    f32x4 u[4], un[4];
+    UReg u[4], un[4];
     f32x4 acc_o[4];
     int o_t0 = 0, o_L = 0;     // pending output of the previous chunk
 
@@ -778,6 +808,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int c = c_begin; c < c_end; ++c) {
             const int par = (c - c_begin) & 1;
             const unsigned char *buf = lds_raw + par * BUF;
+            const int *uexp = reinterpret_cast<const int *>(buf + SL::uexp);
             unsigned char *nbuf = lds_raw + (par ^ 1) * BUF;
             if (c + 1 < c_end) {
                 copy_A(c + 1, nbuf);
@@ -808,7 +839,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
                     ws = mma_f16_k32(frag(buf, SL::negW, I * (KT / 2) + p), sf[p], ws);
                     qs = mma_f16_k32(frag(buf, SL::qg, I * (KT / 2) + p), sf[p], qs);
                 }
-                vp[I] = u[I] + ws * uS;
+                vp[I] = f16x4_to_quad(u[I]) * exp2i(uexp[I * KT + vt]) + ws * uS;
                 acc_o[I] = qs * uS;
             }
 
@@ -826,8 +857,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             uint16_t *ob = obuf + par * 64 * OP;
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
-                f32x4 a = mma_f16_k32(frag(buf, SL::aqk, I * 2), vf0, zero4());
-                if (I >= 2) a = mma_f16_k32(frag(buf, SL::aqk, I * 2 + 1), vf1, a);
+                f32x4 a = mma_f16_k32(frag(buf, SL::aqk, aqk_frag(I, 0)), vf0, zero4());
+                if (I >= 2) a = mma_f16_k32(frag(buf, SL::aqk, aqk_frag(I, 1)), vf1, a);
                 acc_o[I] += a * uV;
                 *reinterpret_cast<u32x2 *>(ob + (16 * I + ln) * OP + 16 * wave + 4 * lg) =
                     transpose_tile_bf16(acc_o[I], lane);
