@@ -1,0 +1,437 @@
+// kda_intra.hip -- intra-chunk kernel of the bf16 prefill path for gfx950.
+//
+// One 4-wave workgroup per (chunk, head) item, persistent over items, two
+// workgroups per CU (77 KiB of LDS each at d = 128), so that one workgroup's
+// memory traffic, barriers and serial steps overlap the other's math.  Per
+// item it computes, in the chunk form of the s1mplewind "kimi-k3" notes
+// (section "Chunkwise 形式", steps 1-6):
+//   A_kk = StrictTril(Diag(beta)(Gamma*K)(K/Gamma)^T),  A_qk = Tril((Gamma*Q)(K/Gamma)^T)
+//   T = (I + A_kk)^{-1},  M = T Diag(beta),  W = M (Gamma*K),  U = M V
+// and writes the slab the inter-chunk kernel consumes (kda_chunk.h): -W,
+// Gamma*Q, ((gamma_C/Gamma)*K)^T, A_qk, gamma_C and U.
+//
+// Decays use the block-relative form of the devpress K3 walk-through (§3.2,
+// Eq 5): within a 16-token block the gate sums to at least -80, so every
+// factor below is exp2 of a log-decay difference that is <= 0, or <= 80 ln 2
+// ... on a diagonal block.
+//
+// Ownership: wave w holds row block b = (w + rot) & 3 (rot varies by item so
+// that the unequal per-block work spreads over the SIMDs); lane (ln, lg) =
+// (l % 16, l / 16) holds row 16b + ln and channels 16kt + 4lg + {0..3} of
+// every K16 tile kt.  That is the MFMA row-operand layout, so the block's
+// keys and queries feed the Gram products straight from registers:
+//   tile (I, b), I >= b, of A_kk is  kr_I (A, rows r) x ke_b fac (B, rows i)
+//   and of A_qk^T is                 ke_b fac (A, rows i) x qr_I (B, rows r),
+// with kr = k exp2(Gl), qr = q exp2(Gl) (Gl: log-decay from the block start,
+// inclusive) and ke = k exp2(bt - Gl) (bt: the block's total log-decay); fac
+// is exp2(-bt_b) on the diagonal tile and the decay of the blocks strictly
+// between b and I otherwise.  Only kr and qr of blocks 1..3 go through LDS.
+// Products are split-bf16 (hi + lo, three MFMAs), good to about 2^-16.
+//
+// Phases (barriers between them):
+//   1  gate, block-local cumulative log-decay (DPP row scan), kr / qr / ke
+//   F  per-channel decay factors of the chunk
+//   2  Gamma*Q, K~^T (transposed by an identity MFMA), Gram tiles -> A_kk, A_qk
+//   3  (Gamma*K)^T and V^T fragments into LDS; prefetch of the next item;
+//      inverses of the four diagonal 16x16 blocks (forward substitution)
+//   4  off-diagonal blocks of T, one block row per step (fp32 MFMA)
+//   4b M = T Diag(beta), split into bf16 fragments
+//   5  -W and U, stored in the slab
+// ---------------------------------------------------------------------------
+#include "kda_chunk.h"
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+// Transpose of a 16x16 tile held in the row-operand layout (lane (m, g) holds
+// X[m][4g + j]), rounded to fp16: as the A operand of a 16x16x16 fp16 MFMA
+// against the identity it gives D = X, whose accumulator lane (n, g) holds
+// X[4g + j][n] -- four consecutive rows of column n.  Exact for finite values.
+__device__ __forceinline__ u32x2 transpose_tile_f16(f32x4 x, int lane) {
+    const int n = lane & 15, g = lane >> 4;
+    const u32x2 a = quad_to_f16(x);
+    const uint32_t one = 0x3c00u;  // fp16 1.0
+    uint32_t e[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) e[j] = (4 * g + j == n) ? one : 0u;
+    const u32x2 b = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+    const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b),
+                                                          zero4(), 0, 0, 0);
+    return quad_to_f16(d);
+}
+
+// x = hi + lo, both bf16-valued, per element.
+__device__ __forceinline__ void split_quad(f32x4 x, f32x4 &hi, f32x4 &lo) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        hi[j] = bf16_bits_to_f32(f32_to_bf16_bits(x[j]));
+        lo[j] = x[j] - hi[j];
+    }
+}
+
+// A zero the compiler cannot see through.  Lane-dependent constants built
+// from `lane + opaque_zero()` inside the item loop are rebuilt per item
+// instead of being hoisted out of the loop and kept live (or spilled) across it.
+__device__ __forceinline__ int opaque_zero() {
+    int z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    return z;
+}
+
+template <int D>
+struct Intra4Lds {
+    static constexpr int KT = D / 16, NP = D / 32;
+    static constexpr size_t FR = 1024;
+    // X, phases 1-2: split row fragments of kr and qr of row blocks 1..3,
+    //   [block - 1][kr, qr][pair p][hi, lo] fragments.
+    // X, phases 3-5: (Gamma*K)^T fragments [t][row pair f][hi, lo], then V^T
+    //   fragments [t][f]; the 8 bytes of block 2f + s sit at slot s of a lane.
+    static constexpr size_t X = 0;
+    static constexpr size_t XB = 12 * NP * FR;
+    static constexpr size_t GKT = X, VT = X + 4 * KT * FR;
+    // A_kk, then T: the diagonal blocks in place, T_IJ (I > J) at block (J, I).
+    static constexpr int AP = 68;
+    static constexpr size_t A = X + XB;
+    // F, phases 1-3: block log-decay totals bt [4][D], then 18 factor rows
+    //   [18][D]: exp2(-bt_J) (0..3), prefix decays pfx_I (4..7), suffix
+    //   decays sfx_J (8..11), decays strictly between J < I (12 + off_index).
+    // F, phases 4b-5: M split fragments [aqk_frag(I, pj)][hi, lo].
+    static constexpr size_t F = A + 64 * AP * 4;
+    static constexpr size_t FB = 12 * FR;
+    static constexpr size_t BETA = F + FB;
+    static constexpr size_t bytes = BETA + 64 * 4;
+    static_assert((4 + 18) * D * 4 <= (int)FB, "bt and the factors fit the M region");
+};
+
+// Raw inputs of the lane's row for one item.
+template <int D>
+struct Rows4 {
+    static constexpr int KT = D / 16;
+    float beta;
+    f32x4 z[KT];
+    u32x2 k[KT], q[KT], v[KT];
+};
+
+// Rows past the chunk's end read the chunk's first row; the consumer masks
+// them.  Loads are unconditional and in order of use.
+template <int D>
+__device__ __forceinline__ void load_rows4(Rows4<D> &R, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                           const float *z, const float *beta, int4 ent, int h, int H, int row,
+                                           int lg) {
+    constexpr int KT = D / 16;
+    const size_t trow = (size_t)(ent.y + (row < ent.z ? row : 0)) * H + h;
+    const size_t base = trow * D + 4 * lg;
+    R.beta = beta[trow];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        const size_t idx = base + 16 * kt;
+        R.z[kt] = ld4(z + idx);
+        R.k[kt] = *reinterpret_cast<const u32x2 *>(k + idx);
+        R.q[kt] = *reinterpret_cast<const u32x2 *>(q + idx);
+        R.v[kt] = *reinterpret_cast<const u32x2 *>(v + idx);
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) intra4_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const float *__restrict__ z, const float *__restrict__ A, const float *__restrict__ beta,
+    const int32_t *__restrict__ meta, const int4 *__restrict__ table, int N, int H, int max_chunks,
+    unsigned char *__restrict__ slabs, size_t slab_stride) {
+    using SL = Slab<D, false>;
+    using LY = Intra4Lds<D>;
+    constexpr int KT = D / 16, NP = D / 32;
+    constexpr size_t FR = LY::FR;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    unsigned char *X = lds_raw + LY::X;
+    float (*a)[LY::AP] = reinterpret_cast<float (*)[LY::AP]>(lds_raw + LY::A);
+    float *Fp = reinterpret_cast<float *>(lds_raw + LY::F);
+    float *bt_lds = Fp;                 // [4][D]
+    float *fac_lds = Fp + 4 * D;        // [18][D]
+    unsigned char *msp = lds_raw + LY::F;
+    float *sbeta = reinterpret_cast<float *>(lds_raw + LY::BETA);
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index in an SGPR
+    const int total = meta[N] * H;
+    const int stride = gridDim.x;
+    // block rotation: differs between neighbouring workgroups and advances per item
+    const int rot0 = blockIdx.x + 2 * (2 * (int)blockIdx.x >= (int)gridDim.x);
+
+    int it = blockIdx.x;
+    if (it >= total) return;
+    // Chunk-table entries and A_h are read through the scalar cache, whose
+    // loads every barrier waits for: fetch them one item ahead of their use.
+    int4 ent = table[it / H];
+    int4 ent_next = (it + stride < total) ? table[(it + stride) / H] : make_int4(0, 0, 0, 0);
+    float a_cur = A[it % H];
+
+    for (int iter = 0; it < total; it += stride, ++iter) {
+        const int chunk = it / H, h = it % H;
+        const int L = ent.z;
+        const int b = (wave + rot0 + iter) & 3;        // this wave's row block
+        // lane coordinates, rebuilt per item (see opaque_zero)
+        const int lane = (tid & 63) + opaque_zero();
+        const int ln = lane & 15, lg = lane >> 4;
+        const int row = 16 * b + ln;
+        const bool ok = row < L;
+        unsigned char *slab = slabs + ((size_t)h * max_chunks + chunk) * slab_stride;
+        const float ea = __expf(a_cur);
+        const int it_next = it + stride;
+        const int4 ent_after = (it_next + stride < total) ? table[(it_next + stride) / H] : make_int4(0, 0, 0, 0);
+        const float a_next = it_next < total ? A[it_next % H] : 0.f;
+
+        // ---- phase 1: gate, block-local cumulative log2-decay, row operands.
+        // The raw inputs are loaded here, not prefetched: the second workgroup
+        // on the CU computes while this one waits.
+        Rows4<D> R;
+        load_rows4<D>(R, q, k, v, z, beta, ent, h, H, row, lg);
+        if (lg == 0) sbeta[row] = ok ? R.beta : 0.f;
+        f32x4 kr[KT], qr[KT], ke[KT];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+            const f32x4 kq = ok ? quad_f32<false>(R.k[kt]) : zero4();
+            const f32x4 qq = ok ? quad_f32<false>(R.q[kt]) : zero4();
+            f32x4 gl, bt, rf, kev;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                gl[j] = row16_inclusive_scan(ok ? gate_log2(ea, R.z[kt][j]) : 0.f);
+                bt[j] = row16_last(gl[j]);
+                rf[j] = fast_exp2(gl[j]);
+                kev[j] = kq[j] * fast_exp2(bt[j] - gl[j]);
+            }
+            kr[kt] = kq * rf;
+            qr[kt] = qq * rf;
+            ke[kt] = kev;
+            if (ln == 15) *reinterpret_cast<f32x4 *>(bt_lds + b * D + 16 * kt + 4 * lg) = bt;
+        }
+        if (b > 0) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                u32x4 hi, lo;
+                unsigned char *dk = X + ((size_t)(((b - 1) * 2 + 0) * NP + p) * 2) * FR + lane * 16;
+                quads_to_bf16_split(kr[2 * p], kr[2 * p + 1], hi, lo);
+                *reinterpret_cast<u32x4 *>(dk) = hi;
+                *reinterpret_cast<u32x4 *>(dk + FR) = lo;
+                unsigned char *dq = X + ((size_t)(((b - 1) * 2 + 1) * NP + p) * 2) * FR + lane * 16;
+                quads_to_bf16_split(qr[2 * p], qr[2 * p + 1], hi, lo);
+                *reinterpret_cast<u32x4 *>(dq) = hi;
+                *reinterpret_cast<u32x4 *>(dq + FR) = lo;
+            }
+        }
+        __syncthreads();
+
+        // ---- per-channel decay factors
+        for (int c = tid; c < D; c += 256) {
+            const float b0 = bt_lds[c], b1 = bt_lds[D + c], b2 = bt_lds[2 * D + c], b3 = bt_lds[3 * D + c];
+            float *f = fac_lds + c;
+            f[0 * D] = exp2f(-b0);
+            f[1 * D] = exp2f(-b1);
+            f[2 * D] = exp2f(-b2);
+            f[3 * D] = exp2f(-b3);
+            f[4 * D] = 1.f;
+            f[5 * D] = exp2f(b0);
+            f[6 * D] = exp2f(b0 + b1);
+            f[7 * D] = exp2f(b0 + b1 + b2);
+            f[8 * D] = exp2f(b1 + b2 + b3);
+            f[9 * D] = exp2f(b2 + b3);
+            f[10 * D] = exp2f(b3);
+            f[11 * D] = 1.f;
+            f[12 * D] = 1.f;             // (0,1)
+            f[13 * D] = exp2f(b1);       // (0,2)
+            f[14 * D] = exp2f(b1 + b2);  // (0,3)
+            f[15 * D] = 1.f;             // (1,2)
+            f[16 * D] = exp2f(b2);       // (1,3)
+            f[17 * D] = 1.f;             // (2,3)
+            reinterpret_cast<float *>(slab + SL::gamma)[c] = exp2f(b0 + b1 + b2 + b3);
+        }
+        __syncthreads();
+
+        // ---- phase 2: Gamma*Q, K~^T, Gram tiles (I, b) for I >= b
+        {
+            const float *pfx = fac_lds + (4 + b) * D;
+            const float *sfx = fac_lds + (8 + b) * D;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const int c0 = 32 * p + 4 * lg, c1 = c0 + 16;
+                store_f16(slab + SL::qg + ((size_t)(b * NP + p) * 64 + lane) * 16, qr[2 * p] * ld4(pfx + c0),
+                          qr[2 * p + 1] * ld4(pfx + c1));
+            }
+#pragma unroll
+            for (int t = 0; t < KT; ++t) {
+                const u32x2 kd = transpose_tile_f16(ke[t] * ld4(sfx + 16 * t + 4 * lg), lane);
+                *reinterpret_cast<u32x2 *>(slab + SL::kdT + ((size_t)(t * SL::NCF + (b >> 1)) * 64 + lane) * 16 +
+                                           (b & 1) * 8) = kd;
+            }
+        }
+        for (int I = b; I < 4; ++I) {
+            const float *fac = fac_lds + (I == b ? b : 12 + off_index(b, I)) * D;
+            f32x4 akk = zero4(), aqt = zero4();
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const int c0 = 32 * p + 4 * lg, c1 = c0 + 16;
+                u32x4 kch, kcl, krh, krl, qrh, qrl;
+                quads_to_bf16_split(ke[2 * p] * ld4(fac + c0), ke[2 * p + 1] * ld4(fac + c1), kch, kcl);
+                if (I == b) {
+                    quads_to_bf16_split(kr[2 * p], kr[2 * p + 1], krh, krl);
+                    quads_to_bf16_split(qr[2 * p], qr[2 * p + 1], qrh, qrl);
+                } else {
+                    const unsigned char *dk = X + ((size_t)(((I - 1) * 2 + 0) * NP + p) * 2) * FR + lane * 16;
+                    const unsigned char *dq = X + ((size_t)(((I - 1) * 2 + 1) * NP + p) * 2) * FR + lane * 16;
+                    krh = *reinterpret_cast<const u32x4 *>(dk);
+                    krl = *reinterpret_cast<const u32x4 *>(dk + FR);
+                    qrh = *reinterpret_cast<const u32x4 *>(dq);
+                    qrl = *reinterpret_cast<const u32x4 *>(dq + FR);
+                }
+                akk = mma3_bf16(krh, krl, kch, kcl, akk);
+                aqt = mma3_bf16(kch, kcl, qrh, qrl, aqt);
+            }
+            // A_kk tile: lane (n = i, g) holds the sum for rows r = 4g + j of block I
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int rl = 4 * lg + j;
+                float x = akk[j] * sbeta[16 * I + rl];
+                if (I == b && ln >= rl) x = 0.f;
+                a[16 * I + rl][16 * b + ln] = x;
+            }
+            // A_qk: lane (n = r, g) holds columns i = 4g + j of row r -- the
+            // operand fragment of row tile I, column block b
+            f32x4 aq;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) aq[j] = (I == b && 4 * lg + j > ln) ? 0.f : aqt[j];
+            unsigned char *base = slab + SL::aqk + ((size_t)aqk_frag(I, b >> 1) * 64 + lane) * 16 + (b & 1) * 8;
+            *reinterpret_cast<u32x2 *>(base) = quad_to_f16(aq);
+            if (I == b && (b & 1) == 0)  // the tile right of an even diagonal shares its fragment
+                *reinterpret_cast<u32x2 *>(base + 8) = u32x2{0u, 0u};
+        }
+        __syncthreads();
+
+        // ---- phase 3: transposed (Gamma*K) split and V fragments into X
+        {
+            const float *pfx = fac_lds + (4 + b) * D;
+#pragma unroll
+            for (int t = 0; t < KT; ++t) {
+                f32x4 hi, lo;
+                split_quad(kr[t] * ld4(pfx + 16 * t + 4 * lg), hi, lo);
+                unsigned char *dg = X + LY::GKT + ((size_t)((t * 2 + (b >> 1)) * 2) * FR) + lane * 16 + (b & 1) * 8;
+                *reinterpret_cast<u32x2 *>(dg) = transpose_tile_bf16(hi, lane);
+                *reinterpret_cast<u32x2 *>(dg + FR) = transpose_tile_bf16(lo, lane);
+                const f32x4 vq = ok ? quad_f32<false>(R.v[t]) : zero4();
+                *reinterpret_cast<u32x2 *>(X + LY::VT + (size_t)(t * 2 + (b >> 1)) * FR + lane * 16 + (b & 1) * 8) =
+                    transpose_tile_bf16(vq, lane);
+            }
+        }
+        if (lane < 16) {
+            // column `lane` of (I + A_bb)^{-1}: forward substitution, updating
+            // every later row as soon as an entry is final
+            const int o = 16 * b;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = (r == lane) ? 1.f : 0.f;
+#pragma unroll
+            for (int i = 0; i < 15; ++i) {
+                const float ci = x[i];
+#pragma unroll
+                for (int r = i + 1; r < 16; ++r) x[r] -= a[o + r][o + i] * ci;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) a[o + r][o + lane] = x[r];
+        }
+        __syncthreads();
+
+        // ---- phase 4: T_IJ = -T_II sum_{J<=m<I} A_Im T_mJ, stored at block (J, I)
+        for (int I = 1; I < 4; ++I) {
+            if (wave < I) {
+                const int J = wave;
+                f32x4 x = zero4();
+                for (int m = J; m < I; ++m)
+                    x = mma_f32_k16(lds_quad(a, 16 * I + ln, 16 * m + 4 * lg), lds_col4(a, 16 * J + 4 * lg, 16 * m + ln),
+                                    x);
+                const f32x4 y = mma_f32_k16(lds_quad(a, 16 * I + ln, 16 * I + 4 * lg), x, zero4());
+#pragma unroll
+                for (int j = 0; j < 4; ++j) a[16 * J + 4 * lg + j][16 * I + ln] = -y[j];
+            }
+            __syncthreads();
+        }
+
+        // ---- phase 4b: M = T Diag(beta) for the rows of block b, split
+#pragma unroll
+        for (int pj = 0; pj < 2; ++pj) {
+            if (2 * pj <= b) {
+                f32x4 x[2];
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const int J = 2 * pj + s;
+                    const f32x4 tq = J < b ? lds_quad(a, 16 * J + ln, 16 * b + 4 * lg)
+                                           : (J == b ? lds_quad(a, 16 * b + ln, 16 * b + 4 * lg) : zero4());
+                    x[s] = tq * ld4(sbeta + 16 * J + 4 * lg);
+                }
+                u32x4 hi, lo;
+                quads_to_bf16_split(x[0], x[1], hi, lo);
+                unsigned char *d = msp + (size_t)aqk_frag(b, pj) * 2 * FR + lane * 16;
+                *reinterpret_cast<u32x4 *>(d) = hi;
+                *reinterpret_cast<u32x4 *>(d + FR) = lo;
+            }
+        }
+        __syncthreads();
+
+        // ---- phase 5: -W (from W^T tiles) and U
+        for_wave_units<4 * NP, 4>(wave, [&](int unit) {
+            const int p = unit % NP, I = unit / NP;
+            f32x4 acc0 = zero4(), acc1 = zero4();
+            for (int pj = 0; pj <= (I >> 1); ++pj) {
+                const unsigned char *mb = msp + (size_t)aqk_frag(I, pj) * 2 * FR + lane * 16;
+                const u32x4 mh = *reinterpret_cast<const u32x4 *>(mb);
+                const u32x4 ml = *reinterpret_cast<const u32x4 *>(mb + FR);
+                const unsigned char *ga = X + LY::GKT + ((size_t)((2 * p * 2 + pj) * 2) * FR) + lane * 16;
+                const unsigned char *gb = X + LY::GKT + ((size_t)(((2 * p + 1) * 2 + pj) * 2) * FR) + lane * 16;
+                acc0 = mma3_bf16(*reinterpret_cast<const u32x4 *>(ga), *reinterpret_cast<const u32x4 *>(ga + FR), mh, ml,
+                                 acc0);
+                acc1 = mma3_bf16(*reinterpret_cast<const u32x4 *>(gb), *reinterpret_cast<const u32x4 *>(gb + FR), mh, ml,
+                                 acc1);
+            }
+            store_f16(slab + SL::negW + ((size_t)(I * NP + p) * 64 + lane) * 16, -acc0, -acc1);
+        });
+        for_wave_units<4 * KT, 4>(wave, [&](int unit) {
+            const int w = unit % KT, I = unit / KT;
+            f32x4 acc = zero4();
+            for (int pj = 0; pj <= (I >> 1); ++pj) {
+                const unsigned char *mb = msp + (size_t)aqk_frag(I, pj) * 2 * FR + lane * 16;
+                const u32x4 vb = *reinterpret_cast<const u32x4 *>(X + LY::VT + (size_t)(w * 2 + pj) * FR + lane * 16);
+                acc = mma_bf16_k32(*reinterpret_cast<const u32x4 *>(mb), vb, acc);
+                acc = mma_bf16_k32(*reinterpret_cast<const u32x4 *>(mb + FR), vb, acc);
+            }
+            float m = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(acc[j]));
+            const int e = scale_exp(wave_max_nonneg(m));
+            *reinterpret_cast<u32x2 *>(slab + SL::u + ((size_t)(I * KT + w) * 64 + lane) * 8) = quad_to_f16(acc * exp2i(-e));
+            if (lane == 0) reinterpret_cast<int *>(slab + SL::uexp)[I * KT + w] = e;
+        });
+        ent = ent_next;
+        ent_next = ent_after;
+        a_cur = a_next;
+        __syncthreads();
+    }
+}
+
+template <int D>
+int launch_intra_bf16(const PrefillArgs &a, const int32_t *meta, const int4 *table, unsigned char *slabs) {
+    using LY = Intra4Lds<D>;
+    const long long items = (long long)a.plan.max_chunks * a.H;
+    if (items <= 0) return 0;
+    if (!set_lds(&intra4_kernel<D>, LY::bytes)) return -1;
+    const int grid = (int)std::min<long long>(items, 2LL * device_cus());
+    hipLaunchKernelGGL(intra4_kernel<D>, dim3(grid), dim3(256), LY::bytes, a.stream,
+                       reinterpret_cast<const uint16_t *>(a.q), reinterpret_cast<const uint16_t *>(a.k),
+                       reinterpret_cast<const uint16_t *>(a.v), a.z, a.A, a.beta, meta, table, a.N, a.H,
+                       a.plan.max_chunks, slabs, a.plan.slab_bytes);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template int launch_intra_bf16<32>(const PrefillArgs &, const int32_t *, const int4 *, unsigned char *);
+template int launch_intra_bf16<64>(const PrefillArgs &, const int32_t *, const int4 *, unsigned char *);
+template int launch_intra_bf16<128>(const PrefillArgs &, const int32_t *, const int4 *, unsigned char *);
+
+}  // namespace kda
