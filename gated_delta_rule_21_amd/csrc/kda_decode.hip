@@ -12,7 +12,10 @@
 //   o_j    = S_j . q = r_j + beta e_j (k . q)
 // The row's key channels are spread over LPR = dk/16 neighbouring lanes with
 // 16 channels each, so the reductions are log2(LPR) lane exchanges inside a
-// wavefront and no LDS or barrier is needed.  The state is the only large
+// wavefront and no LDS or barrier is needed.  A workgroup has one thread per
+// (row, 16 channels) up to 1024 threads, so at d = 128 every thread owns one
+// 64-byte piece of one row: the whole 64 KiB state of a head is in flight at
+// once, which is what keeps the HBM queues full.  The state is the only large
 // stream (2 * dk * dv * 4 bytes per head), which makes the kernel HBM-bound
 // ("Kimi K3：架构…" §11.4, §13.2).
 #include "kda_device.h"
@@ -21,12 +24,12 @@
 namespace kda {
 
 template <int DK, int DV, bool F32IO>
-__global__ void __launch_bounds__(256) decode_kernel(
+__global__ void __launch_bounds__(1024) decode_kernel(
     const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
     const float *__restrict__ z, const float *__restrict__ A, const float *__restrict__ beta,
     float *__restrict__ S, void *__restrict__ o, int H) {
     constexpr int LPR = DK / 16;                 // lanes per state row
-    constexpr int THREADS = (DV * LPR < 256) ? DV * LPR : 256;
+    constexpr int THREADS = (DV * LPR < 1024) ? DV * LPR : 1024;
     constexpr int ROWS_PER_PASS = THREADS / LPR;
     constexpr int PASSES = DV / ROWS_PER_PASS;
     static_assert(PASSES * ROWS_PER_PASS == DV, "row split");
@@ -37,6 +40,21 @@ __global__ void __launch_bounds__(256) decode_kernel(
     const int cl = t % LPR;                      // lane within the row
     const int rg = t / LPR;                      // row within the pass
 
+    float *Sp = S + (size_t)pair * DV * DK;
+    // The state is the stream: issue every load of this thread's rows first,
+    // before the small per-head inputs, so that no state load waits behind
+    // the gate arithmetic.
+    f32x4 s[PASSES][4];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int row = rg + ROWS_PER_PASS * p;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            s[p][m] = __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4 *>(Sp + (size_t)row * DK + 4 * (cl + LPR * m)));
+    }
+
+    __builtin_amdgcn_sched_barrier(0);  // keep the state loads ahead of everything else
     // Key channels owned by this lane: float4 groups cl + LPR * m, m = 0..3.
     const size_t krow = (size_t)pair * DK;
     float kk[16], qq[16], aa[16];
@@ -45,10 +63,12 @@ __global__ void __launch_bounds__(256) decode_kernel(
     for (int m = 0; m < 4; ++m) {
         const int c0 = 4 * (cl + LPR * m);
         const f32x4 zv = *reinterpret_cast<const f32x4 *>(z + krow + c0);
+        const f32x4 kv = load_io4<F32IO>(k, krow + c0);
+        const f32x4 qv = load_io4<F32IO>(q, krow + c0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            kk[4 * m + j] = load_io<F32IO>(k, krow + c0 + j);
-            qq[4 * m + j] = load_io<F32IO>(q, krow + c0 + j);
+            kk[4 * m + j] = kv[j];
+            qq[4 * m + j] = qv[j];
             aa[4 * m + j] = exp2f(gate_log2(ea, zv[j]));
         }
     }
@@ -60,18 +80,6 @@ __global__ void __launch_bounds__(256) decode_kernel(
     for (int i = 0; i < 16; ++i) kq += kk[i] * qq[i];
 #pragma unroll
     for (int off = 1; off < LPR; off <<= 1) kq += __shfl_xor(kq, off, 64);
-
-    float *Sp = S + (size_t)pair * DV * DK;
-    // Issue every load of this thread's rows before any arithmetic.
-    f32x4 s[PASSES][4];
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-        const int row = rg + ROWS_PER_PASS * p;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-            s[p][m] = __builtin_nontemporal_load(
-                reinterpret_cast<const f32x4 *>(Sp + (size_t)row * DK + 4 * (cl + LPR * m)));
-    }
 
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
@@ -110,7 +118,7 @@ __global__ void __launch_bounds__(256) decode_kernel(
 template <int D, bool F32IO>
 static int launch_decode_t(const DecodeArgs &a) {
     constexpr int LPR = D / 16;
-    constexpr int THREADS = (D * LPR < 256) ? D * LPR : 256;
+    constexpr int THREADS = (D * LPR < 1024) ? D * LPR : 1024;
     dim3 grid((unsigned)(a.N * a.H));
     hipLaunchKernelGGL((decode_kernel<D, D, F32IO>), grid, dim3(THREADS), 0, a.stream, a.q, a.k,
                        a.v, a.z, a.A, a.beta, a.S, a.o, a.H);

@@ -54,6 +54,16 @@ __device__ __forceinline__ float load_io(const void *p, size_t i) {
         return bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(p)[i]);
     }
 }
+// Elements i .. i + 3 (i a multiple of 4) of an io-dtype array as fp32.
+template <bool F32IO>
+__device__ __forceinline__ f32x4 load_io4(const void *p, size_t i) {
+    if constexpr (F32IO) {
+        return *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(p) + i);
+    } else {
+        const u32x2 w = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint16_t *>(p) + i);
+        return f32x4{bf16_lo_half(w[0]), bf16_hi_half(w[0]), bf16_lo_half(w[1]), bf16_hi_half(w[1])};
+    }
+}
 template <bool F32IO>
 __device__ __forceinline__ void store_io(void *p, size_t i, float x) {
     if constexpr (F32IO) {
