@@ -573,10 +573,12 @@ __global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
 //
 // Staging: the operands every wave shares (-W, Gamma*Q, K~^T, A_qk, gamma)
 // reach LDS by direct global->LDS copies (global_load_lds_dwordx4, one 1 KiB
-// fragment per wave instruction).  bf16 path: two whole-chunk buffers, the
-// next chunk streams in while this one computes.  fp32 path (larger
-// fragments): region B of this chunk streams during phase A, region A of the
-// next chunk during phase B.
+// fragment per wave instruction).  bf16 path: region A (-W, Gamma*Q: needed
+// first in a step) rotates through three buffers and is fetched two chunks
+// ahead, region B through two, fetched one chunk ahead; a step ends by
+// waiting for everything except the A copies it issued last.  fp32 path
+// (larger fragments): region B of this chunk streams during phase A, region
+// A of the next chunk during phase B.
 // ---------------------------------------------------------------------------
 template <int D, bool F32IO>
 struct InterShape {
@@ -584,11 +586,13 @@ struct InterShape {
     static constexpr int KT = D / 16;
     static constexpr int WPG = KT < 4 ? KT : 4;          // waves per workgroup
     static constexpr int NT = 64 * WPG;
-    static constexpr int NBUF = F32IO ? 1 : 2;
-    // bf16 path: two output staging tiles of 64 rows x (16 * WPG) bf16 columns
+    // bf16 path: region A ring of 3, region B ring of 2, and two output
+    // staging tiles of 64 rows x (16 * WPG) bf16 columns
+    static constexpr size_t ABYTES = (size_t)SL::FA * SL::FRAG, BBYTES = (size_t)SL::FB * SL::FRAG;
     static constexpr int OPITCH = 16 * WPG + 8;                  // bf16 elements per staged row
     static constexpr size_t obuf_bytes = F32IO ? 0 : (size_t)64 * OPITCH * 2;
-    static constexpr size_t lds_bytes = (size_t)NBUF * (SL::FA + SL::FB) * SL::FRAG + 2 * obuf_bytes;
+    static constexpr size_t ring_bytes = 3 * ABYTES + 2 * BBYTES;
+    static constexpr size_t lds_bytes = F32IO ? (size_t)(SL::FA + SL::FB) * SL::FRAG : ring_bytes + 2 * obuf_bytes;
 };
 
 // Copy `nfrag` consecutive 1 KiB fragments from global `src` to LDS `dst`,
@@ -686,7 +690,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
         // transposes its 64 x 16 tile in registers, stages it in LDS, and after
         // the next barrier every lane stores 16-byte pieces of full rows.
         constexpr int OP = SHP::OPITCH;
-        uint16_t *obuf = reinterpret_cast<uint16_t *>(lds_raw + SHP::NBUF * BUF);
+        constexpr size_t AB = SHP::ABYTES, BB = SHP::BBYTES;
+        unsigned char *aring = lds_raw, *bring = lds_raw + 3 * AB;
+        uint16_t *obuf = reinterpret_cast<uint16_t *>(lds_raw + SHP::ring_bytes);
         auto flush_o = [&](int par, int t0, int L) {
             const uint16_t *ob = obuf + par * 64 * OP;
             constexpr int SEG = 16 * WPG / 8;                   // 16-byte pieces per row
@@ -698,24 +704,41 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
                         *reinterpret_cast<const u32x4 *>(ob + r * OP + 8 * sgm);
             }
         };
+        auto copyA = [&](int c, unsigned char *dst) { copy_frags_to_lds(slab_of(c), dst, SL::FA, wave, WPG, lane); };
+        auto copyB = [&](int c, unsigned char *dst) {
+            copy_frags_to_lds(slab_of(c) + SL::kdT, dst, SL::FB, wave, WPG, lane);
+        };
+        // A copies per wave: the last of a step's memory operations, and the
+        // only ones still allowed in flight at its end
+        constexpr int NA = SL::FA / WPG;
+        static_assert(SL::FA % WPG == 0 && NA < 16, "A fragments per wave");
         if (c_begin < c_end) {
-            copy_A(c_begin, lds_raw);
-            copy_B(c_begin, lds_raw);
+            copyA(c_begin, aring);
+            copyB(c_begin, bring);
             load_u(c_begin, u);
+            if (c_begin + 1 < c_end) copyA(c_begin + 1, aring + AB);
         }
         wait_all_memory();
         __syncthreads();
         for (int c = c_begin; c < c_end; ++c) {
-            const int par = (c - c_begin) & 1;
-            const unsigned char *buf = lds_raw + par * BUF;
-            const int *uexp = reinterpret_cast<const int *>(buf + SL::uexp);
-            unsigned char *nbuf = lds_raw + (par ^ 1) * BUF;
+            const int i = c - c_begin;
+            const int par = i & 1;
+            const unsigned char *abuf = aring + (i % 3) * AB;
+            const unsigned char *bbuf = bring + par * BB;
+            // a region-B offset of the slab, seen in the B buffer
+            auto fragB = [&](size_t off, int idx) -> u32x4 {
+                return *reinterpret_cast<const u32x4 *>(bbuf + (off - SL::kdT) + ((size_t)idx * 64 + lane) * 16);
+            };
+            auto fragA = [&](size_t off, int idx) -> u32x4 {
+                return *reinterpret_cast<const u32x4 *>(abuf + off + ((size_t)idx * 64 + lane) * 16);
+            };
+            const int *uexp = reinterpret_cast<const int *>(bbuf + (SL::uexp - SL::kdT));
+            if (o_L > 0) flush_o(par ^ 1, o_t0, o_L);   // the previous chunk's rows
             if (c + 1 < c_end) {
-                copy_A(c + 1, nbuf);
-                copy_B(c + 1, nbuf);
+                copyB(c + 1, bring + (par ^ 1) * BB);
                 load_u(c + 1, un);
             }
-            if (o_L > 0) flush_o(par ^ 1, o_t0, o_L);   // the previous chunk's rows
+            if (c + 2 < c_end) copyA(c + 2, aring + ((i + 2) % 3) * AB);
             const int4 ent = table[c];
 
             // S -> fp16 with a per-wave power-of-two scale
@@ -736,8 +759,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
                 f32x4 ws = zero4(), qs = zero4();
 #pragma unroll
                 for (int p = 0; p < KT / 2; ++p) {
-                    ws = mma_f16_k32(frag(buf, SL::negW, I * (KT / 2) + p), sf[p], ws);
-                    qs = mma_f16_k32(frag(buf, SL::qg, I * (KT / 2) + p), sf[p], qs);
+                    ws = mma_f16_k32(fragA(SL::negW, I * (KT / 2) + p), sf[p], ws);
+                    qs = mma_f16_k32(fragA(SL::qg, I * (KT / 2) + p), sf[p], qs);
                 }
                 vp[I] = f16x4_to_quad(u[I]) * exp2i(uexp[I * KT + vt]) + ws * uS;
                 acc_o[I] = qs * uS;
@@ -757,22 +780,27 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             uint16_t *ob = obuf + par * 64 * OP;
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
-                f32x4 a = mma_f16_k32(frag(buf, SL::aqk, aqk_frag(I, 0)), vf0, zero4());
-                if (I >= 2) a = mma_f16_k32(frag(buf, SL::aqk, aqk_frag(I, 1)), vf1, a);
+                f32x4 a = mma_f16_k32(fragB(SL::aqk, aqk_frag(I, 0)), vf0, zero4());
+                if (I >= 2) a = mma_f16_k32(fragB(SL::aqk, aqk_frag(I, 1)), vf1, a);
                 acc_o[I] += a * uV;
                 *reinterpret_cast<u32x2 *>(ob + (16 * I + ln) * OP + 16 * wave + 4 * lg) =
                     transpose_tile_bf16(acc_o[I], lane);
             }
-            const f32x4 *gam = gamma_of(buf);
+            const f32x4 *gam = reinterpret_cast<const f32x4 *>(bbuf + (SL::gamma - SL::kdT));
 #pragma unroll
             for (int t = 0; t < KT; ++t) {
-                f32x4 a = mma_f16_k32(frag(buf, SL::kdT, t * 2), vf0, zero4());
-                a = mma_f16_k32(frag(buf, SL::kdT, t * 2 + 1), vf1, a);
+                f32x4 a = mma_f16_k32(fragB(SL::kdT, t * 2), vf0, zero4());
+                a = mma_f16_k32(fragB(SL::kdT, t * 2 + 1), vf1, a);
                 S[t] = S[t] * gam[4 * t + lg] + a * uV;
             }
             o_t0 = ent.y;
             o_L = ent.z;
-            wait_all_memory();
+            // everything but this step's A copies must have landed (memory
+            // operations complete in issue order)
+            if (c + 2 < c_end)
+                __builtin_amdgcn_s_waitcnt((NA & 15) | (0x7 << 4) | (0xf << 8) | ((NA >> 4) << 14));
+            else
+                wait_all_memory();
             __syncthreads();
 #pragma unroll
             for (int I = 0; I < 4; ++I) u[I] = un[I];
