@@ -39,6 +39,38 @@ PREFILL_FLOPS_PER_PAIR = 6 * 128 * 128 + 5 * 64 * 128 + (64 * 64) // 3
 DECODE_BYTES_PER_PAIR = 2 * 128 * 128 * 4 + 4 * 128 * 2 + 128 * 4 + 4
 
 
+def kernel_sources_digest() -> str:
+    """sha256 (first 16 hex digits) over the HIP sources and the public header."""
+    import glob
+    import hashlib
+    files = sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", "*.hip")) +
+                   glob.glob(os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", "*.h")) +
+                   [os.path.join(ROOT, "include", "kda.h")])
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per kda_prefill launch from the committed FETCH_SIZE / WRITE_SIZE
+    summary, or None when the kernels have changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "kda_k3_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            parts = line.strip().split(":")
+            if len(parts) == 2 and parts[0] in ("prefill_traffic_bytes", "sources_sha256"):
+                vals[parts[0]] = parts[1].strip()
+    if vals.get("sources_sha256") != kernel_sources_digest() or "prefill_traffic_bytes" not in vals:
+        return None
+    return int(vals["prefill_traffic_bytes"])
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -156,6 +188,7 @@ def main():
         del src, dst
 
     pairs = T * H
+    traffic = measured_traffic()
     pre_bytes = PREFILL_BYTES_PER_PAIR * pairs
     pre_gbps = pre_bytes / (pre_ms * 1e-3) / 1e9
     pre_tflops = PREFILL_FLOPS_PER_PAIR * pairs / (pre_ms * 1e-3) / 1e12
@@ -188,7 +221,7 @@ def main():
                    "state_GBps": round(dec_gbps, 1), "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                    "ms_in_step": round(dec_ms_step, 4)},
         "roofline": {"bound": "hbm", "achieved": round(pre_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(pre_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(pre_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "kda_prefill (chunk table + intra + inter kernels), "
                                "1540 algorithmic B per (token, head) x 6291456 pairs per launch"},
     }
