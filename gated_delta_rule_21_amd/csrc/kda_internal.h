@@ -25,6 +25,7 @@ struct PrefillPlan {
     size_t slab_bytes;       // per (chunk, head) intermediate slab
     size_t off_meta;         // int32 [N + 1] per-sequence first chunk, then [1] total
     size_t off_table;        // int32x4 [max_chunks]: sequence, first token, length, -
+    size_t off_null;         // the null row: z = -inf [dk] fp32, zeros [max(dk,dv)] io dtype, beta = 0
     size_t off_slabs;        // slabs, head-major: [H][max_chunks]
     size_t total;
 };
@@ -49,6 +50,7 @@ int launch_decode(const DecodeArgs &a);
 int launch_prefill(const PrefillArgs &a);
 // Intra-chunk kernel of the bf16 path (kda_intra.hip), D = 32, 64, 128.
 template <int D>
-int launch_intra_bf16(const PrefillArgs &a, const int32_t *meta, const int4 *table, unsigned char *slabs);
+int launch_intra_bf16(const PrefillArgs &a, const int32_t *meta, const int4 *table, const float *null_row,
+                      unsigned char *slabs);
 
 }  // namespace kda

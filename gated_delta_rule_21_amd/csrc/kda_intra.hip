@@ -113,23 +113,30 @@ struct Rows4 {
     u32x2 k[KT], q[KT], v[KT];
 };
 
-// Rows past the chunk's end read the chunk's first row; the consumer masks
-// them.  Loads are unconditional and in order of use.
+// Rows past the chunk's end read the null row instead (z = -inf, so the gate
+// is 0 and nothing decays; k = q = v = 0; beta = 0), which makes every later
+// step correct for them without masks.  Loads are unconditional and in order
+// of use.
 template <int D>
 __device__ __forceinline__ void load_rows4(Rows4<D> &R, const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                                           const float *z, const float *beta, int4 ent, int h, int H, int row,
-                                           int lg) {
+                                           const float *z, const float *beta, const float *null_row, int4 ent, int h,
+                                           int H, int row, int lg) {
     constexpr int KT = D / 16;
-    const size_t trow = (size_t)(ent.y + (row < ent.z ? row : 0)) * H + h;
-    const size_t base = trow * D + 4 * lg;
-    R.beta = beta[trow];
+    const bool ok = row < ent.z;
+    const size_t trow = (size_t)(ent.y + row) * H + h;
+    const uint16_t *nz16 = reinterpret_cast<const uint16_t *>(null_row + D);
+    const float *zr = ok ? z + trow * D : null_row;
+    const uint16_t *kr = ok ? k + trow * D : nz16;
+    const uint16_t *qr = ok ? q + trow * D : nz16;
+    const uint16_t *vr = ok ? v + trow * D : nz16;
+    R.beta = ok ? beta[trow] : null_row[2 * D];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
-        const size_t idx = base + 16 * kt;
-        R.z[kt] = ld4(z + idx);
-        R.k[kt] = *reinterpret_cast<const u32x2 *>(k + idx);
-        R.q[kt] = *reinterpret_cast<const u32x2 *>(q + idx);
-        R.v[kt] = *reinterpret_cast<const u32x2 *>(v + idx);
+        const int c = 16 * kt + 4 * lg;
+        R.z[kt] = ld4(zr + c);
+        R.k[kt] = *reinterpret_cast<const u32x2 *>(kr + c);
+        R.q[kt] = *reinterpret_cast<const u32x2 *>(qr + c);
+        R.v[kt] = *reinterpret_cast<const u32x2 *>(vr + c);
     }
 }
 
@@ -137,8 +144,8 @@ template <int D>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) intra4_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ z, const float *__restrict__ A, const float *__restrict__ beta,
-    const int32_t *__restrict__ meta, const int4 *__restrict__ table, int N, int H, int max_chunks,
-    unsigned char *__restrict__ slabs, size_t slab_stride) {
+    const int32_t *__restrict__ meta, const int4 *__restrict__ table, const float *__restrict__ null_row, int N,
+    int H, int max_chunks, unsigned char *__restrict__ slabs, size_t slab_stride) {
     using SL = Slab<D, false>;
     using LY = Intra4Lds<D>;
     constexpr int KT = D / 16, NP = D / 32;
@@ -169,13 +176,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     for (int iter = 0; it < total; it += stride, ++iter) {
         const int chunk = it / H, h = it % H;
-        const int L = ent.z;
         const int b = (wave + rot0 + iter) & 3;        // this wave's row block
         // lane coordinates, rebuilt per item (see opaque_zero)
         const int lane = (tid & 63) + opaque_zero();
         const int ln = lane & 15, lg = lane >> 4;
         const int row = 16 * b + ln;
-        const bool ok = row < L;
         unsigned char *slab = slabs + ((size_t)h * max_chunks + chunk) * slab_stride;
         const float ea = __expf(a_cur);
         const int it_next = it + stride;
@@ -186,17 +191,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         // The raw inputs are loaded here, not prefetched: the second workgroup
         // on the CU computes while this one waits.
         Rows4<D> R;
-        load_rows4<D>(R, q, k, v, z, beta, ent, h, H, row, lg);
-        if (lg == 0) sbeta[row] = ok ? R.beta : 0.f;
+        load_rows4<D>(R, q, k, v, z, beta, null_row, ent, h, H, row, lg);
+        if (lg == 0) sbeta[row] = R.beta;
         f32x4 kr[KT], qr[KT], ke[KT];
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
-            const f32x4 kq = ok ? quad_f32<false>(R.k[kt]) : zero4();
-            const f32x4 qq = ok ? quad_f32<false>(R.q[kt]) : zero4();
+            const f32x4 kq = quad_f32<false>(R.k[kt]);
+            const f32x4 qq = quad_f32<false>(R.q[kt]);
             f32x4 gl, bt, rf, kev;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                gl[j] = row16_inclusive_scan(ok ? gate_log2(ea, R.z[kt][j]) : 0.f);
+                gl[j] = row16_inclusive_scan(gate_log2(ea, R.z[kt][j]));
                 bt[j] = row16_last(gl[j]);
                 rf[j] = fast_exp2(gl[j]);
                 kev[j] = kq[j] * fast_exp2(bt[j] - gl[j]);
@@ -273,7 +278,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
                 const int c0 = 32 * p + 4 * lg, c1 = c0 + 16;
                 u32x4 kch, kcl, krh, krl, qrh, qrl;
                 quads_to_bf16_split(ke[2 * p] * ld4(fac + c0), ke[2 * p + 1] * ld4(fac + c1), kch, kcl);
-                if (I == b) {
+                if (I == 0) {   // block 0's own rows are not in X
                     quads_to_bf16_split(kr[2 * p], kr[2 * p + 1], krh, krl);
                     quads_to_bf16_split(qr[2 * p], qr[2 * p + 1], qrh, qrl);
                 } else {
@@ -317,7 +322,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
                 unsigned char *dg = X + LY::GKT + ((size_t)((t * 2 + (b >> 1)) * 2) * FR) + lane * 16 + (b & 1) * 8;
                 *reinterpret_cast<u32x2 *>(dg) = transpose_tile_bf16(hi, lane);
                 *reinterpret_cast<u32x2 *>(dg + FR) = transpose_tile_bf16(lo, lane);
-                const f32x4 vq = ok ? quad_f32<false>(R.v[t]) : zero4();
+                const f32x4 vq = quad_f32<false>(R.v[t]);
                 *reinterpret_cast<u32x2 *>(X + LY::VT + (size_t)(t * 2 + (b >> 1)) * FR + lane * 16 + (b & 1) * 8) =
                     transpose_tile_bf16(vq, lane);
             }
@@ -393,22 +398,40 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
             store_f16(slab + SL::negW + ((size_t)(I * NP + p) * 64 + lane) * 16, -acc0, -acc1);
         });
-        for_wave_units<4 * KT, 4>(wave, [&](int unit) {
-            const int w = unit % KT, I = unit / KT;
-            f32x4 acc = zero4();
-            for (int pj = 0; pj <= (I >> 1); ++pj) {
-                const unsigned char *mb = msp + (size_t)aqk_frag(I, pj) * 2 * FR + lane * 16;
-                const u32x4 vb = *reinterpret_cast<const u32x4 *>(X + LY::VT + (size_t)(w * 2 + pj) * FR + lane * 16);
-                acc = mma_bf16_k32(*reinterpret_cast<const u32x4 *>(mb), vb, acc);
-                acc = mma_bf16_k32(*reinterpret_cast<const u32x4 *>(mb + FR), vb, acc);
-            }
+        {
+            // U tiles of this wave, then one power-of-two exponent for all of them
+            constexpr int NU = (4 * KT + 3) / 4;
+            f32x4 uacc[NU];
             float m = 0.f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(acc[j]));
+            for (int r = 0; r < NU; ++r) {
+                const int unit = wave + 4 * r;
+                const int w = unit % KT, I = unit / KT;
+                f32x4 acc = zero4();
+                if ((4 * KT) % 4 == 0 || unit < 4 * KT) {
+                    for (int pj = 0; pj <= (I >> 1); ++pj) {
+                        const unsigned char *mb = msp + (size_t)aqk_frag(I, pj) * 2 * FR + lane * 16;
+                        const u32x4 vb =
+                            *reinterpret_cast<const u32x4 *>(X + LY::VT + (size_t)(w * 2 + pj) * FR + lane * 16);
+                        acc = mma_bf16_k32(*reinterpret_cast<const u32x4 *>(mb), vb, acc);
+                        acc = mma_bf16_k32(*reinterpret_cast<const u32x4 *>(mb + FR), vb, acc);
+                    }
+                }
+                uacc[r] = acc;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(acc[j]));
+            }
             const int e = scale_exp(wave_max_nonneg(m));
-            *reinterpret_cast<u32x2 *>(slab + SL::u + ((size_t)(I * KT + w) * 64 + lane) * 8) = quad_to_f16(acc * exp2i(-e));
-            if (lane == 0) reinterpret_cast<int *>(slab + SL::uexp)[I * KT + w] = e;
-        });
+            const float sc = exp2i(-e);
+#pragma unroll
+            for (int r = 0; r < NU; ++r) {
+                const int unit = wave + 4 * r;
+                const int w = unit % KT, I = unit / KT;
+                *reinterpret_cast<u32x2 *>(slab + SL::u + ((size_t)(I * KT + w) * 64 + lane) * 8) =
+                    quad_to_f16(uacc[r] * sc);
+                if (lane == 0) reinterpret_cast<int *>(slab + SL::uexp)[I * KT + w] = e;
+            }
+        }
         ent = ent_next;
         ent_next = ent_after;
         a_cur = a_next;
@@ -417,7 +440,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 template <int D>
-int launch_intra_bf16(const PrefillArgs &a, const int32_t *meta, const int4 *table, unsigned char *slabs) {
+int launch_intra_bf16(const PrefillArgs &a, const int32_t *meta, const int4 *table, const float *null_row,
+                      unsigned char *slabs) {
     using LY = Intra4Lds<D>;
     const long long items = (long long)a.plan.max_chunks * a.H;
     if (items <= 0) return 0;
@@ -425,13 +449,16 @@ int launch_intra_bf16(const PrefillArgs &a, const int32_t *meta, const int4 *tab
     const int grid = (int)std::min<long long>(items, 2LL * device_cus());
     hipLaunchKernelGGL(intra4_kernel<D>, dim3(grid), dim3(256), LY::bytes, a.stream,
                        reinterpret_cast<const uint16_t *>(a.q), reinterpret_cast<const uint16_t *>(a.k),
-                       reinterpret_cast<const uint16_t *>(a.v), a.z, a.A, a.beta, meta, table, a.N, a.H,
+                       reinterpret_cast<const uint16_t *>(a.v), a.z, a.A, a.beta, meta, table, null_row, a.N, a.H,
                        a.plan.max_chunks, slabs, a.plan.slab_bytes);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-template int launch_intra_bf16<32>(const PrefillArgs &, const int32_t *, const int4 *, unsigned char *);
-template int launch_intra_bf16<64>(const PrefillArgs &, const int32_t *, const int4 *, unsigned char *);
-template int launch_intra_bf16<128>(const PrefillArgs &, const int32_t *, const int4 *, unsigned char *);
+template int launch_intra_bf16<32>(const PrefillArgs &, const int32_t *, const int4 *, const float *,
+                                     unsigned char *);
+template int launch_intra_bf16<64>(const PrefillArgs &, const int32_t *, const int4 *, const float *,
+                                     unsigned char *);
+template int launch_intra_bf16<128>(const PrefillArgs &, const int32_t *, const int4 *, const float *,
+                                     unsigned char *);
 
 }  // namespace kda

@@ -56,7 +56,8 @@ bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, PrefillPlan *
     p->slab_bytes = sb;
     p->off_meta = 0;
     p->off_table = align256((size_t)(N + 2) * 4);
-    p->off_slabs = p->off_table + align256((size_t)p->max_chunks * 16);
+    p->off_null = p->off_table + align256((size_t)p->max_chunks * 16);
+    p->off_slabs = p->off_null + align256((size_t)dk * 4 + (size_t)dk * 4 + 4);
     p->total = p->off_slabs + (size_t)H * p->max_chunks * sb;
     return true;
 }
@@ -70,10 +71,15 @@ bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, PrefillPlan *
 __global__ void __launch_bounds__(256) chunk_table_kernel(const int32_t *__restrict__ cu, int N,
                                                           int T, int max_chunks,
                                                           int32_t *__restrict__ meta,
-                                                          int4 *__restrict__ table) {
+                                                          int4 *__restrict__ table,
+                                                          float *__restrict__ null_row, int d) {
     __shared__ int32_t scan[256];
     __shared__ int32_t carry;
     const int tid = threadIdx.x;
+    // The null row that rows past a chunk's end read instead of real inputs:
+    // z = -inf gives a zero gate (no decay), and k = q = v = 0, beta = 0.
+    for (int c = tid; c < 2 * d + 1; c += 256)
+        null_row[c] = c < d ? -__builtin_inff() : 0.f;
     if (tid == 0) carry = 0;
     __syncthreads();
     for (int base = 0; base < N; base += 256) {
@@ -872,12 +878,13 @@ static int launch_prefill_t(const PrefillArgs &a) {
     unsigned char *slabs = a.ws + p.off_slabs;
 
     hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, a.stream, a.cu, a.N, a.T,
-                       p.max_chunks, meta, table);
+                       p.max_chunks, meta, table, reinterpret_cast<float *>(a.ws + p.off_null), D);
     if (hipGetLastError() != hipSuccess) return -1;
 
     const long long items = (long long)p.max_chunks * a.H;
     if constexpr (!F32IO) {
-        if (launch_intra_bf16<D>(a, meta, table, slabs) != 0) return -1;
+        if (launch_intra_bf16<D>(a, meta, table, reinterpret_cast<const float *>(a.ws + p.off_null), slabs) != 0)
+            return -1;
     } else if (items > 0) {
         const size_t lds = sizeof(IntraLds<D>);
         if (!set_lds(&intra_kernel<D, F32IO>, lds)) return -1;
