@@ -79,6 +79,10 @@ __device__ __forceinline__ void store_io(void *p, size_t i, float x) {
 // `ea` is exp(A_h).  sigmoid saturates to exactly 0 or 1 at the ends, so the
 // result spans [-5 log2 e, 0].
 // ---------------------------------------------------------------------------
+// The same with nel = -exp(A_h) log2(e) precomputed once per head.
+__device__ __forceinline__ float gate_log2_nel(float nel, float z) {
+    return kGminLog2e * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * nel));
+}
 __device__ __forceinline__ float gate_log2(float ea, float z) {
     float x = ea * z;
     float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
@@ -203,15 +207,16 @@ __device__ __forceinline__ f32x4 mma3_bf16(u32x4 ah, u32x4 al, u32x4 bh, u32x4 b
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// Transpose of a 16x16 accumulator tile, rounded to bf16: the tile enters a
-// 16x16x16 bf16 MFMA as its own A operand (lane (n, g) holds X[4g + j][n],
-// which is the A layout of X^T) against the identity, so the result lane
-// (n, g) holds X[n][4g + j] -- four consecutive columns of row n.  Exact for
-// finite values (each product is a bf16 value times 1 or 0); a non-finite
-// entry turns its whole row non-finite (inf * 0).
-__device__ __forceinline__ u32x2 transpose_tile_bf16(f32x4 x, int lane) {
+// Transpose of a 16x16 tile of packed bf16 values: the tile enters a
+// 16x16x16 bf16 MFMA as its A operand against the identity, so D = A.  Read
+// through the fragment convention, a tile whose lane (m, g) holds X[m][4g + j]
+// (row layout) comes out with lane (n, g) holding X[4g + j][n] (column
+// layout), and an accumulator tile (lane (n, g) holds X[4g + j][n]) comes out
+// with lane (n, g) holding X[n][4g + j].  Exact for finite values (each
+// product is a bf16 value times 1 or 0); a non-finite entry turns its whole
+// row non-finite (inf * 0).
+__device__ __forceinline__ u32x2 transpose_bf16_bits(u32x2 a, int lane) {
     const int n = lane & 15, g = lane >> 4;
-    const u32x2 a = u32x2{f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3])};
     // identity B operand: lane (n, g) holds I[4g + j][n]
     const uint32_t one = 0x3f80u;  // bf16 1.0
     uint32_t e[4];
@@ -221,6 +226,10 @@ __device__ __forceinline__ u32x2 transpose_tile_bf16(f32x4 x, int lane) {
     const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
                                                              __builtin_bit_cast(s16x4, b), zero4(), 0, 0, 0);
     return u32x2{f32x2_to_bf16x2(d[0], d[1]), f32x2_to_bf16x2(d[2], d[3])};
+}
+// The same for a tile of fp32 values, rounded to bf16 first.
+__device__ __forceinline__ u32x2 transpose_tile_bf16(f32x4 x, int lane) {
+    return transpose_bf16_bits(u32x2{f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3])}, lane);
 }
 
 }  // namespace kda

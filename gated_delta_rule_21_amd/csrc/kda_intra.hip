@@ -61,15 +61,6 @@ __device__ __forceinline__ u32x2 transpose_tile_f16(f32x4 x, int lane) {
     return quad_to_f16(d);
 }
 
-// x = hi + lo, both bf16-valued, per element.
-__device__ __forceinline__ void split_quad(f32x4 x, f32x4 &hi, f32x4 &lo) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        hi[j] = bf16_bits_to_f32(f32_to_bf16_bits(x[j]));
-        lo[j] = x[j] - hi[j];
-    }
-}
-
 // A zero the compiler cannot see through.  Lane-dependent constants built
 // from `lane + opaque_zero()` inside the item loop are rebuilt per item
 // instead of being hoisted out of the loop and kept live (or spilled) across it.
@@ -182,7 +173,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int ln = lane & 15, lg = lane >> 4;
         const int row = 16 * b + ln;
         unsigned char *slab = slabs + ((size_t)h * max_chunks + chunk) * slab_stride;
-        const float ea = __expf(a_cur);
+        const float nel = -__expf(a_cur) * kLog2e;       // the gate's exp2 argument per unit z
         const int it_next = it + stride;
         const int4 ent_after = (it_next + stride < total) ? table[(it_next + stride) / H] : make_int4(0, 0, 0, 0);
         const float a_next = it_next < total ? A[it_next % H] : 0.f;
@@ -201,7 +192,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
             f32x4 gl, bt, rf, kev;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                gl[j] = row16_inclusive_scan(gate_log2(ea, R.z[kt][j]));
+                gl[j] = row16_inclusive_scan(gate_log2_nel(nel, R.z[kt][j]));
                 bt[j] = row16_last(gl[j]);
                 rf[j] = fast_exp2(gl[j]);
                 kev[j] = kq[j] * fast_exp2(bt[j] - gl[j]);
@@ -317,14 +308,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
             const float *pfx = fac_lds + (4 + b) * D;
 #pragma unroll
             for (int t = 0; t < KT; ++t) {
-                f32x4 hi, lo;
-                split_quad(kr[t] * ld4(pfx + 16 * t + 4 * lg), hi, lo);
+                // Gamma*K = hi + lo, both bf16, packed
+                const f32x4 gk = kr[t] * ld4(pfx + 16 * t + 4 * lg);
+                const u32x2 hi = u32x2{f32x2_to_bf16x2(gk[0], gk[1]), f32x2_to_bf16x2(gk[2], gk[3])};
+                const f32x4 lf = gk - f32x4{bf16_lo_half(hi[0]), bf16_hi_half(hi[0]), bf16_lo_half(hi[1]),
+                                            bf16_hi_half(hi[1])};
+                const u32x2 lo = u32x2{f32x2_to_bf16x2(lf[0], lf[1]), f32x2_to_bf16x2(lf[2], lf[3])};
                 unsigned char *dg = X + LY::GKT + ((size_t)((t * 2 + (b >> 1)) * 2) * FR) + lane * 16 + (b & 1) * 8;
-                *reinterpret_cast<u32x2 *>(dg) = transpose_tile_bf16(hi, lane);
-                *reinterpret_cast<u32x2 *>(dg + FR) = transpose_tile_bf16(lo, lane);
-                const f32x4 vq = quad_f32<false>(R.v[t]);
+                *reinterpret_cast<u32x2 *>(dg) = transpose_bf16_bits(hi, lane);
+                *reinterpret_cast<u32x2 *>(dg + FR) = transpose_bf16_bits(lo, lane);
                 *reinterpret_cast<u32x2 *>(X + LY::VT + (size_t)(t * 2 + (b >> 1)) * FR + lane * 16 + (b & 1) * 8) =
-                    transpose_tile_bf16(vq, lane);
+                    transpose_bf16_bits(R.v[t], lane);
             }
         }
         if (lane < 16) {
