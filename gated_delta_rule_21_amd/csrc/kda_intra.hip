@@ -32,8 +32,8 @@
 //   1  gate, block-local cumulative log-decay (DPP row scan), kr / qr / ke
 //   F  per-channel decay factors of the chunk
 //   2  Gamma*Q, K~^T (transposed by an identity MFMA), Gram tiles -> A_kk, A_qk
-//   3  (Gamma*K)^T and V^T fragments into LDS; prefetch of the next item;
-//      inverses of the four diagonal 16x16 blocks (forward substitution)
+//   3  (Gamma*K)^T and V^T fragments into LDS; inverses of the four
+//      diagonal 16x16 blocks (forward substitution)
 //   4  off-diagonal blocks of T, one block row per step (fp32 MFMA)
 //   4b M = T Diag(beta), split into bf16 fragments
 //   5  -W and U, stored in the slab

@@ -717,7 +717,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
         // A copies per wave: the last of a step's memory operations, and the
         // only ones still allowed in flight at its end
         constexpr int NA = SL::FA / WPG;
-        static_assert(SL::FA % WPG == 0 && NA < 16, "A fragments per wave");
+        static_assert(SL::FA % WPG == 0 && NA < 16 && NA % 4 == 0, "A fragments per wave");
+        // token range of the sequence, from its first and last chunk records:
+        // chunk c starts at t_first + 64 (c - c_begin), with at most t_end - start rows
+        int t_first = 0, t_end = 0;
+        if (c_begin < c_end) {
+            const int4 e0 = table[c_begin], e1 = table[c_end - 1];
+            t_first = e0.y;
+            t_end = e1.y + e1.z;
+        }
         if (c_begin < c_end) {
             copyA(c_begin, aring);
             copyB(c_begin, bring);
@@ -741,11 +749,20 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             const int *uexp = reinterpret_cast<const int *>(bbuf + (SL::uexp - SL::kdT));
             if (o_L > 0) flush_o(par ^ 1, o_t0, o_L);   // the previous chunk's rows
             if (c + 1 < c_end) {
-                copyB(c + 1, bring + (par ^ 1) * BB);
                 load_u(c + 1, un);
+                copyB(c + 1, bring + (par ^ 1) * BB);
             }
-            if (c + 2 < c_end) copyA(c + 2, aring + ((i + 2) % 3) * AB);
-            const int4 ent = table[c];
+            // A copies of chunk c + 2, issued a few at a time between this
+            // step's products so that the memory pipeline works under the math
+            const bool fetch_a = c + 2 < c_end;
+            const unsigned char *a_src = slab_of(fetch_a ? c + 2 : c);
+            unsigned char *a_dst = aring + ((i + 2) % 3) * AB;
+            auto copyA_part = [&](int r) {
+                const int f = wave + r * WPG;
+                __builtin_amdgcn_global_load_lds(a_src + (size_t)f * 1024 + lane * 16,
+                                                 (__attribute__((address_space(3))) void *)(a_dst + f * 1024), 16, 0,
+                                                 0);
+            };
 
             // S -> fp16 with a per-wave power-of-two scale
             float m = 0.f;
@@ -762,6 +779,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             f32x4 vp[4];
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
+                if (fetch_a) {
+#pragma unroll
+                    for (int r = 0; r < NA / 4; ++r) copyA_part(I * (NA / 4) + r);
+                }
                 f32x4 ws = zero4(), qs = zero4();
 #pragma unroll
                 for (int p = 0; p < KT / 2; ++p) {
@@ -799,8 +820,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
                 a = mma_f16_k32(fragB(SL::kdT, t * 2 + 1), vf1, a);
                 S[t] = S[t] * gam[4 * t + lg] + a * uV;
             }
-            o_t0 = ent.y;
-            o_L = ent.z;
+            o_t0 = t_first + kChunk * i;
+            o_L = min(kChunk, t_end - o_t0);
             // everything but this step's A copies must have landed (memory
             // operations complete in issue order)
             if (c + 2 < c_end)
