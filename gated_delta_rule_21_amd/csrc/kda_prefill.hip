@@ -693,8 +693,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     if constexpr (!F32IO) {
         // ------------------------------------------------------------- bf16 path
         // Output rows go out as whole 16 * WPG-column segments: each wave
-        // transposes its 64 x 16 tile in registers, stages it in LDS, and after
-        // the next barrier every lane stores 16-byte pieces of full rows.
+        // computes its 64 x 16 tile row-major (O^T products), stages it in LDS,
+        // and after the next barrier every lane stores 16-byte pieces of full rows.
         constexpr int OP = SHP::OPITCH;
         constexpr size_t AB = SHP::ABYTES, BB = SHP::BBYTES;
         unsigned char *aring = lds_raw, *bring = lds_raw + 3 * AB;
@@ -787,7 +787,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
                 for (int p = 0; p < KT / 2; ++p) {
                     ws = mma_f16_k32(fragA(SL::negW, I * (KT / 2) + p), sf[p], ws);
-                    qs = mma_f16_k32(fragA(SL::qg, I * (KT / 2) + p), sf[p], qs);
+                    // O^T = S^T (Gamma*Q)^T: the same fragments with the operands
+                    // swapped, so the accumulator holds O row-major (lane (n, g):
+                    // row n, columns 4g..4g+3) and o needs no transpose
+                    qs = mma_f16_k32(sf[p], fragA(SL::qg, I * (KT / 2) + p), qs);
                 }
                 vp[I] = f16x4_to_quad(u[I]) * exp2i(uexp[I * KT + vt]) + ws * uS;
                 acc_o[I] = qs * uS;
@@ -807,11 +810,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             uint16_t *ob = obuf + par * 64 * OP;
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
-                f32x4 a = mma_f16_k32(fragB(SL::aqk, aqk_frag(I, 0)), vf0, zero4());
-                if (I >= 2) a = mma_f16_k32(fragB(SL::aqk, aqk_frag(I, 1)), vf1, a);
+                // (A_qk V')^T = V'^T A_qk^T, row-major like O above
+                f32x4 a = mma_f16_k32(vf0, fragB(SL::aqk, aqk_frag(I, 0)), zero4());
+                if (I >= 2) a = mma_f16_k32(vf1, fragB(SL::aqk, aqk_frag(I, 1)), a);
                 acc_o[I] += a * uV;
                 *reinterpret_cast<u32x2 *>(ob + (16 * I + ln) * OP + 16 * wave + 4 * lg) =
-                    transpose_tile_bf16(acc_o[I], lane);
+                    u32x2{f32x2_to_bf16x2(acc_o[I][0], acc_o[I][1]), f32x2_to_bf16x2(acc_o[I][2], acc_o[I][3])};
             }
             const f32x4 *gam = reinterpret_cast<const f32x4 *>(bbuf + (SL::gamma - SL::kdT));
 #pragma unroll
