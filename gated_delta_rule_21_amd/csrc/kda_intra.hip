@@ -106,29 +106,57 @@ struct Rows4 {
 
 // Rows past the chunk's end read the null row instead (z = -inf, so the gate
 // is 0 and nothing decays; k = q = v = 0; beta = 0), which makes every later
-// step correct for them without masks.  Loads are unconditional and in order
-// of use.
+// step correct for them without masks.  Loads are unconditional.
 template <int D>
-__device__ __forceinline__ void load_rows4(Rows4<D> &R, const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                                           const float *z, const float *beta, const float *null_row, int4 ent, int h,
-                                           int H, int row, int lg) {
-    constexpr int KT = D / 16;
-    const bool ok = row < ent.z;
-    const size_t trow = (size_t)(ent.y + row) * H + h;
+__device__ __forceinline__ void row_sources(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *z,
+                                            const float *null_row, int4 ent, int h, int H, int row,
+                                            const float *&zr, const uint16_t *&kr, const uint16_t *&qr,
+                                            const uint16_t *&vr, size_t &trow, bool &ok) {
+    ok = row < ent.z;
+    trow = (size_t)(ent.y + row) * H + h;
     const uint16_t *nz16 = reinterpret_cast<const uint16_t *>(null_row + D);
-    const float *zr = ok ? z + trow * D : null_row;
-    const uint16_t *kr = ok ? k + trow * D : nz16;
-    const uint16_t *qr = ok ? q + trow * D : nz16;
-    const uint16_t *vr = ok ? v + trow * D : nz16;
+    zr = ok ? z + trow * D : null_row;
+    kr = ok ? k + trow * D : nz16;
+    qr = ok ? q + trow * D : nz16;
+    vr = ok ? v + trow * D : nz16;
+}
+// z and beta: fetched one item ahead (the gate needs them first)
+template <int D>
+__device__ __forceinline__ void load_rows4_z(Rows4<D> &R, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                             const float *z, const float *beta, const float *null_row, int4 ent,
+                                             int h, int H, int row, int lg) {
+    constexpr int KT = D / 16;
+    const float *zr; const uint16_t *kr, *qr, *vr; size_t trow; bool ok;
+    row_sources<D>(q, k, v, z, null_row, ent, h, H, row, zr, kr, qr, vr, trow, ok);
     R.beta = ok ? beta[trow] : null_row[2 * D];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) R.z[kt] = ld4(zr + 16 * kt + 4 * lg);
+}
+// k, q: loaded at the start of the item, in flight while the gate runs
+template <int D>
+__device__ __forceinline__ void load_rows4_kq(Rows4<D> &R, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                               const float *z, const float *null_row, int4 ent, int h, int H,
+                                               int row, int lg) {
+    constexpr int KT = D / 16;
+    const float *zr; const uint16_t *kr, *qr, *vr; size_t trow; bool ok;
+    row_sources<D>(q, k, v, z, null_row, ent, h, H, row, zr, kr, qr, vr, trow, ok);
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
         const int c = 16 * kt + 4 * lg;
-        R.z[kt] = ld4(zr + c);
         R.k[kt] = *reinterpret_cast<const u32x2 *>(kr + c);
         R.q[kt] = *reinterpret_cast<const u32x2 *>(qr + c);
-        R.v[kt] = *reinterpret_cast<const u32x2 *>(vr + c);
     }
+}
+// v: loaded when the Gram phase has released its registers
+template <int D>
+__device__ __forceinline__ void load_rows4_v(Rows4<D> &R, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                             const float *z, const float *null_row, int4 ent, int h, int H, int row,
+                                             int lg) {
+    constexpr int KT = D / 16;
+    const float *zr; const uint16_t *kr, *qr, *vr; size_t trow; bool ok;
+    row_sources<D>(q, k, v, z, null_row, ent, h, H, row, zr, kr, qr, vr, trow, ok);
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) R.v[kt] = *reinterpret_cast<const u32x2 *>(vr + 16 * kt + 4 * lg);
 }
 
 template <int D>
@@ -164,6 +192,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     int4 ent = table[it / H];
     int4 ent_next = (it + stride < total) ? table[(it + stride) / H] : make_int4(0, 0, 0, 0);
     float a_cur = A[it % H];
+    // Raw inputs of the current item; the next item's are fetched during the
+    // solve (phase 4), when few registers are live.
+    Rows4<D> R;
+    load_rows4_z<D>(R, q, k, v, z, beta, null_row, ent, it % H, H, 16 * ((wave + rot0) & 3) + (threadIdx.x & 15),
+                    (threadIdx.x >> 4) & 3);
+    __builtin_amdgcn_s_waitcnt(0);
 
     for (int iter = 0; it < total; it += stride, ++iter) {
         const int chunk = it / H, h = it % H;
@@ -178,11 +212,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int4 ent_after = (it_next + stride < total) ? table[(it_next + stride) / H] : make_int4(0, 0, 0, 0);
         const float a_next = it_next < total ? A[it_next % H] : 0.f;
 
-        // ---- phase 1: gate, block-local cumulative log2-decay, row operands.
-        // The raw inputs are loaded here, not prefetched: the second workgroup
-        // on the CU computes while this one waits.
-        Rows4<D> R;
-        load_rows4<D>(R, q, k, v, z, beta, null_row, ent, h, H, row, lg);
+        // ---- phase 1: gate, block-local cumulative log2-decay, row operands
+        load_rows4_kq<D>(R, q, k, v, z, null_row, ent, h, H, row, lg);
         if (lg == 0) sbeta[row] = R.beta;
         f32x4 kr[KT], qr[KT], ke[KT];
 #pragma unroll
@@ -304,6 +335,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         __syncthreads();
 
         // ---- phase 3: transposed (Gamma*K) split and V fragments into X
+        load_rows4_v<D>(R, q, k, v, z, null_row, ent, h, H, row, lg);
         {
             const float *pfx = fac_lds + (4 + b) * D;
 #pragma unroll
@@ -339,6 +371,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
         __syncthreads();
 
+        // the gate inputs of the next item
+        if (it_next < total)
+            load_rows4_z<D>(R, q, k, v, z, beta, null_row, ent_next, it_next % H, H,
+                            16 * ((wave + rot0 + iter + 1) & 3) + ln, lg);
         // ---- phase 4: T_IJ = -T_II sum_{J<=m<I} A_Im T_mJ, stored at block (J, I)
         for (int I = 1; I < 4; ++I) {
             if (wave < I) {
