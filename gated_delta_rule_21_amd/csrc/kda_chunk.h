@@ -69,11 +69,6 @@ __device__ __forceinline__ f32x4 lds_col4(const float (*a)[P], int row0, int col
     return f32x4{a[row0][col], a[row0 + 1][col], a[row0 + 2][col], a[row0 + 3][col]};
 }
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
-__device__ __forceinline__ u32x4 cat2(u32x2 a, u32x2 b) { return u32x4{a[0], a[1], b[0], b[1]}; }
-template <int TP>
-__device__ __forceinline__ u32x2 lds_bf16x4(const uint16_t (*a)[TP], int row, int col) {
-    return *reinterpret_cast<const u32x2 *>(&a[row][col]);
-}
 
 // Inclusive prefix sum over the 16 lanes of each DPP row (row_shr by 1, 2,
 // 4, 8; lanes shifted in from outside the row read 0).

@@ -33,17 +33,10 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) { return f32x2_to_bf16x2(x, 0.f) & 0xffffu; }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 __device__ __forceinline__ float bf16_lo_half(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi_half(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): 16 mantissa bits in total.
-__device__ __forceinline__ void split_bf16(float x, uint32_t &hi, uint32_t &lo) {
-    hi = f32_to_bf16_bits(x);
-    lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
-}
-__device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return lo16 | (hi16 << 16); }
 
 // Load element i of an io-dtype array as fp32.
 template <bool F32IO>
@@ -226,10 +219,6 @@ __device__ __forceinline__ u32x2 transpose_bf16_bits(u32x2 a, int lane) {
     const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
                                                              __builtin_bit_cast(s16x4, b), zero4(), 0, 0, 0);
     return u32x2{f32x2_to_bf16x2(d[0], d[1]), f32x2_to_bf16x2(d[2], d[3])};
-}
-// The same for a tile of fp32 values, rounded to bf16 first.
-__device__ __forceinline__ u32x2 transpose_tile_bf16(f32x4 x, int lane) {
-    return transpose_bf16_bits(u32x2{f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3])}, lane);
 }
 
 }  // namespace kda

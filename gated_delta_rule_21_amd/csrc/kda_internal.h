@@ -48,9 +48,12 @@ size_t slab_bytes(int dk, int dv, bool f32io);
 
 int launch_decode(const DecodeArgs &a);
 int launch_prefill(const PrefillArgs &a);
-// Intra-chunk kernel of the bf16 path (kda_intra.hip), D = 32, 64, 128.
+// Intra-chunk kernels (kda_intra.hip: bf16 path; kda_intra_f32.hip: fp32
+// path), D = 32, 64, 128.
 template <int D>
 int launch_intra_bf16(const PrefillArgs &a, const int32_t *meta, const int4 *table, const float *null_row,
                       unsigned char *slabs);
+template <int D>
+int launch_intra_f32(const PrefillArgs &a, const int32_t *meta, const int4 *table, unsigned char *slabs);
 
 }  // namespace kda

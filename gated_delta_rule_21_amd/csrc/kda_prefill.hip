@@ -4,10 +4,11 @@
 //   chunk_table_kernel  cu_seqlens -> first chunk of every sequence and a
 //                       (sequence, first token, length) record per chunk;
 //                       chunks of 64 tokens start at every sequence start.
-//   intra_kernel        one workgroup per (chunk, head): the bounded gate,
+//   intra kernels       (kda_intra.hip for bf16 inputs, kda_intra_f32.hip for
+//                       fp32) parallel over (chunk, head): the bounded gate,
 //                       chunk-local log-decays, the decay-rescaled Gram
 //                       matrices, the unit-lower-triangular solve and the
-//                       W / U products.  Writes one "slab" of MFMA-ready
+//                       W / U products.  Write one "slab" of MFMA-ready
 //                       fragments per (chunk, head).
 //   inter_kernel        one wavefront per (sequence, head, 16 value columns):
 //                       walks the sequence's chunks in order, carrying the
@@ -115,453 +116,6 @@ __global__ void __launch_bounds__(256) chunk_table_kernel(const int32_t *__restr
         const int s = min(max(cu[n], 0), T), e = min(max(cu[n + 1], 0), T);
         const int first = s + (c - meta[n]) * kChunk;
         table[c] = make_int4(n, first, min(kChunk, e - first), 0);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Intra-chunk kernel.  Persistent: each workgroup walks (chunk, head) items
-// with a stride of the grid size and prefetches the next item's raw inputs
-// into registers while it computes the current one.
-//
-// In phase 1 wave w owns the 16-row block I = w; lane (ln, lg) = (l % 16,
-// l / 16) holds row 16w + ln and key channels 16kt + 4lg + {0..3}.  That is
-// the MFMA A-operand layout, and a scan over the 16 lanes of a row group
-// gives the block-local cumulative log-decay of every channel.
-// ---------------------------------------------------------------------------
-template <int D>
-struct IntraLds {
-    static constexpr int P = D + 4;          // fp32 row pitch (floats)
-    static constexpr int RB = 4 * P;         // row pitch (bytes) of the row-operand arrays
-    static constexpr int TP = 64 + 4;        // row pitch (elements) of the transposed bf16 arrays
-    // Row operands k_r exp2(Gl_r) and q_r exp2(Gl_r).  bf16 path: per row,
-    // [pair p][hi, lo][lane group][8 bf16], so one 16-byte read is one MFMA
-    // fragment slot; fp32 path: [64][P] floats.  After the Gram phase the
-    // bf16 path reuses both arrays for (Gamma*K)^T split into hi and lo, and
-    // ke's array for M = T Diag(beta) split in the same fragment-row layout.
-    unsigned char krs[64 * RB];
-    unsigned char qrs[64 * RB];
-    float ke[64][P];      // k_i exp2(bt_J - Gl_i); fp32 path: V after the Gram phase
-    float a[64][68];      // A_kk, then T = (I + A_kk)^{-1} in place
-    uint16_t vt[D][TP];   // bf16 path: V^T (bf16 bits)
-    float beta[64];
-    float bt[4][D];       // block log2-decay totals
-    float pfx[4][D];      // exp2(sum_{m<I} bt_m)       chunk start -> start of block I
-    float sfx[4][D];      // exp2(sum_{m>J} bt_m)       end of block J -> chunk end
-    float dg[4][D];       // exp2(-bt_J)                undo one block: diagonal column factor
-    float off[6][D];      // exp2(sum_{J<m<I} bt_m)     blocks strictly between J and I
-};
-
-constexpr int kIntraWaves = 8;
-// Row pitch (bytes) of the split M array: 2 pairs x (hi, lo) x 64 B plus 16 B
-// so that the 16 rows a wave reads at once fall on different LDS banks.
-constexpr int kMsRow = 2 * 128 + 16;
-
-// Raw inputs of one (chunk, head) item for one lane of an 8-wave group:
-// wave w loads row block (w & 3), key-channel half (w >> 2).  Lanes whose
-// row lies past the chunk's end load the chunk's first row instead; the
-// consumer masks them.  Every load is unconditional and issued in the order
-// of use, so a wait for one prefetched register never has to cover the
-// stores issued after the prefetch.
-template <int D, bool F32IO>
-struct IntraRegs {
-    static constexpr int KH = D / 32;  // K16 tiles per channel half
-    using Q = typename std::conditional<F32IO, f32x4, u32x2>::type;
-    float beta;
-    f32x4 z[KH];
-    Q k[KH], q[KH], v[KH];
-};
-
-template <int D, bool F32IO>
-__device__ __forceinline__ void intra_load(IntraRegs<D, F32IO> &R, const void *q, const void *k,
-                                           const void *v, const float *z, const float *beta,
-                                           int4 ent, int h, int H, int lane, int wave) {
-    constexpr int KH = D / 32;
-    constexpr int ES = F32IO ? 4 : 2;
-    using Q = typename IntraRegs<D, F32IO>::Q;
-    const int ln = lane & 15, lg = lane >> 4;
-    const int row = 16 * (wave & 3) + ln;
-    const size_t trow = (size_t)(ent.y + (row < ent.z ? row : 0)) * H + h;
-    const size_t base = trow * D + (D / 2) * (wave >> 2) + 4 * lg;
-    const unsigned char *kb = reinterpret_cast<const unsigned char *>(k);
-    const unsigned char *qb = reinterpret_cast<const unsigned char *>(q);
-    const unsigned char *vb = reinterpret_cast<const unsigned char *>(v);
-    R.beta = beta[trow];
-#pragma unroll
-    for (int kk = 0; kk < KH; ++kk) {
-        const size_t idx = base + 16 * kk;
-        R.z[kk] = ld4(z + idx);
-        R.k[kk] = *reinterpret_cast<const Q *>(kb + idx * ES);
-        R.q[kk] = *reinterpret_cast<const Q *>(qb + idx * ES);
-        R.v[kk] = *reinterpret_cast<const Q *>(vb + idx * ES);
-    }
-}
-
-// Split bf16 row operand in the fragment-row layout: row r, K16 tile kt,
-// lane group g -> 8 bytes of hi at [kt/2][0][g][kt%2], 8 bytes of lo at [kt/2][1][g][kt%2].
-template <int RB>
-__device__ __forceinline__ void store_row_split(unsigned char *arr, int row, int kt, int g, f32x4 x) {
-    const u32x2 hv = {f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3])};
-    const f32x4 hq = f32x4{bf16_lo_half(hv[0]), bf16_hi_half(hv[0]), bf16_lo_half(hv[1]), bf16_hi_half(hv[1])};
-    const f32x4 r4 = x - hq;
-    const u32x2 lv = {f32x2_to_bf16x2(r4[0], r4[1]), f32x2_to_bf16x2(r4[2], r4[3])};
-    unsigned char *b = arr + row * RB + (kt >> 1) * 128 + g * 16 + (kt & 1) * 8;
-    *reinterpret_cast<u32x2 *>(b) = hv;
-    *reinterpret_cast<u32x2 *>(b + 64) = lv;
-}
-
-template <int D, bool F32IO>
-__global__ void __launch_bounds__(64 * kIntraWaves) intra_kernel(
-    const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ v,
-    const float *__restrict__ z, const float *__restrict__ A, const float *__restrict__ beta,
-    const int32_t *__restrict__ meta, const int4 *__restrict__ table, int N, int H,
-    int max_chunks, unsigned char *__restrict__ slabs, size_t slab_stride) {
-    using SL = Slab<D, F32IO>;
-    using LDS = IntraLds<D>;
-    constexpr int KT = D / 16, KH = D / 32;
-    constexpr int NW = kIntraWaves, NTH = 64 * NW;
-    constexpr int P = LDS::P, RB = LDS::RB, TP = LDS::TP;
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
-    LDS &s = *reinterpret_cast<LDS *>(lds_raw);
-    float (*krf)[P] = reinterpret_cast<float (*)[P]>(s.krs);   // fp32 path views
-    float (*qrf)[P] = reinterpret_cast<float (*)[P]>(s.qrs);
-    uint16_t (*gkh)[TP] = reinterpret_cast<uint16_t (*)[TP]>(s.krs);               // bf16 path:
-    uint16_t (*gkl)[TP] = reinterpret_cast<uint16_t (*)[TP]>(s.krs + D * TP * 2);  // (Gamma*K)^T
-    unsigned char *msp = reinterpret_cast<unsigned char *>(&s.ke[0][0]);          // bf16 path: M split
-
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index in an SGPR
-    const int ln = lane & 15, lg = lane >> 4;
-    const int blk = wave & 3, half = wave >> 2;   // phase-1 ownership: row block, channel half
-    const int total = meta[N] * H;
-    const int stride = gridDim.x;
-
-    int it = blockIdx.x;
-    if (it >= total) return;
-    IntraRegs<D, F32IO> R;
-    int4 ent = table[it / H];
-    intra_load<D, F32IO>(R, q, k, v, z, beta, ent, it % H, H, lane, wave);
-    // Nothing else is in flight here: settle these loads so that the waits at
-    // the loop head are set by the loop body alone, where the previous item's
-    // stores stay in flight behind the prefetched loads.
-    __builtin_amdgcn_s_waitcnt(0);
-    // Chunk-table entries and A_h are read through the scalar cache, whose
-    // loads every barrier waits for: fetch them one item ahead of their use.
-    int4 ent_next = (it + stride < total) ? table[(it + stride) / H] : make_int4(0, 0, 0, 0);
-    float a_cur = A[it % H];
-
-    for (; it < total; it += stride) {
-        const int chunk = it / H, h = it % H;
-        const int L = ent.z;
-        unsigned char *slab = slabs + ((size_t)h * max_chunks + chunk) * slab_stride;
-        const float ea = __expf(a_cur);
-        const int it_next = it + stride;
-        const int4 ent_after = (it_next + stride < total) ? table[(it_next + stride) / H] : make_int4(0, 0, 0, 0);
-        const float a_next = it_next < total ? A[it_next % H] : 0.f;
-        const int row = 16 * blk + ln;
-        const bool ok = row < L;
-
-        // ---- phase 1: gate, block-local cumulative log2-decay, row operands
-        for (int i = tid; i < 64 * 68; i += NTH) (&s.a[0][0])[i] = 0.f;
-        if (lg == 0 && wave < 4) s.beta[row] = ok ? R.beta : 0.f;
-        f32x4 krv[KH], qrv[KH], vreg[KH];
-#pragma unroll
-        for (int kk = 0; kk < KH; ++kk) {
-            const int kt = half * KH + kk;
-            const int c0 = 16 * kt + 4 * lg;
-            const f32x4 kq = ok ? quad_f32<F32IO>(R.k[kk]) : zero4();
-            const f32x4 qq = ok ? quad_f32<F32IO>(R.q[kk]) : zero4();
-            vreg[kk] = ok ? quad_f32<F32IO>(R.v[kk]) : zero4();
-            f32x4 gl, bt, rf, kev;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                gl[j] = row16_inclusive_scan(ok ? gate_log2(ea, R.z[kk][j]) : 0.f);
-                bt[j] = row16_last(gl[j]);
-                rf[j] = fast_exp2(gl[j]);
-                kev[j] = kq[j] * fast_exp2(bt[j] - gl[j]);
-            }
-            krv[kk] = kq * rf;
-            qrv[kk] = qq * rf;
-            *reinterpret_cast<f32x4 *>(&s.ke[row][c0]) = kev;
-            if (ln == 15) *reinterpret_cast<f32x4 *>(&s.bt[blk][c0]) = bt;
-            if constexpr (F32IO) {
-                *reinterpret_cast<f32x4 *>(&krf[row][c0]) = krv[kk];
-                *reinterpret_cast<f32x4 *>(&qrf[row][c0]) = qrv[kk];
-            } else {
-                store_row_split<RB>(s.krs, row, kt, lg, krv[kk]);
-                store_row_split<RB>(s.qrs, row, kt, lg, qrv[kk]);
-                const u32x2 vv = ok ? R.v[kk] : u32x2{0u, 0u};
-                s.vt[c0 + 0][row] = (uint16_t)(vv[0] & 0xffffu);
-                s.vt[c0 + 1][row] = (uint16_t)(vv[0] >> 16);
-                s.vt[c0 + 2][row] = (uint16_t)(vv[1] & 0xffffu);
-                s.vt[c0 + 3][row] = (uint16_t)(vv[1] >> 16);
-            }
-        }
-        // The raw inputs are consumed: fetch the next item (bf16 path; the
-        // fp32 path keeps V in registers until phase 3 and fetches there).
-        if constexpr (!F32IO) {
-            if (it_next < total) intra_load<D, F32IO>(R, q, k, v, z, beta, ent_next, it_next % H, H, lane, wave);
-        }
-        __syncthreads();
-
-        for (int c = tid; c < D; c += NTH) {
-            const float b0 = s.bt[0][c], b1 = s.bt[1][c], b2 = s.bt[2][c], b3 = s.bt[3][c];
-            s.pfx[0][c] = 1.f;
-            s.pfx[1][c] = exp2f(b0);
-            s.pfx[2][c] = exp2f(b0 + b1);
-            s.pfx[3][c] = exp2f(b0 + b1 + b2);
-            s.sfx[0][c] = exp2f(b1 + b2 + b3);
-            s.sfx[1][c] = exp2f(b2 + b3);
-            s.sfx[2][c] = exp2f(b3);
-            s.sfx[3][c] = 1.f;
-            s.dg[0][c] = exp2f(-b0);
-            s.dg[1][c] = exp2f(-b1);
-            s.dg[2][c] = exp2f(-b2);
-            s.dg[3][c] = exp2f(-b3);
-            s.off[0][c] = 1.f;             // (0,1)
-            s.off[1][c] = exp2f(b1);       // (0,2)
-            s.off[2][c] = exp2f(b1 + b2);  // (0,3)
-            s.off[3][c] = 1.f;             // (1,2)
-            s.off[4][c] = exp2f(b2);       // (1,3)
-            s.off[5][c] = 1.f;             // (2,3)
-            reinterpret_cast<float *>(slab + SL::gamma)[c] = exp2f(b0 + b1 + b2 + b3);
-        }
-        __syncthreads();
-
-        // ---- phase 2: decayed Gram tiles A_kk (I, J) and A_qk^T, J <= I.
-        // A_kk[r][i] = beta_r sum_c k_rc k_ic e^{G_rc - G_ic} is (row operand of
-        // block I) x (ke of block J) x factor: exp2(-bt_J) on the diagonal block
-        // (the <= e^80 case), the decay of the blocks strictly between J and I
-        // otherwise (<= 1).
-        for_wave_units<10, NW>(wave, [&](int tile) {
-            const int I = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
-            const int J = tile - (I * (I + 1)) / 2;
-            const float *fac = (I == J) ? s.dg[J] : s.off[off_index(J, I)];
-            f32x4 akk = zero4(), aqt = zero4();
-            if constexpr (F32IO) {
-#pragma unroll
-                for (int kt = 0; kt < KT; ++kt) {
-                    const int c0 = 16 * kt + 4 * lg;
-                    const f32x4 kc = lds_quad(s.ke, 16 * J + ln, c0) * ld4(fac + c0);
-                    akk = mma_f32_k16(lds_quad(krf, 16 * I + ln, c0), kc, akk);
-                    aqt = mma_f32_k16(kc, lds_quad(qrf, 16 * I + ln, c0), aqt);
-                }
-            } else {
-                const unsigned char *kr_row = s.krs + (16 * I + ln) * RB + lg * 16;
-                const unsigned char *qr_row = s.qrs + (16 * I + ln) * RB + lg * 16;
-#pragma unroll
-                for (int p = 0; p < KT / 2; ++p) {
-                    const int c0 = 32 * p + 4 * lg, c1 = c0 + 16;
-                    const u32x4 krh = *reinterpret_cast<const u32x4 *>(kr_row + p * 128);
-                    const u32x4 krl = *reinterpret_cast<const u32x4 *>(kr_row + p * 128 + 64);
-                    const u32x4 qrh = *reinterpret_cast<const u32x4 *>(qr_row + p * 128);
-                    const u32x4 qrl = *reinterpret_cast<const u32x4 *>(qr_row + p * 128 + 64);
-                    u32x4 kch, kcl;
-                    quads_to_bf16_split(lds_quad(s.ke, 16 * J + ln, c0) * ld4(fac + c0),
-                                        lds_quad(s.ke, 16 * J + ln, c1) * ld4(fac + c1), kch, kcl);
-                    akk = mma3_bf16(krh, krl, kch, kcl, akk);
-                    aqt = mma3_bf16(kch, kcl, qrh, qrl, aqt);
-                }
-            }
-            // A_kk: lane (n = i, g) holds rows r = 4g + j of the tile
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int rl = 4 * lg + j;
-                float x = akk[j] * s.beta[16 * I + rl];
-                if (I == J && ln >= rl) x = 0.f;
-                s.a[16 * I + rl][16 * J + ln] = x;
-            }
-            // A_qk^T: lane (n = r, g) holds i = 4g + j, i.e. the A_qk operand
-            // fragment of row tile I; keep i <= r on the diagonal tile.
-            f32x4 aq;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) aq[j] = (I == J && 4 * lg + j > ln) ? 0.f : aqt[j];
-            if constexpr (F32IO) {
-                *reinterpret_cast<f32x4 *>(slab + SL::aqk + ((size_t)(I * 4 + J) * 64 + lane) * 16) = aq;
-            } else {
-                const int qf = J >> 1, hh = J & 1;
-                unsigned char *base = slab + SL::aqk + ((size_t)aqk_frag(I, qf) * 64 + lane) * 16 + hh * 8;
-                *reinterpret_cast<u32x2 *>(base) = quad_to_f16(aq);
-                if (I == J && (I & 1) == 0)  // the tile right of an even diagonal shares its fragment
-                    *reinterpret_cast<u32x2 *>(base + 8) = u32x2{0u, 0u};
-            }
-        });
-
-        // Gamma*Q fragments (row tile I, key fragment f) and the transposed,
-        // end-of-chunk-decayed keys ((gamma_C/Gamma)*K)^T (key tile t, row fragment f).
-        for_wave_units<4 * SL::NKF, NW>(wave, [&](int fr) {
-            const int I = fr / SL::NKF, f = fr % SL::NKF;
-            unsigned char *dst = slab + SL::qg + ((size_t)fr * SL::SPL * 64 + lane) * 16;
-            if constexpr (F32IO) {
-                const int c0 = 16 * f + 4 * lg;
-                *reinterpret_cast<f32x4 *>(dst) = lds_quad(qrf, 16 * I + ln, c0) * ld4(&s.pfx[I][c0]);
-            } else {
-                const unsigned char *qr_row = s.qrs + (16 * I + ln) * RB + lg * 16;
-                f32x4 h0, h1, l0, l1;
-                bf16_to_quads(*reinterpret_cast<const u32x4 *>(qr_row + f * 128), h0, h1);
-                bf16_to_quads(*reinterpret_cast<const u32x4 *>(qr_row + f * 128 + 64), l0, l1);
-                const int c0 = 32 * f + 4 * lg, c1 = c0 + 16;
-                store_f16(dst, (h0 + l0) * ld4(&s.pfx[I][c0]), (h1 + l1) * ld4(&s.pfx[I][c1]));
-            }
-        });
-        for_wave_units<KT * SL::NCF, NW>(wave, [&](int fr) {
-            const int t = fr / SL::NCF, f = fr % SL::NCF;
-            const int c = 16 * t + ln;
-            unsigned char *dst = slab + SL::kdT + ((size_t)fr * SL::SPL * 64 + lane) * 16;
-            if constexpr (F32IO) {
-                const int J = f;
-                *reinterpret_cast<f32x4 *>(dst) = lds_col4(s.ke, 16 * J + 4 * lg, c) * s.sfx[J][c];
-            } else {
-                const int J0 = 2 * f, J1 = 2 * f + 1;
-                store_f16(dst, lds_col4(s.ke, 16 * J0 + 4 * lg, c) * s.sfx[J0][c],
-                          lds_col4(s.ke, 16 * J1 + 4 * lg, c) * s.sfx[J1][c]);
-            }
-        });
-        __syncthreads();
-
-        // ---- phase 3: (Gamma*K)^T (bf16) or V (fp32 path) into the freed
-        // arrays, and the diagonal 16x16 inverses, in place.
-        if constexpr (F32IO) {
-#pragma unroll
-            for (int kk = 0; kk < KH; ++kk)
-                *reinterpret_cast<f32x4 *>(&s.ke[row][16 * (half * KH + kk) + 4 * lg]) = vreg[kk];
-            if (it_next < total) intra_load<D, F32IO>(R, q, k, v, z, beta, ent_next, it_next % H, H, lane, wave);
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < KH; ++kk) {
-                const int c0 = 16 * (half * KH + kk) + 4 * lg;
-                const f32x4 gk = krv[kk] * ld4(&s.pfx[blk][c0]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    uint32_t hb, lb;
-                    split_bf16(gk[j], hb, lb);
-                    gkh[c0 + j][row] = (uint16_t)hb;
-                    gkl[c0 + j][row] = (uint16_t)lb;
-                }
-            }
-        }
-        if (wave < 4 && lane < 16) {
-            // forward substitution for column `lane` of (I + A_ww)^{-1}
-            const int b = 16 * wave;
-            float col[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float x = (r == lane) ? 1.f : 0.f;
-#pragma unroll
-                for (int i = 0; i < r; ++i) x -= s.a[b + r][b + i] * col[i];
-                col[r] = x;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s.a[b + r][b + lane] = col[r];
-        }
-        __syncthreads();
-
-        // ---- phase 4: off-diagonal blocks, T_IJ = -T_II sum_{J<=m<I} A_Im T_mJ
-        // (fp32 MFMA), written over A_IJ once every wave has read row block I.
-        for (int I = 1; I < 4; ++I) {
-            f32x4 y = zero4();
-            if (wave < I) {
-                const int J = wave;
-                f32x4 x = zero4();
-                for (int m = J; m < I; ++m)
-                    x = mma_f32_k16(lds_quad(s.a, 16 * I + ln, 16 * m + 4 * lg),
-                                    lds_col4(s.a, 16 * m + 4 * lg, 16 * J + ln), x);
-                y = mma_f32_k16(lds_quad(s.a, 16 * I + ln, 16 * I + 4 * lg), x, zero4());
-            }
-            __syncthreads();
-            if (wave < I) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) s.a[16 * I + 4 * lg + j][16 * wave + ln] = -y[j];
-            }
-            __syncthreads();
-        }
-
-        // ---- phase 4b (bf16 path): M = T Diag(beta), split once, in the
-        // fragment-row layout [row][J pair][hi, lo][lane group][8 bf16] with
-        // rows kMsRow bytes apart.
-        if constexpr (!F32IO) {
-            const int pj = half;
-            const int c0 = 32 * pj + 4 * lg, c1 = c0 + 16;
-            u32x4 mh, ml;
-            quads_to_bf16_split(lds_quad(s.a, row, c0) * ld4(&s.beta[c0]),
-                                lds_quad(s.a, row, c1) * ld4(&s.beta[c1]), mh, ml);
-            unsigned char *b = msp + row * kMsRow + pj * 128 + lg * 16;
-            *reinterpret_cast<u32x4 *>(b) = mh;
-            *reinterpret_cast<u32x4 *>(b + 64) = ml;
-            __syncthreads();
-        }
-
-        // ---- phase 5: -W fragments (from W^T tiles) and U tiles; M = T Diag(beta).
-        // W^T tile (t, I) = sum_J (Gamma*K)^T_{tJ} M^T_{JI}: the accumulator
-        // lane (n = r, g) holds W[16I + r][16t + 4g + j], the A-operand
-        // fragment of -W in the state-propagation product.
-        for_wave_units<4 * SL::NKF, NW>(wave, [&](int unit) {
-            const int I = unit / SL::NKF, tp = unit % SL::NKF;
-            const int nJ = I + 1;
-            if constexpr (F32IO) {
-                const int t = tp;
-                f32x4 acc = zero4();
-                for (int J = 0; J < nJ; ++J) {
-                    const int cJ = 16 * J + 4 * lg;
-                    const f32x4 mq = lds_quad(s.a, 16 * I + ln, cJ) * ld4(&s.beta[cJ]);
-                    const f32x4 gk = lds_col4(krf, 16 * J + 4 * lg, 16 * t + ln) * s.pfx[J][16 * t + ln];
-                    acc = mma_f32_k16(gk, mq, acc);
-                }
-                *reinterpret_cast<f32x4 *>(slab + SL::negW + ((size_t)(I * SL::NKF + tp) * 64 + lane) * 16) = -acc;
-            } else {
-                const int ca = 32 * tp + ln, cb = ca + 16;
-                f32x4 acc0 = zero4(), acc1 = zero4();
-                for (int pj = 0; pj < (nJ + 1) / 2; ++pj) {
-                    const int cJ0 = 32 * pj + 4 * lg, cJ1 = cJ0 + 16;
-                    const unsigned char *mb = msp + (16 * I + ln) * kMsRow + pj * 128 + lg * 16;
-                    const u32x4 mh = *reinterpret_cast<const u32x4 *>(mb);
-                    const u32x4 ml = *reinterpret_cast<const u32x4 *>(mb + 64);
-                    const u32x4 gah = cat2(lds_bf16x4(gkh, ca, cJ0), lds_bf16x4(gkh, ca, cJ1));
-                    const u32x4 gal = cat2(lds_bf16x4(gkl, ca, cJ0), lds_bf16x4(gkl, ca, cJ1));
-                    const u32x4 gbh = cat2(lds_bf16x4(gkh, cb, cJ0), lds_bf16x4(gkh, cb, cJ1));
-                    const u32x4 gbl = cat2(lds_bf16x4(gkl, cb, cJ0), lds_bf16x4(gkl, cb, cJ1));
-                    acc0 = mma3_bf16(gah, gal, mh, ml, acc0);
-                    acc1 = mma3_bf16(gbh, gbl, mh, ml, acc1);
-                }
-                store_f16(slab + SL::negW + ((size_t)(I * SL::NKF + tp) * 64 + lane) * 16, -acc0, -acc1);
-            }
-        });
-        // U tile (I, w) = sum_J M_{IJ} V_{Jw}, in the accumulator layout the
-        // state-propagation kernel starts V' from.
-        for_wave_units<4 * KT, NW>(wave, [&](int unit) {
-            const int I = unit / KT, w = unit % KT;
-            const int nJ = I + 1;
-            f32x4 acc = zero4();
-            if constexpr (F32IO) {
-                for (int J = 0; J < nJ; ++J) {
-                    const int cJ = 16 * J + 4 * lg;
-                    const f32x4 mq = lds_quad(s.a, 16 * I + ln, cJ) * ld4(&s.beta[cJ]);
-                    acc = mma_f32_k16(mq, lds_col4(s.ke, 16 * J + 4 * lg, 16 * w + ln), acc);
-                }
-            } else {
-                for (int pj = 0; pj < (nJ + 1) / 2; ++pj) {
-                    const int cJ0 = 32 * pj + 4 * lg, cJ1 = cJ0 + 16;
-                    const unsigned char *mb = msp + (16 * I + ln) * kMsRow + pj * 128 + lg * 16;
-                    const u32x4 vb = cat2(lds_bf16x4(s.vt, 16 * w + ln, cJ0), lds_bf16x4(s.vt, 16 * w + ln, cJ1));
-                    acc = mma_bf16_k32(*reinterpret_cast<const u32x4 *>(mb), vb, acc);
-                    acc = mma_bf16_k32(*reinterpret_cast<const u32x4 *>(mb + 64), vb, acc);
-                }
-            }
-            if constexpr (F32IO) {
-                *reinterpret_cast<f32x4 *>(slab + SL::u + ((size_t)(I * KT + w) * 64 + lane) * 16) = acc;
-            } else {
-                float m = 0.f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(acc[j]));
-                const int e = scale_exp(wave_max_nonneg(m));
-                *reinterpret_cast<u32x2 *>(slab + SL::u + ((size_t)(I * KT + w) * 64 + lane) * 8) =
-                    quad_to_f16(acc * exp2i(-e));
-                if (lane == 0) reinterpret_cast<int *>(slab + SL::uexp)[I * KT + w] = e;
-            }
-        });
-        ent = ent_next;
-        ent_next = ent_after;
-        a_cur = a_next;
-        __syncthreads();
     }
 }
 
@@ -906,18 +460,11 @@ static int launch_prefill_t(const PrefillArgs &a) {
                        p.max_chunks, meta, table, reinterpret_cast<float *>(a.ws + p.off_null), D);
     if (hipGetLastError() != hipSuccess) return -1;
 
-    const long long items = (long long)p.max_chunks * a.H;
     if constexpr (!F32IO) {
         if (launch_intra_bf16<D>(a, meta, table, reinterpret_cast<const float *>(a.ws + p.off_null), slabs) != 0)
             return -1;
-    } else if (items > 0) {
-        const size_t lds = sizeof(IntraLds<D>);
-        if (!set_lds(&intra_kernel<D, F32IO>, lds)) return -1;
-        const int grid = (int)std::min<long long>(items, (long long)device_cus());
-        hipLaunchKernelGGL((intra_kernel<D, F32IO>), dim3(grid), dim3(64 * kIntraWaves), lds, a.stream, a.q, a.k,
-                           a.v, a.z, a.A, a.beta, meta, table, a.N, a.H, p.max_chunks, slabs,
-                           p.slab_bytes);
-        if (hipGetLastError() != hipSuccess) return -1;
+    } else {
+        if (launch_intra_f32<D>(a, meta, table, slabs) != 0) return -1;
     }
 
     using SHP = InterShape<D, F32IO>;
