@@ -78,6 +78,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--decode-steps", type=int, default=1000)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-small-head", action="store_true",
+                   help="skip the side measurement of the small-head prefill (B=2, H=8, T=8192)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the oracle sample")
     p.add_argument("--copy-probe-gib", type=float, default=0.0,
@@ -117,6 +119,38 @@ def cpu_baseline(pre: dict, target_s: float) -> dict:
             "sample": "fp64 token-loop oracle (C, OpenMP over heads) on the first %d of %d tokens "
                       "of all %d heads of the prefill workload, %.2f s wall; host %s, %d logical "
                       "cores" % (tok, T, H, dt, platform.processor() or platform.machine(), cores)}
+
+
+def small_head_prefill(kda, W, dev, reps: int = 10) -> dict:
+    """Side measurement: the small-head prefill (B=2, H=8, T=8192 each,
+    d=128, bf16), split into segments by the automatic choice and unsplit.
+    HIP events on the launch stream, inputs resident, workspace preallocated."""
+    import torch
+    d = W.make("small_head", device=dev)
+    T, H, D = d["q"].shape
+    N = d["cu_seqlens"].numel() - 1
+    o = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    out = {"workload": "small_head B=2 H=8 T=8192 per sequence d=128 bf16, h0 given"}
+    for P, key in ((0, "auto"), (1, "unsplit")):
+        with kda.prefill_segments(P):
+            segs = kda.kda_prefill_segments(N, T, H, D, D, kda.KDA_BF16)
+            ws = kda.prefill_workspace(N, T, H, D, kda.KDA_BF16, dev)
+            run = lambda: kda.prefill(d["q"], d["k"], d["v"], d["z"], d["A"], d["beta"],
+                                      d["cu_seqlens"], h0=d["h0"], o=o, hT=hT, workspace=ws)
+            for _ in range(3):
+                run()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            del ws
+        out[key] = {"segments": segs, "ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1)}
+    return out
 
 
 def main():
@@ -225,6 +259,8 @@ def main():
                      "kernel": "kda_prefill (chunk table + intra + inter kernels), "
                                "1540 algorithmic B per (token, head) x 6291456 pairs per launch"},
     }
+    if not args.no_small_head:
+        line["small_head"] = small_head_prefill(kda, W, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -9,6 +9,8 @@ Entry points (same names as the C ABI in include/kda.h):
   kda_prefill(...)                  raw C call, pointers as ints
   kda_decode(...)                   raw C call
   kda_prefill_workspace_size(...)
+  kda_set_prefill_segments(P), kda_prefill_segments(...)
+                                    segment split of long sequences
   kda_status_string(status)
 Convenience wrappers over torch tensors:
   prefill(q, k, v, z, A, beta, cu_seqlens, h0=None, ...) -> (o, hT)
@@ -52,6 +54,10 @@ def lib():
     L.kda_prefill_workspace_size.restype = sz
     L.kda_decode.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, vp, vp]
     L.kda_decode.restype = ci
+    L.kda_set_prefill_segments.argtypes = [ci]
+    L.kda_set_prefill_segments.restype = ci
+    L.kda_prefill_segments.argtypes = [ci, ci, ci, ci, ci, ci]
+    L.kda_prefill_segments.restype = ci
     L.kda_status_string.argtypes = [ci]
     L.kda_status_string.restype = ctypes.c_char_p
     L.kda_build_info.restype = ctypes.c_char_p
@@ -74,6 +80,14 @@ def kda_decode(io_dtype, q, k, v, z, A, beta, S_inout, N, H, dk, dv, o, stream) 
 
 def kda_prefill_workspace_size(N, T, H, dk, dv, io_dtype) -> int:
     return int(lib().kda_prefill_workspace_size(N, T, H, dk, dv, io_dtype))
+
+
+def kda_set_prefill_segments(segments: int) -> int:
+    return lib().kda_set_prefill_segments(segments)
+
+
+def kda_prefill_segments(N, T, H, dk, dv, io_dtype) -> int:
+    return lib().kda_prefill_segments(N, T, H, dk, dv, io_dtype)
 
 
 def kda_status_string(status: int) -> str:
@@ -153,6 +167,25 @@ def prefill(q, k, v, z, A, beta, cu_seqlens, h0=None, o=None, hT=None, workspace
     if st != 0:
         raise KdaError("kda_prefill", st)
     return o, hT
+
+
+class prefill_segments:
+    """Context manager: kda_prefill splits sequences into `segments`
+    segments (0 = automatic, 1 = never) inside the block, then restores the
+    automatic choice.  Size workspaces inside the block."""
+
+    def __init__(self, segments: int):
+        self.segments = segments
+
+    def __enter__(self):
+        st = kda_set_prefill_segments(self.segments)
+        if st != 0:
+            raise KdaError("kda_set_prefill_segments", st)
+        return self
+
+    def __exit__(self, *exc):
+        kda_set_prefill_segments(0)
+        return False
 
 
 def decode(q, k, v, z, A, beta, S, o=None):

@@ -12,6 +12,8 @@
 #include "kda.h"
 #include "kda_internal.h"
 
+static_assert(KDA_MAX_PREFILL_SEGMENTS == kda::kMaxSegments, "segment limit");
+
 namespace {
 
 bool supported_dim(int dk, int dv) { return dk == dv && (dk == 32 || dk == 64 || dk == 128); }
@@ -60,8 +62,20 @@ size_t kda_prefill_workspace_size(int N, int T, int H, int dk, int dv, kda_dtype
     if (io_dtype != KDA_BF16 && io_dtype != KDA_F32) return 0;
     if (!supported_dim(dk, dv) || N < 0 || T < 0 || H <= 0) return 0;
     kda::PrefillPlan p;
-    if (!kda::plan_prefill(N, T, H, dk, dv, io_dtype == KDA_F32, &p)) return 0;
+    if (!kda::plan_prefill(N, T, H, dk, dv, io_dtype == KDA_F32, kda::choose_segments(N, T, H, dk), &p)) return 0;
     return p.total;
+}
+
+int kda_prefill_segments(int N, int T, int H, int dk, int dv, kda_dtype io_dtype) {
+    if (io_dtype != KDA_BF16 && io_dtype != KDA_F32) return 0;
+    if (!supported_dim(dk, dv) || N < 0 || T < 0 || H <= 0) return 0;
+    return kda::choose_segments(N, T, H, dk);
+}
+
+int kda_set_prefill_segments(int segments) {
+    if (segments < 0 || segments > KDA_MAX_PREFILL_SEGMENTS) return KDA_ERR_INVALID_ARGUMENT;
+    kda::set_prefill_segments(segments);
+    return KDA_OK;
 }
 
 int kda_prefill(kda_dtype io_dtype, const void *q, const void *k, const void *v, const float *z,
@@ -79,7 +93,7 @@ int kda_prefill(kda_dtype io_dtype, const void *q, const void *k, const void *v,
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_MISALIGNED;
 
     kda::PrefillPlan plan;
-    if (!kda::plan_prefill(N, T, H, dk, dv, io_dtype == KDA_F32, &plan))
+    if (!kda::plan_prefill(N, T, H, dk, dv, io_dtype == KDA_F32, kda::choose_segments(N, T, H, dk), &plan))
         return KDA_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < plan.total) return KDA_ERR_WORKSPACE_TOO_SMALL;
 

@@ -22,13 +22,20 @@ struct DecodeArgs {
 // workspace base; every region is 256-byte aligned.
 struct PrefillPlan {
     int max_chunks;          // ceil(T / 64) + N: an upper bound on the chunk count
+    int P;                   // segment slots per sequence (1: no split)
     size_t slab_bytes;       // per (chunk, head) intermediate slab
     size_t off_meta;         // int32 [N + 1] per-sequence first chunk, then [1] total
     size_t off_table;        // int32x4 [max_chunks]: sequence, first token, length, -
     size_t off_null;         // the null row: z = -inf [dk] fp32, zeros [max(dk,dv)] io dtype, beta = 0
+    size_t off_segs;         // int32x4 [N * P]: sequence, first chunk, end chunk, flags
+    size_t off_trans;        // P > 1: fp32 [N * P][H][2][dk * dk]: M row-major, then S~ in state layout
+    size_t off_sin;          // P > 1: fp32 [N * P][H][dv][dk] incoming state of every segment
     size_t off_slabs;        // slabs, head-major: [H][max_chunks]
     size_t total;
 };
+
+// Largest segment count per sequence.
+constexpr int kMaxSegments = 16;
 
 struct PrefillArgs {
     bool f32io;
@@ -43,7 +50,11 @@ struct PrefillArgs {
     hipStream_t stream;
 };
 
-bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, PrefillPlan *plan);
+bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, int P, PrefillPlan *plan);
+// Segment count the prefill uses for these sizes, and the process-wide
+// setting that overrides it (0: automatic).
+int choose_segments(int N, int T, int H, int d);
+void set_prefill_segments(int p);
 size_t slab_bytes(int dk, int dv, bool f32io);
 
 int launch_decode(const DecodeArgs &a);

@@ -34,6 +34,7 @@
 #include "kda_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 namespace kda {
@@ -50,22 +51,36 @@ size_t slab_bytes(int dk, int dv, bool f32io) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, PrefillPlan *p) {
+bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, int P, PrefillPlan *p) {
     size_t sb = slab_bytes(dk, dv, f32io);
-    if (sb == 0 || N < 0 || T < 0 || H <= 0) return false;
+    if (sb == 0 || N < 0 || T < 0 || H <= 0 || P < 1 || P > kMaxSegments) return false;
     p->max_chunks = (int)(((long long)T + kChunk - 1) / kChunk + N);
     p->slab_bytes = sb;
+    p->P = P;
     p->off_meta = 0;
     p->off_table = align256((size_t)(N + 2) * 4);
     p->off_null = p->off_table + align256((size_t)p->max_chunks * 16);
-    p->off_slabs = p->off_null + align256((size_t)dk * 4 + (size_t)dk * 4 + 4);
+    p->off_segs = p->off_null + align256((size_t)dk * 4 + (size_t)dk * 4 + 4);
+    const size_t units = (size_t)N * P * H, dd = (size_t)dk * dk * 4;
+    p->off_trans = p->off_segs + align256((size_t)N * P * 16);
+    p->off_sin = p->off_trans + (P > 1 ? units * 2 * dd : 0);
+    p->off_slabs = p->off_sin + (P > 1 ? units * dd : 0);
     p->total = p->off_slabs + (size_t)H * p->max_chunks * sb;
     return true;
 }
 
+// Segment flags: a sequence's chunks are split into runs ("segments") that
+// the inter kernel walks independently once each segment's incoming state is
+// known (intra-device context parallelism).
+constexpr int kSegValid = 1, kSegFirst = 2, kSegLast = 4;
+// inter_kernel modes: the outputs and final states; the segment's transition
+// matrix M (run from the identity with U = 0); its offset S~ (run from zero)
+constexpr int kModeOutput = 0, kModeTransM = 1, kModeTransS = 2;
+
 // ---------------------------------------------------------------------------
 // Chunk table.  One workgroup.  meta[n] = first chunk of sequence n,
-// meta[N] = number of chunks; table[c] = {n, first token, length, 0}.
+// meta[N] = number of chunks; table[c] = {n, first token, length, 0};
+// segs[n P + k] = {n, first chunk, end chunk, flags} of segment k of sequence n.
 // Sequence bounds are clamped to [0, T] and the chunk count to max_chunks,
 // so a malformed cu_seqlens can give wrong results but no stray access.
 // ---------------------------------------------------------------------------
@@ -73,7 +88,8 @@ __global__ void __launch_bounds__(256) chunk_table_kernel(const int32_t *__restr
                                                           int T, int max_chunks,
                                                           int32_t *__restrict__ meta,
                                                           int4 *__restrict__ table,
-                                                          float *__restrict__ null_row, int d) {
+                                                          float *__restrict__ null_row, int d, int P,
+                                                          int4 *__restrict__ segs) {
     __shared__ int32_t scan[256];
     __shared__ int32_t carry;
     const int tid = threadIdx.x;
@@ -116,6 +132,20 @@ __global__ void __launch_bounds__(256) chunk_table_kernel(const int32_t *__restr
         const int s = min(max(cu[n], 0), T), e = min(max(cu[n + 1], 0), T);
         const int first = s + (c - meta[n]) * kChunk;
         table[c] = make_int4(n, first, min(kChunk, e - first), 0);
+    }
+    // segments: sequence n is cut into Pn = clamp(chunks, 1, P) runs of
+    // consecutive chunks of near-equal length; slots past Pn are invalid
+    for (int i = tid; i < N * P; i += 256) {
+        const int n = i / P, k = i % P;
+        const int c0 = meta[n], nc = meta[n + 1] - c0;
+        const int pn = max(1, min(P, nc));
+        int4 r = make_int4(n, 0, 0, 0);
+        if (k < pn) {
+            r.y = c0 + (int)((long long)k * nc / pn);
+            r.z = c0 + (int)((long long)(k + 1) * nc / pn);
+            r.w = kSegValid | (k == 0 ? kSegFirst : 0) | (k == pn - 1 ? kSegLast : 0);
+        }
+        segs[i] = r;
     }
 }
 
@@ -189,11 +219,12 @@ __device__ __forceinline__ void store_o_tile(void *o, const f32x4 (&acc)[4], int
     }
 }
 
-template <int D, bool F32IO>
+template <int D, bool F32IO, int MODE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) inter_kernel(
-    const float *__restrict__ h0, const int32_t *__restrict__ meta, const int4 *__restrict__ table,
-    int N, int H, int max_chunks, const unsigned char *__restrict__ slabs, size_t slab_stride,
-    void *__restrict__ o, float *__restrict__ hT, int groups) {
+    const float *__restrict__ h0, const float *__restrict__ s_in, const int4 *__restrict__ segs,
+    const int4 *__restrict__ table, int nseg, int H, int max_chunks, const unsigned char *__restrict__ slabs,
+    size_t slab_stride, void *__restrict__ o, float *__restrict__ hT, float *__restrict__ trans, int groups) {
+    static_assert(MODE == kModeOutput || MODE == kModeTransM || MODE == kModeTransS, "mode");
     using SL = Slab<D, F32IO>;
     using SHP = InterShape<D, F32IO>;
     constexpr int KT = D / 16;
@@ -201,26 +232,47 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     constexpr size_t BUF = (size_t)(SL::FA + SL::FB) * SL::FRAG;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
 
-    // blockIdx -> (pair, column group) with every group of a pair on the same XCD
+    // blockIdx -> (segment and head, column group) with every group of a
+    // (segment, head) on the same XCD
     const int b = blockIdx.x;
     const int xcd = b & 7, rest = b >> 3;
     const int cg = rest % groups;
-    const int pair = (rest / groups) * 8 + xcd;
-    if (pair >= N * H) return;
-    const int n = pair / H, h = pair % H;
+    const int unit = (rest / groups) * 8 + xcd;
+    if (unit >= nseg * H) return;
+    const int sg = unit / H, h = unit % H;
+    const int4 rec = segs[sg];
+    if (!(rec.w & kSegValid)) return;
+    if (MODE != kModeOutput && (rec.w & kSegLast)) return;   // no transition after the last segment
+    const int n = rec.x;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index in an SGPR
     const int ln = lane & 15, lg = lane >> 4;
     const int vt = cg * WPG + wave;
     const int col = 16 * vt + ln;
 
+    // initial state: h0 (or zero) for a sequence in one segment, otherwise
+    // the incoming state the combine kernel wrote (for the first segment a
+    // copy of h0, so that h0 is never read here when hT may overwrite it);
+    // the identity for the transition matrix, zero for its offset
     f32x4 S[KT];
-    const size_t srow = ((size_t)pair * D + col) * D;
+    {
+        const float *src = nullptr;
+        if constexpr (MODE == kModeOutput)
+            src = (rec.w & kSegFirst) && (rec.w & kSegLast)
+                      ? (h0 ? h0 + ((size_t)(n * H + h) * D + col) * D : nullptr)
+                      : s_in + ((size_t)(sg * H + h) * D + col) * D;
 #pragma unroll
-    for (int t = 0; t < KT; ++t)
-        S[t] = h0 ? *reinterpret_cast<const f32x4 *>(h0 + srow + 16 * t + 4 * lg) : zero4();
+        for (int t = 0; t < KT; ++t) {
+            if constexpr (MODE == kModeTransM) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) S[t][j] = (16 * t + 4 * lg + j == col) ? 1.f : 0.f;
+            } else {
+                S[t] = src ? *reinterpret_cast<const f32x4 *>(src + 16 * t + 4 * lg) : zero4();
+            }
+        }
+    }
 
-    const int c_begin = meta[n], c_end = meta[n + 1];
+    const int c_begin = rec.y, c_end = rec.z;
     auto slab_of = [&](int c) { return slabs + ((size_t)h * max_chunks + c) * slab_stride; };
     // U: fp32 tiles (fp32 path) or fp16 tiles with a per-tile exponent (bf16 path)
     using UReg = typename std::conditional<F32IO, f32x4, u32x2>::type;
@@ -283,7 +335,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
         if (c_begin < c_end) {
             copyA(c_begin, aring);
             copyB(c_begin, bring);
-            load_u(c_begin, u);
+            if constexpr (MODE != kModeTransM) load_u(c_begin, u);
             if (c_begin + 1 < c_end) copyA(c_begin + 1, aring + AB);
         }
         wait_all_memory();
@@ -301,9 +353,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
                 return *reinterpret_cast<const u32x4 *>(abuf + off + ((size_t)idx * 64 + lane) * 16);
             };
             const int *uexp = reinterpret_cast<const int *>(bbuf + (SL::uexp - SL::kdT));
-            if (o_L > 0) flush_o(par ^ 1, o_t0, o_L);   // the previous chunk's rows
+            if constexpr (MODE == kModeOutput) {
+                if (o_L > 0) flush_o(par ^ 1, o_t0, o_L);   // the previous chunk's rows
+            }
             if (c + 1 < c_end) {
-                load_u(c + 1, un);
+                if constexpr (MODE != kModeTransM) load_u(c + 1, un);
                 copyB(c + 1, bring + (par ^ 1) * BB);
             }
             // A copies of chunk c + 2, issued a few at a time between this
@@ -344,9 +398,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
                     // O^T = S^T (Gamma*Q)^T: the same fragments with the operands
                     // swapped, so the accumulator holds O row-major (lane (n, g):
                     // row n, columns 4g..4g+3) and o needs no transpose
-                    qs = mma_f16_k32(sf[p], fragA(SL::qg, I * (KT / 2) + p), qs);
+                    if constexpr (MODE == kModeOutput) qs = mma_f16_k32(sf[p], fragA(SL::qg, I * (KT / 2) + p), qs);
                 }
-                vp[I] = f16x4_to_quad(u[I]) * exp2i(uexp[I * KT + vt]) + ws * uS;
+                if constexpr (MODE == kModeTransM)
+                    vp[I] = ws * uS;
+                else
+                    vp[I] = f16x4_to_quad(u[I]) * exp2i(uexp[I * KT + vt]) + ws * uS;
                 acc_o[I] = qs * uS;
             }
 
@@ -361,15 +418,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             const u32x4 vf0 = quads_to_f16(vp[0] * dV, vp[1] * dV);
             const u32x4 vf1 = quads_to_f16(vp[2] * dV, vp[3] * dV);
 
-            uint16_t *ob = obuf + par * 64 * OP;
+            if constexpr (MODE == kModeOutput) {
+                uint16_t *ob = obuf + par * 64 * OP;
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                // (A_qk V')^T = V'^T A_qk^T, row-major like O above
-                f32x4 a = mma_f16_k32(vf0, fragB(SL::aqk, aqk_frag(I, 0)), zero4());
-                if (I >= 2) a = mma_f16_k32(vf1, fragB(SL::aqk, aqk_frag(I, 1)), a);
-                acc_o[I] += a * uV;
-                *reinterpret_cast<u32x2 *>(ob + (16 * I + ln) * OP + 16 * wave + 4 * lg) =
-                    u32x2{f32x2_to_bf16x2(acc_o[I][0], acc_o[I][1]), f32x2_to_bf16x2(acc_o[I][2], acc_o[I][3])};
+                for (int I = 0; I < 4; ++I) {
+                    // (A_qk V')^T = V'^T A_qk^T, row-major like O above
+                    f32x4 a = mma_f16_k32(vf0, fragB(SL::aqk, aqk_frag(I, 0)), zero4());
+                    if (I >= 2) a = mma_f16_k32(vf1, fragB(SL::aqk, aqk_frag(I, 1)), a);
+                    acc_o[I] += a * uV;
+                    *reinterpret_cast<u32x2 *>(ob + (16 * I + ln) * OP + 16 * wave + 4 * lg) =
+                        u32x2{f32x2_to_bf16x2(acc_o[I][0], acc_o[I][1]), f32x2_to_bf16x2(acc_o[I][2], acc_o[I][3])};
+                }
             }
             const f32x4 *gam = reinterpret_cast<const f32x4 *>(bbuf + (SL::gamma - SL::kdT));
 #pragma unroll
@@ -387,44 +446,60 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             else
                 wait_all_memory();
             __syncthreads();
+            if constexpr (MODE != kModeTransM) {
 #pragma unroll
-            for (int I = 0; I < 4; ++I) u[I] = un[I];
+                for (int I = 0; I < 4; ++I) u[I] = un[I];
+            }
         }
-        if (o_L > 0) flush_o((c_end - c_begin - 1) & 1, o_t0, o_L);
+        if constexpr (MODE == kModeOutput) {
+            if (o_L > 0) flush_o((c_end - c_begin - 1) & 1, o_t0, o_L);
+        }
         o_L = 0;
     } else {
         // ------------------------------------------------------------- fp32 path
         unsigned char *buf = lds_raw;
         if (c_begin < c_end) {
             copy_A(c_begin, buf);
-            load_u(c_begin, u);
+            if constexpr (MODE != kModeTransM) load_u(c_begin, u);
         }
         wait_all_memory();
         __syncthreads();
         for (int c = c_begin; c < c_end; ++c) {
             copy_B(c, buf);
-            if (c + 1 < c_end) load_u(c + 1, un);
-            if (o_L > 0) store_o_tile<F32IO>(o, acc_o, o_t0, o_L, H, h, D, col, lg);
+            if constexpr (MODE != kModeTransM) {
+                if (c + 1 < c_end) load_u(c + 1, un);
+            }
+            if constexpr (MODE == kModeOutput) {
+                if (o_L > 0) store_o_tile<F32IO>(o, acc_o, o_t0, o_L, H, h, D, col, lg);
+            }
             const int4 ent = table[c];
             f32x4 vp[4];
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
-                vp[I] = u[I];
+                if constexpr (MODE == kModeTransM)
+                    vp[I] = zero4();
+                else
+                    vp[I] = u[I];
                 acc_o[I] = zero4();
 #pragma unroll
                 for (int t = 0; t < KT; ++t) {
                     vp[I] = mma_f32_k16(__builtin_bit_cast(f32x4, frag(buf, SL::negW, I * KT + t)), S[t], vp[I]);
-                    acc_o[I] = mma_f32_k16(__builtin_bit_cast(f32x4, frag(buf, SL::qg, I * KT + t)), S[t], acc_o[I]);
+                    if constexpr (MODE == kModeOutput)
+                        acc_o[I] =
+                            mma_f32_k16(__builtin_bit_cast(f32x4, frag(buf, SL::qg, I * KT + t)), S[t], acc_o[I]);
                 }
             }
             wait_all_memory();
             __syncthreads();
             if (c + 1 < c_end) copy_A(c + 1, buf);
+            if constexpr (MODE == kModeOutput) {
 #pragma unroll
-            for (int I = 0; I < 4; ++I)
+                for (int I = 0; I < 4; ++I)
 #pragma unroll
-                for (int J = 0; J <= I; ++J)
-                    acc_o[I] = mma_f32_k16(__builtin_bit_cast(f32x4, frag(buf, SL::aqk, I * 4 + J)), vp[J], acc_o[I]);
+                    for (int J = 0; J <= I; ++J)
+                        acc_o[I] =
+                            mma_f32_k16(__builtin_bit_cast(f32x4, frag(buf, SL::aqk, I * 4 + J)), vp[J], acc_o[I]);
+            }
             const f32x4 *gam = gamma_of(buf);
 #pragma unroll
             for (int t = 0; t < KT; ++t) {
@@ -437,15 +512,111 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             o_L = ent.z;
             wait_all_memory();
             __syncthreads();
+            if constexpr (MODE != kModeTransM) {
 #pragma unroll
-            for (int I = 0; I < 4; ++I) u[I] = un[I];
+                for (int I = 0; I < 4; ++I) u[I] = un[I];
+            }
         }
     }
-    if (o_L > 0) store_o_tile<F32IO>(o, acc_o, o_t0, o_L, H, h, D, col, lg);
-    if (hT) {
+    if constexpr (MODE == kModeOutput) {
+        if (o_L > 0) store_o_tile<F32IO>(o, acc_o, o_t0, o_L, H, h, D, col, lg);
+        if (hT && (rec.w & kSegLast)) {
+            float *dst = hT + ((size_t)(n * H + h) * D + col) * D;
 #pragma unroll
-        for (int t = 0; t < KT; ++t) *reinterpret_cast<f32x4 *>(hT + srow + 16 * t + 4 * lg) = S[t];
+            for (int t = 0; t < KT; ++t) *reinterpret_cast<f32x4 *>(dst + 16 * t + 4 * lg) = S[t];
+        }
+    } else if constexpr (MODE == kModeTransS) {
+        // the offset S~ of the transition, in the state layout [value column][key]
+        float *dst = trans + (((size_t)(sg * H + h) * 2 + 1) * D + col) * D;
+#pragma unroll
+        for (int t = 0; t < KT; ++t) *reinterpret_cast<f32x4 *>(dst + 16 * t + 4 * lg) = S[t];
+    } else {
+        // the transition matrix M (dk x dk), row-major: M[i][j] at i * D + j;
+        // this lane holds M[16t + 4g + j][col]
+        float *dst = trans + ((size_t)(sg * H + h) * 2) * D * D;
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dst[(size_t)(16 * t + 4 * lg + j) * D + col] = S[t][j];
     }
+}
+
+// ---------------------------------------------------------------------------
+// Segment combine.  The per-chunk update S <- (Diag(gamma_C) - K~^T W) S + K~^T U
+// is affine in S, so a segment maps its incoming state S_in to M S_in + S~
+// (the cross-device merge of "Kimi K3：架构…" §9.3 and the KCP recurrence of
+// P3 Eq 17, applied here to segments on one device).  For a sequence in
+// Pn > 1 segments: S_in(0) = h0 (or zero), S_in(k + 1) = M_k S_in(k) + S~_k,
+// each written to the segment's slot of s_in.  One wave per (sequence, head,
+// 16 value columns), the state in fp32 accumulators, fp32 MFMA; M is read
+// row-major from the transition buffer as A fragments.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ h0, const int4 *__restrict__ segs,
+                                                      int N, int H, int P, const float *__restrict__ trans,
+                                                      float *__restrict__ s_in, int groups) {
+    constexpr int KT = D / 16;
+    constexpr int WPG = KT < 4 ? KT : 4;
+    const int b = blockIdx.x;
+    const int xcd = b & 7, rest = b >> 3;
+    const int cg = rest % groups;
+    const int unit = (rest / groups) * 8 + xcd;
+    if (unit >= N * H) return;
+    const int n = unit / H, h = unit % H;
+    if (segs[n * P].w & kSegLast) return;   // one segment: its pass reads h0 itself
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int ln = lane & 15, lg = lane >> 4;
+    const int col = 16 * (cg * WPG + wave) + ln;
+
+    f32x4 S[KT];
+    const float *src = h0 ? h0 + ((size_t)(n * H + h) * D + col) * D : nullptr;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) S[t] = src ? *reinterpret_cast<const f32x4 *>(src + 16 * t + 4 * lg) : zero4();
+    auto store = [&](int sg) {
+        float *dst = s_in + ((size_t)(sg * H + h) * D + col) * D;
+#pragma unroll
+        for (int t = 0; t < KT; ++t) *reinterpret_cast<f32x4 *>(dst + 16 * t + 4 * lg) = S[t];
+    };
+    store(n * P);
+    for (int k = 0; k + 1 < P; ++k) {
+        const int sg = n * P + k;
+        if (segs[sg].w & kSegLast) break;
+        const float *M = trans + (size_t)(sg * H + h) * 2 * D * D;
+        const float *St = M + (size_t)D * D + (size_t)col * D;
+        f32x4 nx[KT];
+#pragma unroll
+        for (int I = 0; I < KT; ++I) {
+            nx[I] = *reinterpret_cast<const f32x4 *>(St + 16 * I + 4 * lg);
+#pragma unroll
+            for (int t = 0; t < KT; ++t)
+                nx[I] = mma_f32_k16(*reinterpret_cast<const f32x4 *>(M + (size_t)(16 * I + ln) * D + 16 * t + 4 * lg),
+                                    S[t], nx[I]);
+        }
+#pragma unroll
+        for (int t = 0; t < KT; ++t) S[t] = nx[t];
+        store(sg + 1);
+    }
+}
+
+// Segments per sequence.  A set count (kda_set_prefill_segments) wins;
+// otherwise a sequence is split only when the (sequence, head, column group)
+// workgroups of one pass fill less than half the device, into as many
+// segments as fill it once, each of at least 4 chunks.
+static std::atomic<int> g_segments{0};
+
+void set_prefill_segments(int p) { g_segments.store(p); }
+
+int choose_segments(int N, int T, int H, int d) {
+    const int forced = g_segments.load();
+    if (forced > 0) return forced;
+    if (N <= 0 || T <= 0 || H <= 0) return 1;
+    const long long blocks = (long long)N * H * (d == 128 ? 2 : 1);
+    const int cus = device_cus();
+    if (2 * blocks >= cus) return 1;
+    const long long avg_chunks = (long long)T / kChunk / N;
+    const long long p = std::min<long long>({(long long)kMaxSegments, cus / blocks, avg_chunks / 4});
+    return p > 1 ? (int)p : 1;
 }
 
 // ---------------------------------------------------------------------------
@@ -456,8 +627,9 @@ static int launch_prefill_t(const PrefillArgs &a) {
     int4 *table = reinterpret_cast<int4 *>(a.ws + p.off_table);
     unsigned char *slabs = a.ws + p.off_slabs;
 
+    int4 *segs = reinterpret_cast<int4 *>(a.ws + p.off_segs);
     hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, a.stream, a.cu, a.N, a.T,
-                       p.max_chunks, meta, table, reinterpret_cast<float *>(a.ws + p.off_null), D);
+                       p.max_chunks, meta, table, reinterpret_cast<float *>(a.ws + p.off_null), D, p.P, segs);
     if (hipGetLastError() != hipSuccess) return -1;
 
     if constexpr (!F32IO) {
@@ -469,15 +641,30 @@ static int launch_prefill_t(const PrefillArgs &a) {
 
     using SHP = InterShape<D, F32IO>;
     const int groups = SHP::KT / SHP::WPG;
-    const int pairs = a.N * a.H;
-    if (pairs > 0) {
-        if (!set_lds(&inter_kernel<D, F32IO>, SHP::lds_bytes)) return -1;
-        const int pair_blocks = (pairs + 7) / 8 * 8;
-        hipLaunchKernelGGL((inter_kernel<D, F32IO>), dim3(pair_blocks * groups), dim3(SHP::NT),
-                           SHP::lds_bytes, a.stream, a.h0, meta, table, a.N, a.H, p.max_chunks, slabs,
-                           p.slab_bytes, a.o, a.hT, groups);
+    if (a.N == 0) return 0;
+    const int nseg = a.N * p.P;
+    const int unit_blocks = (nseg * a.H + 7) / 8 * 8;
+    float *trans = reinterpret_cast<float *>(a.ws + p.off_trans);
+    float *s_in = reinterpret_cast<float *>(a.ws + p.off_sin);
+    auto inter = [&](auto mode) -> bool {
+        constexpr int M = decltype(mode)::value;
+        if (!set_lds(&inter_kernel<D, F32IO, M>, SHP::lds_bytes)) return false;
+        hipLaunchKernelGGL((inter_kernel<D, F32IO, M>), dim3(unit_blocks * groups), dim3(SHP::NT), SHP::lds_bytes,
+                           a.stream, a.h0, s_in, segs, table, nseg, a.H, p.max_chunks, slabs, p.slab_bytes, a.o,
+                           a.hT, trans, groups);
+        return hipGetLastError() == hipSuccess;
+    };
+    if (p.P > 1) {
+        // transitions of every segment but a sequence's last, then the
+        // incoming state of every segment
+        if (!inter(std::integral_constant<int, kModeTransM>{})) return -1;
+        if (!inter(std::integral_constant<int, kModeTransS>{})) return -1;
+        const int chain_blocks = (a.N * a.H + 7) / 8 * 8;
+        hipLaunchKernelGGL((combine_kernel<D>), dim3(chain_blocks * groups), dim3(SHP::NT), 0, a.stream, a.h0, segs,
+                           a.N, a.H, p.P, trans, s_in, groups);
         if (hipGetLastError() != hipSuccess) return -1;
     }
+    if (!inter(std::integral_constant<int, kModeOutput>{})) return -1;
     return 0;
 }
 

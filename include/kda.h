@@ -70,9 +70,39 @@ typedef enum kda_status {
 /*
  * Workspace bytes kda_prefill needs for these sizes.  Depends only on the
  * arguments (an upper bound over every cu_seqlens with N sequences and T
- * tokens).  Returns 0 for sizes kda_prefill would reject.
+ * tokens), the segment setting below and the device's compute-unit count.
+ * Returns 0 for sizes kda_prefill would reject.
  */
 size_t kda_prefill_workspace_size(int N, int T, int H, int dk, int dv, kda_dtype io_dtype);
+
+/*
+ * Intra-device context parallelism ("Kimi K3：架构…" §8.1 and §11.1: a
+ * planner splits one sequence over a device's compute units; the pieces'
+ * state transitions are computed without the incoming state and merged
+ * exactly).  kda_prefill may cut each sequence into up to P segments of
+ * consecutive 64-token chunks.  For every segment but a sequence's last it
+ * computes the affine map S_in -> M S_in + S~ of its chunks (M in
+ * R^{dk x dk}, S~ in R^{dk x dv}), composes the maps in order from h0
+ * (the merge S = S~ + M S_in of the KCP scheme, P3 Eq 17), and then runs
+ * every segment's outputs from its own incoming state in parallel.  The
+ * result equals the unsplit recurrence up to rounding.
+ *
+ * The default (0) splits only when the workgroups of one pass would fill
+ * less than half of the device: few sequences times heads, long sequences.
+ *
+ * kda_set_prefill_segments sets a process-wide segment count: 0 = automatic,
+ * 1 = never split, 2..KDA_MAX_PREFILL_SEGMENTS = split every sequence of at
+ * least that many chunks into that many segments (shorter ones into one
+ * segment per chunk).  Returns KDA_OK or KDA_ERR_INVALID_ARGUMENT.  It
+ * changes kda_prefill_workspace_size: set it before sizing a workspace, and
+ * not while another thread sizes or launches a prefill.
+ *
+ * kda_prefill_segments returns the segment count kda_prefill would use for
+ * these sizes now (>= 1), or 0 for sizes kda_prefill would reject.
+ */
+#define KDA_MAX_PREFILL_SEGMENTS 16
+int kda_set_prefill_segments(int segments);
+int kda_prefill_segments(int N, int T, int H, int dk, int dv, kda_dtype io_dtype);
 
 /*
  * Chunkwise prefill over N packed sequences (T tokens in total).

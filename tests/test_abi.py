@@ -20,7 +20,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["kda_build_info", "kda_decode", "kda_prefill",
-                                           "kda_prefill_workspace_size", "kda_status_string"])
+                                           "kda_prefill_segments", "kda_prefill_workspace_size",
+                                           "kda_set_prefill_segments", "kda_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -94,3 +95,29 @@ def test_decode_rejects_bad_arguments():
     assert d(q=None) == -2
     assert d(S=FAKE + 8) == -5
     assert d(o=FAKE + 4096) == -8                 # o on top of k
+
+
+def test_segment_setting():
+    """The segment count: range checks, the forced value, and the workspace
+    growing by the transitions (2 d^2) and incoming states (d^2) in fp32 per
+    (segment, head)."""
+    try:
+        assert kda.kda_set_prefill_segments(-1) == -1
+        assert kda.kda_set_prefill_segments(17) == -1
+        assert kda.kda_set_prefill_segments(1) == 0
+        assert kda.kda_prefill_segments(2, 16384, 8, 128, 128, kda.KDA_BF16) == 1
+        base = kda.kda_prefill_workspace_size(2, 16384, 8, 128, 128, kda.KDA_BF16)
+        for P in (2, 7, 16):
+            assert kda.kda_set_prefill_segments(P) == 0
+            assert kda.kda_prefill_segments(2, 16384, 8, 128, 128, kda.KDA_BF16) == P
+            n = kda.kda_prefill_workspace_size(2, 16384, 8, 128, 128, kda.KDA_BF16)
+            extra = 2 * P * 8 * 3 * 128 * 128 * 4
+            assert n - base == extra + (256 if 2 * P * 16 > 256 else 0), (P, n - base)
+        assert kda.kda_prefill_segments(2, 16384, 8, 96, 96, kda.KDA_BF16) == 0
+    finally:
+        kda.kda_set_prefill_segments(0)
+    # automatic choice: one segment when one pass fills half the device or
+    # the sequences are short
+    assert kda.kda_prefill_segments(1, 65536, 96, 128, 128, kda.KDA_BF16) == 1
+    assert kda.kda_prefill_segments(1, 256, 2, 32, 32, kda.KDA_F32) == 1
+    assert kda.kda_prefill_segments(0, 0, 2, 32, 32, kda.KDA_F32) == 1

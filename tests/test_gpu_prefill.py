@@ -131,11 +131,6 @@ def test_split_and_carry():
     assert rel_l2(host(h2), host(hT)) <= BF16_TOL
 
 
-def test_small_head_workload_full():
-    """B=2, H=8, T=8192 each, d=128, bf16: every output against the oracle."""
-    check(W.make("small_head"), "bf16", label="small_head")
-
-
 def test_k3_prefill_sampled_heads():
     """B=1, H=96, T=65536: full GPU run, oracle on 6 sampled heads."""
     d = W.make("k3_prefill", device="cuda")
