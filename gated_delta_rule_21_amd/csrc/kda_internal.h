@@ -34,8 +34,10 @@ struct PrefillPlan {
     size_t total;
 };
 
-// Largest segment count per sequence.
+// Largest segment count per sequence (at most 64: the combine kernel reads
+// a sequence's segment records one per lane of a wave).
 constexpr int kMaxSegments = 16;
+static_assert(kMaxSegments <= 64, "segment records per wave");
 
 struct PrefillArgs {
     bool f32io;

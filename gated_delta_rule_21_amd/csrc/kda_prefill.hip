@@ -10,9 +10,18 @@
 //                       matrices, the unit-lower-triangular solve and the
 //                       W / U products.  Write one "slab" of MFMA-ready
 //                       fragments per (chunk, head).
-//   inter_kernel        one wavefront per (sequence, head, 16 value columns):
-//                       walks the sequence's chunks in order, carrying the
-//                       fp32 state in MFMA accumulators.
+//   inter_kernel        one wavefront per (segment, head, 16 value columns):
+//                       walks the segment's chunks in order, carrying the
+//                       fp32 state in MFMA accumulators.  A segment is a whole
+//                       sequence unless long sequences are split (below).
+//   combine_kernel      only for split sequences: composes the segments'
+//                       affine state maps into every segment's incoming state.
+//
+// Split sequences (intra-device context parallelism, "Kimi K3：架构…" §11.1
+// and the KCP merge of P3 Eq 17): inter_kernel first runs in its transition
+// mode over every segment but a sequence's last, producing the map
+// S_in -> M S_in + S~ of its chunks; combine_kernel chains the maps from h0;
+// inter_kernel then runs every segment's outputs in parallel.
 //
 // The algebra is the chunk form of the s1mplewind "kimi-k3" notes (section
 // "Chunkwise 形式", derivation steps 1-6), in the d_k x d_v state
@@ -73,9 +82,10 @@ bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, int P, Prefil
 // the inter kernel walks independently once each segment's incoming state is
 // known (intra-device context parallelism).
 constexpr int kSegValid = 1, kSegFirst = 2, kSegLast = 4;
-// inter_kernel modes: the outputs and final states; the segment's transition
-// matrix M (run from the identity with U = 0); its offset S~ (run from zero)
-constexpr int kModeOutput = 0, kModeTransM = 1, kModeTransS = 2;
+// inter_kernel modes: the outputs and final states; or the segment's
+// transition, two states carried side by side over the same chunk operands:
+// the matrix M (run from the identity with U = 0) and the offset S~ (run from zero)
+constexpr int kModeOutput = 0, kModeTrans = 1;
 
 // ---------------------------------------------------------------------------
 // Chunk table.  One workgroup.  meta[n] = first chunk of sequence n,
@@ -219,12 +229,29 @@ __device__ __forceinline__ void store_o_tile(void *o, const f32x4 (&acc)[4], int
     }
 }
 
+// x (n f32x4 tiles, n even) -> fp16 K32 fragments scaled by the power of two
+// that the wave's largest magnitude asks for; returns the factor that undoes it
+template <int n>
+__device__ __forceinline__ float to_f16_scaled(const f32x4 *x, u32x4 *out) {
+    float m = 0.f;
+#pragma unroll
+    for (int t = 0; t < n; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(x[t][j]));
+    const int e = scale_exp(wave_max_nonneg(m));
+    const float d = exp2i(-e);
+#pragma unroll
+    for (int p = 0; p < n / 2; ++p) out[p] = quads_to_f16(x[2 * p] * d, x[2 * p + 1] * d);
+    return exp2i(e);
+}
+
 template <int D, bool F32IO, int MODE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) inter_kernel(
     const float *__restrict__ h0, const float *__restrict__ s_in, const int4 *__restrict__ segs,
     const int4 *__restrict__ table, int nseg, int H, int max_chunks, const unsigned char *__restrict__ slabs,
     size_t slab_stride, void *__restrict__ o, float *__restrict__ hT, float *__restrict__ trans, int groups) {
-    static_assert(MODE == kModeOutput || MODE == kModeTransM || MODE == kModeTransS, "mode");
+    static_assert(MODE == kModeOutput || MODE == kModeTrans, "mode");
+    constexpr bool TR = MODE == kModeTrans;
     using SL = Slab<D, F32IO>;
     using SHP = InterShape<D, F32IO>;
     constexpr int KT = D / 16;
@@ -253,19 +280,20 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     // initial state: h0 (or zero) for a sequence in one segment, otherwise
     // the incoming state the combine kernel wrote (for the first segment a
     // copy of h0, so that h0 is never read here when hT may overwrite it);
-    // the identity for the transition matrix, zero for its offset
-    f32x4 S[KT];
+    // a transition starts M from the identity (in S) and S~ from zero (in S2)
+    f32x4 S[KT], S2[TR ? KT : 1];
     {
         const float *src = nullptr;
-        if constexpr (MODE == kModeOutput)
+        if constexpr (!TR)
             src = (rec.w & kSegFirst) && (rec.w & kSegLast)
                       ? (h0 ? h0 + ((size_t)(n * H + h) * D + col) * D : nullptr)
                       : s_in + ((size_t)(sg * H + h) * D + col) * D;
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
-            if constexpr (MODE == kModeTransM) {
+            if constexpr (TR) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) S[t][j] = (16 * t + 4 * lg + j == col) ? 1.f : 0.f;
+                S2[t] = zero4();
             } else {
                 S[t] = src ? *reinterpret_cast<const f32x4 *>(src + 16 * t + 4 * lg) : zero4();
             }
@@ -335,7 +363,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
         if (c_begin < c_end) {
             copyA(c_begin, aring);
             copyB(c_begin, bring);
-            if constexpr (MODE != kModeTransM) load_u(c_begin, u);
+            load_u(c_begin, u);
             if (c_begin + 1 < c_end) copyA(c_begin + 1, aring + AB);
         }
         wait_all_memory();
@@ -357,7 +385,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
                 if (o_L > 0) flush_o(par ^ 1, o_t0, o_L);   // the previous chunk's rows
             }
             if (c + 1 < c_end) {
-                if constexpr (MODE != kModeTransM) load_u(c + 1, un);
+                load_u(c + 1, un);
                 copyB(c + 1, bring + (par ^ 1) * BB);
             }
             // A copies of chunk c + 2, issued a few at a time between this
@@ -372,51 +400,49 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
                                                  0);
             };
 
-            // S -> fp16 with a per-wave power-of-two scale
-            float m = 0.f;
-#pragma unroll
-            for (int t = 0; t < KT; ++t)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(S[t][j]));
-            const int eS = scale_exp(wave_max_nonneg(m));
-            const float dS = exp2i(-eS), uS = exp2i(eS);
-            u32x4 sf[KT / 2];
-#pragma unroll
-            for (int p = 0; p < KT / 2; ++p) sf[p] = quads_to_f16(S[2 * p] * dS, S[2 * p + 1] * dS);
+            // S -> fp16 with a per-wave power-of-two scale (and S2 with its own)
+            u32x4 sf[KT / 2], sf2[TR ? KT / 2 : 1];
+            const float uS = to_f16_scaled<KT>(S, sf);
+            float uS2 = 0.f;
+            if constexpr (TR) uS2 = to_f16_scaled<KT>(S2, sf2);
 
-            f32x4 vp[4];
+            f32x4 vp[4], vp2[TR ? 4 : 1];
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 if (fetch_a) {
 #pragma unroll
                     for (int r = 0; r < NA / 4; ++r) copyA_part(I * (NA / 4) + r);
                 }
-                f32x4 ws = zero4(), qs = zero4();
+                f32x4 ws = zero4(), qs = zero4(), ws2 = zero4();
 #pragma unroll
                 for (int p = 0; p < KT / 2; ++p) {
-                    ws = mma_f16_k32(fragA(SL::negW, I * (KT / 2) + p), sf[p], ws);
-                    // O^T = S^T (Gamma*Q)^T: the same fragments with the operands
-                    // swapped, so the accumulator holds O row-major (lane (n, g):
-                    // row n, columns 4g..4g+3) and o needs no transpose
-                    if constexpr (MODE == kModeOutput) qs = mma_f16_k32(sf[p], fragA(SL::qg, I * (KT / 2) + p), qs);
+                    const u32x4 fw = fragA(SL::negW, I * (KT / 2) + p);
+                    ws = mma_f16_k32(fw, sf[p], ws);
+                    if constexpr (TR) {
+                        ws2 = mma_f16_k32(fw, sf2[p], ws2);
+                    } else {
+                        // O^T = S^T (Gamma*Q)^T: the same fragments with the operands
+                        // swapped, so the accumulator holds O row-major (lane (n, g):
+                        // row n, columns 4g..4g+3) and o needs no transpose
+                        qs = mma_f16_k32(sf[p], fragA(SL::qg, I * (KT / 2) + p), qs);
+                    }
                 }
-                if constexpr (MODE == kModeTransM)
+                const f32x4 uu = f16x4_to_quad(u[I]) * exp2i(uexp[I * KT + vt]);
+                if constexpr (TR) {
                     vp[I] = ws * uS;
-                else
-                    vp[I] = f16x4_to_quad(u[I]) * exp2i(uexp[I * KT + vt]) + ws * uS;
-                acc_o[I] = qs * uS;
+                    vp2[I] = uu + ws2 * uS2;
+                } else {
+                    vp[I] = uu + ws * uS;
+                    acc_o[I] = qs * uS;
+                }
             }
 
             // V' -> fp16 with its own per-wave scale
-            m = 0.f;
-#pragma unroll
-            for (int I = 0; I < 4; ++I)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(vp[I][j]));
-            const int eV = scale_exp(wave_max_nonneg(m));
-            const float dV = exp2i(-eV), uV = exp2i(eV);
-            const u32x4 vf0 = quads_to_f16(vp[0] * dV, vp[1] * dV);
-            const u32x4 vf1 = quads_to_f16(vp[2] * dV, vp[3] * dV);
+            u32x4 vf[2], vf2[2];
+            const float uV = to_f16_scaled<4>(vp, vf);
+            float uV2 = 0.f;
+            if constexpr (TR) uV2 = to_f16_scaled<4>(vp2, vf2);
+            const u32x4 vf0 = vf[0], vf1 = vf[1];
 
             if constexpr (MODE == kModeOutput) {
                 uint16_t *ob = obuf + par * 64 * OP;
@@ -433,9 +459,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             const f32x4 *gam = reinterpret_cast<const f32x4 *>(bbuf + (SL::gamma - SL::kdT));
 #pragma unroll
             for (int t = 0; t < KT; ++t) {
-                f32x4 a = mma_f16_k32(fragB(SL::kdT, t * 2), vf0, zero4());
-                a = mma_f16_k32(fragB(SL::kdT, t * 2 + 1), vf1, a);
-                S[t] = S[t] * gam[4 * t + lg] + a * uV;
+                const u32x4 k0 = fragB(SL::kdT, t * 2), k1 = fragB(SL::kdT, t * 2 + 1);
+                const f32x4 g = gam[4 * t + lg];
+                f32x4 a = mma_f16_k32(k0, vf0, zero4());
+                a = mma_f16_k32(k1, vf1, a);
+                S[t] = S[t] * g + a * uV;
+                if constexpr (TR) {
+                    f32x4 a2 = mma_f16_k32(k0, vf2[0], zero4());
+                    a2 = mma_f16_k32(k1, vf2[1], a2);
+                    S2[t] = S2[t] * g + a2 * uV2;
+                }
             }
             o_t0 = t_first + kChunk * i;
             o_L = min(kChunk, t_end - o_t0);
@@ -446,10 +479,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             else
                 wait_all_memory();
             __syncthreads();
-            if constexpr (MODE != kModeTransM) {
 #pragma unroll
-                for (int I = 0; I < 4; ++I) u[I] = un[I];
-            }
+            for (int I = 0; I < 4; ++I) u[I] = un[I];
         }
         if constexpr (MODE == kModeOutput) {
             if (o_L > 0) flush_o((c_end - c_begin - 1) & 1, o_t0, o_L);
@@ -460,31 +491,30 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
         unsigned char *buf = lds_raw;
         if (c_begin < c_end) {
             copy_A(c_begin, buf);
-            if constexpr (MODE != kModeTransM) load_u(c_begin, u);
+            load_u(c_begin, u);
         }
         wait_all_memory();
         __syncthreads();
         for (int c = c_begin; c < c_end; ++c) {
             copy_B(c, buf);
-            if constexpr (MODE != kModeTransM) {
-                if (c + 1 < c_end) load_u(c + 1, un);
-            }
+            if (c + 1 < c_end) load_u(c + 1, un);
             if constexpr (MODE == kModeOutput) {
                 if (o_L > 0) store_o_tile<F32IO>(o, acc_o, o_t0, o_L, H, h, D, col, lg);
             }
             const int4 ent = table[c];
-            f32x4 vp[4];
+            f32x4 vp[4], vp2[TR ? 4 : 1];
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
-                if constexpr (MODE == kModeTransM)
-                    vp[I] = zero4();
-                else
-                    vp[I] = u[I];
+                vp[I] = TR ? zero4() : u[I];
+                if constexpr (TR) vp2[I] = u[I];
                 acc_o[I] = zero4();
 #pragma unroll
                 for (int t = 0; t < KT; ++t) {
-                    vp[I] = mma_f32_k16(__builtin_bit_cast(f32x4, frag(buf, SL::negW, I * KT + t)), S[t], vp[I]);
-                    if constexpr (MODE == kModeOutput)
+                    const f32x4 fw = __builtin_bit_cast(f32x4, frag(buf, SL::negW, I * KT + t));
+                    vp[I] = mma_f32_k16(fw, S[t], vp[I]);
+                    if constexpr (TR)
+                        vp2[I] = mma_f32_k16(fw, S2[t], vp2[I]);
+                    else
                         acc_o[I] =
                             mma_f32_k16(__builtin_bit_cast(f32x4, frag(buf, SL::qg, I * KT + t)), S[t], acc_o[I]);
                 }
@@ -503,19 +533,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             const f32x4 *gam = gamma_of(buf);
 #pragma unroll
             for (int t = 0; t < KT; ++t) {
-                S[t] = S[t] * gam[4 * t + lg];
+                const f32x4 g = gam[4 * t + lg];
+                S[t] = S[t] * g;
+                if constexpr (TR) S2[t] = S2[t] * g;
 #pragma unroll
-                for (int J = 0; J < 4; ++J)
-                    S[t] = mma_f32_k16(__builtin_bit_cast(f32x4, frag(buf, SL::kdT, t * 4 + J)), vp[J], S[t]);
+                for (int J = 0; J < 4; ++J) {
+                    const f32x4 fk = __builtin_bit_cast(f32x4, frag(buf, SL::kdT, t * 4 + J));
+                    S[t] = mma_f32_k16(fk, vp[J], S[t]);
+                    if constexpr (TR) S2[t] = mma_f32_k16(fk, vp2[J], S2[t]);
+                }
             }
             o_t0 = ent.y;
             o_L = ent.z;
             wait_all_memory();
             __syncthreads();
-            if constexpr (MODE != kModeTransM) {
 #pragma unroll
-                for (int I = 0; I < 4; ++I) u[I] = un[I];
-            }
+            for (int I = 0; I < 4; ++I) u[I] = un[I];
         }
     }
     if constexpr (MODE == kModeOutput) {
@@ -525,11 +558,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
             for (int t = 0; t < KT; ++t) *reinterpret_cast<f32x4 *>(dst + 16 * t + 4 * lg) = S[t];
         }
-    } else if constexpr (MODE == kModeTransS) {
-        // the offset S~ of the transition, in the state layout [value column][key]
-        float *dst = trans + (((size_t)(sg * H + h) * 2 + 1) * D + col) * D;
-#pragma unroll
-        for (int t = 0; t < KT; ++t) *reinterpret_cast<f32x4 *>(dst + 16 * t + 4 * lg) = S[t];
     } else {
         // the transition matrix M (dk x dk), row-major: M[i][j] at i * D + j;
         // this lane holds M[16t + 4g + j][col]
@@ -538,6 +566,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int t = 0; t < KT; ++t)
 #pragma unroll
             for (int j = 0; j < 4; ++j) dst[(size_t)(16 * t + 4 * lg + j) * D + col] = S[t][j];
+        // the offset S~, in the state layout [value column][key]
+        float *dst2 = trans + (((size_t)(sg * H + h) * 2 + 1) * D + col) * D;
+#pragma unroll
+        for (int t = 0; t < KT; ++t) *reinterpret_cast<f32x4 *>(dst2 + 16 * t + 4 * lg) = S2[t];
     }
 }
 
@@ -547,55 +579,82 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 // (the cross-device merge of "Kimi K3：架构…" §9.3 and the KCP recurrence of
 // P3 Eq 17, applied here to segments on one device).  For a sequence in
 // Pn > 1 segments: S_in(0) = h0 (or zero), S_in(k + 1) = M_k S_in(k) + S~_k,
-// each written to the segment's slot of s_in.  One wave per (sequence, head,
-// 16 value columns), the state in fp32 accumulators, fp32 MFMA; M is read
-// row-major from the transition buffer as A fragments.
+// each written to the segment's slot of s_in.
+//
+// One workgroup per (sequence, head, 16 value columns); wave I owns rows
+// [16 I, 16 I + 16) of the d_k x 16 slice.  The slice lives in LDS between
+// steps (column-major, padded); each step is a 16 x 16 x d_k fp32 MFMA
+// product per wave.  M_k and S~_k do not depend on the chain, so each
+// step's rows are loaded two steps ahead.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ h0, const int4 *__restrict__ segs,
-                                                      int N, int H, int P, const float *__restrict__ trans,
-                                                      float *__restrict__ s_in, int groups) {
+__global__ void __launch_bounds__(D * 4) combine_kernel(const float *__restrict__ h0, const int4 *__restrict__ segs,
+                                                        int N, int H, int P, const float *__restrict__ trans,
+                                                        float *__restrict__ s_in) {
     constexpr int KT = D / 16;
-    constexpr int WPG = KT < 4 ? KT : 4;
-    const int b = blockIdx.x;
-    const int xcd = b & 7, rest = b >> 3;
-    const int cg = rest % groups;
-    const int unit = (rest / groups) * 8 + xcd;
+    constexpr int PITCH = D + 4;                 // floats per column in LDS
+    __shared__ __attribute__((aligned(16))) float sS[16 * PITCH];
+    const int vt = blockIdx.x % KT, unit = blockIdx.x / KT;
     if (unit >= N * H) return;
     const int n = unit / H, h = unit % H;
-    if (segs[n * P].w & kSegLast) return;   // one segment: its pass reads h0 itself
     const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int I = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int ln = lane & 15, lg = lane >> 4;
-    const int col = 16 * (cg * WPG + wave) + ln;
+    const int col = 16 * vt + ln;
+    const int row = 16 * I + 4 * lg;             // this lane's 4 accumulator rows (and S~ rows)
+    float *slot = sS + ln * PITCH;               // column ln of the slice
 
-    f32x4 S[KT];
-    const float *src = h0 ? h0 + ((size_t)(n * H + h) * D + col) * D : nullptr;
+    auto out_ptr = [&](int sg) { return s_in + ((size_t)(sg * H + h) * D + col) * D + row; };
+    auto m_rows = [&](int sg) { return trans + (size_t)(sg * H + h) * 2 * D * D + (size_t)(16 * I + ln) * D + 4 * lg; };
+    auto st_ptr = [&](int sg) { return trans + ((size_t)(sg * H + h) * 2 + 1) * D * D + (size_t)col * D + row; };
+
+    // Operands of step k are loaded two steps ahead.  The first two steps'
+    // loads go out together with h0 and the segment records (indices 0 and 1
+    // are in bounds for every sequence: P >= 2 here).  Later fetches are
+    // issued on every path, indices clamped to the last step, so that the
+    // compiler can count the loads in flight and waits only for the ones a
+    // step uses.
+    f32x4 mA[KT], sA, mB[KT], sB;
+    auto fetch = [&](int k, f32x4(&mm)[KT], f32x4 &ss) {
 #pragma unroll
-    for (int t = 0; t < KT; ++t) S[t] = src ? *reinterpret_cast<const f32x4 *>(src + 16 * t + 4 * lg) : zero4();
-    auto store = [&](int sg) {
-        float *dst = s_in + ((size_t)(sg * H + h) * D + col) * D;
-#pragma unroll
-        for (int t = 0; t < KT; ++t) *reinterpret_cast<f32x4 *>(dst + 16 * t + 4 * lg) = S[t];
+        for (int t = 0; t < KT; ++t) mm[t] = *reinterpret_cast<const f32x4 *>(m_rows(n * P + k) + 16 * t);
+        ss = *reinterpret_cast<const f32x4 *>(st_ptr(n * P + k));
     };
-    store(n * P);
-    for (int k = 0; k + 1 < P; ++k) {
-        const int sg = n * P + k;
-        if (segs[sg].w & kSegLast) break;
-        const float *M = trans + (size_t)(sg * H + h) * 2 * D * D;
-        const float *St = M + (size_t)D * D + (size_t)col * D;
-        f32x4 nx[KT];
+    const f32x4 S0 = h0 ? *reinterpret_cast<const f32x4 *>(h0 + ((size_t)(n * H + h) * D + col) * D + row) : zero4();
+    // steps = segments - 1 = index of the last segment (one record per lane, P <= 64)
+    const unsigned long long lasts = __ballot(lane < P && (segs[n * P + lane].w & kSegLast));
+    fetch(0, mA, sA);
+    fetch(1, mB, sB);
+    if (lasts == 0) return;
+    const int steps = __builtin_ctzll(lasts);
+    if (steps == 0) return;   // one segment: its pass reads h0 itself
+    *reinterpret_cast<f32x4 *>(slot + row) = S0;
+    *reinterpret_cast<f32x4 *>(out_ptr(n * P)) = S0;
+
+    auto step = [&](int k, const f32x4(&mm)[KT], const f32x4 &ss) {
+        f32x4 b[KT];
 #pragma unroll
-        for (int I = 0; I < KT; ++I) {
-            nx[I] = *reinterpret_cast<const f32x4 *>(St + 16 * I + 4 * lg);
+        for (int t = 0; t < KT; ++t) b[t] = *reinterpret_cast<const f32x4 *>(slot + 16 * t + 4 * lg);
+        // two independent accumulation chains
+        f32x4 acc0 = ss, acc1 = zero4();
 #pragma unroll
-            for (int t = 0; t < KT; ++t)
-                nx[I] = mma_f32_k16(*reinterpret_cast<const f32x4 *>(M + (size_t)(16 * I + ln) * D + 16 * t + 4 * lg),
-                                    S[t], nx[I]);
+        for (int t = 0; t < KT; t += 2) {
+            acc0 = mma_f32_k16(mm[t], b[t], acc0);
+            acc1 = mma_f32_k16(mm[t + 1], b[t + 1], acc1);
         }
-#pragma unroll
-        for (int t = 0; t < KT; ++t) S[t] = nx[t];
-        store(sg + 1);
+        const f32x4 acc = acc0 + acc1;
+        __syncthreads();                          // every wave has read S_in(k)
+        *reinterpret_cast<f32x4 *>(slot + row) = acc;
+        *reinterpret_cast<f32x4 *>(out_ptr(n * P + k + 1)) = acc;
+        __syncthreads();
+    };
+    const int kl = steps - 1;
+    __syncthreads();
+    for (int k = 0; k < steps; k += 2) {
+        step(k, mA, sA);
+        fetch(min(k + 2, kl), mA, sA);
+        if (k + 1 < steps) step(k + 1, mB, sB);
+        fetch(min(k + 3, kl), mB, sB);
     }
 }
 
@@ -655,13 +714,11 @@ static int launch_prefill_t(const PrefillArgs &a) {
         return hipGetLastError() == hipSuccess;
     };
     if (p.P > 1) {
-        // transitions of every segment but a sequence's last, then the
+        // the transition of every segment but a sequence's last, then the
         // incoming state of every segment
-        if (!inter(std::integral_constant<int, kModeTransM>{})) return -1;
-        if (!inter(std::integral_constant<int, kModeTransS>{})) return -1;
-        const int chain_blocks = (a.N * a.H + 7) / 8 * 8;
-        hipLaunchKernelGGL((combine_kernel<D>), dim3(chain_blocks * groups), dim3(SHP::NT), 0, a.stream, a.h0, segs,
-                           a.N, a.H, p.P, trans, s_in, groups);
+        if (!inter(std::integral_constant<int, kModeTrans>{})) return -1;
+        hipLaunchKernelGGL((combine_kernel<D>), dim3(a.N * a.H * (D / 16)), dim3(D * 4), 0, a.stream, a.h0, segs,
+                           a.N, a.H, p.P, trans, s_in);
         if (hipGetLastError() != hipSuccess) return -1;
     }
     if (!inter(std::integral_constant<int, kModeOutput>{})) return -1;
