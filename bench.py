@@ -78,6 +78,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--decode-steps", type=int, default=1000)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-decode-window", action="store_true",
+                   help="skip the side measurement of the speculative decode step")
     p.add_argument("--no-small-head", action="store_true",
                    help="skip the side measurement of the small-head prefill (B=2, H=8, T=8192)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -151,6 +153,40 @@ def small_head_prefill(kda, W, dev, reps: int = 10) -> dict:
             del ws
         out[key] = {"segments": segs, "ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1)}
     return out
+
+
+def decode_window_step(kda, W, dev, reps: int = 200) -> dict:
+    """Side measurement: one speculative-decode step, 256 sequences x 96
+    heads x 128^2: replay of a 4-token window with n_accept ~ U{0..4}, then a
+    new 4-token window.  Algorithmic bytes: the state read once, written once
+    where something was accepted, the accepted replay tokens' k, v, z, beta,
+    and the window's q, k, v, z, beta and o."""
+    import torch
+    Lr = L = 4
+    d = W.random_decode_window(256, 96, 128, Lr=Lr, L=L, io="bf16", device=dev)
+    N, H, D = d["N"], d["H"], d["dk"]
+    S = d["S"].clone()
+    o = torch.empty((N, L, H, D), dtype=torch.bfloat16, device=dev)
+    run = lambda: kda.decode_window(d["A"], S, window=d["window"], replay=d["replay"],
+                                    n_accept=d["n_accept"], o=o)
+    for _ in range(5):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    acc = d["n_accept"].cpu()
+    state = D * D * 4
+    per_head = (state * N + state * int((acc > 0).sum()) + 1028 * int(acc.sum()) + 1540 * L * N)
+    gbps = per_head * H / (ms * 1e-3) / 1e9
+    return {"workload": "spec decode 256x96 d=128 bf16, replay 4 (n_accept ~ U{0..4}), window 4",
+            "ms": round(ms, 4), "algorithmic_GBps": round(gbps, 1),
+            "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "accepted_tokens": int(acc.sum()), "window_tokens": N * L}
 
 
 def main():
@@ -261,6 +297,8 @@ def main():
     }
     if not args.no_small_head:
         line["small_head"] = small_head_prefill(kda, W, dev)
+    if not args.no_decode_window:
+        line["decode_window"] = decode_window_step(kda, W, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -8,6 +8,7 @@ the library is missing or the tensors are not on a GPU, the call raises.
 Entry points (same names as the C ABI in include/kda.h):
   kda_prefill(...)                  raw C call, pointers as ints
   kda_decode(...)                   raw C call
+  kda_decode_window(...)            raw C call: replay + multi-token window
   kda_prefill_workspace_size(...)
   kda_set_prefill_segments(P), kda_prefill_segments(...)
                                     segment split of long sequences
@@ -15,6 +16,7 @@ Entry points (same names as the C ABI in include/kda.h):
 Convenience wrappers over torch tensors:
   prefill(q, k, v, z, A, beta, cu_seqlens, h0=None, ...) -> (o, hT)
   decode(q, k, v, z, A, beta, S) -> o          (S updated in place)
+  decode_window(A, S, window=..., replay=..., n_accept=...) -> o
 """
 from __future__ import annotations
 
@@ -54,6 +56,9 @@ def lib():
     L.kda_prefill_workspace_size.restype = sz
     L.kda_decode.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, vp, vp]
     L.kda_decode.restype = ci
+    L.kda_decode_window.argtypes = [ci, vp, vp, vp, vp, vp, ci, vp, vp, vp, vp, vp, ci, vp, vp, ci, ci,
+                                    ci, ci, vp, ci, vp]
+    L.kda_decode_window.restype = ci
     L.kda_set_prefill_segments.argtypes = [ci]
     L.kda_set_prefill_segments.restype = ci
     L.kda_prefill_segments.argtypes = [ci, ci, ci, ci, ci, ci]
@@ -76,6 +81,12 @@ def kda_prefill(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv, 
 
 def kda_decode(io_dtype, q, k, v, z, A, beta, S_inout, N, H, dk, dv, o, stream) -> int:
     return lib().kda_decode(io_dtype, q, k, v, z, A, beta, S_inout, N, H, dk, dv, o, stream)
+
+
+def kda_decode_window(io_dtype, rk, rv, rz, rbeta, n_accept, Lr, q, k, v, z, beta, L, A, S_inout,
+                      N, H, dk, dv, o, commit_window, stream) -> int:
+    return lib().kda_decode_window(io_dtype, rk, rv, rz, rbeta, n_accept, Lr, q, k, v, z, beta, L,
+                                   A, S_inout, N, H, dk, dv, o, commit_window, stream)
 
 
 def kda_prefill_workspace_size(N, T, H, dk, dv, io_dtype) -> int:
@@ -202,3 +213,41 @@ def decode(q, k, v, z, A, beta, S, o=None):
     if st != 0:
         raise KdaError("kda_decode", st)
     return o
+
+
+def decode_window(A, S, window=None, replay=None, n_accept=None, o=None, commit_window=False):
+    """Multi-token decode with replay.  S ([N, H, dv, dk] fp32) is the
+    committed state and is updated in place.
+
+    replay: dict of k, v, z, beta with shapes [N, Lr, H, d] ([N, Lr, H] for
+            beta), normally the window of the previous call; n_accept: [N]
+            int32 accepted replay tokens.
+    window: dict of q, k, v, z, beta with shapes [N, L, H, d].
+    Returns o [N, L, H, dv] (None when there is no window)."""
+    torch = _torch()
+    N, H, dv, dk = S.shape
+    _check_gpu(A=A, S=S, n_accept=n_accept, o=o)
+    rk = rv = rz = rb = None
+    Lr = 0
+    if replay is not None:
+        rk, rv, rz, rb = replay["k"], replay["v"], replay["z"], replay["beta"]
+        _check_gpu(rk=rk, rv=rv, rz=rz, rbeta=rb)
+        Lr = rk.shape[1]
+        if n_accept is None:
+            raise ValueError("n_accept is required with a replay window")
+    q = k = v = z = b = None
+    L = 0
+    if window is not None:
+        q, k, v, z, b = (window[n] for n in ("q", "k", "v", "z", "beta"))
+        _check_gpu(q=q, k=k, v=v, z=z, beta=b)
+        L = q.shape[1]
+    ref = q if q is not None else rk
+    io = _io_code(ref) if ref is not None else KDA_F32
+    if L > 0 and o is None:
+        o = torch.empty((N, L, H, dv), dtype=q.dtype, device=S.device)
+    st = kda_decode_window(io, _ptr(rk), _ptr(rv), _ptr(rz), _ptr(rb), _ptr(n_accept), Lr,
+                           _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(b), L, _ptr(A), _ptr(S),
+                           N, H, dk, dv, _ptr(o), 1 if commit_window else 0, _stream(S.device))
+    if st != 0:
+        raise KdaError("kda_decode_window", st)
+    return o if L > 0 else None

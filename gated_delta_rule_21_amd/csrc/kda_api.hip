@@ -13,6 +13,7 @@
 #include "kda_internal.h"
 
 static_assert(KDA_MAX_PREFILL_SEGMENTS == kda::kMaxSegments, "segment limit");
+static_assert(KDA_MAX_DECODE_WINDOW == kda::kMaxWindow, "window limit");
 
 namespace {
 
@@ -164,6 +165,45 @@ int kda_decode(kda_dtype io_dtype, const void *q, const void *k, const void *v, 
     a.N = N; a.H = H; a.dk = dk; a.dv = dv;
     a.stream = reinterpret_cast<hipStream_t>(stream);
     return kda::launch_decode(a) == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_decode_window(kda_dtype io_dtype, const void *rk, const void *rv, const float *rz,
+                      const float *rbeta, const int32_t *n_accept, int Lr, const void *q, const void *k,
+                      const void *v, const float *z, const float *beta, int L, const float *A,
+                      float *S_inout, int N, int H, int dk, int dv, void *o, int commit_window,
+                      void *stream) {
+    if (io_dtype != KDA_BF16 && io_dtype != KDA_F32) return KDA_ERR_UNSUPPORTED_DTYPE;
+    if (N < 0 || H <= 0 || Lr < 0 || L < 0 || Lr > KDA_MAX_DECODE_WINDOW || L > KDA_MAX_DECODE_WINDOW ||
+        (commit_window != 0 && commit_window != 1))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (!supported_dim(dk, dv)) return KDA_ERR_UNSUPPORTED_DIM;
+    if (!A) return KDA_ERR_NULL_POINTER;
+    if (N > 0 && !S_inout) return KDA_ERR_NULL_POINTER;
+    if (N > 0 && Lr > 0 && (!rk || !rv || !rz || !rbeta || !n_accept)) return KDA_ERR_NULL_POINTER;
+    if (N > 0 && L > 0 && (!q || !k || !v || !z || !beta || !o)) return KDA_ERR_NULL_POINTER;
+    const void *ptrs[] = {rk, rv, rz, rbeta, n_accept, q, k, v, z, beta, A, S_inout, o};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    const size_t nh = (size_t)N * H, io = io_size(io_dtype);
+    const size_t st_bytes = nh * dv * dk * 4, o_bytes = nh * L * dv * io;
+    const size_t r = nh * Lr, w = nh * L;
+    const struct { const void *p; size_t n; } ins[] = {
+        {rk, r * dk * io}, {rv, r * dv * io}, {rz, r * dk * 4}, {rbeta, r * 4}, {n_accept, (size_t)N * 4},
+        {q, w * dk * io}, {k, w * dk * io}, {v, w * dv * io}, {z, w * dk * 4}, {beta, w * 4},
+        {A, (size_t)H * 4}};
+    for (const auto &in : ins)
+        if (overlaps(o, o_bytes, in.p, in.n) || overlaps(S_inout, st_bytes, in.p, in.n)) return KDA_ERR_ALIAS;
+    if (overlaps(o, o_bytes, S_inout, st_bytes)) return KDA_ERR_ALIAS;
+
+    kda::DecodeWindowArgs a;
+    a.f32io = io_dtype == KDA_F32;
+    a.rk = rk; a.rv = rv; a.rz = rz; a.rbeta = rbeta; a.n_accept = n_accept; a.Lr = Lr;
+    a.q = q; a.k = k; a.v = v; a.z = z; a.beta = beta; a.L = L;
+    a.A = A; a.S = S_inout; a.o = o;
+    a.N = N; a.H = H; a.dk = dk; a.dv = dv;
+    a.commit_window = commit_window == 1;
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+    return kda::launch_decode_window(a) == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -18,6 +18,29 @@ struct DecodeArgs {
     hipStream_t stream;
 };
 
+// Multi-token decode with replay: the replay window (inputs cached from the
+// previous call, n_accept[n] of its Lr tokens committed now) and the new
+// window of L tokens.  Inputs [N][len][H][d].
+struct DecodeWindowArgs {
+    bool f32io;
+    const void *rk, *rv;
+    const float *rz, *rbeta;
+    const int32_t *n_accept;
+    int Lr;
+    const void *q, *k, *v;
+    const float *z, *beta;
+    int L;
+    const float *A;
+    float *S;
+    void *o;
+    int N, H, dk, dv;
+    bool commit_window;
+    hipStream_t stream;
+};
+
+// Longest replay and window the decode-window kernel stages in LDS.
+constexpr int kMaxWindow = 16;
+
 // Workspace plan of the chunkwise prefill.  Offsets are bytes from the
 // workspace base; every region is 256-byte aligned.
 struct PrefillPlan {
@@ -60,6 +83,7 @@ void set_prefill_segments(int p);
 size_t slab_bytes(int dk, int dv, bool f32io);
 
 int launch_decode(const DecodeArgs &a);
+int launch_decode_window(const DecodeWindowArgs &a);
 int launch_prefill(const PrefillArgs &a);
 // Intra-chunk kernels (kda_intra.hip: bf16 path; kda_intra_f32.hip: fp32
 // path), D = 32, 64, 128.

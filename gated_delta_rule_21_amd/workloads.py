@@ -183,6 +183,37 @@ def random_decode(N: int, H: int, d: int, io: str = "bf16", state_std: float = 0
     return dict(q=q, k=k, v=v, z=z, A=A, beta=beta, S=S, N=N, H=H, dk=d, dv=d, io=io)
 
 
+def random_decode_window(N: int, H: int, d: int, Lr: int, L: int, io: str = "bf16",
+                         state_std: float = 0.05, seed: int = BASE_SEED + 5, device="cpu") -> dict:
+    """Draw a decode-window batch: the committed state, a replay window of Lr
+    tokens with n_accept ~ U{0..Lr} per sequence, and a new window of L
+    tokens.  Per-token inputs are drawn as in random_decode (unit-norm q and
+    k); layouts [N][len][H][d]."""
+    device = torch.device(device)
+    g = _gen(device, seed)
+    f32 = torch.float32
+    A = torch.rand(H, generator=g, device=device, dtype=f32) * 2.0 - 1.0
+    S = torch.randn(N, H, d, d, generator=g, device=device, dtype=f32) * state_std
+
+    def tokens(n_tok, with_q):
+        out = {}
+        if with_q:
+            out["q"] = _unit_rows(torch.randn(N, n_tok, H, d, generator=g, device=device,
+                                              dtype=f32)).to(torch_dtype(io))
+        out["k"] = _unit_rows(torch.randn(N, n_tok, H, d, generator=g, device=device,
+                                          dtype=f32)).to(torch_dtype(io))
+        out["v"] = torch.randn(N, n_tok, H, d, generator=g, device=device, dtype=f32).to(torch_dtype(io))
+        out["z"] = torch.randn(N, n_tok, H, d, generator=g, device=device, dtype=f32)
+        out["beta"] = torch.sigmoid(torch.randn(N, n_tok, H, generator=g, device=device, dtype=f32))
+        return out
+
+    replay = tokens(Lr, False)
+    window = tokens(L, True)
+    n_accept = torch.randint(0, Lr + 1, (N,), generator=g, device=device, dtype=torch.int32)
+    return dict(A=A, S=S, replay=replay, window=window, n_accept=n_accept, N=N, H=H, dk=d, dv=d,
+                Lr=Lr, L=L, io=io)
+
+
 def make(name: str, device="cpu", seed: Optional[int] = None, **over) -> dict:
     """Inputs for a named workload (see WORKLOADS)."""
     w = WORKLOADS[name]

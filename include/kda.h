@@ -146,6 +146,42 @@ int kda_decode(kda_dtype io_dtype, const void *q, const void *k, const void *v,
                const float *z, const float *A, const float *beta, float *S_inout, int N,
                int H, int dk, int dv, void *o, void *stream);
 
+/*
+ * Multi-token decode with replay (speculative decoding).  A state updated in
+ * place cannot be rolled back when draft tokens are rejected; instead the
+ * caller keeps the committed state and the small per-token inputs of the
+ * draft window, and once the verifier has decided, the accepted tokens are
+ * replayed on chip in the same pass that runs the next window ("Kimi K3：
+ * 架构…" §11.3 and §13.2: projected inputs cached, accepted tokens replayed,
+ * replay + bonus token + next draft window merged into one decode loop).
+ *
+ * Per sequence n and head, in one pass over the state:
+ *   1. the first a = clamp(n_accept[n], 0, Lr) tokens of the replay window
+ *      advance S_inout (no outputs);
+ *   2. that state is written back to S_inout (the committed state);
+ *   3. the L tokens of the new window advance a copy of it and produce
+ *      o_t = S_t^T q_t for every window token; the copy is dropped, or, when
+ *      commit_window is 1, written back instead of the state of step 2.
+ * The state is read once and written at most once per call (not at all when
+ * a = 0 and commit_window is 0).
+ *
+ *   rk, rv, rz, rbeta   replay window [N][Lr][H][dk or dv] (io dtype for rk,
+ *                       rv; fp32 rz; rbeta [N][Lr][H] fp32): the k, v, z,
+ *                       beta passed as the window of the previous call
+ *   n_accept            [N] int32 device array, accepted replay tokens
+ *   q, k, v, z, beta    new window [N][L][H][...], same dtypes as kda_decode
+ *   A                   [H] fp32;  S_inout [N][H][dv][dk] fp32
+ *   o                   [N][L][H][dv] io dtype
+ *   0 <= Lr, L <= KDA_MAX_DECODE_WINDOW; pointers of an empty window may be
+ *   NULL.  Lr = 0, L = 1, commit_window = 1 is one kda_decode step.
+ */
+#define KDA_MAX_DECODE_WINDOW 16
+int kda_decode_window(kda_dtype io_dtype, const void *rk, const void *rv, const float *rz,
+                      const float *rbeta, const int32_t *n_accept, int Lr, const void *q,
+                      const void *k, const void *v, const float *z, const float *beta, int L,
+                      const float *A, float *S_inout, int N, int H, int dk, int dv, void *o,
+                      int commit_window, void *stream);
+
 /* Static, human-readable text for a kda_status value. */
 const char *kda_status_string(int status);
 

@@ -19,7 +19,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["kda_build_info", "kda_decode", "kda_prefill",
+    assert declared_functions() == sorted(["kda_build_info", "kda_decode", "kda_decode_window", "kda_prefill",
                                            "kda_prefill_segments", "kda_prefill_workspace_size",
                                            "kda_set_prefill_segments", "kda_status_string"])
 
@@ -121,3 +121,22 @@ def test_segment_setting():
     assert kda.kda_prefill_segments(1, 65536, 96, 128, 128, kda.KDA_BF16) == 1
     assert kda.kda_prefill_segments(1, 256, 2, 32, 32, kda.KDA_F32) == 1
     assert kda.kda_prefill_segments(0, 0, 2, 32, 32, kda.KDA_F32) == 1
+
+
+def test_decode_window_rejects_bad_arguments():
+    def w(**o):
+        a = dict(io=0, rk=FAKE, rv=FAKE + 4096, rz=FAKE + 8192, rb=FAKE + 12288, acc=FAKE + 16384, Lr=2,
+                 q=FAKE + 20480, k=FAKE + 24576, v=FAKE + 28672, z=FAKE + 32768, b=FAKE + 36864, L=3,
+                 A=FAKE + 40960, S=1 << 22, N=2, H=2, d=32, o=1 << 23, commit=0)
+        a.update(o)
+        return kda.kda_decode_window(a["io"], a["rk"], a["rv"], a["rz"], a["rb"], a["acc"], a["Lr"], a["q"],
+                                     a["k"], a["v"], a["z"], a["b"], a["L"], a["A"], a["S"], a["N"], a["H"],
+                                     a["d"], a["d"], a["o"], a["commit"], None)
+    assert w(io=4) == -4
+    assert w(Lr=17) == -1 and w(L=17) == -1 and w(L=-1) == -1 and w(N=-1) == -1
+    assert w(commit=2) == -1
+    assert w(d=48) == -3
+    assert w(acc=None) == -2 and w(rk=None) == -2 and w(q=None) == -2 and w(S=None) == -2
+    assert w(rk=None, rv=None, rz=None, rb=None, acc=None, Lr=0, o=FAKE + 8) == -5   # misaligned o
+    assert w(o=FAKE + 24576) == -8                # o on top of k
+    assert w(S=FAKE) == -8                        # state on top of the replay keys
