@@ -78,6 +78,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--decode-steps", type=int, default=1000)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-checkpoints", action="store_true",
+                   help="skip the side measurement of the prefill with 512-token checkpoints")
     p.add_argument("--no-decode-window", action="store_true",
                    help="skip the side measurement of the speculative decode step")
     p.add_argument("--no-small-head", action="store_true",
@@ -189,6 +191,29 @@ def decode_window_step(kda, W, dev, reps: int = 200) -> dict:
             "accepted_tokens": int(acc.sum()), "window_tokens": N * L}
 
 
+def prefill_checkpoint_cost(kda, pre, o, hT, ws, interval: int = 512, reps: int = 5) -> dict:
+    """Side measurement: the same K3 prefill saving the state every
+    `interval` tokens (prefix-reuse checkpoints)."""
+    import torch
+    T, H, D = pre["q"].shape
+    ck = torch.empty((T // interval, H, D, D), dtype=torch.float32, device=pre["q"].device)
+    run = lambda: kda.prefill_checkpoints(pre["q"], pre["k"], pre["v"], pre["z"], pre["A"], pre["beta"],
+                                          pre["cu_seqlens"], interval, h0=None, o=o, hT=hT,
+                                          checkpoints=ck, workspace=ws)
+    run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del ck
+    return {"interval": interval, "checkpoints": T // interval, "ms": round(ms, 4),
+            "checkpoint_GB": round((T // interval) * H * D * D * 4 / 1e9, 3)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -295,6 +320,8 @@ def main():
                      "kernel": "kda_prefill (chunk table + intra + inter kernels), "
                                "1540 algorithmic B per (token, head) x 6291456 pairs per launch"},
     }
+    if not args.no_checkpoints:
+        line["prefill_checkpoints"] = prefill_checkpoint_cost(kda, pre, o, hT, ws)
     if not args.no_small_head:
         line["small_head"] = small_head_prefill(kda, W, dev)
     if not args.no_decode_window:

@@ -9,6 +9,7 @@ Entry points (same names as the C ABI in include/kda.h):
   kda_prefill(...)                  raw C call, pointers as ints
   kda_decode(...)                   raw C call
   kda_decode_window(...)            raw C call: replay + multi-token window
+  kda_prefill_checkpoints(...)      raw C call: prefill + state checkpoints
   kda_prefill_workspace_size(...)
   kda_set_prefill_segments(P), kda_prefill_segments(...)
                                     segment split of long sequences
@@ -17,6 +18,7 @@ Convenience wrappers over torch tensors:
   prefill(q, k, v, z, A, beta, cu_seqlens, h0=None, ...) -> (o, hT)
   decode(q, k, v, z, A, beta, S) -> o          (S updated in place)
   decode_window(A, S, window=..., replay=..., n_accept=...) -> o
+  prefill_checkpoints(..., interval) -> (o, hT, checkpoints, offsets)
 """
 from __future__ import annotations
 
@@ -56,6 +58,9 @@ def lib():
     L.kda_prefill_workspace_size.restype = sz
     L.kda_decode.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, vp, vp]
     L.kda_decode.restype = ci
+    L.kda_prefill_checkpoints.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, vp,
+                                          vp, ci, vp, vp, vp, sz, vp]
+    L.kda_prefill_checkpoints.restype = ci
     L.kda_decode_window.argtypes = [ci, vp, vp, vp, vp, vp, ci, vp, vp, vp, vp, vp, ci, vp, vp, ci, ci,
                                     ci, ci, vp, ci, vp]
     L.kda_decode_window.restype = ci
@@ -81,6 +86,14 @@ def kda_prefill(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv, 
 
 def kda_decode(io_dtype, q, k, v, z, A, beta, S_inout, N, H, dk, dv, o, stream) -> int:
     return lib().kda_decode(io_dtype, q, k, v, z, A, beta, S_inout, N, H, dk, dv, o, stream)
+
+
+def kda_prefill_checkpoints(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv, o, hT,
+                            interval, checkpoints, checkpoint_offsets, workspace, workspace_bytes,
+                            stream) -> int:
+    return lib().kda_prefill_checkpoints(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk,
+                                         dv, o, hT, interval, checkpoints, checkpoint_offsets,
+                                         workspace, workspace_bytes, stream)
 
 
 def kda_decode_window(io_dtype, rk, rv, rz, rbeta, n_accept, Lr, q, k, v, z, beta, L, A, S_inout,
@@ -251,3 +264,36 @@ def decode_window(A, S, window=None, replay=None, n_accept=None, o=None, commit_
     if st != 0:
         raise KdaError("kda_decode_window", st)
     return o if L > 0 else None
+
+
+def prefill_checkpoints(q, k, v, z, A, beta, cu_seqlens, interval: int, h0=None, o=None, hT=None,
+                        checkpoints=None, offsets=None, workspace=None):
+    """prefill() that also saves the state every `interval` tokens of every
+    sequence.  Returns (o, hT, checkpoints [T // interval, H, dv, dk],
+    offsets [N + 1]): sequence n's checkpoints are
+    checkpoints[offsets[n]:offsets[n + 1]], in token order."""
+    torch = _torch()
+    _check_gpu(q=q, k=k, v=v, z=z, A=A, beta=beta, cu_seqlens=cu_seqlens, h0=h0, o=o, hT=hT,
+               checkpoints=checkpoints, offsets=offsets, workspace=workspace)
+    io = _io_code(q)
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    dev = q.device
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
+    if hT is None:
+        hT = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
+    if checkpoints is None:
+        checkpoints = torch.empty((T // interval, H, dv, dk), dtype=torch.float32, device=dev)
+    if offsets is None:
+        offsets = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = prefill_workspace(N, T, H, dk, io, dev)
+    st = kda_prefill_checkpoints(io, _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A), _ptr(beta), _ptr(h0),
+                                 _ptr(cu_seqlens), N, T, H, dk, dv, _ptr(o), _ptr(hT), interval,
+                                 _ptr(checkpoints), _ptr(offsets), _ptr(workspace), workspace.numel(),
+                                 _stream(dev))
+    if st != 0:
+        raise KdaError("kda_prefill_checkpoints", st)
+    return o, hT, checkpoints, offsets

@@ -79,16 +79,21 @@ int kda_set_prefill_segments(int segments) {
     return KDA_OK;
 }
 
-int kda_prefill(kda_dtype io_dtype, const void *q, const void *k, const void *v, const float *z,
-                const float *A, const float *beta, const float *h0, const int32_t *cu_seqlens,
-                int N, int T, int H, int dk, int dv, void *o, float *hT, void *workspace,
-                size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int prefill_impl(kda_dtype io_dtype, const void *q, const void *k, const void *v, const float *z,
+                 const float *A, const float *beta, const float *h0, const int32_t *cu_seqlens, int N,
+                 int T, int H, int dk, int dv, void *o, float *hT, int interval, float *ck,
+                 int32_t *ck_offsets, void *workspace, size_t workspace_bytes, void *stream) {
     if (io_dtype != KDA_BF16 && io_dtype != KDA_F32) return KDA_ERR_UNSUPPORTED_DTYPE;
+    if ((ck || ck_offsets) && (interval <= 0 || interval % 64 != 0)) return KDA_ERR_INVALID_ARGUMENT;
     if (N < 0 || T < 0 || H <= 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!supported_dim(dk, dv)) return KDA_ERR_UNSUPPORTED_DIM;
     if (!A || !cu_seqlens || !workspace) return KDA_ERR_NULL_POINTER;
     if (T > 0 && (!q || !k || !v || !z || !beta || !o)) return KDA_ERR_NULL_POINTER;
-    const void *ptrs[] = {q, k, v, z, A, beta, h0, cu_seqlens, o, hT};
+    const void *ptrs[] = {q, k, v, z, A, beta, h0, cu_seqlens, o, hT, ck, ck_offsets};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_MISALIGNED;
@@ -112,6 +117,15 @@ int kda_prefill(kda_dtype io_dtype, const void *q, const void *k, const void *v,
     }
     if (hT && h0 && hT != h0 && overlaps(hT, st_bytes, h0, st_bytes)) return KDA_ERR_ALIAS;
     if (overlaps(o, o_bytes, hT, st_bytes)) return KDA_ERR_ALIAS;
+    // checkpoints and their offsets overlap nothing else
+    const size_t ck_bytes = interval > 0 ? (size_t)(T / interval) * H * dv * dk * 4 : 0;
+    const size_t off_bytes = (size_t)(N + 1) * 4;
+    for (const auto &in : ins)
+        if (overlaps(ck, ck_bytes, in.p, in.n) || overlaps(ck_offsets, off_bytes, in.p, in.n)) return KDA_ERR_ALIAS;
+    if (overlaps(ck, ck_bytes, o, o_bytes) || overlaps(ck, ck_bytes, hT, st_bytes) ||
+        overlaps(ck_offsets, off_bytes, o, o_bytes) || overlaps(ck_offsets, off_bytes, hT, st_bytes) ||
+        overlaps(ck, ck_bytes, ck_offsets, off_bytes))
+        return KDA_ERR_ALIAS;
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (debug_check_cu()) {
@@ -131,10 +145,34 @@ int kda_prefill(kda_dtype io_dtype, const void *q, const void *k, const void *v,
     a.cu = cu_seqlens;
     a.N = N; a.T = T; a.H = H; a.dk = dk; a.dv = dv;
     a.o = o; a.hT = hT;
+    a.ck = ck_bytes > 0 ? ck : nullptr;
+    a.ck_offsets = ck_offsets;
+    a.ck_interval = (ck || ck_offsets) ? interval : 0;
     a.ws = static_cast<unsigned char *>(workspace);
     a.plan = plan;
     a.stream = st;
     return kda::launch_prefill(a) == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_prefill(kda_dtype io_dtype, const void *q, const void *k, const void *v, const float *z,
+                const float *A, const float *beta, const float *h0, const int32_t *cu_seqlens,
+                int N, int T, int H, int dk, int dv, void *o, float *hT, void *workspace,
+                size_t workspace_bytes, void *stream) {
+    return prefill_impl(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv, o, hT, 0, nullptr,
+                        nullptr, workspace, workspace_bytes, stream);
+}
+
+int kda_prefill_checkpoints(kda_dtype io_dtype, const void *q, const void *k, const void *v,
+                            const float *z, const float *A, const float *beta, const float *h0,
+                            const int32_t *cu_seqlens, int N, int T, int H, int dk, int dv, void *o,
+                            float *hT, int interval, float *checkpoints, int32_t *checkpoint_offsets,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    return prefill_impl(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv, o, hT, interval,
+                        checkpoints, checkpoint_offsets, workspace, workspace_bytes, stream);
 }
 
 int kda_decode(kda_dtype io_dtype, const void *q, const void *k, const void *v, const float *z,

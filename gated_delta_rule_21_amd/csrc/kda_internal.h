@@ -50,6 +50,7 @@ struct PrefillPlan {
     size_t off_meta;         // int32 [N + 1] per-sequence first chunk, then [1] total
     size_t off_table;        // int32x4 [max_chunks]: sequence, first token, length, -
     size_t off_null;         // the null row: z = -inf [dk] fp32, zeros [max(dk,dv)] io dtype, beta = 0
+    size_t off_ckoff;        // int32 [N + 1]: first checkpoint of every sequence, then the total
     size_t off_segs;         // int32x4 [N * P]: sequence, first chunk, end chunk, flags
     size_t off_trans;        // P > 1: fp32 [N * P][H][2][dk * dk]: M row-major, then S~ in state layout
     size_t off_sin;          // P > 1: fp32 [N * P][H][dv][dk] incoming state of every segment
@@ -70,6 +71,9 @@ struct PrefillArgs {
     int N, T, H, dk, dv;
     void *o;
     float *hT;
+    float *ck;               // checkpoints [T / ck_interval][H][dv][dk] fp32, or NULL
+    int32_t *ck_offsets;     // caller's copy of the per-sequence checkpoint offsets, or NULL
+    int ck_interval;         // tokens between checkpoints, a multiple of 64
     unsigned char *ws;
     PrefillPlan plan;
     hipStream_t stream;

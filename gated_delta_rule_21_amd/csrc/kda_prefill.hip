@@ -69,7 +69,8 @@ bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, int P, Prefil
     p->off_meta = 0;
     p->off_table = align256((size_t)(N + 2) * 4);
     p->off_null = p->off_table + align256((size_t)p->max_chunks * 16);
-    p->off_segs = p->off_null + align256((size_t)dk * 4 + (size_t)dk * 4 + 4);
+    p->off_ckoff = p->off_null + align256((size_t)dk * 4 + (size_t)dk * 4 + 4);
+    p->off_segs = p->off_ckoff + align256((size_t)(N + 1) * 4);
     const size_t units = (size_t)N * P * H, dd = (size_t)dk * dk * 4;
     p->off_trans = p->off_segs + align256((size_t)N * P * 16);
     p->off_sin = p->off_trans + (P > 1 ? units * 2 * dd : 0);
@@ -90,7 +91,8 @@ constexpr int kModeOutput = 0, kModeTrans = 1;
 // ---------------------------------------------------------------------------
 // Chunk table.  One workgroup.  meta[n] = first chunk of sequence n,
 // meta[N] = number of chunks; table[c] = {n, first token, length, 0};
-// segs[n P + k] = {n, first chunk, end chunk, flags} of segment k of sequence n.
+// segs[n P + k] = {n, first chunk, end chunk, flags} of segment k of sequence n;
+// with checkpoints, ck_off[n] = index of sequence n's first checkpoint.
 // Sequence bounds are clamped to [0, T] and the chunk count to max_chunks,
 // so a malformed cu_seqlens can give wrong results but no stray access.
 // ---------------------------------------------------------------------------
@@ -99,7 +101,9 @@ __global__ void __launch_bounds__(256) chunk_table_kernel(const int32_t *__restr
                                                           int32_t *__restrict__ meta,
                                                           int4 *__restrict__ table,
                                                           float *__restrict__ null_row, int d, int P,
-                                                          int4 *__restrict__ segs) {
+                                                          int4 *__restrict__ segs, int ck_chunks, int ck_cap,
+                                                          int32_t *__restrict__ ck_off,
+                                                          int32_t *__restrict__ ck_off_user) {
     __shared__ int32_t scan[256];
     __shared__ int32_t carry;
     const int tid = threadIdx.x;
@@ -156,6 +160,41 @@ __global__ void __launch_bounds__(256) chunk_table_kernel(const int32_t *__restr
             r.w = kSegValid | (k == 0 ? kSegFirst : 0) | (k == pn - 1 ? kSegLast : 0);
         }
         segs[i] = r;
+    }
+    // checkpoints: sequence n has floor(len / (64 ck_chunks)) of them, the
+    // first at index ck_off[n]; indices are clamped to the caller's ck_cap
+    if (ck_chunks > 0) {
+        __syncthreads();
+        if (tid == 0) carry = 0;
+        __syncthreads();
+        for (int base = 0; base < N; base += 256) {
+            const int n = base + tid;
+            int cnt = 0;
+            if (n < N) {
+                const int s = min(max(cu[n], 0), T), e = min(max(cu[n + 1], 0), T);
+                cnt = e > s ? (e - s) / (kChunk * ck_chunks) : 0;
+            }
+            scan[tid] = cnt;
+            __syncthreads();
+            for (int off = 1; off < 256; off <<= 1) {
+                int x = tid >= off ? scan[tid - off] : 0;
+                __syncthreads();
+                scan[tid] += x;
+                __syncthreads();
+            }
+            if (n < N) {
+                const int first = min(carry + scan[tid] - cnt, ck_cap);
+                ck_off[n] = first;
+                if (ck_off_user) ck_off_user[n] = first;
+            }
+            __syncthreads();
+            if (tid == 255) carry += scan[255];
+            __syncthreads();
+        }
+        if (tid == 0) {
+            ck_off[N] = min(carry, ck_cap);
+            if (ck_off_user) ck_off_user[N] = min(carry, ck_cap);
+        }
     }
 }
 
@@ -249,7 +288,8 @@ template <int D, bool F32IO, int MODE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) inter_kernel(
     const float *__restrict__ h0, const float *__restrict__ s_in, const int4 *__restrict__ segs,
     const int4 *__restrict__ table, int nseg, int H, int max_chunks, const unsigned char *__restrict__ slabs,
-    size_t slab_stride, void *__restrict__ o, float *__restrict__ hT, float *__restrict__ trans, int groups) {
+    size_t slab_stride, void *__restrict__ o, float *__restrict__ hT, float *__restrict__ trans, int groups,
+    const int32_t *__restrict__ meta, const int32_t *__restrict__ ck_off, float *__restrict__ ck, int ck_chunks) {
     static_assert(MODE == kModeOutput || MODE == kModeTrans, "mode");
     constexpr bool TR = MODE == kModeTrans;
     using SL = Slab<D, F32IO>;
@@ -301,6 +341,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
 
     const int c_begin = rec.y, c_end = rec.z;
+    // state checkpoints (output mode): after every chunk that ends 64 ck_chunks
+    // tokens into the sequence, up to the sequence's count
+    int ck_c0 = 0, ck_first = 0, ck_count = 0;
+    if (MODE == kModeOutput && ck) {
+        ck_c0 = meta[n];
+        ck_first = ck_off[n];
+        ck_count = ck_off[n + 1] - ck_first;
+    }
+    auto checkpoint = [&](int c) {   // S holds the state after chunk c
+        if (MODE != kModeOutput || !ck) return;
+        const int pos = c - ck_c0 + 1;
+        if (pos % ck_chunks != 0 || pos / ck_chunks > ck_count) return;
+        float *dst = ck + (((size_t)(ck_first + pos / ck_chunks - 1) * H + h) * D + col) * D;
+#pragma unroll
+        for (int t = 0; t < KT; ++t) *reinterpret_cast<f32x4 *>(dst + 16 * t + 4 * lg) = S[t];
+    };
     auto slab_of = [&](int c) { return slabs + ((size_t)h * max_chunks + c) * slab_stride; };
     // U: fp32 tiles (fp32 path) or fp16 tiles with a per-tile exponent (bf16 path)
     using UReg = typename std::conditional<F32IO, f32x4, u32x2>::type;
@@ -383,6 +439,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             const int *uexp = reinterpret_cast<const int *>(bbuf + (SL::uexp - SL::kdT));
             if constexpr (MODE == kModeOutput) {
                 if (o_L > 0) flush_o(par ^ 1, o_t0, o_L);   // the previous chunk's rows
+                if (i > 0) checkpoint(c - 1);
             }
             if (c + 1 < c_end) {
                 load_u(c + 1, un);
@@ -484,6 +541,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
         }
         if constexpr (MODE == kModeOutput) {
             if (o_L > 0) flush_o((c_end - c_begin - 1) & 1, o_t0, o_L);
+            if (c_begin < c_end) checkpoint(c_end - 1);
         }
         o_L = 0;
     } else {
@@ -500,6 +558,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             if (c + 1 < c_end) load_u(c + 1, un);
             if constexpr (MODE == kModeOutput) {
                 if (o_L > 0) store_o_tile<F32IO>(o, acc_o, o_t0, o_L, H, h, D, col, lg);
+                if (c > c_begin) checkpoint(c - 1);
             }
             const int4 ent = table[c];
             f32x4 vp[4], vp2[TR ? 4 : 1];
@@ -553,6 +612,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
     if constexpr (MODE == kModeOutput) {
         if (o_L > 0) store_o_tile<F32IO>(o, acc_o, o_t0, o_L, H, h, D, col, lg);
+        if (F32IO && c_begin < c_end) checkpoint(c_end - 1);
         if (hT && (rec.w & kSegLast)) {
             float *dst = hT + ((size_t)(n * H + h) * D + col) * D;
 #pragma unroll
@@ -687,8 +747,12 @@ static int launch_prefill_t(const PrefillArgs &a) {
     unsigned char *slabs = a.ws + p.off_slabs;
 
     int4 *segs = reinterpret_cast<int4 *>(a.ws + p.off_segs);
+    int32_t *ck_off = reinterpret_cast<int32_t *>(a.ws + p.off_ckoff);
+    const int ck_chunks = (a.ck || a.ck_offsets) ? a.ck_interval / kChunk : 0;
+    const int ck_cap = ck_chunks ? a.T / a.ck_interval : 0;
     hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, a.stream, a.cu, a.N, a.T,
-                       p.max_chunks, meta, table, reinterpret_cast<float *>(a.ws + p.off_null), D, p.P, segs);
+                       p.max_chunks, meta, table, reinterpret_cast<float *>(a.ws + p.off_null), D, p.P, segs,
+                       ck_chunks, ck_cap, ck_off, a.ck_offsets);
     if (hipGetLastError() != hipSuccess) return -1;
 
     if constexpr (!F32IO) {
@@ -710,7 +774,7 @@ static int launch_prefill_t(const PrefillArgs &a) {
         if (!set_lds(&inter_kernel<D, F32IO, M>, SHP::lds_bytes)) return false;
         hipLaunchKernelGGL((inter_kernel<D, F32IO, M>), dim3(unit_blocks * groups), dim3(SHP::NT), SHP::lds_bytes,
                            a.stream, a.h0, s_in, segs, table, nseg, a.H, p.max_chunks, slabs, p.slab_bytes, a.o,
-                           a.hT, trans, groups);
+                           a.hT, trans, groups, meta, ck_off, a.ck, ck_chunks);
         return hipGetLastError() == hipSuccess;
     };
     if (p.P > 1) {

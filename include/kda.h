@@ -76,6 +76,32 @@ typedef enum kda_status {
 size_t kda_prefill_workspace_size(int N, int T, int H, int dk, int dv, kda_dtype io_dtype);
 
 /*
+ * kda_prefill that also saves state checkpoints for prefix reuse ("Kimi
+ * K3：架构…" §12.2: KDA checkpoints are large, so they are kept at a coarser
+ * grain than the token hash blocks, e.g. at 512-token endpoints; the s1mplewind
+ * notes, "KDA存checkpoint").
+ *
+ *   interval            tokens between checkpoints, a positive multiple of 64
+ *   checkpoints         [T / interval][H][dv][dk] fp32 device buffer (T / interval
+ *                       rounded down: an upper bound on the count for any
+ *                       cu_seqlens); checkpoint j of sequence n is the state
+ *                       after the first (j + 1) * interval tokens of the
+ *                       sequence (h0 included), for j < floor(len_n / interval),
+ *                       stored at index checkpoint_offsets[n] + j; sequence-major
+ *   checkpoint_offsets  [N + 1] int32 device buffer or NULL: first checkpoint
+ *                       index of every sequence, then the total
+ * Entries past the total are left untouched.  Everything else, including the
+ * workspace size and the error behaviour, is kda_prefill's; checkpoints and
+ * offsets may overlap no other argument.  With checkpoints = NULL and
+ * checkpoint_offsets = NULL this is kda_prefill (interval is then ignored).
+ */
+int kda_prefill_checkpoints(kda_dtype io_dtype, const void *q, const void *k, const void *v,
+                            const float *z, const float *A, const float *beta, const float *h0,
+                            const int32_t *cu_seqlens, int N, int T, int H, int dk, int dv, void *o,
+                            float *hT, int interval, float *checkpoints, int32_t *checkpoint_offsets,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Intra-device context parallelism ("Kimi K3：架构…" §8.1 and §11.1: a
  * planner splits one sequence over a device's compute units; the pieces'
  * state transitions are computed without the incoming state and merged

@@ -20,6 +20,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["kda_build_info", "kda_decode", "kda_decode_window", "kda_prefill",
+                                           "kda_prefill_checkpoints",
                                            "kda_prefill_segments", "kda_prefill_workspace_size",
                                            "kda_set_prefill_segments", "kda_status_string"])
 
@@ -140,3 +141,21 @@ def test_decode_window_rejects_bad_arguments():
     assert w(rk=None, rv=None, rz=None, rb=None, acc=None, Lr=0, o=FAKE + 8) == -5   # misaligned o
     assert w(o=FAKE + 24576) == -8                # o on top of k
     assert w(S=FAKE) == -8                        # state on top of the replay keys
+
+
+def test_prefill_checkpoints_rejects_bad_arguments():
+    def c(**o):
+        a = dict(interval=512, ck=1 << 26, off=(1 << 26) - 4096, T=4096, ws_bytes=1 << 40)
+        a.update(o)
+        return kda.kda_prefill_checkpoints(0, FAKE, FAKE + 4096 * 64, FAKE + 2 * 4096 * 64, FAKE + 3 * 4096 * 64,
+                                           FAKE + 4 * 4096 * 64, FAKE + 6 * 4096 * 64, None, FAKE + 7 * 4096 * 64,
+                                           1, a["T"], 2, 32, 32, 1 << 25, None, a["interval"], a["ck"], a["off"],
+                                           1 << 30, a["ws_bytes"], None)
+    assert c(interval=0) == -1
+    assert c(interval=100) == -1
+    assert c(interval=-64) == -1
+    assert c(ck=(1 << 26) + 8) == -5
+    assert c(ck=1 << 25) == -8                       # checkpoints on top of o
+    assert c(ck=FAKE) == -8                          # checkpoints on top of q
+    assert c(off=1 << 30) == -8                      # offsets inside the workspace
+    assert c(ck=None, off=None, interval=0, ws_bytes=0) == -6   # no checkpoints: plain prefill checks
