@@ -10,6 +10,8 @@ Contents
   decode(...)        one decode step (C)
   gate(A, z)         the bounded log-decay, numpy fp64
   chunkwise.prefill  the chunkwise-parallel form, numpy fp64 (a cross-check)
+  features           the q/k/v feature path (ShortConv -> Swish -> L2Norm) and
+                     the output gate (Sigmoid(g) * RMSNorm(o)), numpy fp64
 
 Every input array is numpy: q, k, v either float32 or the raw uint16 bits of
 bfloat16 (``workloads.as_numpy`` makes them); z, A, beta float32; the
