@@ -78,6 +78,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--decode-steps", type=int, default=1000)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-features", action="store_true",
+                   help="skip the side measurement of the feature path and output gate")
     p.add_argument("--no-checkpoints", action="store_true",
                    help="skip the side measurement of the prefill with 512-token checkpoints")
     p.add_argument("--no-decode-window", action="store_true",
@@ -214,6 +216,39 @@ def prefill_checkpoint_cost(kda, pre, o, hT, ws, interval: int = 512, reps: int 
             "checkpoint_GB": round((T // interval) * H * D * D * 4 / 1e9, 3)}
 
 
+def feature_path_cost(kda, W, dev, reps: int = 10) -> dict:
+    """Side measurement at the K3 prefill shape (T=65536, H=96, d=128, bf16):
+    the ShortConv -> Swish -> L2Norm feature path for q, k, v (with a carried
+    window) and the Sigmoid(g) * RMSNorm(o) output gate.  Algorithmic bytes:
+    three inputs read and three outputs written; o and g read and y written."""
+    import torch
+    f = W.random_features([65536], 96, 128, "bf16", window=True, device=dev)
+    T, H, D = f["xq"].shape
+    q, k, v = (torch.empty_like(f["xq"]) for _ in range(3))
+    win_out = torch.empty_like(f["window"])
+    y = torch.empty_like(f["o"])
+
+    def timed(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_qkv = timed(lambda: kda.qkv_shortconv(f["xq"], f["xk"], f["xv"], f["wq"], f["wk"], f["wv"],
+                                             f["cu_seqlens"], conv_state_in=f["window"],
+                                             conv_state_out=win_out, q=q, k=k, v=v))
+    ms_gate = timed(lambda: kda.output_gate(f["o"], f["g"], f["w"], 1e-6, y=y))
+    row = T * H * D * 2
+    return {"workload": "K3 shape T=65536 H=96 d=128 bf16",
+            "qkv_shortconv": {"ms": round(ms_qkv, 4), "GBps": round(6 * row / (ms_qkv * 1e-3) / 1e9, 1)},
+            "output_gate": {"ms": round(ms_gate, 4), "GBps": round(3 * row / (ms_gate * 1e-3) / 1e9, 1)}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -320,6 +355,8 @@ def main():
                      "kernel": "kda_prefill (chunk table + intra + inter kernels), "
                                "1540 algorithmic B per (token, head) x 6291456 pairs per launch"},
     }
+    if not args.no_features:
+        line["feature_path"] = feature_path_cost(kda, W, dev)
     if not args.no_checkpoints:
         line["prefill_checkpoints"] = prefill_checkpoint_cost(kda, pre, o, hT, ws)
     if not args.no_small_head:

@@ -10,6 +10,8 @@ Entry points (same names as the C ABI in include/kda.h):
   kda_decode(...)                   raw C call
   kda_decode_window(...)            raw C call: replay + multi-token window
   kda_prefill_checkpoints(...)      raw C call: prefill + state checkpoints
+  kda_qkv_shortconv(...)            raw C call: ShortConv -> Swish -> L2Norm feature path
+  kda_output_gate(...)              raw C call: Sigmoid(g) * RMSNorm(o)
   kda_prefill_workspace_size(...)
   kda_set_prefill_segments(P), kda_prefill_segments(...)
                                     segment split of long sequences
@@ -19,6 +21,8 @@ Convenience wrappers over torch tensors:
   decode(q, k, v, z, A, beta, S) -> o          (S updated in place)
   decode_window(A, S, window=..., replay=..., n_accept=...) -> o
   prefill_checkpoints(..., interval) -> (o, hT, checkpoints, offsets)
+  qkv_shortconv(xq, xk, xv, wq, wk, wv, cu_seqlens, ...) -> (q, k, v)
+  output_gate(o, g, w, eps) -> y
 """
 from __future__ import annotations
 
@@ -58,6 +62,11 @@ def lib():
     L.kda_prefill_workspace_size.restype = sz
     L.kda_decode.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, vp, vp]
     L.kda_decode.restype = ci
+    L.kda_qkv_shortconv.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, vp, vp, vp, vp,
+                                    vp, vp]
+    L.kda_qkv_shortconv.restype = ci
+    L.kda_output_gate.argtypes = [ci, vp, vp, vp, ctypes.c_float, ci, ci, ci, vp, vp]
+    L.kda_output_gate.restype = ci
     L.kda_prefill_checkpoints.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, vp,
                                           vp, ci, vp, vp, vp, sz, vp]
     L.kda_prefill_checkpoints.restype = ci
@@ -86,6 +95,16 @@ def kda_prefill(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv, 
 
 def kda_decode(io_dtype, q, k, v, z, A, beta, S_inout, N, H, dk, dv, o, stream) -> int:
     return lib().kda_decode(io_dtype, q, k, v, z, A, beta, S_inout, N, H, dk, dv, o, stream)
+
+
+def kda_qkv_shortconv(io_dtype, xq, xk, xv, wq, wk, wv, cu_seqlens, N, T, H, dk, dv, conv_state_in,
+                      conv_state_out, q, k, v, stream) -> int:
+    return lib().kda_qkv_shortconv(io_dtype, xq, xk, xv, wq, wk, wv, cu_seqlens, N, T, H, dk, dv,
+                                   conv_state_in, conv_state_out, q, k, v, stream)
+
+
+def kda_output_gate(io_dtype, o, g, w, eps, T, H, dv, y, stream) -> int:
+    return lib().kda_output_gate(io_dtype, o, g, w, eps, T, H, dv, y, stream)
 
 
 def kda_prefill_checkpoints(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv, o, hT,
@@ -297,3 +316,38 @@ def prefill_checkpoints(q, k, v, z, A, beta, cu_seqlens, interval: int, h0=None,
     if st != 0:
         raise KdaError("kda_prefill_checkpoints", st)
     return o, hT, checkpoints, offsets
+
+
+def qkv_shortconv(xq, xk, xv, wq, wk, wv, cu_seqlens, conv_state_in=None, conv_state_out=None,
+                  q=None, k=None, v=None):
+    """The feature path: returns (q, k, v) = (L2Norm(Swish(ShortConv(xq))), ...,
+    Swish(ShortConv(xv))).  conv_state_* are [N, 3, H, 3 d] windows of the
+    last pre-convolution tokens (conv_state_out may be conv_state_in)."""
+    torch = _torch()
+    _check_gpu(xq=xq, xk=xk, xv=xv, wq=wq, wk=wk, wv=wv, cu_seqlens=cu_seqlens,
+               conv_state_in=conv_state_in, conv_state_out=conv_state_out, q=q, k=k, v=v)
+    io = _io_code(xq)
+    T, H, d = xq.shape
+    N = cu_seqlens.numel() - 1
+    q = torch.empty_like(xq) if q is None else q
+    k = torch.empty_like(xk) if k is None else k
+    v = torch.empty_like(xv) if v is None else v
+    st = kda_qkv_shortconv(io, _ptr(xq), _ptr(xk), _ptr(xv), _ptr(wq), _ptr(wk), _ptr(wv),
+                           _ptr(cu_seqlens), N, T, H, d, xv.shape[-1], _ptr(conv_state_in),
+                           _ptr(conv_state_out), _ptr(q), _ptr(k), _ptr(v), _stream(xq.device))
+    if st != 0:
+        raise KdaError("kda_qkv_shortconv", st)
+    return q, k, v
+
+
+def output_gate(o, g, w, eps: float, y=None):
+    """y = Sigmoid(g) * RMSNorm(o) per (token, head) row; y may be o or g."""
+    torch = _torch()
+    _check_gpu(o=o, g=g, w=w, y=y)
+    T, H, dv = o.shape
+    y = torch.empty_like(o) if y is None else y
+    st = kda_output_gate(_io_code(o), _ptr(o), _ptr(g), _ptr(w), float(eps), T, H, dv, _ptr(y),
+                         _stream(o.device))
+    if st != 0:
+        raise KdaError("kda_output_gate", st)
+    return y

@@ -205,6 +205,62 @@ int kda_decode(kda_dtype io_dtype, const void *q, const void *k, const void *v, 
     return kda::launch_decode(a) == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 
+int kda_qkv_shortconv(kda_dtype io_dtype, const void *xq, const void *xk, const void *xv, const float *wq,
+                      const float *wk, const float *wv, const int32_t *cu_seqlens, int N, int T, int H, int dk,
+                      int dv, const void *conv_state_in, void *conv_state_out, void *q, void *k, void *v,
+                      void *stream) {
+    if (io_dtype != KDA_BF16 && io_dtype != KDA_F32) return KDA_ERR_UNSUPPORTED_DTYPE;
+    if (N < 0 || T < 0 || H <= 0 || (T > 0 && N == 0)) return KDA_ERR_INVALID_ARGUMENT;
+    if (!supported_dim(dk, dv)) return KDA_ERR_UNSUPPORTED_DIM;
+    if (!cu_seqlens || !wq || !wk || !wv) return KDA_ERR_NULL_POINTER;
+    if (T > 0 && (!xq || !xk || !xv || !q || !k || !v)) return KDA_ERR_NULL_POINTER;
+    const void *ptrs[] = {xq, xk, xv, wq, wk, wv, cu_seqlens, conv_state_in, conv_state_out, q, k, v};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    const size_t io = io_size(io_dtype), tok = (size_t)T * H * dk * io;
+    const size_t win = (size_t)N * 3 * H * 3 * dk * io;
+    const struct { const void *p; size_t n; } ins[] = {
+        {xq, tok}, {xk, tok}, {xv, tok}, {wq, (size_t)H * dk * 16}, {wk, (size_t)H * dk * 16},
+        {wv, (size_t)H * dk * 16}, {cu_seqlens, (size_t)(N + 1) * 4}, {conv_state_in, win}};
+    const struct { const void *p; size_t n; } outs[] = {{q, tok}, {k, tok}, {v, tok}, {conv_state_out, win}};
+    for (const auto &ot : outs) {
+        for (const auto &in : ins)
+            if (!(ot.p == conv_state_out && in.p == conv_state_in && ot.p == in.p) && overlaps(ot.p, ot.n, in.p, in.n))
+                return KDA_ERR_ALIAS;
+        for (const auto &o2 : outs)
+            if (&o2 != &ot && overlaps(ot.p, ot.n, o2.p, o2.n)) return KDA_ERR_ALIAS;
+    }
+    kda::FeatureArgs a;
+    a.f32io = io_dtype == KDA_F32;
+    a.xq = xq; a.xk = xk; a.xv = xv; a.wq = wq; a.wk = wk; a.wv = wv;
+    a.cu = cu_seqlens; a.N = N; a.T = T; a.H = H; a.d = dk;
+    a.win_in = conv_state_in; a.win_out = conv_state_out;
+    a.q = q; a.k = k; a.v = v;
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+    return kda::launch_features(a) == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_output_gate(kda_dtype io_dtype, const void *o, const void *g, const float *w, float eps, int T, int H,
+                    int dv, void *y, void *stream) {
+    if (io_dtype != KDA_BF16 && io_dtype != KDA_F32) return KDA_ERR_UNSUPPORTED_DTYPE;
+    if (T < 0 || H <= 0 || !(eps >= 0.f)) return KDA_ERR_INVALID_ARGUMENT;
+    if (!(dv == 32 || dv == 64 || dv == 128)) return KDA_ERR_UNSUPPORTED_DIM;
+    if (!w) return KDA_ERR_NULL_POINTER;
+    if (T > 0 && (!o || !g || !y)) return KDA_ERR_NULL_POINTER;
+    const void *ptrs[] = {o, g, w, y};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    const size_t n = (size_t)T * H * dv * io_size(io_dtype);
+    // y may be o or g exactly (every element is read before it is written), nothing else
+    if ((y != o && overlaps(y, n, o, n)) || (y != g && overlaps(y, n, g, n)) || overlaps(y, n, w, (size_t)dv * 4))
+        return KDA_ERR_ALIAS;
+    kda::GateArgs a;
+    a.f32io = io_dtype == KDA_F32;
+    a.o = o; a.g = g; a.w = w; a.eps = eps; a.T = T; a.H = H; a.dv = dv; a.y = y;
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+    return kda::launch_output_gate(a) == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
 int kda_decode_window(kda_dtype io_dtype, const void *rk, const void *rv, const float *rz,
                       const float *rbeta, const int32_t *n_accept, int Lr, const void *q, const void *k,
                       const void *v, const float *z, const float *beta, int L, const float *A,

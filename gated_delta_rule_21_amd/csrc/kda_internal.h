@@ -38,6 +38,31 @@ struct DecodeWindowArgs {
     hipStream_t stream;
 };
 
+// Feature path: q, k = L2Norm(Swish(ShortConv(x))), v = Swish(ShortConv(x)).
+// x [T][H][d] io dtype, w [H][d][4] fp32, windows [N][3][H][3d] io dtype.
+struct FeatureArgs {
+    bool f32io;
+    const void *xq, *xk, *xv;
+    const float *wq, *wk, *wv;
+    const int32_t *cu;
+    int N, T, H, d;
+    const void *win_in;
+    void *win_out;
+    void *q, *k, *v;
+    hipStream_t stream;
+};
+
+// Output gate: y = Sigmoid(g) * RMSNorm(o), rows of dv.
+struct GateArgs {
+    bool f32io;
+    const void *o, *g;
+    const float *w;
+    float eps;
+    int T, H, dv;
+    void *y;
+    hipStream_t stream;
+};
+
 // Longest replay and window the decode-window kernel stages in LDS.
 constexpr int kMaxWindow = 16;
 
@@ -88,6 +113,8 @@ size_t slab_bytes(int dk, int dv, bool f32io);
 
 int launch_decode(const DecodeArgs &a);
 int launch_decode_window(const DecodeWindowArgs &a);
+int launch_features(const FeatureArgs &a);
+int launch_output_gate(const GateArgs &a);
 int launch_prefill(const PrefillArgs &a);
 // Intra-chunk kernels (kda_intra.hip: bf16 path; kda_intra_f32.hip: fp32
 // path), D = 32, 64, 128.

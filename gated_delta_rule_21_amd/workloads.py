@@ -214,6 +214,29 @@ def random_decode_window(N: int, H: int, d: int, Lr: int, L: int, io: str = "bf1
                 Lr=Lr, L=L, io=io)
 
 
+def random_features(lens, H: int, d: int, io: str = "bf16", window: bool = True,
+                    seed: int = BASE_SEED + 6, device="cpu") -> dict:
+    """Draw inputs of the feature path and output gate: pre-convolution
+    projections x ~ N(0, 1) in the io dtype, taps ~ N(0, 1/4) fp32, an
+    optional carried window [N, 3, H, 3 d] ~ N(0, 1), the recurrence output o
+    ~ N(0, 1) and gate g ~ N(0, 4) in the io dtype, RMSNorm weight ~ 1 + N(0, 0.1)."""
+    device = torch.device(device)
+    g = _gen(device, seed)
+    f32 = torch.float32
+    T, N = int(sum(lens)), len(lens)
+    io_t = torch_dtype(io)
+    x = lambda: torch.randn(T, H, d, generator=g, device=device, dtype=f32).to(io_t)
+    taps = lambda: torch.randn(H, d, 4, generator=g, device=device, dtype=f32) * 0.5
+    out = dict(xq=x(), xk=x(), xv=x(), wq=taps(), wk=taps(), wv=taps(), cu_seqlens=cu_from_lengths(lens).to(device),
+               N=N, T=T, H=H, d=d, io=io)
+    out["window"] = (torch.randn(N, 3, H, 3 * d, generator=g, device=device, dtype=f32).to(io_t)
+                     if window else None)
+    out["o"] = x()
+    out["g"] = (torch.randn(T, H, d, generator=g, device=device, dtype=f32) * 2.0).to(io_t)
+    out["w"] = 1.0 + 0.1 * torch.randn(d, generator=g, device=device, dtype=f32)
+    return out
+
+
 def make(name: str, device="cpu", seed: Optional[int] = None, **over) -> dict:
     """Inputs for a named workload (see WORKLOADS)."""
     w = WORKLOADS[name]

@@ -208,6 +208,47 @@ int kda_decode_window(kda_dtype io_dtype, const void *rk, const void *rv, const 
                       const float *A, float *S_inout, int N, int H, int dk, int dv, void *o,
                       int commit_window, void *stream);
 
+/*
+ * The q/k/v feature path ("Kimi K3：架构…" §3.2; devpress K3 walk-through
+ * §3.1):  q = L2Norm(Swish(ShortConv(xq))), k = L2Norm(Swish(ShortConv(xk))),
+ * v = Swish(ShortConv(xv)), with Swish(u) = u * sigmoid(u) and the L2 norm over
+ * each (token, head) row.  ShortConv is a causal depthwise convolution over the
+ * tokens of each sequence with 4 taps per channel:
+ *   c_t = w[0] x_{t-3} + w[1] x_{t-2} + w[2] x_{t-1} + w[3] x_t,
+ * where positions before the sequence's first token read the carried window.
+ *
+ *   xq, xk, xv         [T][H][d] io dtype: the projected inputs W_q x, W_k x, W_v x
+ *   wq, wk, wv         [H][d][4] fp32 taps
+ *   cu_seqlens         [N+1] int32 device array, as for kda_prefill
+ *   conv_state_in      [N][3][H][3d] io dtype or NULL (zeros): per sequence the
+ *                      last three pre-convolution tokens before it, oldest
+ *                      first, channels [xq | xk | xv]
+ *   conv_state_out     same shape or NULL: the window after the sequence (the
+ *                      last three tokens of [window, sequence]); may be
+ *                      conv_state_in itself
+ *   q, k, v            [T][H][d] io dtype outputs, ready for kda_prefill; for a
+ *                      decode step use T = N and cu_seqlens = 0, 1, ..., N
+ * dk == dv in {32, 64, 128}.  Outputs may overlap no input (except the state
+ * in place) and no other output.
+ */
+int kda_qkv_shortconv(kda_dtype io_dtype, const void *xq, const void *xk, const void *xv,
+                      const float *wq, const float *wk, const float *wv,
+                      const int32_t *cu_seqlens, int N, int T, int H, int dk, int dv,
+                      const void *conv_state_in, void *conv_state_out, void *q, void *k,
+                      void *v, void *stream);
+
+/*
+ * The output gate ("Kimi K3：架构…" §3.3; devpress §3.3, Eq 6):
+ *   y = Sigmoid(g) * RMSNorm(o),  RMSNorm(o) = o / sqrt(mean(o^2) + eps) * w
+ * per (token, head) row of dv channels.  g is the gate projection W_g x.
+ *
+ *   o, g, y     [T][H][dv] io dtype; y may be o or g (in place)
+ *   w           [dv] fp32 weight, shared by the heads;  eps >= 0
+ * The final projection W_o is not part of the op.
+ */
+int kda_output_gate(kda_dtype io_dtype, const void *o, const void *g, const float *w, float eps,
+                    int T, int H, int dv, void *y, void *stream);
+
 /* Static, human-readable text for a kda_status value. */
 const char *kda_status_string(int status);
 

@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["kda_build_info", "kda_decode", "kda_decode_window", "kda_prefill",
-                                           "kda_prefill_checkpoints",
+                                           "kda_prefill_checkpoints", "kda_qkv_shortconv", "kda_output_gate",
                                            "kda_prefill_segments", "kda_prefill_workspace_size",
                                            "kda_set_prefill_segments", "kda_status_string"])
 
@@ -159,3 +159,31 @@ def test_prefill_checkpoints_rejects_bad_arguments():
     assert c(ck=FAKE) == -8                          # checkpoints on top of q
     assert c(off=1 << 30) == -8                      # offsets inside the workspace
     assert c(ck=None, off=None, interval=0, ws_bytes=0) == -6   # no checkpoints: plain prefill checks
+
+
+def test_feature_path_and_gate_reject_bad_arguments():
+    def f(**o):
+        a = dict(io=0, xq=FAKE, xk=FAKE + 65536, xv=FAKE + 2 * 65536, w=1 << 24, cu=(1 << 24) + 65536, N=1, T=64,
+                 H=2, dk=128, dv=128, win_in=None, win_out=None, q=1 << 26, k=(1 << 26) + 65536,
+                 v=(1 << 26) + 2 * 65536)
+        a.update(o)
+        w2 = None if a["w"] is None else a["w"] + 4096
+        w3 = None if a["w"] is None else a["w"] + 8192
+        return kda.kda_qkv_shortconv(a["io"], a["xq"], a["xk"], a["xv"], a["w"], w2, w3,
+                                     a["cu"], a["N"], a["T"], a["H"], a["dk"], a["dv"], a["win_in"], a["win_out"],
+                                     a["q"], a["k"], a["v"], None)
+    assert f(io=3) == -4
+    assert f(T=64, N=0) == -1 and f(H=0) == -1
+    assert f(dk=64) == -3 and f(dk=48, dv=48) == -3
+    assert f(cu=None) == -2 and f(xq=None) == -2 and f(w=None) == -2
+    assert f(q=(1 << 26) + 4) == -5
+    assert f(q=FAKE) == -8                                   # q on top of xq
+    assert f(k=1 << 26) == -8                                # k on top of q
+    assert f(win_in=1 << 28, win_out=(1 << 28) + 256) == -8  # windows partly overlapping
+    # the gate
+    g = lambda **o: kda.kda_output_gate(o.get("io", 0), o.get("o", FAKE), o.get("g", FAKE + 65536),
+                                        o.get("w", 1 << 24), o.get("eps", 1e-6), 64, 2, o.get("dv", 128),
+                                        o.get("y", 1 << 26), None)
+    assert g(io=2) == -4 and g(eps=-1.0) == -1 and g(eps=float("nan")) == -1
+    assert g(dv=48) == -3 and g(w=None) == -2 and g(y=(1 << 26) + 2) == -5
+    assert g(y=FAKE + 256) == -8                             # y partly over o
