@@ -26,7 +26,9 @@
 // inclusive) and ke = k exp2(bt - Gl) (bt: the block's total log-decay); fac
 // is exp2(-bt_b) on the diagonal tile and the decay of the blocks strictly
 // between b and I otherwise.  Only kr and qr of blocks 1..3 go through LDS.
-// Products are split-bf16 (hi + lo, three MFMAs), good to about 2^-16.
+// Diagonal tiles, where fac reaches e^80, and the W / U products are
+// split-bf16 (hi + lo, three MFMAs, good to about 2^-16); off-diagonal Gram
+// tiles have every factor <= 1 and use fp16 operands (one MFMA).
 //
 // Phases (barriers between them):
 //   1  gate, block-local cumulative log-decay (DPP row scan), kr / qr / ke
@@ -74,8 +76,8 @@ template <int D>
 struct Intra4Lds {
     static constexpr int KT = D / 16, NP = D / 32;
     static constexpr size_t FR = 1024;
-    // X, phases 1-2: split row fragments of kr and qr of row blocks 1..3,
-    //   [block - 1][kr, qr][pair p][hi, lo] fragments.
+    // X, phases 1-2: fp16 row fragments of kr and qr of row blocks 1..3,
+    //   [block - 1][kr, qr][pair p], read by the off-diagonal Gram tiles.
     // X, phases 3-5: (Gamma*K)^T fragments [t][row pair f][hi, lo], then V^T
     //   fragments [t][f]; the 8 bytes of block 2f + s sit at slot s of a lane.
     static constexpr size_t X = 0;
@@ -233,18 +235,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
             ke[kt] = kev;
             if (ln == 15) *reinterpret_cast<f32x4 *>(bt_lds + b * D + 16 * kt + 4 * lg) = bt;
         }
-        if (b > 0) {
+        if (b > 0) {   // other blocks read these for their off-diagonal tiles (fp16)
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
-                u32x4 hi, lo;
-                unsigned char *dk = X + ((size_t)(((b - 1) * 2 + 0) * NP + p) * 2) * FR + lane * 16;
-                quads_to_bf16_split(kr[2 * p], kr[2 * p + 1], hi, lo);
-                *reinterpret_cast<u32x4 *>(dk) = hi;
-                *reinterpret_cast<u32x4 *>(dk + FR) = lo;
-                unsigned char *dq = X + ((size_t)(((b - 1) * 2 + 1) * NP + p) * 2) * FR + lane * 16;
-                quads_to_bf16_split(qr[2 * p], qr[2 * p + 1], hi, lo);
-                *reinterpret_cast<u32x4 *>(dq) = hi;
-                *reinterpret_cast<u32x4 *>(dq + FR) = lo;
+                *reinterpret_cast<u32x4 *>(X + ((size_t)((b - 1) * 2 + 0) * NP + p) * FR + lane * 16) =
+                    quads_to_f16(kr[2 * p], kr[2 * p + 1]);
+                *reinterpret_cast<u32x4 *>(X + ((size_t)((b - 1) * 2 + 1) * NP + p) * FR + lane * 16) =
+                    quads_to_f16(qr[2 * p], qr[2 * p + 1]);
             }
         }
         __syncthreads();
@@ -295,24 +292,33 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int I = b; I < 4; ++I) {
             const float *fac = fac_lds + (I == b ? b : 12 + off_index(b, I)) * D;
             f32x4 akk = zero4(), aqt = zero4();
+            if (I == b) {
+                // diagonal tile: the wave's own rows; fac = exp2(-bt_b) reaches
+                // e^80, beyond fp16, so split-bf16 operands
 #pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                const int c0 = 32 * p + 4 * lg, c1 = c0 + 16;
-                u32x4 kch, kcl, krh, krl, qrh, qrl;
-                quads_to_bf16_split(ke[2 * p] * ld4(fac + c0), ke[2 * p + 1] * ld4(fac + c1), kch, kcl);
-                if (I == 0) {   // block 0's own rows are not in X
+                for (int p = 0; p < NP; ++p) {
+                    const int c0 = 32 * p + 4 * lg, c1 = c0 + 16;
+                    u32x4 kch, kcl, krh, krl, qrh, qrl;
+                    quads_to_bf16_split(ke[2 * p] * ld4(fac + c0), ke[2 * p + 1] * ld4(fac + c1), kch, kcl);
                     quads_to_bf16_split(kr[2 * p], kr[2 * p + 1], krh, krl);
                     quads_to_bf16_split(qr[2 * p], qr[2 * p + 1], qrh, qrl);
-                } else {
-                    const unsigned char *dk = X + ((size_t)(((I - 1) * 2 + 0) * NP + p) * 2) * FR + lane * 16;
-                    const unsigned char *dq = X + ((size_t)(((I - 1) * 2 + 1) * NP + p) * 2) * FR + lane * 16;
-                    krh = *reinterpret_cast<const u32x4 *>(dk);
-                    krl = *reinterpret_cast<const u32x4 *>(dk + FR);
-                    qrh = *reinterpret_cast<const u32x4 *>(dq);
-                    qrl = *reinterpret_cast<const u32x4 *>(dq + FR);
+                    akk = mma3_bf16(krh, krl, kch, kcl, akk);
+                    aqt = mma3_bf16(kch, kcl, qrh, qrl, aqt);
                 }
-                akk = mma3_bf16(krh, krl, kch, kcl, akk);
-                aqt = mma3_bf16(kch, kcl, qrh, qrl, aqt);
+            } else {
+                // off-diagonal tile: every factor is a decay <= 1 and |k|, |q| <= 1,
+                // so fp16 operands (11-bit mantissas) in range
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    const int c0 = 32 * p + 4 * lg, c1 = c0 + 16;
+                    const u32x4 kc = quads_to_f16(ke[2 * p] * ld4(fac + c0), ke[2 * p + 1] * ld4(fac + c1));
+                    const u32x4 kx = *reinterpret_cast<const u32x4 *>(X + ((size_t)((I - 1) * 2 + 0) * NP + p) * FR +
+                                                                      lane * 16);
+                    const u32x4 qx = *reinterpret_cast<const u32x4 *>(X + ((size_t)((I - 1) * 2 + 1) * NP + p) * FR +
+                                                                      lane * 16);
+                    akk = mma_f16_k32(kx, kc, akk);
+                    aqt = mma_f16_k32(kc, qx, aqt);
+                }
             }
             // A_kk tile: lane (n = i, g) holds the sum for rows r = 4g + j of block I
 #pragma unroll
