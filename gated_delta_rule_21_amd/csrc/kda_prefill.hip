@@ -245,6 +245,30 @@ __device__ __forceinline__ void copy_frags_to_lds(const unsigned char *src, unsi
 
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
+// A global load the compiler does not track.  The compiler counts vmcnt for
+// its own loads only up to the first direct global->LDS copy issued after
+// them, and waits for everything (vmcnt(0)) at their use.  Loads issued with
+// this helper before a step's copies are instead covered by the step's
+// explicit in-order wait; `settle` then marks the register as written at
+// that point, so that no use of it can move above the wait.
+__device__ __forceinline__ u32x2 load_untracked(const u32x2 *p) {
+    u32x2 r;
+    asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+    return r;
+}
+__device__ __forceinline__ void settle(u32x2 &r) { asm volatile("" : "+v"(r)); }
+
+// Workgroup barrier for LDS written by ds instructions.  __syncthreads (and
+// any release fence covering LDS) also waits for every direct global->LDS
+// copy still in flight, since those are LDS writes counted by vmcnt --
+// including copies meant for a later step.  Here the caller waits for the
+// copies it needs with an explicit vmcnt; the barrier waits for the wave's
+// own ds operations only.  The asm's memory clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Store a finished 64 x 16 output tile (accumulator layout) for rows < L.
 template <bool F32IO>
 __device__ __forceinline__ void store_o_tile(void *o, const f32x4 (&acc)[4], int t0, int L, int H, int h,
@@ -441,12 +465,18 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
                 if (o_L > 0) flush_o(par ^ 1, o_t0, o_L);   // the previous chunk's rows
                 if (i > 0) checkpoint(c - 1);
             }
-            if (c + 1 < c_end) {
-                load_u(c + 1, un);
-                copyB(c + 1, bring + (par ^ 1) * BB);
+            // The next chunk's U and region B, and the region-A copies of chunk
+            // c + 2 issued a few at a time between this step's products.  They
+            // are issued on every step (chunk indices clamped, into ring slots
+            // that are free) so that the same number of memory operations is in
+            // flight on every path: the compiler can then wait for U by count
+            // instead of draining every copy.
+            {
+                const u32x2 *us = reinterpret_cast<const u32x2 *>(slab_of(min(c + 1, c_end - 1)) + SL::u);
+#pragma unroll
+                for (int I = 0; I < 4; ++I) un[I] = load_untracked(us + (I * KT + vt) * 64 + lane);
             }
-            // A copies of chunk c + 2, issued a few at a time between this
-            // step's products so that the memory pipeline works under the math
+            copyB(min(c + 1, c_end - 1), bring + (par ^ 1) * BB);
             const bool fetch_a = c + 2 < c_end;
             const unsigned char *a_src = slab_of(fetch_a ? c + 2 : c);
             unsigned char *a_dst = aring + ((i + 2) % 3) * AB;
@@ -466,10 +496,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             f32x4 vp[4], vp2[TR ? 4 : 1];
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
-                if (fetch_a) {
 #pragma unroll
-                    for (int r = 0; r < NA / 4; ++r) copyA_part(I * (NA / 4) + r);
-                }
+                for (int r = 0; r < NA / 4; ++r) copyA_part(I * (NA / 4) + r);
                 f32x4 ws = zero4(), qs = zero4(), ws2 = zero4();
 #pragma unroll
                 for (int p = 0; p < KT / 2; ++p) {
@@ -535,7 +563,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
                 __builtin_amdgcn_s_waitcnt((NA & 15) | (0x7 << 4) | (0xf << 8) | ((NA >> 4) << 14));
             else
                 wait_all_memory();
-            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int I = 0; I < 4; ++I) settle(un[I]);   // issued before every copy: landed
+            barrier_lds();
 #pragma unroll
             for (int I = 0; I < 4; ++I) u[I] = un[I];
         }
