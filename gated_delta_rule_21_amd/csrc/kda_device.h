@@ -200,25 +200,4 @@ __device__ __forceinline__ f32x4 mma3_bf16(u32x4 ah, u32x4 al, u32x4 bh, u32x4 b
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// Transpose of a 16x16 tile of packed bf16 values: the tile enters a
-// 16x16x16 bf16 MFMA as its A operand against the identity, so D = A.  Read
-// through the fragment convention, a tile whose lane (m, g) holds X[m][4g + j]
-// (row layout) comes out with lane (n, g) holding X[4g + j][n] (column
-// layout), and an accumulator tile (lane (n, g) holds X[4g + j][n]) comes out
-// with lane (n, g) holding X[n][4g + j].  Exact for finite values (each
-// product is a bf16 value times 1 or 0); a non-finite entry turns its whole
-// row non-finite (inf * 0).
-__device__ __forceinline__ u32x2 transpose_bf16_bits(u32x2 a, int lane) {
-    const int n = lane & 15, g = lane >> 4;
-    // identity B operand: lane (n, g) holds I[4g + j][n]
-    const uint32_t one = 0x3f80u;  // bf16 1.0
-    uint32_t e[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) e[j] = (4 * g + j == n) ? one : 0u;
-    const u32x2 b = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
-    const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                             __builtin_bit_cast(s16x4, b), zero4(), 0, 0, 0);
-    return u32x2{f32x2_to_bf16x2(d[0], d[1]), f32x2_to_bf16x2(d[2], d[3])};
-}
-
 }  // namespace kda

@@ -63,6 +63,22 @@ __device__ __forceinline__ u32x2 transpose_tile_f16(f32x4 x, int lane) {
     return quad_to_f16(d);
 }
 
+// Row-major 16x16 tiles of 16-bit values in LDS (512 bytes: 16 rows of 16
+// channels), written straight from the row layout.  ds_read_b64_tr_b16 with
+// lane l reading the tile's bytes [8 l, 8 l + 8) returns to lane (n, g) rows
+// 4g .. 4g+3 of column n: the tile's transpose in the MFMA operand layout.
+__device__ __forceinline__ u32x2 tile_tr(const unsigned char *tile, int lane) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                         (__attribute__((address_space(3))) s16x4 *)(tile + lane * 8)));
+}
+// K32 operand over row blocks 2f and 2f + 1 of channel tile t, tiles indexed
+// [t][row block] from `base`.
+__device__ __forceinline__ u32x4 tile_tr_k32(const unsigned char *base, int t, int f, int lane) {
+    const u32x2 a = tile_tr(base + (size_t)(t * 4 + 2 * f) * 512, lane);
+    const u32x2 c = tile_tr(base + (size_t)(t * 4 + 2 * f + 1) * 512, lane);
+    return u32x4{a[0], a[1], c[0], c[1]};
+}
+
 // A zero the compiler cannot see through.  Lane-dependent constants built
 // from `lane + opaque_zero()` inside the item loop are rebuilt per item
 // instead of being hoisted out of the loop and kept live (or spilled) across it.
@@ -78,11 +94,11 @@ struct Intra4Lds {
     static constexpr size_t FR = 1024;
     // X, phases 1-2: fp16 row fragments of kr and qr of row blocks 1..3,
     //   [block - 1][kr, qr][pair p], read by the off-diagonal Gram tiles.
-    // X, phases 3-5: (Gamma*K)^T fragments [t][row pair f][hi, lo], then V^T
-    //   fragments [t][f]; the 8 bytes of block 2f + s sit at slot s of a lane.
+    // X, phases 3-5: Gamma*K (bf16 hi, then lo) and V as row-major 16x16
+    //   tiles [channel tile t][row block], read back transposed (tile_tr).
     static constexpr size_t X = 0;
     static constexpr size_t XB = 12 * NP * FR;
-    static constexpr size_t GKT = X, VT = X + 4 * KT * FR;
+    static constexpr size_t GKT = X, GKL = X + KT * 2048, VT = X + 4 * KT * FR;
     // A_kk, then T: the diagonal blocks in place, T_IJ (I > J) at block (J, I).
     static constexpr int AP = 68;
     static constexpr size_t A = X + XB;
@@ -340,7 +356,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
         __syncthreads();
 
-        // ---- phase 3: transposed (Gamma*K) split and V fragments into X
+        // ---- phase 3: Gamma*K (split) and V into X as row-major tiles
         load_rows4_v<D>(R, q, k, v, z, null_row, ent, h, H, row, lg);
         {
             const float *pfx = fac_lds + (4 + b) * D;
@@ -352,11 +368,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
                 const f32x4 lf = gk - f32x4{bf16_lo_half(hi[0]), bf16_hi_half(hi[0]), bf16_lo_half(hi[1]),
                                             bf16_hi_half(hi[1])};
                 const u32x2 lo = u32x2{f32x2_to_bf16x2(lf[0], lf[1]), f32x2_to_bf16x2(lf[2], lf[3])};
-                unsigned char *dg = X + LY::GKT + ((size_t)((t * 2 + (b >> 1)) * 2) * FR) + lane * 16 + (b & 1) * 8;
-                *reinterpret_cast<u32x2 *>(dg) = transpose_bf16_bits(hi, lane);
-                *reinterpret_cast<u32x2 *>(dg + FR) = transpose_bf16_bits(lo, lane);
-                *reinterpret_cast<u32x2 *>(X + LY::VT + (size_t)(t * 2 + (b >> 1)) * FR + lane * 16 + (b & 1) * 8) =
-                    transpose_bf16_bits(R.v[t], lane);
+                const size_t tb = (size_t)(t * 4 + b) * 512 + ln * 32 + lg * 8;   // row ln, channels 4lg..
+                *reinterpret_cast<u32x2 *>(X + LY::GKT + tb) = hi;
+                *reinterpret_cast<u32x2 *>(X + LY::GKL + tb) = lo;
+                *reinterpret_cast<u32x2 *>(X + LY::VT + tb) = R.v[t];
             }
         }
         if (lane < 16) {
@@ -425,12 +440,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
                 const unsigned char *mb = msp + (size_t)aqk_frag(I, pj) * 2 * FR + lane * 16;
                 const u32x4 mh = *reinterpret_cast<const u32x4 *>(mb);
                 const u32x4 ml = *reinterpret_cast<const u32x4 *>(mb + FR);
-                const unsigned char *ga = X + LY::GKT + ((size_t)((2 * p * 2 + pj) * 2) * FR) + lane * 16;
-                const unsigned char *gb = X + LY::GKT + ((size_t)(((2 * p + 1) * 2 + pj) * 2) * FR) + lane * 16;
-                acc0 = mma3_bf16(*reinterpret_cast<const u32x4 *>(ga), *reinterpret_cast<const u32x4 *>(ga + FR), mh, ml,
-                                 acc0);
-                acc1 = mma3_bf16(*reinterpret_cast<const u32x4 *>(gb), *reinterpret_cast<const u32x4 *>(gb + FR), mh, ml,
-                                 acc1);
+                acc0 = mma3_bf16(tile_tr_k32(X + LY::GKT, 2 * p, pj, lane), tile_tr_k32(X + LY::GKL, 2 * p, pj, lane),
+                                 mh, ml, acc0);
+                acc1 = mma3_bf16(tile_tr_k32(X + LY::GKT, 2 * p + 1, pj, lane),
+                                 tile_tr_k32(X + LY::GKL, 2 * p + 1, pj, lane), mh, ml, acc1);
             }
             store_f16(slab + SL::negW + ((size_t)(I * NP + p) * 64 + lane) * 16, -acc0, -acc1);
         });
@@ -447,8 +460,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
                 if ((4 * KT) % 4 == 0 || unit < 4 * KT) {
                     for (int pj = 0; pj <= (I >> 1); ++pj) {
                         const unsigned char *mb = msp + (size_t)aqk_frag(I, pj) * 2 * FR + lane * 16;
-                        const u32x4 vb =
-                            *reinterpret_cast<const u32x4 *>(X + LY::VT + (size_t)(w * 2 + pj) * FR + lane * 16);
+                        const u32x4 vb = tile_tr_k32(X + LY::VT, w, pj, lane);
                         acc = mma_bf16_k32(*reinterpret_cast<const u32x4 *>(mb), vb, acc);
                         acc = mma_bf16_k32(*reinterpret_cast<const u32x4 *>(mb + FR), vb, acc);
                     }
