@@ -8,6 +8,7 @@ Contents
   build()            compile kda_oracle.c (plain C, fp64, OpenMP)
   prefill(...)       token-loop recurrence over packed sequences (C)
   decode(...)        one decode step (C)
+  backward(...)      reverse-mode gradients of the prefill (C)
   gate(A, z)         the bounded log-decay, numpy fp64
   chunkwise.prefill  the chunkwise-parallel form, numpy fp64 (a cross-check)
   features           the q/k/v feature path (ShortConv -> Swish -> L2Norm) and
@@ -66,6 +67,9 @@ def load(path: str = _LIB):
     lib.kda_oracle_decode.argtypes = [ci, vp, vp, vp, fp, fp, fp, fp, ci, ci, ci, ci,
                                       dp, dp, ci]
     lib.kda_oracle_decode.restype = ci
+    lib.kda_oracle_backward.argtypes = [ci, vp, vp, vp, fp, fp, fp, fp, vp, ci, ci, ci, ci, dp, dp,
+                                        dp, dp, dp, dp, dp, dp, dp, ci]
+    lib.kda_oracle_backward.restype = ci
     lib.kda_oracle_gate.argtypes = [ctypes.c_double, ctypes.c_double]
     lib.kda_oracle_gate.restype = ctypes.c_double
     lib.kda_oracle_max_threads.restype = ci
@@ -141,6 +145,38 @@ def decode(q, k, v, z, A, beta, S, nthreads: int = 0, lib_path: str = _LIB):
     if rc != 0:
         raise RuntimeError("kda_oracle_decode failed (%d)" % rc)
     return o, S_out
+
+
+def backward(q, k, v, z, A, beta, h0, cu_seqlens, dO, dhT=None, nthreads: int = 0,
+             lib_path: str = _LIB) -> dict:
+    """Gradients of L = sum(dO * o) + sum(dhT * hT) through the prefill
+    (token recurrence, reverse mode; see kda_oracle.c).  Inputs as for
+    prefill(); dO [T, H, dv] and dhT [N, H, dv, dk] (or None) are widened to
+    float64.  Returns float64 arrays dq, dk, dv, dz, dbeta, dA, dh0 (dh0 is
+    the gradient of h0, whether h0 was given or zero)."""
+    q, k, v = _c(q), _c(k), _c(v)
+    io = _io_code(q)
+    assert _io_code(k) == io and _io_code(v) == io
+    z, A, beta = _c(z, np.float32), _c(A, np.float32), _c(beta, np.float32)
+    h0 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64)
+    cu = _c(np.asarray(cu_seqlens, dtype=np.int32), np.int32)
+    dO = np.ascontiguousarray(dO, dtype=np.float64)
+    dhT = None if dhT is None else np.ascontiguousarray(dhT, dtype=np.float64)
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    N = cu.shape[0] - 1
+    assert dO.shape == (T, H, dv) and int(cu[-1]) == T
+    out = dict(dq=np.zeros((T, H, dk)), dk=np.zeros((T, H, dk)), dv=np.zeros((T, H, dv)),
+               dz=np.zeros((T, H, dk)), dbeta=np.zeros((T, H)), dA=np.zeros(H),
+               dh0=np.zeros((N, H, dv, dk)))
+    rc = load(lib_path).kda_oracle_backward(io, _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A),
+                                            _ptr(beta), _ptr(h0), _ptr(cu), N, H, dk, dv,
+                                            _ptr(dO), _ptr(dhT), _ptr(out["dq"]), _ptr(out["dk"]),
+                                            _ptr(out["dv"]), _ptr(out["dz"]), _ptr(out["dbeta"]),
+                                            _ptr(out["dA"]), _ptr(out["dh0"]), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_backward failed (%d)" % rc)
+    return out
 
 
 def gate(A, z):
