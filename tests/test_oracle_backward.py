@@ -140,6 +140,19 @@ def test_backward_pin(pin):
     pin(run_oracle)
 
 
+def test_chunkwise_backward_matches_token_sweep():
+    """The chunk-form gradients (a second algorithm: matrix derivatives of
+    the chunk formulas) equal the token sweep for several chunk sizes."""
+    from oracle import chunkwise
+    d = inputs(11, [5, 0, 70, 130], 2, 6)
+    ref = run_oracle(d)
+    for C in (1, 3, 16, 64):
+        got = chunkwise.backward(d["q"], d["k"], d["v"], d["z"], d["A"], d["beta"], d["h0"], d["cu"], d["dO"],
+                                 d["dhT"], chunk=C)
+        for name in ref:
+            np.testing.assert_allclose(got[name], ref[name], rtol=1e-10, atol=1e-12, err_msg="%s C=%d" % (name, C))
+
+
 def test_backward_bf16_inputs_match_autograd():
     d = inputs(5, [20, 3], 2, 8)
     bits = {}
