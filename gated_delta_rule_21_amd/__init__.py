@@ -12,7 +12,8 @@ Entry points (same names as the C ABI in include/kda.h):
   kda_prefill_checkpoints(...)      raw C call: prefill + state checkpoints
   kda_qkv_shortconv(...)            raw C call: ShortConv -> Swish -> L2Norm feature path
   kda_output_gate(...)              raw C call: Sigmoid(g) * RMSNorm(o)
-  kda_prefill_workspace_size(...)
+  kda_prefill_backward(...)         raw C call: gradients of the prefill
+  kda_prefill_workspace_size(...), kda_prefill_backward_workspace_size(...)
   kda_set_prefill_segments(P), kda_prefill_segments(...)
                                     segment split of long sequences
   kda_status_string(status)
@@ -23,6 +24,8 @@ Convenience wrappers over torch tensors:
   prefill_checkpoints(..., interval) -> (o, hT, checkpoints, offsets)
   qkv_shortconv(xq, xk, xv, wq, wk, wv, cu_seqlens, ...) -> (q, k, v)
   output_gate(o, g, w, eps) -> y
+  prefill_backward(q, k, v, z, A, beta, cu_seqlens, grad_o, h0=None, grad_hT=None)
+      -> dict(dq, dk, dv, dz, dbeta, dA, dh0)
 """
 from __future__ import annotations
 
@@ -73,6 +76,11 @@ def lib():
     L.kda_decode_window.argtypes = [ci, vp, vp, vp, vp, vp, ci, vp, vp, vp, vp, vp, ci, vp, vp, ci, ci,
                                     ci, ci, vp, ci, vp]
     L.kda_decode_window.restype = ci
+    L.kda_prefill_backward.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, vp, vp,
+                                       vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.kda_prefill_backward.restype = ci
+    L.kda_prefill_backward_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
+    L.kda_prefill_backward_workspace_size.restype = sz
     L.kda_set_prefill_segments.argtypes = [ci]
     L.kda_set_prefill_segments.restype = ci
     L.kda_prefill_segments.argtypes = [ci, ci, ci, ci, ci, ci]
@@ -119,6 +127,18 @@ def kda_decode_window(io_dtype, rk, rv, rz, rbeta, n_accept, Lr, q, k, v, z, bet
                       N, H, dk, dv, o, commit_window, stream) -> int:
     return lib().kda_decode_window(io_dtype, rk, rv, rz, rbeta, n_accept, Lr, q, k, v, z, beta, L,
                                    A, S_inout, N, H, dk, dv, o, commit_window, stream)
+
+
+def kda_prefill_backward(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv, grad_o,
+                         grad_hT, grad_q, grad_k, grad_v, grad_z, grad_beta, grad_A, grad_h0, workspace,
+                         workspace_bytes, stream) -> int:
+    return lib().kda_prefill_backward(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv,
+                                      grad_o, grad_hT, grad_q, grad_k, grad_v, grad_z, grad_beta, grad_A,
+                                      grad_h0, workspace, workspace_bytes, stream)
+
+
+def kda_prefill_backward_workspace_size(N, T, H, dk, dv, io_dtype) -> int:
+    return int(lib().kda_prefill_backward_workspace_size(N, T, H, dk, dv, io_dtype))
 
 
 def kda_prefill_workspace_size(N, T, H, dk, dv, io_dtype) -> int:
@@ -351,3 +371,41 @@ def output_gate(o, g, w, eps: float, y=None):
     if st != 0:
         raise KdaError("kda_output_gate", st)
     return y
+
+
+def prefill_backward(q, k, v, z, A, beta, cu_seqlens, grad_o, h0=None, grad_hT=None, workspace=None,
+                     grads=None):
+    """Gradients of L = sum(grad_o * o) + sum(grad_hT * hT) for the prefill
+    o, hT = prefill(q, k, v, z, A, beta, cu_seqlens, h0).  Returns a dict of
+    fp32 tensors dq, dk, dv, dz [T, H, d], dbeta [T, H], dA [H] and
+    dh0 [N, H, dv, dk].  `grads` may hold preallocated outputs by those names."""
+    torch = _torch()
+    _check_gpu(q=q, k=k, v=v, z=z, A=A, beta=beta, cu_seqlens=cu_seqlens, grad_o=grad_o, h0=h0,
+               grad_hT=grad_hT, workspace=workspace)
+    io = _io_code(q)
+    if grad_o.dtype != q.dtype:
+        raise TypeError("grad_o must have the dtype of q (%s)" % q.dtype)
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    dev = q.device
+    g = dict(grads or {})
+    f32 = dict(dtype=torch.float32, device=dev)
+    for name, shape in (("dq", (T, H, dk)), ("dk", (T, H, dk)), ("dv", (T, H, dv)), ("dz", (T, H, dk)),
+                        ("dbeta", (T, H)), ("dA", (H,)), ("dh0", (N, H, dv, dk))):
+        if g.get(name) is None:
+            g[name] = torch.empty(shape, **f32)
+    _check_gpu(**g)
+    if workspace is None:
+        n = kda_prefill_backward_workspace_size(N, T, H, dk, dv, io)
+        if n == 0:
+            raise ValueError("unsupported backward sizes N=%d T=%d H=%d d=%d" % (N, T, H, dk))
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    st = kda_prefill_backward(io, _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A), _ptr(beta), _ptr(h0),
+                              _ptr(cu_seqlens), N, T, H, dk, dv, _ptr(grad_o), _ptr(grad_hT),
+                              _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dz"]), _ptr(g["dbeta"]),
+                              _ptr(g["dA"]), _ptr(g["dh0"]), _ptr(workspace), workspace.numel(),
+                              _stream(dev))
+    if st != 0:
+        raise KdaError("kda_prefill_backward", st)
+    return g

@@ -175,6 +175,69 @@ int kda_prefill_checkpoints(kda_dtype io_dtype, const void *q, const void *k, co
                         checkpoints, checkpoint_offsets, workspace, workspace_bytes, stream);
 }
 
+size_t kda_prefill_backward_workspace_size(int N, int T, int H, int dk, int dv, kda_dtype io_dtype) {
+    if (io_dtype != KDA_BF16 && io_dtype != KDA_F32) return 0;
+    if (!supported_dim(dk, dv) || N < 0 || T < 0 || H <= 0) return 0;
+    kda::BackwardPlan p;
+    if (!kda::plan_backward(N, T, H, dk, io_dtype == KDA_F32, kda::choose_segments(N, T, H, dk), &p)) return 0;
+    return p.total;
+}
+
+int kda_prefill_backward(kda_dtype io_dtype, const void *q, const void *k, const void *v, const float *z,
+                         const float *A, const float *beta, const float *h0, const int32_t *cu_seqlens,
+                         int N, int T, int H, int dk, int dv, const void *grad_o, const float *grad_hT,
+                         float *grad_q, float *grad_k, float *grad_v, float *grad_z, float *grad_beta,
+                         float *grad_A, float *grad_h0, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+    if (io_dtype != KDA_BF16 && io_dtype != KDA_F32) return KDA_ERR_UNSUPPORTED_DTYPE;
+    if (N < 0 || T < 0 || H <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (!supported_dim(dk, dv)) return KDA_ERR_UNSUPPORTED_DIM;
+    if (!A || !cu_seqlens || !workspace || !grad_A) return KDA_ERR_NULL_POINTER;
+    if (T > 0 && (!q || !k || !v || !z || !beta || !grad_o || !grad_q || !grad_k || !grad_v || !grad_z ||
+                  !grad_beta))
+        return KDA_ERR_NULL_POINTER;
+    const void *ptrs[] = {q, k, v, z, A, beta, h0, cu_seqlens, grad_o, grad_hT, grad_q, grad_k,
+                          grad_v, grad_z, grad_beta, grad_A, grad_h0};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_MISALIGNED;
+
+    kda::BackwardPlan plan;
+    if (!kda::plan_backward(N, T, H, dk, io_dtype == KDA_F32, kda::choose_segments(N, T, H, dk), &plan))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < plan.total) return KDA_ERR_WORKSPACE_TOO_SMALL;
+
+    // every output overlaps no input, no workspace and no other output
+    const size_t tok = (size_t)T * H, io = io_size(io_dtype);
+    const size_t st_bytes = (size_t)N * H * dv * dk * 4;
+    const struct { const void *p; size_t n; } ins[] = {
+        {q, tok * dk * io}, {k, tok * dk * io}, {v, tok * dv * io}, {z, tok * dk * 4},
+        {A, (size_t)H * 4}, {beta, tok * 4}, {cu_seqlens, (size_t)(N + 1) * 4}, {h0, st_bytes},
+        {grad_o, tok * dv * io}, {grad_hT, st_bytes}, {workspace, plan.total}};
+    const struct { const void *p; size_t n; } outs[] = {
+        {grad_q, tok * dk * 4}, {grad_k, tok * dk * 4}, {grad_v, tok * dv * 4}, {grad_z, tok * dk * 4},
+        {grad_beta, tok * 4}, {grad_A, (size_t)H * 4}, {grad_h0, st_bytes}};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (const auto &in : ins)
+            if (overlaps(outs[i].p, outs[i].n, in.p, in.n)) return KDA_ERR_ALIAS;
+        for (size_t j = 0; j < i; ++j)
+            if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return KDA_ERR_ALIAS;
+    }
+
+    kda::BackwardArgs a;
+    a.f32io = io_dtype == KDA_F32;
+    a.q = q; a.k = k; a.v = v; a.z = z; a.A = A; a.beta = beta; a.h0 = h0;
+    a.cu = cu_seqlens;
+    a.N = N; a.T = T; a.H = H; a.d = dk;
+    a.dO = grad_o; a.dhT = grad_hT;
+    a.gq = grad_q; a.gk = grad_k; a.gv = grad_v; a.gz = grad_z; a.gbeta = grad_beta; a.gA = grad_A;
+    a.gh0 = grad_h0;
+    a.ws = static_cast<unsigned char *>(workspace);
+    a.plan = plan;
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+    return kda::launch_prefill_backward(a) == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
 int kda_decode(kda_dtype io_dtype, const void *q, const void *k, const void *v, const float *z,
                const float *A, const float *beta, float *S_inout, int N, int H, int dk, int dv,
                void *o, void *stream) {

@@ -1,0 +1,959 @@
+// kda_backward.hip -- reverse-mode gradients of the chunkwise prefill for gfx950.
+//
+// The pages give the forward recurrence and its chunk form but no backward
+// pass; this one differentiates the chunk form of the s1mplewind "kimi-k3"
+// notes (section "Chunkwise 形式") as matrices.  Per chunk of C = 64 tokens,
+// with S the state at the chunk's start, dS' the gradient of the state at its
+// end, Gamma the inclusive cumulative decay inside the chunk, gamma_C its last
+// row, T = (I + StrictTril(Diag(beta)(Gamma*K)(K/Gamma)^T))^{-1},
+// M = T Diag(beta), W = M (Gamma*K), P = Tril((Gamma*Q)(K/Gamma)^T),
+// K~ = (gamma_C/Gamma)*K and V~ = V - (Gamma*K) S (so V' = M V~):
+//   dV' = P^T dO + K~ dS'
+//   dS  = (Gamma*Q)^T dO + Diag(gamma_C) dS' - W^T dV'      (to the previous chunk)
+//   dV  = M^T dV',  dM = dV' V~^T,  dbeta_j += sum_t dM_tj T_tj
+//   dA_kk = -StrictTril(T^T (dM Diag(beta)) T^T),  dbeta_r += sum_i dA_kk,ri R_ri
+//   dR = Diag(beta) dA_kk,  dP = Tril(dO V'^T)
+//   dQ = Gamma*(dO S^T) + [dP (K/Gamma)]*Gamma
+//   dK = -Gamma*(M^T dV' S^T) + [dR (K/Gamma)]*Gamma + [(dP^T (Gamma*Q) + dR^T (Gamma*K))]/Gamma
+//        + (gamma_C/Gamma)*(V' dS'^T)
+// and the gradient of the log-decay, which a reverse cumulative sum over the
+// chunk turns into the gradient of every token's gate.
+//
+// Pipeline (one call):
+//   1. the forward prefill again, saving the state at every chunk boundary
+//      (kda_prefill's checkpoint path with a 64-token interval);
+//   2. bwd_local_kernel, one workgroup per (chunk, head): R, P, T, W, K~,
+//      gamma_C and the chain's dS-free terms X = P^T dO, Y = (Gamma*Q)^T dO;
+//   3. bwd_chain_kernel, per (sequence, head, value columns): walks the
+//      chunks backwards carrying dS in fp32 MFMA accumulators, stores dS'
+//      and dV' of every chunk, and dh0;
+//   4. bwd_grad_kernel, one workgroup per (chunk, head): every input gradient;
+//   5. bwd_dA_kernel: the per-head sum of the chunks' A gradients, in a fixed
+//      order (the result does not depend on scheduling).
+//
+// Everything after the forward recompute runs in fp32 (fp32 16x16x4 MFMA).
+// Decay factors: a 64-token chunk can decay by e^-320, so no Gamma or 1/Gamma
+// over a chunk is formed where the quotient of two would be needed.  Log2
+// decays are kept relative to the start of each 16-token block (Gb) with the
+// block totals bt; a factor exp2(G_r - G_i), r >= i, is split at a reference
+// point so that both halves are <= 1 when r and i lie in different blocks
+// (the end of i's block or the start of r's), and at the block's middle row
+// when they share one, so neither half exceeds e^40 (eight steps of the
+// bounded gate; devpress K3 walk-through §3.2, Eq 5).  The middle reference
+// keeps gradients as large as 1e20 within fp32 range in those products.
+// ---------------------------------------------------------------------------
+#include "kda_chunk.h"
+#include "kda_device.h"
+#include "kda_internal.h"
+
+#include <algorithm>
+
+namespace kda {
+
+namespace {
+
+constexpr int kBwdWaves = 8, kBwdThreads = 64 * kBwdWaves;
+constexpr int kPS = 68;   // pitch of 64 x 64 fp32 matrices in LDS
+
+// Per-(chunk, head) fp32 record in the workspace; offsets in floats.
+template <int D>
+struct BwdItem {
+    static constexpr size_t kt = 0;              // K~ = (gamma_C/Gamma)*K        [64][D]
+    static constexpr size_t wt = kt + 64 * D;    // W^T                           [D][64]
+    static constexpr size_t xv = wt + 64 * D;    // X^T, then dV'^T               [D][64]
+    static constexpr size_t ys = xv + 64 * D;    // Y^T, then dS' (state layout)  [D][D]
+    static constexpr size_t gam = ys + D * D;    // gamma_C                       [D]
+    static constexpr size_t r = gam + D;         // R, strictly lower             [64][64]
+    static constexpr size_t t = r + 64 * 64;     // T                             [64][64]
+    static constexpr size_t floats = (t + 64 * 64 + 63) / 64 * 64;
+};
+
+__device__ __forceinline__ f32x4 rd4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ void wr4(float *p, f32x4 x) { *reinterpret_cast<f32x4 *>(p) = x; }
+// p[0], p[ld], p[2 ld], p[3 ld]: four rows of one column
+__device__ __forceinline__ f32x4 rdcol4(const float *p, int ld) {
+    return f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
+}
+__device__ __forceinline__ f32x4 exp2x4(f32x4 x) {
+    return f32x4{fast_exp2(x[0]), fast_exp2(x[1]), fast_exp2(x[2]), fast_exp2(x[3])};
+}
+__device__ __forceinline__ f32x4 splat4(float x) { return f32x4{x, x, x, x}; }
+
+// sum_{m = lo}^{hi - 1} bt[m][c] (zero when lo >= hi); bt is [4][D].
+template <int D>
+__device__ __forceinline__ f32x4 span4(const float *bt, int lo, int hi, int c) {
+    f32x4 s = zero4();
+    for (int m = lo; m < hi; ++m) s += rd4(bt + m * D + c);
+    return s;
+}
+template <int D>
+__device__ __forceinline__ float span1(const float *bt, int lo, int hi, int c) {
+    float s = 0.f;
+    for (int m = lo; m < hi; ++m) s += bt[m * D + c];
+    return s;
+}
+
+// Rows [0, 64) of a chunk's [T][H][D] slice into LDS as fp32 (pitch D + 4);
+// rows >= L are zero.
+template <int D, bool F32IO>
+__device__ __forceinline__ void stage_rows(float *dst, const void *src, int t0, int L, int h, int H,
+                                           int tid) {
+    constexpr int PB = D + 4, Q = D / 4;
+    for (int i = tid; i < 64 * Q; i += kBwdThreads) {
+        const int r = i / Q, c = 4 * (i % Q);
+        f32x4 x = zero4();
+        if (r < L) x = load_io4<F32IO>(src, ((size_t)(t0 + r) * H + h) * D + c);
+        wr4(dst + r * PB + c, x);
+    }
+}
+
+// Gb[r][c]: log2-decay of rows 16 I .. r of r's block I (inclusive), and the
+// block totals bt[I][c].  Rows >= L add nothing (zero gate).
+template <int D>
+__device__ __forceinline__ void stage_decay(float *Gb, float *bt, const float *z, float ea, int t0, int L,
+                                            int h, int H, int tid) {
+    constexpr int PB = D + 4;
+    if (tid < 4 * D) {
+        const int c = tid % D, I = tid / D;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = 16 * I + i;
+            x[i] = r < L ? z[((size_t)(t0 + r) * H + h) * D + c] : 0.f;
+        }
+        float run = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = 16 * I + i;
+            run += r < L ? gate_log2(ea, x[i]) : 0.f;
+            Gb[r * PB + c] = run;
+        }
+        bt[I * D + c] = run;
+    }
+}
+
+// LDS carve-up of the two per-item kernels (floats).
+template <int D>
+struct LocalLds {
+    static constexpr int PB = D + 4;
+    static constexpr int q = 0, k = q + 64 * PB, gb = k + 64 * PB, r = gb + 64 * PB, p = r + 64 * kPS;
+    static constexpr int beta = p + 64 * kPS, bt = beta + 64, floats = bt + 4 * D;
+};
+template <int D>
+struct GradLds {
+    static constexpr int PB = D + 4;
+    static constexpr int k = 0, gb = k + 64 * PB, x = gb + 64 * PB, s0 = x + 64 * PB, s1 = s0 + 64 * kPS;
+    static constexpr int beta = s1 + 64 * kPS, bt = beta + 64, db = bt + 4 * D, pd = db + 64, dgc = pd + 64;
+    static constexpr int red = dgc + D, part = red + 8 * D, floats = part + kBwdWaves;
+    static_assert(64 * PB <= 2 * 64 * kPS, "the gradient of the log-decay fits the two small matrices");
+};
+
+// ---------------------------------------------------------------------------
+// Stage 2: per (chunk, head), the terms of the chain that do not depend on dS.
+// ---------------------------------------------------------------------------
+template <int D, bool F32IO>
+__global__ void __launch_bounds__(kBwdThreads) bwd_local_kernel(
+    const void *__restrict__ q, const void *__restrict__ k, const float *__restrict__ z,
+    const float *__restrict__ A, const float *__restrict__ beta, const void *__restrict__ dO,
+    const int32_t *__restrict__ meta, const int4 *__restrict__ table, int N, int H, int max_chunks,
+    float *__restrict__ items) {
+    using IT = BwdItem<D>;
+    using SL = LocalLds<D>;
+    constexpr int PB = D + 4, KT = D / 16;
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    float *Qs = lds + SL::q, *Ks = lds + SL::k, *Gb = lds + SL::gb, *Rs = lds + SL::r, *Ps = lds + SL::p;
+    float *bet = lds + SL::beta, *bt = lds + SL::bt;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    const int chunk = blockIdx.x / H, h = blockIdx.x % H;
+    if (chunk >= meta[N]) return;
+    const int4 ent = table[chunk];
+    const int t0 = ent.y, L = ent.z;
+    float *item = items + ((size_t)h * max_chunks + chunk) * IT::floats;
+
+    stage_rows<D, F32IO>(Qs, q, t0, L, h, H, tid);
+    stage_rows<D, F32IO>(Ks, k, t0, L, h, H, tid);
+    stage_decay<D>(Gb, bt, z, __expf(A[h]), t0, L, h, H, tid);
+    if (tid < 64) bet[tid] = tid < L ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
+    __syncthreads();
+
+    // Decayed Gram tiles (I, J), J <= I: R = (K.K) and P = (Q.K) with the
+    // per-channel factor exp2(G_r - G_i); R strictly lower, P lower.
+    for (int u = wave; u < 32; u += kBwdWaves) {
+        const bool isP = u >= 16;
+        const int I = (u & 15) >> 2, J = u & 3;
+        float *dst = isP ? Ps : Rs;
+        f32x4 acc = zero4();
+        if (J <= I) {
+            const float *src = isP ? Qs : Ks;
+            const int r = 16 * I + ln, i = 16 * J + ln, mid = 16 * I + 7;
+#pragma unroll
+            for (int kk = 0; kk < KT; ++kk) {
+                const int c = 16 * kk + 4 * lg;
+                const f32x4 gr = rd4(Gb + r * PB + c), gi = rd4(Gb + i * PB + c);
+                f32x4 fa, fb;
+                if (I == J) {
+                    const f32x4 gm = rd4(Gb + mid * PB + c);
+                    fa = gr - gm;
+                    fb = gm - gi;
+                } else {
+                    fa = gr;
+                    fb = span4<D>(bt, J, I, c) - gi;
+                }
+                acc = mma_f32_k16(rd4(src + r * PB + c) * exp2x4(fa), rd4(Ks + i * PB + c) * exp2x4(fb), acc);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int rr = 16 * I + 4 * lg + j, ii = 16 * J + ln;
+            const bool keep = isP ? ii <= rr : ii < rr;
+            dst[rr * kPS + ii] = keep ? acc[j] : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // R to the record; Diag(beta) R in place, then T = (I + Diag(beta) R)^{-1}
+    for (int i = tid; i < 64 * 16; i += kBwdThreads) {
+        const int r = i >> 4, c = 4 * (i & 15);
+        const f32x4 x = rd4(Rs + r * kPS + c);
+        wr4(item + IT::r + r * 64 + c, x);
+        wr4(Rs + r * kPS + c, x * bet[r]);
+    }
+    __syncthreads();
+    // diagonal 16 x 16 blocks by forward substitution, one lane per column
+    if (wave < 4 && lane < 16) {
+        const int b = 16 * wave;
+        float col[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float x = (r == lane) ? 1.f : 0.f;
+#pragma unroll
+            for (int i = 0; i < r; ++i) x -= Rs[(b + r) * kPS + b + i] * col[i];
+            col[r] = x;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Rs[(b + r) * kPS + b + lane] = col[r];
+    }
+    __syncthreads();
+    // blocks below the diagonal: T_IJ = -T_II sum_{J <= m < I} A_Im T_mJ
+    for (int I = 1; I < 4; ++I) {
+        f32x4 y = zero4();
+        if (wave < I) {
+            const int J = wave;
+            f32x4 x = zero4();
+            for (int m = J; m < I; ++m)
+                x = mma_f32_k16(rd4(Rs + (16 * I + ln) * kPS + 16 * m + 4 * lg),
+                                rdcol4(Rs + (16 * m + 4 * lg) * kPS + 16 * J + ln, kPS), x);
+            y = mma_f32_k16(rd4(Rs + (16 * I + ln) * kPS + 16 * I + 4 * lg), x, zero4());
+        }
+        __syncthreads();
+        if (wave < I) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Rs[(16 * I + 4 * lg + j) * kPS + 16 * wave + ln] = -y[j];
+        }
+        __syncthreads();
+    }
+    for (int i = tid; i < 64 * 16; i += kBwdThreads) {
+        const int r = i >> 4, c = 4 * (i & 15);
+        wr4(item + IT::t + r * 64 + c, rd4(Rs + r * kPS + c));
+    }
+
+    // W = M (Gamma*K), stored transposed: tile (t block mt, channel block nt)
+    for (int u = wave; u < 4 * KT; u += kBwdWaves) {
+        const int mt = u / KT, nt = u % KT;
+        const int c = 16 * nt + ln;
+        f32x4 acc = zero4();
+        for (int kk = 0; kk <= mt; ++kk) {
+            const int s = 16 * kk + 4 * lg;
+            const f32x4 a = rd4(Rs + (16 * mt + ln) * kPS + s) * rd4(bet + s);
+            const f32x4 g = rdcol4(Gb + s * PB + c, PB) + splat4(span1<D>(bt, 0, kk, c));
+            acc = mma_f32_k16(a, rdcol4(Ks + s * PB + c, PB) * exp2x4(g), acc);
+        }
+        wr4(item + IT::wt + (size_t)c * 64 + 16 * mt + 4 * lg, acc);
+    }
+    // K~ = (gamma_C/Gamma)*K and gamma_C
+    for (int i = tid; i < 64 * (D / 4); i += kBwdThreads) {
+        const int r = i / (D / 4), c = 4 * (i % (D / 4));
+        const f32x4 e = span4<D>(bt, r >> 4, 4, c) - rd4(Gb + r * PB + c);
+        wr4(item + IT::kt + (size_t)r * D + c, rd4(Ks + r * PB + c) * exp2x4(e));
+    }
+    for (int c = tid; c < D; c += kBwdThreads) item[IT::gam + c] = fast_exp2(span1<D>(bt, 0, 4, c));
+    __syncthreads();
+
+    // dO replaces K
+    float *DOs = Ks;
+    stage_rows<D, F32IO>(DOs, dO, t0, L, h, H, tid);
+    __syncthreads();
+
+    // Y = (Gamma*Q)^T dO, stored transposed: tile (key block mt, value block nt)
+    for (int u = wave; u < KT * KT; u += kBwdWaves) {
+        const int mt = u / KT, nt = u % KT;
+        const int c = 16 * mt + ln;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int t = 16 * kk + 4 * lg;
+            const f32x4 g = rdcol4(Gb + t * PB + c, PB) + splat4(span1<D>(bt, 0, kk, c));
+            acc = mma_f32_k16(rdcol4(Qs + t * PB + c, PB) * exp2x4(g), rdcol4(DOs + t * PB + 16 * nt + ln, PB),
+                              acc);
+        }
+        wr4(item + IT::ys + (size_t)(16 * nt + ln) * D + 16 * mt + 4 * lg, acc);
+    }
+    // X = P^T dO, stored transposed: tile (row block mt, value block nt)
+    for (int u = wave; u < 4 * KT; u += kBwdWaves) {
+        const int mt = u / KT, nt = u % KT;
+        f32x4 acc = zero4();
+        for (int kk = mt; kk < 4; ++kk) {
+            const int t = 16 * kk + 4 * lg;
+            acc = mma_f32_k16(rdcol4(Ps + t * kPS + 16 * mt + ln, kPS), rdcol4(DOs + t * PB + 16 * nt + ln, PB),
+                              acc);
+        }
+        wr4(item + IT::xv + (size_t)(16 * nt + ln) * 64 + 16 * mt + 4 * lg, acc);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 3: the reverse chain.  Wave w of a workgroup owns 16 value columns;
+// its slice of dS (D x 16) lives in accumulators, so both products of a step
+// are wave-local:
+//   dV' = X + K~ dS'           (accumulator of K~ dS' = B operand of W^T dV')
+//   dS  = Y + gamma_C * dS' - W^T dV'
+// K~ and W^T of the next chunk go global -> registers during a step and
+// registers -> LDS after it (double buffer, one barrier per step).
+// ---------------------------------------------------------------------------
+template <int D>
+struct ChainShape {
+    static constexpr int KT = D / 16;
+    static constexpr int NW = KT < 4 ? KT : 4;     // waves per workgroup
+    static constexpr int NT = 64 * NW;
+    static constexpr int PB = D + 4;
+    static constexpr int buf = 64 * PB + D * kPS;  // floats per buffer: K~ then W^T
+    static constexpr int NS = 2 * 64 * D / 4 / NT; // float4 per thread per stage
+    static constexpr size_t lds_bytes = 2 * (size_t)buf * 4;
+};
+
+template <int D>
+__global__ void __launch_bounds__(ChainShape<D>::NT) bwd_chain_kernel(const int32_t *__restrict__ meta,
+                                                                       const float *__restrict__ dhT,
+                                                                       float *__restrict__ items, int N, int H,
+                                                                       int max_chunks, int groups,
+                                                                       float *__restrict__ dh0) {
+    using IT = BwdItem<D>;
+    using SH = ChainShape<D>;
+    constexpr int KT = SH::KT, PB = SH::PB, NS = SH::NS;
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    const int unit = blockIdx.x / groups, grp = blockIdx.x % groups;
+    const int n = unit / H, h = unit % H;
+    if (n >= N) return;
+    const int ct = grp * SH::NW + wave;  // value column tile of this wave
+    const int v = 16 * ct + ln;
+    const int c_begin = meta[n], c_end = meta[n + 1];
+    auto rec = [&](int c) { return items + ((size_t)h * max_chunks + c) * IT::floats; };
+
+    const size_t sb = ((size_t)n * H + h) * D * D + (size_t)v * D + 4 * lg;
+    f32x4 dS[KT];
+#pragma unroll
+    for (int rc = 0; rc < KT; ++rc) dS[rc] = dhT ? rd4(dhT + sb + 16 * rc) : zero4();
+
+    f32x4 st[NS];
+    auto load_stage = [&](const float *src) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) st[s] = rd4(src + 4 * (tid + s * SH::NT));
+    };
+    auto store_stage = [&](float *dst) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int i = tid + s * SH::NT;  // float4 index into [K~ | W^T]
+            if (i < 16 * D) {
+                const int r = i / (D / 4), c = 4 * (i % (D / 4));
+                wr4(dst + r * PB + c, st[s]);
+            } else {
+                const int j = i - 16 * D, r = j >> 4, c = 4 * (j & 15);
+                wr4(dst + 64 * PB + r * kPS + c, st[s]);
+            }
+        }
+    };
+    f32x4 X[4], Y[KT], G[KT];
+    auto fetch = [&](const float *it) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) X[rt] = rd4(it + IT::xv + (size_t)v * 64 + 16 * rt + 4 * lg);
+#pragma unroll
+        for (int rc = 0; rc < KT; ++rc) {
+            Y[rc] = rd4(it + IT::ys + (size_t)v * D + 16 * rc + 4 * lg);
+            G[rc] = rd4(it + IT::gam + 16 * rc + 4 * lg);
+        }
+    };
+
+    if (c_end > c_begin) {
+        load_stage(rec(c_end - 1) + IT::kt);
+        store_stage(lds);
+        fetch(rec(c_end - 1));
+        __syncthreads();
+        int b = 0;
+        for (int c = c_end - 1; c >= c_begin; --c, b ^= 1) {
+            const bool more = c > c_begin;
+            const float *Kt = lds + b * SH::buf, *Wt = Kt + 64 * PB;
+            f32x4 Xc[4], Yc[KT], Gc[KT];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) Xc[rt] = X[rt];
+#pragma unroll
+            for (int rc = 0; rc < KT; ++rc) {
+                Yc[rc] = Y[rc];
+                Gc[rc] = G[rc];
+            }
+            if (more) {
+                load_stage(rec(c - 1) + IT::kt);
+                fetch(rec(c - 1));
+            }
+            f32x4 dv[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 acc = Xc[rt];
+#pragma unroll
+                for (int kk = 0; kk < KT; ++kk)
+                    acc = mma_f32_k16(rd4(Kt + (16 * rt + ln) * PB + 16 * kk + 4 * lg), dS[kk], acc);
+                dv[rt] = acc;
+            }
+            f32x4 nd[KT];
+#pragma unroll
+            for (int rc = 0; rc < KT; ++rc) {
+                f32x4 acc = Yc[rc] + Gc[rc] * dS[rc];
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+                    acc = mma_f32_k16(rd4(Wt + (16 * rc + ln) * kPS + 16 * kt + 4 * lg), -dv[kt], acc);
+                nd[rc] = acc;
+            }
+            float *it = rec(c);
+#pragma unroll
+            for (int rc = 0; rc < KT; ++rc) wr4(it + IT::ys + (size_t)v * D + 16 * rc + 4 * lg, dS[rc]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) wr4(it + IT::xv + (size_t)v * 64 + 16 * rt + 4 * lg, dv[rt]);
+#pragma unroll
+            for (int rc = 0; rc < KT; ++rc) dS[rc] = nd[rc];
+            if (more) store_stage(lds + (b ^ 1) * SH::buf);
+            __syncthreads();
+        }
+    }
+    if (dh0) {
+#pragma unroll
+        for (int rc = 0; rc < KT; ++rc) wr4(dh0 + sb + 16 * rc, dS[rc]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 4: per (chunk, head), every input gradient.
+// ---------------------------------------------------------------------------
+template <int D, bool F32IO>
+__global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
+    const void *__restrict__ q, const void *__restrict__ k, const void *__restrict__ vin,
+    const float *__restrict__ z, const float *__restrict__ A, const float *__restrict__ beta,
+    const float *__restrict__ h0, const void *__restrict__ dO, const int32_t *__restrict__ meta,
+    const int4 *__restrict__ table, const int32_t *__restrict__ ck_off, const float *__restrict__ ck, int ck_cap,
+    int N, int H, int max_chunks, const float *__restrict__ items, float *__restrict__ gq,
+    float *__restrict__ gk, float *gv, float *__restrict__ gz, float *__restrict__ gbeta,
+    float *__restrict__ dA_part) {
+    using IT = BwdItem<D>;
+    using SL = GradLds<D>;
+    constexpr int PB = D + 4, KT = D / 16;
+    constexpr int NU = (4 * KT + kBwdWaves - 1) / kBwdWaves;  // [t][c] tiles per wave
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    float *Ks = lds + SL::k, *Gb = lds + SL::gb, *Xs = lds + SL::x, *S0 = lds + SL::s0, *S1 = lds + SL::s1;
+    float *bet = lds + SL::beta, *bt = lds + SL::bt, *db = lds + SL::db, *pd = lds + SL::pd, *dgc = lds + SL::dgc;
+    float *red = lds + SL::red, *part = lds + SL::part;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    const int chunk = blockIdx.x / H, h = blockIdx.x % H;
+    if (chunk >= meta[N]) return;
+    const int4 ent = table[chunk];
+    const int n = ent.x, t0 = ent.y, L = ent.z;
+    const float *item = items + ((size_t)h * max_chunks + chunk) * IT::floats;
+    const float *dvp = item + IT::xv;   // dV'^T [v][t]
+    const float *dsp = item + IT::ys;   // dS' [v][c]
+    const float ea = __expf(A[h]);
+    // state at the chunk's start, [v][c]; NULL = zero
+    const float *Sg = nullptr;
+    {
+        const int j = chunk - meta[n];
+        if (j == 0) {
+            if (h0) Sg = h0 + ((size_t)n * H + h) * D * D;
+        } else if (ck) {
+            const int idx = ck_off[n] + j - 1;
+            if (idx >= 0 && idx < ck_cap) Sg = ck + ((size_t)idx * H + h) * D * D;
+        }
+    }
+    auto row_io = [&](const void *p, int r, int c) -> f32x4 {
+        return r < L ? load_io4<F32IO>(p, ((size_t)(t0 + r) * H + h) * D + c) : zero4();
+    };
+
+    // ---- K, the block log-decays, V, beta
+    stage_rows<D, F32IO>(Ks, k, t0, L, h, H, tid);
+    stage_rows<D, F32IO>(Xs, vin, t0, L, h, H, tid);
+    stage_decay<D>(Gb, bt, z, ea, t0, L, h, H, tid);
+    if (tid < 64) {
+        bet[tid] = tid < L ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
+        db[tid] = 0.f;
+    }
+    __syncthreads();
+
+    // ---- V~ = V - (Gamma*K) S, in place
+    for (int u = wave; u < 4 * KT; u += kBwdWaves) {
+        const int mt = u / KT, nt = u % KT;
+        f32x4 acc = zero4();
+        if (Sg) {
+            const int r = 16 * mt + ln;
+#pragma unroll
+            for (int kk = 0; kk < KT; ++kk) {
+                const int c = 16 * kk + 4 * lg;
+                const f32x4 a = rd4(Ks + r * PB + c) * exp2x4(rd4(Gb + r * PB + c) + span4<D>(bt, 0, mt, c));
+                acc = mma_f32_k16(a, rd4(Sg + (size_t)(16 * nt + ln) * D + c), acc);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Xs[(16 * mt + 4 * lg + j) * PB + 16 * nt + ln] -= acc[j];
+    }
+    for (int i = tid; i < 64 * 16; i += kBwdThreads) {
+        const int r = i >> 4, c = 4 * (i & 15);
+        wr4(S0 + r * kPS + c, rd4(item + IT::t + r * 64 + c));
+    }
+    __syncthreads();
+
+    // ---- dM = dV' V~^T -> S1;  V' = M V~ (registers, then over V~);
+    //      dV = M^T dV' -> gv
+    for (int u = wave; u < 16; u += kBwdWaves) {
+        const int mt = u >> 2, nt = u & 3;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kk = 0; kk < KT; ++kk) {
+            const int c = 16 * kk + 4 * lg;
+            acc = mma_f32_k16(rdcol4(dvp + (size_t)c * 64 + 16 * mt + ln, 64), rd4(Xs + (16 * nt + ln) * PB + c),
+                              acc);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S1[(16 * mt + 4 * lg + j) * kPS + 16 * nt + ln] = acc[j];
+    }
+    f32x4 vp[NU];
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+        const int u = wave + i * kBwdWaves;
+        vp[i] = zero4();
+        if (u < 4 * KT) {
+            const int mt = u / KT, nt = u % KT;
+            for (int kk = 0; kk <= mt; ++kk) {
+                const int s = 16 * kk + 4 * lg;
+                vp[i] = mma_f32_k16(rd4(S0 + (16 * mt + ln) * kPS + s) * rd4(bet + s),
+                                    rdcol4(Xs + s * PB + 16 * nt + ln, PB), vp[i]);
+            }
+        }
+    }
+    for (int u = wave; u < 4 * KT; u += kBwdWaves) {
+        const int mt = u / KT, nt = u % KT;
+        const int v = 16 * nt + ln;
+        f32x4 acc = zero4();
+        for (int kk = mt; kk < 4; ++kk) {
+            const int t = 16 * kk + 4 * lg;
+            acc = mma_f32_k16(rdcol4(S0 + t * kPS + 16 * mt + ln, kPS) * bet[16 * mt + ln],
+                              rd4(dvp + (size_t)v * 64 + t), acc);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * mt + 4 * lg + j;
+            if (r < L) gv[((size_t)(t0 + r) * H + h) * D + v] = acc[j];
+        }
+    }
+    __threadfence_block();
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+        const int u = wave + i * kBwdWaves;
+        if (u < 4 * KT) {
+            const int mt = u / KT, nt = u % KT;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Xs[(16 * mt + 4 * lg + j) * PB + 16 * nt + ln] = vp[i][j];
+        }
+    }
+
+    // ---- dbeta_j = sum_t dM_tj T_tj;  E = (dM Diag(beta)) T^T (registers)
+    if (tid < 64) {
+        float s = 0.f;
+        for (int t = tid; t < 64; ++t) s += S1[t * kPS + tid] * S0[t * kPS + tid];
+        db[tid] = s;
+    }
+    f32x4 e[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = wave + i * kBwdWaves, mt = u >> 2, nt = u & 3;
+        e[i] = zero4();
+        for (int kk = 0; kk <= nt; ++kk) {
+            const int s = 16 * kk + 4 * lg;
+            e[i] = mma_f32_k16(rd4(S1 + (16 * mt + ln) * kPS + s) * rd4(bet + s), rd4(S0 + (16 * nt + ln) * kPS + s),
+                               e[i]);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = wave + i * kBwdWaves, mt = u >> 2, nt = u & 3;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S1[(16 * mt + 4 * lg + j) * kPS + 16 * nt + ln] = e[i][j];
+    }
+    __syncthreads();
+    // ---- dA_kk = -StrictTril(T^T E) (registers, then over T)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = wave + i * kBwdWaves, mt = u >> 2, nt = u & 3;
+        e[i] = zero4();
+        if (nt <= mt) {
+            for (int kk = mt; kk < 4; ++kk) {
+                const int t = 16 * kk + 4 * lg;
+                e[i] = mma_f32_k16(rdcol4(S0 + t * kPS + 16 * mt + ln, kPS), rdcol4(S1 + t * kPS + 16 * nt + ln, kPS),
+                                   e[i]);
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = wave + i * kBwdWaves, mt = u >> 2, nt = u & 3;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * mt + 4 * lg + j, w = 16 * nt + ln;
+            S0[r * kPS + w] = w < r ? -e[i][j] : 0.f;
+        }
+    }
+    __syncthreads();
+    // ---- dbeta_r += sum_i dA_kk,ri R_ri;  write dbeta
+    if (tid < 64) {
+        float s = db[tid];
+        const float *Rg = item + IT::r + tid * 64;
+        for (int w = 0; w < tid; ++w) s += S0[tid * kPS + w] * Rg[w];
+        if (tid < L) gbeta[(size_t)(t0 + tid) * H + h] = s;
+    }
+
+    // ---- dP = Tril(dO V'^T): the strictly lower part -> S1 (E is dead), the
+    //      diagonal -> pd.  A diagonal term dP_rr q_r k_r enters the log-decay
+    //      gradient of row r twice with opposite signs (its decay factor is 1),
+    //      so it is kept out of the decay-masked sums and added to dq and dk
+    //      on its own;  the [t][c] products that
+    //      read S, dS' or dV: dQ_S = Gamma*(dO S^T), dKg = -Gamma*(dV S^T),
+    //      dKt = (gamma_C/Gamma)*(V' dS'^T)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = wave + i * kBwdWaves, mt = u >> 2, nt = u & 3;
+        f32x4 acc = zero4();
+        if (nt <= mt) {
+#pragma unroll
+            for (int kk = 0; kk < KT; ++kk) {
+                const int c = 16 * kk + 4 * lg;
+                acc = mma_f32_k16(row_io(dO, 16 * mt + ln, c), rd4(Xs + (16 * nt + ln) * PB + c), acc);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * mt + 4 * lg + j, s = 16 * nt + ln;
+            S1[r * kPS + s] = s < r ? acc[j] : 0.f;
+            if (s == r) pd[r] = acc[j];
+        }
+    }
+    f32x4 dq[NU], dkg[NU], dkt[NU], dki[NU];
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+        const int u = wave + i * kBwdWaves;
+        dq[i] = dkg[i] = dkt[i] = dki[i] = zero4();
+        if (u < 4 * KT) {
+            const int rb = u / KT, ct = u % KT;
+            const int r = 16 * rb + ln, c = 16 * ct + ln;
+            const bool rok = r < L;
+#pragma unroll
+            for (int kk = 0; kk < KT; ++kk) {
+                const int vv = 16 * kk + 4 * lg;
+                if (Sg) {
+                    const f32x4 sb = rdcol4(Sg + (size_t)vv * D + c, D);
+                    dq[i] = mma_f32_k16(row_io(dO, r, vv), sb, dq[i]);
+                    const f32x4 zr = rok ? rd4(gv + ((size_t)(t0 + r) * H + h) * D + vv) : zero4();
+                    dkg[i] = mma_f32_k16(zr, sb, dkg[i]);
+                }
+                dkt[i] = mma_f32_k16(rd4(Xs + r * PB + vv), rdcol4(dsp + (size_t)vv * D + c, D), dkt[i]);
+            }
+            // lane (n = c, g) holds rows 16 rb + 4 lg + j
+            const f32x4 g = rdcol4(Gb + (16 * rb + 4 * lg) * PB + c, PB);
+            dq[i] *= exp2x4(g + splat4(span1<D>(bt, 0, rb, c)));
+            dkg[i] *= -exp2x4(g + splat4(span1<D>(bt, 0, rb, c)));
+            dkt[i] *= exp2x4(splat4(span1<D>(bt, rb, 4, c)) - g);
+        }
+    }
+    // dgC_c = sum_v dS'_cv S_cv
+    for (int c = tid; c < D; c += kBwdThreads) {
+        float s = 0.f;
+        if (Sg)
+            for (int vv = 0; vv < D; ++vv) s += dsp[(size_t)vv * D + c] * Sg[(size_t)vv * D + c];
+        dgc[c] = s;
+    }
+    __syncthreads();
+
+    // ---- Q replaces V'
+    float *Qs = Xs;
+    stage_rows<D, F32IO>(Qs, q, t0, L, h, H, tid);
+    __syncthreads();
+
+    // ---- the decay-masked products of dP (S1) and dA_kk (S0, dR = Diag(beta) dA_kk)
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+        const int u = wave + i * kBwdWaves;
+        if (u >= 4 * KT) continue;
+        const int rb = u / KT, ct = u % KT;
+        const int c = 16 * ct + ln;
+        const float gmid = Gb[(16 * rb + 7) * PB + c];
+        const f32x4 grow = rdcol4(Gb + (16 * rb + 4 * lg) * PB + c, PB);
+        // forward direction, rows r in block rb:
+        //   sum_{i <= r} X_ri k_i exp2(G_r - G_i),  X = dP (to dQ) and dR (to dK)
+        f32x4 qo = zero4(), ko = zero4(), qd = zero4(), kd = zero4();
+        const float br = bet[16 * rb + ln];
+        for (int J = 0; J <= rb; ++J) {
+            const int i0 = 16 * J + 4 * lg;
+            const f32x4 gi = rdcol4(Gb + i0 * PB + c, PB);
+            const f32x4 fb = (J < rb) ? splat4(span1<D>(bt, J, rb, c)) - gi : splat4(gmid) - gi;
+            const f32x4 bk = rdcol4(Ks + i0 * PB + c, PB) * exp2x4(fb);
+            const f32x4 ap = rd4(S1 + (16 * rb + ln) * kPS + 16 * J + 4 * lg);
+            const f32x4 ar = rd4(S0 + (16 * rb + ln) * kPS + 16 * J + 4 * lg) * br;
+            if (J < rb) {
+                qo = mma_f32_k16(ap, bk, qo);
+                ko = mma_f32_k16(ar, bk, ko);
+            } else {
+                qd = mma_f32_k16(ap, bk, qd);
+                kd = mma_f32_k16(ar, bk, kd);
+            }
+        }
+        const f32x4 fo = exp2x4(grow), fd = exp2x4(grow - splat4(gmid));
+        dq[i] += qo * fo + qd * fd;
+        dkg[i] += ko * fo + kd * fd;
+        // backward direction, rows i in block rb:
+        //   sum_{r >= i} (dP_ri q_r + dR_ri k_r) exp2(G_r - G_i)
+        f32x4 xo = zero4(), xd = zero4();
+        for (int I = rb; I < 4; ++I) {
+            const int r0 = 16 * I + 4 * lg;
+            const f32x4 gr = rdcol4(Gb + r0 * PB + c, PB);
+            const f32x4 fr = (I > rb) ? gr + splat4(span1<D>(bt, rb + 1, I, c)) : gr - splat4(gmid);
+            const f32x4 ex = exp2x4(fr);
+            const f32x4 bq = rdcol4(Qs + r0 * PB + c, PB) * ex;
+            const f32x4 bk = rdcol4(Ks + r0 * PB + c, PB) * ex;
+            const f32x4 ap = rdcol4(S1 + r0 * kPS + 16 * rb + ln, kPS);
+            const f32x4 ar = rdcol4(S0 + r0 * kPS + 16 * rb + ln, kPS) * rd4(bet + r0);
+            if (I > rb) {
+                xo = mma_f32_k16(ap, bq, xo);
+                xo = mma_f32_k16(ar, bk, xo);
+            } else {
+                xd = mma_f32_k16(ap, bq, xd);
+                xd = mma_f32_k16(ar, bk, xd);
+            }
+        }
+        dki[i] = xo * exp2x4(splat4(bt[rb * D + c]) - grow) + xd * exp2x4(splat4(gmid) - grow);
+    }
+
+    // ---- outputs dq, dk; the log-decay gradient terms (registers)
+    f32x4 gG[NU], gKt[NU];
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+        const int u = wave + i * kBwdWaves;
+        gG[i] = gKt[i] = zero4();
+        if (u >= 4 * KT) continue;
+        const int rb = u / KT, ct = u % KT;
+        const int c = 16 * ct + ln;
+        const f32x4 kv = rdcol4(Ks + (16 * rb + 4 * lg) * PB + c, PB);
+        const f32x4 qv = rdcol4(Qs + (16 * rb + 4 * lg) * PB + c, PB);
+        gG[i] = kv * (dkg[i] - dki[i]) + qv * dq[i];
+        gKt[i] = kv * dkt[i];
+        const f32x4 pdr = rd4(pd + 16 * rb + 4 * lg);
+        const f32x4 dqo = dq[i] + pdr * kv;
+        const f32x4 dko = dkg[i] + dki[i] + dkt[i] + pdr * qv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * rb + 4 * lg + j;
+            if (r < L) {
+                const size_t o = ((size_t)(t0 + r) * H + h) * D + c;
+                gq[o] = dqo[j];
+                gk[o] = dko[j];
+            }
+        }
+    }
+    __syncthreads();
+    // gradient of the log-decay over S0|S1, the K~ terms over K
+    float *Gg = S0, *Gt = Ks;
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+        const int u = wave + i * kBwdWaves;
+        if (u >= 4 * KT) continue;
+        const int rb = u / KT, ct = u % KT;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * rb + 4 * lg + j;
+            Gg[r * PB + 16 * ct + ln] = gG[i][j];
+            Gt[r * PB + 16 * ct + ln] = gKt[i][j];
+        }
+    }
+    __syncthreads();
+    // per channel: block sums, then the cumulative sums inside each block:
+    //   dg_t = sum_{r >= t} gG_r + sum_{r < t} gKt_r + dgC * gamma_C
+    // (gKt_r = k_r dK~_r: the factor gamma_C / Gamma_r depends on the gates of
+    // rows r + 1 .. C only, so it is summed forward, not as total - suffix)
+    float dA_acc = 0.f;
+    if (tid < 4 * D) {
+        const int c = tid % D, I = tid / D;
+        float s = 0.f, st = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            s += Gg[(16 * I + i) * PB + c];
+            st += Gt[(16 * I + i) * PB + c];
+        }
+        red[I * D + c] = s;
+        red[(4 + I) * D + c] = st;
+    }
+    __syncthreads();
+    if (tid < 4 * D) {
+        const int c = tid % D, I = tid / D;
+        float fw[16];
+        float pre = 0.f;
+        for (int m = 0; m < I; ++m) pre += red[(4 + m) * D + c];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            fw[i] = pre;
+            pre += Gt[(16 * I + i) * PB + c];
+        }
+        const float base = dgc[c] * fast_exp2(span1<D>(bt, 0, 4, c));
+        float run = 0.f;
+        for (int m = I + 1; m < 4; ++m) run += red[m * D + c];
+#pragma unroll
+        for (int i = 15; i >= 0; --i) {
+            const int r = 16 * I + i;
+            run += Gg[r * PB + c];
+            const float dg = run + fw[i] + base;
+            if (r < L) {
+                const size_t o = ((size_t)(t0 + r) * H + h) * D + c;
+                // sigmoid'(x) = e / (1 + e)^2 with e = exp(-|x|): no cancellation
+                // where the gate saturates
+                const float x = ea * z[o];
+                const float ex = expf(-fabsf(x));
+                const float dx = dg * -5.0f * ex / ((1.f + ex) * (1.f + ex));
+                gz[o] = dx * ea;
+                dA_acc += dx * x;
+            }
+        }
+    }
+    // fixed-order block reduction of the A gradient
+    for (int off = 32; off > 0; off >>= 1) dA_acc += __shfl_xor(dA_acc, off);
+    if (lane == 0) part[wave] = dA_acc;
+    __syncthreads();
+    if (tid == 0) {
+        float s = 0.f;
+        for (int w = 0; w < kBwdWaves; ++w) s += part[w];
+        dA_part[(size_t)chunk * H + h] = s;
+    }
+}
+
+// Stage 5: dA[h] = sum over chunks of the per-(chunk, head) parts.
+__global__ void __launch_bounds__(256) bwd_dA_kernel(const int32_t *__restrict__ meta, int N, int H,
+                                                     const float *__restrict__ part, float *__restrict__ dA) {
+    __shared__ float red[256];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const int total = meta[N];
+    float s = 0.f;
+    for (int c = tid; c < total; c += 256) s += part[(size_t)c * H + h];
+    red[tid] = s;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if (tid < off) red[tid] += red[tid + off];
+        __syncthreads();
+    }
+    if (tid == 0) dA[h] = red[0];
+}
+
+template <int D, bool F32IO>
+int launch_backward_t(const BackwardArgs &a) {
+    const BackwardPlan &p = a.plan;
+    unsigned char *fws = a.ws + p.off_fwd;
+    PrefillArgs fa;
+    fa.f32io = F32IO;
+    fa.q = a.q; fa.k = a.k; fa.v = a.v; fa.z = a.z; fa.A = a.A; fa.beta = a.beta; fa.h0 = a.h0;
+    fa.cu = a.cu;
+    fa.N = a.N; fa.T = a.T; fa.H = a.H; fa.dk = D; fa.dv = D;
+    fa.o = a.ws + p.off_o;
+    fa.hT = nullptr;
+    float *ck = p.ck_cap > 0 ? reinterpret_cast<float *>(a.ws + p.off_ck) : nullptr;
+    fa.ck = ck;
+    fa.ck_offsets = nullptr;
+    fa.ck_interval = ck ? kChunk : 0;
+    fa.ws = fws;
+    fa.plan = p.fwd;
+    fa.stream = a.stream;
+    if (launch_prefill(fa) != 0) return -1;
+
+    const int32_t *meta = reinterpret_cast<const int32_t *>(fws + p.fwd.off_meta);
+    const int4 *table = reinterpret_cast<const int4 *>(fws + p.fwd.off_table);
+    const int32_t *ck_off = reinterpret_cast<const int32_t *>(fws + p.fwd.off_ckoff);
+    float *items = reinterpret_cast<float *>(a.ws + p.off_items);
+    float *part = reinterpret_cast<float *>(a.ws + p.off_dA);
+    const int max_chunks = p.fwd.max_chunks;
+    const long long blocks = (long long)max_chunks * a.H;
+
+    if (blocks > 0) {
+        const size_t lds = sizeof(float) * LocalLds<D>::floats;
+        if (!set_lds(&bwd_local_kernel<D, F32IO>, lds)) return -1;
+        hipLaunchKernelGGL((bwd_local_kernel<D, F32IO>), dim3((unsigned)blocks), dim3(kBwdThreads), lds, a.stream,
+                           a.q, a.k, a.z, a.A, a.beta, a.dO, meta, table, a.N, a.H, max_chunks, items);
+        if (hipGetLastError() != hipSuccess) return -1;
+    }
+    if (a.N > 0) {
+        using SH = ChainShape<D>;
+        const int groups = SH::KT / SH::NW;
+        if (!set_lds(&bwd_chain_kernel<D>, SH::lds_bytes)) return -1;
+        hipLaunchKernelGGL((bwd_chain_kernel<D>), dim3(a.N * a.H * groups), dim3(SH::NT), SH::lds_bytes, a.stream,
+                           meta, a.dhT, items, a.N, a.H, max_chunks, groups, a.gh0);
+        if (hipGetLastError() != hipSuccess) return -1;
+    }
+    if (blocks > 0) {
+        const size_t lds = sizeof(float) * GradLds<D>::floats;
+        if (!set_lds(&bwd_grad_kernel<D, F32IO>, lds)) return -1;
+        hipLaunchKernelGGL((bwd_grad_kernel<D, F32IO>), dim3((unsigned)blocks), dim3(kBwdThreads), lds, a.stream,
+                           a.q, a.k, a.v, a.z, a.A, a.beta, a.h0, a.dO, meta, table, ck_off, ck, p.ck_cap, a.N,
+                           a.H, max_chunks, items, a.gq, a.gk, a.gv, a.gz, a.gbeta, part);
+        if (hipGetLastError() != hipSuccess) return -1;
+    }
+    hipLaunchKernelGGL(bwd_dA_kernel, dim3(a.H), dim3(256), 0, a.stream, meta, a.N, a.H, part, a.gA);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace
+
+size_t backward_item_bytes(int d) {
+    switch (d) {
+        case 32: return BwdItem<32>::floats * 4;
+        case 64: return BwdItem<64>::floats * 4;
+        case 128: return BwdItem<128>::floats * 4;
+    }
+    return 0;
+}
+
+static size_t align256b(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool plan_backward(int N, int T, int H, int d, bool f32io, int P, BackwardPlan *p) {
+    if (!plan_prefill(N, T, H, d, d, f32io, P, &p->fwd)) return false;
+    const size_t item = backward_item_bytes(d);
+    if (item == 0) return false;
+    p->ck_cap = T / kChunk;
+    p->off_fwd = 0;
+    p->off_o = align256b(p->fwd.total);
+    p->off_ck = p->off_o + align256b((size_t)T * H * d * (f32io ? 4 : 2));
+    p->off_items = p->off_ck + align256b((size_t)p->ck_cap * H * d * d * 4);
+    p->off_dA = p->off_items + (size_t)H * p->fwd.max_chunks * item;
+    p->total = p->off_dA + align256b((size_t)p->fwd.max_chunks * H * 4);
+    return true;
+}
+
+int launch_prefill_backward(const BackwardArgs &a) {
+    switch (a.d) {
+        case 32: return a.f32io ? launch_backward_t<32, true>(a) : launch_backward_t<32, false>(a);
+        case 64: return a.f32io ? launch_backward_t<64, true>(a) : launch_backward_t<64, false>(a);
+        case 128: return a.f32io ? launch_backward_t<128, true>(a) : launch_backward_t<128, false>(a);
+    }
+    return -1;
+}
+
+}  // namespace kda

@@ -104,7 +104,31 @@ struct PrefillArgs {
     hipStream_t stream;
 };
 
+// Workspace plan of the prefill backward: the forward's own workspace, its
+// discarded outputs, the state at every chunk boundary, and one fp32 record
+// per (chunk, head).
+struct BackwardPlan {
+    PrefillPlan fwd;         // at off_fwd
+    int ck_cap;              // T / 64: chunk-boundary states stored
+    size_t off_fwd, off_o, off_ck, off_items, off_dA, total;
+};
+
+struct BackwardArgs {
+    bool f32io;
+    const void *q, *k, *v;
+    const float *z, *A, *beta, *h0;
+    const int32_t *cu;
+    int N, T, H, d;
+    const void *dO;          // [T][H][d] io dtype
+    const float *dhT;        // [N][H][d][d] or NULL
+    float *gq, *gk, *gv, *gz, *gbeta, *gA, *gh0;   // fp32 gradients; gh0 may be NULL
+    unsigned char *ws;
+    BackwardPlan plan;
+    hipStream_t stream;
+};
+
 bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, int P, PrefillPlan *plan);
+bool plan_backward(int N, int T, int H, int d, bool f32io, int P, BackwardPlan *plan);
 // Segment count the prefill uses for these sizes, and the process-wide
 // setting that overrides it (0: automatic).
 int choose_segments(int N, int T, int H, int d);
@@ -116,6 +140,7 @@ int launch_decode_window(const DecodeWindowArgs &a);
 int launch_features(const FeatureArgs &a);
 int launch_output_gate(const GateArgs &a);
 int launch_prefill(const PrefillArgs &a);
+int launch_prefill_backward(const BackwardArgs &a);
 // Intra-chunk kernels (kda_intra.hip: bf16 path; kda_intra_f32.hip: fp32
 // path), D = 32, 64, 128.
 template <int D>

@@ -165,6 +165,18 @@ def random_prefill(lens, H: int, d: int, io: str = "bf16", h0_std: Optional[floa
                 N=N, H=H, dk=dk, dv=dv, T=T, io=io)
 
 
+def random_cotangents(T: int, N: int, H: int, d: int, io: str = "bf16", final_state: bool = True,
+                      seed: int = BASE_SEED + 7, device="cpu") -> dict:
+    """Upstream gradients for the prefill backward: dO ~ N(0, 1) [T, H, d] in
+    the io dtype and, optionally, dhT ~ N(0, 1) [N, H, d, d] fp32."""
+    device = torch.device(device)
+    g = _gen(device, seed)
+    f32 = torch.float32
+    dO = torch.randn(T, H, d, generator=g, device=device, dtype=f32).to(torch_dtype(io))
+    dhT = torch.randn(N, H, d, d, generator=g, device=device, dtype=f32) if final_state else None
+    return dict(dO=dO, dhT=dhT)
+
+
 def random_decode(N: int, H: int, d: int, io: str = "bf16", state_std: float = 0.05,
                   seed: int = BASE_SEED + 3, device="cpu", z_shift: float = 0.0) -> dict:
     """Draw one decode batch: one token per sequence plus the fp32 state."""

@@ -249,6 +249,39 @@ int kda_qkv_shortconv(kda_dtype io_dtype, const void *xq, const void *xk, const 
 int kda_output_gate(kda_dtype io_dtype, const void *o, const void *g, const float *w, float eps,
                     int T, int H, int dv, void *y, void *stream);
 
+/*
+ * Gradients of the chunkwise prefill, for training.  The pages give the
+ * forward recurrence and its chunk form (the s1mplewind "kimi-k3" notes,
+ * "Chunkwise 形式"; "Kimi K3：架构…" §3.1) and note that training keeps
+ * per-head intermediate states (the "分析" part of the same notes); they give
+ * no backward formula.  This call returns the exact reverse-mode gradients of
+ *   L = sum(grad_o * o) + sum(grad_hT * hT)
+ * with o, hT = kda_prefill(q, k, v, z, A, beta, h0, cu_seqlens), obtained by
+ * differentiating the chunk form as matrices: it runs the forward prefill
+ * again, keeping the state at every 64-token chunk boundary, then walks each
+ * sequence's chunks backwards carrying dL/dS, then computes every input
+ * gradient per (chunk, head).  Arithmetic after the forward recompute is fp32.
+ *
+ *   q .. cu_seqlens, N .. dv   as for kda_prefill (the same inputs)
+ *   grad_o      [T][H][dv] io dtype
+ *   grad_hT     [N][H][dv][dk] fp32, or NULL for zeros
+ *   grad_q, grad_k, grad_z   [T][H][dk] fp32;  grad_v [T][H][dv] fp32
+ *   grad_beta   [T][H] fp32;  grad_A [H] fp32 (summed over every token,
+ *               in a fixed order: the result does not vary between runs)
+ *   grad_h0     [N][H][dv][dk] fp32 (state layout), or NULL to skip
+ *   workspace   at least kda_prefill_backward_workspace_size(...) bytes,
+ *               256-byte aligned; contents on entry ignored, on return undefined
+ * Outputs may overlap no input, no other output and the workspace
+ * (KDA_ERR_ALIAS).  Errors and asynchrony as for kda_prefill.
+ */
+size_t kda_prefill_backward_workspace_size(int N, int T, int H, int dk, int dv, kda_dtype io_dtype);
+int kda_prefill_backward(kda_dtype io_dtype, const void *q, const void *k, const void *v,
+                         const float *z, const float *A, const float *beta, const float *h0,
+                         const int32_t *cu_seqlens, int N, int T, int H, int dk, int dv,
+                         const void *grad_o, const float *grad_hT, float *grad_q, float *grad_k,
+                         float *grad_v, float *grad_z, float *grad_beta, float *grad_A,
+                         float *grad_h0, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static, human-readable text for a kda_status value. */
 const char *kda_status_string(int status);
 

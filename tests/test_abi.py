@@ -22,6 +22,7 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["kda_build_info", "kda_decode", "kda_decode_window", "kda_prefill",
                                            "kda_prefill_checkpoints", "kda_qkv_shortconv", "kda_output_gate",
                                            "kda_prefill_segments", "kda_prefill_workspace_size",
+                                           "kda_prefill_backward", "kda_prefill_backward_workspace_size",
                                            "kda_set_prefill_segments", "kda_status_string"])
 
 
@@ -187,3 +188,41 @@ def test_feature_path_and_gate_reject_bad_arguments():
     assert g(io=2) == -4 and g(eps=-1.0) == -1 and g(eps=float("nan")) == -1
     assert g(dv=48) == -3 and g(w=None) == -2 and g(y=(1 << 26) + 2) == -5
     assert g(y=FAKE + 256) == -8                             # y partly over o
+
+
+def test_backward_workspace_size():
+    # per (chunk, head) fp32 record + chunk-boundary states + the forward's own workspace
+    n1 = kda.kda_prefill_backward_workspace_size(1, 4096, 4, 128, 128, kda.KDA_BF16)
+    f1 = kda.kda_prefill_workspace_size(1, 4096, 4, 128, 128, kda.KDA_BF16)
+    assert n1 > f1 + (4096 // 64) * 4 * 128 * 128 * 4
+    n2 = kda.kda_prefill_backward_workspace_size(1, 4096 + 64, 4, 128, 128, kda.KDA_BF16)
+    assert n2 > n1
+    assert kda.kda_prefill_backward_workspace_size(1, 100, 2, 32, 64, kda.KDA_BF16) == 0
+    assert kda.kda_prefill_backward_workspace_size(1, 100, 2, 32, 32, 5) == 0
+    assert kda.kda_prefill_backward_workspace_size(0, 0, 2, 32, 32, kda.KDA_F32) > 0
+
+
+def test_prefill_backward_rejects_bad_arguments():
+    T, H, d = 128, 2, 32
+    span = T * H * d * 4
+
+    def b(**o):
+        base = 1 << 24
+        a = dict(io=0, q=base, k=base + span, v=base + 2 * span, z=base + 3 * span, A=base + 4 * span,
+                 beta=base + 4 * span + 256, cu=base + 5 * span, dO=base + 6 * span, dhT=None,
+                 gq=1 << 26, gk=(1 << 26) + span, gv=(1 << 26) + 2 * span, gz=(1 << 26) + 3 * span,
+                 gb=(1 << 26) + 4 * span, gA=(1 << 26) + 5 * span, gh0=None, d=d, N=1, ws=1 << 30,
+                 ws_bytes=1 << 40)
+        a.update(o)
+        return kda.kda_prefill_backward(a["io"], a["q"], a["k"], a["v"], a["z"], a["A"], a["beta"], None, a["cu"],
+                                        a["N"], T, H, a["d"], a["d"], a["dO"], a["dhT"], a["gq"], a["gk"], a["gv"],
+                                        a["gz"], a["gb"], a["gA"], a["gh0"], a["ws"], a["ws_bytes"], None)
+    assert b(io=3) == -4
+    assert b(N=-1) == -1
+    assert b(d=48) == -3
+    assert b(gA=None) == -2 and b(dO=None) == -2 and b(gq=None) == -2 and b(ws=None) == -2
+    assert b(gq=(1 << 26) + 4) == -5 and b(ws=(1 << 30) + 16) == -5
+    assert b(ws_bytes=16) == -6
+    assert b(gq=1 << 24) == -8                    # grad_q on top of q
+    assert b(gk=(1 << 26) + 64) == -8             # grad_k over grad_q
+    assert b(gh0=(1 << 30) + 256) == -8           # grad_h0 inside the workspace
