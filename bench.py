@@ -80,6 +80,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-features", action="store_true",
                    help="skip the side measurement of the feature path and output gate")
+    p.add_argument("--no-backward", action="store_true",
+                   help="skip the side measurement of the prefill backward")
     p.add_argument("--no-checkpoints", action="store_true",
                    help="skip the side measurement of the prefill with 512-token checkpoints")
     p.add_argument("--no-decode-window", action="store_true",
@@ -214,6 +216,43 @@ def prefill_checkpoint_cost(kda, pre, o, hT, ws, interval: int = 512, reps: int 
     del ck
     return {"interval": interval, "checkpoints": T // interval, "ms": round(ms, 4),
             "checkpoint_GB": round((T // interval) * H * D * D * 4 / 1e9, 3)}
+
+
+def prefill_backward_cost(kda, W, pre, reps: int = 3) -> dict:
+    """Side measurement: gradients of the K3 prefill (kda_prefill_backward:
+    forward recompute with chunk-boundary states, then the fp32 backward
+    kernels).  Algorithmic bytes per (token, head): q, k, v and dO read in
+    bf16, z and beta in fp32, dq, dk, dv, dz and dbeta written in fp32."""
+    import torch
+    T, H, D = pre["q"].shape
+    dev = pre["q"].device
+    cot = W.random_cotangents(T, 1, H, D, "bf16", final_state=True, device=dev)
+    ws = torch.empty(kda.kda_prefill_backward_workspace_size(1, T, H, D, D, kda.KDA_BF16), dtype=torch.uint8,
+                     device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {n: torch.empty((T, H, D), **f32) for n in ("dq", "dk", "dv", "dz")}
+    g.update(dbeta=torch.empty((T, H), **f32), dA=torch.empty((H,), **f32), dh0=torch.empty((1, H, D, D), **f32))
+    run = lambda: kda.prefill_backward(pre["q"], pre["k"], pre["v"], pre["z"], pre["A"], pre["beta"],
+                                       pre["cu_seqlens"], cot["dO"], h0=None, grad_hT=cot["dhT"], workspace=ws,
+                                       grads=g)
+    run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    per_pair = 4 * 2 * D + 4 * D + 4 + 4 * 4 * D + 4
+    gbps = per_pair * T * H / (ms * 1e-3) / 1e9
+    out = {"workload": "K3 shape T=65536 H=96 d=128 bf16, dO bf16, dhT fp32", "ms": round(ms, 3),
+           "tokens_per_s": round(T / (ms * 1e-3), 1), "algorithmic_B_per_pair": per_pair,
+           "algorithmic_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+           "workspace_GB": round(ws.numel() / 1e9, 2)}
+    del ws, g, cot
+    torch.cuda.empty_cache()
+    return out
 
 
 def feature_path_cost(kda, W, dev, reps: int = 10) -> dict:
@@ -357,6 +396,8 @@ def main():
     }
     if not args.no_features:
         line["feature_path"] = feature_path_cost(kda, W, dev)
+    if not args.no_backward:
+        line["prefill_backward"] = prefill_backward_cost(kda, W, pre)
     if not args.no_checkpoints:
         line["prefill_checkpoints"] = prefill_checkpoint_cost(kda, pre, o, hT, ws)
     if not args.no_small_head:

@@ -143,8 +143,8 @@ template <int D>
 struct GradLds {
     static constexpr int PB = D + 4;
     static constexpr int k = 0, gb = k + 64 * PB, x = gb + 64 * PB, s0 = x + 64 * PB, s1 = s0 + 64 * kPS;
-    static constexpr int beta = s1 + 64 * kPS, bt = beta + 64, db = bt + 4 * D, pd = db + 64, dgc = pd + 64;
-    static constexpr int red = dgc + D, part = red + 8 * D, floats = part + kBwdWaves;
+    static constexpr int beta = s1 + 64 * kPS, bt = beta + 64, pd = bt + 4 * D, dgc = pd + 64;
+    static constexpr int red = dgc + D, part = red + (8 * D > 512 ? 8 * D : 512), floats = part + kBwdWaves;
     static_assert(64 * PB <= 2 * 64 * kPS, "the gradient of the log-decay fits the two small matrices");
 };
 
@@ -458,7 +458,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
     constexpr int NU = (4 * KT + kBwdWaves - 1) / kBwdWaves;  // [t][c] tiles per wave
     extern __shared__ __attribute__((aligned(16))) float lds[];
     float *Ks = lds + SL::k, *Gb = lds + SL::gb, *Xs = lds + SL::x, *S0 = lds + SL::s0, *S1 = lds + SL::s1;
-    float *bet = lds + SL::beta, *bt = lds + SL::bt, *db = lds + SL::db, *pd = lds + SL::pd, *dgc = lds + SL::dgc;
+    float *bet = lds + SL::beta, *bt = lds + SL::bt, *pd = lds + SL::pd, *dgc = lds + SL::dgc;
     float *red = lds + SL::red, *part = lds + SL::part;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
     const int chunk = blockIdx.x / H, h = blockIdx.x % H;
@@ -488,10 +488,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
     stage_rows<D, F32IO>(Ks, k, t0, L, h, H, tid);
     stage_rows<D, F32IO>(Xs, vin, t0, L, h, H, tid);
     stage_decay<D>(Gb, bt, z, ea, t0, L, h, H, tid);
-    if (tid < 64) {
-        bet[tid] = tid < L ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
-        db[tid] = 0.f;
-    }
+    if (tid < 64) bet[tid] = tid < L ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
     __syncthreads();
 
     // ---- V~ = V - (Gamma*K) S, in place
@@ -527,8 +524,16 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
             acc = mma_f32_k16(rdcol4(dvp + (size_t)c * 64 + 16 * mt + ln, 64), rd4(Xs + (16 * nt + ln) * PB + c),
                               acc);
         }
+        // dbeta_j partial over the tile's rows: sum_t dM_tj T_tj
+        float p = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) S1[(16 * mt + 4 * lg + j) * kPS + 16 * nt + ln] = acc[j];
+        for (int j = 0; j < 4; ++j) {
+            S1[(16 * mt + 4 * lg + j) * kPS + 16 * nt + ln] = acc[j];
+            p += acc[j] * S0[(16 * mt + 4 * lg + j) * kPS + 16 * nt + ln];
+        }
+        p += __shfl_xor(p, 16);
+        p += __shfl_xor(p, 32);
+        if (lg == 0) red[mt * 64 + 16 * nt + ln] = p;
     }
     f32x4 vp[NU];
 #pragma unroll
@@ -571,12 +576,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
         }
     }
 
-    // ---- dbeta_j = sum_t dM_tj T_tj;  E = (dM Diag(beta)) T^T (registers)
-    if (tid < 64) {
-        float s = 0.f;
-        for (int t = tid; t < 64; ++t) s += S1[t * kPS + tid] * S0[t * kPS + tid];
-        db[tid] = s;
-    }
+    // ---- E = (dM Diag(beta)) T^T (registers)
     f32x4 e[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -610,22 +610,32 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
         }
     }
     __syncthreads();
+    // dA_kk over T;  dbeta_r partials sum_i dA_kk,ri R_ri over the tile's columns
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int u = wave + i * kBwdWaves, mt = u >> 2, nt = u & 3;
+        f32x4 p = zero4();
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 16 * mt + 4 * lg + j, w = 16 * nt + ln;
-            S0[r * kPS + w] = w < r ? -e[i][j] : 0.f;
+            const float x = w < r ? -e[i][j] : 0.f;
+            S0[r * kPS + w] = x;
+            if (w < r) p[j] = x * item[IT::r + r * 64 + w];
         }
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p[j] += __shfl_xor(p[j], m);
+        }
+        if (ln == 0) wr4(red + 256 + nt * 64 + 16 * mt + 4 * lg, p);
     }
     __syncthreads();
-    // ---- dbeta_r += sum_i dA_kk,ri R_ri;  write dbeta
-    if (tid < 64) {
-        float s = db[tid];
-        const float *Rg = item + IT::r + tid * 64;
-        for (int w = 0; w < tid; ++w) s += S0[tid * kPS + w] * Rg[w];
-        if (tid < L) gbeta[(size_t)(t0 + tid) * H + h] = s;
+    // ---- dbeta = column sums of dM o T + row sums of dA_kk o R
+    if (tid < 64 && tid < L) {
+        float s = 0.f;
+        for (int m = 0; m < 4; ++m) s += red[m * 64 + tid];
+        for (int m = 0; m < 4; ++m) s += red[256 + m * 64 + tid];
+        gbeta[(size_t)(t0 + tid) * H + h] = s;
     }
 
     // ---- dP = Tril(dO V'^T): the strictly lower part -> S1 (E is dead), the
@@ -662,16 +672,24 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
             const int rb = u / KT, ct = u % KT;
             const int r = 16 * rb + ln, c = 16 * ct + ln;
             const bool rok = r < L;
+            float gc = 0.f;   // dgC_c = sum_v dS'_cv S_cv, from the row-block-0 tiles
 #pragma unroll
             for (int kk = 0; kk < KT; ++kk) {
                 const int vv = 16 * kk + 4 * lg;
+                const f32x4 dsb = rdcol4(dsp + (size_t)vv * D + c, D);
                 if (Sg) {
                     const f32x4 sb = rdcol4(Sg + (size_t)vv * D + c, D);
                     dq[i] = mma_f32_k16(row_io(dO, r, vv), sb, dq[i]);
                     const f32x4 zr = rok ? rd4(gv + ((size_t)(t0 + r) * H + h) * D + vv) : zero4();
                     dkg[i] = mma_f32_k16(zr, sb, dkg[i]);
+                    gc += sb[0] * dsb[0] + sb[1] * dsb[1] + sb[2] * dsb[2] + sb[3] * dsb[3];
                 }
-                dkt[i] = mma_f32_k16(rd4(Xs + r * PB + vv), rdcol4(dsp + (size_t)vv * D + c, D), dkt[i]);
+                dkt[i] = mma_f32_k16(rd4(Xs + r * PB + vv), dsb, dkt[i]);
+            }
+            if (rb == 0) {
+                gc += __shfl_xor(gc, 16);
+                gc += __shfl_xor(gc, 32);
+                if (lg == 0) dgc[c] = gc;
             }
             // lane (n = c, g) holds rows 16 rb + 4 lg + j
             const f32x4 g = rdcol4(Gb + (16 * rb + 4 * lg) * PB + c, PB);
@@ -679,13 +697,6 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
             dkg[i] *= -exp2x4(g + splat4(span1<D>(bt, 0, rb, c)));
             dkt[i] *= exp2x4(splat4(span1<D>(bt, rb, 4, c)) - g);
         }
-    }
-    // dgC_c = sum_v dS'_cv S_cv
-    for (int c = tid; c < D; c += kBwdThreads) {
-        float s = 0.f;
-        if (Sg)
-            for (int vv = 0; vv < D; ++vv) s += dsp[(size_t)vv * D + c] * Sg[(size_t)vv * D + c];
-        dgc[c] = s;
     }
     __syncthreads();
 
