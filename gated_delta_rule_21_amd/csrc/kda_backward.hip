@@ -26,7 +26,7 @@
 //      gamma_C and the chain's dS-free terms X = P^T dO, Y = (Gamma*Q)^T dO;
 //   3. bwd_chain_kernel, per (sequence, head, value columns): walks the
 //      chunks backwards carrying dS in fp32 MFMA accumulators, stores dS'
-//      and dV' of every chunk, and dh0;
+//      (key-major) and dV' (both orientations) of every chunk, and dh0;
 //   4. bwd_grad_kernel, one workgroup per (chunk, head): every input gradient;
 //   5. bwd_dA_kernel: the per-head sum of the chunks' A gradients, in a fixed
 //      order (the result does not depend on scheduling).
@@ -61,7 +61,8 @@ struct BwdItem {
     static constexpr size_t kt = 0;              // K~ = (gamma_C/Gamma)*K        [64][D]
     static constexpr size_t wt = kt + 64 * D;    // W^T                           [D][64]
     static constexpr size_t xv = wt + 64 * D;    // X^T, then dV'^T               [D][64]
-    static constexpr size_t ys = xv + 64 * D;    // Y^T, then dS' (state layout)  [D][D]
+    static constexpr size_t dvr = xv + 64 * D;   // dV'                           [64][D]
+    static constexpr size_t ys = dvr + 64 * D;   // Y, then dS'                   [D][D] (key-major)
     static constexpr size_t gam = ys + D * D;    // gamma_C                       [D]
     static constexpr size_t r = gam + D;         // R, strictly lower             [64][64]
     static constexpr size_t t = r + 64 * 64;     // T                             [64][64]
@@ -284,7 +285,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_local_kernel(
     stage_rows<D, F32IO>(DOs, dO, t0, L, h, H, tid);
     __syncthreads();
 
-    // Y = (Gamma*Q)^T dO, stored transposed: tile (key block mt, value block nt)
+    // Y = (Gamma*Q)^T dO, key-major [c][v]: tile (key block mt, value block nt)
     for (int u = wave; u < KT * KT; u += kBwdWaves) {
         const int mt = u / KT, nt = u % KT;
         const int c = 16 * mt + ln;
@@ -296,7 +297,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_local_kernel(
             acc = mma_f32_k16(rdcol4(Qs + t * PB + c, PB) * exp2x4(g), rdcol4(DOs + t * PB + 16 * nt + ln, PB),
                               acc);
         }
-        wr4(item + IT::ys + (size_t)(16 * nt + ln) * D + 16 * mt + 4 * lg, acc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) item[IT::ys + (size_t)(16 * mt + 4 * lg + j) * D + 16 * nt + ln] = acc[j];
     }
     // X = P^T dO, stored transposed: tile (row block mt, value block nt)
     for (int u = wave; u < 4 * KT; u += kBwdWaves) {
@@ -379,7 +381,7 @@ __global__ void __launch_bounds__(ChainShape<D>::NT) bwd_chain_kernel(const int3
         for (int rt = 0; rt < 4; ++rt) X[rt] = rd4(it + IT::xv + (size_t)v * 64 + 16 * rt + 4 * lg);
 #pragma unroll
         for (int rc = 0; rc < KT; ++rc) {
-            Y[rc] = rd4(it + IT::ys + (size_t)v * D + 16 * rc + 4 * lg);
+            Y[rc] = rdcol4(it + IT::ys + (size_t)(16 * rc + 4 * lg) * D + v, D);
             G[rc] = rd4(it + IT::gam + 16 * rc + 4 * lg);
         }
     };
@@ -424,10 +426,19 @@ __global__ void __launch_bounds__(ChainShape<D>::NT) bwd_chain_kernel(const int3
                 nd[rc] = acc;
             }
             float *it = rec(c);
+            // dS' over Y (the same lanes read and write the same addresses),
+            // dV' over X^T and row-major beside it
 #pragma unroll
-            for (int rc = 0; rc < KT; ++rc) wr4(it + IT::ys + (size_t)v * D + 16 * rc + 4 * lg, dS[rc]);
+            for (int rc = 0; rc < KT; ++rc) {
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) wr4(it + IT::xv + (size_t)v * 64 + 16 * rt + 4 * lg, dv[rt]);
+                for (int j = 0; j < 4; ++j) it[IT::ys + (size_t)(16 * rc + 4 * lg + j) * D + v] = dS[rc][j];
+            }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                wr4(it + IT::xv + (size_t)v * 64 + 16 * rt + 4 * lg, dv[rt]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) it[IT::dvr + (size_t)(16 * rt + 4 * lg + j) * D + v] = dv[rt][j];
+            }
 #pragma unroll
             for (int rc = 0; rc < KT; ++rc) dS[rc] = nd[rc];
             if (more) store_stage(lds + (b ^ 1) * SH::buf);
@@ -456,6 +467,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
     using SL = GradLds<D>;
     constexpr int PB = D + 4, KT = D / 16;
     constexpr int NU = (4 * KT + kBwdWaves - 1) / kBwdWaves;  // [t][c] tiles per wave
+    static_assert(kBwdWaves % KT == 0, "a wave's [t][c] tiles share one column block");
     extern __shared__ __attribute__((aligned(16))) float lds[];
     float *Ks = lds + SL::k, *Gb = lds + SL::gb, *Xs = lds + SL::x, *S0 = lds + SL::s0, *S1 = lds + SL::s1;
     float *bet = lds + SL::beta, *bt = lds + SL::bt, *pd = lds + SL::pd, *dgc = lds + SL::dgc;
@@ -467,7 +479,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
     const int n = ent.x, t0 = ent.y, L = ent.z;
     const float *item = items + ((size_t)h * max_chunks + chunk) * IT::floats;
     const float *dvp = item + IT::xv;   // dV'^T [v][t]
-    const float *dsp = item + IT::ys;   // dS' [v][c]
+    const float *dvr = item + IT::dvr;  // dV' [t][v]
+    const float *dsp = item + IT::ys;   // dS' [c][v]
     const float ea = __expf(A[h]);
     // state at the chunk's start, [v][c]; NULL = zero
     const float *Sg = nullptr;
@@ -521,8 +534,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
 #pragma unroll
         for (int kk = 0; kk < KT; ++kk) {
             const int c = 16 * kk + 4 * lg;
-            acc = mma_f32_k16(rdcol4(dvp + (size_t)c * 64 + 16 * mt + ln, 64), rd4(Xs + (16 * nt + ln) * PB + c),
-                              acc);
+            acc = mma_f32_k16(rd4(dvr + (size_t)(16 * mt + ln) * D + c), rd4(Xs + (16 * nt + ln) * PB + c), acc);
         }
         // dbeta_j partial over the tile's rows: sum_t dM_tj T_tj
         float p = 0.f;
@@ -664,6 +676,14 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
         }
     }
     f32x4 dq[NU], dkg[NU], dkt[NU], dki[NU];
+    // B fragments of S for this wave's key columns (every tile of a wave has
+    // the same column block, wave % KT): S_cv for c = 16 ct + ln, v = 16 kk + 4 lg + j
+    f32x4 sfr[KT];
+    {
+        const int c = 16 * (wave % KT) + ln;
+#pragma unroll
+        for (int kk = 0; kk < KT; ++kk) sfr[kk] = Sg ? rdcol4(Sg + (size_t)(16 * kk + 4 * lg) * D + c, D) : zero4();
+    }
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
         const int u = wave + i * kBwdWaves;
@@ -676,9 +696,9 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
 #pragma unroll
             for (int kk = 0; kk < KT; ++kk) {
                 const int vv = 16 * kk + 4 * lg;
-                const f32x4 dsb = rdcol4(dsp + (size_t)vv * D + c, D);
+                const f32x4 dsb = rd4(dsp + (size_t)c * D + vv);
                 if (Sg) {
-                    const f32x4 sb = rdcol4(Sg + (size_t)vv * D + c, D);
+                    const f32x4 sb = sfr[kk];
                     dq[i] = mma_f32_k16(row_io(dO, r, vv), sb, dq[i]);
                     const f32x4 zr = rok ? rd4(gv + ((size_t)(t0 + r) * H + h) * D + vv) : zero4();
                     dkg[i] = mma_f32_k16(zr, sb, dkg[i]);
