@@ -39,13 +39,17 @@ PREFILL_FLOPS_PER_PAIR = 6 * 128 * 128 + 5 * 64 * 128 + (64 * 64) // 3
 DECODE_BYTES_PER_PAIR = 2 * 128 * 128 * 4 + 4 * 128 * 2 + 128 * 4 + 4
 
 
+# The sources of the kernels one kda_prefill launch runs (chunk table, intra, inter,
+# combine) and the headers they include: a change to any of them makes the committed
+# traffic figure stale.
+PREFILL_SOURCES = ("kda_prefill.hip", "kda_intra.hip", "kda_intra_f32.hip", "kda_chunk.h", "kda_device.h",
+                   "kda_internal.h")
+
+
 def kernel_sources_digest() -> str:
-    """sha256 (first 16 hex digits) over the HIP sources and the public header."""
-    import glob
+    """sha256 (first 16 hex digits) over the prefill kernels' sources."""
     import hashlib
-    files = sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", "*.hip")) +
-                   glob.glob(os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", "*.h")) +
-                   [os.path.join(ROOT, "include", "kda.h")])
+    files = [os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", f) for f in PREFILL_SOURCES]
     h = hashlib.sha256()
     for f in files:
         h.update(os.path.relpath(f, ROOT).encode())
