@@ -320,7 +320,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     using SHP = InterShape<D, F32IO>;
     constexpr int KT = D / 16;
     constexpr int WPG = SHP::WPG;
-    constexpr size_t BUF = (size_t)(SL::FA + SL::FB) * SL::FRAG;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
 
     // blockIdx -> (segment and head, column group) with every group of a
@@ -487,6 +486,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
                                                  0);
             };
 
+            // LDS reads are issued a phase ahead of their use, so their latency
+            // hides behind VALU and MFMA work instead of stalling each product:
+            // the -W and Gamma*Q fragments of row tile 0 and the U exponents
+            // before the S conversion, those of row tile I + 1 during tile I,
+            // and K~^T, A_qk and gamma_C during the last tile.
+            u32x4 fwc[KT / 2], fqc[KT / 2];
+            auto read_tile = [&](int I, u32x4 *fw, u32x4 *fq) {
+#pragma unroll
+                for (int p = 0; p < KT / 2; ++p) {
+                    fw[p] = fragA(SL::negW, I * (KT / 2) + p);
+                    if constexpr (!TR) fq[p] = fragA(SL::qg, I * (KT / 2) + p);
+                }
+            };
+            read_tile(0, fwc, fqc);
+            int uex[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) uex[I] = uexp[I * KT + vt];
             // S -> fp16 with a per-wave power-of-two scale (and S2 with its own)
             u32x4 sf[KT / 2], sf2[TR ? KT / 2 : 1];
             const float uS = to_f16_scaled<KT>(S, sf);
@@ -494,14 +510,29 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             if constexpr (TR) uS2 = to_f16_scaled<KT>(S2, sf2);
 
             f32x4 vp[4], vp2[TR ? 4 : 1];
+            u32x4 kfr[2 * KT], afr[MODE == kModeOutput ? SL::NAQ : 1];
+            f32x4 gmr[KT];
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
 #pragma unroll
                 for (int r = 0; r < NA / 4; ++r) copyA_part(I * (NA / 4) + r);
+                u32x4 fwn[KT / 2], fqn[KT / 2];
+                if (I < 3) read_tile(I + 1, fwn, fqn);
+                if (I == 3) {
+#pragma unroll
+                    for (int t = 0; t < 2 * KT; ++t) kfr[t] = fragB(SL::kdT, t);
+                    const f32x4 *gp = reinterpret_cast<const f32x4 *>(bbuf + (SL::gamma - SL::kdT));
+#pragma unroll
+                    for (int t = 0; t < KT; ++t) gmr[t] = gp[4 * t + lg];
+                    if constexpr (MODE == kModeOutput) {
+#pragma unroll
+                        for (int f = 0; f < SL::NAQ; ++f) afr[f] = fragB(SL::aqk, f);
+                    }
+                }
                 f32x4 ws = zero4(), qs = zero4(), ws2 = zero4();
 #pragma unroll
                 for (int p = 0; p < KT / 2; ++p) {
-                    const u32x4 fw = fragA(SL::negW, I * (KT / 2) + p);
+                    const u32x4 fw = fwc[p];
                     ws = mma_f16_k32(fw, sf[p], ws);
                     if constexpr (TR) {
                         ws2 = mma_f16_k32(fw, sf2[p], ws2);
@@ -509,10 +540,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
                         // O^T = S^T (Gamma*Q)^T: the same fragments with the operands
                         // swapped, so the accumulator holds O row-major (lane (n, g):
                         // row n, columns 4g..4g+3) and o needs no transpose
-                        qs = mma_f16_k32(sf[p], fragA(SL::qg, I * (KT / 2) + p), qs);
+                        qs = mma_f16_k32(sf[p], fqc[p], qs);
                     }
                 }
-                const f32x4 uu = f16x4_to_quad(u[I]) * exp2i(uexp[I * KT + vt]);
+                if (I < 3) {
+#pragma unroll
+                    for (int p = 0; p < KT / 2; ++p) {
+                        fwc[p] = fwn[p];
+                        fqc[p] = fqn[p];
+                    }
+                }
+                const f32x4 uu = f16x4_to_quad(u[I]) * exp2i(uex[I]);
                 if constexpr (TR) {
                     vp[I] = ws * uS;
                     vp2[I] = uu + ws2 * uS2;
@@ -534,18 +572,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
                     // (A_qk V')^T = V'^T A_qk^T, row-major like O above
-                    f32x4 a = mma_f16_k32(vf0, fragB(SL::aqk, aqk_frag(I, 0)), zero4());
-                    if (I >= 2) a = mma_f16_k32(vf1, fragB(SL::aqk, aqk_frag(I, 1)), a);
+                    f32x4 a = mma_f16_k32(vf0, afr[aqk_frag(I, 0)], zero4());
+                    if (I >= 2) a = mma_f16_k32(vf1, afr[aqk_frag(I, 1)], a);
                     acc_o[I] += a * uV;
                     *reinterpret_cast<u32x2 *>(ob + (16 * I + ln) * OP + 16 * wave + 4 * lg) =
                         u32x2{f32x2_to_bf16x2(acc_o[I][0], acc_o[I][1]), f32x2_to_bf16x2(acc_o[I][2], acc_o[I][3])};
                 }
             }
-            const f32x4 *gam = reinterpret_cast<const f32x4 *>(bbuf + (SL::gamma - SL::kdT));
 #pragma unroll
             for (int t = 0; t < KT; ++t) {
-                const u32x4 k0 = fragB(SL::kdT, t * 2), k1 = fragB(SL::kdT, t * 2 + 1);
-                const f32x4 g = gam[4 * t + lg];
+                const u32x4 k0 = kfr[t * 2], k1 = kfr[t * 2 + 1];
+                const f32x4 g = gmr[t];
                 f32x4 a = mma_f16_k32(k0, vf0, zero4());
                 a = mma_f16_k32(k1, vf1, a);
                 S[t] = S[t] * g + a * uV;
