@@ -105,3 +105,15 @@ def test_backward_k3_sampled_heads():
     got = gpu_grads(to_gpu(inp), to_gpu(cot))
     heads = [5, 77]
     check(got, oracle_grads(inp, cot, heads), BF16_TOL, heads)
+
+
+@pytest.mark.parametrize("lens", [[0, 0], []])
+def test_backward_empty(lens):
+    """No tokens: dh0 = dhT, dA = 0 (and nothing else to write); no sequences at all."""
+    print("backward empty", lens, flush=True)
+    H, d = 2, 32
+    inp = W.random_prefill(lens, H, d, "f32", h0_std=0.1, seed=998)
+    cot = W.random_cotangents(0, len(lens), H, d, "f32", seed=999)
+    got = gpu_grads(to_gpu(inp), to_gpu(cot))
+    assert torch.equal(got["dh0"].cpu(), cot["dhT"])
+    assert torch.equal(got["dA"].cpu(), torch.zeros(H))
