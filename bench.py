@@ -90,6 +90,8 @@ def parse():
                    help="skip the side measurement of the prefill with 512-token checkpoints")
     p.add_argument("--no-decode-window", action="store_true",
                    help="skip the side measurement of the speculative decode step")
+    p.add_argument("--no-varlen", action="store_true",
+                   help="skip the side measurement of the varlen packed prefill (32 sequences, 262144 tokens)")
     p.add_argument("--no-small-head", action="store_true",
                    help="skip the side measurement of the small-head prefill (B=2, H=8, T=8192)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -163,6 +165,38 @@ def small_head_prefill(kda, W, dev, reps: int = 10) -> dict:
             del ws
         out[key] = {"segments": segs, "ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1)}
     return out
+
+
+def varlen_prefill(kda, W, dev, reps: int = 5) -> dict:
+    """Side measurement: the varlen packed prefill (32 lognormal lengths
+    summing to 262,144 tokens, H=96, d=128, bf16, h0 given), with the
+    per-(token, head) algorithmic bytes of the K3 figure."""
+    import torch
+    d = W.make("k3_varlen", device=dev)
+    T, H, D = d["q"].shape
+    N = d["cu_seqlens"].numel() - 1
+    o = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    ws = kda.prefill_workspace(N, T, H, D, kda.KDA_BF16, dev)
+    run = lambda: kda.prefill(d["q"], d["k"], d["v"], d["z"], d["A"], d["beta"], d["cu_seqlens"], h0=d["h0"],
+                              o=o, hT=hT, workspace=ws)
+    run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbps = PREFILL_BYTES_PER_PAIR * T * H / (ms * 1e-3) / 1e9
+    lens = (d["cu_seqlens"][1:] - d["cu_seqlens"][:-1]).tolist()
+    del ws, o, hT, d
+    torch.cuda.empty_cache()
+    return {"workload": "k3_varlen: 32 lognormal(ln 8192, 1) lengths summing to 262144 (shortest %d, longest %d), "
+                        "H=96 d=128 bf16, h0 given" % (min(lens), max(lens)),
+            "ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "algorithmic_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
 def decode_window_step(kda, W, dev, reps: int = 200) -> dict:
@@ -404,6 +438,8 @@ def main():
         line["prefill_backward"] = prefill_backward_cost(kda, W, pre)
     if not args.no_checkpoints:
         line["prefill_checkpoints"] = prefill_checkpoint_cost(kda, pre, o, hT, ws)
+    if not args.no_varlen:
+        line["varlen"] = varlen_prefill(kda, W, dev)
     if not args.no_small_head:
         line["small_head"] = small_head_prefill(kda, W, dev)
     if not args.no_decode_window:

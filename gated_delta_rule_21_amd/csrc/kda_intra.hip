@@ -371,7 +371,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
                 const size_t tb = (size_t)(t * 4 + b) * 512 + ln * 32 + lg * 8;   // row ln, channels 4lg..
                 *reinterpret_cast<u32x2 *>(X + LY::GKT + tb) = hi;
                 *reinterpret_cast<u32x2 *>(X + LY::GKL + tb) = lo;
-                *reinterpret_cast<u32x2 *>(X + LY::VT + tb) = R.v[t];
             }
         }
         if (lane < 16) {
@@ -390,6 +389,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int r = 0; r < 16; ++r) a[o + r][o + lane] = x[r];
         }
+        // V last: its loads, issued at the top of the phase, complete behind
+        // the Gamma*K split and the diagonal solve instead of stalling them
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+            *reinterpret_cast<u32x2 *>(X + LY::VT + (size_t)(t * 4 + b) * 512 + ln * 32 + lg * 8) = R.v[t];
         __syncthreads();
 
         // the gate inputs of the next item
