@@ -80,6 +80,23 @@ __device__ __forceinline__ f32x4 exp2x4(f32x4 x) {
 }
 __device__ __forceinline__ f32x4 splat4(float x) { return f32x4{x, x, x, x}; }
 
+// acc + A B over two K16 tiles (a0, b0: tile 2p; a1, b1: tile 2p + 1) in the
+// fp32 fragment layout.  fp32 path: four fp32 MFMAs per tile.  bf16 path: each
+// operand split into bf16 hi + lo and three 16x16x32 bf16 MFMAs (hi hi, hi lo,
+// lo hi), good to about 2^-16 relative per term.
+template <bool F32>
+__device__ __forceinline__ f32x4 mma_k32(f32x4 a0, f32x4 a1, f32x4 b0, f32x4 b1, f32x4 acc) {
+    if constexpr (F32) {
+        acc = mma_f32_k16(a0, b0, acc);
+        return mma_f32_k16(a1, b1, acc);
+    } else {
+        u32x4 ah, al, bh, bl;
+        quads_to_bf16_split(a0, a1, ah, al);
+        quads_to_bf16_split(b0, b1, bh, bl);
+        return mma3_bf16(ah, al, bh, bl, acc);
+    }
+}
+
 // sum_{m = lo}^{hi - 1} bt[m][c] (zero when lo >= hi); bt is [4][D].
 template <int D>
 __device__ __forceinline__ f32x4 span4(const float *bt, int lo, int hi, int c) {
@@ -510,12 +527,14 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
         f32x4 acc = zero4();
         if (Sg) {
             const int r = 16 * mt + ln;
-#pragma unroll
-            for (int kk = 0; kk < KT; ++kk) {
+            auto kg = [&](int kk) {
                 const int c = 16 * kk + 4 * lg;
-                const f32x4 a = rd4(Ks + r * PB + c) * exp2x4(rd4(Gb + r * PB + c) + span4<D>(bt, 0, mt, c));
-                acc = mma_f32_k16(a, rd4(Sg + (size_t)(16 * nt + ln) * D + c), acc);
-            }
+                return rd4(Ks + r * PB + c) * exp2x4(rd4(Gb + r * PB + c) + span4<D>(bt, 0, mt, c));
+            };
+            auto sb = [&](int kk) { return rd4(Sg + (size_t)(16 * nt + ln) * D + 16 * kk + 4 * lg); };
+#pragma unroll
+            for (int kp = 0; kp < KT / 2; ++kp)
+                acc = mma_k32<F32IO>(kg(2 * kp), kg(2 * kp + 1), sb(2 * kp), sb(2 * kp + 1), acc);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) Xs[(16 * mt + 4 * lg + j) * PB + 16 * nt + ln] -= acc[j];
@@ -693,18 +712,35 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
             const int r = 16 * rb + ln, c = 16 * ct + ln;
             const bool rok = r < L;
             float gc = 0.f;   // dgC_c = sum_v dS'_cv S_cv, from the row-block-0 tiles
+            const size_t orow = ((size_t)(t0 + r) * H + h) * D;
 #pragma unroll
-            for (int kk = 0; kk < KT; ++kk) {
-                const int vv = 16 * kk + 4 * lg;
-                const f32x4 dsb = rd4(dsp + (size_t)c * D + vv);
+            for (int kp = 0; kp < KT / 2; ++kp) {
+                const int v0 = 32 * kp + 4 * lg, v1 = v0 + 16;
+                const f32x4 ds0 = rd4(dsp + (size_t)c * D + v0), ds1 = rd4(dsp + (size_t)c * D + v1);
                 if (Sg) {
-                    const f32x4 sb = sfr[kk];
-                    dq[i] = mma_f32_k16(row_io(dO, r, vv), sb, dq[i]);
-                    const f32x4 zr = rok ? rd4(gv + ((size_t)(t0 + r) * H + h) * D + vv) : zero4();
-                    dkg[i] = mma_f32_k16(zr, sb, dkg[i]);
-                    gc += sb[0] * dsb[0] + sb[1] * dsb[1] + sb[2] * dsb[2] + sb[3] * dsb[3];
+                    const f32x4 s0 = sfr[2 * kp], s1 = sfr[2 * kp + 1];
+                    const f32x4 z0 = rok ? rd4(gv + orow + v0) : zero4(), z1 = rok ? rd4(gv + orow + v1) : zero4();
+                    if constexpr (F32IO) {
+                        dq[i] = mma_k32<true>(row_io(dO, r, v0), row_io(dO, r, v1), s0, s1, dq[i]);
+                    } else {
+                        // dO is bf16 already: its hi part is exact and its lo part zero
+                        u32x4 dh = u32x4{0u, 0u, 0u, 0u};
+                        if (rok) {
+                            const uint16_t *dp = reinterpret_cast<const uint16_t *>(dO) + orow;
+                            const u32x2 w0 = *reinterpret_cast<const u32x2 *>(dp + v0);
+                            const u32x2 w1 = *reinterpret_cast<const u32x2 *>(dp + v1);
+                            dh = u32x4{w0[0], w0[1], w1[0], w1[1]};
+                        }
+                        u32x4 sh, sl;
+                        quads_to_bf16_split(s0, s1, sh, sl);
+                        dq[i] = mma_bf16_k32(dh, sh, dq[i]);
+                        dq[i] = mma_bf16_k32(dh, sl, dq[i]);
+                    }
+                    dkg[i] = mma_k32<F32IO>(z0, z1, s0, s1, dkg[i]);
+                    gc += s0[0] * ds0[0] + s0[1] * ds0[1] + s0[2] * ds0[2] + s0[3] * ds0[3];
+                    gc += s1[0] * ds1[0] + s1[1] * ds1[1] + s1[2] * ds1[2] + s1[3] * ds1[3];
                 }
-                dkt[i] = mma_f32_k16(rd4(Xs + r * PB + vv), dsb, dkt[i]);
+                dkt[i] = mma_k32<F32IO>(rd4(Xs + r * PB + v0), rd4(Xs + r * PB + v1), ds0, ds1, dkt[i]);
             }
             if (rb == 0) {
                 gc += __shfl_xor(gc, 16);
