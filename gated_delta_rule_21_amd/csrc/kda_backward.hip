@@ -47,6 +47,7 @@
 #include "kda_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace kda {
 
@@ -150,6 +151,62 @@ __device__ __forceinline__ void stage_decay(float *Gb, float *bt, const float *z
     }
 }
 
+// Raw inputs of one (chunk, head) item for one thread of the local kernel:
+// the quads of q, k and dO it stages (io dtype; rows past the chunk's end
+// zero), the 16 gate logits of thread (c, I) = (tid % D, tid / D), and beta.
+// The next item's are fetched into registers while the current one computes.
+template <int D, bool F32IO>
+struct LocalIn {
+    static constexpr int Q = D / 4, NQ = 64 * Q / kBwdThreads;
+    using Quad = typename std::conditional<F32IO, f32x4, u32x2>::type;
+    Quad q[NQ], k[NQ], o[NQ];
+    float z[16];
+    float beta;
+};
+
+template <int D, bool F32IO>
+__device__ __forceinline__ typename LocalIn<D, F32IO>::Quad load_quad(const void *p, size_t i) {
+    if constexpr (F32IO)
+        return *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(p) + i);
+    else
+        return *reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint16_t *>(p) + i);
+}
+
+template <int D, bool F32IO>
+__device__ __forceinline__ void load_local(LocalIn<D, F32IO> &R, const void *q, const void *k, const void *dO,
+                                           const float *z, const float *beta, int t0, int L, int h, int H,
+                                           int tid) {
+    using LI = LocalIn<D, F32IO>;
+#pragma unroll
+    for (int s = 0; s < LI::NQ; ++s) {
+        const int i = tid + s * kBwdThreads, r = i / LI::Q, c = 4 * (i % LI::Q);
+        const size_t off = ((size_t)(t0 + r) * H + h) * D + c;
+        R.q[s] = r < L ? load_quad<D, F32IO>(q, off) : typename LI::Quad{};
+        R.k[s] = r < L ? load_quad<D, F32IO>(k, off) : typename LI::Quad{};
+        R.o[s] = r < L ? load_quad<D, F32IO>(dO, off) : typename LI::Quad{};
+    }
+    if (tid < 4 * D) {
+        const int c = tid % D, I = tid / D;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = 16 * I + i;
+            R.z[i] = r < L ? z[((size_t)(t0 + r) * H + h) * D + c] : 0.f;
+        }
+    }
+    R.beta = (tid < 64 && tid < L) ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
+}
+
+// Rows [0, 64) of staged quads into LDS as fp32 (pitch D + 4).
+template <int D, bool F32IO>
+__device__ __forceinline__ void stage_quads(float *dst, const typename LocalIn<D, F32IO>::Quad *x, int tid) {
+    using LI = LocalIn<D, F32IO>;
+#pragma unroll
+    for (int s = 0; s < LI::NQ; ++s) {
+        const int i = tid + s * kBwdThreads, r = i / LI::Q, c = 4 * (i % LI::Q);
+        wr4(dst + r * (D + 4) + c, quad_f32<F32IO>(x[s]));
+    }
+}
+
 // LDS carve-up of the two per-item kernels (floats).
 template <int D>
 struct LocalLds {
@@ -182,151 +239,184 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_local_kernel(
     float *Qs = lds + SL::q, *Ks = lds + SL::k, *Gb = lds + SL::gb, *Rs = lds + SL::r, *Ps = lds + SL::p;
     float *bet = lds + SL::beta, *bt = lds + SL::bt;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
-    const int chunk = blockIdx.x / H, h = blockIdx.x % H;
-    if (chunk >= meta[N]) return;
-    const int4 ent = table[chunk];
-    const int t0 = ent.y, L = ent.z;
-    float *item = items + ((size_t)h * max_chunks + chunk) * IT::floats;
+    using LI = LocalIn<D, F32IO>;
+    const int total = meta[N] * H;
+    int it = blockIdx.x;
+    if (it >= total) return;
+    LI R;
+    int4 ent = table[it / H];
+    load_local<D, F32IO>(R, q, k, dO, z, beta, ent.y, ent.z, it % H, H, tid);
 
-    stage_rows<D, F32IO>(Qs, q, t0, L, h, H, tid);
-    stage_rows<D, F32IO>(Ks, k, t0, L, h, H, tid);
-    stage_decay<D>(Gb, bt, z, __expf(A[h]), t0, L, h, H, tid);
-    if (tid < 64) bet[tid] = tid < L ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
-    __syncthreads();
+    // persistent: items blockIdx.x, + gridDim.x, ...; the next item's inputs
+    // load into R while this one computes
+    for (; it < total; it += gridDim.x) {
+        const int chunk = it / H, h = it % H;
+        const int t0 = ent.y, L = ent.z;
+        float *item = items + ((size_t)h * max_chunks + chunk) * IT::floats;
+        const float ea = __expf(A[h]);
 
-    // Decayed Gram tiles (I, J), J <= I: R = (K.K) and P = (Q.K) with the
-    // per-channel factor exp2(G_r - G_i); R strictly lower, P lower.
-    for (int u = wave; u < 32; u += kBwdWaves) {
-        const bool isP = u >= 16;
-        const int I = (u & 15) >> 2, J = u & 3;
-        float *dst = isP ? Ps : Rs;
-        f32x4 acc = zero4();
-        if (J <= I) {
-            const float *src = isP ? Qs : Ks;
-            const int r = 16 * I + ln, i = 16 * J + ln, mid = 16 * I + 7;
+        stage_quads<D, F32IO>(Qs, R.q, tid);
+        stage_quads<D, F32IO>(Ks, R.k, tid);
+        typename LI::Quad ocur[LI::NQ];
 #pragma unroll
-            for (int kk = 0; kk < KT; ++kk) {
-                const int c = 16 * kk + 4 * lg;
-                const f32x4 gr = rd4(Gb + r * PB + c), gi = rd4(Gb + i * PB + c);
-                f32x4 fa, fb;
-                if (I == J) {
-                    const f32x4 gm = rd4(Gb + mid * PB + c);
-                    fa = gr - gm;
-                    fb = gm - gi;
-                } else {
-                    fa = gr;
-                    fb = span4<D>(bt, J, I, c) - gi;
-                }
-                acc = mma_f32_k16(rd4(src + r * PB + c) * exp2x4(fa), rd4(Ks + i * PB + c) * exp2x4(fb), acc);
+        for (int s = 0; s < LI::NQ; ++s) ocur[s] = R.o[s];
+        if (tid < 4 * D) {
+            // Gb and bt from the staged gate logits (as stage_decay)
+            const int c = tid % D, I = tid / D;
+            float run = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = 16 * I + i;
+                run += r < L ? gate_log2(ea, R.z[i]) : 0.f;
+                Gb[r * (D + 4) + c] = run;
+            }
+            bt[I * D + c] = run;
+        }
+        if (tid < 64) bet[tid] = R.beta;
+        {
+            const int it_next = it + gridDim.x;
+            if (it_next < total) {
+                ent = table[it_next / H];
+                load_local<D, F32IO>(R, q, k, dO, z, beta, ent.y, ent.z, it_next % H, H, tid);
             }
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int rr = 16 * I + 4 * lg + j, ii = 16 * J + ln;
-            const bool keep = isP ? ii <= rr : ii < rr;
-            dst[rr * kPS + ii] = keep ? acc[j] : 0.f;
-        }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // R to the record; Diag(beta) R in place, then T = (I + Diag(beta) R)^{-1}
-    for (int i = tid; i < 64 * 16; i += kBwdThreads) {
-        const int r = i >> 4, c = 4 * (i & 15);
-        const f32x4 x = rd4(Rs + r * kPS + c);
-        wr4(item + IT::r + r * 64 + c, x);
-        wr4(Rs + r * kPS + c, x * bet[r]);
-    }
-    __syncthreads();
-    // diagonal 16 x 16 blocks by forward substitution, one lane per column
-    if (wave < 4 && lane < 16) {
-        const int b = 16 * wave;
-        float col[16];
+        // Decayed Gram tiles (I, J), J <= I: R = (K.K) and P = (Q.K) with the
+        // per-channel factor exp2(G_r - G_i); R strictly lower, P lower.
+        for (int u = wave; u < 32; u += kBwdWaves) {
+            const bool isP = u >= 16;
+            const int I = (u & 15) >> 2, J = u & 3;
+            float *dst = isP ? Ps : Rs;
+            f32x4 acc = zero4();
+            if (J <= I) {
+                const float *src = isP ? Qs : Ks;
+                const int r = 16 * I + ln, i = 16 * J + ln, mid = 16 * I + 7;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float x = (r == lane) ? 1.f : 0.f;
+                for (int kk = 0; kk < KT; ++kk) {
+                    const int c = 16 * kk + 4 * lg;
+                    const f32x4 gr = rd4(Gb + r * PB + c), gi = rd4(Gb + i * PB + c);
+                    f32x4 fa, fb;
+                    if (I == J) {
+                        const f32x4 gm = rd4(Gb + mid * PB + c);
+                        fa = gr - gm;
+                        fb = gm - gi;
+                    } else {
+                        fa = gr;
+                        fb = span4<D>(bt, J, I, c) - gi;
+                    }
+                    acc = mma_f32_k16(rd4(src + r * PB + c) * exp2x4(fa), rd4(Ks + i * PB + c) * exp2x4(fb), acc);
+                }
+            }
 #pragma unroll
-            for (int i = 0; i < r; ++i) x -= Rs[(b + r) * kPS + b + i] * col[i];
-            col[r] = x;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Rs[(b + r) * kPS + b + lane] = col[r];
-    }
-    __syncthreads();
-    // blocks below the diagonal: T_IJ = -T_II sum_{J <= m < I} A_Im T_mJ
-    for (int I = 1; I < 4; ++I) {
-        f32x4 y = zero4();
-        if (wave < I) {
-            const int J = wave;
-            f32x4 x = zero4();
-            for (int m = J; m < I; ++m)
-                x = mma_f32_k16(rd4(Rs + (16 * I + ln) * kPS + 16 * m + 4 * lg),
-                                rdcol4(Rs + (16 * m + 4 * lg) * kPS + 16 * J + ln, kPS), x);
-            y = mma_f32_k16(rd4(Rs + (16 * I + ln) * kPS + 16 * I + 4 * lg), x, zero4());
+            for (int j = 0; j < 4; ++j) {
+                const int rr = 16 * I + 4 * lg + j, ii = 16 * J + ln;
+                const bool keep = isP ? ii <= rr : ii < rr;
+                dst[rr * kPS + ii] = keep ? acc[j] : 0.f;
+            }
         }
         __syncthreads();
-        if (wave < I) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) Rs[(16 * I + 4 * lg + j) * kPS + 16 * wave + ln] = -y[j];
+
+        // R to the record; Diag(beta) R in place, then T = (I + Diag(beta) R)^{-1}
+        for (int i = tid; i < 64 * 16; i += kBwdThreads) {
+            const int r = i >> 4, c = 4 * (i & 15);
+            const f32x4 x = rd4(Rs + r * kPS + c);
+            wr4(item + IT::r + r * 64 + c, x);
+            wr4(Rs + r * kPS + c, x * bet[r]);
         }
         __syncthreads();
-    }
-    for (int i = tid; i < 64 * 16; i += kBwdThreads) {
-        const int r = i >> 4, c = 4 * (i & 15);
-        wr4(item + IT::t + r * 64 + c, rd4(Rs + r * kPS + c));
-    }
-
-    // W = M (Gamma*K), stored transposed: tile (t block mt, channel block nt)
-    for (int u = wave; u < 4 * KT; u += kBwdWaves) {
-        const int mt = u / KT, nt = u % KT;
-        const int c = 16 * nt + ln;
-        f32x4 acc = zero4();
-        for (int kk = 0; kk <= mt; ++kk) {
-            const int s = 16 * kk + 4 * lg;
-            const f32x4 a = rd4(Rs + (16 * mt + ln) * kPS + s) * rd4(bet + s);
-            const f32x4 g = rdcol4(Gb + s * PB + c, PB) + splat4(span1<D>(bt, 0, kk, c));
-            acc = mma_f32_k16(a, rdcol4(Ks + s * PB + c, PB) * exp2x4(g), acc);
-        }
-        wr4(item + IT::wt + (size_t)c * 64 + 16 * mt + 4 * lg, acc);
-    }
-    // K~ = (gamma_C/Gamma)*K and gamma_C
-    for (int i = tid; i < 64 * (D / 4); i += kBwdThreads) {
-        const int r = i / (D / 4), c = 4 * (i % (D / 4));
-        const f32x4 e = span4<D>(bt, r >> 4, 4, c) - rd4(Gb + r * PB + c);
-        wr4(item + IT::kt + (size_t)r * D + c, rd4(Ks + r * PB + c) * exp2x4(e));
-    }
-    for (int c = tid; c < D; c += kBwdThreads) item[IT::gam + c] = fast_exp2(span1<D>(bt, 0, 4, c));
-    __syncthreads();
-
-    // dO replaces K
-    float *DOs = Ks;
-    stage_rows<D, F32IO>(DOs, dO, t0, L, h, H, tid);
-    __syncthreads();
-
-    // Y = (Gamma*Q)^T dO, key-major [c][v]: tile (key block mt, value block nt)
-    for (int u = wave; u < KT * KT; u += kBwdWaves) {
-        const int mt = u / KT, nt = u % KT;
-        const int c = 16 * mt + ln;
-        f32x4 acc = zero4();
+        // diagonal 16 x 16 blocks by forward substitution, one lane per column
+        if (wave < 4 && lane < 16) {
+            const int b = 16 * wave;
+            float col[16];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int t = 16 * kk + 4 * lg;
-            const f32x4 g = rdcol4(Gb + t * PB + c, PB) + splat4(span1<D>(bt, 0, kk, c));
-            acc = mma_f32_k16(rdcol4(Qs + t * PB + c, PB) * exp2x4(g), rdcol4(DOs + t * PB + 16 * nt + ln, PB),
-                              acc);
-        }
+            for (int r = 0; r < 16; ++r) {
+                float x = (r == lane) ? 1.f : 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) item[IT::ys + (size_t)(16 * mt + 4 * lg + j) * D + 16 * nt + ln] = acc[j];
-    }
-    // X = P^T dO, stored transposed: tile (row block mt, value block nt)
-    for (int u = wave; u < 4 * KT; u += kBwdWaves) {
-        const int mt = u / KT, nt = u % KT;
-        f32x4 acc = zero4();
-        for (int kk = mt; kk < 4; ++kk) {
-            const int t = 16 * kk + 4 * lg;
-            acc = mma_f32_k16(rdcol4(Ps + t * kPS + 16 * mt + ln, kPS), rdcol4(DOs + t * PB + 16 * nt + ln, PB),
-                              acc);
+                for (int i = 0; i < r; ++i) x -= Rs[(b + r) * kPS + b + i] * col[i];
+                col[r] = x;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Rs[(b + r) * kPS + b + lane] = col[r];
         }
-        wr4(item + IT::xv + (size_t)(16 * nt + ln) * 64 + 16 * mt + 4 * lg, acc);
+        __syncthreads();
+        // blocks below the diagonal: T_IJ = -T_II sum_{J <= m < I} A_Im T_mJ
+        for (int I = 1; I < 4; ++I) {
+            f32x4 y = zero4();
+            if (wave < I) {
+                const int J = wave;
+                f32x4 x = zero4();
+                for (int m = J; m < I; ++m)
+                    x = mma_f32_k16(rd4(Rs + (16 * I + ln) * kPS + 16 * m + 4 * lg),
+                                    rdcol4(Rs + (16 * m + 4 * lg) * kPS + 16 * J + ln, kPS), x);
+                y = mma_f32_k16(rd4(Rs + (16 * I + ln) * kPS + 16 * I + 4 * lg), x, zero4());
+            }
+            __syncthreads();
+            if (wave < I) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Rs[(16 * I + 4 * lg + j) * kPS + 16 * wave + ln] = -y[j];
+            }
+            __syncthreads();
+        }
+        for (int i = tid; i < 64 * 16; i += kBwdThreads) {
+            const int r = i >> 4, c = 4 * (i & 15);
+            wr4(item + IT::t + r * 64 + c, rd4(Rs + r * kPS + c));
+        }
+
+        // W = M (Gamma*K), stored transposed: tile (t block mt, channel block nt)
+        for (int u = wave; u < 4 * KT; u += kBwdWaves) {
+            const int mt = u / KT, nt = u % KT;
+            const int c = 16 * nt + ln;
+            f32x4 acc = zero4();
+            for (int kk = 0; kk <= mt; ++kk) {
+                const int s = 16 * kk + 4 * lg;
+                const f32x4 a = rd4(Rs + (16 * mt + ln) * kPS + s) * rd4(bet + s);
+                const f32x4 g = rdcol4(Gb + s * PB + c, PB) + splat4(span1<D>(bt, 0, kk, c));
+                acc = mma_f32_k16(a, rdcol4(Ks + s * PB + c, PB) * exp2x4(g), acc);
+            }
+            wr4(item + IT::wt + (size_t)c * 64 + 16 * mt + 4 * lg, acc);
+        }
+        // K~ = (gamma_C/Gamma)*K and gamma_C
+        for (int i = tid; i < 64 * (D / 4); i += kBwdThreads) {
+            const int r = i / (D / 4), c = 4 * (i % (D / 4));
+            const f32x4 e = span4<D>(bt, r >> 4, 4, c) - rd4(Gb + r * PB + c);
+            wr4(item + IT::kt + (size_t)r * D + c, rd4(Ks + r * PB + c) * exp2x4(e));
+        }
+        for (int c = tid; c < D; c += kBwdThreads) item[IT::gam + c] = fast_exp2(span1<D>(bt, 0, 4, c));
+        __syncthreads();
+
+        // dO replaces K
+        float *DOs = Ks;
+        stage_quads<D, F32IO>(DOs, ocur, tid);
+        __syncthreads();
+
+        // Y = (Gamma*Q)^T dO, key-major [c][v]: tile (key block mt, value block nt)
+        for (int u = wave; u < KT * KT; u += kBwdWaves) {
+            const int mt = u / KT, nt = u % KT;
+            const int c = 16 * mt + ln;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int t = 16 * kk + 4 * lg;
+                const f32x4 g = rdcol4(Gb + t * PB + c, PB) + splat4(span1<D>(bt, 0, kk, c));
+                acc = mma_f32_k16(rdcol4(Qs + t * PB + c, PB) * exp2x4(g), rdcol4(DOs + t * PB + 16 * nt + ln, PB),
+                                  acc);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) item[IT::ys + (size_t)(16 * mt + 4 * lg + j) * D + 16 * nt + ln] = acc[j];
+        }
+        // X = P^T dO, stored transposed: tile (row block mt, value block nt)
+        for (int u = wave; u < 4 * KT; u += kBwdWaves) {
+            const int mt = u / KT, nt = u % KT;
+            f32x4 acc = zero4();
+            for (int kk = mt; kk < 4; ++kk) {
+                const int t = 16 * kk + 4 * lg;
+                acc = mma_f32_k16(rdcol4(Ps + t * kPS + 16 * mt + ln, kPS), rdcol4(DOs + t * PB + 16 * nt + ln, PB),
+                                  acc);
+            }
+            wr4(item + IT::xv + (size_t)(16 * nt + ln) * 64 + 16 * mt + 4 * lg, acc);
+        }
+        __syncthreads();   // LDS is restaged for the next item
     }
 }
 
@@ -963,7 +1053,8 @@ int launch_backward_t(const BackwardArgs &a) {
     if (blocks > 0) {
         const size_t lds = sizeof(float) * LocalLds<D>::floats;
         if (!set_lds(&bwd_local_kernel<D, F32IO>, lds)) return -1;
-        hipLaunchKernelGGL((bwd_local_kernel<D, F32IO>), dim3((unsigned)blocks), dim3(kBwdThreads), lds, a.stream,
+        const unsigned grid = (unsigned)std::min<long long>(blocks, (long long)device_cus());
+        hipLaunchKernelGGL((bwd_local_kernel<D, F32IO>), dim3(grid), dim3(kBwdThreads), lds, a.stream,
                            a.q, a.k, a.z, a.A, a.beta, a.dO, meta, table, a.N, a.H, max_chunks, items);
         if (hipGetLastError() != hipSuccess) return -1;
     }
