@@ -208,11 +208,20 @@ __device__ __forceinline__ void stage_quads(float *dst, const typename LocalIn<D
 }
 
 // LDS carve-up of the two per-item kernels (floats).
+// Local kernel: q, k and the block log-decays Gb are staged first, then
+// turned into block-referenced operands in place (qA = q 2^Gb and kA = k 2^Gb
+// over q and k, kB = k 2^(bt - Gb) over Gb), with per-channel factor vectors
+// [I][D]: pre = 2^(sum_{m<I} bt_m), suf = 2^(sum_{m>I} bt_m), off[J][I] =
+// 2^(sum_{J<m<I} bt_m), dgA = 2^-Gb_mid(I), dgB = 2^(Gb_mid(I) - bt_I), where
+// mid(I) is block I's row 7.  Every decay factor of the products below is one
+// operand times one of these vectors.
 template <int D>
 struct LocalLds {
     static constexpr int PB = D + 4;
     static constexpr int q = 0, k = q + 64 * PB, gb = k + 64 * PB, r = gb + 64 * PB, p = r + 64 * kPS;
-    static constexpr int beta = p + 64 * kPS, bt = beta + 64, floats = bt + 4 * D;
+    static constexpr int beta = p + 64 * kPS, bt = beta + 64, gmid = bt + 4 * D;
+    static constexpr int pre = gmid + 4 * D, suf = pre + 4 * D, off = suf + 4 * D, dga = off + 16 * D;
+    static constexpr int dgb = dga + 4 * D, floats = dgb + 4 * D;
 };
 template <int D>
 struct GradLds {
@@ -237,7 +246,10 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_local_kernel(
     constexpr int PB = D + 4, KT = D / 16;
     extern __shared__ __attribute__((aligned(16))) float lds[];
     float *Qs = lds + SL::q, *Ks = lds + SL::k, *Gb = lds + SL::gb, *Rs = lds + SL::r, *Ps = lds + SL::p;
-    float *bet = lds + SL::beta, *bt = lds + SL::bt;
+    float *bet = lds + SL::beta, *bt = lds + SL::bt, *gmid = lds + SL::gmid;
+    float *fpre = lds + SL::pre, *fsuf = lds + SL::suf, *foff = lds + SL::off, *fdga = lds + SL::dga,
+          *fdgb = lds + SL::dgb;
+    float *kB = Gb;   // after the operand pass
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
     using LI = LocalIn<D, F32IO>;
     const int total = meta[N] * H;
@@ -269,6 +281,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_local_kernel(
                 const int r = 16 * I + i;
                 run += r < L ? gate_log2(ea, R.z[i]) : 0.f;
                 Gb[r * (D + 4) + c] = run;
+                if (i == 7) gmid[I * D + c] = run;
             }
             bt[I * D + c] = run;
         }
@@ -282,8 +295,45 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_local_kernel(
         }
         __syncthreads();
 
+        // factor vectors, and the operands qA, kA (in place) and kB (over Gb)
+        for (int c = tid; c < D; c += kBwdThreads) {
+            const float b0 = bt[c], b1 = bt[D + c], b2 = bt[2 * D + c], b3 = bt[3 * D + c];
+            fpre[c] = 1.f;
+            fpre[D + c] = fast_exp2(b0);
+            fpre[2 * D + c] = fast_exp2(b0 + b1);
+            fpre[3 * D + c] = fast_exp2(b0 + b1 + b2);
+            fsuf[c] = fast_exp2(b1 + b2 + b3);
+            fsuf[D + c] = fast_exp2(b2 + b3);
+            fsuf[2 * D + c] = fast_exp2(b3);
+            fsuf[3 * D + c] = 1.f;
+            foff[(0 * 4 + 1) * D + c] = 1.f;
+            foff[(0 * 4 + 2) * D + c] = fast_exp2(b1);
+            foff[(0 * 4 + 3) * D + c] = fast_exp2(b1 + b2);
+            foff[(1 * 4 + 2) * D + c] = 1.f;
+            foff[(1 * 4 + 3) * D + c] = fast_exp2(b2);
+            foff[(2 * 4 + 3) * D + c] = 1.f;
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const float gm = gmid[I * D + c];
+                fdga[I * D + c] = fast_exp2(-gm);
+                fdgb[I * D + c] = fast_exp2(gm - bt[I * D + c]);
+            }
+        }
+        for (int i = tid; i < 64 * (D / 4); i += kBwdThreads) {
+            const int r = i / (D / 4), c = 4 * (i % (D / 4));
+            const f32x4 g = rd4(Gb + r * PB + c);
+            const f32x4 ea4 = exp2x4(g), eb4 = exp2x4(rd4(bt + (r >> 4) * D + c) - g);
+            const f32x4 kv = rd4(Ks + r * PB + c);
+            wr4(Qs + r * PB + c, rd4(Qs + r * PB + c) * ea4);
+            wr4(Ks + r * PB + c, kv * ea4);
+            wr4(kB + r * PB + c, kv * eb4);
+        }
+        __syncthreads();
+
         // Decayed Gram tiles (I, J), J <= I: R = (K.K) and P = (Q.K) with the
         // per-channel factor exp2(G_r - G_i); R strictly lower, P lower.
+        //   J < I:  qA/kA_r . kB_i off[J][I]
+        //   J = I:  qA/kA_r dgA[I] . kB_i dgB[I]   (halves <= e^40)
         for (int u = wave; u < 32; u += kBwdWaves) {
             const bool isP = u >= 16;
             const int I = (u & 15) >> 2, J = u & 3;
@@ -291,21 +341,15 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_local_kernel(
             f32x4 acc = zero4();
             if (J <= I) {
                 const float *src = isP ? Qs : Ks;
-                const int r = 16 * I + ln, i = 16 * J + ln, mid = 16 * I + 7;
+                const int r = 16 * I + ln, i = 16 * J + ln;
+                const float *fa = I == J ? fdga + I * D : nullptr;
+                const float *fb = I == J ? fdgb + I * D : foff + (J * 4 + I) * D;
 #pragma unroll
                 for (int kk = 0; kk < KT; ++kk) {
                     const int c = 16 * kk + 4 * lg;
-                    const f32x4 gr = rd4(Gb + r * PB + c), gi = rd4(Gb + i * PB + c);
-                    f32x4 fa, fb;
-                    if (I == J) {
-                        const f32x4 gm = rd4(Gb + mid * PB + c);
-                        fa = gr - gm;
-                        fb = gm - gi;
-                    } else {
-                        fa = gr;
-                        fb = span4<D>(bt, J, I, c) - gi;
-                    }
-                    acc = mma_f32_k16(rd4(src + r * PB + c) * exp2x4(fa), rd4(Ks + i * PB + c) * exp2x4(fb), acc);
+                    f32x4 av = rd4(src + r * PB + c);
+                    if (I == J) av *= rd4(fa + c);
+                    acc = mma_f32_k16(av, rd4(kB + i * PB + c) * rd4(fb + c), acc);
                 }
             }
 #pragma unroll
@@ -371,16 +415,14 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_local_kernel(
             for (int kk = 0; kk <= mt; ++kk) {
                 const int s = 16 * kk + 4 * lg;
                 const f32x4 a = rd4(Rs + (16 * mt + ln) * kPS + s) * rd4(bet + s);
-                const f32x4 g = rdcol4(Gb + s * PB + c, PB) + splat4(span1<D>(bt, 0, kk, c));
-                acc = mma_f32_k16(a, rdcol4(Ks + s * PB + c, PB) * exp2x4(g), acc);
+                acc = mma_f32_k16(a, rdcol4(Ks + s * PB + c, PB) * fpre[kk * D + c], acc);
             }
             wr4(item + IT::wt + (size_t)c * 64 + 16 * mt + 4 * lg, acc);
         }
         // K~ = (gamma_C/Gamma)*K and gamma_C
         for (int i = tid; i < 64 * (D / 4); i += kBwdThreads) {
             const int r = i / (D / 4), c = 4 * (i % (D / 4));
-            const f32x4 e = span4<D>(bt, r >> 4, 4, c) - rd4(Gb + r * PB + c);
-            wr4(item + IT::kt + (size_t)r * D + c, rd4(Ks + r * PB + c) * exp2x4(e));
+            wr4(item + IT::kt + (size_t)r * D + c, rd4(kB + r * PB + c) * rd4(fsuf + (r >> 4) * D + c));
         }
         for (int c = tid; c < D; c += kBwdThreads) item[IT::gam + c] = fast_exp2(span1<D>(bt, 0, 4, c));
         __syncthreads();
@@ -398,9 +440,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_local_kernel(
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const int t = 16 * kk + 4 * lg;
-                const f32x4 g = rdcol4(Gb + t * PB + c, PB) + splat4(span1<D>(bt, 0, kk, c));
-                acc = mma_f32_k16(rdcol4(Qs + t * PB + c, PB) * exp2x4(g), rdcol4(DOs + t * PB + 16 * nt + ln, PB),
-                                  acc);
+                acc = mma_f32_k16(rdcol4(Qs + t * PB + c, PB) * fpre[kk * D + c],
+                                  rdcol4(DOs + t * PB + 16 * nt + ln, PB), acc);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) item[IT::ys + (size_t)(16 * mt + 4 * lg + j) * D + 16 * nt + ln] = acc[j];
