@@ -993,8 +993,14 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
     // (gKt_r = k_r dK~_r: the factor gamma_C / Gamma_r depends on the gates of
     // rows r + 1 .. C only, so it is summed forward, not as total - suffix)
     float dA_acc = 0.f;
+    float zr[16];   // this thread's gate logits, fetched before the block sums
     if (tid < 4 * D) {
         const int c = tid % D, I = tid / D;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = 16 * I + i;
+            zr[i] = r < L ? z[((size_t)(t0 + r) * H + h) * D + c] : 0.f;
+        }
         float s = 0.f, st = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -1027,9 +1033,9 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
                 const size_t o = ((size_t)(t0 + r) * H + h) * D + c;
                 // sigmoid'(x) = e / (1 + e)^2 with e = exp(-|x|): no cancellation
                 // where the gate saturates
-                const float x = ea * z[o];
-                const float ex = expf(-fabsf(x));
-                const float dx = dg * -5.0f * ex / ((1.f + ex) * (1.f + ex));
+                const float x = ea * zr[i];
+                const float ex = fast_exp2(-fabsf(x) * kLog2e);
+                const float dx = dg * -5.0f * ex * __builtin_amdgcn_rcpf((1.f + ex) * (1.f + ex));
                 gz[o] = dx * ea;
                 dA_acc += dx * x;
             }
