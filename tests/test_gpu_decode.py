@@ -31,6 +31,13 @@ def test_decode_small(io, d):
     assert rel_l2(S, rS) <= 1e-6, rel_l2(S, rS)
 
 
+def test_decode_empty_batch():
+    """N = 0: accepted, nothing launched."""
+    inp = W.random_decode(0, 3, 64, "bf16", 0.05, seed=5)
+    o, S, ro, rS = _run(inp)
+    assert o.shape[0] == 0 and S.shape[0] == 0 and ro.shape[0] == 0
+
+
 def test_decode_k3_full_shape():
     """256 sequences x 96 heads x 128 x 128, the batched decode workload."""
     inp = W.make("k3_decode")

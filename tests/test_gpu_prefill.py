@@ -64,6 +64,24 @@ def test_no_h0_no_hT():
     assert rel_l2(host(o), ro) <= BF16_TOL
 
 
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [32, 128])
+def test_empty_sequences_and_batch(io, d):
+    """No tokens: every sequence empty leaves its state as it came in (hT
+    equals h0 bit for bit, or zero without h0), and an empty batch (N = 0,
+    T = 0) is accepted and does nothing."""
+    print("empty", io, d, flush=True)
+    for lens, h0_std in (([0, 0, 0], 0.05), ([0, 0], None), ([], None)):
+        inp = W.random_prefill(lens, 2, d, io, h0_std=h0_std, seed=12)
+        g = to_gpu(inp)
+        o, hT = gpu_prefill(g)
+        assert o.shape == (0, 2, d) and hT.shape == (len(lens), 2, d, d)
+        want = g["h0"] if h0_std is not None else torch.zeros_like(hT)
+        assert torch.equal(hT, want), lens
+        _, rh = oracle_prefill(inp)
+        assert np.array_equal(host(hT), rh), lens
+
+
 def test_hT_may_alias_h0():
     inp = W.random_prefill([100, 70], 2, 128, "bf16", h0_std=0.1, seed=9)
     g = to_gpu(inp)
