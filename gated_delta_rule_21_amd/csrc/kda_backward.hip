@@ -825,34 +825,55 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
             if (s == r) pd[r] = acc[j];
         }
     }
+    static_assert((4 * KT) % kBwdWaves == 0, "every wave has NU tiles");
     f32x4 dq[NU], dkg[NU], dkt[NU], dki[NU];
-    // B fragments of S for this wave's key columns (every tile of a wave has
-    // the same column block, wave % KT): S_cv for c = 16 ct + ln, v = 16 kk + 4 lg + j
+#pragma unroll
+    for (int i = 0; i < NU; ++i) dq[i] = dkg[i] = dkt[i] = dki[i] = zero4();
+    // Every tile of a wave has the same key-column block ct = wave % KT; its
+    // row blocks are (wave + i kBwdWaves) / KT.  The loop runs over pairs of
+    // value tiles (kp) outside the wave's tiles, so the S and dS' fragments of
+    // a pair are loaded, and on the bf16 path split into bf16 hi + lo, once
+    // for all of them.
+    const int ct = wave % KT, c = 16 * ct + ln;
+    // B fragments of S: S_cv for c = 16 ct + ln, v = 16 kk + 4 lg + j
     f32x4 sfr[KT];
-    {
-        const int c = 16 * (wave % KT) + ln;
 #pragma unroll
-        for (int kk = 0; kk < KT; ++kk) sfr[kk] = Sg ? rdcol4(Sg + (size_t)(16 * kk + 4 * lg) * D + c, D) : zero4();
-    }
+    for (int kk = 0; kk < KT; ++kk) sfr[kk] = Sg ? rdcol4(Sg + (size_t)(16 * kk + 4 * lg) * D + c, D) : zero4();
+    float gc = 0.f;   // dgC_c = sum_v dS'_cv S_cv
+    auto products = [&](auto has_state) {
+        constexpr bool HS = decltype(has_state)::value;
 #pragma unroll
-    for (int i = 0; i < NU; ++i) {
-        const int u = wave + i * kBwdWaves;
-        dq[i] = dkg[i] = dkt[i] = dki[i] = zero4();
-        if (u < 4 * KT) {
-            const int rb = u / KT, ct = u % KT;
-            const int r = 16 * rb + ln, c = 16 * ct + ln;
-            const bool rok = r < L;
-            float gc = 0.f;   // dgC_c = sum_v dS'_cv S_cv, from the row-block-0 tiles
-            const size_t orow = ((size_t)(t0 + r) * H + h) * D;
+        for (int kp = 0; kp < KT / 2; ++kp) {
+            const int v0 = 32 * kp + 4 * lg, v1 = v0 + 16;
+            const f32x4 ds0 = rd4(dsp + (size_t)c * D + v0), ds1 = rd4(dsp + (size_t)c * D + v1);
+            const f32x4 s0 = sfr[2 * kp], s1 = sfr[2 * kp + 1];
+            u32x4 dsh, dsl, sh, sl;
+            if constexpr (!F32IO) {
+                quads_to_bf16_split(ds0, ds1, dsh, dsl);
+                if constexpr (HS) quads_to_bf16_split(s0, s1, sh, sl);
+            }
+            if constexpr (HS) {
+                gc += s0[0] * ds0[0] + s0[1] * ds0[1] + s0[2] * ds0[2] + s0[3] * ds0[3];
+                gc += s1[0] * ds1[0] + s1[1] * ds1[1] + s1[2] * ds1[2] + s1[3] * ds1[3];
+            }
 #pragma unroll
-            for (int kp = 0; kp < KT / 2; ++kp) {
-                const int v0 = 32 * kp + 4 * lg, v1 = v0 + 16;
-                const f32x4 ds0 = rd4(dsp + (size_t)c * D + v0), ds1 = rd4(dsp + (size_t)c * D + v1);
-                if (Sg) {
-                    const f32x4 s0 = sfr[2 * kp], s1 = sfr[2 * kp + 1];
+            for (int i = 0; i < NU; ++i) {
+                const int r = 16 * ((wave + i * kBwdWaves) / KT) + ln;
+                const bool rok = r < L;
+                const size_t orow = ((size_t)(t0 + r) * H + h) * D;
+                const f32x4 x0 = rd4(Xs + r * PB + v0), x1 = rd4(Xs + r * PB + v1);
+                if constexpr (F32IO) {
+                    dkt[i] = mma_k32<true>(x0, x1, ds0, ds1, dkt[i]);
+                } else {
+                    u32x4 xh, xl;
+                    quads_to_bf16_split(x0, x1, xh, xl);
+                    dkt[i] = mma3_bf16(xh, xl, dsh, dsl, dkt[i]);
+                }
+                if constexpr (HS) {
                     const f32x4 z0 = rok ? rd4(gv + orow + v0) : zero4(), z1 = rok ? rd4(gv + orow + v1) : zero4();
                     if constexpr (F32IO) {
                         dq[i] = mma_k32<true>(row_io(dO, r, v0), row_io(dO, r, v1), s0, s1, dq[i]);
+                        dkg[i] = mma_k32<true>(z0, z1, s0, s1, dkg[i]);
                     } else {
                         // dO is bf16 already: its hi part is exact and its lo part zero
                         u32x4 dh = u32x4{0u, 0u, 0u, 0u};
@@ -862,28 +883,32 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
                             const u32x2 w1 = *reinterpret_cast<const u32x2 *>(dp + v1);
                             dh = u32x4{w0[0], w0[1], w1[0], w1[1]};
                         }
-                        u32x4 sh, sl;
-                        quads_to_bf16_split(s0, s1, sh, sl);
                         dq[i] = mma_bf16_k32(dh, sh, dq[i]);
                         dq[i] = mma_bf16_k32(dh, sl, dq[i]);
+                        u32x4 zh, zl;
+                        quads_to_bf16_split(z0, z1, zh, zl);
+                        dkg[i] = mma3_bf16(zh, zl, sh, sl, dkg[i]);
                     }
-                    dkg[i] = mma_k32<F32IO>(z0, z1, s0, s1, dkg[i]);
-                    gc += s0[0] * ds0[0] + s0[1] * ds0[1] + s0[2] * ds0[2] + s0[3] * ds0[3];
-                    gc += s1[0] * ds1[0] + s1[1] * ds1[1] + s1[2] * ds1[2] + s1[3] * ds1[3];
                 }
-                dkt[i] = mma_k32<F32IO>(rd4(Xs + r * PB + v0), rd4(Xs + r * PB + v1), ds0, ds1, dkt[i]);
             }
-            if (rb == 0) {
-                gc += __shfl_xor(gc, 16);
-                gc += __shfl_xor(gc, 32);
-                if (lg == 0) dgc[c] = gc;
-            }
-            // lane (n = c, g) holds rows 16 rb + 4 lg + j
-            const f32x4 g = rdcol4(Gb + (16 * rb + 4 * lg) * PB + c, PB);
-            dq[i] *= exp2x4(g + splat4(span1<D>(bt, 0, rb, c)));
-            dkg[i] *= -exp2x4(g + splat4(span1<D>(bt, 0, rb, c)));
-            dkt[i] *= exp2x4(splat4(span1<D>(bt, rb, 4, c)) - g);
         }
+    };
+    if (Sg)
+        products(std::true_type{});
+    else
+        products(std::false_type{});
+    // the wave that holds row block 0 of column block ct
+    gc += __shfl_xor(gc, 16);
+    gc += __shfl_xor(gc, 32);
+    if (wave < KT && lg == 0) dgc[c] = gc;
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+        const int rb = (wave + i * kBwdWaves) / KT;
+        // lane (n = c, g) holds rows 16 rb + 4 lg + j
+        const f32x4 g = rdcol4(Gb + (16 * rb + 4 * lg) * PB + c, PB);
+        dq[i] *= exp2x4(g + splat4(span1<D>(bt, 0, rb, c)));
+        dkg[i] *= -exp2x4(g + splat4(span1<D>(bt, 0, rb, c)));
+        dkt[i] *= exp2x4(splat4(span1<D>(bt, rb, 4, c)) - g);
     }
     __syncthreads();
 
