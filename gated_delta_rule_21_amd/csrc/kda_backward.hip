@@ -31,7 +31,11 @@
 //   5. bwd_dA_kernel: the per-head sum of the chunks' A gradients, in a fixed
 //      order (the result does not depend on scheduling).
 //
-// Everything after the forward recompute runs in fp32 (fp32 16x16x4 MFMA).
+// Everything after the forward recompute accumulates in fp32.  fp32 inputs:
+// fp32 16x16x4 MFMA throughout.  bf16 inputs: the chain's two products, V~
+// and the products against S and dS' take both operands split into bf16
+// hi + lo (three 16x16x32 MFMAs, about 2^-16 relative per term); the rest
+// stays on fp32 MFMA.
 // Decay factors: a 64-token chunk can decay by e^-320, so no Gamma or 1/Gamma
 // over a chunk is formed where the quotient of two would be needed.  Log2
 // decays are kept relative to the start of each 16-token block (Gb) with the
@@ -481,7 +485,7 @@ struct ChainShape {
     static constexpr size_t lds_bytes = 2 * (size_t)buf * 4;
 };
 
-template <int D>
+template <int D, bool F32IO>
 __global__ void __launch_bounds__(ChainShape<D>::NT) bwd_chain_kernel(const int32_t *__restrict__ meta,
                                                                        const float *__restrict__ dhT,
                                                                        float *__restrict__ items, int N, int H,
@@ -555,23 +559,57 @@ __global__ void __launch_bounds__(ChainShape<D>::NT) bwd_chain_kernel(const int3
                 load_stage(rec(c - 1) + IT::kt);
                 fetch(rec(c - 1));
             }
-            f32x4 dv[4];
+            f32x4 dv[4], nd[KT];
+            if constexpr (F32IO) {
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                f32x4 acc = Xc[rt];
+                for (int rt = 0; rt < 4; ++rt) {
+                    f32x4 acc = Xc[rt];
 #pragma unroll
-                for (int kk = 0; kk < KT; ++kk)
-                    acc = mma_f32_k16(rd4(Kt + (16 * rt + ln) * PB + 16 * kk + 4 * lg), dS[kk], acc);
-                dv[rt] = acc;
-            }
-            f32x4 nd[KT];
+                    for (int kk = 0; kk < KT; ++kk)
+                        acc = mma_f32_k16(rd4(Kt + (16 * rt + ln) * PB + 16 * kk + 4 * lg), dS[kk], acc);
+                    dv[rt] = acc;
+                }
 #pragma unroll
-            for (int rc = 0; rc < KT; ++rc) {
-                f32x4 acc = Yc[rc] + Gc[rc] * dS[rc];
+                for (int rc = 0; rc < KT; ++rc) {
+                    f32x4 acc = Yc[rc] + Gc[rc] * dS[rc];
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt)
-                    acc = mma_f32_k16(rd4(Wt + (16 * rc + ln) * kPS + 16 * kt + 4 * lg), -dv[kt], acc);
-                nd[rc] = acc;
+                    for (int kt = 0; kt < 4; ++kt)
+                        acc = mma_f32_k16(rd4(Wt + (16 * rc + ln) * kPS + 16 * kt + 4 * lg), -dv[kt], acc);
+                    nd[rc] = acc;
+                }
+            } else {
+                // bf16 path: both operands of each product split into bf16
+                // hi + lo (three 16x16x32 MFMAs per pair of K16 tiles)
+                u32x4 sh[KT / 2], sl[KT / 2];
+#pragma unroll
+                for (int kp = 0; kp < KT / 2; ++kp) quads_to_bf16_split(dS[2 * kp], dS[2 * kp + 1], sh[kp], sl[kp]);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    f32x4 acc = Xc[rt];
+                    const float *kr = Kt + (16 * rt + ln) * PB + 4 * lg;
+#pragma unroll
+                    for (int kp = 0; kp < KT / 2; ++kp) {
+                        u32x4 ah, al;
+                        quads_to_bf16_split(rd4(kr + 32 * kp), rd4(kr + 32 * kp + 16), ah, al);
+                        acc = mma3_bf16(ah, al, sh[kp], sl[kp], acc);
+                    }
+                    dv[rt] = acc;
+                }
+                u32x4 vh[2], vl[2];
+#pragma unroll
+                for (int kp = 0; kp < 2; ++kp) quads_to_bf16_split(-dv[2 * kp], -dv[2 * kp + 1], vh[kp], vl[kp]);
+#pragma unroll
+                for (int rc = 0; rc < KT; ++rc) {
+                    f32x4 acc = Yc[rc] + Gc[rc] * dS[rc];
+                    const float *wr = Wt + (16 * rc + ln) * kPS + 4 * lg;
+#pragma unroll
+                    for (int kp = 0; kp < 2; ++kp) {
+                        u32x4 ah, al;
+                        quads_to_bf16_split(rd4(wr + 32 * kp), rd4(wr + 32 * kp + 16), ah, al);
+                        acc = mma3_bf16(ah, al, vh[kp], vl[kp], acc);
+                    }
+                    nd[rc] = acc;
+                }
             }
             float *it = rec(c);
             // dS' over Y (the same lanes read and write the same addresses),
@@ -1133,8 +1171,8 @@ int launch_backward_t(const BackwardArgs &a) {
     if (a.N > 0) {
         using SH = ChainShape<D>;
         const int groups = SH::KT / SH::NW;
-        if (!set_lds(&bwd_chain_kernel<D>, SH::lds_bytes)) return -1;
-        hipLaunchKernelGGL((bwd_chain_kernel<D>), dim3(a.N * a.H * groups), dim3(SH::NT), SH::lds_bytes, a.stream,
+        if (!set_lds(&bwd_chain_kernel<D, F32IO>, SH::lds_bytes)) return -1;
+        hipLaunchKernelGGL((bwd_chain_kernel<D, F32IO>), dim3(a.N * a.H * groups), dim3(SH::NT), SH::lds_bytes, a.stream,
                            meta, a.dhT, items, a.N, a.H, max_chunks, groups, a.gh0);
         if (hipGetLastError() != hipSuccess) return -1;
     }
