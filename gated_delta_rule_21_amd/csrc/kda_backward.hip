@@ -227,6 +227,21 @@ struct LocalLds {
     static constexpr int pre = gmid + 4 * D, suf = pre + 4 * D, off = suf + 4 * D, dga = off + 16 * D;
     static constexpr int dgb = dga + 4 * D, floats = dgb + 4 * D;
 };
+
+// The bf16 path stores K~ and W^T as split bf16 A fragments of the chain's
+// products: fragment f of a region is 2 KiB, 64 lanes x 16 B of bf16 hi
+// parts, then 64 x 16 B of lo parts, each lane's 16 B holding K16 tiles 2p
+// (bytes 0-7) and 2p + 1 (bytes 8-15) of its K32 pair in the layout of
+// quads_to_bf16_split.  This writes one tile's half of a lane's slots.
+__device__ __forceinline__ void store_split_half(float *region, int f, int half, int lane, f32x4 x) {
+    const u32x2 hi = {f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3])};
+    const f32x4 r = x - f32x4{bf16_lo_half(hi[0]), bf16_hi_half(hi[0]), bf16_lo_half(hi[1]), bf16_hi_half(hi[1])};
+    const u32x2 lo = {f32x2_to_bf16x2(r[0], r[1]), f32x2_to_bf16x2(r[2], r[3])};
+    unsigned char *p = reinterpret_cast<unsigned char *>(region) + (size_t)f * 2048 + lane * 16 + half * 8;
+    *reinterpret_cast<u32x2 *>(p) = hi;
+    *reinterpret_cast<u32x2 *>(p + 1024) = lo;
+}
+
 template <int D>
 struct GradLds {
     static constexpr int PB = D + 4;
@@ -267,7 +282,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_local_kernel(
     // load into R while this one computes
     for (; it < total; it += gridDim.x) {
         const int chunk = it / H, h = it % H;
-        const int t0 = ent.y, L = ent.z;
+        const int L = ent.z;
         float *item = items + ((size_t)h * max_chunks + chunk) * IT::floats;
         const float ea = __expf(A[h]);
 
@@ -421,12 +436,20 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_local_kernel(
                 const f32x4 a = rd4(Rs + (16 * mt + ln) * kPS + s) * rd4(bet + s);
                 acc = mma_f32_k16(a, rdcol4(Ks + s * PB + c, PB) * fpre[kk * D + c], acc);
             }
-            wr4(item + IT::wt + (size_t)c * 64 + 16 * mt + 4 * lg, acc);
+            if constexpr (F32IO)
+                wr4(item + IT::wt + (size_t)c * 64 + 16 * mt + 4 * lg, acc);
+            else   // lane (n, g) holds W^T[16 nt + n][16 mt + 4 g + j]: A operand of W^T (-dV')
+                store_split_half(item + IT::wt, nt * 2 + (mt >> 1), mt & 1, lane, acc);
         }
         // K~ = (gamma_C/Gamma)*K and gamma_C
         for (int i = tid; i < 64 * (D / 4); i += kBwdThreads) {
             const int r = i / (D / 4), c = 4 * (i % (D / 4));
-            wr4(item + IT::kt + (size_t)r * D + c, rd4(kB + r * PB + c) * rd4(fsuf + (r >> 4) * D + c));
+            const f32x4 x = rd4(kB + r * PB + c) * rd4(fsuf + (r >> 4) * D + c);
+            if constexpr (F32IO)
+                wr4(item + IT::kt + (size_t)r * D + c, x);
+            else   // A operand of K~ dS: row r = 16 rt + m, key c = 32 kp + 16 half + 4 g
+                store_split_half(item + IT::kt, (r >> 4) * (D / 32) + (c >> 5), (c >> 4) & 1, (r & 15) + 16 * ((c & 15) >> 2),
+                                 x);
         }
         for (int c = tid; c < D; c += kBwdThreads) item[IT::gam + c] = fast_exp2(span1<D>(bt, 0, 4, c));
         __syncthreads();
@@ -481,7 +504,8 @@ struct ChainShape {
     static constexpr int NT = 64 * NW;
     static constexpr int PB = D + 4;
     static constexpr int buf = 64 * PB + D * kPS;  // floats per buffer: K~ then W^T
-    static constexpr int NS = 2 * 64 * D / 4 / NT; // float4 per thread per stage
+    static constexpr int NS = 2 * 64 * D / 4 / NT; // float4 per thread per stage (fp32 path)
+    static constexpr int NF = 2 * 64 * D * 4 / 1024; // 1 KiB pieces of [K~ | W^T] (bf16 path)
     static constexpr size_t lds_bytes = 2 * (size_t)buf * 4;
 };
 
@@ -509,7 +533,17 @@ __global__ void __launch_bounds__(ChainShape<D>::NT) bwd_chain_kernel(const int3
 #pragma unroll
     for (int rc = 0; rc < KT; ++rc) dS[rc] = dhT ? rd4(dhT + sb + 16 * rc) : zero4();
 
-    f32x4 st[NS];
+    // fp32 path: [K~ | W^T] fp32 rows through registers into padded LDS rows.
+    // bf16 path: split bf16 fragments, copied straight into LDS, 1 KiB per
+    // wave instruction.
+    f32x4 st[F32IO ? NS : 1];
+    auto copy_stage = [&](const float *src, float *dst) {
+        const unsigned char *s8 = reinterpret_cast<const unsigned char *>(src);
+        unsigned char *d8 = reinterpret_cast<unsigned char *>(dst);
+        for (int f = wave; f < SH::NF; f += SH::NW)
+            __builtin_amdgcn_global_load_lds(s8 + (size_t)f * 1024 + lane * 16,
+                                             (__attribute__((address_space(3))) void *)(d8 + f * 1024), 16, 0, 0);
+    };
     auto load_stage = [&](const float *src) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) st[s] = rd4(src + 4 * (tid + s * SH::NT));
@@ -539,9 +573,14 @@ __global__ void __launch_bounds__(ChainShape<D>::NT) bwd_chain_kernel(const int3
     };
 
     if (c_end > c_begin) {
-        load_stage(rec(c_end - 1) + IT::kt);
-        store_stage(lds);
+        if constexpr (F32IO) {
+            load_stage(rec(c_end - 1) + IT::kt);
+            store_stage(lds);
+        } else {
+            copy_stage(rec(c_end - 1) + IT::kt, lds);
+        }
         fetch(rec(c_end - 1));
+        __builtin_amdgcn_s_waitcnt(0);   // the direct copies have landed
         __syncthreads();
         int b = 0;
         for (int c = c_end - 1; c >= c_begin; --c, b ^= 1) {
@@ -556,7 +595,10 @@ __global__ void __launch_bounds__(ChainShape<D>::NT) bwd_chain_kernel(const int3
                 Gc[rc] = G[rc];
             }
             if (more) {
-                load_stage(rec(c - 1) + IT::kt);
+                if constexpr (F32IO)
+                    load_stage(rec(c - 1) + IT::kt);
+                else
+                    copy_stage(rec(c - 1) + IT::kt, lds + (b ^ 1) * SH::buf);
                 fetch(rec(c - 1));
             }
             f32x4 dv[4], nd[KT];
@@ -579,18 +621,23 @@ __global__ void __launch_bounds__(ChainShape<D>::NT) bwd_chain_kernel(const int3
                 }
             } else {
                 // bf16 path: both operands of each product split into bf16
-                // hi + lo (three 16x16x32 MFMAs per pair of K16 tiles)
+                // hi + lo (three 16x16x32 MFMAs per pair of K16 tiles); K~ and
+                // W^T arrive split, as fragments f = 2 KiB pieces of the buffer
+                const unsigned char *fb = reinterpret_cast<const unsigned char *>(Kt);
+                auto afrag = [&](int f, u32x4 &hi, u32x4 &lo) {
+                    hi = *reinterpret_cast<const u32x4 *>(fb + (size_t)f * 2048 + lane * 16);
+                    lo = *reinterpret_cast<const u32x4 *>(fb + (size_t)f * 2048 + 1024 + lane * 16);
+                };
                 u32x4 sh[KT / 2], sl[KT / 2];
 #pragma unroll
                 for (int kp = 0; kp < KT / 2; ++kp) quads_to_bf16_split(dS[2 * kp], dS[2 * kp + 1], sh[kp], sl[kp]);
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
                     f32x4 acc = Xc[rt];
-                    const float *kr = Kt + (16 * rt + ln) * PB + 4 * lg;
 #pragma unroll
                     for (int kp = 0; kp < KT / 2; ++kp) {
                         u32x4 ah, al;
-                        quads_to_bf16_split(rd4(kr + 32 * kp), rd4(kr + 32 * kp + 16), ah, al);
+                        afrag(rt * (KT / 2) + kp, ah, al);
                         acc = mma3_bf16(ah, al, sh[kp], sl[kp], acc);
                     }
                     dv[rt] = acc;
@@ -601,11 +648,10 @@ __global__ void __launch_bounds__(ChainShape<D>::NT) bwd_chain_kernel(const int3
 #pragma unroll
                 for (int rc = 0; rc < KT; ++rc) {
                     f32x4 acc = Yc[rc] + Gc[rc] * dS[rc];
-                    const float *wr = Wt + (16 * rc + ln) * kPS + 4 * lg;
 #pragma unroll
                     for (int kp = 0; kp < 2; ++kp) {
                         u32x4 ah, al;
-                        quads_to_bf16_split(rd4(wr + 32 * kp), rd4(wr + 32 * kp + 16), ah, al);
+                        afrag(2 * KT + rc * 2 + kp, ah, al);
                         acc = mma3_bf16(ah, al, vh[kp], vl[kp], acc);
                     }
                     nd[rc] = acc;
@@ -627,7 +673,11 @@ __global__ void __launch_bounds__(ChainShape<D>::NT) bwd_chain_kernel(const int3
             }
 #pragma unroll
             for (int rc = 0; rc < KT; ++rc) dS[rc] = nd[rc];
-            if (more) store_stage(lds + (b ^ 1) * SH::buf);
+            if constexpr (F32IO) {
+                if (more) store_stage(lds + (b ^ 1) * SH::buf);
+            } else {
+                __builtin_amdgcn_s_waitcnt(0);   // the next chunk's direct copies have landed
+            }
             __syncthreads();
         }
     }
