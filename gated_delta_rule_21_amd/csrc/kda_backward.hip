@@ -102,6 +102,16 @@ __device__ __forceinline__ f32x4 mma_k32(f32x4 a0, f32x4 a1, f32x4 b0, f32x4 b1,
     }
 }
 
+// The same for a B operand that holds bf16 values exactly (dO on the bf16
+// path): only A is split, two MFMAs.
+__device__ __forceinline__ f32x4 mma_k32_exact_b(f32x4 a0, f32x4 a1, f32x4 b0, f32x4 b1, f32x4 acc) {
+    u32x4 ah, al;
+    quads_to_bf16_split(a0, a1, ah, al);
+    const u32x4 bh = quads_to_bf16(b0, b1);
+    acc = mma_bf16_k32(ah, bh, acc);
+    return mma_bf16_k32(al, bh, acc);
+}
+
 // sum_{m = lo}^{hi - 1} bt[m][c] (zero when lo >= hi); bt is [4][D].
 template <int D>
 __device__ __forceinline__ f32x4 span4(const float *bt, int lo, int hi, int c) {
@@ -363,12 +373,17 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_local_kernel(
                 const int r = 16 * I + ln, i = 16 * J + ln;
                 const float *fa = I == J ? fdga + I * D : nullptr;
                 const float *fb = I == J ? fdgb + I * D : foff + (J * 4 + I) * D;
+                auto av = [&](int c) { return I == J ? rd4(src + r * PB + c) * rd4(fa + c) : rd4(src + r * PB + c); };
+                auto bv = [&](int c) { return rd4(kB + i * PB + c) * rd4(fb + c); };
+                if constexpr (F32IO) {
 #pragma unroll
-                for (int kk = 0; kk < KT; ++kk) {
-                    const int c = 16 * kk + 4 * lg;
-                    f32x4 av = rd4(src + r * PB + c);
-                    if (I == J) av *= rd4(fa + c);
-                    acc = mma_f32_k16(av, rd4(kB + i * PB + c) * rd4(fb + c), acc);
+                    for (int kk = 0; kk < KT; ++kk) acc = mma_f32_k16(av(16 * kk + 4 * lg), bv(16 * kk + 4 * lg), acc);
+                } else {
+#pragma unroll
+                    for (int kp = 0; kp < KT / 2; ++kp) {
+                        const int c0 = 32 * kp + 4 * lg, c1 = c0 + 16;
+                        acc = mma_k32<false>(av(c0), av(c1), bv(c0), bv(c1), acc);
+                    }
                 }
             }
 #pragma unroll
@@ -431,10 +446,18 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_local_kernel(
             const int mt = u / KT, nt = u % KT;
             const int c = 16 * nt + ln;
             f32x4 acc = zero4();
-            for (int kk = 0; kk <= mt; ++kk) {
+            auto av = [&](int kk) {
                 const int s = 16 * kk + 4 * lg;
-                const f32x4 a = rd4(Rs + (16 * mt + ln) * kPS + s) * rd4(bet + s);
-                acc = mma_f32_k16(a, rdcol4(Ks + s * PB + c, PB) * fpre[kk * D + c], acc);
+                return rd4(Rs + (16 * mt + ln) * kPS + s) * rd4(bet + s);
+            };
+            auto bv = [&](int kk) { return rdcol4(Ks + (16 * kk + 4 * lg) * PB + c, PB) * fpre[kk * D + c]; };
+            if constexpr (F32IO) {
+                for (int kk = 0; kk <= mt; ++kk) acc = mma_f32_k16(av(kk), bv(kk), acc);
+            } else {
+                // K16 tile mt + 1 of the last pair, when there is one, is the
+                // zero block of T above the diagonal
+                for (int kp = 0; 2 * kp <= mt; ++kp)
+                    acc = mma_k32<false>(av(2 * kp), av(2 * kp + 1), bv(2 * kp), bv(2 * kp + 1), acc);
             }
             if constexpr (F32IO)
                 wr4(item + IT::wt + (size_t)c * 64 + 16 * mt + 4 * lg, acc);
@@ -464,11 +487,14 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_local_kernel(
             const int mt = u / KT, nt = u % KT;
             const int c = 16 * mt + ln;
             f32x4 acc = zero4();
+            auto av = [&](int kk) { return rdcol4(Qs + (16 * kk + 4 * lg) * PB + c, PB) * fpre[kk * D + c]; };
+            auto bv = [&](int kk) { return rdcol4(DOs + (16 * kk + 4 * lg) * PB + 16 * nt + ln, PB); };
+            if constexpr (F32IO) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int t = 16 * kk + 4 * lg;
-                acc = mma_f32_k16(rdcol4(Qs + t * PB + c, PB) * fpre[kk * D + c],
-                                  rdcol4(DOs + t * PB + 16 * nt + ln, PB), acc);
+                for (int kk = 0; kk < 4; ++kk) acc = mma_f32_k16(av(kk), bv(kk), acc);
+            } else {
+#pragma unroll
+                for (int kp = 0; kp < 2; ++kp) acc = mma_k32_exact_b(av(2 * kp), av(2 * kp + 1), bv(2 * kp), bv(2 * kp + 1), acc);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) item[IT::ys + (size_t)(16 * mt + 4 * lg + j) * D + 16 * nt + ln] = acc[j];
@@ -477,10 +503,15 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_local_kernel(
         for (int u = wave; u < 4 * KT; u += kBwdWaves) {
             const int mt = u / KT, nt = u % KT;
             f32x4 acc = zero4();
-            for (int kk = mt; kk < 4; ++kk) {
-                const int t = 16 * kk + 4 * lg;
-                acc = mma_f32_k16(rdcol4(Ps + t * kPS + 16 * mt + ln, kPS), rdcol4(DOs + t * PB + 16 * nt + ln, PB),
-                                  acc);
+            auto av = [&](int kk) { return rdcol4(Ps + (16 * kk + 4 * lg) * kPS + 16 * mt + ln, kPS); };
+            auto bv = [&](int kk) { return rdcol4(DOs + (16 * kk + 4 * lg) * PB + 16 * nt + ln, PB); };
+            if constexpr (F32IO) {
+                for (int kk = mt; kk < 4; ++kk) acc = mma_f32_k16(av(kk), bv(kk), acc);
+            } else {
+                // K16 tile mt - 1 of the first pair, when there is one, is the
+                // zero block of P above the diagonal
+                for (int kp = mt >> 1; kp < 2; ++kp)
+                    acc = mma_k32_exact_b(av(2 * kp), av(2 * kp + 1), bv(2 * kp), bv(2 * kp + 1), acc);
             }
             wr4(item + IT::xv + (size_t)(16 * nt + ln) * 64 + 16 * mt + 4 * lg, acc);
         }
