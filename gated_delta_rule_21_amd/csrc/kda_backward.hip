@@ -112,6 +112,15 @@ __device__ __forceinline__ f32x4 mma_k32_exact_b(f32x4 a0, f32x4 a1, f32x4 b0, f
     return mma_bf16_k32(al, bh, acc);
 }
 
+// And for an A operand that holds bf16 values exactly: only B is split.
+__device__ __forceinline__ f32x4 mma_k32_exact_a(f32x4 a0, f32x4 a1, f32x4 b0, f32x4 b1, f32x4 acc) {
+    u32x4 bh, bl;
+    quads_to_bf16_split(b0, b1, bh, bl);
+    const u32x4 ah = quads_to_bf16(a0, a1);
+    acc = mma_bf16_k32(ah, bh, acc);
+    return mma_bf16_k32(ah, bl, acc);
+}
+
 // sum_{m = lo}^{hi - 1} bt[m][c] (zero when lo >= hi); bt is [4][D].
 template <int D>
 __device__ __forceinline__ f32x4 span4(const float *bt, int lo, int hi, int c) {
@@ -800,10 +809,12 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
     for (int u = wave; u < 16; u += kBwdWaves) {
         const int mt = u >> 2, nt = u & 3;
         f32x4 acc = zero4();
+        {
+            const float *ar = dvr + (size_t)(16 * mt + ln) * D + 4 * lg, *br = Xs + (16 * nt + ln) * PB + 4 * lg;
 #pragma unroll
-        for (int kk = 0; kk < KT; ++kk) {
-            const int c = 16 * kk + 4 * lg;
-            acc = mma_f32_k16(rd4(dvr + (size_t)(16 * mt + ln) * D + c), rd4(Xs + (16 * nt + ln) * PB + c), acc);
+            for (int kp = 0; kp < KT / 2; ++kp)
+                acc = mma_k32<F32IO>(rd4(ar + 32 * kp), rd4(ar + 32 * kp + 16), rd4(br + 32 * kp), rd4(br + 32 * kp + 16),
+                                     acc);
         }
         // dbeta_j partial over the tile's rows: sum_t dM_tj T_tj
         float p = 0.f;
@@ -823,10 +834,17 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
         vp[i] = zero4();
         if (u < 4 * KT) {
             const int mt = u / KT, nt = u % KT;
-            for (int kk = 0; kk <= mt; ++kk) {
+            auto av = [&](int kk) {
                 const int s = 16 * kk + 4 * lg;
-                vp[i] = mma_f32_k16(rd4(S0 + (16 * mt + ln) * kPS + s) * rd4(bet + s),
-                                    rdcol4(Xs + s * PB + 16 * nt + ln, PB), vp[i]);
+                return rd4(S0 + (16 * mt + ln) * kPS + s) * rd4(bet + s);
+            };
+            auto bv = [&](int kk) { return rdcol4(Xs + (16 * kk + 4 * lg) * PB + 16 * nt + ln, PB); };
+            if constexpr (F32IO) {
+                for (int kk = 0; kk <= mt; ++kk) vp[i] = mma_f32_k16(av(kk), bv(kk), vp[i]);
+            } else {
+                // the pair's K16 tile mt + 1, when there is one, is a zero block of T
+                for (int kp = 0; 2 * kp <= mt; ++kp)
+                    vp[i] = mma_k32<false>(av(2 * kp), av(2 * kp + 1), bv(2 * kp), bv(2 * kp + 1), vp[i]);
             }
         }
     }
@@ -834,10 +852,15 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
         const int mt = u / KT, nt = u % KT;
         const int v = 16 * nt + ln;
         f32x4 acc = zero4();
-        for (int kk = mt; kk < 4; ++kk) {
-            const int t = 16 * kk + 4 * lg;
-            acc = mma_f32_k16(rdcol4(S0 + t * kPS + 16 * mt + ln, kPS) * bet[16 * mt + ln],
-                              rd4(dvp + (size_t)v * 64 + t), acc);
+        const float bm = bet[16 * mt + ln];
+        auto av = [&](int kk) { return rdcol4(S0 + (16 * kk + 4 * lg) * kPS + 16 * mt + ln, kPS) * bm; };
+        auto bv = [&](int kk) { return rd4(dvp + (size_t)v * 64 + 16 * kk + 4 * lg); };
+        if constexpr (F32IO) {
+            for (int kk = mt; kk < 4; ++kk) acc = mma_f32_k16(av(kk), bv(kk), acc);
+        } else {
+            // the pair's K16 tile mt - 1, when there is one, is a zero block of T
+            for (int kp = mt >> 1; kp < 2; ++kp)
+                acc = mma_k32<false>(av(2 * kp), av(2 * kp + 1), bv(2 * kp), bv(2 * kp + 1), acc);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -863,10 +886,17 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
     for (int i = 0; i < 2; ++i) {
         const int u = wave + i * kBwdWaves, mt = u >> 2, nt = u & 3;
         e[i] = zero4();
-        for (int kk = 0; kk <= nt; ++kk) {
+        auto av = [&](int kk) {
             const int s = 16 * kk + 4 * lg;
-            e[i] = mma_f32_k16(rd4(S1 + (16 * mt + ln) * kPS + s) * rd4(bet + s), rd4(S0 + (16 * nt + ln) * kPS + s),
-                               e[i]);
+            return rd4(S1 + (16 * mt + ln) * kPS + s) * rd4(bet + s);
+        };
+        auto bv = [&](int kk) { return rd4(S0 + (16 * nt + ln) * kPS + 16 * kk + 4 * lg); };
+        if constexpr (F32IO) {
+            for (int kk = 0; kk <= nt; ++kk) e[i] = mma_f32_k16(av(kk), bv(kk), e[i]);
+        } else {
+            // the pair's K16 tile nt + 1, when there is one, is a zero block of T
+            for (int kp = 0; 2 * kp <= nt; ++kp)
+                e[i] = mma_k32<false>(av(2 * kp), av(2 * kp + 1), bv(2 * kp), bv(2 * kp + 1), e[i]);
         }
     }
     __syncthreads();
@@ -883,10 +913,14 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
         const int u = wave + i * kBwdWaves, mt = u >> 2, nt = u & 3;
         e[i] = zero4();
         if (nt <= mt) {
-            for (int kk = mt; kk < 4; ++kk) {
-                const int t = 16 * kk + 4 * lg;
-                e[i] = mma_f32_k16(rdcol4(S0 + t * kPS + 16 * mt + ln, kPS), rdcol4(S1 + t * kPS + 16 * nt + ln, kPS),
-                                   e[i]);
+            auto av = [&](int kk) { return rdcol4(S0 + (16 * kk + 4 * lg) * kPS + 16 * mt + ln, kPS); };
+            auto bv = [&](int kk) { return rdcol4(S1 + (16 * kk + 4 * lg) * kPS + 16 * nt + ln, kPS); };
+            if constexpr (F32IO) {
+                for (int kk = mt; kk < 4; ++kk) e[i] = mma_f32_k16(av(kk), bv(kk), e[i]);
+            } else {
+                // the pair's K16 tile mt - 1, when there is one, is a zero block of T
+                for (int kp = mt >> 1; kp < 2; ++kp)
+                    e[i] = mma_k32<false>(av(2 * kp), av(2 * kp + 1), bv(2 * kp), bv(2 * kp + 1), e[i]);
             }
         }
     }
@@ -931,10 +965,16 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
         const int u = wave + i * kBwdWaves, mt = u >> 2, nt = u & 3;
         f32x4 acc = zero4();
         if (nt <= mt) {
+            const float *br = Xs + (16 * nt + ln) * PB + 4 * lg;
 #pragma unroll
-            for (int kk = 0; kk < KT; ++kk) {
-                const int c = 16 * kk + 4 * lg;
-                acc = mma_f32_k16(row_io(dO, 16 * mt + ln, c), rd4(Xs + (16 * nt + ln) * PB + c), acc);
+            for (int kp = 0; kp < KT / 2; ++kp) {
+                const int c0 = 32 * kp + 4 * lg, c1 = c0 + 16;
+                if constexpr (F32IO)
+                    acc = mma_k32<true>(row_io(dO, 16 * mt + ln, c0), row_io(dO, 16 * mt + ln, c1), rd4(br + 32 * kp),
+                                        rd4(br + 32 * kp + 16), acc);
+                else   // dO is exactly bf16
+                    acc = mma_k32_exact_a(row_io(dO, 16 * mt + ln, c0), row_io(dO, 16 * mt + ln, c1),
+                                          rd4(br + 32 * kp), rd4(br + 32 * kp + 16), acc);
             }
         }
 #pragma unroll

@@ -71,17 +71,18 @@ def test_backward_ragged(io, d, H, lens, h0, dhT, segments):
     check(got, oracle_grads(inp, cot), F32_BWD_TOL if io == "f32" else BF16_TOL)
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("z_shift,beta_zero", [(-30.0, True), (-30.0, False), (8.0, False)])
-def test_backward_degenerate_gates(z_shift, beta_zero):
+def test_backward_degenerate_gates(z_shift, beta_zero, io):
     """No decay and no write (constant state), no decay (the DeltaNet rule),
-    and the strongest decay the gate allows (alpha -> e^-5)."""
-    print("backward gates", z_shift, beta_zero, flush=True)
-    inp = W.random_prefill([200, 70], 2, 64, "f32", h0_std=0.3, seed=990, z_shift=z_shift)
+    and the strongest decay the gate allows (alpha -> e^-5), on both paths."""
+    print("backward gates", z_shift, beta_zero, io, flush=True)
+    inp = W.random_prefill([200, 70], 2, 64, io, h0_std=0.3, seed=990, z_shift=z_shift)
     if beta_zero:
         inp["beta"].zero_()
-    cot = W.random_cotangents(270, 2, 2, 64, "f32", seed=991)
+    cot = W.random_cotangents(270, 2, 2, 64, io, seed=991)
     got = gpu_grads(to_gpu(inp), to_gpu(cot))
-    check(got, oracle_grads(inp, cot), F32_BWD_TOL)
+    check(got, oracle_grads(inp, cot), F32_BWD_TOL if io == "f32" else BF16_TOL)
 
 
 def test_backward_repeatable():
