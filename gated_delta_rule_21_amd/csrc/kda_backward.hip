@@ -534,8 +534,10 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_local_kernel(
 // are wave-local:
 //   dV' = X + K~ dS'           (accumulator of K~ dS' = B operand of W^T dV')
 //   dS  = Y + gamma_C * dS' - W^T dV'
-// K~ and W^T of the next chunk go global -> registers during a step and
-// registers -> LDS after it (double buffer, one barrier per step).
+// K~ and W^T of the next chunk are staged during a step into the other half
+// of a double buffer (one barrier per step): fp32 path, global -> registers
+// -> padded LDS rows; bf16 path, split bf16 fragments copied global -> LDS
+// directly, both products on split-bf16 MFMA.
 // ---------------------------------------------------------------------------
 template <int D>
 struct ChainShape {
