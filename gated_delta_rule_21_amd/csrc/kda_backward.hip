@@ -27,7 +27,7 @@
 //   3. bwd_chain_kernel, per (sequence, head, value columns): walks the
 //      chunks backwards carrying dS in fp32 MFMA accumulators, stores dS'
 //      (key-major) and dV' (both orientations) of every chunk, and dh0;
-//   4. bwd_grad_kernel, one workgroup per (chunk, head): every input gradient;
+//   4. bwd_grad_kernel, persistent over (chunk, head) items: every input gradient;
 //   5. bwd_dA_kernel: the per-head sum of the chunks' A gradients, in a fixed
 //      order (the result does not depend on scheduling).
 //
@@ -149,31 +149,6 @@ __device__ __forceinline__ void stage_rows(float *dst, const void *src, int t0, 
     }
 }
 
-// Gb[r][c]: log2-decay of rows 16 I .. r of r's block I (inclusive), and the
-// block totals bt[I][c].  Rows >= L add nothing (zero gate).
-template <int D>
-__device__ __forceinline__ void stage_decay(float *Gb, float *bt, const float *z, float ea, int t0, int L,
-                                            int h, int H, int tid) {
-    constexpr int PB = D + 4;
-    if (tid < 4 * D) {
-        const int c = tid % D, I = tid / D;
-        float x[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = 16 * I + i;
-            x[i] = r < L ? z[((size_t)(t0 + r) * H + h) * D + c] : 0.f;
-        }
-        float run = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = 16 * I + i;
-            run += r < L ? gate_log2(ea, x[i]) : 0.f;
-            Gb[r * PB + c] = run;
-        }
-        bt[I * D + c] = run;
-    }
-}
-
 // Raw inputs of one (chunk, head) item for one thread of the local kernel:
 // the quads of q, k and dO it stages (io dtype; rows past the chunk's end
 // zero), the 16 gate logits of thread (c, I) = (tid % D, tid / D), and beta.
@@ -217,6 +192,63 @@ __device__ __forceinline__ void load_local(LocalIn<D, F32IO> &R, const void *q, 
         }
     }
     R.beta = (tid < 64 && tid < L) ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
+}
+
+// A zero the compiler cannot see through.  Lane-dependent constants built
+// from `lane + opaque_zero()` inside a persistent item loop are rebuilt per
+// item instead of being hoisted out of the loop and kept live (or spilled)
+// across it.
+__device__ __forceinline__ int opaque_zero() {
+    int z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    return z;
+}
+
+// Raw inputs of one (chunk, head) item for one thread of the grad kernel:
+// quads of k and v (io dtype; rows past the chunk's end zero), the 16 gate
+// logits of thread (c, I) = (tid % D, tid / D), beta, and two quads of the
+// item's T.  The next item's are fetched into registers during the current
+// item's last phase.
+template <int D, bool F32IO>
+struct GradIn {
+    static constexpr int Q = D / 4, NQ = 64 * Q / kBwdThreads;
+    using Quad = typename std::conditional<F32IO, f32x4, u32x2>::type;
+    Quad k[NQ], v[NQ];
+    float z[16];
+    float beta;
+    f32x4 t[64 * 16 / kBwdThreads];
+};
+
+template <int D, bool F32IO>
+__device__ __forceinline__ void load_grad_rows(GradIn<D, F32IO> &R, const void *k, const void *v,
+                                               const float *beta, const float *item_t, int t0, int L, int h, int H,
+                                               int tid) {
+    using GI = GradIn<D, F32IO>;
+#pragma unroll
+    for (int s = 0; s < GI::NQ; ++s) {
+        const int i = tid + s * kBwdThreads, r = i / GI::Q, c = 4 * (i % GI::Q);
+        const size_t off = ((size_t)(t0 + r) * H + h) * D + c;
+        R.k[s] = r < L ? load_quad<D, F32IO>(k, off) : typename GI::Quad{};
+        R.v[s] = r < L ? load_quad<D, F32IO>(v, off) : typename GI::Quad{};
+    }
+    R.beta = (tid < 64 && tid < L) ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
+#pragma unroll
+    for (int s = 0; s < 64 * 16 / kBwdThreads; ++s) {
+        const int i = tid + s * kBwdThreads;
+        R.t[s] = rd4(item_t + (i >> 4) * 64 + 4 * (i & 15));
+    }
+}
+template <int D, bool F32IO>
+__device__ __forceinline__ void load_grad_z(GradIn<D, F32IO> &R, const float *z, int t0, int L, int h, int H,
+                                            int tid) {
+    if (tid < 4 * D) {
+        const int c = tid % D, I = tid / D;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = 16 * I + i;
+            R.z[i] = r < L ? z[((size_t)(t0 + r) * H + h) * D + c] : 0.f;
+        }
+    }
 }
 
 // Rows [0, 64) of staged quads into LDS as fp32 (pitch D + 4).
@@ -311,7 +343,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_local_kernel(
 #pragma unroll
         for (int s = 0; s < LI::NQ; ++s) ocur[s] = R.o[s];
         if (tid < 4 * D) {
-            // Gb and bt from the staged gate logits (as stage_decay)
+            // Gb (inclusive block scans of the log2 gate) and the block totals bt
             const int c = tid % D, I = tid / D;
             float run = 0.f;
 #pragma unroll
@@ -480,8 +512,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_local_kernel(
             if constexpr (F32IO)
                 wr4(item + IT::kt + (size_t)r * D + c, x);
             else   // A operand of K~ dS: row r = 16 rt + m, key c = 32 kp + 16 half + 4 g
-                store_split_half(item + IT::kt, (r >> 4) * (D / 32) + (c >> 5), (c >> 4) & 1, (r & 15) + 16 * ((c & 15) >> 2),
-                                 x);
+                store_split_half(item + IT::kt, (r >> 4) * (D / 32) + (c >> 5), (c >> 4) & 1,
+                                 (r & 15) + 16 * ((c & 15) >> 2), x);
         }
         for (int c = tid; c < D; c += kBwdThreads) item[IT::gam + c] = fast_exp2(span1<D>(bt, 0, 4, c));
         __syncthreads();
@@ -503,7 +535,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_local_kernel(
                 for (int kk = 0; kk < 4; ++kk) acc = mma_f32_k16(av(kk), bv(kk), acc);
             } else {
 #pragma unroll
-                for (int kp = 0; kp < 2; ++kp) acc = mma_k32_exact_b(av(2 * kp), av(2 * kp + 1), bv(2 * kp), bv(2 * kp + 1), acc);
+                for (int kp = 0; kp < 2; ++kp)
+                    acc = mma_k32_exact_b(av(2 * kp), av(2 * kp + 1), bv(2 * kp), bv(2 * kp + 1), acc);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) item[IT::ys + (size_t)(16 * mt + 4 * lg + j) * D + 16 * nt + ln] = acc[j];
@@ -750,491 +783,530 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
     float *Ks = lds + SL::k, *Gb = lds + SL::gb, *Xs = lds + SL::x, *S0 = lds + SL::s0, *S1 = lds + SL::s1;
     float *bet = lds + SL::beta, *bt = lds + SL::bt, *pd = lds + SL::pd, *dgc = lds + SL::dgc;
     float *red = lds + SL::red, *part = lds + SL::part;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
-    const int chunk = blockIdx.x / H, h = blockIdx.x % H;
-    if (chunk >= meta[N]) return;
-    const int4 ent = table[chunk];
-    const int n = ent.x, t0 = ent.y, L = ent.z;
-    const float *item = items + ((size_t)h * max_chunks + chunk) * IT::floats;
-    const float *dvp = item + IT::xv;   // dV'^T [v][t]
-    const float *dvr = item + IT::dvr;  // dV' [t][v]
-    const float *dsp = item + IT::ys;   // dS' [c][v]
-    const float ea = __expf(A[h]);
-    // state at the chunk's start, [v][c]; NULL = zero
-    const float *Sg = nullptr;
-    {
-        const int j = chunk - meta[n];
-        if (j == 0) {
-            if (h0) Sg = h0 + ((size_t)n * H + h) * D * D;
-        } else if (ck) {
-            const int idx = ck_off[n] + j - 1;
-            if (idx >= 0 && idx < ck_cap) Sg = ck + ((size_t)idx * H + h) * D * D;
-        }
-    }
-    auto row_io = [&](const void *p, int r, int c) -> f32x4 {
-        return r < L ? load_io4<F32IO>(p, ((size_t)(t0 + r) * H + h) * D + c) : zero4();
-    };
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave index in an SGPR
+    const int total = meta[N] * H;
+    int it = blockIdx.x;
+    if (it >= total) return;
+    auto rec = [&](int i) { return items + ((size_t)(i % H) * max_chunks + i / H) * IT::floats; };
+    GradIn<D, F32IO> R;
+    int4 ent = table[it / H];
+    load_grad_rows<D, F32IO>(R, k, vin, beta, rec(it) + IT::t, ent.y, ent.z, it % H, H, threadIdx.x);
+    load_grad_z<D, F32IO>(R, z, ent.y, ent.z, it % H, H, threadIdx.x);
 
-    // ---- K, the block log-decays, V, beta
-    stage_rows<D, F32IO>(Ks, k, t0, L, h, H, tid);
-    stage_rows<D, F32IO>(Xs, vin, t0, L, h, H, tid);
-    stage_decay<D>(Gb, bt, z, ea, t0, L, h, H, tid);
-    if (tid < 64) bet[tid] = tid < L ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
-    __syncthreads();
-
-    // ---- V~ = V - (Gamma*K) S, in place
-    for (int u = wave; u < 4 * KT; u += kBwdWaves) {
-        const int mt = u / KT, nt = u % KT;
-        f32x4 acc = zero4();
-        if (Sg) {
-            const int r = 16 * mt + ln;
-            auto kg = [&](int kk) {
-                const int c = 16 * kk + 4 * lg;
-                return rd4(Ks + r * PB + c) * exp2x4(rd4(Gb + r * PB + c) + span4<D>(bt, 0, mt, c));
-            };
-            auto sb = [&](int kk) { return rd4(Sg + (size_t)(16 * nt + ln) * D + 16 * kk + 4 * lg); };
-#pragma unroll
-            for (int kp = 0; kp < KT / 2; ++kp)
-                acc = mma_k32<F32IO>(kg(2 * kp), kg(2 * kp + 1), sb(2 * kp), sb(2 * kp + 1), acc);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Xs[(16 * mt + 4 * lg + j) * PB + 16 * nt + ln] -= acc[j];
-    }
-    for (int i = tid; i < 64 * 16; i += kBwdThreads) {
-        const int r = i >> 4, c = 4 * (i & 15);
-        wr4(S0 + r * kPS + c, rd4(item + IT::t + r * 64 + c));
-    }
-    __syncthreads();
-
-    // ---- dM = dV' V~^T -> S1;  V' = M V~ (registers, then over V~);
-    //      dV = M^T dV' -> gv
-    for (int u = wave; u < 16; u += kBwdWaves) {
-        const int mt = u >> 2, nt = u & 3;
-        f32x4 acc = zero4();
+    // persistent: items blockIdx.x, + gridDim.x, ...  Every LDS region but
+    // `part` is last read before an item's final barrier, and `part` is next
+    // written many barriers into the following item, so items need no barrier
+    // between them.
+    for (; it < total; it += gridDim.x) {
+        // thread and lane coordinates, rebuilt per item (see opaque_zero)
+        const int tid = (int)threadIdx.x + opaque_zero();
+        const int lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+        const int chunk = it / H, h = it % H;
+        const int n = ent.x, t0 = ent.y, L = ent.z;
+        const float *item = rec(it);
+        const float *dvp = item + IT::xv;   // dV'^T [v][t]
+        const float *dvr = item + IT::dvr;  // dV' [t][v]
+        const float *dsp = item + IT::ys;   // dS' [c][v]
+        const float ea = __expf(A[h]);
+        // state at the chunk's start, [v][c]; NULL = zero
+        const float *Sg = nullptr;
         {
-            const float *ar = dvr + (size_t)(16 * mt + ln) * D + 4 * lg, *br = Xs + (16 * nt + ln) * PB + 4 * lg;
-#pragma unroll
-            for (int kp = 0; kp < KT / 2; ++kp)
-                acc = mma_k32<F32IO>(rd4(ar + 32 * kp), rd4(ar + 32 * kp + 16), rd4(br + 32 * kp), rd4(br + 32 * kp + 16),
-                                     acc);
-        }
-        // dbeta_j partial over the tile's rows: sum_t dM_tj T_tj
-        float p = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            S1[(16 * mt + 4 * lg + j) * kPS + 16 * nt + ln] = acc[j];
-            p += acc[j] * S0[(16 * mt + 4 * lg + j) * kPS + 16 * nt + ln];
-        }
-        p += __shfl_xor(p, 16);
-        p += __shfl_xor(p, 32);
-        if (lg == 0) red[mt * 64 + 16 * nt + ln] = p;
-    }
-    f32x4 vp[NU];
-#pragma unroll
-    for (int i = 0; i < NU; ++i) {
-        const int u = wave + i * kBwdWaves;
-        vp[i] = zero4();
-        if (u < 4 * KT) {
-            const int mt = u / KT, nt = u % KT;
-            auto av = [&](int kk) {
-                const int s = 16 * kk + 4 * lg;
-                return rd4(S0 + (16 * mt + ln) * kPS + s) * rd4(bet + s);
-            };
-            auto bv = [&](int kk) { return rdcol4(Xs + (16 * kk + 4 * lg) * PB + 16 * nt + ln, PB); };
-            if constexpr (F32IO) {
-                for (int kk = 0; kk <= mt; ++kk) vp[i] = mma_f32_k16(av(kk), bv(kk), vp[i]);
-            } else {
-                // the pair's K16 tile mt + 1, when there is one, is a zero block of T
-                for (int kp = 0; 2 * kp <= mt; ++kp)
-                    vp[i] = mma_k32<false>(av(2 * kp), av(2 * kp + 1), bv(2 * kp), bv(2 * kp + 1), vp[i]);
+            const int j = chunk - meta[n];
+            if (j == 0) {
+                if (h0) Sg = h0 + ((size_t)n * H + h) * D * D;
+            } else if (ck) {
+                const int idx = ck_off[n] + j - 1;
+                if (idx >= 0 && idx < ck_cap) Sg = ck + ((size_t)idx * H + h) * D * D;
             }
         }
-    }
-    for (int u = wave; u < 4 * KT; u += kBwdWaves) {
-        const int mt = u / KT, nt = u % KT;
-        const int v = 16 * nt + ln;
-        f32x4 acc = zero4();
-        const float bm = bet[16 * mt + ln];
-        auto av = [&](int kk) { return rdcol4(S0 + (16 * kk + 4 * lg) * kPS + 16 * mt + ln, kPS) * bm; };
-        auto bv = [&](int kk) { return rd4(dvp + (size_t)v * 64 + 16 * kk + 4 * lg); };
-        if constexpr (F32IO) {
-            for (int kk = mt; kk < 4; ++kk) acc = mma_f32_k16(av(kk), bv(kk), acc);
-        } else {
-            // the pair's K16 tile mt - 1, when there is one, is a zero block of T
-            for (int kp = mt >> 1; kp < 2; ++kp)
-                acc = mma_k32<false>(av(2 * kp), av(2 * kp + 1), bv(2 * kp), bv(2 * kp + 1), acc);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * mt + 4 * lg + j;
-            if (r < L) gv[((size_t)(t0 + r) * H + h) * D + v] = acc[j];
-        }
-    }
-    __threadfence_block();
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < NU; ++i) {
-        const int u = wave + i * kBwdWaves;
-        if (u < 4 * KT) {
-            const int mt = u / KT, nt = u % KT;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) Xs[(16 * mt + 4 * lg + j) * PB + 16 * nt + ln] = vp[i][j];
-        }
-    }
-
-    // ---- E = (dM Diag(beta)) T^T (registers)
-    f32x4 e[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int u = wave + i * kBwdWaves, mt = u >> 2, nt = u & 3;
-        e[i] = zero4();
-        auto av = [&](int kk) {
-            const int s = 16 * kk + 4 * lg;
-            return rd4(S1 + (16 * mt + ln) * kPS + s) * rd4(bet + s);
+        auto row_io = [&](const void *p, int r, int c) -> f32x4 {
+            return r < L ? load_io4<F32IO>(p, ((size_t)(t0 + r) * H + h) * D + c) : zero4();
         };
-        auto bv = [&](int kk) { return rd4(S0 + (16 * nt + ln) * kPS + 16 * kk + 4 * lg); };
-        if constexpr (F32IO) {
-            for (int kk = 0; kk <= nt; ++kk) e[i] = mma_f32_k16(av(kk), bv(kk), e[i]);
-        } else {
-            // the pair's K16 tile nt + 1, when there is one, is a zero block of T
-            for (int kp = 0; 2 * kp <= nt; ++kp)
-                e[i] = mma_k32<false>(av(2 * kp), av(2 * kp + 1), bv(2 * kp), bv(2 * kp + 1), e[i]);
+
+        // ---- K, the block log-decays, V, beta, T (from the registers)
+        stage_quads<D, F32IO>(Ks, R.k, tid);
+        stage_quads<D, F32IO>(Xs, R.v, tid);
+        if (tid < 4 * D) {
+            const int c = tid % D, I = tid / D;
+            float run = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = 16 * I + i;
+                run += r < L ? gate_log2(ea, R.z[i]) : 0.f;
+                Gb[r * PB + c] = run;
+            }
+            bt[I * D + c] = run;
         }
-    }
-    __syncthreads();
+        if (tid < 64) bet[tid] = R.beta;
+        f32x4 tq[64 * 16 / kBwdThreads];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int u = wave + i * kBwdWaves, mt = u >> 2, nt = u & 3;
+        for (int s = 0; s < 64 * 16 / kBwdThreads; ++s) tq[s] = R.t[s];
+        __syncthreads();
+
+        // ---- V~ = V - (Gamma*K) S, in place
+        for (int u = wave; u < 4 * KT; u += kBwdWaves) {
+            const int mt = u / KT, nt = u % KT;
+            f32x4 acc = zero4();
+            if (Sg) {
+                const int r = 16 * mt + ln;
+                auto kg = [&](int kk) {
+                    const int c = 16 * kk + 4 * lg;
+                    return rd4(Ks + r * PB + c) * exp2x4(rd4(Gb + r * PB + c) + span4<D>(bt, 0, mt, c));
+                };
+                auto sb = [&](int kk) { return rd4(Sg + (size_t)(16 * nt + ln) * D + 16 * kk + 4 * lg); };
 #pragma unroll
-        for (int j = 0; j < 4; ++j) S1[(16 * mt + 4 * lg + j) * kPS + 16 * nt + ln] = e[i][j];
-    }
-    __syncthreads();
-    // ---- dA_kk = -StrictTril(T^T E) (registers, then over T)
+                for (int kp = 0; kp < KT / 2; ++kp)
+                    acc = mma_k32<F32IO>(kg(2 * kp), kg(2 * kp + 1), sb(2 * kp), sb(2 * kp + 1), acc);
+            }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int u = wave + i * kBwdWaves, mt = u >> 2, nt = u & 3;
-        e[i] = zero4();
-        if (nt <= mt) {
-            auto av = [&](int kk) { return rdcol4(S0 + (16 * kk + 4 * lg) * kPS + 16 * mt + ln, kPS); };
-            auto bv = [&](int kk) { return rdcol4(S1 + (16 * kk + 4 * lg) * kPS + 16 * nt + ln, kPS); };
+            for (int j = 0; j < 4; ++j) Xs[(16 * mt + 4 * lg + j) * PB + 16 * nt + ln] -= acc[j];
+        }
+#pragma unroll
+        for (int s = 0; s < 64 * 16 / kBwdThreads; ++s) {
+            const int i = tid + s * kBwdThreads, r = i >> 4, c = 4 * (i & 15);
+            wr4(S0 + r * kPS + c, tq[s]);
+        }
+        __syncthreads();
+
+        // ---- dM = dV' V~^T -> S1;  V' = M V~ (registers, then over V~);
+        //      dV = M^T dV' -> gv
+        for (int u = wave; u < 16; u += kBwdWaves) {
+            const int mt = u >> 2, nt = u & 3;
+            f32x4 acc = zero4();
+            {
+                const float *ar = dvr + (size_t)(16 * mt + ln) * D + 4 * lg, *br = Xs + (16 * nt + ln) * PB + 4 * lg;
+#pragma unroll
+                for (int kp = 0; kp < KT / 2; ++kp)
+                    acc = mma_k32<F32IO>(rd4(ar + 32 * kp), rd4(ar + 32 * kp + 16), rd4(br + 32 * kp),
+                                         rd4(br + 32 * kp + 16), acc);
+            }
+            // dbeta_j partial over the tile's rows: sum_t dM_tj T_tj
+            float p = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                S1[(16 * mt + 4 * lg + j) * kPS + 16 * nt + ln] = acc[j];
+                p += acc[j] * S0[(16 * mt + 4 * lg + j) * kPS + 16 * nt + ln];
+            }
+            p += __shfl_xor(p, 16);
+            p += __shfl_xor(p, 32);
+            if (lg == 0) red[mt * 64 + 16 * nt + ln] = p;
+        }
+        f32x4 vp[NU];
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int u = wave + i * kBwdWaves;
+            vp[i] = zero4();
+            if (u < 4 * KT) {
+                const int mt = u / KT, nt = u % KT;
+                auto av = [&](int kk) {
+                    const int s = 16 * kk + 4 * lg;
+                    return rd4(S0 + (16 * mt + ln) * kPS + s) * rd4(bet + s);
+                };
+                auto bv = [&](int kk) { return rdcol4(Xs + (16 * kk + 4 * lg) * PB + 16 * nt + ln, PB); };
+                if constexpr (F32IO) {
+                    for (int kk = 0; kk <= mt; ++kk) vp[i] = mma_f32_k16(av(kk), bv(kk), vp[i]);
+                } else {
+                    // the pair's K16 tile mt + 1, when there is one, is a zero block of T
+                    for (int kp = 0; 2 * kp <= mt; ++kp)
+                        vp[i] = mma_k32<false>(av(2 * kp), av(2 * kp + 1), bv(2 * kp), bv(2 * kp + 1), vp[i]);
+                }
+            }
+        }
+        for (int u = wave; u < 4 * KT; u += kBwdWaves) {
+            const int mt = u / KT, nt = u % KT;
+            const int v = 16 * nt + ln;
+            f32x4 acc = zero4();
+            const float bm = bet[16 * mt + ln];
+            auto av = [&](int kk) { return rdcol4(S0 + (16 * kk + 4 * lg) * kPS + 16 * mt + ln, kPS) * bm; };
+            auto bv = [&](int kk) { return rd4(dvp + (size_t)v * 64 + 16 * kk + 4 * lg); };
             if constexpr (F32IO) {
-                for (int kk = mt; kk < 4; ++kk) e[i] = mma_f32_k16(av(kk), bv(kk), e[i]);
+                for (int kk = mt; kk < 4; ++kk) acc = mma_f32_k16(av(kk), bv(kk), acc);
             } else {
                 // the pair's K16 tile mt - 1, when there is one, is a zero block of T
                 for (int kp = mt >> 1; kp < 2; ++kp)
+                    acc = mma_k32<false>(av(2 * kp), av(2 * kp + 1), bv(2 * kp), bv(2 * kp + 1), acc);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * mt + 4 * lg + j;
+                if (r < L) gv[((size_t)(t0 + r) * H + h) * D + v] = acc[j];
+            }
+        }
+        __threadfence_block();
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int u = wave + i * kBwdWaves;
+            if (u < 4 * KT) {
+                const int mt = u / KT, nt = u % KT;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Xs[(16 * mt + 4 * lg + j) * PB + 16 * nt + ln] = vp[i][j];
+            }
+        }
+
+        // ---- E = (dM Diag(beta)) T^T (registers)
+        f32x4 e[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int u = wave + i * kBwdWaves, mt = u >> 2, nt = u & 3;
+            e[i] = zero4();
+            auto av = [&](int kk) {
+                const int s = 16 * kk + 4 * lg;
+                return rd4(S1 + (16 * mt + ln) * kPS + s) * rd4(bet + s);
+            };
+            auto bv = [&](int kk) { return rd4(S0 + (16 * nt + ln) * kPS + 16 * kk + 4 * lg); };
+            if constexpr (F32IO) {
+                for (int kk = 0; kk <= nt; ++kk) e[i] = mma_f32_k16(av(kk), bv(kk), e[i]);
+            } else {
+                // the pair's K16 tile nt + 1, when there is one, is a zero block of T
+                for (int kp = 0; 2 * kp <= nt; ++kp)
                     e[i] = mma_k32<false>(av(2 * kp), av(2 * kp + 1), bv(2 * kp), bv(2 * kp + 1), e[i]);
             }
         }
-    }
-    __syncthreads();
-    // dA_kk over T;  dbeta_r partials sum_i dA_kk,ri R_ri over the tile's columns
+        __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int u = wave + i * kBwdWaves, mt = u >> 2, nt = u & 3;
-        f32x4 p = zero4();
+        for (int i = 0; i < 2; ++i) {
+            const int u = wave + i * kBwdWaves, mt = u >> 2, nt = u & 3;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * mt + 4 * lg + j, w = 16 * nt + ln;
-            const float x = w < r ? -e[i][j] : 0.f;
-            S0[r * kPS + w] = x;
-            if (w < r) p[j] = x * item[IT::r + r * 64 + w];
+            for (int j = 0; j < 4; ++j) S1[(16 * mt + 4 * lg + j) * kPS + 16 * nt + ln] = e[i][j];
         }
+        __syncthreads();
+        // ---- dA_kk = -StrictTril(T^T E) (registers, then over T)
 #pragma unroll
-        for (int m = 1; m < 16; m <<= 1) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) p[j] += __shfl_xor(p[j], m);
+        for (int i = 0; i < 2; ++i) {
+            const int u = wave + i * kBwdWaves, mt = u >> 2, nt = u & 3;
+            e[i] = zero4();
+            if (nt <= mt) {
+                auto av = [&](int kk) { return rdcol4(S0 + (16 * kk + 4 * lg) * kPS + 16 * mt + ln, kPS); };
+                auto bv = [&](int kk) { return rdcol4(S1 + (16 * kk + 4 * lg) * kPS + 16 * nt + ln, kPS); };
+                if constexpr (F32IO) {
+                    for (int kk = mt; kk < 4; ++kk) e[i] = mma_f32_k16(av(kk), bv(kk), e[i]);
+                } else {
+                    // the pair's K16 tile mt - 1, when there is one, is a zero block of T
+                    for (int kp = mt >> 1; kp < 2; ++kp)
+                        e[i] = mma_k32<false>(av(2 * kp), av(2 * kp + 1), bv(2 * kp), bv(2 * kp + 1), e[i]);
+                }
+            }
         }
-        if (ln == 0) wr4(red + 256 + nt * 64 + 16 * mt + 4 * lg, p);
-    }
-    __syncthreads();
-    // ---- dbeta = column sums of dM o T + row sums of dA_kk o R
-    if (tid < 64 && tid < L) {
-        float s = 0.f;
-        for (int m = 0; m < 4; ++m) s += red[m * 64 + tid];
-        for (int m = 0; m < 4; ++m) s += red[256 + m * 64 + tid];
-        gbeta[(size_t)(t0 + tid) * H + h] = s;
-    }
+        __syncthreads();
+        // dA_kk over T;  dbeta_r partials sum_i dA_kk,ri R_ri over the tile's columns
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int u = wave + i * kBwdWaves, mt = u >> 2, nt = u & 3;
+            f32x4 p = zero4();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * mt + 4 * lg + j, w = 16 * nt + ln;
+                const float x = w < r ? -e[i][j] : 0.f;
+                S0[r * kPS + w] = x;
+                if (w < r) p[j] = x * item[IT::r + r * 64 + w];
+            }
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) p[j] += __shfl_xor(p[j], m);
+            }
+            if (ln == 0) wr4(red + 256 + nt * 64 + 16 * mt + 4 * lg, p);
+        }
+        __syncthreads();
+        // ---- dbeta = column sums of dM o T + row sums of dA_kk o R
+        if (tid < 64 && tid < L) {
+            float s = 0.f;
+            for (int m = 0; m < 4; ++m) s += red[m * 64 + tid];
+            for (int m = 0; m < 4; ++m) s += red[256 + m * 64 + tid];
+            gbeta[(size_t)(t0 + tid) * H + h] = s;
+        }
 
-    // ---- dP = Tril(dO V'^T): the strictly lower part -> S1 (E is dead), the
-    //      diagonal -> pd.  A diagonal term dP_rr q_r k_r enters the log-decay
-    //      gradient of row r twice with opposite signs (its decay factor is 1),
-    //      so it is kept out of the decay-masked sums and added to dq and dk
-    //      on its own;  the [t][c] products that
-    //      read S, dS' or dV: dQ_S = Gamma*(dO S^T), dKg = -Gamma*(dV S^T),
-    //      dKt = (gamma_C/Gamma)*(V' dS'^T)
+        // ---- dP = Tril(dO V'^T): the strictly lower part -> S1 (E is dead), the
+        //      diagonal -> pd.  A diagonal term dP_rr q_r k_r enters the log-decay
+        //      gradient of row r twice with opposite signs (its decay factor is 1),
+        //      so it is kept out of the decay-masked sums and added to dq and dk
+        //      on its own;  the [t][c] products that
+        //      read S, dS' or dV: dQ_S = Gamma*(dO S^T), dKg = -Gamma*(dV S^T),
+        //      dKt = (gamma_C/Gamma)*(V' dS'^T)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int u = wave + i * kBwdWaves, mt = u >> 2, nt = u & 3;
-        f32x4 acc = zero4();
-        if (nt <= mt) {
-            const float *br = Xs + (16 * nt + ln) * PB + 4 * lg;
+        for (int i = 0; i < 2; ++i) {
+            const int u = wave + i * kBwdWaves, mt = u >> 2, nt = u & 3;
+            f32x4 acc = zero4();
+            if (nt <= mt) {
+                const float *br = Xs + (16 * nt + ln) * PB + 4 * lg;
+#pragma unroll
+                for (int kp = 0; kp < KT / 2; ++kp) {
+                    const int c0 = 32 * kp + 4 * lg, c1 = c0 + 16;
+                    if constexpr (F32IO)
+                        acc = mma_k32<true>(row_io(dO, 16 * mt + ln, c0), row_io(dO, 16 * mt + ln, c1),
+                                            rd4(br + 32 * kp), rd4(br + 32 * kp + 16), acc);
+                    else   // dO is exactly bf16
+                        acc = mma_k32_exact_a(row_io(dO, 16 * mt + ln, c0), row_io(dO, 16 * mt + ln, c1),
+                                              rd4(br + 32 * kp), rd4(br + 32 * kp + 16), acc);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * mt + 4 * lg + j, s = 16 * nt + ln;
+                S1[r * kPS + s] = s < r ? acc[j] : 0.f;
+                if (s == r) pd[r] = acc[j];
+            }
+        }
+        static_assert((4 * KT) % kBwdWaves == 0, "every wave has NU tiles");
+        f32x4 dq[NU], dkg[NU], dkt[NU], dki[NU];
+#pragma unroll
+        for (int i = 0; i < NU; ++i) dq[i] = dkg[i] = dkt[i] = dki[i] = zero4();
+        // Every tile of a wave has the same key-column block ct = wave % KT; its
+        // row blocks are (wave + i kBwdWaves) / KT.  The loop runs over pairs of
+        // value tiles (kp) outside the wave's tiles, so the S and dS' fragments of
+        // a pair are loaded, and on the bf16 path split into bf16 hi + lo, once
+        // for all of them.
+        const int ct = wave % KT, c = 16 * ct + ln;
+        // B fragments of S: S_cv for c = 16 ct + ln, v = 16 kk + 4 lg + j
+        f32x4 sfr[KT];
+#pragma unroll
+        for (int kk = 0; kk < KT; ++kk) sfr[kk] = Sg ? rdcol4(Sg + (size_t)(16 * kk + 4 * lg) * D + c, D) : zero4();
+        float gc = 0.f;   // dgC_c = sum_v dS'_cv S_cv
+        auto products = [&](auto has_state) {
+            constexpr bool HS = decltype(has_state)::value;
 #pragma unroll
             for (int kp = 0; kp < KT / 2; ++kp) {
-                const int c0 = 32 * kp + 4 * lg, c1 = c0 + 16;
-                if constexpr (F32IO)
-                    acc = mma_k32<true>(row_io(dO, 16 * mt + ln, c0), row_io(dO, 16 * mt + ln, c1), rd4(br + 32 * kp),
-                                        rd4(br + 32 * kp + 16), acc);
-                else   // dO is exactly bf16
-                    acc = mma_k32_exact_a(row_io(dO, 16 * mt + ln, c0), row_io(dO, 16 * mt + ln, c1),
-                                          rd4(br + 32 * kp), rd4(br + 32 * kp + 16), acc);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * mt + 4 * lg + j, s = 16 * nt + ln;
-            S1[r * kPS + s] = s < r ? acc[j] : 0.f;
-            if (s == r) pd[r] = acc[j];
-        }
-    }
-    static_assert((4 * KT) % kBwdWaves == 0, "every wave has NU tiles");
-    f32x4 dq[NU], dkg[NU], dkt[NU], dki[NU];
-#pragma unroll
-    for (int i = 0; i < NU; ++i) dq[i] = dkg[i] = dkt[i] = dki[i] = zero4();
-    // Every tile of a wave has the same key-column block ct = wave % KT; its
-    // row blocks are (wave + i kBwdWaves) / KT.  The loop runs over pairs of
-    // value tiles (kp) outside the wave's tiles, so the S and dS' fragments of
-    // a pair are loaded, and on the bf16 path split into bf16 hi + lo, once
-    // for all of them.
-    const int ct = wave % KT, c = 16 * ct + ln;
-    // B fragments of S: S_cv for c = 16 ct + ln, v = 16 kk + 4 lg + j
-    f32x4 sfr[KT];
-#pragma unroll
-    for (int kk = 0; kk < KT; ++kk) sfr[kk] = Sg ? rdcol4(Sg + (size_t)(16 * kk + 4 * lg) * D + c, D) : zero4();
-    float gc = 0.f;   // dgC_c = sum_v dS'_cv S_cv
-    auto products = [&](auto has_state) {
-        constexpr bool HS = decltype(has_state)::value;
-#pragma unroll
-        for (int kp = 0; kp < KT / 2; ++kp) {
-            const int v0 = 32 * kp + 4 * lg, v1 = v0 + 16;
-            const f32x4 ds0 = rd4(dsp + (size_t)c * D + v0), ds1 = rd4(dsp + (size_t)c * D + v1);
-            const f32x4 s0 = sfr[2 * kp], s1 = sfr[2 * kp + 1];
-            u32x4 dsh, dsl, sh, sl;
-            if constexpr (!F32IO) {
-                quads_to_bf16_split(ds0, ds1, dsh, dsl);
-                if constexpr (HS) quads_to_bf16_split(s0, s1, sh, sl);
-            }
-            if constexpr (HS) {
-                gc += s0[0] * ds0[0] + s0[1] * ds0[1] + s0[2] * ds0[2] + s0[3] * ds0[3];
-                gc += s1[0] * ds1[0] + s1[1] * ds1[1] + s1[2] * ds1[2] + s1[3] * ds1[3];
-            }
-#pragma unroll
-            for (int i = 0; i < NU; ++i) {
-                const int r = 16 * ((wave + i * kBwdWaves) / KT) + ln;
-                const bool rok = r < L;
-                const size_t orow = ((size_t)(t0 + r) * H + h) * D;
-                const f32x4 x0 = rd4(Xs + r * PB + v0), x1 = rd4(Xs + r * PB + v1);
-                if constexpr (F32IO) {
-                    dkt[i] = mma_k32<true>(x0, x1, ds0, ds1, dkt[i]);
-                } else {
-                    u32x4 xh, xl;
-                    quads_to_bf16_split(x0, x1, xh, xl);
-                    dkt[i] = mma3_bf16(xh, xl, dsh, dsl, dkt[i]);
+                const int v0 = 32 * kp + 4 * lg, v1 = v0 + 16;
+                const f32x4 ds0 = rd4(dsp + (size_t)c * D + v0), ds1 = rd4(dsp + (size_t)c * D + v1);
+                const f32x4 s0 = sfr[2 * kp], s1 = sfr[2 * kp + 1];
+                u32x4 dsh, dsl, sh, sl;
+                if constexpr (!F32IO) {
+                    quads_to_bf16_split(ds0, ds1, dsh, dsl);
+                    if constexpr (HS) quads_to_bf16_split(s0, s1, sh, sl);
                 }
                 if constexpr (HS) {
-                    const f32x4 z0 = rok ? rd4(gv + orow + v0) : zero4(), z1 = rok ? rd4(gv + orow + v1) : zero4();
+                    gc += s0[0] * ds0[0] + s0[1] * ds0[1] + s0[2] * ds0[2] + s0[3] * ds0[3];
+                    gc += s1[0] * ds1[0] + s1[1] * ds1[1] + s1[2] * ds1[2] + s1[3] * ds1[3];
+                }
+#pragma unroll
+                for (int i = 0; i < NU; ++i) {
+                    const int r = 16 * ((wave + i * kBwdWaves) / KT) + ln;
+                    const bool rok = r < L;
+                    const size_t orow = ((size_t)(t0 + r) * H + h) * D;
+                    const f32x4 x0 = rd4(Xs + r * PB + v0), x1 = rd4(Xs + r * PB + v1);
                     if constexpr (F32IO) {
-                        dq[i] = mma_k32<true>(row_io(dO, r, v0), row_io(dO, r, v1), s0, s1, dq[i]);
-                        dkg[i] = mma_k32<true>(z0, z1, s0, s1, dkg[i]);
+                        dkt[i] = mma_k32<true>(x0, x1, ds0, ds1, dkt[i]);
                     } else {
-                        // dO is bf16 already: its hi part is exact and its lo part zero
-                        u32x4 dh = u32x4{0u, 0u, 0u, 0u};
-                        if (rok) {
-                            const uint16_t *dp = reinterpret_cast<const uint16_t *>(dO) + orow;
-                            const u32x2 w0 = *reinterpret_cast<const u32x2 *>(dp + v0);
-                            const u32x2 w1 = *reinterpret_cast<const u32x2 *>(dp + v1);
-                            dh = u32x4{w0[0], w0[1], w1[0], w1[1]};
+                        u32x4 xh, xl;
+                        quads_to_bf16_split(x0, x1, xh, xl);
+                        dkt[i] = mma3_bf16(xh, xl, dsh, dsl, dkt[i]);
+                    }
+                    if constexpr (HS) {
+                        const f32x4 z0 = rok ? rd4(gv + orow + v0) : zero4(), z1 = rok ? rd4(gv + orow + v1) : zero4();
+                        if constexpr (F32IO) {
+                            dq[i] = mma_k32<true>(row_io(dO, r, v0), row_io(dO, r, v1), s0, s1, dq[i]);
+                            dkg[i] = mma_k32<true>(z0, z1, s0, s1, dkg[i]);
+                        } else {
+                            // dO is bf16 already: its hi part is exact and its lo part zero
+                            u32x4 dh = u32x4{0u, 0u, 0u, 0u};
+                            if (rok) {
+                                const uint16_t *dp = reinterpret_cast<const uint16_t *>(dO) + orow;
+                                const u32x2 w0 = *reinterpret_cast<const u32x2 *>(dp + v0);
+                                const u32x2 w1 = *reinterpret_cast<const u32x2 *>(dp + v1);
+                                dh = u32x4{w0[0], w0[1], w1[0], w1[1]};
+                            }
+                            dq[i] = mma_bf16_k32(dh, sh, dq[i]);
+                            dq[i] = mma_bf16_k32(dh, sl, dq[i]);
+                            u32x4 zh, zl;
+                            quads_to_bf16_split(z0, z1, zh, zl);
+                            dkg[i] = mma3_bf16(zh, zl, sh, sl, dkg[i]);
                         }
-                        dq[i] = mma_bf16_k32(dh, sh, dq[i]);
-                        dq[i] = mma_bf16_k32(dh, sl, dq[i]);
-                        u32x4 zh, zl;
-                        quads_to_bf16_split(z0, z1, zh, zl);
-                        dkg[i] = mma3_bf16(zh, zl, sh, sl, dkg[i]);
                     }
                 }
             }
-        }
-    };
-    if (Sg)
-        products(std::true_type{});
-    else
-        products(std::false_type{});
-    // the wave that holds row block 0 of column block ct
-    gc += __shfl_xor(gc, 16);
-    gc += __shfl_xor(gc, 32);
-    if (wave < KT && lg == 0) dgc[c] = gc;
+        };
+        if (Sg)
+            products(std::true_type{});
+        else
+            products(std::false_type{});
+        // the wave that holds row block 0 of column block ct
+        gc += __shfl_xor(gc, 16);
+        gc += __shfl_xor(gc, 32);
+        if (wave < KT && lg == 0) dgc[c] = gc;
 #pragma unroll
-    for (int i = 0; i < NU; ++i) {
-        const int rb = (wave + i * kBwdWaves) / KT;
-        // lane (n = c, g) holds rows 16 rb + 4 lg + j
-        const f32x4 g = rdcol4(Gb + (16 * rb + 4 * lg) * PB + c, PB);
-        dq[i] *= exp2x4(g + splat4(span1<D>(bt, 0, rb, c)));
-        dkg[i] *= -exp2x4(g + splat4(span1<D>(bt, 0, rb, c)));
-        dkt[i] *= exp2x4(splat4(span1<D>(bt, rb, 4, c)) - g);
-    }
-    __syncthreads();
+        for (int i = 0; i < NU; ++i) {
+            const int rb = (wave + i * kBwdWaves) / KT;
+            // lane (n = c, g) holds rows 16 rb + 4 lg + j
+            const f32x4 g = rdcol4(Gb + (16 * rb + 4 * lg) * PB + c, PB);
+            dq[i] *= exp2x4(g + splat4(span1<D>(bt, 0, rb, c)));
+            dkg[i] *= -exp2x4(g + splat4(span1<D>(bt, 0, rb, c)));
+            dkt[i] *= exp2x4(splat4(span1<D>(bt, rb, 4, c)) - g);
+        }
+        __syncthreads();
 
-    // ---- Q replaces V'
-    float *Qs = Xs;
-    stage_rows<D, F32IO>(Qs, q, t0, L, h, H, tid);
-    __syncthreads();
+        // ---- Q replaces V'
+        float *Qs = Xs;
+        stage_rows<D, F32IO>(Qs, q, t0, L, h, H, tid);
+        __syncthreads();
 
-    // ---- the decay-masked products of dP (S1) and dA_kk (S0, dR = Diag(beta) dA_kk)
+        // ---- the decay-masked products of dP (S1) and dA_kk (S0, dR = Diag(beta) dA_kk)
 #pragma unroll
-    for (int i = 0; i < NU; ++i) {
-        const int u = wave + i * kBwdWaves;
-        if (u >= 4 * KT) continue;
-        const int rb = u / KT, ct = u % KT;
-        const int c = 16 * ct + ln;
-        const float gmid = Gb[(16 * rb + 7) * PB + c];
-        const f32x4 grow = rdcol4(Gb + (16 * rb + 4 * lg) * PB + c, PB);
-        // forward direction, rows r in block rb:
-        //   sum_{i <= r} X_ri k_i exp2(G_r - G_i),  X = dP (to dQ) and dR (to dK)
-        f32x4 qo = zero4(), ko = zero4(), qd = zero4(), kd = zero4();
-        const float br = bet[16 * rb + ln];
-        for (int J = 0; J <= rb; ++J) {
-            const int i0 = 16 * J + 4 * lg;
-            const f32x4 gi = rdcol4(Gb + i0 * PB + c, PB);
-            const f32x4 fb = (J < rb) ? splat4(span1<D>(bt, J, rb, c)) - gi : splat4(gmid) - gi;
-            const f32x4 bk = rdcol4(Ks + i0 * PB + c, PB) * exp2x4(fb);
-            const f32x4 ap = rd4(S1 + (16 * rb + ln) * kPS + 16 * J + 4 * lg);
-            const f32x4 ar = rd4(S0 + (16 * rb + ln) * kPS + 16 * J + 4 * lg) * br;
-            if (J < rb) {
-                qo = mma_f32_k16(ap, bk, qo);
-                ko = mma_f32_k16(ar, bk, ko);
-            } else {
-                qd = mma_f32_k16(ap, bk, qd);
-                kd = mma_f32_k16(ar, bk, kd);
+        for (int i = 0; i < NU; ++i) {
+            const int u = wave + i * kBwdWaves;
+            if (u >= 4 * KT) continue;
+            const int rb = u / KT, ct = u % KT;
+            const int c = 16 * ct + ln;
+            const float gmid = Gb[(16 * rb + 7) * PB + c];
+            const f32x4 grow = rdcol4(Gb + (16 * rb + 4 * lg) * PB + c, PB);
+            // forward direction, rows r in block rb:
+            //   sum_{i <= r} X_ri k_i exp2(G_r - G_i),  X = dP (to dQ) and dR (to dK)
+            f32x4 qo = zero4(), ko = zero4(), qd = zero4(), kd = zero4();
+            const float br = bet[16 * rb + ln];
+            for (int J = 0; J <= rb; ++J) {
+                const int i0 = 16 * J + 4 * lg;
+                const f32x4 gi = rdcol4(Gb + i0 * PB + c, PB);
+                const f32x4 fb = (J < rb) ? splat4(span1<D>(bt, J, rb, c)) - gi : splat4(gmid) - gi;
+                const f32x4 bk = rdcol4(Ks + i0 * PB + c, PB) * exp2x4(fb);
+                const f32x4 ap = rd4(S1 + (16 * rb + ln) * kPS + 16 * J + 4 * lg);
+                const f32x4 ar = rd4(S0 + (16 * rb + ln) * kPS + 16 * J + 4 * lg) * br;
+                if (J < rb) {
+                    qo = mma_f32_k16(ap, bk, qo);
+                    ko = mma_f32_k16(ar, bk, ko);
+                } else {
+                    qd = mma_f32_k16(ap, bk, qd);
+                    kd = mma_f32_k16(ar, bk, kd);
+                }
             }
-        }
-        const f32x4 fo = exp2x4(grow), fd = exp2x4(grow - splat4(gmid));
-        dq[i] += qo * fo + qd * fd;
-        dkg[i] += ko * fo + kd * fd;
-        // backward direction, rows i in block rb:
-        //   sum_{r >= i} (dP_ri q_r + dR_ri k_r) exp2(G_r - G_i)
-        f32x4 xo = zero4(), xd = zero4();
-        for (int I = rb; I < 4; ++I) {
-            const int r0 = 16 * I + 4 * lg;
-            const f32x4 gr = rdcol4(Gb + r0 * PB + c, PB);
-            const f32x4 fr = (I > rb) ? gr + splat4(span1<D>(bt, rb + 1, I, c)) : gr - splat4(gmid);
-            const f32x4 ex = exp2x4(fr);
-            const f32x4 bq = rdcol4(Qs + r0 * PB + c, PB) * ex;
-            const f32x4 bk = rdcol4(Ks + r0 * PB + c, PB) * ex;
-            const f32x4 ap = rdcol4(S1 + r0 * kPS + 16 * rb + ln, kPS);
-            const f32x4 ar = rdcol4(S0 + r0 * kPS + 16 * rb + ln, kPS) * rd4(bet + r0);
-            if (I > rb) {
-                xo = mma_f32_k16(ap, bq, xo);
-                xo = mma_f32_k16(ar, bk, xo);
-            } else {
-                xd = mma_f32_k16(ap, bq, xd);
-                xd = mma_f32_k16(ar, bk, xd);
+            const f32x4 fo = exp2x4(grow), fd = exp2x4(grow - splat4(gmid));
+            dq[i] += qo * fo + qd * fd;
+            dkg[i] += ko * fo + kd * fd;
+            // backward direction, rows i in block rb:
+            //   sum_{r >= i} (dP_ri q_r + dR_ri k_r) exp2(G_r - G_i)
+            f32x4 xo = zero4(), xd = zero4();
+            for (int I = rb; I < 4; ++I) {
+                const int r0 = 16 * I + 4 * lg;
+                const f32x4 gr = rdcol4(Gb + r0 * PB + c, PB);
+                const f32x4 fr = (I > rb) ? gr + splat4(span1<D>(bt, rb + 1, I, c)) : gr - splat4(gmid);
+                const f32x4 ex = exp2x4(fr);
+                const f32x4 bq = rdcol4(Qs + r0 * PB + c, PB) * ex;
+                const f32x4 bk = rdcol4(Ks + r0 * PB + c, PB) * ex;
+                const f32x4 ap = rdcol4(S1 + r0 * kPS + 16 * rb + ln, kPS);
+                const f32x4 ar = rdcol4(S0 + r0 * kPS + 16 * rb + ln, kPS) * rd4(bet + r0);
+                if (I > rb) {
+                    xo = mma_f32_k16(ap, bq, xo);
+                    xo = mma_f32_k16(ar, bk, xo);
+                } else {
+                    xd = mma_f32_k16(ap, bq, xd);
+                    xd = mma_f32_k16(ar, bk, xd);
+                }
             }
+            dki[i] = xo * exp2x4(splat4(bt[rb * D + c]) - grow) + xd * exp2x4(splat4(gmid) - grow);
         }
-        dki[i] = xo * exp2x4(splat4(bt[rb * D + c]) - grow) + xd * exp2x4(splat4(gmid) - grow);
-    }
 
-    // ---- outputs dq, dk; the log-decay gradient terms (registers)
-    f32x4 gG[NU], gKt[NU];
+        // ---- outputs dq, dk; the log-decay gradient terms (registers)
+        f32x4 gG[NU], gKt[NU];
 #pragma unroll
-    for (int i = 0; i < NU; ++i) {
-        const int u = wave + i * kBwdWaves;
-        gG[i] = gKt[i] = zero4();
-        if (u >= 4 * KT) continue;
-        const int rb = u / KT, ct = u % KT;
-        const int c = 16 * ct + ln;
-        const f32x4 kv = rdcol4(Ks + (16 * rb + 4 * lg) * PB + c, PB);
-        const f32x4 qv = rdcol4(Qs + (16 * rb + 4 * lg) * PB + c, PB);
-        gG[i] = kv * (dkg[i] - dki[i]) + qv * dq[i];
-        gKt[i] = kv * dkt[i];
-        const f32x4 pdr = rd4(pd + 16 * rb + 4 * lg);
-        const f32x4 dqo = dq[i] + pdr * kv;
-        const f32x4 dko = dkg[i] + dki[i] + dkt[i] + pdr * qv;
+        for (int i = 0; i < NU; ++i) {
+            const int u = wave + i * kBwdWaves;
+            gG[i] = gKt[i] = zero4();
+            if (u >= 4 * KT) continue;
+            const int rb = u / KT, ct = u % KT;
+            const int c = 16 * ct + ln;
+            const f32x4 kv = rdcol4(Ks + (16 * rb + 4 * lg) * PB + c, PB);
+            const f32x4 qv = rdcol4(Qs + (16 * rb + 4 * lg) * PB + c, PB);
+            gG[i] = kv * (dkg[i] - dki[i]) + qv * dq[i];
+            gKt[i] = kv * dkt[i];
+            const f32x4 pdr = rd4(pd + 16 * rb + 4 * lg);
+            const f32x4 dqo = dq[i] + pdr * kv;
+            const f32x4 dko = dkg[i] + dki[i] + dkt[i] + pdr * qv;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * rb + 4 * lg + j;
-            if (r < L) {
-                const size_t o = ((size_t)(t0 + r) * H + h) * D + c;
-                gq[o] = dqo[j];
-                gk[o] = dko[j];
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * rb + 4 * lg + j;
+                if (r < L) {
+                    const size_t o = ((size_t)(t0 + r) * H + h) * D + c;
+                    gq[o] = dqo[j];
+                    gk[o] = dko[j];
+                }
             }
         }
-    }
-    __syncthreads();
-    // gradient of the log-decay over S0|S1, the K~ terms over K
-    float *Gg = S0, *Gt = Ks;
+        __syncthreads();
+        // gradient of the log-decay over S0|S1, the K~ terms over K
+        float *Gg = S0, *Gt = Ks;
 #pragma unroll
-    for (int i = 0; i < NU; ++i) {
-        const int u = wave + i * kBwdWaves;
-        if (u >= 4 * KT) continue;
-        const int rb = u / KT, ct = u % KT;
+        for (int i = 0; i < NU; ++i) {
+            const int u = wave + i * kBwdWaves;
+            if (u >= 4 * KT) continue;
+            const int rb = u / KT, ct = u % KT;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * rb + 4 * lg + j;
-            Gg[r * PB + 16 * ct + ln] = gG[i][j];
-            Gt[r * PB + 16 * ct + ln] = gKt[i][j];
-        }
-    }
-    __syncthreads();
-    // per channel: block sums, then the cumulative sums inside each block:
-    //   dg_t = sum_{r >= t} gG_r + sum_{r < t} gKt_r + dgC * gamma_C
-    // (gKt_r = k_r dK~_r: the factor gamma_C / Gamma_r depends on the gates of
-    // rows r + 1 .. C only, so it is summed forward, not as total - suffix)
-    float dA_acc = 0.f;
-    float zr[16];   // this thread's gate logits, fetched before the block sums
-    if (tid < 4 * D) {
-        const int c = tid % D, I = tid / D;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = 16 * I + i;
-            zr[i] = r < L ? z[((size_t)(t0 + r) * H + h) * D + c] : 0.f;
-        }
-        float s = 0.f, st = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            s += Gg[(16 * I + i) * PB + c];
-            st += Gt[(16 * I + i) * PB + c];
-        }
-        red[I * D + c] = s;
-        red[(4 + I) * D + c] = st;
-    }
-    __syncthreads();
-    if (tid < 4 * D) {
-        const int c = tid % D, I = tid / D;
-        float fw[16];
-        float pre = 0.f;
-        for (int m = 0; m < I; ++m) pre += red[(4 + m) * D + c];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            fw[i] = pre;
-            pre += Gt[(16 * I + i) * PB + c];
-        }
-        const float base = dgc[c] * fast_exp2(span1<D>(bt, 0, 4, c));
-        float run = 0.f;
-        for (int m = I + 1; m < 4; ++m) run += red[m * D + c];
-#pragma unroll
-        for (int i = 15; i >= 0; --i) {
-            const int r = 16 * I + i;
-            run += Gg[r * PB + c];
-            const float dg = run + fw[i] + base;
-            if (r < L) {
-                const size_t o = ((size_t)(t0 + r) * H + h) * D + c;
-                // sigmoid'(x) = e / (1 + e)^2 with e = exp(-|x|): no cancellation
-                // where the gate saturates
-                const float x = ea * zr[i];
-                const float ex = fast_exp2(-fabsf(x) * kLog2e);
-                const float dx = dg * -5.0f * ex * __builtin_amdgcn_rcpf((1.f + ex) * (1.f + ex));
-                gz[o] = dx * ea;
-                dA_acc += dx * x;
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * rb + 4 * lg + j;
+                Gg[r * PB + 16 * ct + ln] = gG[i][j];
+                Gt[r * PB + 16 * ct + ln] = gKt[i][j];
             }
         }
-    }
-    // fixed-order block reduction of the A gradient
-    for (int off = 32; off > 0; off >>= 1) dA_acc += __shfl_xor(dA_acc, off);
-    if (lane == 0) part[wave] = dA_acc;
-    __syncthreads();
-    if (tid == 0) {
-        float s = 0.f;
-        for (int w = 0; w < kBwdWaves; ++w) s += part[w];
-        dA_part[(size_t)chunk * H + h] = s;
+        __syncthreads();
+        // per channel: block sums, then the cumulative sums inside each block:
+        //   dg_t = sum_{r >= t} gG_r + sum_{r < t} gKt_r + dgC * gamma_C
+        // (gKt_r = k_r dK~_r: the factor gamma_C / Gamma_r depends on the gates of
+        // rows r + 1 .. C only, so it is summed forward, not as total - suffix)
+        // the next item's rows, beta and T, into registers while this one
+        // finishes (its gate logits follow once the dz pass is done).  The
+        // loads are issued on every pass, the last one reloading this item,
+        // so that the registers are fully redefined and no old value stays
+        // live across the item.
+        const int it_next = it + gridDim.x < total ? it + gridDim.x : it;
+        ent = table[it_next / H];
+        load_grad_rows<D, F32IO>(R, k, vin, beta, rec(it_next) + IT::t, ent.y, ent.z, it_next % H, H, tid);
+        float dA_acc = 0.f;
+        float zr[16];   // this thread's gate logits, fetched before the block sums
+        if (tid < 4 * D) {
+            const int c = tid % D, I = tid / D;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = 16 * I + i;
+                zr[i] = r < L ? z[((size_t)(t0 + r) * H + h) * D + c] : 0.f;
+            }
+            float s = 0.f, st = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s += Gg[(16 * I + i) * PB + c];
+                st += Gt[(16 * I + i) * PB + c];
+            }
+            red[I * D + c] = s;
+            red[(4 + I) * D + c] = st;
+        }
+        __syncthreads();
+        if (tid < 4 * D) {
+            const int c = tid % D, I = tid / D;
+            float fw[16];
+            float pre = 0.f;
+            for (int m = 0; m < I; ++m) pre += red[(4 + m) * D + c];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                fw[i] = pre;
+                pre += Gt[(16 * I + i) * PB + c];
+            }
+            const float base = dgc[c] * fast_exp2(span1<D>(bt, 0, 4, c));
+            float run = 0.f;
+            for (int m = I + 1; m < 4; ++m) run += red[m * D + c];
+#pragma unroll
+            for (int i = 15; i >= 0; --i) {
+                const int r = 16 * I + i;
+                run += Gg[r * PB + c];
+                const float dg = run + fw[i] + base;
+                if (r < L) {
+                    const size_t o = ((size_t)(t0 + r) * H + h) * D + c;
+                    // sigmoid'(x) = e / (1 + e)^2 with e = exp(-|x|): no cancellation
+                    // where the gate saturates
+                    const float x = ea * zr[i];
+                    const float ex = fast_exp2(-fabsf(x) * kLog2e);
+                    const float dx = dg * -5.0f * ex * __builtin_amdgcn_rcpf((1.f + ex) * (1.f + ex));
+                    gz[o] = dx * ea;
+                    dA_acc += dx * x;
+                }
+            }
+        }
+        load_grad_z<D, F32IO>(R, z, ent.y, ent.z, it_next % H, H, tid);
+        // fixed-order block reduction of the A gradient
+        for (int off = 32; off > 0; off >>= 1) dA_acc += __shfl_xor(dA_acc, off);
+        if (lane == 0) part[wave] = dA_acc;
+        __syncthreads();
+        if (tid == 0) {
+            float s = 0.f;
+            for (int w = 0; w < kBwdWaves; ++w) s += part[w];
+            dA_part[(size_t)chunk * H + h] = s;
+        }
     }
 }
 
@@ -1295,14 +1367,15 @@ int launch_backward_t(const BackwardArgs &a) {
         using SH = ChainShape<D>;
         const int groups = SH::KT / SH::NW;
         if (!set_lds(&bwd_chain_kernel<D, F32IO>, SH::lds_bytes)) return -1;
-        hipLaunchKernelGGL((bwd_chain_kernel<D, F32IO>), dim3(a.N * a.H * groups), dim3(SH::NT), SH::lds_bytes, a.stream,
-                           meta, a.dhT, items, a.N, a.H, max_chunks, groups, a.gh0);
+        hipLaunchKernelGGL((bwd_chain_kernel<D, F32IO>), dim3(a.N * a.H * groups), dim3(SH::NT), SH::lds_bytes,
+                           a.stream, meta, a.dhT, items, a.N, a.H, max_chunks, groups, a.gh0);
         if (hipGetLastError() != hipSuccess) return -1;
     }
     if (blocks > 0) {
         const size_t lds = sizeof(float) * GradLds<D>::floats;
         if (!set_lds(&bwd_grad_kernel<D, F32IO>, lds)) return -1;
-        hipLaunchKernelGGL((bwd_grad_kernel<D, F32IO>), dim3((unsigned)blocks), dim3(kBwdThreads), lds, a.stream,
+        const unsigned grid = (unsigned)std::min<long long>(blocks, (long long)device_cus());
+        hipLaunchKernelGGL((bwd_grad_kernel<D, F32IO>), dim3(grid), dim3(kBwdThreads), lds, a.stream,
                            a.q, a.k, a.v, a.z, a.A, a.beta, a.h0, a.dO, meta, table, ck_off, ck, p.ck_cap, a.N,
                            a.H, max_chunks, items, a.gq, a.gk, a.gv, a.gz, a.gbeta, part);
         if (hipGetLastError() != hipSuccess) return -1;
