@@ -217,6 +217,7 @@ struct GradIn {
     float z[16];
     float beta;
     f32x4 t[64 * 16 / kBwdThreads];
+    f32x4 s[D / 16];   // the state's rows 16 (wave % KT) + ln, all key quads: B operands of V~
 };
 
 template <int D, bool F32IO>
@@ -237,6 +238,12 @@ __device__ __forceinline__ void load_grad_rows(GradIn<D, F32IO> &R, const void *
         const int i = tid + s * kBwdThreads;
         R.t[s] = rd4(item_t + (i >> 4) * 64 + 4 * (i & 15));
     }
+}
+template <int D, bool F32IO>
+__device__ __forceinline__ void load_grad_state(GradIn<D, F32IO> &R, const float *Sg, int nt, int ln, int lg) {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+        R.s[kk] = Sg ? rd4(Sg + (size_t)(16 * nt + ln) * D + 16 * kk + 4 * lg) : zero4();
 }
 template <int D, bool F32IO>
 __device__ __forceinline__ void load_grad_z(GradIn<D, F32IO> &R, const float *z, int t0, int L, int h, int H,
@@ -788,10 +795,19 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
     int it = blockIdx.x;
     if (it >= total) return;
     auto rec = [&](int i) { return items + ((size_t)(i % H) * max_chunks + i / H) * IT::floats; };
+    // state at the start of chunk `chunk` of sequence n, [v][c]; NULL = zero
+    auto state_of = [&](int chunk, int h, int n) -> const float * {
+        const int j = chunk - meta[n];
+        if (j == 0) return h0 ? h0 + ((size_t)n * H + h) * D * D : nullptr;
+        if (!ck) return nullptr;
+        const int idx = ck_off[n] + j - 1;
+        return (idx >= 0 && idx < ck_cap) ? ck + ((size_t)idx * H + h) * D * D : nullptr;
+    };
     GradIn<D, F32IO> R;
     int4 ent = table[it / H];
     load_grad_rows<D, F32IO>(R, k, vin, beta, rec(it) + IT::t, ent.y, ent.z, it % H, H, threadIdx.x);
     load_grad_z<D, F32IO>(R, z, ent.y, ent.z, it % H, H, threadIdx.x);
+    load_grad_state<D, F32IO>(R, state_of(it / H, it % H, ent.x), wave % KT, threadIdx.x & 15, (threadIdx.x >> 4) & 3);
 
     // persistent: items blockIdx.x, + gridDim.x, ...  Every LDS region but
     // `part` is last read before an item's final barrier, and `part` is next
@@ -808,17 +824,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
         const float *dvr = item + IT::dvr;  // dV' [t][v]
         const float *dsp = item + IT::ys;   // dS' [c][v]
         const float ea = __expf(A[h]);
-        // state at the chunk's start, [v][c]; NULL = zero
-        const float *Sg = nullptr;
-        {
-            const int j = chunk - meta[n];
-            if (j == 0) {
-                if (h0) Sg = h0 + ((size_t)n * H + h) * D * D;
-            } else if (ck) {
-                const int idx = ck_off[n] + j - 1;
-                if (idx >= 0 && idx < ck_cap) Sg = ck + ((size_t)idx * H + h) * D * D;
-            }
-        }
+        const float *Sg = state_of(chunk, h, n);   // the state at the chunk's start
         auto row_io = [&](const void *p, int r, int c) -> f32x4 {
             return r < L ? load_io4<F32IO>(p, ((size_t)(t0 + r) * H + h) * D + c) : zero4();
         };
@@ -853,10 +859,10 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
                     const int c = 16 * kk + 4 * lg;
                     return rd4(Ks + r * PB + c) * exp2x4(rd4(Gb + r * PB + c) + span4<D>(bt, 0, mt, c));
                 };
-                auto sb = [&](int kk) { return rd4(Sg + (size_t)(16 * nt + ln) * D + 16 * kk + 4 * lg); };
+                // B operands: the state's rows 16 nt + ln, fetched during the previous item
 #pragma unroll
                 for (int kp = 0; kp < KT / 2; ++kp)
-                    acc = mma_k32<F32IO>(kg(2 * kp), kg(2 * kp + 1), sb(2 * kp), sb(2 * kp + 1), acc);
+                    acc = mma_k32<F32IO>(kg(2 * kp), kg(2 * kp + 1), R.s[2 * kp], R.s[2 * kp + 1], acc);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) Xs[(16 * mt + 4 * lg + j) * PB + 16 * nt + ln] -= acc[j];
@@ -1248,6 +1254,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
         const int it_next = it + gridDim.x < total ? it + gridDim.x : it;
         ent = table[it_next / H];
         load_grad_rows<D, F32IO>(R, k, vin, beta, rec(it_next) + IT::t, ent.y, ent.z, it_next % H, H, tid);
+        load_grad_state<D, F32IO>(R, state_of(it_next / H, it_next % H, ent.x), wave % KT, ln, lg);
         float dA_acc = 0.f;
         float zr[16];   // this thread's gate logits, fetched before the block sums
         if (tid < 4 * D) {
