@@ -266,25 +266,25 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int c = tid; c < D; c += 256) {
             const float b0 = bt_lds[c], b1 = bt_lds[D + c], b2 = bt_lds[2 * D + c], b3 = bt_lds[3 * D + c];
             float *f = fac_lds + c;
-            f[0 * D] = exp2f(-b0);
-            f[1 * D] = exp2f(-b1);
-            f[2 * D] = exp2f(-b2);
-            f[3 * D] = exp2f(-b3);
+            f[0 * D] = fast_exp2(-b0);
+            f[1 * D] = fast_exp2(-b1);
+            f[2 * D] = fast_exp2(-b2);
+            f[3 * D] = fast_exp2(-b3);
             f[4 * D] = 1.f;
-            f[5 * D] = exp2f(b0);
-            f[6 * D] = exp2f(b0 + b1);
-            f[7 * D] = exp2f(b0 + b1 + b2);
-            f[8 * D] = exp2f(b1 + b2 + b3);
-            f[9 * D] = exp2f(b2 + b3);
-            f[10 * D] = exp2f(b3);
+            f[5 * D] = fast_exp2(b0);
+            f[6 * D] = fast_exp2(b0 + b1);
+            f[7 * D] = fast_exp2(b0 + b1 + b2);
+            f[8 * D] = fast_exp2(b1 + b2 + b3);
+            f[9 * D] = fast_exp2(b2 + b3);
+            f[10 * D] = fast_exp2(b3);
             f[11 * D] = 1.f;
             f[12 * D] = 1.f;             // (0,1)
-            f[13 * D] = exp2f(b1);       // (0,2)
-            f[14 * D] = exp2f(b1 + b2);  // (0,3)
+            f[13 * D] = fast_exp2(b1);       // (0,2)
+            f[14 * D] = fast_exp2(b1 + b2);  // (0,3)
             f[15 * D] = 1.f;             // (1,2)
-            f[16 * D] = exp2f(b2);       // (1,3)
+            f[16 * D] = fast_exp2(b2);       // (1,3)
             f[17 * D] = 1.f;             // (2,3)
-            reinterpret_cast<float *>(slab + SL::gamma)[c] = exp2f(b0 + b1 + b2 + b3);
+            reinterpret_cast<float *>(slab + SL::gamma)[c] = fast_exp2(b0 + b1 + b2 + b3);
         }
         __syncthreads();
 
