@@ -59,6 +59,10 @@ CASES = [
     ("bf16", 128, 3, [300, 64, 17, 0, 129], True, True, 0),
     ("bf16", 32, 2, [1000, 63], True, True, 3),
     ("bf16", 64, 2, [777], False, True, 0),
+    # more (chunk, head) items than CUs, over several sequences: the persistent
+    # local and grad kernels carry the next item's inputs across sequence ends
+    ("bf16", 32, 2, [3000, 5000, 100, 0, 4100], True, True, 0),
+    ("f32", 32, 2, [4100, 0, 3000, 5000, 100], True, True, 0),
 ]
 
 
