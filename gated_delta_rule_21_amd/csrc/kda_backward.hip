@@ -112,15 +112,6 @@ __device__ __forceinline__ f32x4 mma_k32_exact_b(f32x4 a0, f32x4 a1, f32x4 b0, f
     return mma_bf16_k32(al, bh, acc);
 }
 
-// And for an A operand that holds bf16 values exactly: only B is split.
-__device__ __forceinline__ f32x4 mma_k32_exact_a(f32x4 a0, f32x4 a1, f32x4 b0, f32x4 b1, f32x4 acc) {
-    u32x4 bh, bl;
-    quads_to_bf16_split(b0, b1, bh, bl);
-    const u32x4 ah = quads_to_bf16(a0, a1);
-    acc = mma_bf16_k32(ah, bh, acc);
-    return mma_bf16_k32(ah, bl, acc);
-}
-
 // sum_{m = lo}^{hi - 1} bt[m][c] (zero when lo >= hi); bt is [4][D].
 template <int D>
 __device__ __forceinline__ f32x4 span4(const float *bt, int lo, int hi, int c) {
@@ -945,8 +936,26 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
             const int u = wave + i * kBwdWaves;
             if (u < 4 * KT) {
                 const int mt = u / KT, nt = u % KT;
+                if constexpr (F32IO) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) Xs[(16 * mt + 4 * lg + j) * PB + 16 * nt + ln] = vp[i][j];
+                    for (int j = 0; j < 4; ++j) Xs[(16 * mt + 4 * lg + j) * PB + 16 * nt + ln] = vp[i][j];
+                } else {
+                    // bf16 path: V' split once into bf16 hi + lo; each 16-byte row
+                    // quad holds [4 hi | 4 lo] in place of its four floats, the
+                    // order quads_to_bf16_split gives, so readers take the
+                    // fragments as loaded
+                    uint16_t *xb = reinterpret_cast<uint16_t *>(Xs);
+                    const int c = 16 * nt + ln;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float x = vp[i][j];
+                        const uint32_t hb = f32x2_to_bf16x2(x, 0.f) & 0xffffu;
+                        const uint32_t lb = f32x2_to_bf16x2(x - bf16_bits_to_f32(hb), 0.f) & 0xffffu;
+                        const size_t e = (size_t)(16 * mt + 4 * lg + j) * (2 * PB) + (c >> 2) * 8 + (c & 3);
+                        xb[e] = (uint16_t)hb;
+                        xb[e + 4] = (uint16_t)lb;
+                    }
+                }
             }
         }
 
@@ -1042,9 +1051,13 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
                     if constexpr (F32IO)
                         acc = mma_k32<true>(row_io(dO, 16 * mt + ln, c0), row_io(dO, 16 * mt + ln, c1),
                                             rd4(br + 32 * kp), rd4(br + 32 * kp + 16), acc);
-                    else   // dO is exactly bf16
-                        acc = mma_k32_exact_a(row_io(dO, 16 * mt + ln, c0), row_io(dO, 16 * mt + ln, c1),
-                                              rd4(br + 32 * kp), rd4(br + 32 * kp + 16), acc);
+                    else {   // dO is exactly bf16; V' is stored split
+                        const u32x4 q0 = *reinterpret_cast<const u32x4 *>(br + 32 * kp);
+                        const u32x4 q1 = *reinterpret_cast<const u32x4 *>(br + 32 * kp + 16);
+                        const u32x4 ah = quads_to_bf16(row_io(dO, 16 * mt + ln, c0), row_io(dO, 16 * mt + ln, c1));
+                        acc = mma_bf16_k32(ah, u32x4{q0[0], q0[1], q1[0], q1[1]}, acc);
+                        acc = mma_bf16_k32(ah, u32x4{q0[2], q0[3], q1[2], q1[3]}, acc);
+                    }
                 }
             }
 #pragma unroll
@@ -1090,13 +1103,13 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_grad_kernel(
                     const int r = 16 * ((wave + i * kBwdWaves) / KT) + ln;
                     const bool rok = r < L;
                     const size_t orow = ((size_t)(t0 + r) * H + h) * D;
-                    const f32x4 x0 = rd4(Xs + r * PB + v0), x1 = rd4(Xs + r * PB + v1);
                     if constexpr (F32IO) {
-                        dkt[i] = mma_k32<true>(x0, x1, ds0, ds1, dkt[i]);
-                    } else {
-                        u32x4 xh, xl;
-                        quads_to_bf16_split(x0, x1, xh, xl);
-                        dkt[i] = mma3_bf16(xh, xl, dsh, dsl, dkt[i]);
+                        dkt[i] = mma_k32<true>(rd4(Xs + r * PB + v0), rd4(Xs + r * PB + v1), ds0, ds1, dkt[i]);
+                    } else {   // V' is stored split
+                        const u32x4 q0 = *reinterpret_cast<const u32x4 *>(Xs + r * PB + v0);
+                        const u32x4 q1 = *reinterpret_cast<const u32x4 *>(Xs + r * PB + v1);
+                        dkt[i] = mma3_bf16(u32x4{q0[0], q0[1], q1[0], q1[1]}, u32x4{q0[2], q0[3], q1[2], q1[3]}, dsh,
+                                           dsl, dkt[i]);
                     }
                     if constexpr (HS) {
                         const f32x4 z0 = rok ? rd4(gv + orow + v0) : zero4(), z1 = rok ? rd4(gv + orow + v1) : zero4();
