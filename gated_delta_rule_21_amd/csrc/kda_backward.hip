@@ -32,10 +32,11 @@
 //      order (the result does not depend on scheduling).
 //
 // Everything after the forward recompute accumulates in fp32.  fp32 inputs:
-// fp32 16x16x4 MFMA throughout.  bf16 inputs: the chain's two products, V~
-// and the products against S and dS' take both operands split into bf16
-// hi + lo (three 16x16x32 MFMAs, about 2^-16 relative per term); the rest
-// stays on fp32 MFMA.
+// fp32 16x16x4 MFMA throughout.  bf16 inputs: the products run on K32 pairs of
+// 16x16x32 bf16 MFMAs with each fp32 operand split into bf16 hi + lo (three
+// MFMAs, about 2^-16 relative per term; two when the other operand is the
+// exact bf16 dO); the blocked inverse (T) and the decay-masked products of
+// dP and dA_kk stay on fp32 MFMA.
 // Decay factors: a 64-token chunk can decay by e^-320, so no Gamma or 1/Gamma
 // over a chunk is formed where the quotient of two would be needed.  Log2
 // decays are kept relative to the start of each 16-token block (Gb) with the
