@@ -47,32 +47,49 @@ PREFILL_SOURCES = ("kda_prefill.hip", "kda_intra.hip", "kda_intra_f32.hip", "kda
 
 
 def kernel_sources_digest() -> str:
-    """sha256 (first 16 hex digits) over the prefill kernels' sources."""
+    """sha256 (first 16 hex digits) over the prefill kernels' sources, with
+    comments and whitespace removed: a figure taken on the kernels stays
+    valid through comment edits and goes stale with any change to the code."""
     import hashlib
+    import re
     files = [os.path.join(ROOT, "gated_delta_rule_21_amd", "csrc", f) for f in PREFILL_SOURCES]
     h = hashlib.sha256()
     for f in files:
         h.update(os.path.relpath(f, ROOT).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            code = fh.read()
+        code = re.sub(r"/\*.*?\*/", "", code, flags=re.S)     # block comments
+        code = re.sub(r"//[^\n]*", "", code)                    # line comments
+        h.update("".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per kda_prefill launch from the committed FETCH_SIZE / WRITE_SIZE
-    summary, or None when the kernels have changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", "kda_k3_traffic.md")
+def profile_value(fname: str, key: str):
+    """An integer `key: value` line of a committed rocprofv3 summary under
+    profiles/, or None when the file is missing or the prefill kernels' sources
+    have changed since it was taken (its `sources_sha256` line differs)."""
+    path = os.path.join(ROOT, "profiles", fname)
     if not os.path.exists(path):
         return None
     vals = {}
     with open(path) as f:
         for line in f:
             parts = line.strip().split(":")
-            if len(parts) == 2 and parts[0] in ("prefill_traffic_bytes", "sources_sha256"):
+            if len(parts) == 2 and parts[0] in (key, "sources_sha256"):
                 vals[parts[0]] = parts[1].strip()
-    if vals.get("sources_sha256") != kernel_sources_digest() or "prefill_traffic_bytes" not in vals:
+    if vals.get("sources_sha256") != kernel_sources_digest() or key not in vals:
         return None
-    return int(vals["prefill_traffic_bytes"])
+    return int(vals[key])
+
+
+def measured_traffic():
+    """HBM bytes per kda_prefill launch (FETCH_SIZE / WRITE_SIZE summary)."""
+    return profile_value("kda_k3_traffic.md", "prefill_traffic_bytes")
+
+
+def counted_mfma_flops():
+    """16-bit MFMA FLOPs per kda_prefill launch (SQ_INSTS_VALU_MFMA_MOPS_* x 512)."""
+    return profile_value("kda_k3_prefill_counters.md", "prefill_mfma16_flops")
 
 
 def parse():
@@ -100,6 +117,18 @@ def parse():
                    help="after timing, run one plain device copy of this many GiB (a known "
                         "byte count that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
+
+
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (or the platform string)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def cpu_baseline(pre: dict, target_s: float) -> dict:
@@ -131,38 +160,44 @@ def cpu_baseline(pre: dict, target_s: float) -> dict:
         dt = run(tok)
     return {"value": tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "fp64 token-loop oracle (C, OpenMP over heads) on the first %d of %d tokens "
-                      "of all %d heads of the prefill workload, %.2f s wall; host %s, %d logical "
-                      "cores" % (tok, T, H, dt, platform.processor() or platform.machine(), cores)}
+                      "of all %d heads of the prefill workload, %.2f s wall; host CPU %s, %d logical "
+                      "cores, %d threads used" % (tok, T, H, dt, cpu_model(), cores, threads)}
 
 
-def small_head_prefill(kda, W, dev, reps: int = 10) -> dict:
+def small_head_prefill(kda, W, dev, reps: int = 12, sets: int = 3) -> dict:
     """Side measurement: the small-head prefill (B=2, H=8, T=8192 each,
     d=128, bf16), split into segments by the automatic choice and unsplit.
-    HIP events on the launch stream, inputs resident, workspace preallocated."""
+    One set of inputs and outputs is about 235 MB, under the 256 MB Infinity
+    Cache, so the timed calls rotate over `sets` independently drawn sets
+    (about 0.7 GB in all).  HIP events on the launch stream, inputs resident,
+    workspace preallocated."""
     import torch
-    d = W.make("small_head", device=dev)
-    T, H, D = d["q"].shape
-    N = d["cu_seqlens"].numel() - 1
-    o = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
-    hT = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
-    out = {"workload": "small_head B=2 H=8 T=8192 per sequence d=128 bf16, h0 given"}
+    ins = [W.make("small_head", device=dev, seed=W.BASE_SEED + 1 + 100 * i) for i in range(sets)]
+    T, H, D = ins[0]["q"].shape
+    N = ins[0]["cu_seqlens"].numel() - 1
+    outs = [(torch.empty((T, H, D), dtype=torch.bfloat16, device=dev),
+             torch.empty((N, H, D, D), dtype=torch.float32, device=dev)) for _ in range(sets)]
+    out = {"workload": "small_head B=2 H=8 T=8192 per sequence d=128 bf16, h0 given; %d input sets "
+                       "rotated" % sets}
     for P, key in ((0, "auto"), (1, "unsplit")):
-        with kda.prefill_segments(P):
-            segs = kda.kda_prefill_segments(N, T, H, D, D, kda.KDA_BF16)
-            ws = kda.prefill_workspace(N, T, H, D, kda.KDA_BF16, dev)
-            run = lambda: kda.prefill(d["q"], d["k"], d["v"], d["z"], d["A"], d["beta"],
-                                      d["cu_seqlens"], h0=d["h0"], o=o, hT=hT, workspace=ws)
-            for _ in range(3):
-                run()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            e0.record()
-            for _ in range(reps):
-                run()
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / reps
-            del ws
+        segs = P if P > 0 else kda.kda_prefill_segments(N, T, H, D, D, kda.KDA_BF16)
+        ws = kda.prefill_workspace(N, T, H, D, kda.KDA_BF16, dev, segments=P)
+
+        def run(i):
+            d, (o, hT) = ins[i % sets], outs[i % sets]
+            kda.prefill(d["q"], d["k"], d["v"], d["z"], d["A"], d["beta"], d["cu_seqlens"], h0=d["h0"],
+                        o=o, hT=hT, workspace=ws, segments=P)
+        for i in range(sets):
+            run(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(reps):
+            run(i)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        del ws
         out[key] = {"segments": segs, "ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1)}
     return out
 
@@ -396,6 +431,7 @@ def main():
 
     pairs = T * H
     traffic = measured_traffic()
+    mfma_flops = counted_mfma_flops()
     pre_bytes = PREFILL_BYTES_PER_PAIR * pairs
     pre_gbps = pre_bytes / (pre_ms * 1e-3) / 1e9
     pre_tflops = PREFILL_FLOPS_PER_PAIR * pairs / (pre_ms * 1e-3) / 1e12
@@ -404,8 +440,10 @@ def main():
 
     line = {
         "metric": METRIC,
-        "value": round((T + Nd) / (step_ms * 1e-3), 1),
+        "value": round(T / (pre_ms * 1e-3), 1),
         "unit": "tokens/s",
+        "value_is": "prefill tokens/s: %d tokens / the mean kda_prefill time (HIP events on the launch "
+                    "stream) over the timed steps; decode is reported under 'decode'" % T,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -423,7 +461,11 @@ def main():
                     "algorithmic_GBps": round(pre_gbps, 1),
                     "hbm_frac": round(pre_gbps / HBM_PEAK_GBPS, 4),
                     "useful_TFLOPs": round(pre_tflops, 2),
-                    "mfma_useful_frac": round(pre_tflops / BF16_DENSE_PEAK_TFLOPS, 4)},
+                    "mfma_useful_frac": round(pre_tflops / BF16_DENSE_PEAK_TFLOPS, 4),
+                    "mfma_counted_frac": (None if mfma_flops is None else
+                                          round(mfma_flops / (pre_ms * 1e-3) / 1e12 / BF16_DENSE_PEAK_TFLOPS, 4)),
+                    "mfma_counted_source": "profiles/kda_k3_prefill_counters.md: 16-bit MFMA MOPS x 512 per "
+                                           "launch (rocprofv3 --pmc) / this run's launch time"},
         "decode": {"ms_per_step": round(dec_ms, 4), "steps": args.decode_steps,
                    "state_GBps": round(dec_gbps, 1), "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                    "ms_in_step": round(dec_ms_step, 4)},

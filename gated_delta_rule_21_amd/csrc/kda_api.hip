@@ -59,12 +59,46 @@ const char *kda_build_info(void) {
            "fp32 MFMA 16x16x4, d in {32,64,128}";
 }
 
-size_t kda_prefill_workspace_size(int N, int T, int H, int dk, int dv, kda_dtype io_dtype) {
+}  // extern "C"
+
+namespace {
+
+// Segment count of a call: the caller's, or the automatic choice (0).
+// -1 for an out-of-range request.
+int segments_of(const kda_prefill_options *opt, int N, int T, int H, int d) {
+    const int s = opt ? opt->segments : 0;
+    if (s < 0 || s > KDA_MAX_PREFILL_SEGMENTS) return -1;
+    return s > 0 ? s : kda::choose_segments(N, T, H, d);
+}
+
+bool checkpoints_requested(const kda_prefill_options *opt) {
+    return opt && (opt->checkpoints || opt->checkpoint_offsets);
+}
+
+size_t prefill_ws(int N, int T, int H, int dk, int dv, kda_dtype io_dtype, const kda_prefill_options *opt) {
     if (io_dtype != KDA_BF16 && io_dtype != KDA_F32) return 0;
     if (!supported_dim(dk, dv) || N < 0 || T < 0 || H <= 0) return 0;
+    const int P = segments_of(opt, N, T, H, dk);
+    if (P < 1) return 0;
     kda::PrefillPlan p;
-    if (!kda::plan_prefill(N, T, H, dk, dv, io_dtype == KDA_F32, kda::choose_segments(N, T, H, dk), &p)) return 0;
+    if (!kda::plan_prefill(N, T, H, dk, dv, io_dtype == KDA_F32, P, &p)) return 0;
     return p.total;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_prefill_workspace_size(int N, int T, int H, int dk, int dv, kda_dtype io_dtype) {
+    return prefill_ws(N, T, H, dk, dv, io_dtype, nullptr);
+}
+
+size_t kda_prefill_ex_workspace_size(int N, int T, int H, int dk, int dv, kda_dtype io_dtype,
+                                     const kda_prefill_options *options) {
+    if (checkpoints_requested(options) &&
+        (options->checkpoint_interval <= 0 || options->checkpoint_interval % 64 != 0))
+        return 0;
+    return prefill_ws(N, T, H, dk, dv, io_dtype, options);
 }
 
 int kda_prefill_segments(int N, int T, int H, int dk, int dv, kda_dtype io_dtype) {
@@ -73,22 +107,21 @@ int kda_prefill_segments(int N, int T, int H, int dk, int dv, kda_dtype io_dtype
     return kda::choose_segments(N, T, H, dk);
 }
 
-int kda_set_prefill_segments(int segments) {
-    if (segments < 0 || segments > KDA_MAX_PREFILL_SEGMENTS) return KDA_ERR_INVALID_ARGUMENT;
-    kda::set_prefill_segments(segments);
-    return KDA_OK;
-}
-
 }  // extern "C"
 
 namespace {
 
 int prefill_impl(kda_dtype io_dtype, const void *q, const void *k, const void *v, const float *z,
                  const float *A, const float *beta, const float *h0, const int32_t *cu_seqlens, int N,
-                 int T, int H, int dk, int dv, void *o, float *hT, int interval, float *ck,
-                 int32_t *ck_offsets, void *workspace, size_t workspace_bytes, void *stream) {
+                 int T, int H, int dk, int dv, void *o, float *hT, const kda_prefill_options *opt,
+                 void *workspace, size_t workspace_bytes, void *stream) {
     if (io_dtype != KDA_BF16 && io_dtype != KDA_F32) return KDA_ERR_UNSUPPORTED_DTYPE;
+    float *ck = opt ? opt->checkpoints : nullptr;
+    int32_t *ck_offsets = opt ? opt->checkpoint_offsets : nullptr;
+    const int interval = (ck || ck_offsets) ? opt->checkpoint_interval : 0;
     if ((ck || ck_offsets) && (interval <= 0 || interval % 64 != 0)) return KDA_ERR_INVALID_ARGUMENT;
+    const int P = segments_of(opt, N, T, H, dk);
+    if (P < 1) return KDA_ERR_INVALID_ARGUMENT;
     if (N < 0 || T < 0 || H <= 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!supported_dim(dk, dv)) return KDA_ERR_UNSUPPORTED_DIM;
     if (!A || !cu_seqlens || !workspace) return KDA_ERR_NULL_POINTER;
@@ -99,8 +132,7 @@ int prefill_impl(kda_dtype io_dtype, const void *q, const void *k, const void *v
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_MISALIGNED;
 
     kda::PrefillPlan plan;
-    if (!kda::plan_prefill(N, T, H, dk, dv, io_dtype == KDA_F32, kda::choose_segments(N, T, H, dk), &plan))
-        return KDA_ERR_INVALID_ARGUMENT;
+    if (!kda::plan_prefill(N, T, H, dk, dv, io_dtype == KDA_F32, P, &plan)) return KDA_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < plan.total) return KDA_ERR_WORKSPACE_TOO_SMALL;
 
     const size_t tok = (size_t)T * H;
@@ -147,7 +179,7 @@ int prefill_impl(kda_dtype io_dtype, const void *q, const void *k, const void *v
     a.o = o; a.hT = hT;
     a.ck = ck_bytes > 0 ? ck : nullptr;
     a.ck_offsets = ck_offsets;
-    a.ck_interval = (ck || ck_offsets) ? interval : 0;
+    a.ck_interval = interval;
     a.ws = static_cast<unsigned char *>(workspace);
     a.plan = plan;
     a.stream = st;
@@ -162,24 +194,27 @@ int kda_prefill(kda_dtype io_dtype, const void *q, const void *k, const void *v,
                 const float *A, const float *beta, const float *h0, const int32_t *cu_seqlens,
                 int N, int T, int H, int dk, int dv, void *o, float *hT, void *workspace,
                 size_t workspace_bytes, void *stream) {
-    return prefill_impl(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv, o, hT, 0, nullptr,
-                        nullptr, workspace, workspace_bytes, stream);
+    return prefill_impl(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv, o, hT, nullptr,
+                        workspace, workspace_bytes, stream);
 }
 
-int kda_prefill_checkpoints(kda_dtype io_dtype, const void *q, const void *k, const void *v,
-                            const float *z, const float *A, const float *beta, const float *h0,
-                            const int32_t *cu_seqlens, int N, int T, int H, int dk, int dv, void *o,
-                            float *hT, int interval, float *checkpoints, int32_t *checkpoint_offsets,
-                            void *workspace, size_t workspace_bytes, void *stream) {
-    return prefill_impl(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv, o, hT, interval,
-                        checkpoints, checkpoint_offsets, workspace, workspace_bytes, stream);
+int kda_prefill_ex(kda_dtype io_dtype, const void *q, const void *k, const void *v, const float *z,
+                   const float *A, const float *beta, const float *h0, const int32_t *cu_seqlens, int N,
+                   int T, int H, int dk, int dv, void *o, float *hT, const kda_prefill_options *options,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+    return prefill_impl(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv, o, hT, options,
+                        workspace, workspace_bytes, stream);
 }
 
-size_t kda_prefill_backward_workspace_size(int N, int T, int H, int dk, int dv, kda_dtype io_dtype) {
+size_t kda_prefill_backward_workspace_size(int N, int T, int H, int dk, int dv, kda_dtype io_dtype,
+                                           const kda_prefill_options *options) {
     if (io_dtype != KDA_BF16 && io_dtype != KDA_F32) return 0;
     if (!supported_dim(dk, dv) || N < 0 || T < 0 || H <= 0) return 0;
+    if (checkpoints_requested(options) || (options && options->checkpoint_interval != 0)) return 0;
+    const int P = segments_of(options, N, T, H, dk);
+    if (P < 1) return 0;
     kda::BackwardPlan p;
-    if (!kda::plan_backward(N, T, H, dk, io_dtype == KDA_F32, kda::choose_segments(N, T, H, dk), &p)) return 0;
+    if (!kda::plan_backward(N, T, H, dk, io_dtype == KDA_F32, P, &p)) return 0;
     return p.total;
 }
 
@@ -187,10 +222,14 @@ int kda_prefill_backward(kda_dtype io_dtype, const void *q, const void *k, const
                          const float *A, const float *beta, const float *h0, const int32_t *cu_seqlens,
                          int N, int T, int H, int dk, int dv, const void *grad_o, const float *grad_hT,
                          float *grad_q, float *grad_k, float *grad_v, float *grad_z, float *grad_beta,
-                         float *grad_A, float *grad_h0, void *workspace, size_t workspace_bytes,
-                         void *stream) {
+                         float *grad_A, float *grad_h0, const kda_prefill_options *options, void *workspace,
+                         size_t workspace_bytes, void *stream) {
     if (io_dtype != KDA_BF16 && io_dtype != KDA_F32) return KDA_ERR_UNSUPPORTED_DTYPE;
     if (N < 0 || T < 0 || H <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (checkpoints_requested(options) || (options && options->checkpoint_interval != 0))
+        return KDA_ERR_INVALID_ARGUMENT;
+    const int P = segments_of(options, N, T, H, dk);
+    if (P < 1) return KDA_ERR_INVALID_ARGUMENT;
     if (!supported_dim(dk, dv)) return KDA_ERR_UNSUPPORTED_DIM;
     if (!A || !cu_seqlens || !workspace || !grad_A) return KDA_ERR_NULL_POINTER;
     if (T > 0 && (!q || !k || !v || !z || !beta || !grad_o || !grad_q || !grad_k || !grad_v || !grad_z ||
@@ -203,8 +242,7 @@ int kda_prefill_backward(kda_dtype io_dtype, const void *q, const void *k, const
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_MISALIGNED;
 
     kda::BackwardPlan plan;
-    if (!kda::plan_backward(N, T, H, dk, io_dtype == KDA_F32, kda::choose_segments(N, T, H, dk), &plan))
-        return KDA_ERR_INVALID_ARGUMENT;
+    if (!kda::plan_backward(N, T, H, dk, io_dtype == KDA_F32, P, &plan)) return KDA_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < plan.total) return KDA_ERR_WORKSPACE_TOO_SMALL;
 
     // every output overlaps no input, no workspace and no other output

@@ -20,7 +20,7 @@
 //      o_t = S_t^T q_t; the copy is discarded (or, with commit_window, it is
 //      the state written back in step 4's place).
 // The per-token update is the prediction-error form of the recurrence
-// ("Hybrid KDA–MLA：Kimi K3 注意力机制解析", core update; P5 §3.1):
+// ("Hybrid KDA–MLA：Kimi K3 注意力机制解析", core update; "Kimi K3：架构、训练与推理系统研究" §3.1):
 //   Sbar = alpha * S (per key channel),  e = v - Sbar^T k,
 //   S = Sbar + beta k e^T,  o = S^T q = Sbar^T q + beta e (k . q).
 #include "kda_chunk.h"

@@ -129,10 +129,9 @@ struct BackwardArgs {
 
 bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, int P, PrefillPlan *plan);
 bool plan_backward(int N, int T, int H, int d, bool f32io, int P, BackwardPlan *plan);
-// Segment count the prefill uses for these sizes, and the process-wide
-// setting that overrides it (0: automatic).
+// Segment count the prefill uses for these sizes when the caller asks for
+// the automatic choice.
 int choose_segments(int N, int T, int H, int d);
-void set_prefill_segments(int p);
 size_t slab_bytes(int dk, int dv, bool f32io);
 
 int launch_decode(const DecodeArgs &a);

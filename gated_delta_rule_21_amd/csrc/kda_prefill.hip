@@ -18,8 +18,9 @@
 //                       affine state maps into every segment's incoming state.
 //
 // Split sequences (intra-device context parallelism, "Kimi K3：架构…" §11.1
-// and the KCP merge of P3 Eq 17): inter_kernel first runs in its transition
-// mode over every segment but a sequence's last, producing the map
+// and the KCP merge of the devpress K3 walk-through §8.1, Eq 17): inter_kernel
+// first runs in its transition mode over every segment but a sequence's last,
+// producing the map
 // S_in -> M S_in + S~ of its chunks; combine_kernel chains the maps from h0;
 // inter_kernel then runs every segment's outputs in parallel.
 //
@@ -43,7 +44,6 @@
 #include "kda_internal.h"
 
 #include <algorithm>
-#include <atomic>
 #include <type_traits>
 
 namespace kda {
@@ -705,7 +705,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 // Segment combine.  The per-chunk update S <- (Diag(gamma_C) - K~^T W) S + K~^T U
 // is affine in S, so a segment maps its incoming state S_in to M S_in + S~
 // (the cross-device merge of "Kimi K3：架构…" §9.3 and the KCP recurrence of
-// P3 Eq 17, applied here to segments on one device).  For a sequence in
+// the devpress K3 walk-through §8.1, Eq 17, applied here to segments on one device).  For a sequence in
 // Pn > 1 segments: S_in(0) = h0 (or zero), S_in(k + 1) = M_k S_in(k) + S~_k,
 // each written to the segment's slot of s_in.
 //
@@ -786,17 +786,12 @@ __global__ void __launch_bounds__(D * 4) combine_kernel(const float *__restrict_
     }
 }
 
-// Segments per sequence.  A set count (kda_set_prefill_segments) wins;
-// otherwise a sequence is split only when the (sequence, head, column group)
+// Segments per sequence when the caller leaves the choice to the library:
+// a sequence is split only when the (sequence, head, column group)
 // workgroups of one pass fill less than half the device, into as many
-// segments as fill it once, each of at least 4 chunks.
-static std::atomic<int> g_segments{0};
-
-void set_prefill_segments(int p) { g_segments.store(p); }
-
+// segments as fill it once, each of at least 4 chunks.  A function of the
+// sizes and the current device's compute-unit count only.
 int choose_segments(int N, int T, int H, int d) {
-    const int forced = g_segments.load();
-    if (forced > 0) return forced;
     if (N <= 0 || T <= 0 || H <= 0) return 1;
     const long long blocks = (long long)N * H * (d == 128 ? 2 : 1);
     const int cus = device_cus();

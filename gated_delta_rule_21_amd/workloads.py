@@ -14,7 +14,8 @@ Distributions (identical for every workload unless noted):
   q, k ~ N(0, 1) per element, then L2-normalised over the key dim per
          (token, head) in fp32, then rounded to the I/O dtype (RNE).  The
          pages make unit-norm q and k a property of the caller's feature path
-         (ShortConv -> Swish -> L2Norm, P5 §3.2), not of the recurrence.
+         (ShortConv -> Swish -> L2Norm, "Kimi K3：架构、训练与推理系统研究" §3.2), not of
+         the recurrence.
   v    ~ N(0, 1), rounded to the I/O dtype.
   beta = sigmoid(N(0, 1)) in fp32, used by the library as given.
   z    ~ N(0, 1) in fp32, per token, head and key channel.

@@ -9,7 +9,8 @@
  *    "Kimi K3：架构、训练与推理系统研究" §3.1-3.2; "Hybrid KDA–MLA：Kimi K3
  *    注意力机制解析" (core update and decay design).  No query scale is
  *    applied; q and k are expected to be L2-normalised by the caller (the
- *    feature path of P5 §3.2 ends in an L2Norm), which is not checked.
+ *    feature path of "Kimi K3：架构、训练与推理系统研究" §3.2 ends in an
+ *    L2Norm), which is not checked.
  *
  * Two entry points, matching the two execution paths the pages describe
  * ("Kimi K3：架构…" §14: chunked kernel for prompts, fused recurrent kernel
@@ -26,7 +27,7 @@
  *   z            fp32 decay logits (raw, before the gate)
  *   states       [N][H][dv][dk] fp32: element (n, h, j, i) is S_{i,j}
  *                (row j = value channel, contiguous over key channels; the
- *                [B,H,V,K] state shape of P5 §13.1)
+ *                [B,H,V,K] state shape of "Kimi K3：架构…" §13.1)
  *   cu_seqlens   [N+1] int32, cu[0] = 0, non-decreasing, cu[N] = T
  * The io dtype applies to q, k, v and o; z, A, beta and all states are fp32.
  *
@@ -68,66 +69,73 @@ typedef enum kda_status {
 } kda_status;
 
 /*
- * Workspace bytes kda_prefill needs for these sizes.  Depends only on the
- * arguments (an upper bound over every cu_seqlens with N sequences and T
- * tokens), the segment setting below and the device's compute-unit count.
+ * Per-call options of kda_prefill_ex and kda_prefill_backward.  A NULL
+ * options pointer, or a zero-initialised struct, means the defaults.
+ *
+ * segments: intra-device context parallelism ("Kimi K3：架构、训练与推理系统
+ *   研究" §11.1, and the devpress K3 technical-report walk-through §8.1: a
+ *   planner splits one sequence over a device's compute units; the pieces'
+ *   state transitions are computed without the incoming state and merged
+ *   exactly).  The prefill may cut each sequence into up to P segments of
+ *   consecutive 64-token chunks.  For every segment but a sequence's last it
+ *   computes the affine map S_in -> M S_in + S~ of its chunks (M in
+ *   R^{dk x dk}, S~ in R^{dk x dv}), composes the maps in order from h0 (the
+ *   merge S = S~ + M S_in of the KCP scheme, devpress walk-through §8.1,
+ *   Eq 17), and then runs every segment's outputs from its own incoming state
+ *   in parallel.  The result equals the unsplit recurrence up to rounding.
+ *     0  automatic (default): split only when the workgroups of one pass
+ *        would fill less than half of the device (few sequences times heads,
+ *        long sequences); kda_prefill_segments reports the choice
+ *     1  never split
+ *     2..KDA_MAX_PREFILL_SEGMENTS  split every sequence of at least that many
+ *        chunks into that many segments (shorter ones into one per chunk)
+ *
+ * checkpoint_interval, checkpoints, checkpoint_offsets: state checkpoints
+ *   for prefix reuse ("Kimi K3：架构…" §12.2: KDA checkpoints are large, so
+ *   they are kept at a coarser grain than the token hash blocks, e.g. at
+ *   512-token endpoints; the s1mplewind "kimi-k3" notes, "KDA存checkpoint").
+ *   Prefill only; all three must be zero / NULL for the backward.
+ *     checkpoint_interval  tokens between checkpoints, a positive multiple of
+ *                          64 (ignored when both pointers are NULL)
+ *     checkpoints          [T / interval][H][dv][dk] fp32 device buffer or
+ *                          NULL (T / interval rounded down: an upper bound on
+ *                          the count for any cu_seqlens); checkpoint j of
+ *                          sequence n is the state after the first
+ *                          (j + 1) * interval tokens of the sequence (h0
+ *                          included), for j < floor(len_n / interval), stored
+ *                          at index checkpoint_offsets[n] + j; sequence-major
+ *     checkpoint_offsets   [N + 1] int32 device buffer or NULL: first
+ *                          checkpoint index of every sequence, then the total
+ *   Entries past the total are left untouched; checkpoints and offsets may
+ *   overlap no other argument.
+ */
+#define KDA_MAX_PREFILL_SEGMENTS 16
+typedef struct kda_prefill_options {
+    int segments;
+    int checkpoint_interval;
+    float *checkpoints;
+    int32_t *checkpoint_offsets;
+} kda_prefill_options;
+
+/*
+ * Workspace bytes kda_prefill needs for these sizes (automatic segments).
+ * Depends only on the arguments (an upper bound over every cu_seqlens with
+ * N sequences and T tokens) and the current device's compute-unit count.
  * Returns 0 for sizes kda_prefill would reject.
  */
 size_t kda_prefill_workspace_size(int N, int T, int H, int dk, int dv, kda_dtype io_dtype);
 
 /*
- * kda_prefill that also saves state checkpoints for prefix reuse ("Kimi
- * K3：架构…" §12.2: KDA checkpoints are large, so they are kept at a coarser
- * grain than the token hash blocks, e.g. at 512-token endpoints; the s1mplewind
- * notes, "KDA存checkpoint").
- *
- *   interval            tokens between checkpoints, a positive multiple of 64
- *   checkpoints         [T / interval][H][dv][dk] fp32 device buffer (T / interval
- *                       rounded down: an upper bound on the count for any
- *                       cu_seqlens); checkpoint j of sequence n is the state
- *                       after the first (j + 1) * interval tokens of the
- *                       sequence (h0 included), for j < floor(len_n / interval),
- *                       stored at index checkpoint_offsets[n] + j; sequence-major
- *   checkpoint_offsets  [N + 1] int32 device buffer or NULL: first checkpoint
- *                       index of every sequence, then the total
- * Entries past the total are left untouched.  Everything else, including the
- * workspace size and the error behaviour, is kda_prefill's; checkpoints and
- * offsets may overlap no other argument.  With checkpoints = NULL and
- * checkpoint_offsets = NULL this is kda_prefill (interval is then ignored).
+ * The same for kda_prefill_ex with these options (NULL: the defaults).
+ * Returns 0 for sizes or options kda_prefill_ex would reject.
  */
-int kda_prefill_checkpoints(kda_dtype io_dtype, const void *q, const void *k, const void *v,
-                            const float *z, const float *A, const float *beta, const float *h0,
-                            const int32_t *cu_seqlens, int N, int T, int H, int dk, int dv, void *o,
-                            float *hT, int interval, float *checkpoints, int32_t *checkpoint_offsets,
-                            void *workspace, size_t workspace_bytes, void *stream);
+size_t kda_prefill_ex_workspace_size(int N, int T, int H, int dk, int dv, kda_dtype io_dtype,
+                                     const kda_prefill_options *options);
 
 /*
- * Intra-device context parallelism ("Kimi K3：架构…" §8.1 and §11.1: a
- * planner splits one sequence over a device's compute units; the pieces'
- * state transitions are computed without the incoming state and merged
- * exactly).  kda_prefill may cut each sequence into up to P segments of
- * consecutive 64-token chunks.  For every segment but a sequence's last it
- * computes the affine map S_in -> M S_in + S~ of its chunks (M in
- * R^{dk x dk}, S~ in R^{dk x dv}), composes the maps in order from h0
- * (the merge S = S~ + M S_in of the KCP scheme, P3 Eq 17), and then runs
- * every segment's outputs from its own incoming state in parallel.  The
- * result equals the unsplit recurrence up to rounding.
- *
- * The default (0) splits only when the workgroups of one pass would fill
- * less than half of the device: few sequences times heads, long sequences.
- *
- * kda_set_prefill_segments sets a process-wide segment count: 0 = automatic,
- * 1 = never split, 2..KDA_MAX_PREFILL_SEGMENTS = split every sequence of at
- * least that many chunks into that many segments (shorter ones into one
- * segment per chunk).  Returns KDA_OK or KDA_ERR_INVALID_ARGUMENT.  It
- * changes kda_prefill_workspace_size: set it before sizing a workspace, and
- * not while another thread sizes or launches a prefill.
- *
- * kda_prefill_segments returns the segment count kda_prefill would use for
- * these sizes now (>= 1), or 0 for sizes kda_prefill would reject.
+ * The segment count a prefill with options.segments = 0 uses for these
+ * sizes on the current device (>= 1), or 0 for sizes it would reject.
  */
-#define KDA_MAX_PREFILL_SEGMENTS 16
-int kda_set_prefill_segments(int segments);
 int kda_prefill_segments(int N, int T, int H, int dk, int dv, kda_dtype io_dtype);
 
 /*
@@ -155,6 +163,18 @@ int kda_prefill(kda_dtype io_dtype, const void *q, const void *k, const void *v,
                 const float *z, const float *A, const float *beta, const float *h0,
                 const int32_t *cu_seqlens, int N, int T, int H, int dk, int dv, void *o,
                 float *hT, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_prefill with per-call options (segments, checkpoints; see
+ * kda_prefill_options).  The workspace must hold
+ * kda_prefill_ex_workspace_size(..., options) bytes.  Invalid options return
+ * KDA_ERR_INVALID_ARGUMENT.  With options NULL this is kda_prefill.
+ */
+int kda_prefill_ex(kda_dtype io_dtype, const void *q, const void *k, const void *v,
+                   const float *z, const float *A, const float *beta, const float *h0,
+                   const int32_t *cu_seqlens, int N, int T, int H, int dk, int dv, void *o,
+                   float *hT, const kda_prefill_options *options, void *workspace,
+                   size_t workspace_bytes, void *stream);
 
 /*
  * One decode step for N sequences, one token each.
@@ -263,6 +283,8 @@ int kda_output_gate(kda_dtype io_dtype, const void *o, const void *g, const floa
  * gradient per (chunk, head).  Arithmetic after the forward recompute is fp32.
  *
  *   q .. cu_seqlens, N .. dv   as for kda_prefill (the same inputs)
+ *   options     NULL or options with only `segments` set (the forward
+ *               recompute's segment split); sized by the same pointer
  *   grad_o      [T][H][dv] io dtype
  *   grad_hT     [N][H][dv][dk] fp32, or NULL for zeros
  *   grad_q, grad_k, grad_z   [T][H][dk] fp32;  grad_v [T][H][dv] fp32
@@ -274,13 +296,15 @@ int kda_output_gate(kda_dtype io_dtype, const void *o, const void *g, const floa
  * Outputs may overlap no input, no other output and the workspace
  * (KDA_ERR_ALIAS).  Errors and asynchrony as for kda_prefill.
  */
-size_t kda_prefill_backward_workspace_size(int N, int T, int H, int dk, int dv, kda_dtype io_dtype);
+size_t kda_prefill_backward_workspace_size(int N, int T, int H, int dk, int dv, kda_dtype io_dtype,
+                                           const kda_prefill_options *options);
 int kda_prefill_backward(kda_dtype io_dtype, const void *q, const void *k, const void *v,
                          const float *z, const float *A, const float *beta, const float *h0,
                          const int32_t *cu_seqlens, int N, int T, int H, int dk, int dv,
                          const void *grad_o, const float *grad_hT, float *grad_q, float *grad_k,
                          float *grad_v, float *grad_z, float *grad_beta, float *grad_A,
-                         float *grad_h0, void *workspace, size_t workspace_bytes, void *stream);
+                         float *grad_h0, const kda_prefill_options *options, void *workspace,
+                         size_t workspace_bytes, void *stream);
 
 /* Static, human-readable text for a kda_status value. */
 const char *kda_status_string(int status);

@@ -180,7 +180,8 @@ def backward(q, k, v, z, A, beta, h0, cu_seqlens, dO, dhT=None, nthreads: int = 
 
 
 def gate(A, z):
-    """g = g_min * sigmoid(exp(A_h) * z) in fp64 (P5 §3.2; devpress §3.2 Eq 5).
+    """g = g_min * sigmoid(exp(A_h) * z) in fp64 ("Kimi K3：架构、训练与推理系统研究"
+    §3.2; the devpress K3 walk-through §3.2, Eq 5).
 
     A broadcasts over the head axis: z [..., H, dk], A [H]."""
     A = np.asarray(A, dtype=np.float64)

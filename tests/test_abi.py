@@ -20,10 +20,11 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["kda_build_info", "kda_decode", "kda_decode_window", "kda_prefill",
-                                           "kda_prefill_checkpoints", "kda_qkv_shortconv", "kda_output_gate",
+                                           "kda_prefill_ex", "kda_prefill_ex_workspace_size",
+                                           "kda_qkv_shortconv", "kda_output_gate",
                                            "kda_prefill_segments", "kda_prefill_workspace_size",
                                            "kda_prefill_backward", "kda_prefill_backward_workspace_size",
-                                           "kda_set_prefill_segments", "kda_status_string"])
+                                           "kda_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -99,30 +100,52 @@ def test_decode_rejects_bad_arguments():
     assert d(o=FAKE + 4096) == -8                 # o on top of k
 
 
-def test_segment_setting():
-    """The segment count: range checks, the forced value, and the workspace
-    growing by the transitions (2 d^2) and incoming states (d^2) in fp32 per
-    (segment, head)."""
-    try:
-        assert kda.kda_set_prefill_segments(-1) == -1
-        assert kda.kda_set_prefill_segments(17) == -1
-        assert kda.kda_set_prefill_segments(1) == 0
-        assert kda.kda_prefill_segments(2, 16384, 8, 128, 128, kda.KDA_BF16) == 1
-        base = kda.kda_prefill_workspace_size(2, 16384, 8, 128, 128, kda.KDA_BF16)
-        for P in (2, 7, 16):
-            assert kda.kda_set_prefill_segments(P) == 0
-            assert kda.kda_prefill_segments(2, 16384, 8, 128, 128, kda.KDA_BF16) == P
-            n = kda.kda_prefill_workspace_size(2, 16384, 8, 128, 128, kda.KDA_BF16)
-            extra = 2 * P * 8 * 3 * 128 * 128 * 4
-            assert n - base == extra + (256 if 2 * P * 16 > 256 else 0), (P, n - base)
-        assert kda.kda_prefill_segments(2, 16384, 8, 96, 96, kda.KDA_BF16) == 0
-    finally:
-        kda.kda_set_prefill_segments(0)
+def test_segment_option():
+    """The per-call segment count: range checks, and the workspace growing by
+    the transitions (2 d^2) and incoming states (d^2) in fp32 per (segment,
+    head).  The size is a function of the arguments alone: asking with other
+    options in between changes nothing."""
+    ws = lambda P, **kw: kda.kda_prefill_ex_workspace_size(2, 16384, 8, 128, 128, kda.KDA_BF16,
+                                                          kda.options(P, **kw))
+    assert ws(-1) == 0 and ws(17) == 0
+    base = ws(1)
+    assert base > 0
+    for P in (2, 7, 16):
+        extra = 2 * P * 8 * 3 * 128 * 128 * 4
+        assert ws(P) - base == extra + (256 if 2 * P * 16 > 256 else 0), (P, ws(P) - base)
+    assert ws(1) == base
+    # options NULL and zero-initialised options are the automatic choice
+    auto = kda.kda_prefill_segments(2, 16384, 8, 128, 128, kda.KDA_BF16)
+    assert auto > 1
+    assert kda.kda_prefill_ex_workspace_size(2, 16384, 8, 128, 128, kda.KDA_BF16, None) == ws(auto)
+    assert kda.kda_prefill_workspace_size(2, 16384, 8, 128, 128, kda.KDA_BF16) == ws(0) == ws(auto)
+    assert kda.kda_prefill_segments(2, 16384, 8, 96, 96, kda.KDA_BF16) == 0
+    # checkpoint options: the interval must be a positive multiple of 64 when a buffer is given
+    assert ws(0, interval=100, checkpoints=FAKE) == 0
+    assert ws(0, interval=0, checkpoint_offsets=FAKE) == 0
+    assert ws(0, interval=512, checkpoints=FAKE) == ws(0)
+    # the backward takes the segment option only
+    bw = lambda o: kda.kda_prefill_backward_workspace_size(2, 16384, 8, 128, 128, kda.KDA_BF16, o)
+    assert bw(kda.options(3)) > bw(kda.options(1)) > 0
+    assert bw(kda.options(0, 512, FAKE)) == 0 and bw(kda.options(0, 64)) == 0 and bw(kda.options(99)) == 0
     # automatic choice: one segment when one pass fills half the device or
     # the sequences are short
     assert kda.kda_prefill_segments(1, 65536, 96, 128, 128, kda.KDA_BF16) == 1
     assert kda.kda_prefill_segments(1, 256, 2, 32, 32, kda.KDA_F32) == 1
     assert kda.kda_prefill_segments(0, 0, 2, 32, 32, kda.KDA_F32) == 1
+
+
+def test_prefill_ex_rejects_bad_options():
+    e = lambda opts, ws_bytes=1 << 40: kda.kda_prefill_ex(0, FAKE, FAKE + 4096, FAKE + 8192, FAKE + 16384,
+                                                          FAKE + 32768, FAKE + 40960, None, FAKE + 49152, 1, 16,
+                                                          2, 32, 32, FAKE + 65536, None, opts, 1 << 24,
+                                                          ws_bytes, None)
+    assert e(kda.options(-1)) == -1
+    assert e(kda.options(17)) == -1
+    assert e(kda.options(0, 100, 1 << 26)) == -1
+    assert e(kda.options(0, 0, None, 1 << 26)) == -1
+    assert e(None, ws_bytes=0) == -6
+    assert e(kda.options(4), ws_bytes=kda.kda_prefill_ex_workspace_size(1, 16, 2, 32, 32, 0, kda.options(4)) - 1) == -6
 
 
 def test_decode_window_rejects_bad_arguments():
@@ -148,10 +171,10 @@ def test_prefill_checkpoints_rejects_bad_arguments():
     def c(**o):
         a = dict(interval=512, ck=1 << 26, off=(1 << 26) - 4096, T=4096, ws_bytes=1 << 40)
         a.update(o)
-        return kda.kda_prefill_checkpoints(0, FAKE, FAKE + 4096 * 64, FAKE + 2 * 4096 * 64, FAKE + 3 * 4096 * 64,
-                                           FAKE + 4 * 4096 * 64, FAKE + 6 * 4096 * 64, None, FAKE + 7 * 4096 * 64,
-                                           1, a["T"], 2, 32, 32, 1 << 25, None, a["interval"], a["ck"], a["off"],
-                                           1 << 30, a["ws_bytes"], None)
+        return kda.kda_prefill_ex(0, FAKE, FAKE + 4096 * 64, FAKE + 2 * 4096 * 64, FAKE + 3 * 4096 * 64,
+                                  FAKE + 4 * 4096 * 64, FAKE + 6 * 4096 * 64, None, FAKE + 7 * 4096 * 64,
+                                  1, a["T"], 2, 32, 32, 1 << 25, None,
+                                  kda.options(0, a["interval"], a["ck"], a["off"]), 1 << 30, a["ws_bytes"], None)
     assert c(interval=0) == -1
     assert c(interval=100) == -1
     assert c(interval=-64) == -1
@@ -216,7 +239,8 @@ def test_prefill_backward_rejects_bad_arguments():
         a.update(o)
         return kda.kda_prefill_backward(a["io"], a["q"], a["k"], a["v"], a["z"], a["A"], a["beta"], None, a["cu"],
                                         a["N"], T, H, a["d"], a["d"], a["dO"], a["dhT"], a["gq"], a["gk"], a["gv"],
-                                        a["gz"], a["gb"], a["gA"], a["gh0"], a["ws"], a["ws_bytes"], None)
+                                        a["gz"], a["gb"], a["gA"], a["gh0"], a.get("opts"), a["ws"],
+                                        a["ws_bytes"], None)
     assert b(io=3) == -4
     assert b(N=-1) == -1
     assert b(d=48) == -3
@@ -226,3 +250,127 @@ def test_prefill_backward_rejects_bad_arguments():
     assert b(gq=1 << 24) == -8                    # grad_q on top of q
     assert b(gk=(1 << 26) + 64) == -8             # grad_k over grad_q
     assert b(gh0=(1 << 30) + 256) == -8           # grad_h0 inside the workspace
+    assert b(opts=kda.options(17)) == -1          # segment count out of range
+    assert b(opts=kda.options(0, 512, 1 << 28)) == -1   # checkpoints are a prefill option only
+
+
+# ---------------------------------------------------------------------------
+# The torch wrappers check every tensor's dtype and shape before passing its
+# pointer (the C ABI cannot see either).  CPU tensors get through those checks
+# and are then refused as not being on a GPU; these tests run on the CPU.
+# ---------------------------------------------------------------------------
+import torch  # noqa: E402
+
+
+def _prefill_tensors(T=70, H=2, d=32, N=2, io=torch.bfloat16):
+    return dict(q=torch.zeros(T, H, d, dtype=io), k=torch.zeros(T, H, d, dtype=io),
+                v=torch.zeros(T, H, d, dtype=io), z=torch.zeros(T, H, d), A=torch.zeros(H),
+                beta=torch.zeros(T, H), cu_seqlens=torch.tensor([0, 30, T], dtype=torch.int32)[: N + 1],
+                h0=torch.zeros(N, H, d, d))
+
+
+PREFILL_BAD = [
+    ("k", lambda t: t["k"].float(), TypeError),
+    ("v", lambda t: t["v"].to(torch.float16), TypeError),
+    ("z", lambda t: t["z"].bfloat16(), TypeError),
+    ("z", lambda t: t["z"][:-1].clone(), ValueError),                    # a short z
+    ("A", lambda t: t["A"].double(), TypeError),
+    ("A", lambda t: torch.zeros(3), ValueError),
+    ("beta", lambda t: t["beta"].bfloat16(), TypeError),
+    ("beta", lambda t: torch.zeros(70, 3), ValueError),
+    ("cu_seqlens", lambda t: t["cu_seqlens"].long(), TypeError),        # int64 offsets
+    ("h0", lambda t: t["h0"].bfloat16(), TypeError),
+    ("h0", lambda t: torch.zeros(1, 2, 32, 32), ValueError),
+    ("k", lambda t: t["k"].transpose(0, 1).contiguous().transpose(0, 1), ValueError),   # not contiguous
+]
+
+
+@pytest.mark.parametrize("name,bad,err", PREFILL_BAD)
+def test_prefill_wrapper_rejects(name, bad, err):
+    t = _prefill_tensors()
+    t[name] = bad(t)
+    with pytest.raises(err, match=name):
+        kda.prefill(**t)
+    with pytest.raises(err, match=name):
+        kda.prefill_checkpoints(**t, interval=64)
+    with pytest.raises(err, match=name):
+        kda.prefill_backward(**t, grad_o=torch.zeros(70, 2, 32, dtype=torch.bfloat16))
+
+
+def test_prefill_wrapper_rejects_outputs_and_then_the_device():
+    t = _prefill_tensors()
+    with pytest.raises(TypeError, match="o"):
+        kda.prefill(**t, o=torch.zeros(70, 2, 32))                         # fp32 o with bf16 q
+    with pytest.raises(ValueError, match="hT"):
+        kda.prefill(**t, hT=torch.zeros(2, 2, 32, 16))
+    with pytest.raises(TypeError, match="workspace"):
+        kda.prefill(**t, workspace=torch.zeros(16, dtype=torch.int32))
+    with pytest.raises(ValueError, match="checkpoints"):
+        kda.prefill_checkpoints(**t, interval=64, checkpoints=torch.zeros(2, 2, 32, 32))
+    with pytest.raises(TypeError, match="offsets"):
+        kda.prefill_checkpoints(**t, interval=64, offsets=torch.zeros(3, dtype=torch.int64))
+    with pytest.raises(ValueError, match="interval"):
+        kda.prefill_checkpoints(**t, interval=100)
+    with pytest.raises(TypeError, match="grad_o"):
+        kda.prefill_backward(**t, grad_o=torch.zeros(70, 2, 32))
+    with pytest.raises(ValueError, match="dq"):
+        kda.prefill_backward(**t, grad_o=torch.zeros(70, 2, 32, dtype=torch.bfloat16),
+                             grads=dict(dq=torch.zeros(70, 2, 31)))
+    # every check passed: a CPU tensor is refused, nothing is launched
+    with pytest.raises(ValueError, match="GPU"):
+        kda.prefill(**t)
+
+
+def test_decode_wrappers_reject():
+    N, H, d = 3, 2, 32
+    base = dict(q=torch.zeros(N, H, d, dtype=torch.bfloat16), k=torch.zeros(N, H, d, dtype=torch.bfloat16),
+                v=torch.zeros(N, H, d, dtype=torch.bfloat16), z=torch.zeros(N, H, d), A=torch.zeros(H),
+                beta=torch.zeros(N, H), S=torch.zeros(N, H, d, d))
+    for name, val, err in (("z", torch.zeros(N, H, d, dtype=torch.bfloat16), TypeError),
+                           ("S", torch.zeros(N, H, d, 16), ValueError),
+                           ("S", torch.zeros(N, H, d, d, dtype=torch.float64), TypeError),
+                           ("beta", torch.zeros(N, H + 1), ValueError),
+                           ("k", torch.zeros(N, H, d), TypeError)):
+        with pytest.raises(err, match=name):
+            kda.decode(**dict(base, **{name: val}))
+    with pytest.raises(ValueError, match="GPU"):
+        kda.decode(**base)
+    # the decode window
+    win = dict(q=torch.zeros(N, 2, H, d, dtype=torch.bfloat16), k=torch.zeros(N, 2, H, d, dtype=torch.bfloat16),
+               v=torch.zeros(N, 2, H, d, dtype=torch.bfloat16), z=torch.zeros(N, 2, H, d), beta=torch.zeros(N, 2, H))
+    rep = dict(k=torch.zeros(N, 3, H, d, dtype=torch.bfloat16), v=torch.zeros(N, 3, H, d, dtype=torch.bfloat16),
+               z=torch.zeros(N, 3, H, d), beta=torch.zeros(N, 3, H))
+    acc = torch.zeros(N, dtype=torch.int32)
+    with pytest.raises(ValueError, match="window z"):
+        kda.decode_window(base["A"], base["S"], window=dict(win, z=torch.zeros(N, 3, H, d)))
+    with pytest.raises(TypeError, match="replay v"):
+        kda.decode_window(base["A"], base["S"], replay=dict(rep, v=rep["v"].float()), n_accept=acc)
+    with pytest.raises(TypeError, match="n_accept"):
+        kda.decode_window(base["A"], base["S"], replay=rep, n_accept=acc.long())
+    with pytest.raises(ValueError, match="n_accept"):
+        kda.decode_window(base["A"], base["S"], replay=rep)
+    with pytest.raises(TypeError, match="bfloat16 or float32"):
+        kda.decode_window(base["A"], base["S"], window={n: (t.half() if n == "q" else t) for n, t in win.items()})
+    with pytest.raises(ValueError, match="GPU"):
+        kda.decode_window(base["A"], base["S"], window=win, replay=rep, n_accept=acc)
+
+
+def test_feature_wrappers_reject():
+    T, H, d = 20, 2, 32
+    x = lambda: torch.zeros(T, H, d, dtype=torch.bfloat16)
+    w = lambda: torch.zeros(H, d, 4)
+    cu = torch.tensor([0, T], dtype=torch.int32)
+    with pytest.raises(TypeError, match="wk"):
+        kda.qkv_shortconv(x(), x(), x(), w(), w().bfloat16(), w(), cu)
+    with pytest.raises(ValueError, match="conv_state_in"):
+        kda.qkv_shortconv(x(), x(), x(), w(), w(), w(), cu, conv_state_in=torch.zeros(1, 3, H, d, dtype=torch.bfloat16))
+    with pytest.raises(TypeError, match="cu_seqlens"):
+        kda.qkv_shortconv(x(), x(), x(), w(), w(), w(), cu.long())
+    with pytest.raises(ValueError, match="GPU"):
+        kda.qkv_shortconv(x(), x(), x(), w(), w(), w(), cu)
+    with pytest.raises(TypeError, match="g"):
+        kda.output_gate(x(), x().float(), torch.ones(d), 1e-6)
+    with pytest.raises(ValueError, match="w"):
+        kda.output_gate(x(), x(), torch.ones(d + 1), 1e-6)
+    with pytest.raises(ValueError, match="GPU"):
+        kda.output_gate(x(), x(), torch.ones(d), 1e-6)

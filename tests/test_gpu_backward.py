@@ -32,10 +32,9 @@ def oracle_grads(inp, cot, heads=None):
 
 
 def gpu_grads(g, gc, segments=0):
-    with kda.prefill_segments(segments):
-        out = kda.prefill_backward(g["q"], g["k"], g["v"], g["z"], g["A"], g["beta"], g["cu_seqlens"], gc["dO"],
-                                   h0=g["h0"], grad_hT=gc["dhT"])
-        torch.cuda.synchronize()
+    out = kda.prefill_backward(g["q"], g["k"], g["v"], g["z"], g["A"], g["beta"], g["cu_seqlens"], gc["dO"],
+                               h0=g["h0"], grad_hT=gc["dhT"], segments=segments)
+    torch.cuda.synchronize()
     return out
 
 

@@ -8,7 +8,7 @@ import torch
 import gated_delta_rule_21_amd as kda
 import oracle
 from gated_delta_rule_21_amd import workloads as W
-from gpu_util import BF16_TOL, host, oracle_prefill, rel_l2, to_gpu, tol
+from gpu_util import compare_prefill, compare_states, host, oracle_prefill, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -39,12 +39,12 @@ def oracle_checkpoints(d, interval, heads=None, only=None):
 
 
 def run(g, interval, segments=0):
-    with kda.prefill_segments(segments):
-        T, H, d = g["q"].shape
-        ck = torch.full((T // interval, H, d, d), 7.0, dtype=torch.float32, device="cuda")   # sentinel
-        o, hT, ck, off = kda.prefill_checkpoints(g["q"], g["k"], g["v"], g["z"], g["A"], g["beta"],
-                                                 g["cu_seqlens"], interval, h0=g["h0"], checkpoints=ck)
-        torch.cuda.synchronize()
+    T, H, d = g["q"].shape
+    ck = torch.full((T // interval, H, d, d), 7.0, dtype=torch.float32, device="cuda")   # sentinel
+    o, hT, ck, off = kda.prefill_checkpoints(g["q"], g["k"], g["v"], g["z"], g["A"], g["beta"],
+                                             g["cu_seqlens"], interval, h0=g["h0"], checkpoints=ck,
+                                             segments=segments)
+    torch.cuda.synchronize()
     return o, hT, ck, off
 
 
@@ -60,15 +60,16 @@ def test_checkpoints_ragged(io, d, interval, segments):
     exp, count = oracle_checkpoints(inp, interval)
     offsets = np.cumsum([0] + [n // interval for n in lens])
     assert off.cpu().tolist() == offsets.tolist()
-    e = rel_l2(host(ck[:count]), exp)
-    print("checkpoints %s d=%d interval=%d segments=%d: %d, rel-L2 %.3e" % (io, d, interval, segments, count, e),
+    m = compare_states(host(ck[:count]), exp, io, what="checkpoints")
+    print("checkpoints %s d=%d interval=%d segments=%d: %d, %s" % (io, d, interval, segments, count, m),
           flush=True)
-    assert e <= tol(io), e
+    ro, rh = oracle_prefill(inp)
+    compare_prefill(o, hT, ro, rh, inp["cu_seqlens"], io, label="checkpoint run outputs")
     assert bool((ck[count:] == 7.0).all()), "entries past the total must stay untouched"
     # outputs and final states: the same as without checkpoints, bit for bit
-    with kda.prefill_segments(segments):
-        o2, h2 = kda.prefill(g["q"], g["k"], g["v"], g["z"], g["A"], g["beta"], g["cu_seqlens"], h0=g["h0"])
-        torch.cuda.synchronize()
+    o2, h2 = kda.prefill(g["q"], g["k"], g["v"], g["z"], g["A"], g["beta"], g["cu_seqlens"], h0=g["h0"],
+                         segments=segments)
+    torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(hT, h2)
 
 
@@ -84,19 +85,19 @@ def test_checkpoints_without_h0_and_offsets_only():
     inp = W.random_prefill([700, 300], 2, 64, "bf16", h0_std=None, seed=711)
     g = to_gpu(inp)
     off = torch.full((3,), -1, dtype=torch.int32, device="cuda")
-    st = kda.kda_prefill_checkpoints(kda.KDA_BF16, g["q"].data_ptr(), g["k"].data_ptr(), g["v"].data_ptr(),
-                                     g["z"].data_ptr(), g["A"].data_ptr(), g["beta"].data_ptr(), None,
-                                     g["cu_seqlens"].data_ptr(), 2, 1000, 2, 64, 64,
-                                     torch.empty((1000, 2, 64), dtype=torch.bfloat16, device="cuda").data_ptr(),
-                                     None, 256, None, off.data_ptr(),
-                                     kda.prefill_workspace(2, 1000, 2, 64, kda.KDA_BF16, "cuda").data_ptr(),
-                                     kda.kda_prefill_workspace_size(2, 1000, 2, 64, 64, kda.KDA_BF16),
-                                     torch.cuda.current_stream().cuda_stream)
+    ws = kda.prefill_workspace(2, 1000, 2, 64, kda.KDA_BF16, "cuda")
+    st = kda.kda_prefill_ex(kda.KDA_BF16, g["q"].data_ptr(), g["k"].data_ptr(), g["v"].data_ptr(),
+                            g["z"].data_ptr(), g["A"].data_ptr(), g["beta"].data_ptr(), None,
+                            g["cu_seqlens"].data_ptr(), 2, 1000, 2, 64, 64,
+                            torch.empty((1000, 2, 64), dtype=torch.bfloat16, device="cuda").data_ptr(),
+                            None, kda.options(0, 256, None, off.data_ptr()), ws.data_ptr(), ws.numel(),
+                            torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert st == 0 and off.cpu().tolist() == [0, 2, 3]
     o, hT, ck, off2 = run(dict(g, h0=None), 256)
     exp, count = oracle_checkpoints(dict(inp, h0=None), 256)
-    assert count == 3 and rel_l2(host(ck[:3]), exp) <= BF16_TOL
+    assert count == 3
+    compare_states(host(ck[:3]), exp, "bf16", what="checkpoints")
 
 
 def test_k3_prefill_checkpoints_sampled():
@@ -108,7 +109,6 @@ def test_k3_prefill_checkpoints_sampled():
     heads = [5, 77]
     exp, count = oracle_checkpoints(d, 4096, heads=heads, only={0, 7, 15})
     got = host(ck[[0, 7, 15]][:, heads])
-    e = rel_l2(got, exp)
-    print("k3 checkpoints rel-L2 %.3e" % e, flush=True)
-    assert e <= BF16_TOL
+    m = compare_states(got, exp, "bf16", what="k3 checkpoints")
+    print("k3 checkpoints %s" % m, flush=True)
     assert torch.equal(ck[15], hT[0])

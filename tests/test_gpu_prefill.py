@@ -8,7 +8,8 @@ import torch
 
 import gated_delta_rule_21_amd as kda
 from gated_delta_rule_21_amd import workloads as W
-from gpu_util import BF16_TOL, F32_TOL, host, oracle_prefill, rel_l2, to_gpu, tol
+from gpu_util import (BF16_TOL, F32_TOL, compare_outputs, compare_prefill, host, oracle_prefill, rel_l2,
+                      to_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -22,16 +23,15 @@ def gpu_prefill(g, h0="same", hT=True):
 
 
 def check(d, io, heads=None, label=""):
+    """GPU prefill against the oracle by every measure of gpu_util: whole
+    tensor, per (sequence, head), compute-only and element-wise."""
+    print("case", label, flush=True)
     g = to_gpu(d)
     o, hT = gpu_prefill(g)
     ro, rh = oracle_prefill(d, heads=heads)
     if heads is not None:
         o, hT = o[:, heads], hT[:, heads]
-    eo, eh = rel_l2(host(o), ro), rel_l2(host(hT), rh)
-    print("%s rel-L2 o=%.3e hT=%.3e" % (label, eo, eh), flush=True)
-    assert eo <= tol(io), eo
-    assert eh <= tol(io), eh
-    return eo, eh
+    return compare_prefill(o, hT, ro, rh, d["cu_seqlens"], io, label=label)
 
 
 def test_tiny_f32_workload():
@@ -55,13 +55,33 @@ def test_stress_decay(z_shift):
     check(inp, "bf16", label="z_shift %g" % z_shift)
 
 
+@pytest.mark.parametrize("io,d", [("bf16", 128), ("bf16", 32), ("f32", 64), ("f32", 128)])
+def test_deltanet_ragged(io, d):
+    """alpha = 1 exactly (z = -1e30: the sigmoid underflows to 0, g = 0) with
+    random beta: KDA reduces to the delta rule; ragged lengths."""
+    inp = W.random_prefill([200, 0, 64, 1, 130, 77], 3, d, io, h0_std=0.05, seed=320 + d)
+    inp["z"][:] = -1e30
+    check(inp, io, label="deltanet %s d=%d" % (io, d))
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_decay_floor_attained(io):
+    """z = +1e30: the sigmoid is exactly 1, so g = -5 on every token and
+    channel and every 16-token window sums to exactly -80, the pages' bound
+    attained (devpress K3 walk-through §3.2, Eq 5): the largest in-block
+    decay factor, e^80, is reached on every diagonal block."""
+    inp = W.random_prefill([300, 129, 64], 4, 128, io, h0_std=0.05, seed=330)
+    inp["z"][:] = 1e30
+    check(inp, io, label="decay floor %s" % io)
+
+
 def test_no_h0_no_hT():
     inp = W.random_prefill([150, 90], 2, 64, "bf16", h0_std=None, seed=8)
     g = to_gpu(inp)
     o, hT = gpu_prefill(g, h0=None, hT=False)
     assert hT is None
     ro, _ = oracle_prefill(inp)
-    assert rel_l2(host(o), ro) <= BF16_TOL
+    compare_outputs(host(o), ro, "bf16", inp["cu_seqlens"].tolist())
 
 
 @pytest.mark.parametrize("io", ["bf16", "f32"])
@@ -109,25 +129,34 @@ def test_alpha_one_beta_zero_constant_state():
     o, hT = gpu_prefill(g)
     assert torch.equal(hT.cpu(), inp["h0"])
     ro, _ = oracle_prefill(inp)
-    assert rel_l2(host(o), ro) <= BF16_TOL
+    compare_outputs(host(o), ro, "bf16", inp["cu_seqlens"].tolist())
 
 
-def test_exact_write():
-    """Unit keys with exact binary entries, beta = 1, q = k: o_t = v_t."""
-    r = np.random.Generator(np.random.PCG64(12))
-    T, H, d = 160, 2, 32
+@pytest.mark.parametrize("io,d", [("f32", 32), ("f32", 128), ("bf16", 128)])
+def test_exact_write(io, d):
+    """Unit keys with exact binary entries (four of +-0.5, exact in bf16 too),
+    beta = 1, q = k: o_t = v_t whatever the decay, since
+    S_t^T k_t = (Diag(a) S)^T (I - k k^T) k + v k^T k = v for |k| = 1.
+    Several sequences and a partial chunk; the oracle agrees as well."""
+    r = np.random.Generator(np.random.PCG64(12 + d))
+    lens = [160, 37, 64]
+    T, H = sum(lens), 2
     k = np.zeros((T, H, d), np.float32)
     for t in range(T):
         for h in range(H):
             idx = r.choice(d, 4, replace=False)
             k[t, h, idx] = r.choice([-0.5, 0.5], 4)
-    inp = W.random_prefill([T], H, d, "f32", h0_std=0.2, seed=12)
-    inp["k"] = torch.from_numpy(k)
+    inp = W.random_prefill(lens, H, d, io, h0_std=0.2, seed=12)
+    inp["k"] = torch.from_numpy(k).to(inp["q"].dtype)
     inp["q"] = inp["k"].clone()
     inp["beta"][:] = 1.0
     g = to_gpu(inp)
     o, _ = gpu_prefill(g)
-    assert rel_l2(host(o), inp["v"].double().numpy()) <= F32_TOL
+    cu = inp["cu_seqlens"].tolist()
+    m = compare_outputs(host(o), inp["v"].double().numpy(), io, cu, what="o vs v")
+    print("exact write %s d=%d %s" % (io, d, m), flush=True)
+    ro, _ = oracle_prefill(inp)
+    compare_outputs(host(o), ro, io, cu)
 
 
 def test_split_and_carry():
@@ -145,8 +174,10 @@ def test_split_and_carry():
     o2, h2 = kda.prefill(p2["q"], p2["k"], p2["v"], p2["z"], p2["A"], p2["beta"],
                          torch.tensor([0, 400 - t1], dtype=torch.int32, device="cuda"), h0=h1)
     torch.cuda.synchronize()
+    # against the oracle (the split point, 150, lies inside a chunk)
+    ro, rh = oracle_prefill(inp)
+    compare_prefill(torch.cat([o1, o2]), h2, ro, rh, [0, 400], "bf16", label="split and carry")
     assert rel_l2(host(torch.cat([o1, o2])), host(o)) <= BF16_TOL
-    assert rel_l2(host(h2), host(hT)) <= BF16_TOL
 
 
 def test_k3_prefill_sampled_heads():

@@ -8,22 +8,19 @@ import torch
 
 import gated_delta_rule_21_amd as kda
 from gated_delta_rule_21_amd import workloads as W
-from gpu_util import BF16_TOL, host, oracle_prefill, rel_l2, to_gpu, tol
+from gpu_util import compare_outputs, compare_prefill, host, oracle_prefill, to_gpu
 
 pytestmark = pytest.mark.gpu
 
 
 def run(g, segments, h0="same", hT=None):
-    with kda.prefill_segments(segments):
-        o, hT_ = kda.prefill(g["q"], g["k"], g["v"], g["z"], g["A"], g["beta"], g["cu_seqlens"],
-                             h0=g["h0"] if h0 == "same" else h0, hT=hT)
-        torch.cuda.synchronize()
+    o, hT_ = kda.prefill(g["q"], g["k"], g["v"], g["z"], g["A"], g["beta"], g["cu_seqlens"],
+                         h0=g["h0"] if h0 == "same" else h0, hT=hT, segments=segments)
+    torch.cuda.synchronize()
     return o, hT_
 
 
 def test_segment_count_query():
-    with kda.prefill_segments(5):
-        assert kda.kda_prefill_segments(2, 1000, 4, 64, 64, kda.KDA_BF16) == 5
     assert kda.kda_prefill_segments(1, 65536, 96, 128, 128, kda.KDA_BF16) == 1
     assert kda.kda_prefill_segments(2, 16384, 8, 128, 128, kda.KDA_BF16) > 1
 
@@ -35,13 +32,11 @@ def test_forced_segments_ragged(io, d, P):
     short ones get one segment per chunk."""
     lens = [1000, 0, 64, 1, 450, 77, 640]
     inp = W.random_prefill(lens, 3, d, io, h0_std=0.05, seed=500 + d + P)
+    print("case segments P=%d %s d=%d" % (P, io, d), flush=True)
     g = to_gpu(inp)
     o, hT = run(g, P)
     ro, rh = oracle_prefill(inp)
-    eo, eh = rel_l2(host(o), ro), rel_l2(host(hT), rh)
-    print("segments P=%d %s d=%d rel-L2 o=%.3e hT=%.3e" % (P, io, d, eo, eh), flush=True)
-    assert eo <= tol(io), eo
-    assert eh <= tol(io), eh
+    compare_prefill(o, hT, ro, rh, inp["cu_seqlens"], io, label="segments P=%d %s d=%d" % (P, io, d))
 
 
 @pytest.mark.parametrize("z_shift", [-4.0, 6.0])
@@ -51,8 +46,7 @@ def test_forced_segments_decay_extremes(z_shift):
     g = to_gpu(inp)
     o, hT = run(g, 6)
     ro, rh = oracle_prefill(inp)
-    assert rel_l2(host(o), ro) <= BF16_TOL
-    assert rel_l2(host(hT), rh) <= BF16_TOL
+    compare_prefill(o, hT, ro, rh, inp["cu_seqlens"], "bf16", label="segments z_shift %g" % z_shift)
 
 
 def test_segments_hT_may_alias_h0():
@@ -69,8 +63,7 @@ def test_segments_without_h0():
     g = to_gpu(inp)
     o, hT = run(g, 3, h0=None)
     ro, rh = oracle_prefill(inp)
-    assert rel_l2(host(o), ro) <= BF16_TOL
-    assert rel_l2(host(hT), rh) <= BF16_TOL
+    compare_prefill(o, hT, ro, rh, inp["cu_seqlens"], "bf16", label="segments without h0")
 
 
 def test_segments_constant_state_exact():
@@ -83,7 +76,7 @@ def test_segments_constant_state_exact():
     o, hT = run(g, 5)
     assert torch.equal(hT.cpu(), inp["h0"])
     ro, _ = oracle_prefill(inp)
-    assert rel_l2(host(o), ro) <= BF16_TOL
+    compare_outputs(host(o), ro, "bf16", inp["cu_seqlens"].tolist())
 
 
 def test_segments_deterministic():
@@ -103,7 +96,4 @@ def test_small_head_workload_split_and_unsplit():
     ro, rh = oracle_prefill(d, nthreads=0)
     for P in (0, 1):
         o, hT = run(g, P)
-        eo, eh = rel_l2(host(o), ro), rel_l2(host(hT), rh)
-        print("small_head segments=%s rel-L2 o=%.3e hT=%.3e" % (P or "auto", eo, eh), flush=True)
-        assert eo <= BF16_TOL, eo
-        assert eh <= BF16_TOL, eh
+        compare_prefill(o, hT, ro, rh, d["cu_seqlens"], "bf16", label="small_head segments=%s" % (P or "auto"))
