@@ -9,6 +9,8 @@ Entry points (same names as the C ABI in include/kda.h):
   kda_prefill(...)                  raw C call, pointers as ints
   kda_prefill_ex(..., options, ...) raw C call: prefill with per-call options
                                     (segment count, state checkpoints)
+  kda_prefill_noalloc(...)          raw C call: prefill without a workspace (the
+                                    library's fixed device scratch; no allocation)
   kda_decode(...)                   raw C call
   kda_decode_window(...)            raw C call: replay + multi-token window
   kda_qkv_shortconv(...)            raw C call: ShortConv -> Swish -> L2Norm feature path
@@ -84,6 +86,8 @@ def lib():
     L.kda_prefill_ex.restype = ci
     L.kda_prefill_ex_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci, op]
     L.kda_prefill_ex_workspace_size.restype = sz
+    L.kda_prefill_noalloc.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, vp, vp, vp]
+    L.kda_prefill_noalloc.restype = ci
     L.kda_decode.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, vp, vp]
     L.kda_decode.restype = ci
     L.kda_qkv_shortconv.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, vp, vp, vp, vp,
@@ -126,6 +130,15 @@ def kda_prefill_ex(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk, d
     """opts: a PrefillOptions or None."""
     return lib().kda_prefill_ex(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv, o, hT,
                                 _opt_ref(opts), workspace, workspace_bytes, stream)
+
+
+def kda_prefill_noalloc(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv, o, hT,
+                        stream) -> int:
+    return lib().kda_prefill_noalloc(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv, o,
+                                     hT, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20   # KDA_NOALLOC_SCRATCH_BYTES
 
 
 def kda_decode(io_dtype, q, k, v, z, A, beta, S_inout, N, H, dk, dv, o, stream) -> int:

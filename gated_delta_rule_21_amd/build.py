@@ -20,7 +20,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_decode_window.hip", "kda_features.hip", "kda_prefill.hip", "kda_intra.hip", "kda_intra_f32.hip", "kda_backward.hip"]
+SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_decode_window.hip", "kda_features.hip", "kda_prefill.hip", "kda_intra.hip", "kda_intra_f32.hip", "kda_backward.hip", "kda_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

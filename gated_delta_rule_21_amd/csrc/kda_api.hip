@@ -50,6 +50,7 @@ const char *kda_status_string(int status) {
         case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
         case KDA_ERR_HIP: return "HIP kernel launch failed";
         case KDA_ERR_ALIAS: return "output overlaps an input";
+        case KDA_ERR_SCRATCH_TOO_SMALL: return "sizes need more workspace than the no-alloc scratch holds";
     }
     return "unknown kda status";
 }

@@ -65,7 +65,9 @@ typedef enum kda_status {
     KDA_ERR_MISALIGNED = -5,           /* a pointer is not 16-byte aligned */
     KDA_ERR_WORKSPACE_TOO_SMALL = -6,  /* workspace_bytes < kda_prefill_workspace_size */
     KDA_ERR_HIP = -7,                  /* a kernel launch failed */
-    KDA_ERR_ALIAS = -8                 /* an output overlaps an input it may not alias */
+    KDA_ERR_ALIAS = -8,                /* an output overlaps an input it may not alias */
+    KDA_ERR_SCRATCH_TOO_SMALL = -9     /* kda_prefill_noalloc: the sizes need more workspace
+                                          than KDA_NOALLOC_SCRATCH_BYTES */
 } kda_status;
 
 /*
@@ -175,6 +177,26 @@ int kda_prefill_ex(kda_dtype io_dtype, const void *q, const void *k, const void 
                    const int32_t *cu_seqlens, int N, int T, int H, int dk, int dv, void *o,
                    float *hT, const kda_prefill_options *options, void *workspace,
                    size_t workspace_bytes, void *stream);
+
+/*
+ * kda_prefill for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, results and errors are kda_prefill's (automatic segments),
+ * without the workspace: the call uses a device array of
+ * KDA_NOALLOC_SCRATCH_BYTES (256 MiB) that the library holds on every GPU it
+ * runs on until the process ends, and calls no allocating routine.  Sizes
+ * whose workspace (kda_prefill_workspace_size) exceeds the array return
+ * KDA_ERR_SCRATCH_TOO_SMALL and launch nothing; 256 MiB holds, for example,
+ * a 1024-token chunk of a 96-head prefill at d = 128, or 8 heads x 16384
+ * tokens.  Every call on one GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (two streams, or two threads without ordering) race and
+ * give undefined results.  Nothing in the array needs clearing between calls.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int kda_prefill_noalloc(kda_dtype io_dtype, const void *q, const void *k, const void *v,
+                        const float *z, const float *A, const float *beta, const float *h0,
+                        const int32_t *cu_seqlens, int N, int T, int H, int dk, int dv, void *o,
+                        float *hT, void *stream);
 
 /*
  * One decode step for N sequences, one token each.

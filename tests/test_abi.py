@@ -21,6 +21,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["kda_build_info", "kda_decode", "kda_decode_window", "kda_prefill",
                                            "kda_prefill_ex", "kda_prefill_ex_workspace_size",
+                                           "kda_prefill_noalloc",
                                            "kda_qkv_shortconv", "kda_output_gate",
                                            "kda_prefill_segments", "kda_prefill_workspace_size",
                                            "kda_prefill_backward", "kda_prefill_backward_workspace_size",
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert kda.kda_status_string(0) == "ok"
-    for s in range(-8, 0):
+    for s in range(-9, 0):
         assert kda.kda_status_string(s) != "unknown kda status"
     assert kda.kda_status_string(-99) == "unknown kda status"
 
@@ -85,6 +86,22 @@ def test_prefill_rejects_bad_arguments():
     assert _prefill() == -6                       # workspace one byte short
     big = 1 << 40
     assert _prefill(ws_bytes=big, o=FAKE) == -8   # o on top of q
+
+
+def test_prefill_noalloc_rejects_before_touching_the_device():
+    """Argument errors are kda_prefill's; sizes beyond the fixed scratch are
+    refused with their own status.  All of this is decided on the host."""
+    n = lambda **o: kda.kda_prefill_noalloc(o.get("io", 0), FAKE, FAKE + 4096, FAKE + 8192, FAKE + 16384,
+                                            FAKE + 32768, FAKE + 40960, None, FAKE + 49152, o.get("N", 1),
+                                            o.get("T", 65536), o.get("H", 96), o.get("d", 128), o.get("d", 128),
+                                            1 << 40, None, None)
+    assert n(io=5) == -4 and n(N=-1) == -1 and n(d=48) == -3
+    assert kda.kda_prefill_workspace_size(1, 65536, 96, 128, 128, 0) > kda.NOALLOC_SCRATCH_BYTES
+    assert n() == -9                                   # the K3 prefill does not fit 256 MiB
+    assert kda.kda_status_string(-9) != "unknown kda status"
+    # what does fit: a 1024-token chunk of the 96-head prefill, 8 heads x 16384 tokens
+    assert kda.kda_prefill_workspace_size(1, 1024, 96, 128, 128, 0) <= kda.NOALLOC_SCRATCH_BYTES
+    assert kda.kda_prefill_workspace_size(2, 16384, 8, 128, 128, 0) <= kda.NOALLOC_SCRATCH_BYTES
 
 
 def test_decode_rejects_bad_arguments():
