@@ -328,17 +328,23 @@ def prefill_backward_cost(kda, W, pre, reps: int = 3) -> dict:
     return out
 
 
-def feature_path_cost(kda, W, dev, reps: int = 10) -> dict:
+def feature_path_cost(kda, W, dev, pre, reps: int = 10) -> dict:
     """Side measurement at the K3 prefill shape (T=65536, H=96, d=128, bf16):
     the ShortConv -> Swish -> L2Norm feature path for q, k, v (with a carried
-    window) and the Sigmoid(g) * RMSNorm(o) output gate.  Algorithmic bytes:
-    three inputs read and three outputs written; o and g read and y written."""
+    window) and the Sigmoid(g) * RMSNorm(o) output gate, each alone; then the
+    three separate calls (feature path, kda_prefill on its q, k, v, output
+    gate) against kda_prefill_fused doing the same in one call.  Algorithmic
+    bytes: three inputs read and three outputs written; o and g read and y
+    written."""
     import torch
     f = W.random_features([65536], 96, 128, "bf16", window=True, device=dev)
     T, H, D = f["xq"].shape
     q, k, v = (torch.empty_like(f["xq"]) for _ in range(3))
     win_out = torch.empty_like(f["window"])
     y = torch.empty_like(f["o"])
+    o = torch.empty_like(f["o"])
+    hT = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+    ws = kda.prefill_workspace(1, T, H, D, kda.KDA_BF16, dev)
 
     def timed(fn):
         fn()
@@ -351,14 +357,34 @@ def feature_path_cost(kda, W, dev, reps: int = 10) -> dict:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    ms_qkv = timed(lambda: kda.qkv_shortconv(f["xq"], f["xk"], f["xv"], f["wq"], f["wk"], f["wv"],
-                                             f["cu_seqlens"], conv_state_in=f["window"],
-                                             conv_state_out=win_out, q=q, k=k, v=v))
-    ms_gate = timed(lambda: kda.output_gate(f["o"], f["g"], f["w"], 1e-6, y=y))
+    qkv = lambda: kda.qkv_shortconv(f["xq"], f["xk"], f["xv"], f["wq"], f["wk"], f["wv"], f["cu_seqlens"],
+                                    conv_state_in=f["window"], conv_state_out=win_out, q=q, k=k, v=v)
+    gate = lambda: kda.output_gate(o, f["g"], f["w"], 1e-6, y=y)
+
+    def separate():
+        qkv()
+        kda.prefill(q, k, v, pre["z"], pre["A"], pre["beta"], pre["cu_seqlens"], h0=None, o=o, hT=hT, workspace=ws)
+        gate()
+
+    def fused():
+        kda.prefill_fused(f["xq"], f["xk"], f["xv"], f["wq"], f["wk"], f["wv"], pre["z"], pre["A"], pre["beta"],
+                          pre["cu_seqlens"], f["g"], f["w"], 1e-6, conv_state_in=f["window"],
+                          conv_state_out=win_out, y=y, hT=hT, workspace=ws)
+
+    ms_qkv = timed(qkv)
+    ms_gate = timed(gate)
+    ms_sep = timed(separate)
+    ms_fused = timed(fused)
     row = T * H * D * 2
+    del ws, f, q, k, v, o, y
+    torch.cuda.empty_cache()
     return {"workload": "K3 shape T=65536 H=96 d=128 bf16",
             "qkv_shortconv": {"ms": round(ms_qkv, 4), "GBps": round(6 * row / (ms_qkv * 1e-3) / 1e9, 1)},
-            "output_gate": {"ms": round(ms_gate, 4), "GBps": round(3 * row / (ms_gate * 1e-3) / 1e9, 1)}}
+            "output_gate": {"ms": round(ms_gate, 4), "GBps": round(3 * row / (ms_gate * 1e-3) / 1e9, 1)},
+            "separate_calls": {"ms": round(ms_sep, 4), "what": "kda_qkv_shortconv + kda_prefill + kda_output_gate"},
+            "fused": {"ms": round(ms_fused, 4), "what": "kda_prefill_fused (same inputs and outputs)",
+                      "tokens_per_s": round(T / (ms_fused * 1e-3), 1),
+                      "saved_ms": round(ms_sep - ms_fused, 4)}}
 
 
 def main():
@@ -475,7 +501,7 @@ def main():
                                "1540 algorithmic B per (token, head) x 6291456 pairs per launch"},
     }
     if not args.no_features:
-        line["feature_path"] = feature_path_cost(kda, W, dev)
+        line["feature_path"] = feature_path_cost(kda, W, dev, pre)
     if not args.no_backward:
         line["prefill_backward"] = prefill_backward_cost(kda, W, pre)
     if not args.no_checkpoints:

@@ -11,6 +11,7 @@ Entry points (same names as the C ABI in include/kda.h):
                                     (segment count, state checkpoints)
   kda_prefill_noalloc(...)          raw C call: prefill without a workspace (the
                                     library's fixed device scratch; no allocation)
+  kda_prefill_fused(...)            raw C call: feature path -> prefill -> output gate
   kda_decode(...)                   raw C call
   kda_decode_window(...)            raw C call: replay + multi-token window
   kda_qkv_shortconv(...)            raw C call: ShortConv -> Swish -> L2Norm feature path
@@ -29,6 +30,8 @@ cannot see them):
   decode_window(A, S, window=..., replay=..., n_accept=...) -> o
   prefill_checkpoints(..., interval, segments=0) -> (o, hT, checkpoints, offsets)
   qkv_shortconv(xq, xk, xv, wq, wk, wv, cu_seqlens, ...) -> (q, k, v)
+  prefill_fused(xq, xk, xv, wq, wk, wv, z, A, beta, cu_seqlens, gate, norm_weight, eps, ...)
+      -> (y, hT)                               (the three in one call, bf16)
   output_gate(o, g, w, eps) -> y
   prefill_backward(q, k, v, z, A, beta, cu_seqlens, grad_o, h0=None, grad_hT=None, segments=0)
       -> dict(dq, dk, dv, dz, dbeta, dA, dh0)
@@ -88,6 +91,9 @@ def lib():
     L.kda_prefill_ex_workspace_size.restype = sz
     L.kda_prefill_noalloc.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, vp, vp, vp]
     L.kda_prefill_noalloc.restype = ci
+    L.kda_prefill_fused.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci,
+                                    vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
+    L.kda_prefill_fused.restype = ci
     L.kda_decode.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, vp, vp]
     L.kda_decode.restype = ci
     L.kda_qkv_shortconv.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, vp, vp, vp, vp,
@@ -139,6 +145,14 @@ def kda_prefill_noalloc(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, 
 
 
 NOALLOC_SCRATCH_BYTES = 256 << 20   # KDA_NOALLOC_SCRATCH_BYTES
+
+
+def kda_prefill_fused(io_dtype, xq, xk, xv, wq, wk, wv, conv_state_in, conv_state_out, z, A, beta, h0,
+                      cu_seqlens, N, T, H, dk, dv, gate, norm_weight, eps, y, hT, workspace, workspace_bytes,
+                      stream) -> int:
+    return lib().kda_prefill_fused(io_dtype, xq, xk, xv, wq, wk, wv, conv_state_in, conv_state_out, z, A, beta,
+                                   h0, cu_seqlens, N, T, H, dk, dv, gate, norm_weight, float(eps), y, hT,
+                                   workspace, workspace_bytes, stream)
 
 
 def kda_decode(io_dtype, q, k, v, z, A, beta, S_inout, N, H, dk, dv, o, stream) -> int:
@@ -437,6 +451,54 @@ def prefill_checkpoints(q, k, v, z, A, beta, cu_seqlens, interval: int, h0=None,
     if st != 0:
         raise KdaError("kda_prefill_ex", st)
     return o, hT, checkpoints, offsets
+
+
+def prefill_fused(xq, xk, xv, wq, wk, wv, z, A, beta, cu_seqlens, gate, norm_weight, eps: float, h0=None,
+                  conv_state_in=None, conv_state_out=None, y=None, hT=None, workspace=None, final_state=True):
+    """The feature path, the prefill and the output gate in one call (bf16):
+    y = Sigmoid(gate) * RMSNorm(o) with o, hT = prefill(q, k, v, ...) and q, k,
+    v = qkv_shortconv(xq, xk, xv, ...).  Returns (y, hT); conv_state_out (may
+    be conv_state_in) receives the new conv window."""
+    torch = _torch()
+    _check("xq", xq, (None, None, None), torch.bfloat16)
+    T, H, d = xq.shape
+    dev = xq.device
+    _check("xk", xk, (T, H, d), torch.bfloat16, dev)
+    _check("xv", xv, (T, H, d), torch.bfloat16, dev)
+    for name, t in (("wq", wq), ("wk", wk), ("wv", wv)):
+        _check(name, t, (H, d, 4), torch.float32, dev)
+    _check("z", z, (T, H, d), torch.float32, dev)
+    _check("A", A, (H,), torch.float32, dev)
+    _check("beta", beta, (T, H), torch.float32, dev)
+    _check("cu_seqlens", cu_seqlens, (None,), torch.int32, dev)
+    if cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens needs N + 1 >= 1 entries")
+    N = cu_seqlens.numel() - 1
+    _check("h0", h0, (N, H, d, d), torch.float32, dev)
+    _check("conv_state_in", conv_state_in, (N, 3, H, 3 * d), torch.bfloat16, dev)
+    _check("conv_state_out", conv_state_out, (N, 3, H, 3 * d), torch.bfloat16, dev)
+    _check("gate", gate, (T, H, d), torch.bfloat16, dev)
+    _check("norm_weight", norm_weight, (d,), torch.float32, dev)
+    _check("y", y, (T, H, d), torch.bfloat16, dev)
+    _check("hT", hT, (N, H, d, d), torch.float32, dev)
+    _check("workspace", workspace, (None,), torch.uint8, dev)
+    _on_gpu(dev, xq=xq, xk=xk, xv=xv, wq=wq, wk=wk, wv=wv, z=z, A=A, beta=beta, cu_seqlens=cu_seqlens, h0=h0,
+            conv_state_in=conv_state_in, conv_state_out=conv_state_out, gate=gate, norm_weight=norm_weight, y=y,
+            hT=hT, workspace=workspace)
+    if y is None:
+        y = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+    if hT is None and final_state:
+        hT = torch.empty((N, H, d, d), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = prefill_workspace(N, T, H, d, KDA_BF16, dev)
+    _check_workspace(workspace, kda_prefill_workspace_size(N, T, H, d, d, KDA_BF16), dev)
+    st = kda_prefill_fused(KDA_BF16, _ptr(xq), _ptr(xk), _ptr(xv), _ptr(wq), _ptr(wk), _ptr(wv),
+                           _ptr(conv_state_in), _ptr(conv_state_out), _ptr(z), _ptr(A), _ptr(beta), _ptr(h0),
+                           _ptr(cu_seqlens), N, T, H, d, d, _ptr(gate), _ptr(norm_weight), eps, _ptr(y), _ptr(hT),
+                           _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != 0:
+        raise KdaError("kda_prefill_fused", st)
+    return y, hT
 
 
 def qkv_shortconv(xq, xk, xv, wq, wk, wv, cu_seqlens, conv_state_in=None, conv_state_out=None,

@@ -115,7 +115,7 @@ namespace {
 int prefill_impl(kda_dtype io_dtype, const void *q, const void *k, const void *v, const float *z,
                  const float *A, const float *beta, const float *h0, const int32_t *cu_seqlens, int N,
                  int T, int H, int dk, int dv, void *o, float *hT, const kda_prefill_options *opt,
-                 void *workspace, size_t workspace_bytes, void *stream) {
+                 void *workspace, size_t workspace_bytes, void *stream, const kda::FusedIO *fx = nullptr) {
     if (io_dtype != KDA_BF16 && io_dtype != KDA_F32) return KDA_ERR_UNSUPPORTED_DTYPE;
     float *ck = opt ? opt->checkpoints : nullptr;
     int32_t *ck_offsets = opt ? opt->checkpoint_offsets : nullptr;
@@ -126,7 +126,8 @@ int prefill_impl(kda_dtype io_dtype, const void *q, const void *k, const void *v
     if (N < 0 || T < 0 || H <= 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!supported_dim(dk, dv)) return KDA_ERR_UNSUPPORTED_DIM;
     if (!A || !cu_seqlens || !workspace) return KDA_ERR_NULL_POINTER;
-    if (T > 0 && (!q || !k || !v || !z || !beta || !o)) return KDA_ERR_NULL_POINTER;
+    if (T > 0 && (!z || !beta || !o)) return KDA_ERR_NULL_POINTER;
+    if (T > 0 && !fx && (!q || !k || !v)) return KDA_ERR_NULL_POINTER;
     const void *ptrs[] = {q, k, v, z, A, beta, h0, cu_seqlens, o, hT, ck, ck_offsets};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
@@ -147,6 +148,23 @@ int prefill_impl(kda_dtype io_dtype, const void *q, const void *k, const void *v
     for (const auto &in : ins) {
         if (overlaps(o, o_bytes, in.p, in.n)) return KDA_ERR_ALIAS;
         if (in.p != h0 && overlaps(hT, st_bytes, in.p, in.n)) return KDA_ERR_ALIAS;
+    }
+    if (fx) {
+        // the fused call's inputs and the conv window it writes
+        const size_t xb = tok * dk * io_size(io_dtype), wb = (size_t)H * dk * 16;
+        const size_t win_bytes = (size_t)N * 3 * H * 3 * dk * io_size(io_dtype);
+        const struct { const void *p; size_t n; } fin[] = {
+            {fx->xq, xb}, {fx->xk, xb}, {fx->xv, xb}, {fx->wq, wb}, {fx->wk, wb}, {fx->wv, wb},
+            {fx->win_in, win_bytes}, {fx->g, o_bytes}, {fx->w, (size_t)dv * 4}};
+        for (const auto &in : fin) {
+            if (overlaps(o, o_bytes, in.p, in.n) || overlaps(hT, st_bytes, in.p, in.n)) return KDA_ERR_ALIAS;
+            if (!(in.p == fx->win_in && fx->win_out == fx->win_in) && overlaps(fx->win_out, win_bytes, in.p, in.n))
+                return KDA_ERR_ALIAS;
+        }
+        for (const auto &in : ins)
+            if (overlaps(fx->win_out, win_bytes, in.p, in.n)) return KDA_ERR_ALIAS;
+        if (overlaps(fx->win_out, win_bytes, o, o_bytes) || overlaps(fx->win_out, win_bytes, hT, st_bytes))
+            return KDA_ERR_ALIAS;
     }
     if (hT && h0 && hT != h0 && overlaps(hT, st_bytes, h0, st_bytes)) return KDA_ERR_ALIAS;
     if (overlaps(o, o_bytes, hT, st_bytes)) return KDA_ERR_ALIAS;
@@ -184,6 +202,7 @@ int prefill_impl(kda_dtype io_dtype, const void *q, const void *k, const void *v
     a.ws = static_cast<unsigned char *>(workspace);
     a.plan = plan;
     a.stream = st;
+    a.fused = fx;
     return kda::launch_prefill(a) == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -205,6 +224,28 @@ int kda_prefill_ex(kda_dtype io_dtype, const void *q, const void *k, const void 
                    void *workspace, size_t workspace_bytes, void *stream) {
     return prefill_impl(io_dtype, q, k, v, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv, o, hT, options,
                         workspace, workspace_bytes, stream);
+}
+
+int kda_prefill_fused(kda_dtype io_dtype, const void *xq, const void *xk, const void *xv, const float *wq,
+                      const float *wk, const float *wv, const void *conv_state_in, void *conv_state_out,
+                      const float *z, const float *A, const float *beta, const float *h0, const int32_t *cu_seqlens,
+                      int N, int T, int H, int dk, int dv, const void *gate, const float *norm_weight, float eps,
+                      void *y, float *hT, void *workspace, size_t workspace_bytes, void *stream) {
+    if (io_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED_DTYPE;
+    if (N < 0 || T < 0 || H <= 0 || !(eps >= 0.f)) return KDA_ERR_INVALID_ARGUMENT;
+    if (!supported_dim(dk, dv)) return KDA_ERR_UNSUPPORTED_DIM;
+    if (!wq || !wk || !wv || !norm_weight) return KDA_ERR_NULL_POINTER;
+    if (T > 0 && (!xq || !xk || !xv || !gate)) return KDA_ERR_NULL_POINTER;
+    const void *ptrs[] = {xq, xk, xv, wq, wk, wv, conv_state_in, conv_state_out, gate, norm_weight};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    kda::FusedIO fx;
+    fx.xq = xq; fx.xk = xk; fx.xv = xv;
+    fx.wq = wq; fx.wk = wk; fx.wv = wv;
+    fx.win_in = conv_state_in; fx.win_out = conv_state_out;
+    fx.g = gate; fx.w = norm_weight; fx.eps = eps;
+    return prefill_impl(io_dtype, nullptr, nullptr, nullptr, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv, y, hT,
+                        nullptr, workspace, workspace_bytes, stream, &fx);
 }
 
 size_t kda_prefill_backward_workspace_size(int N, int T, int H, int dk, int dv, kda_dtype io_dtype,

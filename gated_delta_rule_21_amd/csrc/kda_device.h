@@ -82,6 +82,14 @@ __device__ __forceinline__ float gate_log2(float ea, float z) {
     return kGminLog2e * s;
 }
 
+// Swish and the norms of the feature path and the output gate use the
+// hardware reciprocal and reciprocal square root (about 1 ulp) instead of
+// IEEE division: their outputs are rounded to the io dtype, and a correctly
+// rounded division costs about ten instructions.
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_rsq(float x) { return __builtin_amdgcn_rsqf(x); }
+__device__ __forceinline__ float swish(float u) { return u * fast_rcp(1.f + __expf(-u)); }
+
 // 2^x on the transcendental unit (v_exp_f32).  Results below 2^-126 may
 // flush to zero; every use here is a decay factor whose true value is then
 // negligible.

@@ -23,13 +23,6 @@ namespace kda {
 
 constexpr int kTaps = 4;
 
-// Swish and the norms use the hardware reciprocal and reciprocal square root
-// (about 1 ulp) instead of IEEE division: the outputs are rounded to the io
-// dtype, and a correctly rounded division costs about ten instructions here.
-__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
-__device__ __forceinline__ float fast_rsq(float x) { return __builtin_amdgcn_rsqf(x); }
-__device__ __forceinline__ float swish(float u) { return u * fast_rcp(1.f + __expf(-u)); }
-
 // Four consecutive elements of an io-dtype array (8 or 16 bytes).
 template <bool F32IO>
 __device__ __forceinline__ void store_io4(void *p, size_t i, f32x4 x) {
@@ -268,6 +261,19 @@ static int launch_features_t(const FeatureArgs &a) {
         if (hipGetLastError() != hipSuccess) return -1;
     }
     return 0;
+}
+
+int launch_conv_window(bool f32io, const void *xq, const void *xk, const void *xv, const int32_t *cu, int N, int T,
+                       int H, int d, const void *win_in, void *win_out, hipStream_t stream) {
+    if (!win_out || N <= 0) return 0;
+    const long long items = (long long)N * H * (3 * d / 4);
+    if (f32io)
+        hipLaunchKernelGGL((conv_window_kernel<true>), dim3(stride_blocks(items, 256)), dim3(256), 0, stream, xq, xk,
+                           xv, cu, N, T, H, d, win_in, win_out);
+    else
+        hipLaunchKernelGGL((conv_window_kernel<false>), dim3(stride_blocks(items, 256)), dim3(256), 0, stream, xq, xk,
+                           xv, cu, N, T, H, d, win_in, win_out);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_features(const FeatureArgs &a) {

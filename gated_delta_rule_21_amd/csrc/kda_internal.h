@@ -88,6 +88,18 @@ struct PrefillPlan {
 constexpr int kMaxSegments = 16;
 static_assert(kMaxSegments <= 64, "segment records per wave");
 
+// The fused prefill's extra inputs and outputs (bf16 path): the feature
+// path in front of the recurrence and the output gate behind it.
+struct FusedIO {
+    const void *xq, *xk, *xv;    // [T][H][d] projected inputs, io dtype (q, k, v are computed from them)
+    const float *wq, *wk, *wv;   // [H][d][4] ShortConv taps
+    const void *win_in;          // [N][3][H][3d] carried conv window, or NULL (zeros)
+    void *win_out;               // the window after the call, or NULL; may be win_in
+    const void *g;               // [T][H][dv] gate projection, io dtype
+    const float *w;              // [dv] RMSNorm weight
+    float eps;
+};
+
 struct PrefillArgs {
     bool f32io;
     const void *q, *k, *v;
@@ -102,6 +114,8 @@ struct PrefillArgs {
     unsigned char *ws;
     PrefillPlan plan;
     hipStream_t stream;
+    // fused call: q, k, v are NULL and o receives y = Sigmoid(g) * RMSNorm(o)
+    const FusedIO *fused = nullptr;
 };
 
 // Workspace plan of the prefill backward: the forward's own workspace, its
@@ -137,6 +151,9 @@ size_t slab_bytes(int dk, int dv, bool f32io);
 int launch_decode(const DecodeArgs &a);
 int launch_decode_window(const DecodeWindowArgs &a);
 int launch_features(const FeatureArgs &a);
+// Only the carried conv window of the feature path (win_out from x and win_in).
+int launch_conv_window(bool f32io, const void *xq, const void *xk, const void *xv, const int32_t *cu, int N, int T,
+                       int H, int d, const void *win_in, void *win_out, hipStream_t stream);
 int launch_output_gate(const GateArgs &a);
 int launch_prefill(const PrefillArgs &a);
 int launch_prefill_backward(const BackwardArgs &a);

@@ -177,12 +177,104 @@ __device__ __forceinline__ void load_rows4_v(Rows4<D> &R, const uint16_t *q, con
     for (int kt = 0; kt < KT; ++kt) R.v[kt] = *reinterpret_cast<const u32x2 *>(vr + 16 * kt + 4 * lg);
 }
 
-template <int D>
+// The q / k / v feature path of the fused prefill, in place of a row load:
+// ShortConv(4) -> Swish (-> L2Norm over the row's D channels when NORM),
+// rounded to bf16 and packed exactly like a loaded row, so that every later
+// step is the unfused kernel's (the unfused pipeline hands q, k, v over in
+// bf16 as well).  out[kt] = channels 16 kt + 4 lg .. + 3 of row 16 b + ln of
+// the chunk.  Taps on the three earlier tokens come from the lanes of the
+// same 16-lane row by DPP shifts; the block's first three rows take them from
+// the three rows before the block, which lanes 0..2 load: from x inside the
+// sequence, or, at a sequence's first chunk (ent.w set), from the carried
+// window (zeros without one).  Rows past the chunk's end give zeros, like
+// the null row of the unfused kernel.  Tap order, Swish and the L2 norm's
+// hardware reciprocal square root follow the feature kernel.
+// The row SFT tokens before lane ln's: lane ln - SFT of the same 16-lane row
+// (row_shr), or for ln < SFT the pre-block row ln - SFT + 3, held by lane
+// ln + 3 - SFT (row_shl).
+template <int SFT>
+__device__ __forceinline__ u32x2 earlier_tap(u32x2 own, u32x2 pre, int ln) {
+    u32x2 r;
+#pragma unroll
+    for (int wd = 0; wd < 2; ++wd) {
+        const uint32_t from_row = __builtin_amdgcn_update_dpp(0, own[wd], 0x110 + SFT, 0xf, 0xf, true);
+        const uint32_t from_pre =
+            SFT == 3 ? pre[wd] : __builtin_amdgcn_update_dpp(0, pre[wd], 0x100 + (3 - SFT), 0xf, 0xf, true);
+        r[wd] = ln >= SFT ? from_row : from_pre;
+    }
+    return r;
+}
+
+template <int D, bool NORM>
+__device__ __forceinline__ void feature_row(u32x2 (&out)[D / 16], const uint16_t *x, const float *w,
+                                            const uint16_t *win, int which, int4 ent, int h, int H, int b, int ln,
+                                            int lg) {
+    constexpr int KT = D / 16;
+    const int row = 16 * b + ln;
+    const bool ok = row < ent.z;
+    const bool live = 16 * b < ent.z;                     // the block has rows
+    const uint16_t *xr = x + ((size_t)(ent.y + (ok ? row : 0)) * H + h) * D + 4 * lg;
+    const uint16_t *pr = nullptr;
+    if (live && ln < 3) {
+        if (b > 0 || ent.w == 0)
+            pr = x + ((size_t)(ent.y + 16 * b - 3 + ln) * H + h) * D + 4 * lg;
+        else if (win)
+            pr = win + ((size_t)(ent.x * 3 + ln) * H + h) * (3 * D) + which * D + 4 * lg;
+    }
+    u32x2 own[KT], pre[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        own[kt] = live ? *reinterpret_cast<const u32x2 *>(xr + 16 * kt) : u32x2{0u, 0u};
+        pre[kt] = pr ? *reinterpret_cast<const u32x2 *>(pr + 16 * kt) : u32x2{0u, 0u};
+    }
+    // taps of channel 4 lg + j of tile kt: f32x4 index 16 kt + j from wr
+    const f32x4 *wr = reinterpret_cast<const f32x4 *>(w + ((size_t)h * D + 4 * lg) * 4);
+    auto pack = [&](f32x4 y) -> u32x2 {
+        return ok ? u32x2{f32x2_to_bf16x2(y[0], y[1]), f32x2_to_bf16x2(y[2], y[3])} : u32x2{0u, 0u};
+    };
+    f32x4 f[NORM ? KT : 1];
+    float ss = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        u32x2 tap[4];                                     // tap i meets token t - 3 + i
+        tap[3] = own[kt];
+        tap[2] = earlier_tap<1>(own[kt], pre[kt], ln);
+        tap[1] = earlier_tap<2>(own[kt], pre[kt], ln);
+        tap[0] = earlier_tap<3>(own[kt], pre[kt], ln);
+        f32x4 tv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tv[i] = quad_f32<false>(tap[i]);
+        f32x4 fk;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const f32x4 wj = wr[16 * kt + c];
+            float u = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) u += wj[i] * tv[i][c];
+            fk[c] = swish(u);
+        }
+        if constexpr (NORM) {
+            f[kt] = fk;
+            ss += fk[0] * fk[0] + fk[1] * fk[1] + fk[2] * fk[2] + fk[3] * fk[3];
+        } else {
+            out[kt] = pack(fk);                           // no norm: each tile is final
+        }
+    }
+    if constexpr (NORM) {
+        ss += __shfl_xor(ss, 16, 64);                     // the row's other channel groups (lg)
+        ss += __shfl_xor(ss, 32, 64);
+        const float inv = fast_rsq(ss);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) out[kt] = pack(f[kt] * inv);
+    }
+}
+
+template <int D, bool FEAT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) intra4_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ z, const float *__restrict__ A, const float *__restrict__ beta,
     const int32_t *__restrict__ meta, const int4 *__restrict__ table, const float *__restrict__ null_row, int N,
-    int H, int max_chunks, unsigned char *__restrict__ slabs, size_t slab_stride) {
+    int H, int max_chunks, unsigned char *__restrict__ slabs, size_t slab_stride, FusedIO fx) {
     using SL = Slab<D, false>;
     using LY = Intra4Lds<D>;
     constexpr int KT = D / 16, NP = D / 32;
@@ -231,7 +323,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         const float a_next = it_next < total ? A[it_next % H] : 0.f;
 
         // ---- phase 1: gate, block-local cumulative log2-decay, row operands
-        load_rows4_kq<D>(R, q, k, v, z, null_row, ent, h, H, row, lg);
+        if constexpr (FEAT) {
+            feature_row<D, true>(R.k, static_cast<const uint16_t *>(fx.xk), fx.wk,
+                                 static_cast<const uint16_t *>(fx.win_in), 1, ent, h, H, b, ln, lg);
+            feature_row<D, true>(R.q, static_cast<const uint16_t *>(fx.xq), fx.wq,
+                                 static_cast<const uint16_t *>(fx.win_in), 0, ent, h, H, b, ln, lg);
+        } else {
+            load_rows4_kq<D>(R, q, k, v, z, null_row, ent, h, H, row, lg);
+        }
         if (lg == 0) sbeta[row] = R.beta;
         f32x4 kr[KT], qr[KT], ke[KT];
 #pragma unroll
@@ -357,7 +456,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         __syncthreads();
 
         // ---- phase 3: Gamma*K (split) and V into X as row-major tiles
-        load_rows4_v<D>(R, q, k, v, z, null_row, ent, h, H, row, lg);
+        if constexpr (!FEAT) load_rows4_v<D>(R, q, k, v, z, null_row, ent, h, H, row, lg);
         {
             const float *pfx = fac_lds + (4 + b) * D;
 #pragma unroll
@@ -391,6 +490,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
         // V last: its loads, issued at the top of the phase, complete behind
         // the Gamma*K split and the diagonal solve instead of stalling them
+        if constexpr (FEAT)
+            feature_row<D, false>(R.v, static_cast<const uint16_t *>(fx.xv), fx.wv,
+                                  static_cast<const uint16_t *>(fx.win_in), 2, ent, h, H, b, ln, lg);
 #pragma unroll
         for (int t = 0; t < KT; ++t)
             *reinterpret_cast<u32x2 *>(X + LY::VT + (size_t)(t * 4 + b) * 512 + ln * 32 + lg * 8) = R.v[t];
@@ -497,13 +599,16 @@ int launch_intra_bf16(const PrefillArgs &a, const int32_t *meta, const int4 *tab
     using LY = Intra4Lds<D>;
     const long long items = (long long)a.plan.max_chunks * a.H;
     if (items <= 0) return 0;
-    if (!set_lds(&intra4_kernel<D>, LY::bytes)) return -1;
     const int grid = (int)std::min<long long>(items, 2LL * device_cus());
-    hipLaunchKernelGGL(intra4_kernel<D>, dim3(grid), dim3(256), LY::bytes, a.stream,
-                       reinterpret_cast<const uint16_t *>(a.q), reinterpret_cast<const uint16_t *>(a.k),
-                       reinterpret_cast<const uint16_t *>(a.v), a.z, a.A, a.beta, meta, table, null_row, a.N, a.H,
-                       a.plan.max_chunks, slabs, a.plan.slab_bytes);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
+    auto launch = [&](auto kernel, const FusedIO &fx) -> int {
+        if (!set_lds(kernel, LY::bytes)) return -1;
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), LY::bytes, a.stream, reinterpret_cast<const uint16_t *>(a.q),
+                           reinterpret_cast<const uint16_t *>(a.k), reinterpret_cast<const uint16_t *>(a.v), a.z, a.A,
+                           a.beta, meta, table, null_row, a.N, a.H, a.plan.max_chunks, slabs, a.plan.slab_bytes, fx);
+        return hipGetLastError() == hipSuccess ? 0 : -1;
+    };
+    if (a.fused) return launch(intra4_kernel<D, true>, *a.fused);
+    return launch(intra4_kernel<D, false>, FusedIO{});
 }
 
 template int launch_intra_bf16<32>(const PrefillArgs &, const int32_t *, const int4 *, const float *,

@@ -86,11 +86,13 @@ constexpr int kSegValid = 1, kSegFirst = 2, kSegLast = 4;
 // inter_kernel modes: the outputs and final states; or the segment's
 // transition, two states carried side by side over the same chunk operands:
 // the matrix M (run from the identity with U = 0) and the offset S~ (run from zero)
-constexpr int kModeOutput = 0, kModeTrans = 1;
+// the outputs with the output gate applied (fused prefill): y = Sigmoid(g) *
+// RMSNorm(o), one workgroup per head so that a row's RMS covers its dv channels
+constexpr int kModeOutput = 0, kModeTrans = 1, kModeGate = 2;
 
 // ---------------------------------------------------------------------------
 // Chunk table.  One workgroup.  meta[n] = first chunk of sequence n,
-// meta[N] = number of chunks; table[c] = {n, first token, length, 0};
+// meta[N] = number of chunks; table[c] = {n, first token, length, first chunk of n};
 // segs[n P + k] = {n, first chunk, end chunk, flags} of segment k of sequence n;
 // with checkpoints, ck_off[n] = index of sequence n's first checkpoint.
 // Sequence bounds are clamped to [0, T] and the chunk count to max_chunks,
@@ -145,7 +147,9 @@ __global__ void __launch_bounds__(256) chunk_table_kernel(const int32_t *__restr
         const int n = lo;
         const int s = min(max(cu[n], 0), T), e = min(max(cu[n + 1], 0), T);
         const int first = s + (c - meta[n]) * kChunk;
-        table[c] = make_int4(n, first, min(kChunk, e - first), 0);
+        // .w marks a sequence's first chunk (the fused prefill's feature path
+        // reads the carried conv window there)
+        table[c] = make_int4(n, first, min(kChunk, e - first), c == meta[n] ? 1 : 0);
     }
     // segments: sequence n is cut into Pn = clamp(chunks, 1, P) runs of
     // consecutive chunks of near-equal length; slots past Pn are invalid
@@ -219,19 +223,28 @@ __global__ void __launch_bounds__(256) chunk_table_kernel(const int32_t *__restr
 // (larger fragments): region B of this chunk streams during phase A, region
 // A of the next chunk during phase B.
 // ---------------------------------------------------------------------------
-template <int D, bool F32IO>
+template <int D, bool F32IO, int MODE>
 struct InterShape {
     using SL = Slab<D, F32IO>;
+    static constexpr bool GATE = MODE == kModeGate;
     static constexpr int KT = D / 16;
-    static constexpr int WPG = KT < 4 ? KT : 4;          // waves per workgroup
+    // waves per workgroup, 16 value columns each; the gate mode needs whole
+    // rows in one workgroup
+    static constexpr int WPG = GATE ? KT : (KT < 4 ? KT : 4);
     static constexpr int NT = 64 * WPG;
-    // bf16 path: region A ring of 3, region B ring of 2, and two output
-    // staging tiles of 64 rows x (16 * WPG) bf16 columns
+    static constexpr int GROUPS = KT / WPG;              // workgroups per (segment, head)
+    static constexpr int WAVES_PER_SIMD = (NT + 255) / 256;
+    // bf16 path: region A ring of 3, region B ring of 2, and output staging
+    // tiles of 64 rows x (16 * WPG) columns: two in bf16; in the gate mode one
+    // in fp16 with a power-of-two exponent per wave
     static constexpr size_t ABYTES = (size_t)SL::FA * SL::FRAG, BBYTES = (size_t)SL::FB * SL::FRAG;
-    static constexpr int OPITCH = 16 * WPG + 8;                  // bf16 elements per staged row
+    static constexpr int OPITCH = 16 * WPG + 8;                  // elements per staged row
     static constexpr size_t obuf_bytes = F32IO ? 0 : (size_t)64 * OPITCH * 2;
     static constexpr size_t ring_bytes = 3 * ABYTES + 2 * BBYTES;
-    static constexpr size_t lds_bytes = F32IO ? (size_t)(SL::FA + SL::FB) * SL::FRAG : ring_bytes + 2 * obuf_bytes;
+    static constexpr size_t lds_bytes =
+        F32IO ? (size_t)(SL::FA + SL::FB) * SL::FRAG : ring_bytes + (GATE ? obuf_bytes + 64 : 2 * obuf_bytes);
+    static_assert(!(GATE && F32IO), "the gate mode is a bf16-path mode");
+    static_assert(lds_bytes <= 160 * 1024, "LDS per workgroup");
 };
 
 // Copy `nfrag` consecutive 1 KiB fragments from global `src` to LDS `dst`,
@@ -256,7 +269,13 @@ __device__ __forceinline__ u32x2 load_untracked(const u32x2 *p) {
     asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
     return r;
 }
+__device__ __forceinline__ u32x4 load_untracked4(const u32x4 *p) {
+    u32x4 r;
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+    return r;
+}
 __device__ __forceinline__ void settle(u32x2 &r) { asm volatile("" : "+v"(r)); }
+__device__ __forceinline__ void settle(u32x4 &r) { asm volatile("" : "+v"(r)); }
 
 // Workgroup barrier for LDS written by ds instructions.  __syncthreads (and
 // any release fence covering LDS) also waits for every direct global->LDS
@@ -309,15 +328,20 @@ __device__ __forceinline__ float to_f16_scaled(const f32x4 *x, u32x4 *out) {
 }
 
 template <int D, bool F32IO, int MODE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) inter_kernel(
+__global__ void __launch_bounds__((InterShape<D, F32IO, MODE>::NT))
+    __attribute__((amdgpu_waves_per_eu((InterShape<D, F32IO, MODE>::WAVES_PER_SIMD),
+                                       (InterShape<D, F32IO, MODE>::WAVES_PER_SIMD)))) inter_kernel(
     const float *__restrict__ h0, const float *__restrict__ s_in, const int4 *__restrict__ segs,
     const int4 *__restrict__ table, int nseg, int H, int max_chunks, const unsigned char *__restrict__ slabs,
     size_t slab_stride, void *__restrict__ o, float *__restrict__ hT, float *__restrict__ trans, int groups,
-    const int32_t *__restrict__ meta, const int32_t *__restrict__ ck_off, float *__restrict__ ck, int ck_chunks) {
-    static_assert(MODE == kModeOutput || MODE == kModeTrans, "mode");
+    const int32_t *__restrict__ meta, const int32_t *__restrict__ ck_off, float *__restrict__ ck, int ck_chunks,
+    const uint16_t *__restrict__ gate, const float *__restrict__ norm_w, float eps) {
+    static_assert(MODE == kModeOutput || MODE == kModeTrans || MODE == kModeGate, "mode");
     constexpr bool TR = MODE == kModeTrans;
+    constexpr bool OUT = !TR;                       // the mode writes outputs and the final state
+    constexpr bool GATE = MODE == kModeGate;
     using SL = Slab<D, F32IO>;
-    using SHP = InterShape<D, F32IO>;
+    using SHP = InterShape<D, F32IO, MODE>;
     constexpr int KT = D / 16;
     constexpr int WPG = SHP::WPG;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
@@ -332,7 +356,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int sg = unit / H, h = unit % H;
     const int4 rec = segs[sg];
     if (!(rec.w & kSegValid)) return;
-    if (MODE != kModeOutput && (rec.w & kSegLast)) return;   // no transition after the last segment
+    if (TR && (rec.w & kSegLast)) return;   // no transition after the last segment
     const int n = rec.x;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index in an SGPR
@@ -367,13 +391,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     // state checkpoints (output mode): after every chunk that ends 64 ck_chunks
     // tokens into the sequence, up to the sequence's count
     int ck_c0 = 0, ck_first = 0, ck_count = 0;
-    if (MODE == kModeOutput && ck) {
+    if (OUT && ck) {
         ck_c0 = meta[n];
         ck_first = ck_off[n];
         ck_count = ck_off[n + 1] - ck_first;
     }
     auto checkpoint = [&](int c) {   // S holds the state after chunk c
-        if (MODE != kModeOutput || !ck) return;
+        if (!OUT || !ck) return;
         const int pos = c - ck_c0 + 1;
         if (pos % ck_chunks != 0 || pos / ck_chunks > ck_count) return;
         float *dst = ck + (((size_t)(ck_first + pos / ck_chunks - 1) * H + h) * D + col) * D;
@@ -412,15 +436,59 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
         constexpr size_t AB = SHP::ABYTES, BB = SHP::BBYTES;
         unsigned char *aring = lds_raw, *bring = lds_raw + 3 * AB;
         uint16_t *obuf = reinterpret_cast<uint16_t *>(lds_raw + SHP::ring_bytes);
+        int *oexp = reinterpret_cast<int *>(lds_raw + SHP::ring_bytes + SHP::obuf_bytes);   // gate mode
+        constexpr int SEG = 16 * WPG / 8;                       // 16-byte pieces per row
+        constexpr int PPT = 64 * SEG / SHP::NT;                 // pieces per thread (2)
+        static_assert(64 * SEG % SHP::NT == 0, "pieces per thread");
         auto flush_o = [&](int par, int t0, int L) {
             const uint16_t *ob = obuf + par * 64 * OP;
-            constexpr int SEG = 16 * WPG / 8;                   // 16-byte pieces per row
             for (int i = tid; i < 64 * SEG; i += SHP::NT) {
                 const int r = i / SEG, sgm = i % SEG;
                 if (r < L)
                     *reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(o) +
                                                ((size_t)(t0 + r) * H + h) * D + 16 * WPG * cg + 8 * sgm) =
                         *reinterpret_cast<const u32x4 *>(ob + r * OP + 8 * sgm);
+            }
+        };
+        // Gate mode.  The SEG threads of a row are consecutive lanes holding
+        // 8 channels each: the row's sum of squares is a lane-group
+        // reduction, then y = o / sqrt(mean(o^2) + eps) * w * Sigmoid(g), in
+        // the order of the standalone gate kernel, rounded once to bf16.
+        // g of the flushed chunk's rows was loaded during the step before.
+        f32x4 nw[2];
+        u32x4 gcur[PPT], gnext[PPT];
+        if constexpr (GATE) {
+            const int c0 = 8 * (tid % SEG);
+            nw[0] = *reinterpret_cast<const f32x4 *>(norm_w + c0);
+            nw[1] = *reinterpret_cast<const f32x4 *>(norm_w + c0 + 4);
+        }
+        auto flush_gate = [&](int t0, int L) {
+#pragma unroll
+            for (int k = 0; k < PPT; ++k) {
+                const int i = tid + SHP::NT * k;
+                const int r = i / SEG, sgm = i % SEG;
+                const u32x4 raw = *reinterpret_cast<const u32x4 *>(obuf + r * OP + 8 * sgm);
+                const float sc = exp2i(oexp[sgm >> 1]);        // the wave that wrote these 8 columns
+                f32x4 ov[2] = {f16x4_to_quad(u32x2{raw[0], raw[1]}), f16x4_to_quad(u32x2{raw[2], raw[3]})};
+                ov[0] *= sc;
+                ov[1] *= sc;
+                float ss = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ss += ov[0][j] * ov[0][j] + ov[1][j] * ov[1][j];
+#pragma unroll
+                for (int off = 1; off < SEG; off <<= 1) ss += __shfl_xor(ss, off, 64);
+                const float inv = fast_rsq(ss * (1.f / D) + eps);
+                f32x4 gv[2];
+                bf16_to_quads(gcur[k], gv[0], gv[1]);
+                f32x4 y[2];
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        y[hf][j] = ov[hf][j] * inv * nw[hf][j] * fast_rcp(1.f + __expf(-gv[hf][j]));
+                if (r < L)
+                    *reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(o) + ((size_t)(t0 + r) * H + h) * D +
+                                               8 * sgm) = quads_to_bf16(y[0], y[1]);
             }
         };
         auto copyA = [&](int c, unsigned char *dst) { copy_frags_to_lds(slab_of(c), dst, SL::FA, wave, WPG, lane); };
@@ -460,7 +528,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
                 return *reinterpret_cast<const u32x4 *>(abuf + off + ((size_t)idx * 64 + lane) * 16);
             };
             const int *uexp = reinterpret_cast<const int *>(bbuf + (SL::uexp - SL::kdT));
-            if constexpr (MODE == kModeOutput) {
+            if constexpr (GATE) {
+                if (o_L > 0) flush_gate(o_t0, o_L);            // the previous chunk's rows
+            } else if constexpr (OUT) {
                 if (o_L > 0) flush_o(par ^ 1, o_t0, o_L);   // the previous chunk's rows
                 if (i > 0) checkpoint(c - 1);
             }
@@ -474,6 +544,18 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
                 const u32x2 *us = reinterpret_cast<const u32x2 *>(slab_of(min(c + 1, c_end - 1)) + SL::u);
 #pragma unroll
                 for (int I = 0; I < 4; ++I) un[I] = load_untracked(us + (I * KT + vt) * 64 + lane);
+            }
+            if constexpr (GATE) {
+                // this chunk's g rows, flushed at the next step (rows past the
+                // chunk's end read its first row, and are not stored)
+                const int t0 = t_first + kChunk * i, L = min(kChunk, t_end - t0);
+#pragma unroll
+                for (int k = 0; k < PPT; ++k) {
+                    const int pi = tid + SHP::NT * k;
+                    const int r = pi / SEG, sgm = pi % SEG;
+                    gnext[k] = load_untracked4(reinterpret_cast<const u32x4 *>(
+                        gate + ((size_t)(t0 + (r < L ? r : 0)) * H + h) * D + 8 * sgm));
+                }
             }
             copyB(min(c + 1, c_end - 1), bring + (par ^ 1) * BB);
             const bool fetch_a = c + 2 < c_end;
@@ -510,7 +592,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             if constexpr (TR) uS2 = to_f16_scaled<KT>(S2, sf2);
 
             f32x4 vp[4], vp2[TR ? 4 : 1];
-            u32x4 kfr[2 * KT], afr[MODE == kModeOutput ? SL::NAQ : 1];
+            u32x4 kfr[2 * KT], afr[OUT ? SL::NAQ : 1];
             f32x4 gmr[KT];
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
@@ -524,7 +606,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
                     const f32x4 *gp = reinterpret_cast<const f32x4 *>(bbuf + (SL::gamma - SL::kdT));
 #pragma unroll
                     for (int t = 0; t < KT; ++t) gmr[t] = gp[4 * t + lg];
-                    if constexpr (MODE == kModeOutput) {
+                    if constexpr (OUT) {
 #pragma unroll
                         for (int f = 0; f < SL::NAQ; ++f) afr[f] = fragB(SL::aqk, f);
                     }
@@ -567,16 +649,38 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             if constexpr (TR) uV2 = to_f16_scaled<4>(vp2, vf2);
             const u32x4 vf0 = vf[0], vf1 = vf[1];
 
-            if constexpr (MODE == kModeOutput) {
-                uint16_t *ob = obuf + par * 64 * OP;
+            if constexpr (OUT) {
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
                     // (A_qk V')^T = V'^T A_qk^T, row-major like O above
                     f32x4 a = mma_f16_k32(vf0, afr[aqk_frag(I, 0)], zero4());
                     if (I >= 2) a = mma_f16_k32(vf1, afr[aqk_frag(I, 1)], a);
                     acc_o[I] += a * uV;
-                    *reinterpret_cast<u32x2 *>(ob + (16 * I + ln) * OP + 16 * wave + 4 * lg) =
-                        u32x2{f32x2_to_bf16x2(acc_o[I][0], acc_o[I][1]), f32x2_to_bf16x2(acc_o[I][2], acc_o[I][3])};
+                }
+                if constexpr (GATE) {
+                    // o stays fp32 up to the gate: staged as fp16 with a
+                    // power-of-two exponent per wave, the single staging tile
+                    // is rewritten only once every wave has flushed it
+                    float m = 0.f;
+#pragma unroll
+                    for (int I = 0; I < 4; ++I)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(acc_o[I][j]));
+                    const int e = scale_exp(wave_max_nonneg(m));
+                    const float d = exp2i(-e);
+                    barrier_lds();
+#pragma unroll
+                    for (int I = 0; I < 4; ++I)
+                        *reinterpret_cast<u32x2 *>(obuf + (16 * I + ln) * OP + 16 * wave + 4 * lg) =
+                            quad_to_f16(acc_o[I] * d);
+                    if (lane == 0) oexp[wave] = e;
+                } else {
+                    uint16_t *ob = obuf + par * 64 * OP;
+#pragma unroll
+                    for (int I = 0; I < 4; ++I)
+                        *reinterpret_cast<u32x2 *>(ob + (16 * I + ln) * OP + 16 * wave + 4 * lg) =
+                            u32x2{f32x2_to_bf16x2(acc_o[I][0], acc_o[I][1]),
+                                  f32x2_to_bf16x2(acc_o[I][2], acc_o[I][3])};
                 }
             }
 #pragma unroll
@@ -603,11 +707,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int I = 0; I < 4; ++I) settle(un[I]);   // issued before every copy: landed
+            if constexpr (GATE) {
+#pragma unroll
+                for (int k = 0; k < PPT; ++k) settle(gnext[k]);
+            }
             barrier_lds();
 #pragma unroll
             for (int I = 0; I < 4; ++I) u[I] = un[I];
+            if constexpr (GATE) {
+#pragma unroll
+                for (int k = 0; k < PPT; ++k) gcur[k] = gnext[k];
+            }
         }
-        if constexpr (MODE == kModeOutput) {
+        if constexpr (GATE) {
+            if (o_L > 0) flush_gate(o_t0, o_L);
+        } else if constexpr (OUT) {
             if (o_L > 0) flush_o((c_end - c_begin - 1) & 1, o_t0, o_L);
             if (c_begin < c_end) checkpoint(c_end - 1);
         }
@@ -624,7 +738,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int c = c_begin; c < c_end; ++c) {
             copy_B(c, buf);
             if (c + 1 < c_end) load_u(c + 1, un);
-            if constexpr (MODE == kModeOutput) {
+            if constexpr (OUT) {
                 if (o_L > 0) store_o_tile<F32IO>(o, acc_o, o_t0, o_L, H, h, D, col, lg);
                 if (c > c_begin) checkpoint(c - 1);
             }
@@ -649,7 +763,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             wait_all_memory();
             __syncthreads();
             if (c + 1 < c_end) copy_A(c + 1, buf);
-            if constexpr (MODE == kModeOutput) {
+            if constexpr (OUT) {
 #pragma unroll
                 for (int I = 0; I < 4; ++I)
 #pragma unroll
@@ -678,8 +792,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
             for (int I = 0; I < 4; ++I) u[I] = un[I];
         }
     }
-    if constexpr (MODE == kModeOutput) {
-        if (o_L > 0) store_o_tile<F32IO>(o, acc_o, o_t0, o_L, H, h, D, col, lg);
+    if constexpr (OUT) {
+        if (F32IO && o_L > 0) store_o_tile<F32IO>(o, acc_o, o_t0, o_L, H, h, D, col, lg);
         if (F32IO && c_begin < c_end) checkpoint(c_end - 1);
         if (hT && (rec.w & kSegLast)) {
             float *dst = hT + ((size_t)(n * H + h) * D + col) * D;
@@ -825,8 +939,13 @@ static int launch_prefill_t(const PrefillArgs &a) {
         if (launch_intra_f32<D>(a, meta, table, slabs) != 0) return -1;
     }
 
-    using SHP = InterShape<D, F32IO>;
-    const int groups = SHP::KT / SHP::WPG;
+    if constexpr (!F32IO) {
+        // the fused call's new conv window: after the intra kernel has read
+        // the old one (the two may be the same buffer)
+        if (a.fused && launch_conv_window(false, a.fused->xq, a.fused->xk, a.fused->xv, a.cu, a.N, a.T, a.H, D,
+                                          a.fused->win_in, a.fused->win_out, a.stream) != 0)
+            return -1;
+    }
     if (a.N == 0) return 0;
     const int nseg = a.N * p.P;
     const int unit_blocks = (nseg * a.H + 7) / 8 * 8;
@@ -834,10 +953,15 @@ static int launch_prefill_t(const PrefillArgs &a) {
     float *s_in = reinterpret_cast<float *>(a.ws + p.off_sin);
     auto inter = [&](auto mode) -> bool {
         constexpr int M = decltype(mode)::value;
+        using SHP = InterShape<D, F32IO, M>;
+        constexpr int groups = SHP::GROUPS;
         if (!set_lds(&inter_kernel<D, F32IO, M>, SHP::lds_bytes)) return false;
+        const FusedIO *fx = M == kModeGate ? a.fused : nullptr;
         hipLaunchKernelGGL((inter_kernel<D, F32IO, M>), dim3(unit_blocks * groups), dim3(SHP::NT), SHP::lds_bytes,
                            a.stream, a.h0, s_in, segs, table, nseg, a.H, p.max_chunks, slabs, p.slab_bytes, a.o,
-                           a.hT, trans, groups, meta, ck_off, a.ck, ck_chunks);
+                           a.hT, trans, groups, meta, ck_off, a.ck, ck_chunks,
+                           fx ? static_cast<const uint16_t *>(fx->g) : nullptr, fx ? fx->w : nullptr,
+                           fx ? fx->eps : 0.f);
         return hipGetLastError() == hipSuccess;
     };
     if (p.P > 1) {
@@ -847,6 +971,9 @@ static int launch_prefill_t(const PrefillArgs &a) {
         hipLaunchKernelGGL((combine_kernel<D>), dim3(a.N * a.H * (D / 16)), dim3(D * 4), 0, a.stream, a.h0, segs,
                            a.N, a.H, p.P, trans, s_in);
         if (hipGetLastError() != hipSuccess) return -1;
+    }
+    if constexpr (!F32IO) {
+        if (a.fused) return inter(std::integral_constant<int, kModeGate>{}) ? 0 : -1;
     }
     if (!inter(std::integral_constant<int, kModeOutput>{})) return -1;
     return 0;

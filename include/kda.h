@@ -179,6 +179,36 @@ int kda_prefill_ex(kda_dtype io_dtype, const void *q, const void *k, const void 
                    size_t workspace_bytes, void *stream);
 
 /*
+ * The fused prefill: the feature path, the chunkwise prefill and the output
+ * gate in one call, with q, k, v and o never written to memory ("Kimi K3：架构、
+ * 训练与推理系统研究" §13.2: the production kernel fuses ShortConv, the input
+ * norms, the gate, the KDA recurrence and the output norm, so that the large
+ * state and its inputs make fewer HBM round trips; §3.2 and §3.3 define the
+ * pieces, as do kda_qkv_shortconv and kda_output_gate below).  It computes
+ *   q, k, v = kda_qkv_shortconv(xq, xk, xv, wq, wk, wv, conv_state_in)
+ *   o, hT   = kda_prefill(q, k, v, z, A, beta, h0, cu_seqlens)
+ *   y       = kda_output_gate(o, gate, norm_weight, eps)
+ * with q, k, v rounded to bf16 as kda_qkv_shortconv delivers them, and o kept
+ * in fp32 up to the gate (only y is rounded).  conv_state_out, when given,
+ * receives the window after the call and may be conv_state_in.
+ *
+ *   io_dtype         KDA_BF16 only (KDA_ERR_UNSUPPORTED_DTYPE otherwise)
+ *   xq, xk, xv ... conv_state_out   as for kda_qkv_shortconv
+ *   z .. dv          as for kda_prefill (dk == dv)
+ *   gate             [T][H][dv] bf16 gate projection g;  norm_weight [dv] fp32
+ *   y                [T][H][dv] bf16 output;  hT as for kda_prefill
+ *   workspace        kda_prefill_workspace_size(N, T, H, dk, dv, KDA_BF16) bytes
+ * Outputs may overlap no input (except the window in place) and no other
+ * output.  Errors and asynchrony as for kda_prefill.
+ */
+int kda_prefill_fused(kda_dtype io_dtype, const void *xq, const void *xk, const void *xv, const float *wq,
+                      const float *wk, const float *wv, const void *conv_state_in, void *conv_state_out,
+                      const float *z, const float *A, const float *beta, const float *h0,
+                      const int32_t *cu_seqlens, int N, int T, int H, int dk, int dv, const void *gate,
+                      const float *norm_weight, float eps, void *y, float *hT, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
  * kda_prefill for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Arguments, results and errors are kda_prefill's (automatic segments),

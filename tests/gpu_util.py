@@ -114,12 +114,14 @@ def _worst(vals):
     return max(vals) if vals else 0.0
 
 
-def compare_outputs(x, y, io: str, cu=None, what: str = "o", label: str = "") -> dict:
+def compare_outputs(x, y, io: str, cu=None, what: str = "o", label: str = "", elem: bool = True) -> dict:
     """Compare GPU rows x [T, H, d] (already in the io dtype, widened) with
     the oracle's y [T, H, d] (fp64) by every measure of the module docstring;
     `cu` splits the tokens into sequences (one sequence if None).  Every
     measure is computed and printed first; then AssertionError names the
-    first measure, sequence and head over its bar.  Returns the measures."""
+    first measure, sequence and head over its bar.  elem=False leaves the
+    element bound to the caller (an output derived from o by a row-wise
+    normalisation has its own, see test_gpu_fused).  Returns the measures."""
     x = np.asarray(x, np.float64)
     y = np.asarray(y, np.float64)
     assert x.shape == y.shape, (x.shape, y.shape)
@@ -169,7 +171,7 @@ def compare_outputs(x, y, io: str, cu=None, what: str = "o", label: str = "") ->
     c = BF16_ELEM_C if bf else F32_ELEM_C
     rel_el = excess / np.maximum(scale, 1e-300)
     m["elem_max"] = float(rel_el.max()) if excess.size else 0.0
-    over = rel_el > c
+    over = (rel_el > c) if elem else np.zeros(rel_el.shape, bool)
     print("%s %s: %s" % (label, what, ",".join("%s=%.2e" % kv for kv in m.items())), flush=True)
     if over.any():
         t, h, j = np.argwhere(over)[0]
@@ -179,6 +181,34 @@ def compare_outputs(x, y, io: str, cu=None, what: str = "o", label: str = "") ->
     if fails:
         raise AssertionError(fails[0])
     return m
+
+
+def check_gated_elements(x, y, o, g, w, eps: float, cu, label: str = "") -> float:
+    """Element bound of a gated output y = Sigmoid(g) w o / r (r: the RMS of
+    o's row, plus eps), from the oracle's o, g and w.  o's calibrated element
+    bound, |do| <= c max(|o|, U) with U the RMS of o over the (sequence,
+    head), is carried through the row normalisation:
+      |dy| <= half a bf16 ulp + c (|Sigmoid(g) w| max(|o|, U) + |y| U) / r,
+    the second term being the error of r itself.  A row whose RMS is far below
+    its head's magnifies o's absolute error in y; the bound says by how much.
+    Returns the worst error / allowed ratio; AssertionError above 1."""
+    x, y, o, g = (np.asarray(a, np.float64) for a in (x, y, o, g))
+    T, H = o.shape[0], o.shape[1]
+    U = np.zeros((T, H, 1))
+    for n in range(len(cu) - 1):
+        a, b = int(cu[n]), int(cu[n + 1])
+        if b > a:
+            U[a:b] = np.sqrt(np.mean(o[a:b] ** 2, axis=(0, 2), keepdims=True))   # [1, H, 1]
+    r = np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    sw = np.abs(1.0 / (1.0 + np.exp(-g)) * np.asarray(w, np.float64))
+    allowed = (bf16_half_ulp(np.maximum(np.abs(x), np.abs(y))) +
+               BF16_ELEM_C * (sw * np.maximum(np.abs(o), U) + np.abs(y) * U) / r)
+    ratio = np.abs(x - y) / allowed
+    t, h, j = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    print("%s gated element bound: worst error / allowed %.3f at [%d, %d, %d]" % (label, ratio.max(), t, h, j),
+          flush=True)
+    assert ratio.max() <= 1.0, ("gated element", (t, h, j), x[t, h, j], y[t, h, j], allowed[t, h, j])
+    return float(ratio.max())
 
 
 def compare_states(x, y, io: str, what: str = "hT", whole_bar=None, unit_bar=None, label: str = "") -> dict:

@@ -21,7 +21,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["kda_build_info", "kda_decode", "kda_decode_window", "kda_prefill",
                                            "kda_prefill_ex", "kda_prefill_ex_workspace_size",
-                                           "kda_prefill_noalloc",
+                                           "kda_prefill_noalloc", "kda_prefill_fused",
                                            "kda_qkv_shortconv", "kda_output_gate",
                                            "kda_prefill_segments", "kda_prefill_workspace_size",
                                            "kda_prefill_backward", "kda_prefill_backward_workspace_size",

@@ -1,0 +1,137 @@
+"""The fused prefill (feature path -> chunkwise prefill -> output gate in one
+call) against the composition of the three oracles, through the C ABI.
+
+The composition: q, k, v from the feature oracle in fp64, rounded once to
+bf16 (the dtype the feature entry point hands them over in, and the one the
+fused call rounds them to), then the KDA oracle, then the gate oracle on the
+unrounded o (the fused call keeps o in fp32 up to the gate; only y is
+rounded).  y is compared by every measure of gpu_util, hT as a state, and
+the new conv window bit for bit (it is a copy of inputs)."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_21_amd as kda
+import oracle
+from gated_delta_rule_21_amd import workloads as W
+from gpu_util import bf16_rne, check_gated_elements, compare_outputs, compare_states, host
+from oracle import features as F
+
+pytestmark = pytest.mark.gpu
+EPS = 1e-6
+
+
+def widen(t):
+    return None if t is None else t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def inputs(lens, H, d, seed, window=True, h0_std=0.05, device="cpu"):
+    f = W.random_features(lens, H, d, "bf16", window=window, seed=seed, device=device)
+    p = W.random_prefill(lens, H, d, "bf16", h0_std=h0_std, seed=seed + 1, device=device)
+    return dict(xq=f["xq"], xk=f["xk"], xv=f["xv"], wq=f["wq"], wk=f["wk"], wv=f["wv"], window=f["window"],
+                gate=f["g"], norm_w=f["w"], z=p["z"], A=p["A"], beta=p["beta"], h0=p["h0"],
+                cu_seqlens=p["cu_seqlens"])
+
+
+def oracle_fused(d, heads=None):
+    """(y, hT, window_out) of the composition, on a subset of heads if given."""
+    sel = lambda a: a if (heads is None or a is None) else a[:, heads]
+    cu = d["cu_seqlens"].cpu().numpy()
+    win = widen(d["window"])
+    if heads is not None and win is not None:
+        dd = d["xq"].shape[-1]
+        win = np.concatenate([win[..., i * dd:(i + 1) * dd][:, :, heads] for i in range(3)], axis=-1)
+    hsel = (lambda t: t) if heads is None else (lambda t: t[heads])
+    q, k, v, wout = F.qkv_features(sel(widen(d["xq"])), sel(widen(d["xk"])), sel(widen(d["xv"])),
+                                   hsel(widen(d["wq"])), hsel(widen(d["wk"])), hsel(widen(d["wv"])), cu, win)
+    as_bf16 = lambda a: W.as_numpy(torch.from_numpy(bf16_rne(a)).to(torch.bfloat16))
+    h0 = None if d["h0"] is None else W.as_numpy(sel(d["h0"]))
+    ro, rh = oracle.prefill(as_bf16(q), as_bf16(k), as_bf16(v), W.as_numpy(sel(d["z"])),
+                            W.as_numpy(hsel(d["A"])), W.as_numpy(sel(d["beta"])), h0, cu.astype(np.int32))
+    ry = F.output_gate(ro, sel(widen(d["gate"])), widen(d["norm_w"]), EPS)
+    return ry, rh, wout, ro, sel(widen(d["gate"]))
+
+
+def gpu_fused(g, in_place=False):
+    N = g["cu_seqlens"].numel() - 1
+    T, H, d = g["xq"].shape
+    win_in = g["window"]
+    if in_place and win_in is not None:
+        win_out = win_in
+    else:
+        win_out = torch.empty((N, 3, H, 3 * d), dtype=torch.bfloat16, device="cuda")
+    y, hT = kda.prefill_fused(g["xq"], g["xk"], g["xv"], g["wq"], g["wk"], g["wv"], g["z"], g["A"], g["beta"],
+                              g["cu_seqlens"], g["gate"], g["norm_w"], EPS, h0=g["h0"], conv_state_in=win_in,
+                              conv_state_out=win_out)
+    torch.cuda.synchronize()
+    return y, hT, win_out
+
+
+def check(d, label, heads=None, in_place=False):
+    print("case", label, flush=True)
+    g = {n: (t.cuda() if isinstance(t, torch.Tensor) else t) for n, t in d.items()}
+    y, hT, win = gpu_fused(g, in_place)
+    ry, rh, rwin, ro, rgate = oracle_fused(d, heads)
+    cu = d["cu_seqlens"].tolist()
+    if heads is not None:
+        y, hT = y[:, heads], hT[:, heads]
+        dd = d["xq"].shape[-1]
+        win = torch.cat([win[..., i * dd:(i + 1) * dd][:, :, heads] for i in range(3)], dim=-1)
+    compare_states(host(hT), rh, "bf16", label=label)
+    compare_outputs(host(y), ry, "bf16", cu, what="y", label=label, elem=False)
+    check_gated_elements(host(y), ry, ro, rgate, widen(d["norm_w"]), EPS, cu, label)
+    np.testing.assert_array_equal(widen(win), rwin)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_fused_ragged_with_window(d):
+    """Empty sequences, sequences shorter than the conv window (their taps
+    read the carried window), partial chunks and several chunks."""
+    check(inputs([0, 1, 2, 3, 5, 70, 200, 0, 130], 3, d, seed=900 + d), "fused ragged d=%d" % d)
+
+
+def test_fused_without_window_and_in_place():
+    check(inputs([9, 1, 40, 130], 4, 128, seed=910, window=False, h0_std=None), "fused no window, no h0")
+    check(inputs([9, 1, 0, 40, 300], 2, 64, seed=911), "fused window in place", in_place=True)
+
+
+def test_fused_segmented():
+    """One long sequence on few heads: the automatic rule splits it, so the
+    transition and combine passes run before the gated output pass."""
+    assert kda.kda_prefill_segments(1, 2000, 2, 128, 128, kda.KDA_BF16) > 1
+    check(inputs([2000], 2, 128, seed=920), "fused segmented")
+
+
+def test_fused_decay_extremes():
+    d = inputs([300, 129], 2, 128, seed=930)
+    d["z"][:] = 1e30                        # g = -5 on every token: the bound attained
+    check(d, "fused decay floor")
+    d = inputs([300, 129], 2, 128, seed=931)
+    d["z"][:] = -1e30                       # no decay: the delta rule
+    check(d, "fused deltanet")
+
+
+def test_fused_matches_separate_calls():
+    """The same recurrence as the three separate calls: hT and the window
+    agree, and y agrees with the separate path's y within the rounding of o
+    to bf16 that the separate path makes before its gate."""
+    d = inputs([70, 3, 500], 3, 128, seed=940)
+    g = {n: (t.cuda() if isinstance(t, torch.Tensor) else t) for n, t in d.items()}
+    y, hT, win = gpu_fused(g)
+    win2 = torch.empty_like(win)
+    q, k, v = kda.qkv_shortconv(g["xq"], g["xk"], g["xv"], g["wq"], g["wk"], g["wv"], g["cu_seqlens"],
+                                conv_state_in=g["window"], conv_state_out=win2)
+    o, hT2 = kda.prefill(q, k, v, g["z"], g["A"], g["beta"], g["cu_seqlens"], h0=g["h0"])
+    y2 = kda.output_gate(o, g["gate"], g["norm_w"], EPS)
+    torch.cuda.synchronize()
+    assert torch.equal(win, win2)
+    assert float((hT - hT2).norm() / hT2.norm()) < 2e-4
+    assert float((y.float() - y2.float()).norm() / y2.float().norm()) < 3e-3
+
+
+def test_fused_k3_shape_sampled():
+    """T = 65536, H = 96, d = 128 on the GPU; the oracle composition on four
+    heads."""
+    d = inputs([65536], 96, 128, seed=950, h0_std=None, device="cuda")
+    d = {n: (t.cpu() if isinstance(t, torch.Tensor) else t) for n, t in d.items()}
+    check(d, "fused k3", heads=[1, 33, 64, 95])

@@ -62,11 +62,18 @@ def named_vregs(line):
     return regs
 
 
-BF16_INTER = r"_ZN3kda12inter_kernelILi(32|64|128)ELb0ELi[01]E"
+BF16_INTER = r"_ZN3kda12inter_kernelILi(32|64|128)ELb0ELi[012]E"
+
+
+def untracked(lines):
+    """Line indices of the untracked loads: a global load inside an inline-asm block."""
+    return [i for i in range(1, len(lines) - 1)
+            if re.search(r"global_load_dwordx[24] ", lines[i]) and "ASMSTART" in lines[i - 1]]
 
 
 def test_bf16_inter_kernels_found(asm):
-    assert len(kernels(asm, BF16_INTER)) == 6
+    # output, transition and gated-output modes at d = 32, 64, 128
+    assert len(kernels(asm, BF16_INTER)) == 9
 
 
 def test_bf16_inter_kernels_use_no_scratch(asm):
@@ -79,10 +86,10 @@ def test_bf16_inter_kernels_use_no_scratch(asm):
 def test_untracked_loads_are_untouched_until_the_wait(asm):
     for name, body in kernels(asm, BF16_INTER).items():
         lines = body.splitlines()
-        # untracked loads: a global_load_dwordx2 inside an inline-asm block
-        loads = [i for i in range(1, len(lines) - 1)
-                 if "global_load_dwordx2" in lines[i] and "ASMSTART" in lines[i - 1]]
-        assert len(loads) == 4, (name, len(loads))
+        loads = untracked(lines)
+        # four U tiles per step; the gated mode also loads two pieces of g
+        gate = "ELi2EE" in name
+        assert len(loads) == (6 if gate else 4), (name, len(loads))
         # the settle statements: the first run of empty asm blocks after the loads
         settle = None
         for i in range(loads[-1], len(lines) - 1):
@@ -93,7 +100,7 @@ def test_untracked_loads_are_untouched_until_the_wait(asm):
         dest = set()
         for i in loads:
             dest |= vregs(lines[i].split()[1].rstrip(","))
-        assert len(dest) == 8, (name, dest)
+        assert len(dest) == (16 if gate else 8), (name, dest)
         for i in range(loads[0], settle):
             if i in loads:
                 continue

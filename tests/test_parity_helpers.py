@@ -5,7 +5,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import (BF16_COMPUTE_TOL, bf16_half_ulp, bf16_rne, compare_outputs, compare_states)
+from gpu_util import (BF16_COMPUTE_TOL, bf16_half_ulp, bf16_rne, check_gated_elements, compare_outputs,
+                      compare_states)
 
 
 def test_bf16_rne_matches_torch():
@@ -94,3 +95,19 @@ def test_states_per_unit_and_exact_zero():
     x3[1, 2, 0, 0] = 1e-30
     with pytest.raises(AssertionError, match="exactly zero"):
         compare_states(x3, y, "bf16")
+
+
+def test_gated_element_bound():
+    """The rounding of an exact gated output passes; an error of 5 % of an
+    element's scale (|Sigmoid(g) w| max(|o|, U) / r) fails."""
+    r = np.random.Generator(np.random.PCG64(4))
+    eps, cu = 1e-6, [0, 10, 40]
+    o, g, w = r.standard_normal((40, 2, 32)), 2 * r.standard_normal((40, 2, 32)), 1 + 0.1 * r.standard_normal(32)
+    rr = np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    y = w / (1 + np.exp(-g)) * o / rr
+    assert check_gated_elements(bf16_rne(y), y, o, g, w, eps, cu) < 0.5
+    U = np.sqrt(np.mean(o[10:] ** 2, axis=(0, 2)))[1]
+    x = bf16_rne(y)
+    x[20, 1, 3] = y[20, 1, 3] + 0.05 * abs(w[3] / (1 + np.exp(-g[20, 1, 3]))) * max(abs(o[20, 1, 3]), U) / rr[20, 1, 0]
+    with pytest.raises(AssertionError, match="gated element"):
+        check_gated_elements(x, y, o, g, w, eps, cu)
