@@ -36,7 +36,7 @@
 //   2  Gamma*Q, K~^T (transposed by an identity MFMA), Gram tiles -> A_kk, A_qk
 //   3  (Gamma*K)^T and V^T fragments into LDS; inverses of the four
 //      diagonal 16x16 blocks (forward substitution)
-//   4  off-diagonal blocks of T, one block row per step (fp32 MFMA)
+//   4  off-diagonal blocks of T, one block column per wave (fp32 MFMA)
 //   4b M = T Diag(beta), split into bf16 fragments
 //   5  -W and U, stored in the slab
 // ---------------------------------------------------------------------------
@@ -502,20 +502,29 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         if (it_next < total)
             load_rows4_z<D>(R, q, k, v, z, beta, null_row, ent_next, it_next % H, H,
                             16 * ((wave + rot0 + iter + 1) & 3) + ln, lg);
-        // ---- phase 4: T_IJ = -T_II sum_{J<=m<I} A_Im T_mJ, stored at block (J, I)
-        for (int I = 1; I < 4; ++I) {
-            if (wave < I) {
-                const int J = wave;
-                f32x4 x = zero4();
-                for (int m = J; m < I; ++m)
-                    x = mma_f32_k16(lds_quad(a, 16 * I + ln, 16 * m + 4 * lg), lds_col4(a, 16 * J + 4 * lg, 16 * m + ln),
-                                    x);
-                const f32x4 y = mma_f32_k16(lds_quad(a, 16 * I + ln, 16 * I + 4 * lg), x, zero4());
+        // ---- phase 4: T_IJ = -T_II sum_{J<=m<I} A_Im T_mJ, stored at block (J, I).
+        // Block column J needs only A, the diagonal inverses and its own
+        // earlier blocks, so wave J computes the whole column in order with
+        // no barrier in between, keeping each block in registers (an
+        // accumulator is the B operand of the next product).
+        if (wave < 3) {
+            const int J = wave;
+            f32x4 tc[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) a[16 * J + 4 * lg + j][16 * I + ln] = -y[j];
+            for (int I = 1; I < 4; ++I) {
+                if (I > J) {
+                    f32x4 x = mma_f32_k16(lds_quad(a, 16 * I + ln, 16 * J + 4 * lg),
+                                          lds_col4(a, 16 * J + 4 * lg, 16 * J + ln), zero4());
+#pragma unroll
+                    for (int m = 1; m < I; ++m)
+                        if (m > J) x = mma_f32_k16(lds_quad(a, 16 * I + ln, 16 * m + 4 * lg), tc[m], x);
+                    tc[I] = -mma_f32_k16(lds_quad(a, 16 * I + ln, 16 * I + 4 * lg), x, zero4());
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) a[16 * J + 4 * lg + j][16 * I + ln] = tc[I][j];
+                }
             }
-            __syncthreads();
         }
+        __syncthreads();
 
         // ---- phase 4b: M = T Diag(beta) for the rows of block b, split
 #pragma unroll

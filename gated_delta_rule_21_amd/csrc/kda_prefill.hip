@@ -531,7 +531,6 @@ __global__ void __launch_bounds__((InterShape<D, F32IO, MODE>::NT))
             if constexpr (GATE) {
                 if (o_L > 0) flush_gate(o_t0, o_L);            // the previous chunk's rows
             } else if constexpr (OUT) {
-                if (o_L > 0) flush_o(par ^ 1, o_t0, o_L);   // the previous chunk's rows
                 if (i > 0) checkpoint(c - 1);
             }
             // The next chunk's U and region B, and the region-A copies of chunk
@@ -648,6 +647,13 @@ __global__ void __launch_bounds__((InterShape<D, F32IO, MODE>::NT))
             float uV2 = 0.f;
             if constexpr (TR) uV2 = to_f16_scaled<4>(vp2, vf2);
             const u32x4 vf0 = vf[0], vf1 = vf[1];
+            // the previous chunk's rows, stored once this step's chain products
+            // are issued.  The stores follow this step's A copies in issue
+            // order, so the counted wait at the end of the step also waits for
+            // the oldest A copies (harmless) and still covers U and region B.
+            if constexpr (OUT && !GATE) {
+                if (o_L > 0) flush_o(par ^ 1, o_t0, o_L);
+            }
 
             if constexpr (OUT) {
 #pragma unroll
