@@ -100,7 +100,7 @@ def parse():
     p.add_argument("--decode-steps", type=int, default=1000)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-features", action="store_true",
-                   help="skip the side measurement of the feature path and output gate")
+                   help="skip the side measurements of the feature path, the output gate and the fused calls")
     p.add_argument("--no-backward", action="store_true",
                    help="skip the side measurement of the prefill backward")
     p.add_argument("--no-checkpoints", action="store_true",
@@ -387,6 +387,53 @@ def feature_path_cost(kda, W, dev, pre, reps: int = 10) -> dict:
                       "saved_ms": round(ms_sep - ms_fused, 4)}}
 
 
+def decode_fused_cost(kda, W, dev, reps: int = 100) -> dict:
+    """Side measurement at the batched decode shape (256 sequences x 96 heads
+    x 128, bf16, a carried window): one step as the three separate calls
+    (feature path of the token, kda_decode, output gate) against
+    kda_decode_fused, each repeated in place (state and window updated)."""
+    import torch
+    N, H, D = 256, 96, 128
+    f = W.random_features([1] * N, H, D, "bf16", window=True, device=dev)
+    dec = W.random_decode(N, H, D, "bf16", 0.05, device=dev)
+    S = dec["S"]
+    win = f["window"]
+    cu = torch.arange(N + 1, dtype=torch.int32, device=dev)
+    q, k, v = (torch.empty_like(f["xq"]) for _ in range(3))
+    o = torch.empty_like(f["xq"])
+    y = torch.empty_like(f["xq"])
+
+    def separate():
+        kda.qkv_shortconv(f["xq"], f["xk"], f["xv"], f["wq"], f["wk"], f["wv"], cu, conv_state_in=win,
+                          conv_state_out=win, q=q, k=k, v=v)
+        kda.decode(q, k, v, dec["z"], dec["A"], dec["beta"], S, o=o)
+        kda.output_gate(o, f["g"], f["w"], 1e-6, y=y)
+
+    def fused():
+        kda.decode_fused(f["xq"], f["xk"], f["xv"], f["wq"], f["wk"], f["wv"], dec["z"], dec["A"], dec["beta"], S,
+                         f["g"], f["w"], 1e-6, conv_state_in=win, conv_state_out=win, y=y)
+
+    def timed(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_sep = timed(separate)
+    ms_fused = timed(fused)
+    state_bytes = 2 * N * H * D * D * 4
+    return {"workload": "k3_decode 256x96 d=128 bf16, window carried, state updated in place",
+            "separate_calls": {"ms": round(ms_sep, 4), "what": "kda_qkv_shortconv + kda_decode + kda_output_gate"},
+            "fused": {"ms": round(ms_fused, 4), "what": "kda_decode_fused",
+                      "state_GBps": round(state_bytes / (ms_fused * 1e-3) / 1e9, 1),
+                      "saved_ms": round(ms_sep - ms_fused, 4)}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -502,6 +549,7 @@ def main():
     }
     if not args.no_features:
         line["feature_path"] = feature_path_cost(kda, W, dev, pre)
+        line["decode_fused"] = decode_fused_cost(kda, W, dev)
     if not args.no_backward:
         line["prefill_backward"] = prefill_backward_cost(kda, W, pre)
     if not args.no_checkpoints:

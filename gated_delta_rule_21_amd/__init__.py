@@ -13,6 +13,7 @@ Entry points (same names as the C ABI in include/kda.h):
                                     library's fixed device scratch; no allocation)
   kda_prefill_fused(...)            raw C call: feature path -> prefill -> output gate
   kda_decode(...)                   raw C call
+  kda_decode_fused(...)             raw C call: feature path -> decode step -> output gate
   kda_decode_window(...)            raw C call: replay + multi-token window
   kda_qkv_shortconv(...)            raw C call: ShortConv -> Swish -> L2Norm feature path
   kda_output_gate(...)              raw C call: Sigmoid(g) * RMSNorm(o)
@@ -96,6 +97,9 @@ def lib():
     L.kda_prefill_fused.restype = ci
     L.kda_decode.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, vp, vp]
     L.kda_decode.restype = ci
+    L.kda_decode_fused.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                   ctypes.c_float, ci, ci, ci, ci, vp, vp]
+    L.kda_decode_fused.restype = ci
     L.kda_qkv_shortconv.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, vp, vp, vp, vp,
                                     vp, vp]
     L.kda_qkv_shortconv.restype = ci
@@ -157,6 +161,12 @@ def kda_prefill_fused(io_dtype, xq, xk, xv, wq, wk, wv, conv_state_in, conv_stat
 
 def kda_decode(io_dtype, q, k, v, z, A, beta, S_inout, N, H, dk, dv, o, stream) -> int:
     return lib().kda_decode(io_dtype, q, k, v, z, A, beta, S_inout, N, H, dk, dv, o, stream)
+
+
+def kda_decode_fused(io_dtype, xq, xk, xv, wq, wk, wv, conv_state_in, conv_state_out, z, A, beta, S_inout,
+                     gate, norm_weight, eps, N, H, dk, dv, y, stream) -> int:
+    return lib().kda_decode_fused(io_dtype, xq, xk, xv, wq, wk, wv, conv_state_in, conv_state_out, z, A, beta,
+                                  S_inout, gate, norm_weight, float(eps), N, H, dk, dv, y, stream)
 
 
 def kda_qkv_shortconv(io_dtype, xq, xk, xv, wq, wk, wv, cu_seqlens, N, T, H, dk, dv, conv_state_in,
@@ -499,6 +509,41 @@ def prefill_fused(xq, xk, xv, wq, wk, wv, z, A, beta, cu_seqlens, gate, norm_wei
     if st != 0:
         raise KdaError("kda_prefill_fused", st)
     return y, hT
+
+
+def decode_fused(xq, xk, xv, wq, wk, wv, z, A, beta, S, gate, norm_weight, eps: float, conv_state_in=None,
+                 conv_state_out=None, y=None):
+    """One fused decode step (bf16): y = Sigmoid(gate) * RMSNorm(o) with
+    o = decode(q, k, v, z, A, beta, S) and q, k, v the feature path of the new
+    token over the carried window.  S is updated in place; conv_state_out
+    (may be conv_state_in) receives the window after the token.  Returns y."""
+    torch = _torch()
+    _check("xq", xq, (None, None, None), torch.bfloat16)
+    N, H, d = xq.shape
+    dev = xq.device
+    _check("xk", xk, (N, H, d), torch.bfloat16, dev)
+    _check("xv", xv, (N, H, d), torch.bfloat16, dev)
+    for name, t in (("wq", wq), ("wk", wk), ("wv", wv)):
+        _check(name, t, (H, d, 4), torch.float32, dev)
+    _check("z", z, (N, H, d), torch.float32, dev)
+    _check("A", A, (H,), torch.float32, dev)
+    _check("beta", beta, (N, H), torch.float32, dev)
+    _check("S", S, (N, H, d, d), torch.float32, dev)
+    _check("conv_state_in", conv_state_in, (N, 3, H, 3 * d), torch.bfloat16, dev)
+    _check("conv_state_out", conv_state_out, (N, 3, H, 3 * d), torch.bfloat16, dev)
+    _check("gate", gate, (N, H, d), torch.bfloat16, dev)
+    _check("norm_weight", norm_weight, (d,), torch.float32, dev)
+    _check("y", y, (N, H, d), torch.bfloat16, dev)
+    _on_gpu(dev, xq=xq, xk=xk, xv=xv, wq=wq, wk=wk, wv=wv, z=z, A=A, beta=beta, S=S, conv_state_in=conv_state_in,
+            conv_state_out=conv_state_out, gate=gate, norm_weight=norm_weight, y=y)
+    if y is None:
+        y = torch.empty((N, H, d), dtype=torch.bfloat16, device=dev)
+    st = kda_decode_fused(KDA_BF16, _ptr(xq), _ptr(xk), _ptr(xv), _ptr(wq), _ptr(wk), _ptr(wv),
+                          _ptr(conv_state_in), _ptr(conv_state_out), _ptr(z), _ptr(A), _ptr(beta), _ptr(S),
+                          _ptr(gate), _ptr(norm_weight), eps, N, H, d, d, _ptr(y), _stream(dev))
+    if st != 0:
+        raise KdaError("kda_decode_fused", st)
+    return y
 
 
 def qkv_shortconv(xq, xk, xv, wq, wk, wv, cu_seqlens, conv_state_in=None, conv_state_out=None,

@@ -348,6 +348,52 @@ int kda_decode(kda_dtype io_dtype, const void *q, const void *k, const void *v, 
     return kda::launch_decode(a) == 0 ? KDA_OK : KDA_ERR_HIP;
 }
 
+int kda_decode_fused(kda_dtype io_dtype, const void *xq, const void *xk, const void *xv, const float *wq,
+                     const float *wk, const float *wv, const void *conv_state_in, void *conv_state_out,
+                     const float *z, const float *A, const float *beta, float *S_inout, const void *gate,
+                     const float *norm_weight, float eps, int N, int H, int dk, int dv, void *y, void *stream) {
+    if (io_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED_DTYPE;
+    if (N < 0 || H <= 0 || !(eps >= 0.f)) return KDA_ERR_INVALID_ARGUMENT;
+    if (!supported_dim(dk, dv)) return KDA_ERR_UNSUPPORTED_DIM;
+    if (!A || !wq || !wk || !wv || !norm_weight) return KDA_ERR_NULL_POINTER;
+    if (N > 0 && (!xq || !xk || !xv || !z || !beta || !S_inout || !gate || !y)) return KDA_ERR_NULL_POINTER;
+    const void *ptrs[] = {xq, xk, xv, wq, wk, wv, conv_state_in, conv_state_out, z, A, beta, S_inout, gate,
+                          norm_weight, y};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    const size_t nh = (size_t)N * H, d = (size_t)dk;
+    const size_t st_bytes = nh * d * d * 4, y_bytes = nh * d * 2, win_bytes = nh * 3 * 3 * d * 2;
+    const struct { const void *p; size_t n; } ins[] = {
+        {xq, nh * d * 2}, {xk, nh * d * 2}, {xv, nh * d * 2}, {wq, (size_t)H * d * 16}, {wk, (size_t)H * d * 16},
+        {wv, (size_t)H * d * 16}, {z, nh * d * 4}, {A, (size_t)H * 4}, {beta, nh * 4}, {gate, y_bytes},
+        {norm_weight, d * 4}};
+    for (const auto &in : ins)
+        if (overlaps(y, y_bytes, in.p, in.n) || overlaps(S_inout, st_bytes, in.p, in.n) ||
+            (conv_state_out && overlaps(conv_state_out, win_bytes, in.p, in.n)))
+            return KDA_ERR_ALIAS;
+    if (overlaps(y, y_bytes, S_inout, st_bytes)) return KDA_ERR_ALIAS;
+    if (conv_state_out && (overlaps(conv_state_out, win_bytes, y, y_bytes) ||
+                           overlaps(conv_state_out, win_bytes, S_inout, st_bytes)))
+        return KDA_ERR_ALIAS;
+    if (conv_state_in && (overlaps(conv_state_in, win_bytes, y, y_bytes) ||
+                          overlaps(conv_state_in, win_bytes, S_inout, st_bytes)))
+        return KDA_ERR_ALIAS;
+    // the window is read and written by the same thread: in place, or disjoint
+    if (conv_state_in && conv_state_out && conv_state_in != conv_state_out &&
+        overlaps(conv_state_in, win_bytes, conv_state_out, win_bytes))
+        return KDA_ERR_ALIAS;
+
+    kda::DecodeFusedArgs a;
+    a.xq = xq; a.xk = xk; a.xv = xv;
+    a.wq = wq; a.wk = wk; a.wv = wv;
+    a.win_in = conv_state_in; a.win_out = conv_state_out;
+    a.z = z; a.A = A; a.beta = beta; a.S = S_inout;
+    a.gate = gate; a.norm_w = norm_weight; a.eps = eps; a.y = y;
+    a.N = N; a.H = H; a.d = dk;
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+    return kda::launch_decode_fused(a) == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
 int kda_qkv_shortconv(kda_dtype io_dtype, const void *xq, const void *xk, const void *xv, const float *wq,
                       const float *wk, const float *wv, const int32_t *cu_seqlens, int N, int T, int H, int dk,
                       int dv, const void *conv_state_in, void *conv_state_out, void *q, void *k, void *v,

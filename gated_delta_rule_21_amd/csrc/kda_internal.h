@@ -18,6 +18,25 @@ struct DecodeArgs {
     hipStream_t stream;
 };
 
+// The fused decode step (bf16, dk = dv = d): features of the new token from
+// xq, xk, xv and the carried window, the update of S, y = Sigmoid(g) *
+// RMSNorm(o).
+struct DecodeFusedArgs {
+    const void *xq, *xk, *xv;
+    const float *wq, *wk, *wv;
+    const void *win_in;
+    void *win_out;
+    const float *z, *A, *beta;
+    float *S;
+    const void *gate;
+    const float *norm_w;
+    float eps;
+    void *y;
+    int N, H, d;
+    hipStream_t stream;
+};
+int launch_decode_fused(const DecodeFusedArgs &a);
+
 // Multi-token decode with replay: the replay window (inputs cached from the
 // previous call, n_accept[n] of its Lr tokens committed now) and the new
 // window of L tokens.  Inputs [N][len][H][d].

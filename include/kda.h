@@ -245,6 +245,41 @@ int kda_decode(kda_dtype io_dtype, const void *q, const void *k, const void *v,
                int H, int dk, int dv, void *o, void *stream);
 
 /*
+ * The fused decode step: the feature path of the new token, one decode step
+ * and the output gate in one pass over the state ("Kimi K3：架构、训练与推理
+ * 系统研究" §13.2: the production decode kernel runs ShortConv, the input
+ * norms, the gate, the KDA recurrence and the output norm in one recurrent
+ * loop; §3.2–3.4 define the pieces).  For N sequences with one token each it
+ * computes
+ *   q, k, v = kda_qkv_shortconv(xq, xk, xv, wq, wk, wv, conv_state_in)   (T = N)
+ *   o       = kda_decode(q, k, v, z, A, beta, S_inout)
+ *   y       = kda_output_gate(o, gate, norm_weight, eps)
+ * with q, k, v and o kept in fp32 (kda_qkv_shortconv and kda_decode hand them
+ * over in bf16; here only y is rounded).
+ *
+ *   io_dtype         KDA_BF16 only (KDA_ERR_UNSUPPORTED_DTYPE otherwise)
+ *   xq, xk, xv       [N][H][d] bf16 pre-convolution projections of the token
+ *   wq, wk, wv       [H][d][4] fp32 ShortConv taps (tap 3 on the new token)
+ *   conv_state_in    [N][3][H][3 d] bf16 carried window (q | k | v channels,
+ *                    oldest token first), or NULL for zeros
+ *   conv_state_out   the window after this token, or NULL; may be
+ *                    conv_state_in (updated in place), else must not overlap it
+ *   z, A, beta       as for kda_decode;  S_inout [N][H][d][d] fp32, in place
+ *   gate             [N][H][d] bf16 gate projection g;  norm_weight [d] fp32
+ *   eps              RMSNorm epsilon, >= 0
+ *   dk == dv == d    32, 64 or 128
+ *   y                [N][H][d] bf16 output
+ * Outputs (y, S_inout, conv_state_out) may overlap no input and no other
+ * output, except the window in place (KDA_ERR_ALIAS).  Pointers 16-byte
+ * aligned.  Asynchronous on `stream`; N = 0 launches nothing.
+ */
+int kda_decode_fused(kda_dtype io_dtype, const void *xq, const void *xk, const void *xv,
+                     const float *wq, const float *wk, const float *wv, const void *conv_state_in,
+                     void *conv_state_out, const float *z, const float *A, const float *beta,
+                     float *S_inout, const void *gate, const float *norm_weight, float eps, int N,
+                     int H, int dk, int dv, void *y, void *stream);
+
+/*
  * Multi-token decode with replay (speculative decoding).  A state updated in
  * place cannot be rolled back when draft tokens are rejected; instead the
  * caller keeps the committed state and the small per-token inputs of the

@@ -19,7 +19,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["kda_build_info", "kda_decode", "kda_decode_window", "kda_prefill",
+    assert declared_functions() == sorted(["kda_build_info", "kda_decode", "kda_decode_fused", "kda_decode_window",
+                                           "kda_prefill",
                                            "kda_prefill_ex", "kda_prefill_ex_workspace_size",
                                            "kda_prefill_noalloc", "kda_prefill_fused",
                                            "kda_qkv_shortconv", "kda_output_gate",
@@ -115,6 +116,34 @@ def test_decode_rejects_bad_arguments():
     assert d(q=None) == -2
     assert d(S=FAKE + 8) == -5
     assert d(o=FAKE + 4096) == -8                 # o on top of k
+
+
+def test_decode_fused_rejects_bad_arguments():
+    """bf16 only, dk == dv in {32, 64, 128}, eps >= 0, the pointers a step
+    needs, 16-byte alignment, and outputs (y, S, the new window) that overlap
+    an input or each other; the window in place is allowed."""
+    base = dict(io=0, xq=FAKE, xk=FAKE + 4096, xv=FAKE + 8192, wq=FAKE + 12288, wk=FAKE + 16384,
+                wv=FAKE + 20480, win_in=None, win_out=None, z=FAKE + 24576, A=FAKE + 32768, beta=FAKE + 36864,
+                S=FAKE + 40960, gate=FAKE + 57344, w=FAKE + 61440, eps=1e-6, N=2, H=2, dk=32, dv=32,
+                y=FAKE + 65536)
+
+    def d(**o):
+        a = dict(base)
+        a.update(o)
+        return kda.kda_decode_fused(a["io"], a["xq"], a["xk"], a["xv"], a["wq"], a["wk"], a["wv"], a["win_in"],
+                                    a["win_out"], a["z"], a["A"], a["beta"], a["S"], a["gate"], a["w"], a["eps"],
+                                    a["N"], a["H"], a["dk"], a["dv"], a["y"], None)
+    assert d(io=1) == -4                          # fp32 io
+    assert d(N=-1) == -1 and d(H=0) == -1 and d(eps=-1.0) == -1
+    assert d(dk=64) == -3 and d(dk=48, dv=48) == -3
+    assert d(xq=None) == -2 and d(S=None) == -2 and d(gate=None) == -2 and d(w=None) == -2
+    assert d(A=None) == -2 and d(wv=None) == -2
+    assert d(xk=FAKE + 4098) == -5 and d(y=FAKE + 65538) == -5
+    assert d(y=FAKE + 4096) == -8                 # y on top of xk
+    assert d(S=FAKE + 24576) == -8                # the state on top of z
+    assert d(y=FAKE + 40960) == -8                # y on top of the state
+    assert d(win_in=1 << 22, win_out=(1 << 22) + 512) == -8   # two windows that overlap
+    assert d(win_out=FAKE + 57344) == -8          # the new window on top of the gate
 
 
 def test_segment_option():
@@ -391,3 +420,23 @@ def test_feature_wrappers_reject():
         kda.output_gate(x(), x(), torch.ones(d + 1), 1e-6)
     with pytest.raises(ValueError, match="GPU"):
         kda.output_gate(x(), x(), torch.ones(d), 1e-6)
+
+
+def test_decode_fused_wrapper_rejects():
+    N, H, d = 3, 2, 32
+    bf = lambda *s: torch.zeros(*s, dtype=torch.bfloat16)
+    t = dict(xq=bf(N, H, d), xk=bf(N, H, d), xv=bf(N, H, d), wq=torch.zeros(H, d, 4), wk=torch.zeros(H, d, 4),
+             wv=torch.zeros(H, d, 4), z=torch.zeros(N, H, d), A=torch.zeros(H), beta=torch.zeros(N, H),
+             S=torch.zeros(N, H, d, d), gate=bf(N, H, d), norm_weight=torch.ones(d), eps=1e-6)
+    bad = [("xv", bf(N, H, d + 1), ValueError), ("wk", torch.zeros(H, d, 4).bfloat16(), TypeError),
+           ("z", torch.zeros(N, H, d).bfloat16(), TypeError), ("S", torch.zeros(N, H, d, d - 1), ValueError),
+           ("gate", torch.zeros(N, H, d), TypeError), ("norm_weight", torch.ones(d + 1), ValueError)]
+    for name, val, err in bad:
+        with pytest.raises(err, match=name):
+            kda.decode_fused(**dict(t, **{name: val}))
+    with pytest.raises(ValueError, match="conv_state_in"):
+        kda.decode_fused(**t, conv_state_in=bf(N, 3, H, d))
+    with pytest.raises(TypeError, match="y"):
+        kda.decode_fused(**t, y=torch.zeros(N, H, d))
+    with pytest.raises(ValueError, match="GPU"):
+        kda.decode_fused(**t)
