@@ -1,0 +1,106 @@
+"""The entry points under HIP graph capture.
+
+A serving-shaped sequence is captured once with torch.cuda.graph: a
+segmented prefill of a ragged batch into caller-owned o, hT and workspace;
+two decode steps on the prefill's final state, in place; one fused decode
+step on that state with its conv window carried in place; and the prefill
+without a workspace argument (its fixed device scratch).  The graph is
+replayed several times, with other eager calls of the same entry points,
+buffer scribbles and synchronisations between the replays.  Every replay
+must equal the eager run of the same calls bit for bit: the kernels are
+deterministic, and the library makes no allocation, host synchronisation or
+memset on the capturing stream, and reads only what it is given."""
+import pytest
+import torch
+
+import gated_delta_rule_21_amd as kda
+from gated_delta_rule_21_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+EPS = 1e-6
+LENS = [300, 1, 129, 0, 64]
+H, D = 4, 128
+
+
+def to(d, dev):
+    return {n: (t.to(dev) if isinstance(t, torch.Tensor) else t) for n, t in d.items()}
+
+
+def make_state(seed=8100, dev="cuda"):
+    dev = torch.device(dev)
+    p = to(W.random_prefill(LENS, H, D, "bf16", h0_std=0.05, seed=seed), dev)
+    N = len(LENS)
+    T = sum(LENS)
+    dec = [to(W.random_decode(N, H, D, "bf16", 0.05, seed=seed + 10 + i), dev) for i in range(2)]
+    f = to(W.random_features([1] * N, H, D, "bf16", window=True, seed=seed + 20), dev)
+    fz = to(W.random_decode(N, H, D, "bf16", 0.05, seed=seed + 21), dev)
+    bufs = dict(
+        o=torch.empty((T, H, D), dtype=torch.bfloat16, device=dev),
+        hT=torch.empty((N, H, D, D), dtype=torch.float32, device=dev),
+        ws=torch.empty(kda.kda_prefill_ex_workspace_size(N, T, H, D, D, kda.KDA_BF16, kda.options(3)),
+                       dtype=torch.uint8, device=dev),
+        od=[torch.empty((N, H, D), dtype=torch.bfloat16, device=dev) for _ in range(2)],
+        y=torch.empty((N, H, D), dtype=torch.bfloat16, device=dev),
+        win=torch.empty_like(f["window"]),
+        o2=torch.empty((T, H, D), dtype=torch.bfloat16, device=dev),
+        hT2=torch.empty((N, H, D, D), dtype=torch.float32, device=dev),
+    )
+    return p, dec, f, fz, bufs
+
+
+def sequence(p, dec, f, fz, b):
+    """The calls the graph holds, on the current stream."""
+    b["win"].copy_(f["window"])
+    kda.prefill(p["q"], p["k"], p["v"], p["z"], p["A"], p["beta"], p["cu_seqlens"], h0=p["h0"], o=b["o"],
+                hT=b["hT"], workspace=b["ws"], segments=3)
+    for i in range(2):
+        kda.decode(dec[i]["q"], dec[i]["k"], dec[i]["v"], dec[i]["z"], p["A"], dec[i]["beta"], b["hT"],
+                   o=b["od"][i])
+    kda.decode_fused(f["xq"], f["xk"], f["xv"], f["wq"], f["wk"], f["wv"], fz["z"], p["A"], fz["beta"], b["hT"],
+                     f["g"], f["w"], EPS, conv_state_in=b["win"], conv_state_out=b["win"], y=b["y"])
+    N = len(LENS)
+    st = kda.kda_prefill_noalloc(kda.KDA_BF16, p["q"].data_ptr(), p["k"].data_ptr(), p["v"].data_ptr(),
+                                 p["z"].data_ptr(), p["A"].data_ptr(), p["beta"].data_ptr(), p["h0"].data_ptr(),
+                                 p["cu_seqlens"].data_ptr(), N, sum(LENS), H, D, D, b["o2"].data_ptr(),
+                                 b["hT2"].data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert st == 0, kda.kda_status_string(st)
+
+
+def snapshot(b):
+    return [t.clone() for t in (b["o"], b["hT"], b["od"][0], b["od"][1], b["y"], b["win"], b["o2"], b["hT2"])]
+
+
+def scribble(b):
+    for t in (b["o"], b["hT"], b["od"][0], b["od"][1], b["y"], b["win"], b["o2"], b["hT2"]):
+        t.fill_(-7.0)
+
+
+def test_capture_and_replay():
+    print("case graph capture: prefill (3 segments), 2 decode steps, fused decode, noalloc prefill", flush=True)
+    p, dec, f, fz, b = make_state()
+    sequence(p, dec, f, fz, b)            # eager, also the warm-up before capture
+    torch.cuda.synchronize()
+    want = snapshot(b)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            sequence(p, dec, f, fz, b)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    # a second batch through the same entry points (the noalloc scratch
+    # included), run eagerly between replays on other buffers
+    p2, dec2, f2, fz2, b2 = make_state(seed=8200)
+    for rep in range(4):
+        scribble(b)
+        torch.cuda.synchronize()
+        g.replay()
+        if rep % 2 == 0:
+            sequence(p2, dec2, f2, fz2, b2)   # eager work between replays
+        torch.cuda.synchronize()
+        got = snapshot(b)
+        names = ("o", "hT", "od0", "od1", "y", "window", "o noalloc", "hT noalloc")
+        for n, x, y in zip(names, got, want):
+            assert torch.equal(x, y), "replay %d: %s differs from the eager run" % (rep, n)
+    g.reset()
