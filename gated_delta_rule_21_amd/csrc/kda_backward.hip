@@ -1424,10 +1424,16 @@ bool plan_backward(int N, int T, int H, int d, bool f32io, int P, BackwardPlan *
     if (item == 0) return false;
     p->ck_cap = T / kChunk;
     p->off_fwd = 0;
+    // The forward's slabs and its o are dead once the forward has run (the
+    // backward kernels read its chunk table and the stored states only), so
+    // the per-(chunk, head) records start where the slabs do and run over o.
+    // The states and the dA parts are live with the records and come after.
     p->off_o = align256b(p->fwd.total);
-    p->off_ck = p->off_o + align256b((size_t)T * H * d * (f32io ? 4 : 2));
-    p->off_items = p->off_ck + align256b((size_t)p->ck_cap * H * d * d * 4);
-    p->off_dA = p->off_items + (size_t)H * p->fwd.max_chunks * item;
+    const size_t o_end = p->off_o + align256b((size_t)T * H * d * (f32io ? 4 : 2));
+    p->off_items = align256b(p->fwd.off_slabs);
+    const size_t items_end = p->off_items + (size_t)H * p->fwd.max_chunks * item;
+    p->off_ck = align256b(std::max(o_end, items_end));
+    p->off_dA = p->off_ck + align256b((size_t)p->ck_cap * H * d * d * 4);
     p->total = p->off_dA + align256b((size_t)p->fwd.max_chunks * H * 4);
     return true;
 }
