@@ -26,18 +26,20 @@
 // inclusive) and ke = k exp2(bt - Gl) (bt: the block's total log-decay); fac
 // is exp2(-bt_b) on the diagonal tile and the decay of the blocks strictly
 // between b and I otherwise.  Only kr and qr of blocks 1..3 go through LDS.
-// Diagonal tiles, where fac reaches e^80, and the W / U products are
-// split-bf16 (hi + lo, three MFMAs, good to about 2^-16); off-diagonal Gram
-// tiles have every factor <= 1 and use fp16 operands (one MFMA).
+// Diagonal tiles, where fac reaches e^80, and the U product are split-bf16
+// (hi + lo, good to about 2^-16); off-diagonal Gram tiles have every factor
+// <= 1 and use fp16 operands (one MFMA), and so does W = M (Gamma*K), whose
+// result is stored in fp16 anyway: rounding M and Gamma*K (<= 1) to fp16
+// first leaves the chain's error where the final rounding puts it.
 //
 // Phases (barriers between them):
 //   1  gate, block-local cumulative log-decay (DPP row scan), kr / qr / ke
 //   F  per-channel decay factors of the chunk
 //   2  Gamma*Q, K~^T (transposed by an identity MFMA), Gram tiles -> A_kk, A_qk
-//   3  (Gamma*K)^T and V^T fragments into LDS; inverses of the four
+//   3  Gamma*K (fp16) and V tiles into LDS; inverses of the four
 //      diagonal 16x16 blocks (forward substitution)
 //   4  off-diagonal blocks of T, one block column per wave (fp32 MFMA)
-//   4b M = T Diag(beta), split into bf16 fragments
+//   4b M = T Diag(beta): split bf16 fragments (for U) and fp16 ones (for W)
 //   5  -W and U, stored in the slab
 // ---------------------------------------------------------------------------
 #include "kda_chunk.h"
@@ -94,11 +96,15 @@ struct Intra4Lds {
     static constexpr size_t FR = 1024;
     // X, phases 1-2: fp16 row fragments of kr and qr of row blocks 1..3,
     //   [block - 1][kr, qr][pair p], read by the off-diagonal Gram tiles.
-    // X, phases 3-5: Gamma*K (bf16 hi, then lo) and V as row-major 16x16
-    //   tiles [channel tile t][row block], read back transposed (tile_tr).
+    // X, phases 3-5: Gamma*K (fp16) and V as row-major 16x16 tiles
+    //   [channel tile t][row block], read back transposed (tile_tr); from
+    //   phase 4b, the fp16 M fragments [aqk_frag(I, pj)] at M16.
     static constexpr size_t X = 0;
     static constexpr size_t XB = 12 * NP * FR;
-    static constexpr size_t GKT = X, GKL = X + KT * 2048, VT = X + 4 * KT * FR;
+    static constexpr size_t GKT = X, VT = X + 4 * KT * FR;
+    // the six fp16 M fragments: between Gamma*K and V where they fit (d >= 64),
+    // else after everything else
+    static constexpr bool M16_IN_X = GKT + KT * 2048 + 6 * FR <= VT;
     // A_kk, then T: the diagonal blocks in place, T_IJ (I > J) at block (J, I).
     static constexpr int AP = 68;
     static constexpr size_t A = X + XB;
@@ -109,7 +115,8 @@ struct Intra4Lds {
     static constexpr size_t F = A + 64 * AP * 4;
     static constexpr size_t FB = 12 * FR;
     static constexpr size_t BETA = F + FB;
-    static constexpr size_t bytes = BETA + 64 * 4;
+    static constexpr size_t M16 = M16_IN_X ? GKT + KT * 2048 : BETA + 64 * 4;
+    static constexpr size_t bytes = M16_IN_X ? BETA + 64 * 4 : M16 + 6 * FR;
     static_assert((4 + 18) * D * 4 <= (int)FB, "bt and the factors fit the M region");
 };
 
@@ -455,21 +462,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
         __syncthreads();
 
-        // ---- phase 3: Gamma*K (split) and V into X as row-major tiles
+        // ---- phase 3: Gamma*K (fp16) and V into X as row-major tiles
         if constexpr (!FEAT) load_rows4_v<D>(R, q, k, v, z, null_row, ent, h, H, row, lg);
         {
             const float *pfx = fac_lds + (4 + b) * D;
 #pragma unroll
             for (int t = 0; t < KT; ++t) {
-                // Gamma*K = hi + lo, both bf16, packed
-                const f32x4 gk = kr[t] * ld4(pfx + 16 * t + 4 * lg);
-                const u32x2 hi = u32x2{f32x2_to_bf16x2(gk[0], gk[1]), f32x2_to_bf16x2(gk[2], gk[3])};
-                const f32x4 lf = gk - f32x4{bf16_lo_half(hi[0]), bf16_hi_half(hi[0]), bf16_lo_half(hi[1]),
-                                            bf16_hi_half(hi[1])};
-                const u32x2 lo = u32x2{f32x2_to_bf16x2(lf[0], lf[1]), f32x2_to_bf16x2(lf[2], lf[3])};
+                const f32x4 gk = kr[t] * ld4(pfx + 16 * t + 4 * lg);   // Gamma*K <= 1
                 const size_t tb = (size_t)(t * 4 + b) * 512 + ln * 32 + lg * 8;   // row ln, channels 4lg..
-                *reinterpret_cast<u32x2 *>(X + LY::GKT + tb) = hi;
-                *reinterpret_cast<u32x2 *>(X + LY::GKL + tb) = lo;
+                *reinterpret_cast<u32x2 *>(X + LY::GKT + tb) = quad_to_f16(gk);
             }
         }
         if (lane < 16) {
@@ -526,7 +527,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
         __syncthreads();
 
-        // ---- phase 4b: M = T Diag(beta) for the rows of block b, split
+        // ---- phase 4b: M = T Diag(beta) for the rows of block b, split, and in fp16
 #pragma unroll
         for (int pj = 0; pj < 2; ++pj) {
             if (2 * pj <= b) {
@@ -543,6 +544,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
                 unsigned char *d = msp + (size_t)aqk_frag(b, pj) * 2 * FR + lane * 16;
                 *reinterpret_cast<u32x4 *>(d) = hi;
                 *reinterpret_cast<u32x4 *>(d + FR) = lo;
+                *reinterpret_cast<u32x4 *>(X + LY::M16 + (size_t)aqk_frag(b, pj) * FR + lane * 16) =
+                    quads_to_f16(x[0], x[1]);
             }
         }
         __syncthreads();
@@ -552,13 +555,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
             const int p = unit % NP, I = unit / NP;
             f32x4 acc0 = zero4(), acc1 = zero4();
             for (int pj = 0; pj <= (I >> 1); ++pj) {
-                const unsigned char *mb = msp + (size_t)aqk_frag(I, pj) * 2 * FR + lane * 16;
-                const u32x4 mh = *reinterpret_cast<const u32x4 *>(mb);
-                const u32x4 ml = *reinterpret_cast<const u32x4 *>(mb + FR);
-                acc0 = mma3_bf16(tile_tr_k32(X + LY::GKT, 2 * p, pj, lane), tile_tr_k32(X + LY::GKL, 2 * p, pj, lane),
-                                 mh, ml, acc0);
-                acc1 = mma3_bf16(tile_tr_k32(X + LY::GKT, 2 * p + 1, pj, lane),
-                                 tile_tr_k32(X + LY::GKL, 2 * p + 1, pj, lane), mh, ml, acc1);
+                const u32x4 m16 =
+                    *reinterpret_cast<const u32x4 *>(X + LY::M16 + (size_t)aqk_frag(I, pj) * FR + lane * 16);
+                acc0 = mma_f16_k32(tile_tr_k32(X + LY::GKT, 2 * p, pj, lane), m16, acc0);
+                acc1 = mma_f16_k32(tile_tr_k32(X + LY::GKT, 2 * p + 1, pj, lane), m16, acc1);
             }
             store_f16(slab + SL::negW + ((size_t)(I * NP + p) * 64 + lane) * 16, -acc0, -acc1);
         });
