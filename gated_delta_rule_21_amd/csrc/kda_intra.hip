@@ -395,6 +395,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         __syncthreads();
 
         // ---- phase 2: Gamma*Q, K~^T, Gram tiles (I, b) for I >= b
+        // Wave b owns 4 - b Gram tiles, so the waves reach the barrier after
+        // this phase at different times while the other workgroup on the CU
+        // competes for issue.  A wave priority that follows the tile count
+        // (kept through the diagonal solve behind the barrier) lets the
+        // longest chain issue first.
+        if (b == 0) __builtin_amdgcn_s_setprio(3);
+        else if (b == 1) __builtin_amdgcn_s_setprio(2);
+        else if (b == 2) __builtin_amdgcn_s_setprio(1);
         {
             const float *pfx = fac_lds + (4 + b) * D;
             const float *sfx = fac_lds + (8 + b) * D;
@@ -489,6 +497,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int r = 0; r < 16; ++r) a[o + r][o + lane] = x[r];
         }
+        __builtin_amdgcn_s_setprio(0);
         // V last: its loads, issued at the top of the phase, complete behind
         // the Gamma*K split and the diagonal solve instead of stalling them
         if constexpr (FEAT)
