@@ -560,6 +560,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         __syncthreads();
 
         // ---- phase 5: -W (from W^T tiles) and U
+        // Raised priority: this phase's MFMA chains and slab stores end the
+        // item, and issuing them ahead of the other workgroup's work hands
+        // the item over sooner.
+        __builtin_amdgcn_s_setprio(1);
         for_wave_units<4 * NP, 4>(wave, [&](int unit) {
             const int p = unit % NP, I = unit / NP;
             f32x4 acc0 = zero4(), acc1 = zero4();
@@ -604,6 +608,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
                 if (lane == 0) reinterpret_cast<int *>(slab + SL::uexp)[I * KT + w] = e;
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         ent = ent_next;
         ent_next = ent_after;
         a_cur = a_next;
