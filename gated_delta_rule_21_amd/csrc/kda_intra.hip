@@ -336,7 +336,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
             feature_row<D, true>(R.q, static_cast<const uint16_t *>(fx.xq), fx.wq,
                                  static_cast<const uint16_t *>(fx.win_in), 0, ent, h, H, b, ln, lg);
         } else {
+            // the item's row loads issue ahead of the other workgroup's work,
+            // so their latency starts early (likewise the next item's gate
+            // inputs in phase 4)
+            __builtin_amdgcn_s_setprio(3);
             load_rows4_kq<D>(R, q, k, v, z, null_row, ent, h, H, row, lg);
+            __builtin_amdgcn_s_setprio(0);
         }
         if (lg == 0) sbeta[row] = R.beta;
         f32x4 kr[KT], qr[KT], ke[KT];
@@ -509,9 +514,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         __syncthreads();
 
         // the gate inputs of the next item
+        __builtin_amdgcn_s_setprio(3);
         if (it_next < total)
             load_rows4_z<D>(R, q, k, v, z, beta, null_row, ent_next, it_next % H, H,
                             16 * ((wave + rot0 + iter + 1) & 3) + ln, lg);
+        __builtin_amdgcn_s_setprio(0);
         // ---- phase 4: T_IJ = -T_II sum_{J<=m<I} A_Im T_mJ, stored at block (J, I).
         // Block column J needs only A, the diagonal inverses and its own
         // earlier blocks, so wave J computes the whole column in order with
