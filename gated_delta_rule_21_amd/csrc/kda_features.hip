@@ -75,6 +75,8 @@ __global__ void __launch_bounds__(256) shortconv_kernel(
     // base is passed wave-uniform, so lanes that skip the copy shift nothing)
     const unsigned char *xb = static_cast<const unsigned char *>(x);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    // the copies issue ahead of the other workgroups' arithmetic on the CU
+    __builtin_amdgcn_s_setprio(3);
 #pragma unroll
     for (int i0 = 0; i0 < ROWS * PPR; i0 += 256) {
         const int i = i0 + threadIdx.x;
@@ -90,6 +92,7 @@ __global__ void __launch_bounds__(256) shortconv_kernel(
                 *reinterpret_cast<u32x4 *>(tile + (size_t)i * 16) = u32x4{0u, 0u, 0u, 0u};
         }
     }
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
