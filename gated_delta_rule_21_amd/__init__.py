@@ -55,12 +55,13 @@ _lib = None
 class PrefillOptions(ctypes.Structure):
     """struct kda_prefill_options (include/kda.h)."""
     _fields_ = [("segments", ctypes.c_int), ("checkpoint_interval", ctypes.c_int),
-                ("checkpoints", ctypes.c_void_p), ("checkpoint_offsets", ctypes.c_void_p)]
+                ("checkpoints", ctypes.c_void_p), ("checkpoint_offsets", ctypes.c_void_p),
+                ("blocks", ctypes.c_int)]
 
 
-def options(segments: int = 0, interval: int = 0, checkpoints=None, checkpoint_offsets=None):
+def options(segments: int = 0, interval: int = 0, checkpoints=None, checkpoint_offsets=None, blocks: int = 0):
     """A PrefillOptions by value; pointers as ints (or None)."""
-    return PrefillOptions(int(segments), int(interval), checkpoints, checkpoint_offsets)
+    return PrefillOptions(int(segments), int(interval), checkpoints, checkpoint_offsets, int(blocks))
 
 
 class KdaError(RuntimeError):
@@ -303,20 +304,23 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def prefill_workspace(N, T, H, d, io_dtype, device, segments: int = 0):
+def prefill_workspace(N, T, H, d, io_dtype, device, segments: int = 0, blocks: int = 0):
     """Allocate the prefill workspace (a byte tensor of the size the library asks)."""
     torch = _torch()
-    n = kda_prefill_ex_workspace_size(N, T, H, d, d, io_dtype, options(segments))
+    n = kda_prefill_ex_workspace_size(N, T, H, d, d, io_dtype, options(segments, blocks=blocks))
     if n == 0:
-        raise ValueError("unsupported prefill sizes N=%d T=%d H=%d d=%d segments=%d" % (N, T, H, d, segments))
+        raise ValueError("unsupported prefill sizes N=%d T=%d H=%d d=%d segments=%d blocks=%d"
+                         % (N, T, H, d, segments, blocks))
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def prefill(q, k, v, z, A, beta, cu_seqlens, h0=None, o=None, hT=None, workspace=None,
-            final_state: bool = True, segments: int = 0):
+            final_state: bool = True, segments: int = 0, blocks: int = 0):
     """KDA prefill over packed sequences.  Returns (o, hT); hT is None when
     final_state is False and no hT buffer is given.  segments: 0 = automatic,
-    1 = never split, 2..16 = split every long sequence into that many."""
+    1 = never split, 2..16 = split every long sequence into that many.
+    blocks: the chunk-block pipeline, 0 = automatic, 1 = off, 2..16 = that
+    many blocks (bf16 path without segments or checkpoints)."""
     torch = _torch()
     io, N, T, H, dk, dv = _check_prefill_inputs(q, k, v, z, A, beta, cu_seqlens, h0)
     dev = q.device
@@ -329,9 +333,9 @@ def prefill(q, k, v, z, A, beta, cu_seqlens, h0=None, o=None, hT=None, workspace
         o = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
     if hT is None and final_state:
         hT = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
-    opts = options(segments)
+    opts = options(segments, blocks=blocks)
     if workspace is None:
-        workspace = prefill_workspace(N, T, H, dk, io, dev, segments)
+        workspace = prefill_workspace(N, T, H, dk, io, dev, segments, blocks)
     _check_workspace(workspace, kda_prefill_ex_workspace_size(N, T, H, dk, dv, io, opts), dev)
     st = kda_prefill_ex(io, _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A), _ptr(beta), _ptr(h0),
                         _ptr(cu_seqlens), N, T, H, dk, dv, _ptr(o), _ptr(hT), opts, _ptr(workspace),

@@ -76,13 +76,34 @@ bool checkpoints_requested(const kda_prefill_options *opt) {
     return opt && (opt->checkpoints || opt->checkpoint_offsets);
 }
 
+// Chunk blocks of a call: the caller's, or the automatic choice (0); 1 where
+// the pipeline does not apply (fp32 path, segments, checkpoints).  -1 for an
+// out-of-range request or one that conflicts with forced segments.
+int blocks_of(const kda_prefill_options *opt, int N, int T, int H, int d, bool f32io, int P) {
+    const int b = opt ? opt->blocks : 0;
+    if (b < 0 || b > KDA_MAX_PREFILL_BLOCKS) return -1;
+    if (b > 1 && opt->segments > 1) return -1;
+    if (f32io || P > 1 || checkpoints_requested(opt)) return 1;
+    return b > 0 ? b : kda::choose_blocks(N, T, H, d);
+}
+
+// Segment count of a call once forced blocks are taken into account: on the
+// bf16 path without checkpoints, blocks >= 2 with automatic segments mean one
+// segment.
+int segments_with_blocks(const kda_prefill_options *opt, int N, int T, int H, int d, bool f32io) {
+    if (opt && opt->blocks > 1 && opt->segments == 0 && !f32io && !checkpoints_requested(opt)) return 1;
+    return segments_of(opt, N, T, H, d);
+}
+
 size_t prefill_ws(int N, int T, int H, int dk, int dv, kda_dtype io_dtype, const kda_prefill_options *opt) {
     if (io_dtype != KDA_BF16 && io_dtype != KDA_F32) return 0;
     if (!supported_dim(dk, dv) || N < 0 || T < 0 || H <= 0) return 0;
-    const int P = segments_of(opt, N, T, H, dk);
+    const int P = segments_with_blocks(opt, N, T, H, dk, io_dtype == KDA_F32);
     if (P < 1) return 0;
+    const int B = blocks_of(opt, N, T, H, dk, io_dtype == KDA_F32, P);
+    if (B < 1) return 0;
     kda::PrefillPlan p;
-    if (!kda::plan_prefill(N, T, H, dk, dv, io_dtype == KDA_F32, P, &p)) return 0;
+    if (!kda::plan_prefill(N, T, H, dk, dv, io_dtype == KDA_F32, P, B, &p)) return 0;
     return p.total;
 }
 
@@ -121,9 +142,12 @@ int prefill_impl(kda_dtype io_dtype, const void *q, const void *k, const void *v
     int32_t *ck_offsets = opt ? opt->checkpoint_offsets : nullptr;
     const int interval = (ck || ck_offsets) ? opt->checkpoint_interval : 0;
     if ((ck || ck_offsets) && (interval <= 0 || interval % 64 != 0)) return KDA_ERR_INVALID_ARGUMENT;
-    const int P = segments_of(opt, N, T, H, dk);
+    const int P = segments_with_blocks(opt, N, T, H, dk, io_dtype == KDA_F32);
     if (P < 1) return KDA_ERR_INVALID_ARGUMENT;
     if (N < 0 || T < 0 || H <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    // the fused call is never pipelined (its epilogue runs in the inter kernel's gate mode)
+    const int B = fx ? 1 : blocks_of(opt, N, T, H, dk, io_dtype == KDA_F32, P);
+    if (B < 1) return KDA_ERR_INVALID_ARGUMENT;
     if (!supported_dim(dk, dv)) return KDA_ERR_UNSUPPORTED_DIM;
     if (!A || !cu_seqlens || !workspace) return KDA_ERR_NULL_POINTER;
     if (T > 0 && (!z || !beta || !o)) return KDA_ERR_NULL_POINTER;
@@ -134,7 +158,7 @@ int prefill_impl(kda_dtype io_dtype, const void *q, const void *k, const void *v
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_MISALIGNED;
 
     kda::PrefillPlan plan;
-    if (!kda::plan_prefill(N, T, H, dk, dv, io_dtype == KDA_F32, P, &plan)) return KDA_ERR_INVALID_ARGUMENT;
+    if (!kda::plan_prefill(N, T, H, dk, dv, io_dtype == KDA_F32, P, B, &plan)) return KDA_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < plan.total) return KDA_ERR_WORKSPACE_TOO_SMALL;
 
     const size_t tok = (size_t)T * H;

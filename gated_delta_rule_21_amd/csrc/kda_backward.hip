@@ -1419,7 +1419,7 @@ size_t backward_item_bytes(int d) {
 static size_t align256b(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool plan_backward(int N, int T, int H, int d, bool f32io, int P, BackwardPlan *p) {
-    if (!plan_prefill(N, T, H, d, d, f32io, P, &p->fwd)) return false;
+    if (!plan_prefill(N, T, H, d, d, f32io, P, 1, &p->fwd)) return false;
     const size_t item = backward_item_bytes(d);
     if (item == 0) return false;
     p->ck_cap = T / kChunk;

@@ -99,6 +99,9 @@ struct PrefillPlan {
     size_t off_trans;        // P > 1: fp32 [N * P][H][2][dk * dk]: M row-major, then S~ in state layout
     size_t off_sin;          // P > 1: fp32 [N * P][H][dv][dk] incoming state of every segment
     size_t off_slabs;        // slabs, head-major: [H][max_chunks]
+    int blocks;              // block pipeline: chunk blocks (1: off)
+    size_t off_claims;       // blocks > 1: int32 [blocks] item counters
+    size_t off_carry;        // blocks > 1: fp32 [N][H][dv][dk] state between blocks
     size_t total;
 };
 
@@ -160,7 +163,10 @@ struct BackwardArgs {
     hipStream_t stream;
 };
 
-bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, int P, PrefillPlan *plan);
+bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, int P, int blocks, PrefillPlan *plan);
+// Chunk blocks of the pipelined prefill for these sizes when the caller asks
+// for the automatic choice (1: not pipelined).
+int choose_blocks(int N, int T, int H, int d);
 bool plan_backward(int N, int T, int H, int d, bool f32io, int P, BackwardPlan *plan);
 // Segment count the prefill uses for these sizes when the caller asks for
 // the automatic choice.
@@ -180,7 +186,7 @@ int launch_prefill_backward(const BackwardArgs &a);
 // path), D = 32, 64, 128.
 template <int D>
 int launch_intra_bf16(const PrefillArgs &a, const int32_t *meta, const int4 *table, const float *null_row,
-                      unsigned char *slabs);
+                      unsigned char *slabs, int item_lo = 0, int item_hi = 0, int *claims = nullptr);
 template <int D>
 int launch_intra_f32(const PrefillArgs &a, const int32_t *meta, const int4 *table, unsigned char *slabs);
 

@@ -115,8 +115,9 @@ struct Intra4Lds {
     static constexpr size_t F = A + 64 * AP * 4;
     static constexpr size_t FB = 12 * FR;
     static constexpr size_t BETA = F + FB;
-    static constexpr size_t M16 = M16_IN_X ? GKT + KT * 2048 : BETA + 64 * 4;
-    static constexpr size_t bytes = M16_IN_X ? BETA + 64 * 4 : M16 + 6 * FR;
+    static constexpr size_t CLAIM = BETA + 64 * 4;          // [4] int: claimed items
+    static constexpr size_t M16 = M16_IN_X ? GKT + KT * 2048 : CLAIM + 16;
+    static constexpr size_t bytes = M16_IN_X ? CLAIM + 16 : M16 + 6 * FR;
     static_assert((4 + 18) * D * 4 <= (int)FB, "bt and the factors fit the M region");
 };
 
@@ -281,7 +282,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ z, const float *__restrict__ A, const float *__restrict__ beta,
     const int32_t *__restrict__ meta, const int4 *__restrict__ table, const float *__restrict__ null_row, int N,
-    int H, int max_chunks, unsigned char *__restrict__ slabs, size_t slab_stride, FusedIO fx) {
+    int H, int max_chunks, unsigned char *__restrict__ slabs, size_t slab_stride, FusedIO fx, int item_lo,
+    int item_hi, int *__restrict__ claims) {
     using SL = Slab<D, false>;
     using LY = Intra4Lds<D>;
     constexpr int KT = D / 16, NP = D / 32;
@@ -297,17 +299,38 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index in an SGPR
-    const int total = meta[N] * H;
     const int stride = gridDim.x;
     // block rotation: differs between neighbouring workgroups and advances per item
     const int rot0 = blockIdx.x + 2 * (2 * (int)blockIdx.x >= (int)gridDim.x);
 
-    int it = blockIdx.x;
-    if (it >= total) return;
+    // Items [lo, hi): the whole table, each workgroup taking every stride-th
+    // item; or, with `claims`, one block of a pipelined prefill whose items
+    // the workgroups claim from a counter, so that workgroups that start late
+    // (their CUs busy with the previous block's chain) take fewer.  A
+    // workgroup keeps two claims ahead of its current item; tid 0 claims and
+    // publishes through LDS, read by every wave after a barrier.
+    const int total = meta[N] * H;
+    const int lo = claims ? item_lo : 0;
+    const int hi = claims ? min(item_hi, total) : total;
+    int *claim_lds = reinterpret_cast<int *>(lds_raw + LY::CLAIM);
+    int it, it_nx;
+    if (claims) {
+        if (tid == 0) {
+            claim_lds[1] = lo + atomicAdd(claims, 1);
+            claim_lds[2] = lo + atomicAdd(claims, 1);
+        }
+        __syncthreads();
+        it = __builtin_amdgcn_readfirstlane(claim_lds[1]);
+        it_nx = __builtin_amdgcn_readfirstlane(claim_lds[2]);
+    } else {
+        it = lo + (int)blockIdx.x;
+        it_nx = it + stride;
+    }
+    if (it >= hi) return;
     // Chunk-table entries and A_h are read through the scalar cache, whose
     // loads every barrier waits for: fetch them one item ahead of their use.
     int4 ent = table[it / H];
-    int4 ent_next = (it + stride < total) ? table[(it + stride) / H] : make_int4(0, 0, 0, 0);
+    int4 ent_next = it_nx < hi ? table[it_nx / H] : make_int4(0, 0, 0, 0);
     float a_cur = A[it % H];
     // Raw inputs of the current item; the next item's are fetched during the
     // solve (phase 4), when few registers are live.
@@ -316,7 +339,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
                     (threadIdx.x >> 4) & 3);
     __builtin_amdgcn_s_waitcnt(0);
 
-    for (int iter = 0; it < total; it += stride, ++iter) {
+    for (int iter = 0; it < hi; ++iter) {
         const int chunk = it / H, h = it % H;
         const int b = (wave + rot0 + iter) & 3;        // this wave's row block
         // lane coordinates, rebuilt per item (see opaque_zero)
@@ -325,9 +348,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int row = 16 * b + ln;
         unsigned char *slab = slabs + ((size_t)h * max_chunks + chunk) * slab_stride;
         const float nel = -__expf(a_cur) * kLog2e;       // the gate's exp2 argument per unit z
-        const int it_next = it + stride;
-        const int4 ent_after = (it_next + stride < total) ? table[(it_next + stride) / H] : make_int4(0, 0, 0, 0);
-        const float a_next = it_next < total ? A[it_next % H] : 0.f;
+        const int it_next = it_nx;
+        int it_after = it_next + stride;
+        int4 ent_after = make_int4(0, 0, 0, 0);
+        if (claims) {
+            if (tid == 0) claim_lds[0] = lo + atomicAdd(claims, 1);   // read after the first barrier
+        } else if (it_after < hi) {
+            ent_after = table[it_after / H];
+        }
+        const float a_next = it_next < hi ? A[it_next % H] : 0.f;
 
         // ---- phase 1: gate, block-local cumulative log2-decay, row operands
         if constexpr (FEAT) {
@@ -372,6 +401,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         }
         __syncthreads();
+        if (claims) {
+            it_after = __builtin_amdgcn_readfirstlane(claim_lds[0]);
+            if (it_after < hi) ent_after = table[it_after / H];
+        }
 
         // ---- per-channel decay factors
         for (int c = tid; c < D; c += 256) {
@@ -515,7 +548,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 
         // the gate inputs of the next item
         __builtin_amdgcn_s_setprio(3);
-        if (it_next < total)
+        if (it_next < hi)
             load_rows4_z<D>(R, q, k, v, z, beta, null_row, ent_next, it_next % H, H,
                             16 * ((wave + rot0 + iter + 1) & 3) + ln, lg);
         __builtin_amdgcn_s_setprio(0);
@@ -616,6 +649,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         }
         __builtin_amdgcn_s_setprio(0);
+        it = it_next;
+        it_nx = it_after;
         ent = ent_next;
         ent_next = ent_after;
         a_cur = a_next;
@@ -625,16 +660,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 
 template <int D>
 int launch_intra_bf16(const PrefillArgs &a, const int32_t *meta, const int4 *table, const float *null_row,
-                      unsigned char *slabs) {
+                      unsigned char *slabs, int item_lo, int item_hi, int *claims) {
     using LY = Intra4Lds<D>;
-    const long long items = (long long)a.plan.max_chunks * a.H;
+    const long long items = claims ? (long long)item_hi - item_lo : (long long)a.plan.max_chunks * a.H;
     if (items <= 0) return 0;
     const int grid = (int)std::min<long long>(items, 2LL * device_cus());
     auto launch = [&](auto kernel, const FusedIO &fx) -> int {
         if (!set_lds(kernel, LY::bytes)) return -1;
         hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), LY::bytes, a.stream, reinterpret_cast<const uint16_t *>(a.q),
                            reinterpret_cast<const uint16_t *>(a.k), reinterpret_cast<const uint16_t *>(a.v), a.z, a.A,
-                           a.beta, meta, table, null_row, a.N, a.H, a.plan.max_chunks, slabs, a.plan.slab_bytes, fx);
+                           a.beta, meta, table, null_row, a.N, a.H, a.plan.max_chunks, slabs, a.plan.slab_bytes, fx,
+                           item_lo, item_hi, claims);
         return hipGetLastError() == hipSuccess ? 0 : -1;
     };
     if (a.fused) return launch(intra4_kernel<D, true>, *a.fused);
@@ -642,10 +678,10 @@ int launch_intra_bf16(const PrefillArgs &a, const int32_t *meta, const int4 *tab
 }
 
 template int launch_intra_bf16<32>(const PrefillArgs &, const int32_t *, const int4 *, const float *,
-                                     unsigned char *);
+                                     unsigned char *, int, int, int *);
 template int launch_intra_bf16<64>(const PrefillArgs &, const int32_t *, const int4 *, const float *,
-                                     unsigned char *);
+                                     unsigned char *, int, int, int *);
 template int launch_intra_bf16<128>(const PrefillArgs &, const int32_t *, const int4 *, const float *,
-                                     unsigned char *);
+                                     unsigned char *, int, int, int *);
 
 }  // namespace kda

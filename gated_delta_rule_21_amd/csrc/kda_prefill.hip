@@ -44,6 +44,7 @@
 #include "kda_internal.h"
 
 #include <algorithm>
+#include <climits>
 #include <type_traits>
 
 namespace kda {
@@ -60,7 +61,7 @@ size_t slab_bytes(int dk, int dv, bool f32io) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, int P, PrefillPlan *p) {
+bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, int P, int blocks, PrefillPlan *p) {
     size_t sb = slab_bytes(dk, dv, f32io);
     if (sb == 0 || N < 0 || T < 0 || H <= 0 || P < 1 || P > kMaxSegments) return false;
     p->max_chunks = (int)(((long long)T + kChunk - 1) / kChunk + N);
@@ -75,7 +76,10 @@ bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, int P, Prefil
     p->off_trans = p->off_segs + align256((size_t)N * P * 16);
     p->off_sin = p->off_trans + (P > 1 ? units * 2 * dd : 0);
     p->off_slabs = p->off_sin + (P > 1 ? units * dd : 0);
-    p->total = p->off_slabs + (size_t)H * p->max_chunks * sb;
+    p->blocks = P == 1 && !f32io && blocks > 1 ? blocks : 1;
+    p->off_claims = p->off_slabs + (size_t)H * p->max_chunks * sb;
+    p->off_carry = p->off_claims + (p->blocks > 1 ? align256((size_t)p->blocks * 4) : 0);
+    p->total = p->off_carry + (p->blocks > 1 ? (size_t)N * H * dv * dk * 4 : 0);
     return true;
 }
 
@@ -105,10 +109,13 @@ __global__ void __launch_bounds__(256) chunk_table_kernel(const int32_t *__restr
                                                           float *__restrict__ null_row, int d, int P,
                                                           int4 *__restrict__ segs, int ck_chunks, int ck_cap,
                                                           int32_t *__restrict__ ck_off,
-                                                          int32_t *__restrict__ ck_off_user) {
+                                                          int32_t *__restrict__ ck_off_user,
+                                                          int32_t *__restrict__ claims, int nclaims) {
     __shared__ int32_t scan[256];
     __shared__ int32_t carry;
     const int tid = threadIdx.x;
+    // the item counters of a pipelined prefill's blocks
+    if (tid < nclaims) claims[tid] = 0;
     // The null row that rows past a chunk's end read instead of real inputs:
     // z = -inf gives a zero gate (no decay), and k = q = v = 0, beta = 0.
     for (int c = tid; c < 2 * d + 1; c += 256)
@@ -335,7 +342,8 @@ __global__ void __launch_bounds__((InterShape<D, F32IO, MODE>::NT))
     const int4 *__restrict__ table, int nseg, int H, int max_chunks, const unsigned char *__restrict__ slabs,
     size_t slab_stride, void *__restrict__ o, float *__restrict__ hT, float *__restrict__ trans, int groups,
     const int32_t *__restrict__ meta, const int32_t *__restrict__ ck_off, float *__restrict__ ck, int ck_chunks,
-    const uint16_t *__restrict__ gate, const float *__restrict__ norm_w, float eps) {
+    const uint16_t *__restrict__ gate, const float *__restrict__ norm_w, float eps, int blk_lo, int blk_hi,
+    float *__restrict__ carry) {
     static_assert(MODE == kModeOutput || MODE == kModeTrans || MODE == kModeGate, "mode");
     constexpr bool TR = MODE == kModeTrans;
     constexpr bool OUT = !TR;                       // the mode writes outputs and the final state
@@ -364,6 +372,23 @@ __global__ void __launch_bounds__((InterShape<D, F32IO, MODE>::NT))
     const int vt = cg * WPG + wave;
     const int col = 16 * vt + ln;
 
+    // The chunks this launch walks: the segment's, or (block pipeline, bf16
+    // output mode) their part in [blk_lo, blk_hi) of the chunk table.  A
+    // sequence that began in an earlier block starts from `carry`, one that
+    // goes on into a later block leaves its state there.  An empty sequence
+    // belongs to the block holding its position.
+    int c_begin = rec.y, c_end = rec.z;
+    bool from_carry = false, to_carry = false;
+    if (OUT && !GATE && !F32IO && carry) {
+        const int lo_c = max(c_begin, blk_lo), hi_c = min(c_end, blk_hi);
+        const bool here = c_begin < c_end ? lo_c < hi_c : (c_begin >= blk_lo && c_begin < blk_hi);
+        if (!here) return;
+        from_carry = lo_c > c_begin;
+        to_carry = hi_c < c_end;
+        c_begin = lo_c;
+        c_end = hi_c;
+    }
+
     // initial state: h0 (or zero) for a sequence in one segment, otherwise
     // the incoming state the combine kernel wrote (for the first segment a
     // copy of h0, so that h0 is never read here when hT may overwrite it);
@@ -372,7 +397,8 @@ __global__ void __launch_bounds__((InterShape<D, F32IO, MODE>::NT))
     {
         const float *src = nullptr;
         if constexpr (!TR)
-            src = (rec.w & kSegFirst) && (rec.w & kSegLast)
+            src = from_carry ? carry + ((size_t)(n * H + h) * D + col) * D
+                  : (rec.w & kSegFirst) && (rec.w & kSegLast)
                       ? (h0 ? h0 + ((size_t)(n * H + h) * D + col) * D : nullptr)
                       : s_in + ((size_t)(sg * H + h) * D + col) * D;
 #pragma unroll
@@ -387,7 +413,6 @@ __global__ void __launch_bounds__((InterShape<D, F32IO, MODE>::NT))
         }
     }
 
-    const int c_begin = rec.y, c_end = rec.z;
     // state checkpoints (output mode): after every chunk that ends 64 ck_chunks
     // tokens into the sequence, up to the sequence's count
     int ck_c0 = 0, ck_first = 0, ck_count = 0;
@@ -801,8 +826,8 @@ __global__ void __launch_bounds__((InterShape<D, F32IO, MODE>::NT))
     if constexpr (OUT) {
         if (F32IO && o_L > 0) store_o_tile<F32IO>(o, acc_o, o_t0, o_L, H, h, D, col, lg);
         if (F32IO && c_begin < c_end) checkpoint(c_end - 1);
-        if (hT && (rec.w & kSegLast)) {
-            float *dst = hT + ((size_t)(n * H + h) * D + col) * D;
+        if (to_carry || (hT && (rec.w & kSegLast))) {
+            float *dst = (to_carry ? carry : hT) + ((size_t)(n * H + h) * D + col) * D;
 #pragma unroll
             for (int t = 0; t < KT; ++t) *reinterpret_cast<f32x4 *>(dst + 16 * t + 4 * lg) = S[t];
         }
@@ -911,6 +936,18 @@ __global__ void __launch_bounds__(D * 4) combine_kernel(const float *__restrict_
 // workgroups of one pass fill less than half the device, into as many
 // segments as fill it once, each of at least 4 chunks.  A function of the
 // sizes and the current device's compute-unit count only.
+// Pipelined prefill: worth it when the chain's workgroups (N H of them per
+// 64 value columns) leave at least 32 CUs to the intra kernel, and the
+// sequences are long enough that each of the three runs keeps the chain busy
+// for far longer than the per-run launch and delay costs (about 30 us).
+int choose_blocks(int N, int T, int H, int d) {
+    if (N <= 0 || T <= 0 || H <= 0) return 1;
+    const long long chain_wgs = (long long)N * H * (d == 128 ? 2 : 1);
+    if (chain_wgs > device_cus() - 32) return 1;
+    const long long chunks_per_seq = (long long)T / kChunk / N;
+    return chunks_per_seq >= 192 ? 3 : 1;
+}
+
 int choose_segments(int N, int T, int H, int d) {
     if (N <= 0 || T <= 0 || H <= 0) return 1;
     const long long blocks = (long long)N * H * (d == 128 ? 2 : 1);
@@ -922,6 +959,43 @@ int choose_segments(int N, int T, int H, int d) {
 }
 
 // ---------------------------------------------------------------------------
+// Block pipeline helpers.  Each host thread gets, per device, one helper
+// stream (default priority, created on its first pipelined call and kept
+// until the process ends) and the events that order it against the caller's
+// stream; a thread's calls run one after another on the host, so they can
+// reuse them.
+constexpr int kMaxBlocks = 16;
+constexpr int kPipeDelayTicks = 800;   // 8 us of the 100 MHz real-time clock
+
+struct PipeStreams {
+    hipStream_t s1 = nullptr;
+    hipEvent_t ev[kMaxBlocks + 1] = {};
+};
+
+static PipeStreams *pipe_streams() {
+    constexpr int kMaxDevices = 64;
+    thread_local PipeStreams *per_device[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    if (!per_device[dev]) {
+        PipeStreams *ps = new PipeStreams;
+        if (hipStreamCreateWithFlags(&ps->s1, hipStreamNonBlocking) != hipSuccess) return nullptr;
+        for (auto &e : ps->ev)
+            if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return nullptr;
+        per_device[dev] = ps;
+    }
+    return per_device[dev];
+}
+
+// A bounded pause on the caller's stream (one wave sleeping on the 100 MHz
+// real-time clock), between the intra kernel of block j and that of block
+// j + 1, so that block j's inter kernel, released by the same event, claims
+// its CUs first.
+__global__ void __launch_bounds__(64) pipeline_delay_kernel(int ticks) {
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    while (__builtin_amdgcn_s_memrealtime() - t0 < (unsigned long long)ticks) __builtin_amdgcn_s_sleep(8);
+}
+
 template <int D, bool F32IO>
 static int launch_prefill_t(const PrefillArgs &a) {
     const PrefillPlan &p = a.plan;
@@ -931,15 +1005,22 @@ static int launch_prefill_t(const PrefillArgs &a) {
 
     int4 *segs = reinterpret_cast<int4 *>(a.ws + p.off_segs);
     int32_t *ck_off = reinterpret_cast<int32_t *>(a.ws + p.off_ckoff);
+    // block pipeline: the intra kernel of chunk block j + 1 runs beside the
+    // inter kernel of block j (bf16 path without segments, checkpoints or
+    // the fused epilogue)
+    const bool pipe = !F32IO && p.blocks > 1 && p.P == 1 && !a.ck && !a.ck_offsets && !a.fused && a.N > 0;
+    int32_t *claims = reinterpret_cast<int32_t *>(a.ws + p.off_claims);
+    float *carry = reinterpret_cast<float *>(a.ws + p.off_carry);
     const int ck_chunks = (a.ck || a.ck_offsets) ? a.ck_interval / kChunk : 0;
     const int ck_cap = ck_chunks ? a.T / a.ck_interval : 0;
     hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, a.stream, a.cu, a.N, a.T,
                        p.max_chunks, meta, table, reinterpret_cast<float *>(a.ws + p.off_null), D, p.P, segs,
-                       ck_chunks, ck_cap, ck_off, a.ck_offsets);
+                       ck_chunks, ck_cap, ck_off, a.ck_offsets, pipe ? claims : nullptr, pipe ? p.blocks : 0);
     if (hipGetLastError() != hipSuccess) return -1;
 
     if constexpr (!F32IO) {
-        if (launch_intra_bf16<D>(a, meta, table, reinterpret_cast<const float *>(a.ws + p.off_null), slabs) != 0)
+        if (!pipe &&
+            launch_intra_bf16<D>(a, meta, table, reinterpret_cast<const float *>(a.ws + p.off_null), slabs) != 0)
             return -1;
     } else {
         if (launch_intra_f32<D>(a, meta, table, slabs) != 0) return -1;
@@ -957,19 +1038,56 @@ static int launch_prefill_t(const PrefillArgs &a) {
     const int unit_blocks = (nseg * a.H + 7) / 8 * 8;
     float *trans = reinterpret_cast<float *>(a.ws + p.off_trans);
     float *s_in = reinterpret_cast<float *>(a.ws + p.off_sin);
-    auto inter = [&](auto mode) -> bool {
+    auto inter = [&](auto mode, hipStream_t st = nullptr, int blk_lo = 0, int blk_hi = 0,
+                     float *blk_carry = nullptr) -> bool {
         constexpr int M = decltype(mode)::value;
         using SHP = InterShape<D, F32IO, M>;
         constexpr int groups = SHP::GROUPS;
         if (!set_lds(&inter_kernel<D, F32IO, M>, SHP::lds_bytes)) return false;
         const FusedIO *fx = M == kModeGate ? a.fused : nullptr;
         hipLaunchKernelGGL((inter_kernel<D, F32IO, M>), dim3(unit_blocks * groups), dim3(SHP::NT), SHP::lds_bytes,
-                           a.stream, a.h0, s_in, segs, table, nseg, a.H, p.max_chunks, slabs, p.slab_bytes, a.o,
-                           a.hT, trans, groups, meta, ck_off, a.ck, ck_chunks,
+                           blk_carry ? st : a.stream, a.h0, s_in, segs, table, nseg, a.H, p.max_chunks, slabs,
+                           p.slab_bytes, a.o, a.hT, trans, groups, meta, ck_off, a.ck, ck_chunks,
                            fx ? static_cast<const uint16_t *>(fx->g) : nullptr, fx ? fx->w : nullptr,
-                           fx ? fx->eps : 0.f);
+                           fx ? fx->eps : 0.f, blk_lo, blk_hi, blk_carry);
         return hipGetLastError() == hipSuccess;
     };
+    if constexpr (!F32IO) {
+        if (pipe) {
+            // Chunk blocks [j per, (j + 1) per): the intra kernel of block
+            // j + 1 (on the caller's stream, after a short delay so that the
+            // chain's workgroups take their CUs first) runs beside the inter
+            // kernel of block j (on a helper stream); the state crosses block
+            // boundaries through `carry`.  Events order the two streams; no
+            // kernel waits on another.
+            PipeStreams *ps = pipe_streams();
+            if (!ps) return -1;
+            const int B = p.blocks;
+            const int per = (p.max_chunks + B - 1) / B;
+            const float *null_row = reinterpret_cast<const float *>(a.ws + p.off_null);
+            auto intra_block = [&](int j) {
+                return launch_intra_bf16<D>(a, meta, table, null_row, slabs, j * per * a.H, (j + 1) * per * a.H,
+                                            claims + j);
+            };
+            if (intra_block(0) != 0 || hipEventRecord(ps->ev[0], a.stream) != hipSuccess) return -1;
+            for (int j = 0; j < B; ++j) {
+                if (hipStreamWaitEvent(ps->s1, ps->ev[j], 0) != hipSuccess) return -1;
+                if (!inter(std::integral_constant<int, kModeOutput>{}, ps->s1, j * per,
+                           j == B - 1 ? INT_MAX : (j + 1) * per, carry))
+                    return -1;
+                if (j + 1 < B) {
+                    hipLaunchKernelGGL(pipeline_delay_kernel, dim3(1), dim3(64), 0, a.stream, kPipeDelayTicks);
+                    if (hipGetLastError() != hipSuccess || intra_block(j + 1) != 0 ||
+                        hipEventRecord(ps->ev[j + 1], a.stream) != hipSuccess)
+                        return -1;
+                }
+            }
+            if (hipEventRecord(ps->ev[kMaxBlocks], ps->s1) != hipSuccess ||
+                hipStreamWaitEvent(a.stream, ps->ev[kMaxBlocks], 0) != hipSuccess)
+                return -1;
+            return 0;
+        }
+    }
     if (p.P > 1) {
         // the transition of every segment but a sequence's last, then the
         // incoming state of every segment

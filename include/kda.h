@@ -110,13 +110,34 @@ typedef enum kda_status {
  *                          checkpoint index of every sequence, then the total
  *   Entries past the total are left untouched; checkpoints and offsets may
  *   overlap no other argument.
+ *
+ * blocks: the chunk-block pipeline of the bf16 prefill (the pages' kernel
+ *   overlaps intra-chunk work with the serial state propagation: devpress
+ *   walk-through §8.1; "Kimi K3：架构…" §13.1).  The chunk table is cut into
+ *   `blocks` runs of consecutive chunks; the intra-chunk kernel of run j + 1
+ *   runs on the caller's stream beside the inter-chunk kernel of run j on a
+ *   helper stream of the calling thread (created on its first pipelined call,
+ *   default priority, kept until the process ends), and a sequence's state
+ *   crosses run boundaries through the workspace.  Events order the two
+ *   streams, and the call is still asynchronous on `stream` and may be
+ *   captured in a graph.  The outputs are bit-identical to blocks = 1.
+ *     0  automatic (default): on the bf16 path without segments or
+ *        checkpoints, when the chain's workgroups leave CUs free for the
+ *        intra kernel and the sequences are long
+ *     1  off
+ *     2..KDA_MAX_PREFILL_BLOCKS  that many runs (with segments = 0 the
+ *        segment count is then 1; with segments >= 2 the call is rejected);
+ *        ignored, segments included, on the fp32 path and with checkpoints;
+ *        ignored by the fused prefill and by the backward
  */
 #define KDA_MAX_PREFILL_SEGMENTS 16
+#define KDA_MAX_PREFILL_BLOCKS 16
 typedef struct kda_prefill_options {
     int segments;
     int checkpoint_interval;
     float *checkpoints;
     int32_t *checkpoint_offsets;
+    int blocks;
 } kda_prefill_options;
 
 /*

@@ -146,6 +146,36 @@ def test_decode_fused_rejects_bad_arguments():
     assert d(win_out=FAKE + 57344) == -8          # the new window on top of the gate
 
 
+def test_block_option():
+    """The chunk-block pipeline option: range checks, the conflict with forced
+    segments, and the workspace growing by the carried state (N H dk dv fp32)
+    and the block counters wherever the pipeline applies (bf16 path, one
+    segment, no checkpoints; never in the backward)."""
+    assert ctypes.sizeof(kda.PrefillOptions) == 32
+    big = lambda **kw: kda.kda_prefill_ex_workspace_size(1, 65536, 96, 128, 128, kda.KDA_BF16, kda.options(**kw))
+    assert big(blocks=-1) == 0 and big(blocks=17) == 0
+    assert big(segments=3, blocks=3) == 0
+    carry = 96 * 128 * 128 * 4 + 256
+    assert big(blocks=3) - big(blocks=1) == carry
+    assert big(blocks=16) - big(blocks=1) == carry
+    # the K3 shape pipelines by default (the chain leaves CUs free, the sequence is long)
+    assert big() == big(blocks=3) == kda.kda_prefill_workspace_size(1, 65536, 96, 128, 128, kda.KDA_BF16)
+    # not applicable: fp32 io, checkpoints
+    f32 = lambda **kw: kda.kda_prefill_ex_workspace_size(1, 65536, 8, 64, 64, kda.KDA_F32, kda.options(**kw))
+    assert f32(blocks=3) == f32(blocks=1) > 0
+    assert big(blocks=3, interval=512, checkpoints=FAKE) == big(blocks=1, interval=512, checkpoints=FAKE) > 0
+    # forced blocks with automatic segments mean one segment: the small-head
+    # shape, split by default, then needs no segment transitions
+    small = lambda **kw: kda.kda_prefill_ex_workspace_size(2, 16384, 8, 128, 128, kda.KDA_BF16, kda.options(**kw))
+    assert small(blocks=3) == small(segments=1) + 2 * 8 * 128 * 128 * 4 + 256
+    # many short sequences, or a chain that fills the device: no pipeline by default
+    assert kda.kda_prefill_ex_workspace_size(32, 262144, 96, 128, 128, kda.KDA_BF16, kda.options()) == \
+        kda.kda_prefill_ex_workspace_size(32, 262144, 96, 128, 128, kda.KDA_BF16, kda.options(blocks=1))
+    # the backward ignores the option
+    bw = lambda o: kda.kda_prefill_backward_workspace_size(1, 65536, 8, 128, 128, kda.KDA_BF16, o)
+    assert bw(kda.options(blocks=3)) == bw(kda.options(blocks=1)) > 0
+
+
 def test_segment_option():
     """The per-call segment count: range checks, and the workspace growing by
     the transitions (2 d^2) and incoming states (d^2) in fp32 per (segment,

@@ -2,6 +2,8 @@
 
 A serving-shaped sequence is captured once with torch.cuda.graph: a
 segmented prefill of a ragged batch into caller-owned o, hT and workspace;
+the same prefill through the chunk-block pipeline (a helper stream joined by
+events);
 two decode steps on the prefill's final state, in place; one fused decode
 step on that state with its conv window carried in place; and the prefill
 without a workspace argument (its fixed device scratch).  The graph is
@@ -44,6 +46,10 @@ def make_state(seed=8100, dev="cuda"):
         win=torch.empty_like(f["window"]),
         o2=torch.empty((T, H, D), dtype=torch.bfloat16, device=dev),
         hT2=torch.empty((N, H, D, D), dtype=torch.float32, device=dev),
+        o3=torch.empty((T, H, D), dtype=torch.bfloat16, device=dev),
+        hT3=torch.empty((N, H, D, D), dtype=torch.float32, device=dev),
+        ws3=torch.empty(kda.kda_prefill_ex_workspace_size(N, T, H, D, D, kda.KDA_BF16, kda.options(blocks=3)),
+                        dtype=torch.uint8, device=dev),
     )
     return p, dec, f, fz, bufs
 
@@ -53,6 +59,8 @@ def sequence(p, dec, f, fz, b):
     b["win"].copy_(f["window"])
     kda.prefill(p["q"], p["k"], p["v"], p["z"], p["A"], p["beta"], p["cu_seqlens"], h0=p["h0"], o=b["o"],
                 hT=b["hT"], workspace=b["ws"], segments=3)
+    kda.prefill(p["q"], p["k"], p["v"], p["z"], p["A"], p["beta"], p["cu_seqlens"], h0=p["h0"], o=b["o3"],
+                hT=b["hT3"], workspace=b["ws3"], blocks=3)
     for i in range(2):
         kda.decode(dec[i]["q"], dec[i]["k"], dec[i]["v"], dec[i]["z"], p["A"], dec[i]["beta"], b["hT"],
                    o=b["od"][i])
@@ -66,17 +74,25 @@ def sequence(p, dec, f, fz, b):
     assert st == 0, kda.kda_status_string(st)
 
 
+OUTS = ("o", "hT", "od0", "od1", "y", "win", "o2", "hT2", "o3", "hT3")
+
+
+def outputs(b):
+    return [b["od"][0] if n == "od0" else b["od"][1] if n == "od1" else b[n] for n in OUTS]
+
+
 def snapshot(b):
-    return [t.clone() for t in (b["o"], b["hT"], b["od"][0], b["od"][1], b["y"], b["win"], b["o2"], b["hT2"])]
+    return [t.clone() for t in outputs(b)]
 
 
 def scribble(b):
-    for t in (b["o"], b["hT"], b["od"][0], b["od"][1], b["y"], b["win"], b["o2"], b["hT2"]):
+    for t in outputs(b):
         t.fill_(-7.0)
 
 
 def test_capture_and_replay():
-    print("case graph capture: prefill (3 segments), 2 decode steps, fused decode, noalloc prefill", flush=True)
+    print("case graph capture: prefill (3 segments), pipelined prefill, 2 decode steps, fused decode, noalloc "
+          "prefill", flush=True)
     p, dec, f, fz, b = make_state()
     sequence(p, dec, f, fz, b)            # eager, also the warm-up before capture
     torch.cuda.synchronize()
@@ -100,7 +116,6 @@ def test_capture_and_replay():
             sequence(p2, dec2, f2, fz2, b2)   # eager work between replays
         torch.cuda.synchronize()
         got = snapshot(b)
-        names = ("o", "hT", "od0", "od1", "y", "window", "o noalloc", "hT noalloc")
-        for n, x, y in zip(names, got, want):
+        for n, x, y in zip(OUTS, got, want):
             assert torch.equal(x, y), "replay %d: %s differs from the eager run" % (rep, n)
     g.reset()

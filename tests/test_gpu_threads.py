@@ -3,8 +3,9 @@
 The entry points keep no state between calls (the workspace size is a pure
 function of the arguments), so threads may size workspaces and launch
 prefills and decode steps concurrently, each on its own stream with its own
-buffers.  Four threads each run a different mix of calls (segmented and
-unsplit prefills, fp32 and bf16, decode steps on the prefill's state) on
+buffers; a pipelined prefill uses the calling thread's own helper stream.
+Four threads each run a different mix of calls (segmented, pipelined and
+plain prefills, fp32 and bf16, decode steps on the prefill's state) on
 streams of the default priority, all at the same time; every result must
 equal the same calls run one after the other on one stream, bit for bit."""
 import threading
@@ -18,11 +19,11 @@ from gated_delta_rule_21_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # (lens, H, d, io, segments)
-    ([700, 3, 129], 4, 128, "bf16", 3),
-    ([64, 0, 333], 3, 64, "f32", 1),
-    ([1500], 2, 128, "bf16", 0),
-    ([17, 200, 65, 1], 5, 32, "bf16", 2),
+    # (lens, H, d, io, segments, blocks)
+    ([700, 3, 129], 4, 128, "bf16", 3, 0),
+    ([64, 0, 333], 3, 64, "f32", 1, 0),
+    ([1500, 900], 2, 128, "bf16", 0, 3),
+    ([17, 200, 65, 1], 5, 32, "bf16", 2, 0),
 ]
 
 
@@ -31,24 +32,24 @@ def to(d, dev):
 
 
 def prepare(i):
-    lens, H, d, io, P = CASES[i]
+    lens, H, d, io, P, B = CASES[i]
     dev = torch.device("cuda")
     p = to(W.random_prefill(lens, H, d, io, h0_std=0.05, seed=8300 + i), dev)
     dec = to(W.random_decode(len(lens), H, d, io, 0.05, seed=8400 + i), dev)
-    return p, dec, P
+    return p, dec, P, B
 
 
-def work(p, dec, P, reps=3):
+def work(p, dec, P, B, reps=3):
     """Prefill into fresh buffers, then a decode step on its final state;
     repeated, returning every output."""
     outs = []
     N = p["cu_seqlens"].numel() - 1
     T, H, d = p["q"].shape
-    ws = torch.empty(kda.kda_prefill_ex_workspace_size(N, T, H, d, d, kda._io_code(p["q"]), kda.options(P)),
-                     dtype=torch.uint8, device="cuda")
+    n = kda.kda_prefill_ex_workspace_size(N, T, H, d, d, kda._io_code(p["q"]), kda.options(P, blocks=B))
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
     for _ in range(reps):
         o, hT = kda.prefill(p["q"], p["k"], p["v"], p["z"], p["A"], p["beta"], p["cu_seqlens"], h0=p["h0"],
-                            workspace=ws, segments=P)
+                            workspace=ws, segments=P, blocks=B)
         od = kda.decode(dec["q"], dec["k"], dec["v"], dec["z"], p["A"], dec["beta"], hT)
         outs += [o, hT, od]
     return outs
