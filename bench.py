@@ -538,14 +538,14 @@ def main():
                     "mfma_counted_frac": (None if mfma_flops is None else
                                           round(mfma_flops / (pre_ms * 1e-3) / 1e12 / BF16_DENSE_PEAK_TFLOPS, 4)),
                     "mfma_counted_source": "profiles/kda_k3_prefill_counters.md: 16-bit MFMA MOPS x 512 per "
-                                           "launch (rocprofv3 --pmc) / this run's launch time"},
+                                           "call (rocprofv3 --pmc) / this run's call time"},
         "decode": {"ms_per_step": round(dec_ms, 4), "steps": args.decode_steps,
                    "state_GBps": round(dec_gbps, 1), "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                    "ms_in_step": round(dec_ms_step, 4)},
         "roofline": {"bound": "hbm", "achieved": round(pre_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(pre_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "kda_prefill (chunk table + intra + inter kernels), "
-                               "1540 algorithmic B per (token, head) x 6291456 pairs per launch"},
+                     "kernel": "kda_prefill (chunk table, then intra and inter kernels pipelined over three "
+                               "chunk runs), 1540 algorithmic B per (token, head) x 6291456 pairs per call"},
     }
     if not args.no_features:
         line["feature_path"] = feature_path_cost(kda, W, dev, pre)
