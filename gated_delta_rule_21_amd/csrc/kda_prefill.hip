@@ -334,6 +334,20 @@ __device__ __forceinline__ float to_f16_scaled(const f32x4 *x, u32x4 *out) {
     return exp2i(e);
 }
 
+// S <- Diag(gamma_C) S + K~^T V' for one accumulator quad: a = K~^T V' at the
+// scale of V''s fp16 copy and u the power of two that undoes it, so a * u is
+// exact and one fused multiply-add rounds the new state once.  Written out
+// rather than left to the compiler's contraction choice, which can differ
+// between instantiations (output, gated-output and transition modes) and
+// between compiler versions; either choice is within the error bound, but
+// only a fixed one keeps the modes' states bit-identical.
+__device__ __forceinline__ f32x4 decay_add(f32x4 s, f32x4 g, f32x4 a, float u) {
+    f32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = __builtin_fmaf(s[j], g[j], a[j] * u);
+    return r;
+}
+
 template <int D, bool F32IO, int MODE>
 __global__ void __launch_bounds__((InterShape<D, F32IO, MODE>::NT))
     __attribute__((amdgpu_waves_per_eu((InterShape<D, F32IO, MODE>::WAVES_PER_SIMD),
@@ -720,11 +734,11 @@ __global__ void __launch_bounds__((InterShape<D, F32IO, MODE>::NT))
                 const f32x4 g = gmr[t];
                 f32x4 a = mma_f16_k32(k0, vf0, zero4());
                 a = mma_f16_k32(k1, vf1, a);
-                S[t] = S[t] * g + a * uV;
+                S[t] = decay_add(S[t], g, a, uV);
                 if constexpr (TR) {
                     f32x4 a2 = mma_f16_k32(k0, vf2[0], zero4());
                     a2 = mma_f16_k32(k1, vf2[1], a2);
-                    S2[t] = S2[t] * g + a2 * uV2;
+                    S2[t] = decay_add(S2[t], g, a2, uV2);
                 }
             }
             o_t0 = t_first + kChunk * i;
