@@ -8,10 +8,11 @@ the library is missing or the tensors are not on a GPU, the call raises.
 Entry points (same names as the C ABI in include/kda.h):
   kda_prefill(...)                  raw C call, pointers as ints
   kda_prefill_ex(..., options, ...) raw C call: prefill with per-call options
-                                    (segment count, state checkpoints)
+                                    (segment count, state checkpoints, block pipeline)
   kda_prefill_noalloc(...)          raw C call: prefill without a workspace (the
                                     library's fixed device scratch; no allocation)
   kda_prefill_fused(...)            raw C call: feature path -> prefill -> output gate
+  kda_prefill_fused_ex(..., options, ...)  the same with per-call options (segments, blocks)
   kda_decode(...)                   raw C call
   kda_decode_fused(...)             raw C call: feature path -> decode step -> output gate
   kda_decode_window(...)            raw C call: replay + multi-token window
@@ -96,6 +97,9 @@ def lib():
     L.kda_prefill_fused.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci,
                                     vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     L.kda_prefill_fused.restype = ci
+    L.kda_prefill_fused_ex.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci,
+                                       vp, vp, ctypes.c_float, vp, vp, op, vp, sz, vp]
+    L.kda_prefill_fused_ex.restype = ci
     L.kda_decode.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, vp, vp]
     L.kda_decode.restype = ci
     L.kda_decode_fused.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -158,6 +162,14 @@ def kda_prefill_fused(io_dtype, xq, xk, xv, wq, wk, wv, conv_state_in, conv_stat
     return lib().kda_prefill_fused(io_dtype, xq, xk, xv, wq, wk, wv, conv_state_in, conv_state_out, z, A, beta,
                                    h0, cu_seqlens, N, T, H, dk, dv, gate, norm_weight, float(eps), y, hT,
                                    workspace, workspace_bytes, stream)
+
+
+def kda_prefill_fused_ex(io_dtype, xq, xk, xv, wq, wk, wv, conv_state_in, conv_state_out, z, A, beta, h0,
+                         cu_seqlens, N, T, H, dk, dv, gate, norm_weight, eps, y, hT, options, workspace,
+                         workspace_bytes, stream) -> int:
+    return lib().kda_prefill_fused_ex(io_dtype, xq, xk, xv, wq, wk, wv, conv_state_in, conv_state_out, z, A,
+                                      beta, h0, cu_seqlens, N, T, H, dk, dv, gate, norm_weight, float(eps), y, hT,
+                                      options, workspace, workspace_bytes, stream)
 
 
 def kda_decode(io_dtype, q, k, v, z, A, beta, S_inout, N, H, dk, dv, o, stream) -> int:
@@ -468,11 +480,13 @@ def prefill_checkpoints(q, k, v, z, A, beta, cu_seqlens, interval: int, h0=None,
 
 
 def prefill_fused(xq, xk, xv, wq, wk, wv, z, A, beta, cu_seqlens, gate, norm_weight, eps: float, h0=None,
-                  conv_state_in=None, conv_state_out=None, y=None, hT=None, workspace=None, final_state=True):
+                  conv_state_in=None, conv_state_out=None, y=None, hT=None, workspace=None, final_state=True,
+                  segments=0, blocks=0):
     """The feature path, the prefill and the output gate in one call (bf16):
     y = Sigmoid(gate) * RMSNorm(o) with o, hT = prefill(q, k, v, ...) and q, k,
     v = qkv_shortconv(xq, xk, xv, ...).  Returns (y, hT); conv_state_out (may
-    be conv_state_in) receives the new conv window."""
+    be conv_state_in) receives the new conv window.  segments and blocks as for
+    prefill (0: automatic)."""
     torch = _torch()
     _check("xq", xq, (None, None, None), torch.bfloat16)
     T, H, d = xq.shape
@@ -503,15 +517,16 @@ def prefill_fused(xq, xk, xv, wq, wk, wv, z, A, beta, cu_seqlens, gate, norm_wei
         y = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
     if hT is None and final_state:
         hT = torch.empty((N, H, d, d), dtype=torch.float32, device=dev)
+    opts = options(segments, blocks=blocks)
     if workspace is None:
-        workspace = prefill_workspace(N, T, H, d, KDA_BF16, dev)
-    _check_workspace(workspace, kda_prefill_workspace_size(N, T, H, d, d, KDA_BF16), dev)
-    st = kda_prefill_fused(KDA_BF16, _ptr(xq), _ptr(xk), _ptr(xv), _ptr(wq), _ptr(wk), _ptr(wv),
-                           _ptr(conv_state_in), _ptr(conv_state_out), _ptr(z), _ptr(A), _ptr(beta), _ptr(h0),
-                           _ptr(cu_seqlens), N, T, H, d, d, _ptr(gate), _ptr(norm_weight), eps, _ptr(y), _ptr(hT),
-                           _ptr(workspace), workspace.numel(), _stream(dev))
+        workspace = prefill_workspace(N, T, H, d, KDA_BF16, dev, segments, blocks)
+    _check_workspace(workspace, kda_prefill_ex_workspace_size(N, T, H, d, d, KDA_BF16, opts), dev)
+    st = kda_prefill_fused_ex(KDA_BF16, _ptr(xq), _ptr(xk), _ptr(xv), _ptr(wq), _ptr(wk), _ptr(wv),
+                              _ptr(conv_state_in), _ptr(conv_state_out), _ptr(z), _ptr(A), _ptr(beta), _ptr(h0),
+                              _ptr(cu_seqlens), N, T, H, d, d, _ptr(gate), _ptr(norm_weight), eps, _ptr(y),
+                              _ptr(hT), opts, _ptr(workspace), workspace.numel(), _stream(dev))
     if st != 0:
-        raise KdaError("kda_prefill_fused", st)
+        raise KdaError("kda_prefill_fused_ex", st)
     return y, hT
 
 

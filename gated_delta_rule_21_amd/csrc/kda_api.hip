@@ -79,12 +79,12 @@ bool checkpoints_requested(const kda_prefill_options *opt) {
 // Chunk blocks of a call: the caller's, or the automatic choice (0); 1 where
 // the pipeline does not apply (fp32 path, segments, checkpoints).  -1 for an
 // out-of-range request or one that conflicts with forced segments.
-int blocks_of(const kda_prefill_options *opt, int N, int T, int H, int d, bool f32io, int P) {
+int blocks_of(const kda_prefill_options *opt, int N, int T, int H, int d, bool f32io, int P, bool fused = false) {
     const int b = opt ? opt->blocks : 0;
     if (b < 0 || b > KDA_MAX_PREFILL_BLOCKS) return -1;
     if (b > 1 && opt->segments > 1) return -1;
     if (f32io || P > 1 || checkpoints_requested(opt)) return 1;
-    return b > 0 ? b : kda::choose_blocks(N, T, H, d);
+    return b > 0 ? b : kda::choose_blocks(N, T, H, d, fused);
 }
 
 // Segment count of a call once forced blocks are taken into account: on the
@@ -145,8 +145,7 @@ int prefill_impl(kda_dtype io_dtype, const void *q, const void *k, const void *v
     const int P = segments_with_blocks(opt, N, T, H, dk, io_dtype == KDA_F32);
     if (P < 1) return KDA_ERR_INVALID_ARGUMENT;
     if (N < 0 || T < 0 || H <= 0) return KDA_ERR_INVALID_ARGUMENT;
-    // the fused call is never pipelined (its epilogue runs in the inter kernel's gate mode)
-    const int B = fx ? 1 : blocks_of(opt, N, T, H, dk, io_dtype == KDA_F32, P);
+    const int B = blocks_of(opt, N, T, H, dk, io_dtype == KDA_F32, P, fx != nullptr);
     if (B < 1) return KDA_ERR_INVALID_ARGUMENT;
     if (!supported_dim(dk, dv)) return KDA_ERR_UNSUPPORTED_DIM;
     if (!A || !cu_seqlens || !workspace) return KDA_ERR_NULL_POINTER;
@@ -255,7 +254,21 @@ int kda_prefill_fused(kda_dtype io_dtype, const void *xq, const void *xk, const 
                       const float *z, const float *A, const float *beta, const float *h0, const int32_t *cu_seqlens,
                       int N, int T, int H, int dk, int dv, const void *gate, const float *norm_weight, float eps,
                       void *y, float *hT, void *workspace, size_t workspace_bytes, void *stream) {
+    return kda_prefill_fused_ex(io_dtype, xq, xk, xv, wq, wk, wv, conv_state_in, conv_state_out, z, A, beta, h0,
+                                cu_seqlens, N, T, H, dk, dv, gate, norm_weight, eps, y, hT, nullptr, workspace,
+                                workspace_bytes, stream);
+}
+
+int kda_prefill_fused_ex(kda_dtype io_dtype, const void *xq, const void *xk, const void *xv, const float *wq,
+                         const float *wk, const float *wv, const void *conv_state_in, void *conv_state_out,
+                         const float *z, const float *A, const float *beta, const float *h0,
+                         const int32_t *cu_seqlens, int N, int T, int H, int dk, int dv, const void *gate,
+                         const float *norm_weight, float eps, void *y, float *hT, const kda_prefill_options *options,
+                         void *workspace, size_t workspace_bytes, void *stream) {
     if (io_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED_DTYPE;
+    // the gated output mode stores no state checkpoints
+    if (checkpoints_requested(options) || (options && options->checkpoint_interval != 0))
+        return KDA_ERR_INVALID_ARGUMENT;
     if (N < 0 || T < 0 || H <= 0 || !(eps >= 0.f)) return KDA_ERR_INVALID_ARGUMENT;
     if (!supported_dim(dk, dv)) return KDA_ERR_UNSUPPORTED_DIM;
     if (!wq || !wk || !wv || !norm_weight) return KDA_ERR_NULL_POINTER;
@@ -269,7 +282,7 @@ int kda_prefill_fused(kda_dtype io_dtype, const void *xq, const void *xk, const 
     fx.win_in = conv_state_in; fx.win_out = conv_state_out;
     fx.g = gate; fx.w = norm_weight; fx.eps = eps;
     return prefill_impl(io_dtype, nullptr, nullptr, nullptr, z, A, beta, h0, cu_seqlens, N, T, H, dk, dv, y, hT,
-                        nullptr, workspace, workspace_bytes, stream, &fx);
+                        options, workspace, workspace_bytes, stream, &fx);
 }
 
 size_t kda_prefill_backward_workspace_size(int N, int T, int H, int dk, int dv, kda_dtype io_dtype,

@@ -166,7 +166,7 @@ struct BackwardArgs {
 bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, int P, int blocks, PrefillPlan *plan);
 // Chunk blocks of the pipelined prefill for these sizes when the caller asks
 // for the automatic choice (1: not pipelined).
-int choose_blocks(int N, int T, int H, int d);
+int choose_blocks(int N, int T, int H, int d, bool fused = false);
 bool plan_backward(int N, int T, int H, int d, bool f32io, int P, BackwardPlan *plan);
 // Segment count the prefill uses for these sizes when the caller asks for
 // the automatic choice.

@@ -387,13 +387,13 @@ __global__ void __launch_bounds__((InterShape<D, F32IO, MODE>::NT))
     const int col = 16 * vt + ln;
 
     // The chunks this launch walks: the segment's, or (block pipeline, bf16
-    // output mode) their part in [blk_lo, blk_hi) of the chunk table.  A
+    // output and gated-output modes) their part in [blk_lo, blk_hi) of the chunk table.  A
     // sequence that began in an earlier block starts from `carry`, one that
     // goes on into a later block leaves its state there.  An empty sequence
     // belongs to the block holding its position.
     int c_begin = rec.y, c_end = rec.z;
     bool from_carry = false, to_carry = false;
-    if (OUT && !GATE && !F32IO && carry) {
+    if (OUT && !F32IO && carry) {
         const int lo_c = max(c_begin, blk_lo), hi_c = min(c_end, blk_hi);
         const bool here = c_begin < c_end ? lo_c < hi_c : (c_begin >= blk_lo && c_begin < blk_hi);
         if (!here) return;
@@ -954,12 +954,16 @@ __global__ void __launch_bounds__(D * 4) combine_kernel(const float *__restrict_
 // 64 value columns) leave at least 32 CUs to the intra kernel, and the
 // sequences are long enough that every run keeps the chain busy for far
 // longer than the per-run launch and delay costs (tens of microseconds).
-int choose_blocks(int N, int T, int H, int d) {
+// Three runs for the plain call; six for the fused one, whose intra kernel
+// (with the feature path) and chain (with the gate) are both longer, so
+// shorter runs start the chain earlier.  Whether to pipeline does not depend
+// on `fused`, so both calls need the same workspace.
+int choose_blocks(int N, int T, int H, int d, bool fused) {
     if (N <= 0 || T <= 0 || H <= 0) return 1;
     const long long chain_wgs = (long long)N * H * (d == 128 ? 2 : 1);
     if (chain_wgs > device_cus() - 32) return 1;
     const long long chunks_per_seq = (long long)T / kChunk / N;
-    return chunks_per_seq >= 192 ? 3 : 1;
+    return chunks_per_seq >= 192 ? (fused ? 6 : 3) : 1;
 }
 
 int choose_segments(int N, int T, int H, int d) {
@@ -1020,9 +1024,10 @@ static int launch_prefill_t(const PrefillArgs &a) {
     int4 *segs = reinterpret_cast<int4 *>(a.ws + p.off_segs);
     int32_t *ck_off = reinterpret_cast<int32_t *>(a.ws + p.off_ckoff);
     // block pipeline: the intra kernel of chunk block j + 1 runs beside the
-    // inter kernel of block j (bf16 path without segments, checkpoints or
-    // the fused epilogue)
-    const bool pipe = !F32IO && p.blocks > 1 && p.P == 1 && !a.ck && !a.ck_offsets && !a.fused && a.N > 0;
+    // inter kernel of block j (bf16 path without segments or checkpoints; in
+    // the fused call, the feature variant of the intra kernel and the gated
+    // output mode of the inter kernel)
+    const bool pipe = !F32IO && p.blocks > 1 && p.P == 1 && !a.ck && !a.ck_offsets && a.N > 0;
     int32_t *claims = reinterpret_cast<int32_t *>(a.ws + p.off_claims);
     float *carry = reinterpret_cast<float *>(a.ws + p.off_carry);
     const int ck_chunks = (a.ck || a.ck_offsets) ? a.ck_interval / kChunk : 0;
@@ -1042,8 +1047,9 @@ static int launch_prefill_t(const PrefillArgs &a) {
 
     if constexpr (!F32IO) {
         // the fused call's new conv window: after the intra kernel has read
-        // the old one (the two may be the same buffer)
-        if (a.fused && launch_conv_window(false, a.fused->xq, a.fused->xk, a.fused->xv, a.cu, a.N, a.T, a.H, D,
+        // the old one (the two may be the same buffer); pipelined, after the
+        // last intra kernel
+        if (a.fused && !pipe && launch_conv_window(false, a.fused->xq, a.fused->xk, a.fused->xv, a.cu, a.N, a.T, a.H, D,
                                           a.fused->win_in, a.fused->win_out, a.stream) != 0)
             return -1;
     }
@@ -1097,8 +1103,9 @@ static int launch_prefill_t(const PrefillArgs &a) {
             if (intra_block(0) != 0 || hipEventRecord(ps->ev[0], a.stream) != hipSuccess) return -1;
             for (int j = 0; j < B; ++j) {
                 if (hipStreamWaitEvent(ps->s1, ps->ev[j], 0) != hipSuccess) return -1;
-                if (!inter(std::integral_constant<int, kModeOutput>{}, ps->s1, bnd[j], j == B - 1 ? INT_MAX : bnd[j + 1],
-                           carry))
+                const int lo = bnd[j], hi = j == B - 1 ? INT_MAX : bnd[j + 1];
+                if (!(a.fused ? inter(std::integral_constant<int, kModeGate>{}, ps->s1, lo, hi, carry)
+                              : inter(std::integral_constant<int, kModeOutput>{}, ps->s1, lo, hi, carry)))
                     return -1;
                 if (j + 1 < B) {
                     hipLaunchKernelGGL(pipeline_delay_kernel, dim3(1), dim3(64), 0, a.stream, kPipeDelayTicks);
@@ -1107,6 +1114,9 @@ static int launch_prefill_t(const PrefillArgs &a) {
                         return -1;
                 }
             }
+            if (a.fused && launch_conv_window(false, a.fused->xq, a.fused->xk, a.fused->xv, a.cu, a.N, a.T, a.H, D,
+                                              a.fused->win_in, a.fused->win_out, a.stream) != 0)
+                return -1;
             if (hipEventRecord(ps->ev[kMaxBlocks], ps->s1) != hipSuccess ||
                 hipStreamWaitEvent(a.stream, ps->ev[kMaxBlocks], 0) != hipSuccess)
                 return -1;

@@ -123,12 +123,13 @@ typedef enum kda_status {
  *   captured in a graph.  The outputs are bit-identical to blocks = 1.
  *     0  automatic (default): on the bf16 path without segments or
  *        checkpoints, when the chain's workgroups leave CUs free for the
- *        intra kernel and the sequences are long
+ *        intra kernel and the sequences are long (three runs; six in the
+ *        fused prefill, where the decision is the same, so the workspace is)
  *     1  off
  *     2..KDA_MAX_PREFILL_BLOCKS  that many runs (with segments = 0 the
  *        segment count is then 1; with segments >= 2 the call is rejected);
  *        ignored, segments included, on the fp32 path and with checkpoints;
- *        ignored by the fused prefill and by the backward
+ *        ignored by the backward
  */
 #define KDA_MAX_PREFILL_SEGMENTS 16
 #define KDA_MAX_PREFILL_BLOCKS 16
@@ -228,6 +229,23 @@ int kda_prefill_fused(kda_dtype io_dtype, const void *xq, const void *xk, const 
                       const int32_t *cu_seqlens, int N, int T, int H, int dk, int dv, const void *gate,
                       const float *norm_weight, float eps, void *y, float *hT, void *workspace,
                       size_t workspace_bytes, void *stream);
+
+/*
+ * kda_prefill_fused with per-call options (NULL: the defaults, which is
+ * kda_prefill_fused): the segment count and the chunk-block pipeline as for
+ * kda_prefill_ex.  Checkpoints are not available here (the gated output pass
+ * stores no states): a non-NULL checkpoint pointer or a non-zero
+ * checkpoint_interval gives KDA_ERR_INVALID_ARGUMENT.  The workspace is
+ * kda_prefill_ex_workspace_size(N, T, H, dk, dv, KDA_BF16, options) bytes.
+ * The outputs do not depend on `blocks`, bit for bit.
+ */
+int kda_prefill_fused_ex(kda_dtype io_dtype, const void *xq, const void *xk, const void *xv, const float *wq,
+                         const float *wk, const float *wv, const void *conv_state_in, void *conv_state_out,
+                         const float *z, const float *A, const float *beta, const float *h0,
+                         const int32_t *cu_seqlens, int N, int T, int H, int dk, int dv, const void *gate,
+                         const float *norm_weight, float eps, void *y, float *hT,
+                         const kda_prefill_options *options, void *workspace, size_t workspace_bytes,
+                         void *stream);
 
 /*
  * kda_prefill for callers that cannot allocate device memory: code under

@@ -22,7 +22,7 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["kda_build_info", "kda_decode", "kda_decode_fused", "kda_decode_window",
                                            "kda_prefill",
                                            "kda_prefill_ex", "kda_prefill_ex_workspace_size",
-                                           "kda_prefill_noalloc", "kda_prefill_fused",
+                                           "kda_prefill_noalloc", "kda_prefill_fused", "kda_prefill_fused_ex",
                                            "kda_qkv_shortconv", "kda_output_gate",
                                            "kda_prefill_segments", "kda_prefill_workspace_size",
                                            "kda_prefill_backward", "kda_prefill_backward_workspace_size",
@@ -174,6 +174,28 @@ def test_block_option():
     # the backward ignores the option
     bw = lambda o: kda.kda_prefill_backward_workspace_size(1, 65536, 8, 128, 128, kda.KDA_BF16, o)
     assert bw(kda.options(blocks=3)) == bw(kda.options(blocks=1)) > 0
+
+
+def test_prefill_fused_ex_options():
+    """The fused prefill's options: checkpoints are refused (the gated output
+    pass stores no states), out-of-range blocks and forced segments with
+    forced blocks likewise; all decided on the host, before any launch.  With
+    NULL options it is kda_prefill_fused, whose workspace is the plain call's."""
+    def f(opts, io=0, ws_bytes=1 << 40):
+        return kda.kda_prefill_fused_ex(io, FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288, FAKE + 16384,
+                                        FAKE + 20480, None, None, FAKE + 24576, FAKE + 32768, FAKE + 36864, None,
+                                        FAKE + 40960, 1, 64, 2, 32, 32, FAKE + 45056, FAKE + 49152, 1e-6,
+                                        1 << 41, None, opts, FAKE + (1 << 24), ws_bytes, None)
+    assert f(kda.options(interval=512, checkpoints=FAKE)) == -1
+    assert f(kda.options(interval=64)) == -1
+    assert f(kda.options(blocks=17)) == -1 and f(kda.options(blocks=-1)) == -1
+    assert f(kda.options(segments=2, blocks=2)) == -1
+    assert f(kda.options(blocks=2), io=1) == -4
+    assert f(kda.options(blocks=2), ws_bytes=16) == -6     # workspace too small, reported before any launch
+    # the automatic choice pipelines the fused call where it pipelines the plain one: same workspace
+    for shape in ((1, 65536, 96), (2, 16384, 8), (32, 262144, 96)):
+        assert kda.kda_prefill_ex_workspace_size(*shape, 128, 128, kda.KDA_BF16, None) == \
+            kda.kda_prefill_workspace_size(*shape, 128, 128, kda.KDA_BF16)
 
 
 def test_segment_option():

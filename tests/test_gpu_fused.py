@@ -52,7 +52,7 @@ def oracle_fused(d, heads=None):
     return ry, rh, wout, ro, sel(widen(d["gate"]))
 
 
-def gpu_fused(g, in_place=False):
+def gpu_fused(g, in_place=False, segments=0, blocks=0):
     N = g["cu_seqlens"].numel() - 1
     T, H, d = g["xq"].shape
     win_in = g["window"]
@@ -62,15 +62,15 @@ def gpu_fused(g, in_place=False):
         win_out = torch.empty((N, 3, H, 3 * d), dtype=torch.bfloat16, device="cuda")
     y, hT = kda.prefill_fused(g["xq"], g["xk"], g["xv"], g["wq"], g["wk"], g["wv"], g["z"], g["A"], g["beta"],
                               g["cu_seqlens"], g["gate"], g["norm_w"], EPS, h0=g["h0"], conv_state_in=win_in,
-                              conv_state_out=win_out)
+                              conv_state_out=win_out, segments=segments, blocks=blocks)
     torch.cuda.synchronize()
     return y, hT, win_out
 
 
-def check(d, label, heads=None, in_place=False):
+def check(d, label, heads=None, in_place=False, blocks=0):
     print("case", label, flush=True)
     g = {n: (t.cuda() if isinstance(t, torch.Tensor) else t) for n, t in d.items()}
-    y, hT, win = gpu_fused(g, in_place)
+    y, hT, win = gpu_fused(g, in_place, blocks=blocks)
     ry, rh, rwin, ro, rgate = oracle_fused(d, heads)
     cu = d["cu_seqlens"].tolist()
     if heads is not None:
@@ -88,6 +88,27 @@ def test_fused_ragged_with_window(d):
     """Empty sequences, sequences shorter than the conv window (their taps
     read the carried window), partial chunks and several chunks."""
     check(inputs([0, 1, 2, 3, 5, 70, 200, 0, 130], 3, d, seed=900 + d), "fused ragged d=%d" % d)
+
+
+@pytest.mark.parametrize("d,blocks", [(128, 2), (128, 6), (64, 3), (32, 16)])
+def test_fused_blocks_bit_identical_and_oracle(d, blocks):
+    """The fused call pipelined over chunk runs (the feature variant of the
+    intra kernel beside the gated output pass, the state carried between
+    runs): y, hT and the new window bit-identical to blocks = 1, also with the
+    window in place, over ragged lengths with sequences shorter than the
+    window and empty ones at the run ends; and within every bar of the
+    oracle composition."""
+    lens = [700, 0, 1, 2, 129, 64, 0, 333, 1500, 3, 0]
+    d_ = inputs(lens, 3, d, seed=960 + d + blocks)
+    print("case fused blocks d=%d blocks=%d" % (d, blocks), flush=True)
+    g = {n: (t.cuda() if isinstance(t, torch.Tensor) else t) for n, t in d_.items()}
+    y1, h1, w1 = gpu_fused(g, blocks=1)
+    yb, hb, wb = gpu_fused(g, blocks=blocks)
+    assert torch.equal(yb, y1) and torch.equal(hb, h1) and torch.equal(wb, w1)
+    gi = dict(g, window=g["window"].clone())
+    yi, hi, wi = gpu_fused(gi, in_place=True, blocks=blocks)
+    assert torch.equal(yi, y1) and torch.equal(hi, h1) and torch.equal(wi, w1)
+    check(d_, "fused blocks %d d=%d" % (blocks, d), blocks=blocks)
 
 
 def test_fused_without_window_and_in_place():

@@ -3,7 +3,8 @@
 A serving-shaped sequence is captured once with torch.cuda.graph: a
 segmented prefill of a ragged batch into caller-owned o, hT and workspace;
 the same prefill through the chunk-block pipeline (a helper stream joined by
-events);
+events); the fused prefill of the same batch, pipelined, its conv window
+carried in place;
 two decode steps on the prefill's final state, in place; one fused decode
 step on that state with its conv window carried in place; and the prefill
 without a workspace argument (its fixed device scratch).  The graph is
@@ -36,6 +37,7 @@ def make_state(seed=8100, dev="cuda"):
     dec = [to(W.random_decode(N, H, D, "bf16", 0.05, seed=seed + 10 + i), dev) for i in range(2)]
     f = to(W.random_features([1] * N, H, D, "bf16", window=True, seed=seed + 20), dev)
     fz = to(W.random_decode(N, H, D, "bf16", 0.05, seed=seed + 21), dev)
+    ff = to(W.random_features(LENS, H, D, "bf16", window=True, seed=seed + 30), dev)
     bufs = dict(
         o=torch.empty((T, H, D), dtype=torch.bfloat16, device=dev),
         hT=torch.empty((N, H, D, D), dtype=torch.float32, device=dev),
@@ -50,6 +52,12 @@ def make_state(seed=8100, dev="cuda"):
         hT3=torch.empty((N, H, D, D), dtype=torch.float32, device=dev),
         ws3=torch.empty(kda.kda_prefill_ex_workspace_size(N, T, H, D, D, kda.KDA_BF16, kda.options(blocks=3)),
                         dtype=torch.uint8, device=dev),
+        ff=ff,
+        fy=torch.empty((T, H, D), dtype=torch.bfloat16, device=dev),
+        fhT=torch.empty((N, H, D, D), dtype=torch.float32, device=dev),
+        fwin=torch.empty_like(ff["window"]),
+        ws4=torch.empty(kda.kda_prefill_ex_workspace_size(N, T, H, D, D, kda.KDA_BF16, kda.options(blocks=3)),
+                        dtype=torch.uint8, device=dev),
     )
     return p, dec, f, fz, bufs
 
@@ -61,6 +69,11 @@ def sequence(p, dec, f, fz, b):
                 hT=b["hT"], workspace=b["ws"], segments=3)
     kda.prefill(p["q"], p["k"], p["v"], p["z"], p["A"], p["beta"], p["cu_seqlens"], h0=p["h0"], o=b["o3"],
                 hT=b["hT3"], workspace=b["ws3"], blocks=3)
+    ff = b["ff"]
+    b["fwin"].copy_(ff["window"])
+    kda.prefill_fused(ff["xq"], ff["xk"], ff["xv"], ff["wq"], ff["wk"], ff["wv"], p["z"], p["A"], p["beta"],
+                      p["cu_seqlens"], ff["g"], ff["w"], EPS, h0=p["h0"], conv_state_in=b["fwin"],
+                      conv_state_out=b["fwin"], y=b["fy"], hT=b["fhT"], workspace=b["ws4"], blocks=3)
     for i in range(2):
         kda.decode(dec[i]["q"], dec[i]["k"], dec[i]["v"], dec[i]["z"], p["A"], dec[i]["beta"], b["hT"],
                    o=b["od"][i])
@@ -74,7 +87,7 @@ def sequence(p, dec, f, fz, b):
     assert st == 0, kda.kda_status_string(st)
 
 
-OUTS = ("o", "hT", "od0", "od1", "y", "win", "o2", "hT2", "o3", "hT3")
+OUTS = ("o", "hT", "od0", "od1", "y", "win", "o2", "hT2", "o3", "hT3", "fy", "fhT", "fwin")
 
 
 def outputs(b):
@@ -91,8 +104,8 @@ def scribble(b):
 
 
 def test_capture_and_replay():
-    print("case graph capture: prefill (3 segments), pipelined prefill, 2 decode steps, fused decode, noalloc "
-          "prefill", flush=True)
+    print("case graph capture: prefill (3 segments), pipelined prefill, pipelined fused prefill, 2 decode steps, "
+          "fused decode, noalloc prefill", flush=True)
     p, dec, f, fz, b = make_state()
     sequence(p, dec, f, fz, b)            # eager, also the warm-up before capture
     torch.cuda.synchronize()
