@@ -13,6 +13,7 @@ Entry points (same names as the C ABI in include/kda.h):
                                     library's fixed device scratch; no allocation)
   kda_prefill_fused(...)            raw C call: feature path -> prefill -> output gate
   kda_prefill_fused_ex(..., options, ...)  the same with per-call options (segments, blocks)
+  kda_prefill_fused_workspace_size(..., options)  its workspace bytes
   kda_decode(...)                   raw C call
   kda_decode_fused(...)             raw C call: feature path -> decode step -> output gate
   kda_decode_window(...)            raw C call: replay + multi-token window
@@ -100,6 +101,8 @@ def lib():
     L.kda_prefill_fused_ex.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci,
                                        vp, vp, ctypes.c_float, vp, vp, op, vp, sz, vp]
     L.kda_prefill_fused_ex.restype = ci
+    L.kda_prefill_fused_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci, op]
+    L.kda_prefill_fused_workspace_size.restype = sz
     L.kda_decode.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, vp, vp]
     L.kda_decode.restype = ci
     L.kda_decode_fused.argtypes = [ci, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -162,6 +165,10 @@ def kda_prefill_fused(io_dtype, xq, xk, xv, wq, wk, wv, conv_state_in, conv_stat
     return lib().kda_prefill_fused(io_dtype, xq, xk, xv, wq, wk, wv, conv_state_in, conv_state_out, z, A, beta,
                                    h0, cu_seqlens, N, T, H, dk, dv, gate, norm_weight, float(eps), y, hT,
                                    workspace, workspace_bytes, stream)
+
+
+def kda_prefill_fused_workspace_size(N, T, H, dk, dv, io_dtype, opts=None) -> int:
+    return int(lib().kda_prefill_fused_workspace_size(N, T, H, dk, dv, io_dtype, _opt_ref(opts)))
 
 
 def kda_prefill_fused_ex(io_dtype, xq, xk, xv, wq, wk, wv, conv_state_in, conv_state_out, z, A, beta, h0,
@@ -518,9 +525,13 @@ def prefill_fused(xq, xk, xv, wq, wk, wv, z, A, beta, cu_seqlens, gate, norm_wei
     if hT is None and final_state:
         hT = torch.empty((N, H, d, d), dtype=torch.float32, device=dev)
     opts = options(segments, blocks=blocks)
+    need = kda_prefill_fused_workspace_size(N, T, H, d, d, KDA_BF16, opts)
+    if need == 0:
+        raise ValueError("unsupported fused prefill sizes N=%d T=%d H=%d d=%d segments=%d blocks=%d"
+                         % (N, T, H, d, segments, blocks))
     if workspace is None:
-        workspace = prefill_workspace(N, T, H, d, KDA_BF16, dev, segments, blocks)
-    _check_workspace(workspace, kda_prefill_ex_workspace_size(N, T, H, d, d, KDA_BF16, opts), dev)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, need, dev)
     st = kda_prefill_fused_ex(KDA_BF16, _ptr(xq), _ptr(xk), _ptr(xv), _ptr(wq), _ptr(wk), _ptr(wv),
                               _ptr(conv_state_in), _ptr(conv_state_out), _ptr(z), _ptr(A), _ptr(beta), _ptr(h0),
                               _ptr(cu_seqlens), N, T, H, d, d, _ptr(gate), _ptr(norm_weight), eps, _ptr(y),

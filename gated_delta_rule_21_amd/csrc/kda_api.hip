@@ -95,15 +95,16 @@ int segments_with_blocks(const kda_prefill_options *opt, int N, int T, int H, in
     return segments_of(opt, N, T, H, d);
 }
 
-size_t prefill_ws(int N, int T, int H, int dk, int dv, kda_dtype io_dtype, const kda_prefill_options *opt) {
+size_t prefill_ws(int N, int T, int H, int dk, int dv, kda_dtype io_dtype, const kda_prefill_options *opt,
+                  bool fused = false) {
     if (io_dtype != KDA_BF16 && io_dtype != KDA_F32) return 0;
     if (!supported_dim(dk, dv) || N < 0 || T < 0 || H <= 0) return 0;
     const int P = segments_with_blocks(opt, N, T, H, dk, io_dtype == KDA_F32);
     if (P < 1) return 0;
-    const int B = blocks_of(opt, N, T, H, dk, io_dtype == KDA_F32, P);
+    const int B = blocks_of(opt, N, T, H, dk, io_dtype == KDA_F32, P, fused);
     if (B < 1) return 0;
     kda::PrefillPlan p;
-    if (!kda::plan_prefill(N, T, H, dk, dv, io_dtype == KDA_F32, P, B, &p)) return 0;
+    if (!kda::plan_prefill(N, T, H, dk, dv, io_dtype == KDA_F32, P, B, &p, fused)) return 0;
     return p.total;
 }
 
@@ -121,6 +122,13 @@ size_t kda_prefill_ex_workspace_size(int N, int T, int H, int dk, int dv, kda_dt
         (options->checkpoint_interval <= 0 || options->checkpoint_interval % 64 != 0))
         return 0;
     return prefill_ws(N, T, H, dk, dv, io_dtype, options);
+}
+
+size_t kda_prefill_fused_workspace_size(int N, int T, int H, int dk, int dv, kda_dtype io_dtype,
+                                        const kda_prefill_options *options) {
+    if (io_dtype != KDA_BF16) return 0;
+    if (checkpoints_requested(options) || (options && options->checkpoint_interval != 0)) return 0;
+    return prefill_ws(N, T, H, dk, dv, io_dtype, options, true);
 }
 
 int kda_prefill_segments(int N, int T, int H, int dk, int dv, kda_dtype io_dtype) {
@@ -157,7 +165,8 @@ int prefill_impl(kda_dtype io_dtype, const void *q, const void *k, const void *v
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_MISALIGNED;
 
     kda::PrefillPlan plan;
-    if (!kda::plan_prefill(N, T, H, dk, dv, io_dtype == KDA_F32, P, B, &plan)) return KDA_ERR_INVALID_ARGUMENT;
+    if (!kda::plan_prefill(N, T, H, dk, dv, io_dtype == KDA_F32, P, B, &plan, fx != nullptr))
+        return KDA_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < plan.total) return KDA_ERR_WORKSPACE_TOO_SMALL;
 
     const size_t tok = (size_t)T * H;

@@ -41,17 +41,21 @@ __device__ __forceinline__ void seq_bounds(const int32_t *cu, int n, int T, int 
 
 // ShortConv -> Swish (-> L2Norm for q and k).  blockIdx.z: 0 = q, 1 = k, 2 = v;
 // blockIdx.y: a span of 1024 channels of the [H][d] row (256 / (d / 4)
-// heads); blockIdx.x: a range of TR tokens.  The block first copies rows
-// t0 - 3 .. t0 + TR - 1 of its span into LDS (direct global -> LDS copies,
-// 16 bytes per lane), then every thread walks its 4 channels through the
-// range, reading the four taps of each token from LDS.  Only taps before a
-// sequence's first token read the carried window instead.
+// heads); blockIdx.x: a range of TR tokens (tile0 + blockIdx.x).  The block
+// first copies rows t0 - 3 .. t0 + TR - 1 of its span into LDS (direct
+// global -> LDS copies, 16 bytes per lane), then every thread walks its 4
+// channels through the range, reading the four taps of each token from LDS.
+// Only taps before a sequence's first token read the carried window instead.
+// With a chunk table (the pipelined fused prefill), only the tokens of chunks
+// [c_lo, c_hi) are written: from the first token of chunk c_lo to that of
+// chunk c_hi (the end when c_hi is past the last chunk, nchunks[0] of them).
 template <int D, bool F32IO, int TR>
 __global__ void __launch_bounds__(256) shortconv_kernel(
     const void *__restrict__ xq, const void *__restrict__ xk, const void *__restrict__ xv,
     const float *__restrict__ wq, const float *__restrict__ wk, const float *__restrict__ wv,
     const int32_t *__restrict__ cu, int N, int T, int H, const void *__restrict__ win,
-    void *__restrict__ q, void *__restrict__ k, void *__restrict__ v) {
+    void *__restrict__ q, void *__restrict__ k, void *__restrict__ v, int tile0, const int4 *__restrict__ table,
+    const int32_t *__restrict__ nchunks, int c_lo, int c_hi) {
     constexpr int G = D / 4;                     // lanes per row
     constexpr int SPAN = 1024;                   // channels per block: 256 lanes x 4
     constexpr int EB = F32IO ? 4 : 2;            // bytes per element
@@ -67,7 +71,15 @@ __global__ void __launch_bounds__(256) shortconv_kernel(
     const int CW = 3 * D;                        // window channels per head: q | k | v
     const size_t rowc = (size_t)H * D;           // channels per token row
     const int ch0 = blockIdx.y * SPAN;           // first channel of the span
-    const int t0 = blockIdx.x * TR, t1 = min(t0 + TR, T);
+    const int t0 = (tile0 + (int)blockIdx.x) * TR, t1 = min(t0 + TR, T);
+    // the tokens this launch writes (every thread reads the same entries)
+    int w_lo = 0, w_hi = T;
+    if (table) {
+        const int nc = nchunks[0];
+        w_lo = c_lo < nc ? table[c_lo].y : T;
+        w_hi = c_hi < nc ? table[c_hi].y : T;
+    }
+    if (t0 >= t1 || t1 <= w_lo || t0 >= w_hi) return;   // uniform: before any barrier
 
     // stage rows t0 - 3 .. t1 - 1 of channels [ch0, ch0 + SPAN): direct
     // global -> LDS copies of 16 bytes per lane, zeros outside the tensor
@@ -135,7 +147,8 @@ __global__ void __launch_bounds__(256) shortconv_kernel(
         }
         store_io4<F32IO>(out, ((size_t)t * H + h) * D + c0, f);
     };
-    if (t1 - t0 == TR && s <= t0 - P && t1 <= e) {
+    const bool whole = t0 >= w_lo && t1 <= w_hi;
+    if (whole && t1 - t0 == TR && s <= t0 - P && t1 <= e) {
         // the whole range and the three rows before it in one sequence
 #pragma unroll
         for (int j = 0; j < TR; ++j) {
@@ -146,7 +159,7 @@ __global__ void __launch_bounds__(256) shortconv_kernel(
         }
         return;
     }
-    for (int t = t0; t < t1; ++t) {
+    for (int t = max(t0, w_lo); t < min(t1, w_hi); ++t) {
         while (t >= e && n < N - 1) {
             ++n;
             seq_bounds(cu, n, T, s, e);
@@ -252,11 +265,24 @@ template <int D, bool F32IO>
 static int launch_features_t(const FeatureArgs &a) {
     constexpr int TR = F32IO ? 8 : 16;   // staged rows: (TR + 3) x 1024 channels
     if (a.T > 0) {
-        const dim3 grid((unsigned)((a.T + TR - 1) / TR), (unsigned)(((long long)a.H * D + 1023) / 1024), 3);
-        hipLaunchKernelGGL((shortconv_kernel<D, F32IO, TR>), grid, dim3(256), 0, a.stream, a.xq, a.xk, a.xv, a.wq,
-                           a.wk, a.wv, a.cu, a.N, a.T, a.H, a.win_in, a.q, a.k, a.v);
-        if (hipGetLastError() != hipSuccess) return -1;
+        // token tiles: all, or (chunk run) those that can hold its tokens.
+        // Chunk c starts at token 64 (c - N) at the earliest (every chunk but
+        // a sequence's last is full) and at 64 c at the latest.
+        long long lo = 0, hi = a.T;
+        if (a.table) {
+            lo = std::max(0LL, 64LL * ((long long)a.c_lo - a.N));
+            hi = std::min((long long)a.T, 64LL * a.c_hi);
+        }
+        const long long tile0 = lo / TR, tiles = hi > lo ? (hi + TR - 1) / TR - tile0 : 0;
+        if (tiles > 0) {
+            const dim3 grid((unsigned)tiles, (unsigned)(((long long)a.H * D + 1023) / 1024), 3);
+            hipLaunchKernelGGL((shortconv_kernel<D, F32IO, TR>), grid, dim3(256), 0, a.stream, a.xq, a.xk, a.xv,
+                               a.wq, a.wk, a.wv, a.cu, a.N, a.T, a.H, a.win_in, a.q, a.k, a.v, (int)tile0, a.table,
+                               a.nchunks, a.c_lo, a.c_hi);
+            if (hipGetLastError() != hipSuccess) return -1;
+        }
     }
+    if (a.table) return 0;                // the caller writes the window after the last run
     if (a.win_out && a.N > 0) {
         const long long items = (long long)a.N * a.H * (3 * D / 4);
         hipLaunchKernelGGL((conv_window_kernel<F32IO>), dim3(stride_blocks(items, 256)), dim3(256), 0, a.stream, a.xq,

@@ -69,6 +69,12 @@ struct FeatureArgs {
     void *win_out;
     void *q, *k, *v;
     hipStream_t stream;
+    // chunk run of the pipelined fused prefill: only the tokens of chunks
+    // [c_lo, c_hi) of the chunk table are written (nchunks: device count of
+    // chunks), and the window is left to the caller
+    const int4 *table = nullptr;
+    const int32_t *nchunks = nullptr;
+    int c_lo = 0, c_hi = 0;
 };
 
 // Output gate: y = Sigmoid(g) * RMSNorm(o), rows of dv.
@@ -102,6 +108,8 @@ struct PrefillPlan {
     int blocks;              // block pipeline: chunk blocks (1: off)
     size_t off_claims;       // blocks > 1: int32 [blocks] item counters
     size_t off_carry;        // blocks > 1: fp32 [N][H][dv][dk] state between blocks
+    bool staged;             // pipelined fused call: q, k, v staged by the feature kernel
+    size_t off_qkv;          // staged: io dtype [3][T][H][dk] q, k, v
     size_t total;
 };
 
@@ -163,7 +171,10 @@ struct BackwardArgs {
     hipStream_t stream;
 };
 
-bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, int P, int blocks, PrefillPlan *plan);
+// `fused`: the plan of the fused call, which stages q, k, v in the workspace
+// when it is pipelined.
+bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, int P, int blocks, PrefillPlan *plan,
+                  bool fused = false);
 // Chunk blocks of the pipelined prefill for these sizes when the caller asks
 // for the automatic choice (1: not pipelined).
 int choose_blocks(int N, int T, int H, int d, bool fused = false);

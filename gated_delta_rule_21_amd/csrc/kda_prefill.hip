@@ -61,7 +61,7 @@ size_t slab_bytes(int dk, int dv, bool f32io) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, int P, int blocks, PrefillPlan *p) {
+bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, int P, int blocks, PrefillPlan *p, bool fused) {
     size_t sb = slab_bytes(dk, dv, f32io);
     if (sb == 0 || N < 0 || T < 0 || H <= 0 || P < 1 || P > kMaxSegments) return false;
     p->max_chunks = (int)(((long long)T + kChunk - 1) / kChunk + N);
@@ -79,7 +79,9 @@ bool plan_prefill(int N, int T, int H, int dk, int dv, bool f32io, int P, int bl
     p->blocks = P == 1 && !f32io && blocks > 1 ? blocks : 1;
     p->off_claims = p->off_slabs + (size_t)H * p->max_chunks * sb;
     p->off_carry = p->off_claims + (p->blocks > 1 ? align256((size_t)p->blocks * 4) : 0);
-    p->total = p->off_carry + (p->blocks > 1 ? (size_t)N * H * dv * dk * 4 : 0);
+    p->staged = fused && p->blocks > 1;
+    p->off_qkv = p->off_carry + (p->blocks > 1 ? align256((size_t)N * H * dv * dk * 4) : 0);
+    p->total = p->off_qkv + (p->staged ? 3 * align256((size_t)T * H * dk * (f32io ? 4 : 2)) : 0);
     return true;
 }
 
@@ -957,7 +959,7 @@ __global__ void __launch_bounds__(D * 4) combine_kernel(const float *__restrict_
 // Three runs for the plain call; six for the fused one, whose intra kernel
 // (with the feature path) and chain (with the gate) are both longer, so
 // shorter runs start the chain earlier.  Whether to pipeline does not depend
-// on `fused`, so both calls need the same workspace.
+// on `fused`.
 int choose_blocks(int N, int T, int H, int d, bool fused) {
     if (N <= 0 || T <= 0 || H <= 0) return 1;
     const long long chain_wgs = (long long)N * H * (d == 128 ? 2 : 1);
@@ -1025,8 +1027,8 @@ static int launch_prefill_t(const PrefillArgs &a) {
     int32_t *ck_off = reinterpret_cast<int32_t *>(a.ws + p.off_ckoff);
     // block pipeline: the intra kernel of chunk block j + 1 runs beside the
     // inter kernel of block j (bf16 path without segments or checkpoints; in
-    // the fused call, the feature variant of the intra kernel and the gated
-    // output mode of the inter kernel)
+    // the fused call, each intra kernel after a feature pass that stages its
+    // run's q, k, v, and the inter kernel in its gated output mode)
     const bool pipe = !F32IO && p.blocks > 1 && p.P == 1 && !a.ck && !a.ck_offsets && a.N > 0;
     int32_t *claims = reinterpret_cast<int32_t *>(a.ws + p.off_claims);
     float *carry = reinterpret_cast<float *>(a.ws + p.off_carry);
@@ -1048,7 +1050,7 @@ static int launch_prefill_t(const PrefillArgs &a) {
     if constexpr (!F32IO) {
         // the fused call's new conv window: after the intra kernel has read
         // the old one (the two may be the same buffer); pipelined, after the
-        // last intra kernel
+        // last run
         if (a.fused && !pipe && launch_conv_window(false, a.fused->xq, a.fused->xk, a.fused->xv, a.cu, a.N, a.T, a.H, D,
                                           a.fused->win_in, a.fused->win_out, a.stream) != 0)
             return -1;
@@ -1096,8 +1098,38 @@ static int launch_prefill_t(const PrefillArgs &a) {
                 bnd[B] = p.max_chunks;
             }
             const float *null_row = reinterpret_cast<const float *>(a.ws + p.off_null);
+            // The fused call runs its feature path as passes of its own here:
+            // before the intra kernel of each run, the feature kernel stages
+            // that run's q, k, v in the workspace, and the plain intra kernel
+            // reads them; the new conv window is written after the last run.
+            // Inside the intra kernel the feature math lengthens every item
+            // of a kernel bound by latency, which costs more than the HBM
+            // round trip of q, k, v it saves; o still never reaches memory.
+            PrefillArgs ia = a;
+            FeatureArgs fa;
+            if (a.fused) {
+                if (!p.staged) return -1;
+                const size_t qkv = align256((size_t)a.T * a.H * D * 2);
+                unsigned char *qs = a.ws + p.off_qkv;
+                fa.f32io = false;
+                fa.xq = a.fused->xq; fa.xk = a.fused->xk; fa.xv = a.fused->xv;
+                fa.wq = a.fused->wq; fa.wk = a.fused->wk; fa.wv = a.fused->wv;
+                fa.cu = a.cu; fa.N = a.N; fa.T = a.T; fa.H = a.H; fa.d = D;
+                fa.win_in = a.fused->win_in; fa.win_out = nullptr;
+                fa.q = qs; fa.k = qs + qkv; fa.v = qs + 2 * qkv;
+                fa.stream = a.stream;
+                fa.table = table;
+                fa.nchunks = meta + a.N;
+                ia.q = fa.q; ia.k = fa.k; ia.v = fa.v;
+                ia.fused = nullptr;
+            }
             auto intra_block = [&](int j) {
-                return launch_intra_bf16<D>(a, meta, table, null_row, slabs, bnd[j] * a.H, bnd[j + 1] * a.H,
+                if (a.fused) {
+                    fa.c_lo = bnd[j];
+                    fa.c_hi = bnd[j + 1];
+                    if (launch_features(fa) != 0) return -1;
+                }
+                return launch_intra_bf16<D>(ia, meta, table, null_row, slabs, bnd[j] * a.H, bnd[j + 1] * a.H,
                                             claims + j);
             };
             if (intra_block(0) != 0 || hipEventRecord(ps->ev[0], a.stream) != hipSuccess) return -1;
@@ -1114,6 +1146,8 @@ static int launch_prefill_t(const PrefillArgs &a) {
                         return -1;
                 }
             }
+            // the fused call's new conv window, once every run's features
+            // have read the old one (the two may be the same buffer)
             if (a.fused && launch_conv_window(false, a.fused->xq, a.fused->xk, a.fused->xv, a.cu, a.N, a.T, a.H, D,
                                               a.fused->win_in, a.fused->win_out, a.stream) != 0)
                 return -1;

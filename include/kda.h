@@ -124,7 +124,7 @@ typedef enum kda_status {
  *     0  automatic (default): on the bf16 path without segments or
  *        checkpoints, when the chain's workgroups leave CUs free for the
  *        intra kernel and the sequences are long (three runs; six in the
- *        fused prefill, where the decision is the same, so the workspace is)
+ *        fused prefill, which pipelines at the same sizes)
  *     1  off
  *     2..KDA_MAX_PREFILL_BLOCKS  that many runs (with segments = 0 the
  *        segment count is then 1; with segments >= 2 the call is rejected);
@@ -202,11 +202,15 @@ int kda_prefill_ex(kda_dtype io_dtype, const void *q, const void *k, const void 
 
 /*
  * The fused prefill: the feature path, the chunkwise prefill and the output
- * gate in one call, with q, k, v and o never written to memory ("Kimi K3：架构、
- * 训练与推理系统研究" §13.2: the production kernel fuses ShortConv, the input
- * norms, the gate, the KDA recurrence and the output norm, so that the large
- * state and its inputs make fewer HBM round trips; §3.2 and §3.3 define the
- * pieces, as do kda_qkv_shortconv and kda_output_gate below).  It computes
+ * gate in one call, with o never written to memory ("Kimi K3：架构、训练与推理
+ * 系统研究" §13.2: the production kernel fuses ShortConv, the input norms, the
+ * gate, the KDA recurrence and the output norm, so that the large state and
+ * its inputs make fewer HBM round trips; §3.2 and §3.3 define the pieces, as
+ * do kda_qkv_shortconv and kda_output_gate below).  The gate is applied where
+ * the inter-chunk kernel stores o.  The feature path runs inside the
+ * intra-chunk kernel, except where the call is pipelined (see
+ * kda_prefill_options.blocks): there it runs as a pass of its own that
+ * stages q, k, v in the workspace, which is faster on this device.  It computes
  *   q, k, v = kda_qkv_shortconv(xq, xk, xv, wq, wk, wv, conv_state_in)
  *   o, hT   = kda_prefill(q, k, v, z, A, beta, h0, cu_seqlens)
  *   y       = kda_output_gate(o, gate, norm_weight, eps)
@@ -219,7 +223,7 @@ int kda_prefill_ex(kda_dtype io_dtype, const void *q, const void *k, const void 
  *   z .. dv          as for kda_prefill (dk == dv)
  *   gate             [T][H][dv] bf16 gate projection g;  norm_weight [dv] fp32
  *   y                [T][H][dv] bf16 output;  hT as for kda_prefill
- *   workspace        kda_prefill_workspace_size(N, T, H, dk, dv, KDA_BF16) bytes
+ *   workspace        kda_prefill_fused_workspace_size(N, T, H, dk, dv, KDA_BF16, NULL) bytes
  * Outputs may overlap no input (except the window in place) and no other
  * output.  Errors and asynchrony as for kda_prefill.
  */
@@ -236,8 +240,10 @@ int kda_prefill_fused(kda_dtype io_dtype, const void *xq, const void *xk, const 
  * kda_prefill_ex.  Checkpoints are not available here (the gated output pass
  * stores no states): a non-NULL checkpoint pointer or a non-zero
  * checkpoint_interval gives KDA_ERR_INVALID_ARGUMENT.  The workspace is
- * kda_prefill_ex_workspace_size(N, T, H, dk, dv, KDA_BF16, options) bytes.
- * The outputs do not depend on `blocks`, bit for bit.
+ * kda_prefill_fused_workspace_size(N, T, H, dk, dv, KDA_BF16, options) bytes.
+ * For any blocks >= 2 the outputs are bit for bit the same; with blocks = 1
+ * (the feature path inside the intra kernel) q and k may differ from the
+ * feature kernel's in the last bit, from the order of the L2 norm's sum.
  */
 int kda_prefill_fused_ex(kda_dtype io_dtype, const void *xq, const void *xk, const void *xv, const float *wq,
                          const float *wk, const float *wv, const void *conv_state_in, void *conv_state_out,
@@ -246,6 +252,15 @@ int kda_prefill_fused_ex(kda_dtype io_dtype, const void *xq, const void *xk, con
                          const float *norm_weight, float eps, void *y, float *hT,
                          const kda_prefill_options *options, void *workspace, size_t workspace_bytes,
                          void *stream);
+
+/*
+ * Workspace bytes of kda_prefill_fused_ex with these options (NULL: the
+ * defaults, kda_prefill_fused): kda_prefill_ex_workspace_size's, plus
+ * 3 T H dk bf16 values where the call is pipelined (the staged q, k, v).
+ * Returns 0 for sizes or options the call would reject.
+ */
+size_t kda_prefill_fused_workspace_size(int N, int T, int H, int dk, int dv, kda_dtype io_dtype,
+                                        const kda_prefill_options *options);
 
 /*
  * kda_prefill for callers that cannot allocate device memory: code under

@@ -23,6 +23,7 @@ def test_header_declares_the_entry_points():
                                            "kda_prefill",
                                            "kda_prefill_ex", "kda_prefill_ex_workspace_size",
                                            "kda_prefill_noalloc", "kda_prefill_fused", "kda_prefill_fused_ex",
+                                           "kda_prefill_fused_workspace_size",
                                            "kda_qkv_shortconv", "kda_output_gate",
                                            "kda_prefill_segments", "kda_prefill_workspace_size",
                                            "kda_prefill_backward", "kda_prefill_backward_workspace_size",
@@ -180,7 +181,8 @@ def test_prefill_fused_ex_options():
     """The fused prefill's options: checkpoints are refused (the gated output
     pass stores no states), out-of-range blocks and forced segments with
     forced blocks likewise; all decided on the host, before any launch.  With
-    NULL options it is kda_prefill_fused, whose workspace is the plain call's."""
+    NULL options it is kda_prefill_fused.  Its workspace is the plain call's,
+    plus the staged q, k, v (3 T H d bf16) where the call is pipelined."""
     def f(opts, io=0, ws_bytes=1 << 40):
         return kda.kda_prefill_fused_ex(io, FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288, FAKE + 16384,
                                         FAKE + 20480, None, None, FAKE + 24576, FAKE + 32768, FAKE + 36864, None,
@@ -192,10 +194,21 @@ def test_prefill_fused_ex_options():
     assert f(kda.options(segments=2, blocks=2)) == -1
     assert f(kda.options(blocks=2), io=1) == -4
     assert f(kda.options(blocks=2), ws_bytes=16) == -6     # workspace too small, reported before any launch
-    # the automatic choice pipelines the fused call where it pipelines the plain one: same workspace
-    for shape in ((1, 65536, 96), (2, 16384, 8), (32, 262144, 96)):
-        assert kda.kda_prefill_ex_workspace_size(*shape, 128, 128, kda.KDA_BF16, None) == \
-            kda.kda_prefill_workspace_size(*shape, 128, 128, kda.KDA_BF16)
+    fws = lambda N, T, H, **kw: kda.kda_prefill_fused_workspace_size(N, T, H, 128, 128, kda.KDA_BF16,
+                                                                     kda.options(**kw) if kw else None)
+    pws = lambda N, T, H, **kw: kda.kda_prefill_ex_workspace_size(N, T, H, 128, 128, kda.KDA_BF16,
+                                                                  kda.options(**kw) if kw else None)
+    staged = lambda T, H: 3 * ((T * H * 128 * 2 + 255) // 256 * 256)
+    # the K3 shape pipelines by default: q, k, v staged
+    assert fws(1, 65536, 96) == pws(1, 65536, 96) + staged(65536, 96)
+    assert fws(1, 65536, 96, blocks=1) == pws(1, 65536, 96, blocks=1)
+    assert fws(2, 1000, 3, blocks=4) == pws(2, 1000, 3, blocks=4) + staged(1000, 3)
+    # not pipelined (segmented small-head shape, a chain that fills the device): no staging
+    assert fws(2, 16384, 8) == pws(2, 16384, 8) == kda.kda_prefill_workspace_size(2, 16384, 8, 128, 128, 0)
+    assert fws(32, 262144, 96) == pws(32, 262144, 96)
+    # fp32 io and checkpoints are refused
+    assert kda.kda_prefill_fused_workspace_size(1, 1000, 2, 64, 64, kda.KDA_F32, None) == 0
+    assert fws(1, 1000, 2, interval=512) == 0
 
 
 def test_segment_option():

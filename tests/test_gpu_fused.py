@@ -91,24 +91,32 @@ def test_fused_ragged_with_window(d):
 
 
 @pytest.mark.parametrize("d,blocks", [(128, 2), (128, 6), (64, 3), (32, 16)])
-def test_fused_blocks_bit_identical_and_oracle(d, blocks):
-    """The fused call pipelined over chunk runs (the feature variant of the
-    intra kernel beside the gated output pass, the state carried between
-    runs): y, hT and the new window bit-identical to blocks = 1, also with the
-    window in place, over ragged lengths with sequences shorter than the
-    window and empty ones at the run ends; and within every bar of the
-    oracle composition."""
+def test_fused_pipelined(d, blocks):
+    """The fused call pipelined over chunk runs: a feature pass stages q, k,
+    v, then the plain intra kernel runs beside the gated output pass, the
+    state carried between runs.  Over ragged lengths with sequences shorter
+    than the window and empty ones at the run ends: y, hT and the new window
+    bit-identical for two run counts, also with the window in place; hT and
+    the window bit-identical to the separate calls (the same q, k, v, and the
+    same state arithmetic in the output and gated-output passes); y within
+    every bar of the oracle composition."""
     lens = [700, 0, 1, 2, 129, 64, 0, 333, 1500, 3, 0]
     d_ = inputs(lens, 3, d, seed=960 + d + blocks)
-    print("case fused blocks d=%d blocks=%d" % (d, blocks), flush=True)
+    print("case fused pipelined d=%d blocks=%d" % (d, blocks), flush=True)
     g = {n: (t.cuda() if isinstance(t, torch.Tensor) else t) for n, t in d_.items()}
-    y1, h1, w1 = gpu_fused(g, blocks=1)
     yb, hb, wb = gpu_fused(g, blocks=blocks)
-    assert torch.equal(yb, y1) and torch.equal(hb, h1) and torch.equal(wb, w1)
+    y2, h2, w2 = gpu_fused(g, blocks=2 if blocks != 2 else 5)
+    assert torch.equal(yb, y2) and torch.equal(hb, h2) and torch.equal(wb, w2)
     gi = dict(g, window=g["window"].clone())
     yi, hi, wi = gpu_fused(gi, in_place=True, blocks=blocks)
-    assert torch.equal(yi, y1) and torch.equal(hi, h1) and torch.equal(wi, w1)
-    check(d_, "fused blocks %d d=%d" % (blocks, d), blocks=blocks)
+    assert torch.equal(yi, yb) and torch.equal(hi, hb) and torch.equal(wi, wb)
+    ws = torch.empty_like(wb)
+    q, k, v = kda.qkv_shortconv(g["xq"], g["xk"], g["xv"], g["wq"], g["wk"], g["wv"], g["cu_seqlens"],
+                                conv_state_in=g["window"], conv_state_out=ws)
+    _, hs = kda.prefill(q, k, v, g["z"], g["A"], g["beta"], g["cu_seqlens"], h0=g["h0"], blocks=1)
+    torch.cuda.synchronize()
+    assert torch.equal(hb, hs) and torch.equal(wb, ws)
+    check(d_, "fused pipelined %d d=%d" % (blocks, d), blocks=blocks)
 
 
 def test_fused_without_window_and_in_place():

@@ -56,7 +56,7 @@ def make_state(seed=8100, dev="cuda"):
         fy=torch.empty((T, H, D), dtype=torch.bfloat16, device=dev),
         fhT=torch.empty((N, H, D, D), dtype=torch.float32, device=dev),
         fwin=torch.empty_like(ff["window"]),
-        ws4=torch.empty(kda.kda_prefill_ex_workspace_size(N, T, H, D, D, kda.KDA_BF16, kda.options(blocks=3)),
+        ws4=torch.empty(kda.kda_prefill_fused_workspace_size(N, T, H, D, D, kda.KDA_BF16, kda.options(blocks=3)),
                         dtype=torch.uint8, device=dev),
     )
     return p, dec, f, fz, bufs
