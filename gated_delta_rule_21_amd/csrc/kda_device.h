@@ -182,17 +182,20 @@ __device__ __forceinline__ float exp2i(int e) { return __uint_as_float((uint32_t
 
 // Maximum over the 64 lanes of a wavefront of values x >= 0: a DPP max-scan
 // inside each 16-lane row, then the four row maxima through readlane.  The
-// result is wave-uniform.
+// result is wave-uniform.  Non-negative floats order like their bit patterns,
+// so the scan runs on the integers: one DPP-fused integer max per step, with
+// no NaN quieting around it, and the last three maxima in scalar registers.
 __device__ __forceinline__ float wave_max_nonneg(float x) {
-    x = fmaxf(x, KDA_DPP(x, 0x111));
-    x = fmaxf(x, KDA_DPP(x, 0x112));
-    x = fmaxf(x, KDA_DPP(x, 0x114));
-    x = fmaxf(x, KDA_DPP(x, 0x118));
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
-    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+    uint32_t u = __float_as_uint(x);
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x111, 0xf, 0xf, true));
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x112, 0xf, 0xf, true));
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x114, 0xf, 0xf, true));
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x118, 0xf, 0xf, true));
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)u, 15);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)u, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)u, 47);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)u, 63);
+    return __uint_as_float(max(max(r0, r1), max(r2, r3)));
 }
 
 // Lane 15 of each 16-lane row, broadcast to the row.

@@ -256,13 +256,17 @@ struct InterShape {
     static_assert(lds_bytes <= 160 * 1024, "LDS per workgroup");
 };
 
+// Copy one 1 KiB fragment from global `src` to LDS `dst` (16 bytes per lane).
+// Asynchronous: wait on vmcnt before use.
+__device__ __forceinline__ void copy_frag_to_lds(const unsigned char *src, unsigned char *dst, int lane) {
+    __builtin_amdgcn_global_load_lds(src + lane * 16, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+}
+
 // Copy `nfrag` consecutive 1 KiB fragments from global `src` to LDS `dst`,
 // spread over the workgroup's waves.  Asynchronous: wait on vmcnt before use.
 __device__ __forceinline__ void copy_frags_to_lds(const unsigned char *src, unsigned char *dst, int nfrag,
                                                   int wave, int nwaves, int lane) {
-    for (int f = wave; f < nfrag; f += nwaves)
-        __builtin_amdgcn_global_load_lds(src + (size_t)f * 1024 + lane * 16,
-                                         (__attribute__((address_space(3))) void *)(dst + f * 1024), 16, 0, 0);
+    for (int f = wave; f < nfrag; f += nwaves) copy_frag_to_lds(src + (size_t)f * 1024, dst + f * 1024, lane);
 }
 
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
@@ -483,7 +487,9 @@ __global__ void __launch_bounds__((InterShape<D, F32IO, MODE>::NT))
         static_assert(64 * SEG % SHP::NT == 0, "pieces per thread");
         auto flush_o = [&](int par, int t0, int L) {
             const uint16_t *ob = obuf + par * 64 * OP;
-            for (int i = tid; i < 64 * SEG; i += SHP::NT) {
+#pragma unroll
+            for (int k = 0; k < PPT; ++k) {
+                const int i = tid + SHP::NT * k;
                 const int r = i / SEG, sgm = i % SEG;
                 if (r < L)
                     *reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(o) +
@@ -536,6 +542,16 @@ __global__ void __launch_bounds__((InterShape<D, F32IO, MODE>::NT))
         auto copyB = [&](int c, unsigned char *dst) {
             copy_frags_to_lds(slab_of(c) + SL::kdT, dst, SL::FB, wave, WPG, lane);
         };
+        // region B of the slab at `src`, unrolled: wave w copies fragments w,
+        // w + WPG, ...; only the last round depends on the (uniform) wave index
+        auto copyB_from = [&](const unsigned char *src, unsigned char *dst) {
+            constexpr int NB = (SL::FB + WPG - 1) / WPG;
+#pragma unroll
+            for (int r = 0; r < NB; ++r) {
+                const int f = wave + r * WPG;
+                if (r < NB - 1 || f < SL::FB) copy_frag_to_lds(src + SL::kdT + (size_t)f * 1024, dst + f * 1024, lane);
+            }
+        };
         // A copies per wave: the last of a step's memory operations, and the
         // only ones still allowed in flight at its end
         constexpr int NA = SL::FA / WPG;
@@ -556,11 +572,18 @@ __global__ void __launch_bounds__((InterShape<D, F32IO, MODE>::NT))
         }
         wait_all_memory();
         __syncthreads();
+        // the slab of chunk c, and the A ring slot that holds it (the slot
+        // two chunks ahead is the one before it): advanced step by step
+        const unsigned char *slab_c = slab_of(c_begin);
+        int aslot = 0;
         for (int c = c_begin; c < c_end; ++c) {
             const int i = c - c_begin;
             const int par = i & 1;
-            const unsigned char *abuf = aring + (i % 3) * AB;
+            const unsigned char *abuf = aring + aslot * AB;
             const unsigned char *bbuf = bring + par * BB;
+            // chunks c + 1 and c + 2, clamped to the sequence's last chunk
+            const unsigned char *slab_n1 = c + 1 < c_end ? slab_c + slab_stride : slab_c;
+            const unsigned char *slab_n2 = c + 2 < c_end ? slab_c + 2 * slab_stride : slab_c;
             // a region-B offset of the slab, seen in the B buffer
             auto fragB = [&](size_t off, int idx) -> u32x4 {
                 return *reinterpret_cast<const u32x4 *>(bbuf + (off - SL::kdT) + ((size_t)idx * 64 + lane) * 16);
@@ -581,7 +604,7 @@ __global__ void __launch_bounds__((InterShape<D, F32IO, MODE>::NT))
             // flight on every path: the compiler can then wait for U by count
             // instead of draining every copy.
             {
-                const u32x2 *us = reinterpret_cast<const u32x2 *>(slab_of(min(c + 1, c_end - 1)) + SL::u);
+                const u32x2 *us = reinterpret_cast<const u32x2 *>(slab_n1 + SL::u);
 #pragma unroll
                 for (int I = 0; I < 4; ++I) un[I] = load_untracked(us + (I * KT + vt) * 64 + lane);
             }
@@ -597,10 +620,9 @@ __global__ void __launch_bounds__((InterShape<D, F32IO, MODE>::NT))
                         gate + ((size_t)(t0 + (r < L ? r : 0)) * H + h) * D + 8 * sgm));
                 }
             }
-            copyB(min(c + 1, c_end - 1), bring + (par ^ 1) * BB);
-            const bool fetch_a = c + 2 < c_end;
-            const unsigned char *a_src = slab_of(fetch_a ? c + 2 : c);
-            unsigned char *a_dst = aring + ((i + 2) % 3) * AB;
+            copyB_from(slab_n1, bring + (par ^ 1) * BB);
+            const unsigned char *a_src = slab_n2;
+            unsigned char *a_dst = aring + (aslot == 0 ? 2 : aslot - 1) * AB;
             auto copyA_part = [&](int r) {
                 const int f = wave + r * WPG;
                 __builtin_amdgcn_global_load_lds(a_src + (size_t)f * 1024 + lane * 16,
@@ -765,6 +787,8 @@ __global__ void __launch_bounds__((InterShape<D, F32IO, MODE>::NT))
 #pragma unroll
                 for (int k = 0; k < PPT; ++k) gcur[k] = gnext[k];
             }
+            slab_c = slab_n1;
+            aslot = aslot == 2 ? 0 : aslot + 1;
         }
         if constexpr (GATE) {
             if (o_L > 0) flush_gate(o_t0, o_L);
