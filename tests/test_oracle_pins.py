@@ -62,7 +62,7 @@ def test_gate_bounds_random():
 
 def test_decode_is_one_prefill_token():
     """A decode step equals a prefill of one token per sequence, and T steps
-    equal a prefill of T tokens (P5 §11.2: decode advances the state that
+    equal a prefill of T tokens ("Kimi K3：架构、训练与推理系统研究" §11.2: decode advances the state that
     prefill left, one token at a time)."""
     d = pins.rand_inputs(30, [1, 1, 1], H=2, dk=8, dv=6, h0_std=0.5)
     o, hT = pins.call(_run, d)
