@@ -976,20 +976,26 @@ __global__ void __launch_bounds__(D * 4) combine_kernel(const float *__restrict_
 // workgroups of one pass fill less than half the device, into as many
 // segments as fill it once, each of at least 4 chunks.  A function of the
 // sizes and the current device's compute-unit count only.
-// Pipelined prefill: worth it when the chain's workgroups (N H of them per
+// Pipelined prefill, two cases.  When the chain's workgroups (N H of them per
 // 64 value columns) leave at least 32 CUs to the intra kernel, and the
 // sequences are long enough that every run keeps the chain busy for far
-// longer than the per-run launch and delay costs (tens of microseconds).
-// Three runs for the plain call; six for the fused one, whose intra kernel
+// longer than the per-run launch and delay costs (tens of microseconds): three
+// runs for the plain call; six for the fused one, whose intra kernel pass
 // (with the feature path) and chain (with the gate) are both longer, so
-// shorter runs start the chain earlier.  Whether to pipeline does not depend
-// on `fused`.
+// shorter runs start the chain earlier.  When the chain fills the device
+// several times over, runs still help where many long sequences finish at
+// different times: the next run's intra kernel fills the CUs that the last
+// chain workgroups (the longest sequences) leave idle.  Measured at H = 96,
+// d = 128: 32 lognormal lengths averaging 128 chunks 20.2 -> 19.3 ms (fused
+// 32.9 -> 29.3), 32 equal ones 20.1 -> 19.9; 8 sequences of 256 chunks or 16
+// of 96 gained nothing (+0.2 to +2 %), so four runs from 16 sequences of 128
+// chunks up.  Whether to pipeline does not depend on `fused`.
 int choose_blocks(int N, int T, int H, int d, bool fused) {
     if (N <= 0 || T <= 0 || H <= 0) return 1;
     const long long chain_wgs = (long long)N * H * (d == 128 ? 2 : 1);
-    if (chain_wgs > device_cus() - 32) return 1;
     const long long chunks_per_seq = (long long)T / kChunk / N;
-    return chunks_per_seq >= 192 ? (fused ? 6 : 3) : 1;
+    if (chain_wgs <= device_cus() - 32) return chunks_per_seq >= 192 ? (fused ? 6 : 3) : 1;
+    return N >= 16 && chunks_per_seq >= 128 ? 4 : 1;
 }
 
 int choose_segments(int N, int T, int H, int d) {

@@ -124,7 +124,10 @@ typedef enum kda_status {
  *     0  automatic (default): on the bf16 path without segments or
  *        checkpoints, when the chain's workgroups leave CUs free for the
  *        intra kernel and the sequences are long (three runs; six in the
- *        fused prefill, which pipelines at the same sizes)
+ *        fused prefill), or when at least 16 sequences average at least 128
+ *        chunks (four runs: the next run fills the CUs that the chain's
+ *        longest sequences leave idle); the fused prefill pipelines at the
+ *        same sizes
  *     1  off
  *     2..KDA_MAX_PREFILL_BLOCKS  that many runs (with segments = 0 the
  *        segment count is then 1; with segments >= 2 the call is rejected);

@@ -169,9 +169,13 @@ def test_block_option():
     # shape, split by default, then needs no segment transitions
     small = lambda **kw: kda.kda_prefill_ex_workspace_size(2, 16384, 8, 128, 128, kda.KDA_BF16, kda.options(**kw))
     assert small(blocks=3) == small(segments=1) + 2 * 8 * 128 * 128 * 4 + 256
-    # many short sequences, or a chain that fills the device: no pipeline by default
-    assert kda.kda_prefill_ex_workspace_size(32, 262144, 96, 128, 128, kda.KDA_BF16, kda.options()) == \
-        kda.kda_prefill_ex_workspace_size(32, 262144, 96, 128, 128, kda.KDA_BF16, kda.options(blocks=1))
+    # a chain that fills the device: four runs from 16 sequences of 128 chunks on average
+    # (the varlen batch), none for fewer or shorter sequences
+    vw = lambda N, T, **kw: kda.kda_prefill_ex_workspace_size(N, T, 96, 128, 128, kda.KDA_BF16, kda.options(**kw))
+    assert vw(32, 262144) == vw(32, 262144, blocks=4) == vw(32, 262144, blocks=1) + 32 * 96 * 128 * 128 * 4 + 256
+    assert vw(8, 131072) == vw(8, 131072, blocks=1)
+    assert vw(16, 98304) == vw(16, 98304, blocks=1)
+    assert vw(64, 262144) == vw(64, 262144, blocks=1)
     # the backward ignores the option
     bw = lambda o: kda.kda_prefill_backward_workspace_size(1, 65536, 8, 128, 128, kda.KDA_BF16, o)
     assert bw(kda.options(blocks=3)) == bw(kda.options(blocks=1)) > 0
@@ -203,9 +207,10 @@ def test_prefill_fused_ex_options():
     assert fws(1, 65536, 96) == pws(1, 65536, 96) + staged(65536, 96)
     assert fws(1, 65536, 96, blocks=1) == pws(1, 65536, 96, blocks=1)
     assert fws(2, 1000, 3, blocks=4) == pws(2, 1000, 3, blocks=4) + staged(1000, 3)
-    # not pipelined (segmented small-head shape, a chain that fills the device): no staging
+    # not pipelined (segmented small-head shape, a chain of few sequences that fills the device): no staging
     assert fws(2, 16384, 8) == pws(2, 16384, 8) == kda.kda_prefill_workspace_size(2, 16384, 8, 128, 128, 0)
-    assert fws(32, 262144, 96) == pws(32, 262144, 96)
+    assert fws(32, 262144, 96) == pws(32, 262144, 96) + staged(262144, 96)
+    assert fws(8, 131072, 96) == pws(8, 131072, 96)
     # fp32 io and checkpoints are refused
     assert kda.kda_prefill_fused_workspace_size(1, 1000, 2, 64, 64, kda.KDA_F32, None) == 0
     assert fws(1, 1000, 2, interval=512) == 0
