@@ -119,6 +119,29 @@ def test_fused_pipelined(d, blocks):
     check(d_, "fused pipelined %d d=%d" % (blocks, d), blocks=blocks)
 
 
+@pytest.mark.parametrize("lens", [[0, 0], [1], [2, 0, 3]])
+def test_fused_pipelined_degenerate(lens):
+    """Pipelined fused calls over batches with more runs than chunks, all
+    sequences empty, or shorter than the conv window: y and hT equal the
+    separate calls' (hT bit for bit, an empty sequence's being its h0), and
+    the window is the separate feature path's, bit for bit."""
+    print("case fused pipelined degenerate lens=%s" % lens, flush=True)
+    d_ = inputs(lens, 2, 64, seed=990 + len(lens) + sum(lens))
+    g = {n: (t.cuda() if isinstance(t, torch.Tensor) else t) for n, t in d_.items()}
+    yb, hb, wb = gpu_fused(g, blocks=16)
+    ws = torch.empty_like(wb)
+    q, k, v = kda.qkv_shortconv(g["xq"], g["xk"], g["xv"], g["wq"], g["wk"], g["wv"], g["cu_seqlens"],
+                                conv_state_in=g["window"], conv_state_out=ws)
+    _, hs = kda.prefill(q, k, v, g["z"], g["A"], g["beta"], g["cu_seqlens"], h0=g["h0"], blocks=1)
+    torch.cuda.synchronize()
+    assert torch.equal(hb, hs) and torch.equal(wb, ws)
+    for n, L in enumerate(lens):
+        if L == 0:
+            assert torch.equal(hb[n], g["h0"][n])
+    if sum(lens) > 0:
+        check(d_, "fused degenerate %s" % lens, blocks=16)
+
+
 def test_fused_without_window_and_in_place():
     check(inputs([9, 1, 40, 130], 4, 128, seed=910, window=False, h0_std=None), "fused no window, no h0")
     check(inputs([9, 1, 0, 40, 300], 2, 64, seed=911), "fused window in place", in_place=True)

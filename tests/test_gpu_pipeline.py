@@ -41,6 +41,25 @@ def test_blocks_bit_identical_and_oracle(d, blocks, h0):
     compare_prefill(ob, hb, ro, rh, inp["cu_seqlens"], "bf16", label="blocks %d" % blocks)
 
 
+@pytest.mark.parametrize("lens", [[0, 0, 0], [1], [5, 0, 64]])
+def test_blocks_degenerate_batches(lens):
+    """More runs than chunks, every sequence empty, one token: each run may
+    hold no chunk at all; the outputs are still bit-identical to one run and
+    an empty sequence's final state is its h0."""
+    print("case pipeline degenerate lens=%s" % lens, flush=True)
+    inp = W.random_prefill(lens, 2, 64, "bf16", h0_std=0.05, seed=9050 + len(lens) + sum(lens))
+    g = to_gpu(inp)
+    o1, h1 = run(g, 1)
+    ob, hb = run(g, 16)
+    assert torch.equal(ob, o1) and torch.equal(hb, h1)
+    for n, L in enumerate(lens):
+        if L == 0:
+            assert torch.equal(hb[n], g["h0"][n])
+    if sum(lens) > 0:
+        ro, rh = oracle_prefill(inp)
+        compare_prefill(ob, hb, ro, rh, inp["cu_seqlens"], "bf16", label="degenerate %s" % lens)
+
+
 def test_blocks_hT_may_alias_h0():
     print("case pipeline hT aliasing h0", flush=True)
     inp = W.random_prefill(LENS, 2, 128, "bf16", h0_std=0.05, seed=9100)
