@@ -180,7 +180,12 @@ int kda_prefill_segments(int N, int T, int H, int dk, int dv, kda_dtype io_dtype
  *                writing that slice of hT), but must not overlap it otherwise
  *   workspace    device scratch of at least kda_prefill_workspace_size(...)
  *                bytes, 256-byte aligned, owned by the caller; contents on
- *                entry are ignored, on return undefined
+ *                entry are ignored, on return undefined.  The call uses it
+ *                until its work on `stream` completes: calls in flight at the
+ *                same time need workspaces of their own.  A pipelined call's
+ *                chain runs on a helper stream of the calling thread, so two
+ *                pipelined calls from one thread run their chains one after
+ *                the other, whatever streams they were given
  *
  * cu_seqlens content is not read on the host.  With KDA_DEBUG_CHECK_CU=1 in
  * the environment the call copies it to the host, synchronises `stream`
