@@ -441,8 +441,8 @@ def decode_fused_cost(kda, W, dev, reps: int = 100) -> dict:
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on exactly one GPU; --gpus %d is not supported "
-              "(the multi-GPU sharding is described in DESIGN.md)" % args.gpus, file=sys.stderr)
+        print("bench.py: the library runs on one GPU and shards nothing across GPUs; --gpus %d is not "
+              "supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch
