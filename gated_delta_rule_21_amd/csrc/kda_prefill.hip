@@ -1,6 +1,6 @@
 // kda_prefill.hip -- chunkwise-parallel KDA prefill for gfx950.
 //
-// Three kernels on the caller's stream:
+// The kernels, on the caller's stream unless pipelined (below):
 //   chunk_table_kernel  cu_seqlens -> first chunk of every sequence and a
 //                       (sequence, first token, length) record per chunk;
 //                       chunks of 64 tokens start at every sequence start.
@@ -16,6 +16,13 @@
 //                       sequence unless long sequences are split (below).
 //   combine_kernel      only for split sequences: composes the segments'
 //                       affine state maps into every segment's incoming state.
+//
+// Chunk-block pipeline (long sequences, bf16): the chunk table is cut into
+// runs, and the intra kernel of run j + 1 (caller's stream) runs beside the
+// inter kernel of run j (a helper stream of the calling thread, ordered by
+// events); the state crosses run boundaries through the workspace.  The
+// fused call runs the same pipeline with a feature pass before each intra
+// kernel and the inter kernel in its gated output mode.
 //
 // Split sequences (intra-device context parallelism, "Kimi K3：架构…" §11.1
 // and the KCP merge of the devpress K3 walk-through §8.1, Eq 17): inter_kernel
