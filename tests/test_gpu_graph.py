@@ -13,6 +13,8 @@ buffer scribbles and synchronisations between the replays.  Every replay
 must equal the eager run of the same calls bit for bit: the kernels are
 deterministic, and the library makes no allocation, host synchronisation or
 memset on the capturing stream, and reads only what it is given."""
+import threading
+
 import pytest
 import torch
 
@@ -132,3 +134,47 @@ def test_capture_and_replay():
         for n, x, y in zip(OUTS, got, want):
             assert torch.equal(x, y), "replay %d: %s differs from the eager run" % (rep, n)
     g.reset()
+
+
+def test_first_pipelined_call_under_capture():
+    """A thread whose first pipelined call is made under graph capture: the
+    thread's helper stream and events are created during the capture, and the
+    replays equal the eager call bit for bit."""
+    print("case first pipelined call of a thread under capture", flush=True)
+    p = to(W.random_prefill(LENS, H, D, "bf16", h0_std=0.05, seed=8300), "cuda")
+    N, T = len(LENS), sum(LENS)
+    o_want, h_want = kda.prefill(p["q"], p["k"], p["v"], p["z"], p["A"], p["beta"], p["cu_seqlens"], h0=p["h0"],
+                                 blocks=3)
+    torch.cuda.synchronize()
+    ws = torch.empty(kda.kda_prefill_ex_workspace_size(N, T, H, D, D, kda.KDA_BF16, kda.options(blocks=3)),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(o_want)
+    hT = torch.empty_like(h_want)
+    result = {}
+
+    def body():
+        try:
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(g, stream=s):
+                    kda.prefill(p["q"], p["k"], p["v"], p["z"], p["A"], p["beta"], p["cu_seqlens"], h0=p["h0"],
+                                o=o, hT=hT, workspace=ws, blocks=3)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                o.fill_(-7.0)
+                hT.fill_(-7.0)
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                result.setdefault("equal", []).append(torch.equal(o, o_want) and torch.equal(hT, h_want))
+            g.reset()
+        except Exception as e:           # reported by the main thread
+            result["error"] = repr(e)
+
+    t = threading.Thread(target=body)
+    t.start()
+    t.join(timeout=120)
+    assert not t.is_alive()
+    assert "error" not in result, result.get("error")
+    assert result["equal"] == [True, True, True]
