@@ -60,6 +60,26 @@ def test_blocks_degenerate_batches(lens):
         compare_prefill(ob, hb, ro, rh, inp["cu_seqlens"], "bf16", label="degenerate %s" % lens)
 
 
+def test_blocks_chained_calls_equal_one_call():
+    """A long sequence prefilled in two pipelined calls, cut at a chunk
+    boundary and carried through hT -> h0, equals one call bit for bit: the
+    chunks are the same, and so is every value computed on them."""
+    print("case pipeline chained calls", flush=True)
+    inp = W.random_prefill([64 * 40], 3, 128, "bf16", h0_std=0.05, seed=9300)
+    g = to_gpu(inp)
+    o1, h1 = run(g, 1)
+    cut = 64 * 17
+    parts = []
+    for lo, hi, h0 in ((0, cut, g["h0"]), (cut, 64 * 40, None)):
+        sub = {n: g[n][lo:hi].contiguous() for n in ("q", "k", "v", "z", "beta")}
+        sub["A"] = g["A"]
+        sub["cu_seqlens"] = W.cu_from_lengths([hi - lo]).cuda()
+        sub["h0"] = h0 if h0 is not None else parts[-1][1]
+        parts.append(run(sub, 3))
+    assert torch.equal(torch.cat([parts[0][0], parts[1][0]]), o1)
+    assert torch.equal(parts[1][1], h1)
+
+
 def test_blocks_hT_may_alias_h0():
     print("case pipeline hT aliasing h0", flush=True)
     inp = W.random_prefill(LENS, 2, 128, "bf16", h0_std=0.05, seed=9100)
