@@ -142,6 +142,30 @@ def test_fused_pipelined_degenerate(lens):
         check(d_, "fused degenerate %s" % lens, blocks=16)
 
 
+def test_fused_chained_calls_equal_one_call():
+    """A long sequence through two pipelined fused calls, cut at a chunk
+    boundary, with the state (hT -> h0) and the conv window carried, equals
+    one call bit for bit: y, the final state and the final window."""
+    print("case fused chained calls", flush=True)
+    d_ = inputs([64 * 30], 2, 128, seed=995)
+    g = {n: (t.cuda() if isinstance(t, torch.Tensor) else t) for n, t in d_.items()}
+    y1, h1, w1 = gpu_fused(g, blocks=3)
+    cut = 64 * 11
+    outs = []
+    win, h0 = g["window"], g["h0"]
+    for lo, hi in ((0, cut), (cut, 64 * 30)):
+        sub = dict(g)
+        for n in ("xq", "xk", "xv", "z", "beta", "gate"):
+            sub[n] = g[n][lo:hi].contiguous()
+        sub["cu_seqlens"] = W.cu_from_lengths([hi - lo]).cuda()
+        sub["window"], sub["h0"] = win, h0
+        y, hT, win = gpu_fused(sub, blocks=3)
+        h0 = hT
+        outs.append(y)
+    assert torch.equal(torch.cat(outs), y1)
+    assert torch.equal(h0, h1) and torch.equal(win, w1)
+
+
 def test_fused_without_window_and_in_place():
     check(inputs([9, 1, 40, 130], 4, 128, seed=910, window=False, h0_std=None), "fused no window, no h0")
     check(inputs([9, 1, 0, 40, 300], 2, 64, seed=911), "fused window in place", in_place=True)
