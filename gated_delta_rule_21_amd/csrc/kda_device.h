@@ -198,6 +198,26 @@ __device__ __forceinline__ float wave_max_nonneg(float x) {
     return __uint_as_float(max(max(r0, r1), max(r2, r3)));
 }
 
+// Sum over each aligned group of W consecutive lanes (W a power of two up
+// to 64), every lane of the group receiving it: a butterfly over the lane
+// index bits, low bit first.  Inside a 16-lane row the partners are reached
+// by DPP moves, with no trip through the LDS unit: the quad permutations
+// [1,0,3,2] and [2,3,0,1], then the half-row mirror and the row mirror,
+// whose partners hold the same values as lane ^ 4 and lane ^ 8 once each
+// quad, then each half-row, is uniform.  The result equals that of the
+// shuffle butterfly bit for bit (each step adds the same two values).
+template <int W>
+__device__ __forceinline__ float lane_group_sum(float x) {
+    static_assert(W >= 2 && W <= 64 && (W & (W - 1)) == 0, "lane group");
+    x += KDA_DPP(x, 0xb1);
+    if constexpr (W >= 4) x += KDA_DPP(x, 0x4e);
+    if constexpr (W >= 8) x += KDA_DPP(x, 0x141);
+    if constexpr (W >= 16) x += KDA_DPP(x, 0x140);
+    if constexpr (W >= 32) x += __shfl_xor(x, 16, 64);
+    if constexpr (W >= 64) x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
 // Lane 15 of each 16-lane row, broadcast to the row.
 __device__ __forceinline__ float row16_last(float x) { return KDA_DPP(x, 0x15f); }
 

@@ -41,7 +41,8 @@ __device__ __forceinline__ void seq_bounds(const int32_t *cu, int n, int T, int 
 
 // ShortConv -> Swish (-> L2Norm for q and k).  blockIdx.z: 0 = q, 1 = k, 2 = v;
 // blockIdx.y: a span of 1024 channels of the [H][d] row (256 / (d / 4)
-// heads); blockIdx.x: a range of TR tokens (tile0 + blockIdx.x).  The block
+// heads); blockIdx.x: a range of TR tokens (tile0 plus a reordering of
+// blockIdx.x, below).  The block
 // first copies rows t0 - 3 .. t0 + TR - 1 of its span into LDS (direct
 // global -> LDS copies, 16 bytes per lane), then every thread walks its 4
 // channels through the range, reading the four taps of each token from LDS.
@@ -71,7 +72,17 @@ __global__ void __launch_bounds__(256) shortconv_kernel(
     const int CW = 3 * D;                        // window channels per head: q | k | v
     const size_t rowc = (size_t)H * D;           // channels per token row
     const int ch0 = blockIdx.y * SPAN;           // first channel of the span
-    const int t0 = (tile0 + (int)blockIdx.x) * TR, t1 = min(t0 + TR, T);
+    // Workgroups are dealt to the eight XCDs in turn (their L2 caches are
+    // separate), so launch index x takes token tile (x % 8) * per + x / 8:
+    // each XCD walks a contiguous range of tiles in order, and the three
+    // rows before a tile are the previous tile's last rows, just read into
+    // the same L2.  The last gridDim.x % 8 workgroups keep their own tiles.
+    int tx = (int)blockIdx.x;
+    {
+        const int per = (int)gridDim.x / 8;
+        if (tx < 8 * per) tx = (tx % 8) * per + tx / 8;
+    }
+    const int t0 = (tile0 + tx) * TR, t1 = min(t0 + TR, T);
     // the tokens this launch writes (every thread reads the same entries)
     int w_lo = 0, w_hi = T;
     if (table) {
@@ -141,8 +152,7 @@ __global__ void __launch_bounds__(256) shortconv_kernel(
         }
         if (which < 2) {
             float ss = f[0] * f[0] + f[1] * f[1] + f[2] * f[2] + f[3] * f[3];
-#pragma unroll
-            for (int off = 1; off < G; off <<= 1) ss += __shfl_xor(ss, off, 64);
+            ss = lane_group_sum<G>(ss);
             f = f * fast_rsq(ss);
         }
         store_io4<F32IO>(out, ((size_t)t * H + h) * D + c0, f);
@@ -242,8 +252,7 @@ __global__ void __launch_bounds__(256) output_gate_kernel(const void *o, const v
             const long long r = base + m * RPB + threadIdx.x / G;
             if (r >= rows) break;                // uniform over a row's lanes
             float ss = ov[m][0] * ov[m][0] + ov[m][1] * ov[m][1] + ov[m][2] * ov[m][2] + ov[m][3] * ov[m][3];
-#pragma unroll
-            for (int off = 1; off < G; off <<= 1) ss += __shfl_xor(ss, off, 64);
+            ss = lane_group_sum<G>(ss);
             const float inv = fast_rsq(ss * (1.f / D) + eps);
             f32x4 out;
 #pragma unroll
@@ -263,7 +272,9 @@ static unsigned stride_blocks(long long rows, int rows_per_block) {
 
 template <int D, bool F32IO>
 static int launch_features_t(const FeatureArgs &a) {
-    constexpr int TR = F32IO ? 8 : 16;   // staged rows: (TR + 3) x 1024 channels
+    // tokens per tile: TR + 3 staged rows of 1024 channels, 32 KiB in bf16
+    // (five workgroups per CU) and 44 KiB in fp32
+    constexpr int TR = F32IO ? 8 : 13;
     if (a.T > 0) {
         // token tiles: all, or (chunk run) those that can hold its tokens.
         // Chunk c starts at token 64 (c - N) at the earliest (every chunk but

@@ -529,8 +529,7 @@ __global__ void __launch_bounds__((InterShape<D, F32IO, MODE>::NT))
                 float ss = 0.f;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) ss += ov[0][j] * ov[0][j] + ov[1][j] * ov[1][j];
-#pragma unroll
-                for (int off = 1; off < SEG; off <<= 1) ss += __shfl_xor(ss, off, 64);
+                ss = lane_group_sum<SEG>(ss);
                 const float inv = fast_rsq(ss * (1.f / D) + eps);
                 f32x4 gv[2];
                 bf16_to_quads(gcur[k], gv[0], gv[1]);
