@@ -78,8 +78,7 @@ __global__ void __launch_bounds__(1024) decode_kernel(
     float kq = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) kq += kk[i] * qq[i];
-#pragma unroll
-    for (int off = 1; off < LPR; off <<= 1) kq += __shfl_xor(kq, off, 64);
+    kq = lane_group_sum<LPR>(kq);
 
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
@@ -96,11 +95,8 @@ __global__ void __launch_bounds__(1024) decode_kernel(
             pk += sb[i] * kk[i];
             pq += sb[i] * qq[i];
         }
-#pragma unroll
-        for (int off = 1; off < LPR; off <<= 1) {
-            pk += __shfl_xor(pk, off, 64);
-            pq += __shfl_xor(pq, off, 64);
-        }
+        pk = lane_group_sum<LPR>(pk);
+        pq = lane_group_sum<LPR>(pq);
         const float e = load_io<F32IO>(v, (size_t)pair * DV + row) - pk;
         const float be = b * e;
 #pragma unroll
@@ -188,8 +184,7 @@ __global__ void __launch_bounds__(1024) decode_fused_kernel(
         }
         if (which < 2) {
             float ss = f[0] * f[0] + f[1] * f[1] + f[2] * f[2] + f[3] * f[3];
-#pragma unroll
-            for (int off = 1; off < G; off <<= 1) ss += __shfl_xor(ss, off, 64);
+            ss = lane_group_sum<G>(ss);
             f = f * fast_rsq(ss);
         }
         float *dst = which == 0 ? fq : which == 1 ? fk : fv;
@@ -230,8 +225,7 @@ __global__ void __launch_bounds__(1024) decode_fused_kernel(
     float kq = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) kq += kk[i] * qq[i];
-#pragma unroll
-    for (int off = 1; off < LPR; off <<= 1) kq += __shfl_xor(kq, off, 64);
+    kq = lane_group_sum<LPR>(kq);
 
     float sb[16];
 #pragma unroll
@@ -244,11 +238,8 @@ __global__ void __launch_bounds__(1024) decode_fused_kernel(
         pk += sb[i] * kk[i];
         pq += sb[i] * qq[i];
     }
-#pragma unroll
-    for (int off = 1; off < LPR; off <<= 1) {
-        pk += __shfl_xor(pk, off, 64);
-        pq += __shfl_xor(pq, off, 64);
-    }
+    pk = lane_group_sum<LPR>(pk);
+    pq = lane_group_sum<LPR>(pq);
     const float be = b * (fv[row] - pk);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {

@@ -125,8 +125,7 @@ __global__ void __launch_bounds__(1024) decode_window_kernel(
                 for (int j = 0; j < 4; ++j) pq += sb[4 * m + j] * qv[j];
             }
         }
-#pragma unroll
-        for (int off = 1; off < LPR; off <<= 1) pk += __shfl_xor(pk, off, 64);
+        pk = lane_group_sum<LPR>(pk);
         const float be = b * (vv[row] - pk);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -163,11 +162,8 @@ __global__ void __launch_bounds__(1024) decode_window_kernel(
         }
         float pq;
         const float be = advance(img, img + DK, img + 3 * DK, img[3 * DK + DV], qq, pq);
-#pragma unroll
-        for (int off = 1; off < LPR; off <<= 1) {
-            kq += __shfl_xor(kq, off, 64);
-            pq += __shfl_xor(pq, off, 64);
-        }
+        kq = lane_group_sum<LPR>(kq);
+        pq = lane_group_sum<LPR>(pq);
         if (cl == 0) store_io<F32IO>(o, ((size_t)(n * L + u) * H + h) * DV + row, pq + be * kq);
     }
     if (commit_window && acc + L > 0) write_state();
